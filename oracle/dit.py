@@ -1,0 +1,516 @@
+"""Plain NumPy oracle of the chunk-causal joint video+action DiT denoise step.
+
+TEST INFRASTRUCTURE ONLY: see ``oracle/__init__.py`` for who may import it.
+
+Sources (titles of the pages; sections named, never quoted):
+  [ARCH]  "DreamZero (WAM) 模型架构" (vla-model-architecture.pages.dev): §2.1
+          encoders, §2.3 Causal WAN DiT (input sequence construction, single
+          causal DiT block, output split, causal mask), §2.4 multi-embodiment
+          action linears, §3 training pipeline (flow-matching interpolation),
+          §4 inference pipeline (encode once, iterative denoise loop).
+  [WS1]   "DreamZero 单卡推理" (PhyAI ws1 docs): architecture table (DiT runner
+          keeps the attention KV; scheduler owns reference KV, CFG branches, DiT
+          calls and the update), request format (negative prompt for CFG,
+          512 text tokens), continuous requests (frame position, KV reset),
+          Fixed4 vs dynamic16 (DiT re-run only when the prediction changes).
+  [HYPER] hyper.ai summary of arXiv 2602.15922, "方法": chunked autoregressive
+          generation, mask letting the noisy chunk see clean earlier chunks and
+          never future tokens, KV-cache replacement by real observations,
+          DreamZero-Flash decoupled schedules.
+  [N569]  paper walk-through "World Action Models are Zero-shot Policies"
+          (ai.n569.com): training objective (shared timestep, teacher forcing,
+          joint velocity), inference (KV cache + observation feedback),
+          real-time optimisations (CFG in parallel, DiT caching by cosine
+          similarity of successive velocities, DreamZero-Flash Beta schedule).
+
+Readings where the pages are silent, ambiguous or garbled are listed in
+the design doc and are repeated at the function that takes them.
+
+Conventions: time t in [0, 1], t = 0 pure noise, t = 1 clean;
+x_t = t*x1 + (1-t)*eps; velocity target x1 - eps; Euler x += (t_next - t)*v.
+Linear weights are [out, in] (y = x W^T + b). All arithmetic runs in ``dt``
+(float32 by default, float64 on request); softmax is exp(S - rowmax)/sum.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+Array = np.ndarray
+
+
+# ----------------------------------------------------------------------------------------------
+# Elementary operations. Each is the textbook definition written out.
+# ----------------------------------------------------------------------------------------------
+
+def silu(x: Array) -> Array:
+    """SiLU(x) = x * sigmoid(x) ([ARCH] §2.3: time embedding MLP; Wan-style, reading R2)."""
+    return x / (x.dtype.type(1) + np.exp(-x))
+
+
+def gelu_tanh(x: Array) -> Array:
+    """GELU with the tanh approximation: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    one = x.dtype.type(1)
+    c = x.dtype.type(math.sqrt(2.0 / math.pi))
+    return x.dtype.type(0.5) * x * (one + np.tanh(c * (x + x.dtype.type(0.044715) * x * x * x)))
+
+
+def layer_norm(x: Array, eps: float, weight: Optional[Array] = None, bias: Optional[Array] = None) -> Array:
+    """LayerNorm over the last axis, biased variance: (x - mean) / sqrt(var + eps) [* w + b].
+
+    Reading R5: the block norms are LayerNorm (the running implementation's kernel policy on
+    [WS1] names LayerNorm), not the RMSNorm drawn on [ARCH] §2.3.
+    """
+    mu = x.mean(axis=-1, keepdims=True)
+    xc = x - mu
+    var = (xc * xc).mean(axis=-1, keepdims=True)
+    y = xc / np.sqrt(var + x.dtype.type(eps))
+    if weight is not None:
+        y = y * weight
+    if bias is not None:
+        y = y + bias
+    return y
+
+
+def rms_norm(x: Array, eps: float, gain: Optional[Array] = None) -> Array:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) [* g]."""
+    ms = (x * x).mean(axis=-1, keepdims=True)
+    y = x / np.sqrt(ms + x.dtype.type(eps))
+    if gain is not None:
+        y = y * gain
+    return y
+
+
+def linear(x: Array, w: Array, b: Optional[Array] = None) -> Array:
+    """y = x W^T + b with W stored [out, in]."""
+    y = x @ w.T
+    if b is not None:
+        y = y + b
+    return y
+
+
+def modulated_norm(x: Array, shift: Array, scale: Array, eps: float) -> Array:
+    """adaLN: LN(x) (1 + scale) + shift ([ARCH] §2.3 single block: the normed input is modulated
+    by shift and scale from the time embedding; reading R3: scale enters as 1 + scale)."""
+    return layer_norm(x, eps) * (x.dtype.type(1) + scale) + shift
+
+
+def softmax_rows(s: Array) -> Array:
+    """exp(s - rowmax) / rowsum over the last axis. Entries equal to -inf get exactly 0."""
+    m = s.max(axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    return p / p.sum(axis=-1, keepdims=True)
+
+
+def attention(q: Array, k: Array, v: Array, visible: Optional[Array] = None) -> Array:
+    """Scaled dot-product attention per head.
+
+    q [H, Lq, d], k [H, Lk, d], v [H, Lk, d]; ``visible`` [Lq, Lk] bool or None.
+    S = q k^T / sqrt(d); invisible entries are *selected* to -inf (so whatever the
+    hidden keys hold cannot reach the output); P = softmax(S); o = P v  -> [H, Lq, d].
+    Reading R10: scale 1/sqrt(d), softmax in the working precision.
+    """
+    d = q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) * q.dtype.type(1.0 / math.sqrt(d))
+    if visible is not None:
+        s = np.where(visible[None, :, :], s, q.dtype.type(-np.inf))
+    return softmax_rows(s) @ v
+
+
+# ----------------------------------------------------------------------------------------------
+# Time embedding and modulation ([ARCH] §2.3 input sequence: sinusoidal time embedding; single
+# block: modulation of the normed input by shift/scale from the time embedding).
+# ----------------------------------------------------------------------------------------------
+
+def timestep_sinusoid(t: float, freq_dim: int, dt=np.float32) -> Array:
+    """Sinusoidal embedding of the noise level s = 1000 (1 - t).
+
+    Reading R1/R2: t follows x_t = t x1 + (1-t) eps, and the pages' training pipeline samples a
+    noise step in [0, 1000] with noise at the top, so the embedded scalar is s = 1000 (1 - t).
+    emb = [cos(s w_i)]_i ++ [sin(s w_i)]_i with w_i = 10000^(-i/half), i < half = freq_dim/2.
+    The angles and their cos/sin are evaluated in float64 and rounded once to the working type.
+    """
+    half = freq_dim // 2
+    s = 1000.0 * (1.0 - float(t))
+    omega = np.power(10000.0, -np.arange(half, dtype=np.float64) / half)
+    arg = s * omega
+    return np.concatenate([np.cos(arg), np.sin(arg)]).astype(dt)
+
+
+def time_modulation(t: float, g: Dict[str, Array], freq_dim: int, dt=np.float32) -> Tuple[Array, Array]:
+    """e = W2 SiLU(W1 emb + b1) + b2;  e6 = (Wp SiLU(e) + bp) as [6, D].
+
+    Reading R3/R4: one shared time projection to six vectors (shift1, scale1, gate1, shift2,
+    scale2, gate2); each layer adds its own learned [6, D] offset.
+    """
+    emb = timestep_sinusoid(t, freq_dim, dt)
+    e = linear(silu(linear(emb, g["t_w1"], g["t_b1"])), g["t_w2"], g["t_b2"])
+    e6 = linear(silu(e), g["t_wp"], g["t_bp"])
+    return e, e6.reshape(6, -1)
+
+
+# ----------------------------------------------------------------------------------------------
+# 3-D rotary embedding of video tokens ([ARCH] §2.3: video latents go through RoPE; action tokens
+# do not). Reading R9: per-head channel pairs (2j, 2j+1); the first d_t/2 pairs rotate with the
+# frame index, the next d_h/2 with the patch row, the last d_w/2 with the patch column;
+# d_h = d_w = 2 floor(d/6), d_t = d - 2 d_h; frequency theta^(-2j'/d_axis) for local pair j'.
+# ----------------------------------------------------------------------------------------------
+
+def rope_axis_split(head_dim: int) -> Tuple[int, int, int]:
+    dh = 2 * (head_dim // 6)
+    return head_dim - 2 * dh, dh, dh
+
+
+def rope_frequencies(head_dim: int, theta: float) -> Tuple[Array, Array]:
+    """(axis index per pair in {0,1,2}, frequency per pair) for the head_dim/2 pairs."""
+    dts = rope_axis_split(head_dim)
+    axis, freq = [], []
+    for a, da in enumerate(dts):
+        for j in range(da // 2):
+            axis.append(a)
+            freq.append(theta ** (-2.0 * j / da))
+    return np.array(axis, dtype=np.int64), np.array(freq, dtype=np.float64)
+
+
+def video_positions(w, n_chunks: int, start_frame: int) -> Array:
+    """(frame, row, col) of every video token of ``n_chunks`` consecutive chunks, [n*Lv, 3].
+
+    Tokens of a chunk are in raster order (frame, row, col) (reading R8); frame indices are
+    absolute within the attention window: start_frame + chunk * frames_per_chunk + local frame
+    ([WS1] continuous requests: the pipeline carries a frame position across requests).
+    """
+    Hp, Wp, Fc = w.grid_h, w.grid_w, w.frames_per_chunk
+    out = []
+    for c in range(n_chunks):
+        for f in range(Fc):
+            for r in range(Hp):
+                for col in range(Wp):
+                    out.append((start_frame + c * Fc + f, r, col))
+    return np.array(out, dtype=np.int64)
+
+
+def apply_rope(x: Array, pos: Array, head_dim: int, theta: float) -> Array:
+    """Rotate x [T, H, d] (T tokens with positions pos [T, 3]) pair by pair.
+
+    (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a), a = pos[axis(j)] * freq(j).
+    Angles are formed in float64 and rounded once to the working precision.
+    """
+    axis, freq = rope_frequencies(head_dim, theta)
+    ang = pos[:, axis].astype(np.float64) * freq[None, :]          # [T, d/2]
+    c = np.cos(ang).astype(x.dtype)[:, None, :]
+    s = np.sin(ang).astype(x.dtype)[:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Model pieces
+# ----------------------------------------------------------------------------------------------
+
+def cast_params(p: Dict[str, Array], dt) -> Dict[str, Array]:
+    return {k: np.asarray(v, dtype=dt) for k, v in p.items()}
+
+
+def build_context(w, g: Dict[str, Array], txt: Array, img: Optional[Array]) -> Array:
+    """Condition sequence per CFG branch: [txt_b W_txt^T + b ; img W_img^T + b]  -> [br, Lc, D].
+
+    [ARCH] §2.1: image and text features (1536-d) are concatenated into one condition sequence;
+    reading R12: one Linear per modality to the model width. Branch 1 carries the negative
+    (null) prompt ([WS1] request format); the image features are shared by both branches.
+    """
+    ctx_t = linear(txt, g["txt_w"], g["txt_b"])                   # [br, Lt, D]
+    if img is None or w.ctx_img_len == 0:
+        return ctx_t
+    ctx_i = linear(img, g["img_w"], g["img_b"])                   # [Li, D]
+    ctx_i = np.broadcast_to(ctx_i[None], (ctx_t.shape[0],) + ctx_i.shape)
+    return np.concatenate([ctx_t, ctx_i], axis=1)
+
+
+def context_kv(w, lp: Dict[str, Array], ctx: Array) -> Tuple[Array, Array]:
+    """Per-layer cross-attention keys/values of the condition sequence (computed once per request:
+    [ARCH] §4 encodes the conditions once and caches them). Kc = RMS(ctx Wck^T + b) g; Vc = ctx Wcv^T + b.
+    Reading R11: RMSNorm on cross keys and queries, over the full width.
+    """
+    kc = rms_norm(linear(ctx, lp["w_ck"], lp["b_ck"]), w.eps, lp["g_ck"])
+    vc = linear(ctx, lp["w_cv"], lp["b_cv"])
+    return kc, vc
+
+
+def embed_tokens(g: Dict[str, Array], x_video: Array, x_action: Array, w, n_chunks: int) -> Array:
+    """Token sequence of ``n_chunks`` chunks: per chunk [video rows ; action rows] -> [n*Lq, D].
+
+    [ARCH] §2.3: video latent patches are projected and action tokens go through the action
+    projection (one embodiment's Linear, [ARCH] §2.4), and both live in one sequence.
+    x_video [n*Lv, P], x_action [n*La, A].
+    """
+    Lv, La = w.video_tokens, w.action_tokens
+    hv = linear(x_video, g["pe_w"], g["pe_b"])
+    ha = linear(x_action, g["ae_w"], g["ae_b"])
+    rows = []
+    for c in range(n_chunks):
+        rows.append(hv[c * Lv:(c + 1) * Lv])
+        rows.append(ha[c * La:(c + 1) * La])
+    return np.concatenate(rows, axis=0)
+
+
+def token_layout(w, n_chunks: int) -> Tuple[Array, Array, Array]:
+    """(chunk index, group 0=video/1=action, index within the group of the chunk) per token."""
+    Lv, La = w.video_tokens, w.action_tokens
+    chunk, group, local = [], [], []
+    for c in range(n_chunks):
+        chunk += [c] * (Lv + La)
+        group += [0] * Lv + [1] * La
+        local += list(range(Lv)) + list(range(La))
+    return np.array(chunk), np.array(group), np.array(local)
+
+
+@dataclass
+class KVCache:
+    """Per layer, per branch: keys (after RMSNorm and RoPE) and values of clean chunks.
+
+    [WS1] architecture: the DiT runner maintains the attention KV; [HYPER] 方法: after a chunk
+    executes, its entries are replaced by the encoding of the real observation.
+    k[l], v[l]: [br, len, D].
+    """
+    k: List[Array] = field(default_factory=list)
+    v: List[Array] = field(default_factory=list)
+
+    @property
+    def length(self) -> int:
+        return 0 if not self.k else self.k[0].shape[1]
+
+    @staticmethod
+    def empty(layers: int, br: int, dim: int, dt=np.float32) -> "KVCache":
+        z = np.zeros((br, 0, dim), dtype=dt)
+        return KVCache([z.copy() for _ in range(layers)], [z.copy() for _ in range(layers)])
+
+
+def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, ctx_v: Array,
+                  cache_k: Array, cache_v: Array, n_chunks: int, pos: Array) -> Tuple[Array, Array, Array]:
+    """One causal DiT block on all CFG branches.
+
+    h [br, T, D] (T = n_chunks * Lq), mods [T, 6, D] = per-token time modulation (e6 of the token's
+    chunk and group; the layer offset is added here), ctx_k/ctx_v [br, Lc, D], cache_k/cache_v
+    [br, len, D] (clean chunks before these), pos [n*Lv, 3] video positions.
+    Returns (h_out, k_new, v_new) where k_new/v_new [br, T, D] are this call's keys/values.
+
+    Order ([ARCH] §2.3 single block): norm -> modulation -> causal self-attention -> residual ->
+    norm -> cross-attention -> residual -> norm -> FFN -> residual. Readings: R3 (gates on the
+    self-attention and FFN residuals only; (1 + scale)), R5 (LayerNorm), R6 (GELU-tanh FFN),
+    R7 (chunk-level mask, bidirectional inside a chunk), R9 (RoPE), R11 (cross q/k RMSNorm).
+    """
+    br, T, D = h.shape
+    H, d = w.heads, w.head_dim
+    dt = h.dtype
+    m = mods + lp["mod"][None, :, :]                              # [T, 6, D]
+    shift1, scale1, gate1, shift2, scale2, gate2 = (m[:, i, :] for i in range(6))
+    chunk, group, _ = token_layout(w, n_chunks)
+    is_video = group == 0
+    L0 = cache_k.shape[1]
+    # key j is visible to query i if it is cached (a clean earlier chunk) or its chunk <= i's chunk
+    key_chunk = np.concatenate([np.full(L0, -1), chunk])
+    visible = key_chunk[None, :] <= chunk[:, None]
+    oc_all = np.empty_like(h)
+    k_new = np.empty_like(h)
+    v_new = np.empty_like(h)
+    # --- self-attention sub-layer
+    o_all = np.empty_like(h)
+    for b in range(br):
+        y = modulated_norm(h[b], shift1, scale1, w.eps)
+        qkv = linear(y, lp["w_qkv"], lp["b_qkv"])
+        q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
+        q = rms_norm(q, w.eps, lp["g_q"]).reshape(T, H, d)
+        k = rms_norm(k, w.eps, lp["g_k"]).reshape(T, H, d)
+        q[is_video] = apply_rope(q[is_video], pos, d, w.rope_theta)
+        k[is_video] = apply_rope(k[is_video], pos, d, w.rope_theta)
+        k_new[b] = k.reshape(T, D)
+        v_new[b] = v
+        kk = np.concatenate([cache_k[b], k_new[b]], axis=0).reshape(-1, H, d).transpose(1, 0, 2)
+        vv = np.concatenate([cache_v[b], v_new[b]], axis=0).reshape(-1, H, d).transpose(1, 0, 2)
+        o = attention(q.transpose(1, 0, 2), kk, vv, visible)      # [H, T, d]
+        o_all[b] = o.transpose(1, 0, 2).reshape(T, D)
+    h = h + gate1[None] * linear(o_all, lp["w_o"], lp["b_o"])
+    # --- cross-attention sub-layer (no mask, no RoPE, no modulation)
+    for b in range(br):
+        n3 = layer_norm(h[b], w.eps, lp["ln3_w"], lp["ln3_b"])
+        qc = rms_norm(linear(n3, lp["w_cq"], lp["b_cq"]), w.eps, lp["g_cq"]).reshape(T, H, d)
+        kc = ctx_k[b].reshape(-1, H, d).transpose(1, 0, 2)
+        vc = ctx_v[b].reshape(-1, H, d).transpose(1, 0, 2)
+        oc = attention(qc.transpose(1, 0, 2), kc, vc, None).transpose(1, 0, 2).reshape(T, D)
+        oc_all[b] = oc
+    h = h + linear(oc_all, lp["w_co"], lp["b_co"])
+    # --- feed-forward sub-layer
+    y2 = modulated_norm(h, shift2[None], scale2[None], w.eps)
+    f = linear(gelu_tanh(linear(y2, lp["w_ff1"], lp["b_ff1"])), lp["w_ff2"], lp["b_ff2"])
+    h = h + gate2[None] * f
+    return h, k_new, v_new
+
+
+def per_token_time(w, g: Dict[str, Array], t_video: Sequence[float], t_action: Sequence[float],
+                   n_chunks: int, dt) -> Tuple[Array, Array]:
+    """Per-token e6 [T, 6, D] and e [T, D]: the token's chunk picks its timesteps and its group
+    (video/action) picks t_video or t_action ([N569] DreamZero-Flash: decoupled video and action
+    noise levels; with equal values this is the shared timestep of the standard model)."""
+    chunk, group, _ = token_layout(w, n_chunks)
+    table_e6, table_e = {}, {}
+    for c in range(n_chunks):
+        for gi, t in ((0, t_video[c]), (1, t_action[c])):
+            table_e[(c, gi)], table_e6[(c, gi)] = time_modulation(t, g, w.freq_dim, dt)
+    e6 = np.stack([table_e6[(c, gi)] for c, gi in zip(chunk, group)])
+    e = np.stack([table_e[(c, gi)] for c, gi in zip(chunk, group)])
+    return e6, e
+
+
+def head_forward(w, g: Dict[str, Array], h: Array, e: Array, n_chunks: int) -> Tuple[Array, Array]:
+    """Output split ([ARCH] §2.3 output decoding, §2.4 per-embodiment decoder):
+    n = LN(h)(1 + scale_h) + shift_h with (shift_h, scale_h) = head_mod + e;
+    v_video = n_video W_vo^T + b, v_action = n_action W_ao^T + b."""
+    shift = g["head_mod"][0][None] + e
+    scale = g["head_mod"][1][None] + e
+    n = modulated_norm(h, shift[None], scale[None], w.eps)
+    _, group, _ = token_layout(w, n_chunks)
+    vv = linear(n[:, group == 0], g["vo_w"], g["vo_b"])
+    va = linear(n[:, group == 1], g["ao_w"], g["ao_b"])
+    return vv, va
+
+
+@dataclass
+class Model:
+    """Weights of the stack as float arrays: ``g`` global, ``layers[l]`` per layer."""
+    w: object
+    g: Dict[str, Array]
+    layers: List[Dict[str, Array]]
+
+
+def stack_forward(model: Model, cache: KVCache, ctx_kv: List[Tuple[Array, Array]],
+                  x_video: Array, x_action: Array, t_video: Sequence[float], t_action: Sequence[float],
+                  n_chunks: int, start_frame: int, dt=np.float32, commit: bool = False,
+                  layer_fn=None) -> Tuple[Array, Array]:
+    """One pass of the DiT over ``n_chunks`` chunks on all CFG branches.
+
+    x_video [n*Lv, P], x_action [n*La, A] (the same noisy latents for every branch);
+    returns per-branch velocities (v_video [br, n*Lv, P], v_action [br, n*La, A]).
+    With n_chunks = 1 and a cache of clean chunks this is the incremental step; with n_chunks > 1
+    it is the full-sequence pass under the chunk-causal mask ([HYPER] 方法, teacher forcing).
+    commit=True appends this call's keys/values to ``cache`` ([N569] inference: KV cache with
+    real observations).
+    """
+    w = model.w
+    g = model.g
+    br = w.branches
+    e6, e = per_token_time(w, g, t_video, t_action, n_chunks, dt)
+    h0 = embed_tokens(g, x_video.astype(dt), x_action.astype(dt), w, n_chunks)
+    h = np.broadcast_to(h0[None], (br,) + h0.shape).astype(dt).copy()
+    pos = video_positions(w, n_chunks, start_frame)
+    new_k, new_v = [], []
+    for l, lp in enumerate(model.layers):
+        ck, cv = ctx_kv[l]
+        if cache.k:
+            kc, vc = cache.k[l].astype(dt), cache.v[l].astype(dt)
+        else:
+            kc = vc = np.zeros((br, 0, w.dim), dtype=dt)
+        h, kn, vn = (layer_fn or block_forward)(w, lp, h, e6, ck, cv, kc, vc, n_chunks, pos)
+        new_k.append(kn)
+        new_v.append(vn)
+    if commit:
+        for l in range(len(model.layers)):
+            cache.k[l] = np.concatenate([cache.k[l].astype(dt), new_k[l]], axis=1)
+            cache.v[l] = np.concatenate([cache.v[l].astype(dt), new_v[l]], axis=1)
+    return head_forward(w, g, h, e, n_chunks)
+
+
+def kv_append(model: Model, cache: KVCache, ctx_kv, x_video: Array, x_action: Array,
+              start_frame: int, dt=np.float32) -> None:
+    """Commit one clean chunk: a stack pass at t_video = t_action = 1 whose keys/values are
+    appended (reading R17: cached chunks are clean, t = 1). [HYPER] 方法: predicted frames in the
+    KV cache are replaced by real observations after the chunk executes."""
+    stack_forward(model, cache, ctx_kv, x_video, x_action, [1.0], [1.0], 1, start_frame, dt, commit=True)
+
+
+# ----------------------------------------------------------------------------------------------
+# Guidance, Euler update, velocity reuse ([N569] real-time optimisations; BASELINE Euler reading)
+# ----------------------------------------------------------------------------------------------
+
+def cfg_combine(v_branches: Array, guidance: float) -> Array:
+    """Classifier-free guidance: v = v_uncond + w (v_cond - v_uncond); branch 0 is conditional,
+    branch 1 the negative/null prompt ([N569]: the conditional and unconditional passes; [WS1]
+    request format: negative prompt). Reading R13: w applies to video and action alike; the sum
+    is evaluated as w v_cond + (1 - w) v_uncond, which is the same quantity and returns either
+    branch exactly at w = 1 or w = 0."""
+    v0, v1 = v_branches[0], v_branches[1]
+    wc = v_branches.dtype.type(guidance)
+    wu = v_branches.dtype.type(1.0 - guidance)
+    return wc * v0 + wu * v1
+
+
+def euler_update(x: Array, v: Array, t: float, t_next: float) -> Array:
+    """x <- x + (t_next - t) v (reading R14: Euler on the flow-matching ODE)."""
+    return x + x.dtype.type(t_next - t) * v
+
+
+def interpolate(x1: Array, eps: Array, t: float) -> Array:
+    """x_t = t x1 + (1 - t) eps (reading R1 of the pages' linear interpolation)."""
+    return x1.dtype.type(t) * x1 + x1.dtype.type(1.0 - t) * eps
+
+
+def cosine_fp64(a: Array, b: Array) -> float:
+    """Cosine similarity of two flattened tensors, accumulated in float64."""
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    return float(a @ b / math.sqrt((a @ a) * (b @ b)))
+
+
+def denoise_chunk(dit, x_video: Array, x_action: Array, grid: Sequence[float], tau: float,
+                  max_consecutive_reuse: Optional[int] = None):
+    """Euler loop with velocity reuse ([N569] DiT caching; [WS1] dynamic16).
+
+    dit(x_video, x_action, t) -> guided (v_video, v_action). Steps 0 and 1 always run the DiT;
+    at step k >= 2, if the cosine similarity of the two most recent DiT-computed guided video
+    velocities exceeds tau, the DiT is skipped and the latest computed velocity is reused
+    (reading R15). Returns (x_video, x_action, number of DiT calls, per-step flags).
+    """
+    computed: List[Tuple[Array, Array]] = []
+    calls = 0
+    consecutive = 0
+    flags = []
+    xv, xa = x_video.copy(), x_action.copy()
+    for k in range(len(grid) - 1):
+        t, tn = grid[k], grid[k + 1]
+        reuse = False
+        if k >= 2 and len(computed) >= 2:
+            c = cosine_fp64(computed[-1][0], computed[-2][0])
+            if c > tau and (max_consecutive_reuse is None or consecutive < max_consecutive_reuse):
+                reuse = True
+        if reuse:
+            vv, va = computed[-1]
+            consecutive += 1
+        else:
+            vv, va = dit(xv, xa, t)
+            computed.append((vv, va))
+            calls += 1
+            consecutive = 0
+        flags.append(reuse)
+        xv = euler_update(xv, vv, t, tn)
+        xa = euler_update(xa, va, t, tn)
+    return xv, xa, calls, flags
+
+
+# ----------------------------------------------------------------------------------------------
+# Loading the synthetic weights as float arrays
+# ----------------------------------------------------------------------------------------------
+
+def load_model(w, dt=np.float32, layers: Optional[Sequence[int]] = None) -> Model:
+    """Draw the workload's weights (bf16-representable values) from ``synth`` as ``dt`` arrays."""
+    import synth
+    from synth.workloads import draw, global_tensors, layer_tensors
+    g = {s[0]: draw(w, -1, s, "f32").astype(dt) for s in global_tensors(w)}
+    ls = range(w.layers) if layers is None else layers
+    lay = [{s[0]: draw(w, l, s, "f32").astype(dt) for s in layer_tensors(w)} for l in ls]
+    return Model(w, g, lay)

@@ -1,0 +1,200 @@
+"""Model-level pins of the oracle on the tiny workload (width 256, 4 heads of 64, 2 frames of 8x8
+patches + 24 action tokens, 32 text tokens), against invariants the pages fix:
+
+* incremental chunk-by-chunk decoding with the KV cache equals one full-sequence pass under the
+  chunk-causal mask (max abs diff <= 1e-5 in fp32) -- the noisy chunk sees clean earlier chunks
+  and never future tokens (hyper.ai summary, 方法; paper walk-through, training objective);
+* perturbing future-chunk tokens leaves earlier outputs bit-identical (same passages);
+* shifting every frame position leaves the step unchanged (rotary positions are relative);
+* zero gates remove the self-attention and FFN sub-layers exactly;
+* CFG as a batch of 2 equals two single-branch passes;
+* velocity reuse call counts at the threshold extremes (paper walk-through, DiT caching).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from synth.workloads import WORKLOADS, draw_named
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = WORKLOADS[1].with_(layers=2)
+    m = O.load_model(w)
+    txt = draw_named(w, -1, "txt")
+    ctx = O.build_context(w, m.g, txt, None)
+    ckv = [O.context_kv(w, lp, ctx) for lp in m.layers]
+    x1v = [draw_named(w, -1, "x1_video_%d" % c) for c in range(3)]
+    x1a = [draw_named(w, -1, "x1_action_%d" % c) for c in range(3)]
+    epv = [draw_named(w, -1, "eps_video_%d" % c) for c in range(3)]
+    epa = [draw_named(w, -1, "eps_action_%d" % c) for c in range(3)]
+    return w, m, txt, ckv, x1v, x1a, epv, epa
+
+
+def _full(w, m, ckv, xs_v, xs_a, tv, ta, start=0):
+    e = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    return O.stack_forward(m, e, ckv, np.concatenate(xs_v), np.concatenate(xs_a), tv, ta, len(xs_v), start)
+
+
+def test_incremental_equals_full_sequence(tiny):
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    Lv, La, Fc = w.video_tokens, w.action_tokens, w.frames_per_chunk
+    xv2 = O.interpolate(x1v[2], epv[2], 0.5)
+    xa2 = O.interpolate(x1a[2], epa[2], 0.3)
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    O.kv_append(m, cache, ckv, x1v[1], x1a[1], Fc)
+    assert cache.length == 2 * (Lv + La)
+    vv, va = O.stack_forward(m, cache, ckv, xv2, xa2, [0.5], [0.3], 1, 2 * Fc)
+    fv, fa = _full(w, m, ckv, [x1v[0], x1v[1], xv2], [x1a[0], x1a[1], xa2], [1, 1, 0.5], [1, 1, 0.3])
+    assert np.abs(fv[:, 2 * Lv:] - vv).max() <= 1e-5
+    assert np.abs(fa[:, 2 * La:] - va).max() <= 1e-5
+    # the cache matters: without it the chunk's velocity changes
+    e = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    nv, _ = O.stack_forward(m, e, ckv, xv2, xa2, [0.5], [0.3], 1, 2 * Fc)
+    assert np.abs(nv - vv).max() > 1e-3
+
+
+def test_future_perturbation_bit_identical(tiny):
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    Lv, La = w.video_tokens, w.action_tokens
+    a = _full(w, m, ckv, [x1v[0], epv[1]], [x1a[0], epa[1]], [1, 0.2], [1, 0.2])
+    b = _full(w, m, ckv, [x1v[0], epv[1] * 7 + 3], [x1a[0], -epa[1]], [1, 0.9], [1, 0.6])
+    assert np.array_equal(a[0][:, :Lv], b[0][:, :Lv])
+    assert np.array_equal(a[1][:, :La], b[1][:, :La])
+    assert not np.array_equal(a[0][:, Lv:], b[0][:, Lv:])
+
+
+def test_frame_shift_invariance_without_action_tokens(tiny):
+    # Rotary scores depend only on position differences, so with video tokens alone a common shift of
+    # every frame index leaves the step unchanged up to rounding. Action tokens are not rotated, so a
+    # video-action score depends on the absolute frame index and the invariance stops holding once
+    # they are present (checked below as well).
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    w0 = w.with_(action_tokens=0)
+    m0 = O.Model(w0, m.g, m.layers)
+    Fc = w.frames_per_chunk
+    outs = []
+    for start in (0, 5):
+        cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+        O.kv_append(m0, cache, ckv, x1v[0], x1a[0][:0], start)
+        outs.append(O.stack_forward(m0, cache, ckv, epv[1], epa[1][:0], [0.3], [0.3], 1, start + Fc))
+    np.testing.assert_allclose(outs[0][0], outs[1][0], atol=2e-5)
+    outs = []
+    for start in (0, 5):
+        cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+        O.kv_append(m, cache, ckv, x1v[0], x1a[0], start)
+        outs.append(O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.3], [0.3], 1, start + Fc))
+    assert np.abs(outs[0][0] - outs[1][0]).max() > 1e-4
+
+
+def test_frames_are_positions_not_order(tiny):
+    # Placing the same chunk at a different frame offset relative to the cache changes the output
+    # (the rotary positions are used at all), so the invariance above is not vacuous.
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    a = O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.0], [0.0], 1, 2)
+    b = O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.0], [0.0], 1, 9)
+    assert np.abs(a[0] - b[0]).max() > 1e-4
+
+
+def test_zero_gates_remove_self_attention_and_ffn(tiny):
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    g = dict(m.g)
+    g["t_wp"] = np.zeros_like(g["t_wp"])
+    g["t_bp"] = np.zeros_like(g["t_bp"])
+    layers = []
+    for lp in m.layers:
+        lp = dict(lp)
+        mod = lp["mod"].copy()
+        mod[2] = 0.0
+        mod[5] = 0.0
+        lp["mod"] = mod
+        layers.append(lp)
+    m0 = O.Model(w, g, layers)
+    # with both gates zero the output cannot depend on the self-attention or FFN weights
+    layers2 = []
+    for lp in layers:
+        lp = dict(lp)
+        for k in ("w_qkv", "w_o", "w_ff1", "w_ff2", "b_o", "b_ff2"):
+            lp[k] = lp[k] * 3.0 + 0.1
+        layers2.append(lp)
+    m1 = O.Model(w, g, layers2)
+    e = O.KVCache.empty(len(layers), w.branches, w.dim)
+    a = O.stack_forward(m0, e, ckv, epv[1], epa[1], [0.4], [0.4], 1, 0)
+    b = O.stack_forward(m1, e, ckv, epv[1], epa[1], [0.4], [0.4], 1, 0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_cfg_batch_equals_single_branch_runs(tiny):
+    w, m, txt, _, x1v, x1a, epv, epa = tiny
+    full_ctx = O.build_context(w, m.g, txt, None)
+    ckv2 = [O.context_kv(w, lp, full_ctx) for lp in m.layers]
+    e = O.KVCache.empty(len(m.layers), 2, w.dim)
+    both = O.stack_forward(m, e, ckv2, epv[0], epa[0], [0.3], [0.3], 1, 0)
+    w1 = w.with_(branches=1)
+    m1 = O.Model(w1, m.g, m.layers)
+    for b in range(2):
+        ctx_b = O.build_context(w1, m.g, txt[b:b + 1], None)
+        ckv1 = [O.context_kv(w1, lp, ctx_b) for lp in m.layers]
+        e1 = O.KVCache.empty(len(m.layers), 1, w.dim)
+        one = O.stack_forward(m1, e1, ckv1, epv[0], epa[0], [0.3], [0.3], 1, 0)
+        np.testing.assert_allclose(one[0][0], both[0][b], atol=1e-6)
+        np.testing.assert_allclose(one[1][0], both[1][b], atol=1e-6)
+    # the two branches do differ (different text features)
+    assert np.abs(both[0][0] - both[0][1]).max() > 1e-4
+
+
+def _dit_counter(w, m, ckv, cache, start):
+    calls = []
+
+    def dit(xv, xa, t):
+        vb, ab = O.stack_forward(m, cache, ckv, xv, xa, [t], [t], 1, start)
+        out = (O.cfg_combine(vb, w.guidance), O.cfg_combine(ab, w.guidance))
+        calls.append((t, out))
+        return out
+    return dit, calls
+
+
+def test_velocity_reuse_extremes(tiny):
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    grid = [k / 16 for k in range(17)]
+    dit, calls = _dit_counter(w, m, ckv, cache, w.frames_per_chunk)
+    _, _, n_a, flags_a = O.denoise_chunk(dit, epv[1], epa[1], grid, tau=1.5)
+    assert n_a == 16 and len(calls) == 16 and not any(flags_a)
+    dit, calls = _dit_counter(w, m, ckv, cache, w.frames_per_chunk)
+    xv_b, xa_b, n_b, flags_b = O.denoise_chunk(dit, epv[1], epa[1], grid, tau=-1.5)
+    assert n_b == 2 and len(calls) == 2 and flags_b == [False, False] + [True] * 14
+    # after step 1 every update reuses v_1: x_16 = x_0 + v_0/16 + 15 v_1/16 for both modalities
+    (_, (v0v, v0a)), (_, (v1v, v1a)) = calls
+    np.testing.assert_allclose(xv_b, epv[1] + v0v / 16 + 15 * v1v / 16, atol=1e-5)
+    np.testing.assert_allclose(xa_b, epa[1] + v0a / 16 + 15 * v1a / 16, atol=1e-5)
+    # max_consecutive_reuse=1 alternates compute/reuse after step 1
+    dit, calls = _dit_counter(w, m, ckv, cache, w.frames_per_chunk)
+    _, _, n_c, flags_c = O.denoise_chunk(dit, epv[1], epa[1], grid, tau=-1.5, max_consecutive_reuse=1)
+    assert flags_c == [False, False] + [True, False] * 7 and n_c == 9
+
+
+def test_workload_shapes_match_pages():
+    # Hyper-parameters printed on the pages (tests/golden/pages_hyperparams.txt, with citations).
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "pages_hyperparams.txt")
+    vals = {}
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            k, v = line.split("=")
+            vals[k.strip()] = int(v)
+    w = WORKLOADS[3]
+    assert w.layers == vals["layers"] and w.dim == vals["dim"] and w.heads == vals["heads"]
+    assert w.head_dim == vals["head_dim"] and w.ffn_dim == vals["ffn_dim"]
+    assert w.ctx_in_dim == vals["encoder_dim"] and w.action_tokens == vals["action_horizon"]
+    assert w.ctx_text_len == vals["text_len"] and w.patch_dim == vals["latent_channels"] * 4
+    assert w.action_dim == vals["droid_action_dim"]
+    # 320x176 frames, 8x spatial VAE compression, 2x2 patches -> 20 x 11 patch grid
+    assert (vals["frame_w"] // vals["vae_spatial"] // 2, vals["frame_h"] // vals["vae_spatial"] // 2) == (w.grid_w, w.grid_h)
+    assert synth.BASE_SEED == vals["seed"]
