@@ -1,0 +1,212 @@
+/*
+ * wam.h -- C ABI of the MI355X (gfx950) library computing one flow-matching denoising step of
+ * DreamZero's chunk-causal joint video+action DiT ("World Action Model").
+ *
+ * Sources (page titles; sections):
+ *   [ARCH]  "DreamZero (WAM) 模型架构": §2.1 encoders, §2.3 Causal WAN DiT (input sequence,
+ *           single causal block, output split, causal mask), §2.4 per-embodiment action linears,
+ *           §3 flow-matching interpolation, §4 inference (encode once, denoise loop).
+ *   [WS1]   "DreamZero 单卡推理" (PhyAI ws1): architecture table (DiT runner keeps the attention
+ *           KV; scheduler owns reference KV, CFG branches, DiT calls, the update), request format
+ *           (negative prompt, 512 text tokens), continuous requests (frame position, KV reset),
+ *           Fixed4 vs dynamic16.
+ *   [HYPER] hyper.ai summary of arXiv 2602.15922, 方法: chunked AR generation, mask (noisy chunk
+ *           sees clean earlier chunks, never future tokens), KV replaced by real observations.
+ *   [N569]  walk-through "World Action Models are Zero-shot Policies": inference with KV cache,
+ *           CFG passes, DiT caching by cosine similarity of successive velocities, Flash schedule.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are caller-owned DEVICE buffers (one GPU), dense and contiguous, 16-byte aligned
+ *     (256-byte recommended). Structs are host memory. The library never allocates or frees device
+ *     memory and never synchronises: work is enqueued on `stream` (a hipStream_t; NULL = default).
+ *   - Matrices (Linear weights, stored [out][in]) and activations/caches use the element type of
+ *     wam_config.dtype: WAM_BF16 = bfloat16 bit patterns, WAM_F32 = IEEE float (debug mode).
+ *     Vectors (biases, norm gains, modulation tables) and the latents/velocities are always float.
+ *   - Arguments are validated on the host before anything is enqueued: a non-zero status means
+ *     nothing was launched. WAM_E_HIP reports a launch failure (text in wam_last_error()); a
+ *     device fault surfaces at the caller's next synchronisation.
+ *   - Calls on different streams need distinct workspaces; the caches they write must not overlap.
+ *
+ * Time convention: t in [0,1], t = 0 pure noise, t = 1 clean; x_t = t x1 + (1-t) eps; the model
+ * predicts the velocity x1 - eps; one Euler step is x += (t_next - t) v.
+ */
+#ifndef WAM_H_
+#define WAM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WAM_OK = 0,
+  WAM_E_ARG = -1,         /* null pointer or out-of-range scalar */
+  WAM_E_SHAPE = -2,       /* sizes inconsistent or unsupported (e.g. head_dim not 64/128) */
+  WAM_E_CAPACITY = -3,    /* KV cache too small for the rows to be written */
+  WAM_E_HIP = -4,         /* a HIP launch failed */
+  WAM_E_UNSUPPORTED = -5
+} wam_status;
+
+typedef enum { WAM_BF16 = 0, WAM_F32 = 1 } wam_dtype;
+
+/* Model and chunk geometry. [ARCH] §5 table: 40 layers, width 5120, 40 heads of 128; §2.3: FFN
+ * 5120->13824; 1536-d encoder features; 24-step action horizon. Chunk = frames_per_chunk latent
+ * frames of grid_h x grid_w patch tokens (raster order), then action_tokens action tokens. */
+typedef struct {
+  int dim, heads, head_dim, ffn_dim, layers, freq_dim;
+  int patch_dim, action_dim, action_tokens;
+  int frames_per_chunk, grid_h, grid_w;
+  int ctx_in_dim, ctx_text_len, ctx_img_len;
+  int branches;            /* 1, or 2 = CFG batch (branch 0 conditional, branch 1 negative prompt) */
+  float rope_theta, eps;   /* 10000, 1e-6 */
+  wam_dtype dtype;
+} wam_config;
+
+/* One block's parameters ([ARCH] §2.3 single causal block). Matrices [out][in] in dtype;
+ * everything else float. mod: [6][D] per-layer offset added to the shared time modulation
+ * (shift1, scale1, gate1, shift2, scale2, gate2). */
+typedef struct {
+  const void *mod;
+  const void *w_qkv, *b_qkv;   /* [3D][D], [3D]  rows: q | k | v */
+  const void *g_q, *g_k;       /* [D] RMSNorm gains of q and k */
+  const void *w_o, *b_o;       /* [D][D], [D] */
+  const void *ln3_w, *ln3_b;   /* [D] affine LayerNorm before cross-attention */
+  const void *w_cq, *b_cq, *g_cq;
+  const void *w_ck, *b_ck, *g_ck;
+  const void *w_cv, *b_cv;
+  const void *w_co, *b_co;
+  const void *w_ff1, *b_ff1;   /* [F][D], [F] */
+  const void *w_ff2, *b_ff2;   /* [D][F], [D] */
+} wam_block_weights;
+
+typedef struct {
+  const wam_block_weights *blocks;           /* host array [layers] */
+  const void *t_w1, *t_b1, *t_w2, *t_b2;     /* time MLP: [D][freq_dim], [D]; [D][D], [D] */
+  const void *t_wp, *t_bp;                   /* shared modulation projection [6D][D], [6D] */
+  const void *pe_w, *pe_b;                   /* patch embedding [D][patch_dim], [D] */
+  const void *ae_w, *ae_b;                   /* action embedding [D][action_dim], [D] */
+  const void *head_mod;                      /* [2][D] output-head shift/scale offsets */
+  const void *vo_w, *vo_b;                   /* video head [patch_dim][D], [patch_dim] */
+  const void *ao_w, *ao_b;                   /* action head [action_dim][D], [action_dim] */
+  const void *txt_w, *txt_b;                 /* text features -> width [D][ctx_in_dim], [D] */
+  const void *img_w, *img_b;                 /* image features -> width (NULL when ctx_img_len = 0) */
+} wam_weights;
+
+/* Self-attention KV cache of clean chunks ([WS1] architecture: the DiT runner keeps the KV;
+ * [HYPER] 方法: executed chunks are replaced by real observations). Keys after RMSNorm and RoPE.
+ *   k: [layers][branches][heads][capacity][head_dim]
+ *   v: [layers][branches][heads][head_dim][capacity]   (value rows stored key-contiguous)
+ * `length` rows are committed. A forward pass writes its own keys/values into rows
+ * [length, length + n_chunks*Lq) as scratch; committed rows are never modified except by
+ * wam_kv_append, which fills exactly those rows and then advances `length`.
+ * capacity must be a multiple of 64, length a multiple of 8. */
+typedef struct {
+  void *k, *v;
+  int branches, capacity, length;
+} wam_kv_cache;
+
+/* Cross-attention keys/values of the condition sequence, built once per request ([ARCH] §4:
+ * conditions are encoded once and cached).
+ *   k: [layers][branches][heads][ctx_len][head_dim]      (after RMSNorm)
+ *   v: [layers][branches][heads][head_dim][ctx_stride]   (ctx_stride multiple of 64, >= ctx_len) */
+typedef struct {
+  void *k, *v;
+  int branches, ctx_len, ctx_stride;
+} wam_ctx_kv;
+
+/* Bytes of device workspace needed by any call with up to `n_chunks` chunks in one pass
+ * (1 for an incremental step or an append; >1 for a full-sequence pass). */
+size_t wam_workspace_bytes(const wam_config *cfg, int n_chunks);
+
+/* Condition build ([ARCH] §2.1: text and image features concatenated into one condition
+ * sequence; §4: encoded once). ctx_b = [txt_b W_txt^T + b ; img W_img^T + b] per branch, then per
+ * layer Kc = RMSNorm(ctx Wck^T + b) g_ck and Vc = ctx Wcv^T + b into `out`.
+ *   txt: [branches][ctx_text_len][ctx_in_dim] dtype (branch 1 = negative prompt features)
+ *   img: [ctx_img_len][ctx_in_dim] dtype, shared by the branches (NULL when ctx_img_len = 0) */
+wam_status wam_ctx_build(const wam_config *cfg, const wam_weights *w, const void *txt, const void *img,
+                         wam_ctx_kv *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Shared time modulation for `n` timesteps t[0..n) (host floats, n <= 16): e [n][D] and
+ * e6 [n][6][D] (device float). [ARCH] §2.3: sinusoidal time embedding; the modulation's shift and
+ * scale come from it. Embedded scalar s = 1000 (1 - t). */
+wam_status wam_time_embed(const wam_config *cfg, const wam_weights *w, const float *t, int n, float *e,
+                          float *e6, void *ws, size_t ws_bytes, void *stream);
+
+/* One pass of the DiT stack over `n_chunks` chunks for all branches ([WS1]: the DiT runner predicts
+ * the video and action outputs and maintains the attention KV).
+ *   x_video:  [n_chunks * Lv][patch_dim] float, x_action: [n_chunks * La][action_dim] float
+ *             (the same noisy latents feed every branch)
+ *   t_video, t_action: HOST arrays [n_chunks] (per-group timesteps; equal values = shared t)
+ *   start_frame: frame index of the first frame of chunk 0 within the attention window
+ *   v_video: [branches][n_chunks * Lv][patch_dim] float, v_action: [branches][n_chunks*La][action_dim]
+ * n_chunks = 1 is the incremental step: the chunk attends to all committed cache rows and to
+ * itself. n_chunks > 1 is the full-sequence pass under the chunk-causal mask ([HYPER] 方法): chunk c
+ * attends to the committed rows and to chunks 0..c. Writes cache rows [length, length+n*Lq).
+ * Requires length + n_chunks*Lq <= capacity (else WAM_E_CAPACITY). */
+wam_status wam_dit_stack_fwd(const wam_config *cfg, const wam_weights *w, wam_kv_cache *cache,
+                             const wam_ctx_kv *ctx, int n_chunks, const float *x_video, const float *x_action,
+                             const float *t_video, const float *t_action, int start_frame, float *v_video,
+                             float *v_action, void *ws, size_t ws_bytes, void *stream);
+
+/* Commit one clean chunk ([HYPER] 方法: the executed chunk's predicted frames are replaced in the
+ * KV cache by the real observation): a stack pass at t = 1 whose keys/values are written into rows
+ * [length, length+Lq) of every layer; then cache->length += Lq (host bookkeeping, done only when
+ * everything was enqueued). x_video [Lv][patch_dim], x_action [La][action_dim] float. */
+wam_status wam_kv_append(const wam_config *cfg, const wam_weights *w, wam_kv_cache *cache, const wam_ctx_kv *ctx,
+                         const float *x_video, const float *x_action, int start_frame, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* One causal DiT block ([ARCH] §2.3: norm -> modulation -> causal self-attention -> residual ->
+ * norm -> cross-attention -> residual -> norm -> FFN -> residual) on the residual stream
+ *   h:  [branches][n_chunks * Lq][D] float, updated in place
+ *   e6: [n_chunks][2][6][D] float (device): shared time modulation per chunk and token group
+ *       (0 = video, 1 = action), e.g. from wam_time_embed with t = {t_v0, t_a0, t_v1, ...}
+ * `layer` selects the layer's slices of the caches; keys/values go to rows [length, length+n*Lq). */
+wam_status wam_dit_block_fwd(const wam_config *cfg, const wam_block_weights *bw, int layer, wam_kv_cache *cache,
+                             const wam_ctx_kv *ctx, float *h, const float *e6, int n_chunks, int start_frame,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Guidance + Euler + similarity ([N569]: conditional/unconditional passes combined; DiT caching
+ * by the cosine similarity of successive velocities).
+ *   v_video [branches][n_video], v_action [branches][n_action]: per-branch velocities
+ *   guided g = guidance * v_cond + (1 - guidance) * v_uncond (branches = 2) or v (branches = 1)
+ *   x_video += dt_video * g_video; x_action += dt_action * g_action
+ *   g_video / g_action (optional, may be NULL): the guided velocities; g_video may alias prev_video
+ *   prev_video (optional): if given, cos_parts[0..3) = (<g,prev>, |g|^2, |prev|^2) over the video
+ *   part, fp32 partial sums in a fixed order (deterministic). cos_parts is device memory.
+ * Needs wam_workspace_bytes(cfg, 1) of workspace (only a few hundred bytes are used). */
+wam_status wam_flow_step(float *x_video, float *x_action, const float *v_video, const float *v_action, int branches,
+                         float guidance, int n_video, int n_action, float dt_video, float dt_action,
+                         float *g_video, float *g_action, const float *prev_video, float *cos_parts, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* Kernel-level calls, exposed so each kernel can be verified on its own (same kernels as above).
+ *
+ * Linear layer ([ARCH] §2.3: every projection of the block): C[m][n] = act(sum_k A[m][k] W[n][k] +
+ * bias[n]) with A [M][lda], W [N][ldw], C [M][ldc] in `dtype`; bias float [N] or NULL; act 0 = none,
+ * 1 = GELU (tanh approximation, the FFN's activation). K must be a multiple of 64. */
+wam_status wam_op_linear(wam_dtype dtype, const void *A, int lda, const void *W, int ldw, const float *bias, void *C,
+                         int ldc, int M, int N, int K, int act, void *stream);
+
+/* Attention ([ARCH] §2.3 causal self-attention and cross-attention; [HYPER] 方法 mask):
+ * for branch b, head h, query q < Lq: softmax over keys j < limit(q) of (Q.K_j) / sqrt(head_dim), times V,
+ * limit(q) = kv_total, or min(kv_total, kv_base + (q / chunk_q + 1) * chunk_q) when chunk_q > 0.
+ *   Q  [br][H][Lq][d], K [br][H][k_rows][d] (k_rows >= kv_total), Vt [br][H][d][v_stride]
+ *   (v_stride multiple of 8, >= kv_total), O [br*Lq][H*d]; all in dtype; d = 64 or 128. */
+wam_status wam_op_attention(wam_dtype dtype, const void *Q, const void *K, const void *Vt, void *O, int br, int heads,
+                            int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,
+                            void *stream);
+
+/* Host-side: forget every committed row ([WS1] continuous requests: at a window boundary the
+ * old KV is released and the frame position restarts). No device work. */
+void wam_kv_reset(wam_kv_cache *cache);
+
+/* Text of the last non-OK status returned on this thread (empty string if none). */
+const char *wam_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WAM_H_ */

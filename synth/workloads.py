@@ -132,9 +132,16 @@ def input_tensors(w: Workload, n_chunks: int):
     return out
 
 
+MATRIX_NAMES = frozenset({
+    "t_w1", "t_w2", "t_wp", "pe_w", "ae_w", "txt_w", "img_w", "vo_w", "ao_w",
+    "w_qkv", "w_o", "w_cq", "w_ck", "w_cv", "w_co", "w_ff1", "w_ff2",
+})
+
+
 def is_matrix(name: str) -> bool:
-    """Linear weights (2-D, [out, in]) are the tensors a bf16 path stores in bf16."""
-    return name.endswith("_w") or name.startswith("w_") or name in ("t_w1", "t_w2", "t_wp")
+    """Linear weights ([out, in]) are the tensors a bf16 path stores in bf16; every other tensor
+    (biases, gains, LayerNorm affine vectors, modulation tables) stays float32."""
+    return name in MATRIX_NAMES
 
 
 def draw(w: Workload, layer: int, spec, fmt: str = "f32"):

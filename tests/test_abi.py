@@ -1,0 +1,118 @@
+"""The C-ABI library: it loads, exports every function ``include/wam.h`` declares, and rejects bad
+arguments on the host before anything is enqueued (no GPU needed: validation makes no HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import world_action_video_amd as wam
+from synth.workloads import WORKLOADS
+from world_action_video_amd.build import OUT
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(OUT):
+        from world_action_video_amd.build import build
+        build()
+    return wam.load()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "wam.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:wam_status|size_t|void|const char \*)\s*\*?\s*(wam_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(wam.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _cfg(wid=1, dtype="bf16"):
+    from world_action_video_amd.device import make_config
+    return make_config(WORKLOADS[wid], dtype)
+
+
+def test_workspace_bytes_host_only():
+    _lib()
+    c1 = _cfg(1)
+    b1 = wam.wam_workspace_bytes(c1, 1)
+    b2 = wam.wam_workspace_bytes(c1, 2)
+    assert 0 < b1 < b2
+    assert wam.wam_workspace_bytes(c1, 0) == 0 and wam.wam_workspace_bytes(c1, 9) == 0
+    c3 = _cfg(3)
+    M = 2 * 464
+    assert wam.wam_workspace_bytes(c3, 1) >= M * 5120 * 4 + M * 13824 * 2
+    bad = _cfg(1)
+    bad.head_dim = 96
+    assert wam.wam_workspace_bytes(bad, 1) == 0
+
+
+def test_validation_rejects_before_launch():
+    lib = _lib()
+    c = _cfg(1)
+    st = lib.wam_dit_stack_fwd(None, None, None, None, 1, None, None, None, None, 0, None, None, None, 0, None)
+    assert st == wam.WAM_E_ARG and "config" in wam.wam_last_error()
+    st = lib.wam_dit_stack_fwd(ctypes.byref(c), None, None, None, 1, None, None, None, None, 0, None, None, None, 0, None)
+    assert st == wam.WAM_E_ARG and "weights" in wam.wam_last_error()
+    bad = _cfg(1)
+    bad.dim = 250
+    st = lib.wam_dit_stack_fwd(ctypes.byref(bad), None, None, None, 1, None, None, None, None, 0, None, None, None, 0,
+                               None)
+    assert st == wam.WAM_E_SHAPE
+    # capacity overflow is reported as such, with nothing launched (all pointers are fake host values)
+    w = wam.wam_weights()
+    blocks = (wam.wam_block_weights * c.layers)()
+    for b in blocks:
+        for f in wam.BLOCK_FIELDS:
+            setattr(b, f, 0x1000)
+    w.blocks = ctypes.cast(blocks, ctypes.POINTER(wam.wam_block_weights))
+    for f in wam.GLOBAL_FIELDS:
+        setattr(w, f, 0x1000)
+    kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 128, 0)
+    cx = wam.wam_ctx_kv(0x1000, 0x1000, 2, 32, 64)
+    st = lib.wam_dit_stack_fwd(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(cx), 1, 0x1000, 0x1000,
+                               None, None, 0, 0x1000, 0x1000, 0x1000, 1 << 30, None)
+    assert st == wam.WAM_E_CAPACITY
+    kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 100, 0)
+    st = lib.wam_kv_append(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(cx), 0x1000, 0x1000, 0,
+                           0x1000, 1 << 30, None)
+    assert st == wam.WAM_E_SHAPE and kv.length == 0
+    cx_bad = wam.wam_ctx_kv(0x1000, 0x1000, 2, 31, 64)
+    kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 512, 0)
+    st = lib.wam_kv_append(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(cx_bad), 0x1000, 0x1000, 0,
+                           0x1000, 1 << 30, None)
+    assert st == wam.WAM_E_SHAPE and kv.length == 0
+    st = lib.wam_kv_append(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(cx), 0x1000, 0x1000, 0,
+                           0x1000, 16, None)
+    assert st == wam.WAM_E_ARG and "workspace" in wam.wam_last_error() and kv.length == 0
+    blocks[c.layers - 1].w_ff2 = None
+    st = lib.wam_kv_append(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(cx), 0x1000, 0x1000, 0,
+                           0x1000, 1 << 30, None)
+    assert st == wam.WAM_E_ARG and "w_ff2" in wam.wam_last_error() and kv.length == 0
+
+
+def test_op_validation():
+    lib = _lib()
+    assert lib.wam_op_linear(0, 0x1000, 64, 0x1000, 64, None, 0x1000, 64, 4, 4, 60, 0, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_linear(0, None, 64, 0x1000, 64, None, 0x1000, 64, 4, 4, 64, 0, None) == wam.WAM_E_ARG
+    assert lib.wam_op_attention(0, 0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 96, 8, 8, 8, 0, 0, 8, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_attention(0, 0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 64, 8, 8, 12, 0, 0, 12, None) == wam.WAM_E_SHAPE
+    assert lib.wam_flow_step(0x1000, 0x1000, 0x1000, 0x1000, 3, 5.0, 4, 4, 0.1, 0.1, None, None, None, None, None, 0,
+                             None) == wam.WAM_E_SHAPE
+    assert lib.wam_flow_step(0x1000, 0x1000, 0x1000, 0x1000, 2, 5.0, 4, 4, 0.1, 0.1, None, None, 0x1000, None, None, 0,
+                             None) == wam.WAM_E_ARG
+
+
+def test_kv_reset_is_host_only():
+    _lib()
+    kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 512, 464)
+    wam.wam_kv_reset(kv)
+    assert kv.length == 0

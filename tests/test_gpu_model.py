@@ -1,0 +1,247 @@
+"""Stack-level parity of the HIP path (through the C ABI) against the CPU oracle, and the GPU-side
+invariants the pages fix. Tolerances (relative L2 per output tensor, video and action apart):
+2e-2 in bf16 and 1e-4 in the fp32 debug mode.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import world_action_video_amd as wam
+from synth.workloads import WORKLOADS, draw_named
+from world_action_video_amd.device import DeviceCache, DeviceCtx, DeviceModel, to_device, workspace
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+class Rig:
+    """GPU model + condition KV for one workload and dtype, plus the host copies of its inputs."""
+
+    def __init__(self, w, dtype, device):
+        self.w, self.dtype, self.dev = w, dtype, device
+        self.m = DeviceModel(w, dtype, device)
+        self.ws = workspace(self.m.cfg, 2, device)
+        self.txt = draw_named(w, -1, "txt")
+        self.img = draw_named(w, -1, "img") if w.ctx_img_len else None
+        self.ctx = DeviceCtx(w, dtype, device)
+        wam.wam_ctx_build(self.m.cfg, self.m.weights, to_device(self.txt, dtype, device),
+                          to_device(self.img, dtype, device) if self.img is not None else None, self.ctx.c, self.ws)
+
+    def cache(self, chunks=3):
+        return DeviceCache(self.w, chunks * self.w.chunk_tokens, self.dtype, self.dev)
+
+    def f32(self, x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(self.dev)
+
+    def append(self, cache, xv, xa, start):
+        wam.wam_kv_append(self.m.cfg, self.m.weights, cache.c, self.ctx.c, self.f32(xv), self.f32(xa), start, self.ws)
+
+    def step(self, cache, n, xv, xa, tv, ta, start):
+        w = self.w
+        br = self.m.cfg.branches
+        vv = torch.full((br, n * w.video_tokens, w.patch_dim), float("nan"), device=self.dev)
+        va = torch.full((br, n * w.action_tokens, w.action_dim), float("nan"), device=self.dev)
+        wam.wam_dit_stack_fwd(self.m.cfg, self.m.weights, cache.c, self.ctx.c, n, self.f32(xv), self.f32(xa), tv, ta,
+                              start, vv, va, self.ws)
+        torch.cuda.synchronize()
+        return vv.cpu().numpy(), va.cpu().numpy()
+
+
+def tiny_inputs(w):
+    x1v = [draw_named(w, -1, "x1_video_%d" % c) for c in range(3)]
+    x1a = [draw_named(w, -1, "x1_action_%d" % c) for c in range(3)]
+    epv = [draw_named(w, -1, "eps_video_%d" % c) for c in range(3)]
+    epa = [draw_named(w, -1, "eps_action_%d" % c) for c in range(3)]
+    return x1v, x1a, epv, epa
+
+
+@pytest.fixture(scope="module")
+def tiny_oracle():
+    w = WORKLOADS[1].with_(layers=2)
+    m = O.load_model(w)
+    txt = draw_named(w, -1, "txt")
+    ctx = O.build_context(w, m.g, txt, None)
+    ckv = [O.context_kv(w, lp, ctx) for lp in m.layers]
+    return w, m, ckv
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stack_tiny_matches_oracle(gpu, tiny_oracle, dtype):
+    w, m, ckv = tiny_oracle
+    print("stack-tiny", dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    xv1 = O.interpolate(x1v[1], epv[1], 0.5)
+    xa1 = O.interpolate(x1a[1], epa[1], 0.5)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, xv1, xa1, [0.5], [0.5], 1, w.frames_per_chunk)
+
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    assert dc.length == w.chunk_tokens
+    gv, ga = rig.step(dc, 1, xv1, xa1, [0.5], [0.5], w.frames_per_chunk)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
+    assert np.all(np.isfinite(gv)) and np.all(np.isfinite(ga))
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decoupled_timesteps_and_frames(gpu, tiny_oracle, dtype):
+    """Different video/action timesteps and a non-zero window offset, two cached chunks."""
+    w, m, ckv = tiny_oracle
+    print("stack-tiny-decoupled", dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    Fc = w.frames_per_chunk
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 3)
+    O.kv_append(m, cache, ckv, x1v[1], x1a[1], 3 + Fc)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, epv[2], epa[2], [0.1], [0.8], 1, 3 + 2 * Fc)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 3)
+    rig.append(dc, x1v[1], x1a[1], 3 + Fc)
+    gv, ga = rig.step(dc, 1, epv[2], epa[2], [0.1], [0.8], 3 + 2 * Fc)
+    assert rel_l2(gv, ref_v) <= TOL[dtype] and rel_l2(ga, ref_a) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_incremental_equals_full_sequence_gpu(gpu, tiny_oracle, dtype):
+    w, _, _ = tiny_oracle
+    print("inc-vs-full", dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    Lv, La = w.video_tokens, w.action_tokens
+    xv1 = O.interpolate(x1v[1], epv[1], 0.25)
+    xa1 = O.interpolate(x1a[1], epa[1], 0.25)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    iv, ia = rig.step(dc, 1, xv1, xa1, [0.25], [0.25], w.frames_per_chunk)
+    fc = rig.cache()
+    fv, fa = rig.step(fc, 2, np.concatenate([x1v[0], xv1]), np.concatenate([x1a[0], xa1]), [1.0, 0.25], [1.0, 0.25], 0)
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    assert rel_l2(fv[:, Lv:], iv) <= tol and rel_l2(fa[:, La:], ia) <= tol
+    print("bitwise equal:", np.array_equal(fv[:, Lv:], iv), flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_future_perturbation_bit_identical_gpu(gpu, tiny_oracle, dtype):
+    w, _, _ = tiny_oracle
+    print("perturb", dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    Lv, La = w.video_tokens, w.action_tokens
+    rig = Rig(w, dtype, gpu)
+    a = rig.step(rig.cache(), 2, np.concatenate([x1v[0], epv[1]]), np.concatenate([x1a[0], epa[1]]), [1, .2], [1, .2], 0)
+    b = rig.step(rig.cache(), 2, np.concatenate([x1v[0], epv[1] * 7 + 3]), np.concatenate([x1a[0], -epa[1]]),
+                 [1, .9], [1, .6], 0)
+    assert np.array_equal(a[0][:, :Lv], b[0][:, :Lv]) and np.array_equal(a[1][:, :La], b[1][:, :La])
+    assert not np.array_equal(a[0][:, Lv:], b[0][:, Lv:])
+
+
+def test_run_to_run_bitwise_determinism(gpu, tiny_oracle):
+    w, _, _ = tiny_oracle
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    rig = Rig(w, "bf16", gpu)
+    outs = []
+    for _ in range(2):
+        dc = rig.cache()
+        rig.append(dc, x1v[0], x1a[0], 0)
+        outs.append(rig.step(dc, 1, epv[1], epa[1], [0.3], [0.3], w.frames_per_chunk))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_cfg_batch_equals_two_single_branch_calls(gpu, tiny_oracle):
+    w, _, _ = tiny_oracle
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    rig2 = Rig(w, "bf16", gpu)
+    dc = rig2.cache()
+    rig2.append(dc, x1v[0], x1a[0], 0)
+    both = rig2.step(dc, 1, epv[1], epa[1], [0.3], [0.3], w.frames_per_chunk)
+    w1 = w.with_(branches=1)
+    for b in range(2):
+        m1 = DeviceModel(w1, "bf16", gpu)
+        ws = workspace(m1.cfg, 1, gpu)
+        ctx1 = DeviceCtx(w1, "bf16", gpu)
+        wam.wam_ctx_build(m1.cfg, m1.weights, to_device(rig2.txt[b:b + 1], "bf16", gpu), None, ctx1.c, ws)
+        c1 = DeviceCache(w1, 2 * w.chunk_tokens, "bf16", gpu)
+        f32 = rig2.f32
+        wam.wam_kv_append(m1.cfg, m1.weights, c1.c, ctx1.c, f32(x1v[0]), f32(x1a[0]), 0, ws)
+        vv = torch.empty((1, w.video_tokens, w.patch_dim), device=gpu)
+        va = torch.empty((1, w.action_tokens, w.action_dim), device=gpu)
+        wam.wam_dit_stack_fwd(m1.cfg, m1.weights, c1.c, ctx1.c, 1, f32(epv[1]), f32(epa[1]), [0.3], [0.3],
+                              w.frames_per_chunk, vv, va, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(vv.cpu().numpy()[0], both[0][b]) and np.array_equal(va.cpu().numpy()[0], both[1][b])
+
+
+def test_flow_step_matches_oracle(gpu):
+    nv, na = 28160, 192
+    rng = synth.tensor_key(101, 0, "flow")
+    v = synth.fill((2, nv + na), rng, "normal", 1.0)
+    xv = synth.fill((nv,), rng + 1, "normal", 1.0)
+    xa = synth.fill((na,), rng + 2, "normal", 1.0)
+    prev = synth.fill((nv,), rng + 3, "normal", 1.0)
+    vv, va = np.ascontiguousarray(v[:, :nv]), np.ascontiguousarray(v[:, nv:])
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(gpu)  # noqa: E731
+    Xv, Xa, Prev = d(xv), d(xa), d(prev)
+    Gv, Ga = torch.empty(nv, device=gpu), torch.empty(na, device=gpu)
+    cos = torch.empty(3, device=gpu)
+    ws = torch.empty(4096, dtype=torch.uint8, device=gpu)
+    wam.wam_flow_step(Xv, Xa, d(vv), d(va), 2, 5.0, nv, na, 1 / 16, 0.25, Gv, Ga, Prev, cos, ws)
+    torch.cuda.synchronize()
+    gv = O.cfg_combine(vv, 5.0)
+    ga = O.cfg_combine(va, 5.0)
+    np.testing.assert_allclose(Gv.cpu().numpy(), gv, rtol=2e-6, atol=2e-6)
+    np.testing.assert_allclose(Ga.cpu().numpy(), ga, rtol=2e-6, atol=2e-6)
+    np.testing.assert_allclose(Xv.cpu().numpy(), O.euler_update(xv, gv, 0.0, 1 / 16), rtol=2e-6, atol=2e-6)
+    np.testing.assert_allclose(Xa.cpu().numpy(), O.euler_update(xa, ga, 0.0, 0.25), rtol=2e-6, atol=2e-6)
+    c = cos.cpu().numpy().astype(np.float64)
+    g64 = gv.astype(np.float64)
+    p64 = prev.astype(np.float64)
+    np.testing.assert_allclose(c, [g64 @ p64, g64 @ g64, p64 @ p64], rtol=1e-4, atol=1e-2)
+    assert abs(c[0] / np.sqrt(c[1] * c[2]) - O.cosine_fp64(gv, prev)) < 1e-5
+    # guidance 1 returns the conditional branch exactly; one branch = plain Euler
+    Xv2 = d(xv)
+    Gv2 = torch.empty(nv, device=gpu)
+    wam.wam_flow_step(Xv2, Xa, d(vv), d(va), 2, 1.0, nv, na, 0.5, 0.5, Gv2, None, None, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(Gv2.cpu().numpy(), vv[0])
+
+
+@pytest.mark.timeout(900)
+def test_full_width_block_bf16(gpu):
+    """One Wan-14B-sized block (width 5120, 40 heads of 128, FFN 13824), 769 condition tokens, one cached
+    chunk of 464 tokens, CFG batch of 2, bf16, against the fp32 oracle."""
+    w = WORKLOADS[2]
+    print("full-width block: oracle", flush=True)
+    m = O.load_model(w)
+    txt = draw_named(w, -1, "txt")
+    img = draw_named(w, -1, "img")
+    ctx = O.build_context(w, m.g, txt, img)
+    ckv = [O.context_kv(w, lp, ctx) for lp in m.layers]
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    t = float(synth.workloads.timesteps(w, 1)[0])
+    xv1 = O.interpolate(x1v[1], epv[1], t)
+    xa1 = O.interpolate(x1a[1], epa[1], t)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, xv1, xa1, [t], [t], 1, w.frames_per_chunk)
+    del m, ckv, ctx
+    print("full-width block: gpu", flush=True)
+    rig = Rig(w, "bf16", gpu)
+    dc = rig.cache(2)
+    rig.append(dc, x1v[0], x1a[0], 0)
+    gv, ga = rig.step(dc, 1, xv1, xa1, [t], [t], w.frames_per_chunk)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
+    assert ev <= 2e-2 and ea <= 2e-2

@@ -1,0 +1,134 @@
+"""Kernel-level parity through the C ABI (wam_op_linear, wam_op_attention) against the oracle.
+
+Inputs are seeded synth draws (bf16-representable), identical on both sides. Tolerances:
+* linear, bf16: fp32 accumulation of exact bf16 products, then one rounding of the output to bf16,
+  so |gpu - ref| <= 2^-8 |ref| + 2^-8 * 1e-2 (a bf16 half-ulp, plus slack for the summation order);
+* linear, fp32: relative L2 <= 1e-5 (fp32 summation of K products);
+* attention, bf16: probabilities enter the second product rounded to bf16 and the output is
+  rounded to bf16: relative L2 <= 1e-2; fp32: relative L2 <= 1e-5.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import world_action_video_amd as wam
+from world_action_video_amd.device import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def draw(shape, name, sigma=1.0):
+    return synth.fill(shape, synth.tensor_key(100, 0, name), "normal", sigma=sigma)
+
+
+def host(t):
+    return t.float().cpu().numpy()
+
+
+LINEAR_CASES = [(1, 64, 64), (67, 200, 128), (300, 384, 512), (928, 1024, 256), (130, 96, 1024)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", LINEAR_CASES)
+@pytest.mark.parametrize("act", [0, 1])
+def test_op_linear_small(gpu, dtype, M, N, K, act):
+    print("linear", dtype, M, N, K, act, flush=True)
+    a = draw((M, K), "a%d_%d_%d" % (M, N, K))
+    w = draw((N, K), "w%d_%d_%d" % (M, N, K), 0.05)
+    b = draw((N,), "b%d" % N, 0.1)
+    ref = a.astype(np.float64) @ w.astype(np.float64).T + b
+    if act:
+        ref = O.gelu_tanh(ref)
+    dt = wam.WAM_BF16 if dtype == "bf16" else wam.WAM_F32
+    A, W = to_device(a, dtype, gpu), to_device(w, dtype, gpu)
+    B = torch.from_numpy(b).to(gpu)
+    C = torch.full((M, N), float("nan"), dtype=A.dtype, device=gpu)
+    wam.wam_op_linear(dt, A, K, W, K, B, C, N, M, N, K, act)
+    torch.cuda.synchronize()
+    out = host(C)
+    if dtype == "bf16":
+        assert np.all(np.abs(out - ref) <= np.abs(ref) * 2.0 ** -8 + 2.0 ** -8 * 1e-2)
+    else:
+        assert rel_l2(out, ref) <= 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [(928, 15360, 5120), (928, 5120, 13824), (1538, 5120, 1536), (2688, 5120, 5120)])
+def test_op_linear_full_size_sampled(gpu, M, N, K):
+    """The step's real projection shapes in bf16, checked on 4096 sampled outputs computed one by one."""
+    print("linear-full", M, N, K, flush=True)
+    a = draw((M, K), "fa%d_%d" % (M, K))
+    w = draw((N, K), "fw%d_%d" % (N, K), 0.02)
+    b = draw((N,), "fb%d" % N, 0.02)
+    A, W = to_device(a, "bf16", gpu), to_device(w, "bf16", gpu)
+    B = torch.from_numpy(b).to(gpu)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=gpu)
+    wam.wam_op_linear(wam.WAM_BF16, A, K, W, K, B, C, N, M, N, K, 0)
+    torch.cuda.synchronize()
+    out = host(C)
+    rng = np.random.default_rng(7)
+    rows = np.concatenate([rng.integers(0, M, 4000), [0, M - 1] * 48])
+    cols = np.concatenate([rng.integers(0, N, 4000), [0, N - 1, N - 1, 0] * 24])
+    ref = np.einsum("ik,ik->i", a[rows].astype(np.float64), w[cols].astype(np.float64)) + b[cols]
+    got = out[rows, cols]
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-3)
+
+
+def _attn_case(gpu, dtype, br, H, d, Lq, kv_base, chunk_q, kv_total, tag):
+    k_rows = ((kv_total + 63) // 64) * 64 + 64
+    v_stride = ((kv_total + 63) // 64) * 64
+    q = draw((br, H, Lq, d), "q" + tag)
+    k = draw((br, H, k_rows, d), "k" + tag)
+    v = draw((br, H, kv_total, d), "v" + tag)
+    vt = np.zeros((br, H, d, v_stride), np.float32)
+    vt[..., :kv_total] = np.swapaxes(v, -1, -2)
+    # stale values beyond kv_total must not matter: poison them
+    if v_stride > kv_total:
+        vt[..., kv_total:] = np.nan
+    k[:, :, kv_total:] = np.nan
+    Q, K, VT = (to_device(x, dtype, gpu) for x in (q, k, vt))
+    Ot = torch.full((br * Lq, H * d), float("nan"), dtype=Q.dtype, device=gpu)
+    dt = wam.WAM_BF16 if dtype == "bf16" else wam.WAM_F32
+    wam.wam_op_attention(dt, Q, K, VT, Ot, br, H, d, Lq, k_rows, v_stride, kv_base, chunk_q, kv_total)
+    torch.cuda.synchronize()
+    out = host(Ot).reshape(br, Lq, H, d).transpose(0, 2, 1, 3)
+    lim = np.full(Lq, kv_total)
+    if chunk_q > 0:
+        lim = np.minimum(kv_total, kv_base + (np.arange(Lq) // chunk_q + 1) * chunk_q)
+    vis = np.arange(kv_total)[None, :] < lim[:, None]
+    ref = np.stack([O.attention(q[b].astype(np.float64), k[b, :, :kv_total].astype(np.float64),
+                                v[b].astype(np.float64), vis) for b in range(br)])
+    return out, ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Lq,kv_base,chunk_q,kv_total", [
+    (1, 0, 0, 1),            # one key: output = V row
+    (5, 0, 0, 9),
+    (152, 152, 0, 304),      # tiny workload incremental step
+    (304, 0, 152, 304),      # tiny workload full sequence, 2 chunks
+    (200, 64, 72, 250),      # ragged chunk-causal
+    (130, 0, 0, 769),        # cross-attention length
+])
+def test_op_attention(gpu, dtype, d, Lq, kv_base, chunk_q, kv_total):
+    print("attention", dtype, d, Lq, kv_base, chunk_q, kv_total, flush=True)
+    out, ref = _attn_case(gpu, dtype, 2, 3, d, Lq, kv_base, chunk_q, kv_total, "%d_%d_%d_%d_%d" % (d, Lq, kv_base, chunk_q, kv_total))
+    assert np.all(np.isfinite(out))
+    assert rel_l2(out, ref) <= (1e-2 if dtype == "bf16" else 1e-5)
+
+
+def test_op_attention_full_shape_bf16(gpu):
+    """Config-3 self-attention geometry: 928 cached + 464 current keys, 40 heads of 128, 2 branches."""
+    print("attention-full", flush=True)
+    out, ref = _attn_case(gpu, "bf16", 2, 40, 128, 464, 928, 0, 1392, "full")
+    assert rel_l2(out, ref) <= 1e-2

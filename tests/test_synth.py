@@ -38,3 +38,14 @@ def test_bf16_rounding_ties_to_even():
 def test_timesteps_in_unit_interval():
     t = synth.workloads.timesteps(synth.WORKLOADS[3], 1000)
     assert t.min() >= 0 and t.max() < 1 and abs(t.mean() - 0.5) < 0.05
+
+
+def test_matrix_classification_matches_abi_contract():
+    # The C ABI reads Linear weights ([out, in]) in the model dtype and every other tensor as float32;
+    # the uploader must classify each tensor exactly that way (a vector mistaken for a matrix would be
+    # stored as bf16 and read as float, past its end).
+    from synth.workloads import global_tensors, is_matrix, layer_tensors
+    w = synth.WORKLOADS[3]
+    for name, shape, _, _ in global_tensors(w) + layer_tensors(w):
+        linear = len(shape) == 2 and name not in ("mod", "head_mod")
+        assert is_matrix(name) == linear, name

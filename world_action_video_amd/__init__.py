@@ -1,0 +1,194 @@
+"""Python binding of ``libwam.so``: the C-ABI calls under the same names, argument marshalling only.
+
+Every step of the denoising path runs in the library's HIP kernels; this module only converts
+Python objects (torch tensors, ints, floats) into the C structs and pointers of ``include/wam.h``.
+Importing works without a GPU; calling anything needs the built library (``build.build()``) and
+raises if it is missing -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwam.so")
+
+WAM_OK, WAM_E_ARG, WAM_E_SHAPE, WAM_E_CAPACITY, WAM_E_HIP, WAM_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+WAM_BF16, WAM_F32 = 0, 1
+
+EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
+           "wam_dit_block_fwd", "wam_flow_step", "wam_op_linear", "wam_op_attention", "wam_kv_reset",
+           "wam_last_error")
+
+
+class WamError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("wam status %d: %s" % (status, msg))
+        self.status = status
+
+
+class wam_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("dim", "heads", "head_dim", "ffn_dim", "layers", "freq_dim",
+                                             "patch_dim", "action_dim", "action_tokens", "frames_per_chunk",
+                                             "grid_h", "grid_w", "ctx_in_dim", "ctx_text_len", "ctx_img_len",
+                                             "branches")] + \
+              [("rope_theta", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+BLOCK_FIELDS = ("mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "ln3_w", "ln3_b", "w_cq", "b_cq", "g_cq",
+                "w_ck", "b_ck", "g_ck", "w_cv", "b_cv", "w_co", "b_co", "w_ff1", "b_ff1", "w_ff2", "b_ff2")
+GLOBAL_FIELDS = ("t_w1", "t_b1", "t_w2", "t_b2", "t_wp", "t_bp", "pe_w", "pe_b", "ae_w", "ae_b", "head_mod",
+                 "vo_w", "vo_b", "ao_w", "ao_b", "txt_w", "txt_b", "img_w", "img_b")
+
+
+class wam_block_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_FIELDS]
+
+
+class wam_weights(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.POINTER(wam_block_weights))] + [(n, ctypes.c_void_p) for n in GLOBAL_FIELDS]
+
+
+class wam_kv_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("branches", ctypes.c_int),
+                ("capacity", ctypes.c_int), ("length", ctypes.c_int)]
+
+
+class wam_ctx_kv(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("branches", ctypes.c_int),
+                ("ctx_len", ctypes.c_int), ("ctx_stride", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load ``libwam.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libwam.so is not built (run world_action_video_amd/build.py); no fallback exists")
+    lib = ctypes.CDLL(path)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    CFG = ctypes.POINTER(wam_config)
+    W = ctypes.POINTER(wam_weights)
+    KV = ctypes.POINTER(wam_kv_cache)
+    CX = ctypes.POINTER(wam_ctx_kv)
+    sig = {
+        "wam_workspace_bytes": (S, [CFG, I]),
+        "wam_ctx_build": (I, [CFG, W, P, P, CX, P, S, P]),
+        "wam_time_embed": (I, [CFG, W, P, I, P, P, P, S, P]),
+        "wam_dit_stack_fwd": (I, [CFG, W, KV, CX, I, P, P, P, P, I, P, P, P, S, P]),
+        "wam_kv_append": (I, [CFG, W, KV, CX, P, P, I, P, S, P]),
+        "wam_dit_block_fwd": (I, [CFG, ctypes.POINTER(wam_block_weights), I, KV, CX, P, P, I, I, P, S, P]),
+        "wam_flow_step": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P, S, P]),
+        "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P]),
+        "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P]),
+        "wam_kv_reset": (None, [KV]),
+        "wam_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    """Device/host pointer of a torch tensor, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(st: int):
+    if st != WAM_OK:
+        raise WamError(st, load().wam_last_error().decode())
+
+
+def _f32_host(vals):
+    arr = (ctypes.c_float * len(vals))(*[float(v) for v in vals])
+    return ctypes.cast(arr, ctypes.c_void_p).value, arr
+
+
+def wam_workspace_bytes(cfg: wam_config, n_chunks: int) -> int:
+    return int(load().wam_workspace_bytes(ctypes.byref(cfg), n_chunks))
+
+
+def wam_ctx_build(cfg, w, txt, img, ctx: wam_ctx_kv, ws, stream=None):
+    _check(load().wam_ctx_build(ctypes.byref(cfg), ctypes.byref(w), _ptr(txt), _ptr(img), ctypes.byref(ctx),
+                                _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def wam_time_embed(cfg, w, t, e, e6, ws, stream=None):
+    tp, keep = _f32_host(t)
+    _check(load().wam_time_embed(ctypes.byref(cfg), ctypes.byref(w), tp, len(t), _ptr(e), _ptr(e6), _ptr(ws),
+                                 _nbytes(ws), _stream(stream)))
+    del keep
+
+
+def wam_dit_stack_fwd(cfg, w, cache: wam_kv_cache, ctx: wam_ctx_kv, n_chunks, x_video, x_action, t_video, t_action,
+                      start_frame, v_video, v_action, ws, stream=None):
+    tvp, k1 = _f32_host(t_video)
+    tap, k2 = _f32_host(t_action)
+    _check(load().wam_dit_stack_fwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), ctypes.byref(ctx),
+                                    n_chunks, _ptr(x_video), _ptr(x_action), tvp, tap, start_frame, _ptr(v_video),
+                                    _ptr(v_action), _ptr(ws), _nbytes(ws), _stream(stream)))
+    del k1, k2
+
+
+def wam_kv_append(cfg, w, cache: wam_kv_cache, ctx: wam_ctx_kv, x_video, x_action, start_frame, ws, stream=None):
+    _check(load().wam_kv_append(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), ctypes.byref(ctx),
+                                _ptr(x_video), _ptr(x_action), start_frame, _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def wam_dit_block_fwd(cfg, bw: wam_block_weights, layer, cache, ctx, h, e6, n_chunks, start_frame, ws, stream=None):
+    _check(load().wam_dit_block_fwd(ctypes.byref(cfg), ctypes.byref(bw), layer, ctypes.byref(cache),
+                                    ctypes.byref(ctx), _ptr(h), _ptr(e6), n_chunks, start_frame, _ptr(ws),
+                                    _nbytes(ws), _stream(stream)))
+
+
+def wam_flow_step(x_video, x_action, v_video, v_action, branches, guidance, n_video, n_action, dt_video, dt_action,
+                  g_video=None, g_action=None, prev_video=None, cos_parts=None, ws=None, stream=None):
+    _check(load().wam_flow_step(_ptr(x_video), _ptr(x_action), _ptr(v_video), _ptr(v_action), branches,
+                                float(guidance), n_video, n_action, float(dt_video), float(dt_action), _ptr(g_video),
+                                _ptr(g_action), _ptr(prev_video), _ptr(cos_parts), _ptr(ws), _nbytes(ws),
+                                _stream(stream)))
+
+
+def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, stream=None):
+    _check(load().wam_op_linear(dtype, _ptr(A), lda, _ptr(W), ldw, _ptr(bias), _ptr(C), ldc, M, N, K, act,
+                                _stream(stream)))
+
+
+def wam_op_attention(dtype, Q, K, Vt, O, br, heads, head_dim, Lq, k_rows, v_stride, kv_base, chunk_q, kv_total,
+                     stream=None):
+    _check(load().wam_op_attention(dtype, _ptr(Q), _ptr(K), _ptr(Vt), _ptr(O), br, heads, head_dim, Lq, k_rows,
+                                   v_stride, kv_base, chunk_q, kv_total, _stream(stream)))
+
+
+def wam_kv_reset(cache: wam_kv_cache):
+    load().wam_kv_reset(ctypes.byref(cache))
+
+
+def wam_last_error() -> str:
+    return load().wam_last_error().decode()
+
+
+def _nbytes(ws):
+    if ws is None:
+        return 0
+    if isinstance(ws, int):
+        raise TypeError("pass the workspace as a tensor so its size is known")
+    return ws.numel() * ws.element_size()

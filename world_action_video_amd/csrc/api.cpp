@@ -1,0 +1,542 @@
+// C-ABI layer: argument validation, workspace carving and the launch sequence of the DiT step.
+// Every check happens before the first launch, so a non-OK status means nothing was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/wam.h"
+#include "kernels.h"
+
+using namespace wam;
+
+namespace {
+
+thread_local std::string g_err;
+
+wam_status fail(wam_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                        \
+  do {                                                                                       \
+    hipError_t e_ = (expr);                                                                  \
+    if (e_ != hipSuccess) return fail(WAM_E_HIP, "%s: %s", #expr, hipGetErrorString(e_));     \
+  } while (0)
+
+constexpr int kMaxChunks = 8;   // 2 * n_chunks timesteps fit the time-MLP batch of 16
+
+struct Geo {
+  int D, H, d, F, L, P, A, La, Lv, Lq, Lc, Cin, br, freq;
+  size_t esz;
+  DType dt;
+};
+
+Geo geo_of(const wam_config& c) {
+  Geo g;
+  g.D = c.dim; g.H = c.heads; g.d = c.head_dim; g.F = c.ffn_dim; g.L = c.layers; g.P = c.patch_dim;
+  g.A = c.action_dim; g.La = c.action_tokens; g.Lv = c.frames_per_chunk * c.grid_h * c.grid_w;
+  g.Lq = g.Lv + g.La; g.Lc = c.ctx_text_len + c.ctx_img_len; g.Cin = c.ctx_in_dim; g.br = c.branches;
+  g.freq = c.freq_dim;
+  g.dt = c.dtype == WAM_BF16 ? DT_BF16 : DT_F32;
+  g.esz = c.dtype == WAM_BF16 ? 2 : 4;
+  return g;
+}
+
+wam_status check_cfg(const wam_config* c) {
+  if (!c) return fail(WAM_E_ARG, "config is NULL");
+  if (c->dtype != WAM_BF16 && c->dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype %d", (int)c->dtype);
+  if (c->dim <= 0 || c->heads <= 0 || c->layers <= 0 || c->ffn_dim <= 0 || c->freq_dim <= 0)
+    return fail(WAM_E_SHAPE, "non-positive model size");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(WAM_E_SHAPE, "head_dim must be 64 or 128");
+  if (c->dim != c->heads * c->head_dim) return fail(WAM_E_SHAPE, "dim != heads * head_dim");
+  if (c->dim % 64 || c->ffn_dim % 64 || c->ctx_in_dim % 64 || c->ctx_in_dim <= 0)
+    return fail(WAM_E_SHAPE, "dim, ffn_dim and ctx_in_dim must be multiples of 64");
+  if (c->dim > 8192) return fail(WAM_E_SHAPE, "dim above 8192 is not supported");
+  if (c->freq_dim % 8) return fail(WAM_E_SHAPE, "freq_dim must be a multiple of 8");
+  if (c->patch_dim <= 0 || c->action_dim <= 0 || c->action_tokens < 0) return fail(WAM_E_SHAPE, "bad token sizes");
+  if (c->frames_per_chunk <= 0 || c->grid_h <= 0 || c->grid_w <= 0) return fail(WAM_E_SHAPE, "bad chunk geometry");
+  const int lq = c->frames_per_chunk * c->grid_h * c->grid_w + c->action_tokens;
+  if (lq % 8) return fail(WAM_E_SHAPE, "tokens per chunk (%d) must be a multiple of 8", lq);
+  if (c->ctx_text_len <= 0 || c->ctx_img_len < 0) return fail(WAM_E_SHAPE, "bad condition lengths");
+  if (c->branches != 1 && c->branches != 2) return fail(WAM_E_SHAPE, "branches must be 1 or 2");
+  if (!(c->eps > 0.f) || !(c->rope_theta > 0.f)) return fail(WAM_E_ARG, "eps and rope_theta must be positive");
+  return WAM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t h, y, qkv, qh, attn, ffn, rope, emb, h1, e, e6, partials, ctx_a, ctx_b, total;
+};
+
+Layout layout_of(const Geo& g, int n) {
+  Layout L{};
+  const size_t R = (size_t)n * g.Lq, M = (size_t)g.br * R, G = 2 * (size_t)n;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  L.h = take(M * g.D * 4);
+  L.y = take(M * g.D * g.esz);
+  L.qkv = take(M * 3 * g.D * g.esz);
+  L.qh = take(M * g.D * g.esz);
+  L.attn = take(M * g.D * g.esz);
+  L.ffn = take(M * g.F * g.esz);
+  L.rope = take(R * (g.d / 2) * sizeof(float2));
+  L.emb = take(G * g.freq * 4);
+  L.h1 = take(G * g.D * 4);
+  L.e = take(G * g.D * 4);
+  L.e6 = take(G * 6 * g.D * 4);
+  L.partials = take(64 * 3 * 4);
+  size_t stack_total = off;
+  // condition build (never concurrent with a pass on the same workspace): two [br*Lc][D] buffers
+  const size_t cb = align256((size_t)g.br * g.Lc * g.D * g.esz);
+  L.ctx_a = 0;
+  L.ctx_b = cb;
+  L.total = stack_total > 2 * cb ? stack_total : 2 * cb;
+  return L;
+}
+
+template <typename P> P* at(void* ws, size_t off) { return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off); }
+
+const char* const kBlockNames[] = {"mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "ln3_w", "ln3_b",
+                                   "w_cq", "b_cq", "g_cq", "w_ck", "b_ck", "g_ck", "w_cv", "b_cv", "w_co",
+                                   "b_co", "w_ff1", "b_ff1", "w_ff2", "b_ff2"};
+
+wam_status check_block(const wam_block_weights* b, int l) {
+  if (!b) return fail(WAM_E_ARG, "block weights of layer %d are NULL", l);
+  const void* const* p = reinterpret_cast<const void* const*>(b);
+  for (int i = 0; i < (int)(sizeof(wam_block_weights) / sizeof(void*)); ++i)
+    if (!p[i]) return fail(WAM_E_ARG, "layer %d: %s is NULL", l, kBlockNames[i]);
+  return WAM_OK;
+}
+
+wam_status check_weights(const wam_config* c, const wam_weights* w, bool need_blocks) {
+  if (!w) return fail(WAM_E_ARG, "weights are NULL");
+  if (!w->t_w1 || !w->t_b1 || !w->t_w2 || !w->t_b2 || !w->t_wp || !w->t_bp)
+    return fail(WAM_E_ARG, "time-embedding weights are NULL");
+  if (!w->pe_w || !w->pe_b || !w->ae_w || !w->ae_b) return fail(WAM_E_ARG, "token-embedding weights are NULL");
+  if (!w->head_mod || !w->vo_w || !w->vo_b || !w->ao_w || !w->ao_b) return fail(WAM_E_ARG, "head weights are NULL");
+  if (need_blocks) {
+    if (!w->blocks) return fail(WAM_E_ARG, "blocks array is NULL");
+    for (int l = 0; l < c->layers; ++l) {
+      wam_status st = check_block(&w->blocks[l], l);
+      if (st != WAM_OK) return st;
+    }
+  }
+  return WAM_OK;
+}
+
+wam_status check_cache(const Geo& g, const wam_kv_cache* kv, int rows) {
+  if (!kv || !kv->k || !kv->v) return fail(WAM_E_ARG, "KV cache pointers are NULL");
+  if (kv->branches != g.br) return fail(WAM_E_SHAPE, "cache branches %d != config branches %d", kv->branches, g.br);
+  if (kv->capacity <= 0 || kv->capacity % 64) return fail(WAM_E_SHAPE, "cache capacity must be a positive multiple of 64");
+  if (kv->length < 0 || kv->length % 8) return fail(WAM_E_SHAPE, "cache length must be a non-negative multiple of 8");
+  if ((long)kv->length + rows > kv->capacity)
+    return fail(WAM_E_CAPACITY, "cache capacity %d < length %d + %d new rows", kv->capacity, kv->length, rows);
+  return WAM_OK;
+}
+
+wam_status check_ctx(const Geo& g, const wam_ctx_kv* cx) {
+  if (!cx || !cx->k || !cx->v) return fail(WAM_E_ARG, "condition KV pointers are NULL");
+  if (cx->branches != g.br) return fail(WAM_E_SHAPE, "condition KV branches != config branches");
+  if (cx->ctx_len != g.Lc) return fail(WAM_E_SHAPE, "condition length %d != %d", cx->ctx_len, g.Lc);
+  if (cx->ctx_stride < g.Lc || cx->ctx_stride % 64) return fail(WAM_E_SHAPE, "ctx_stride must be a multiple of 64 >= ctx_len");
+  return WAM_OK;
+}
+
+// pointers of one layer inside the caches
+template <typename X> X* layer_ptr(void* base, size_t elems_per_layer, int l, size_t esz) {
+  return reinterpret_cast<X*>(reinterpret_cast<char*>(base) + (size_t)l * elems_per_layer * esz);
+}
+
+struct Pass {   // everything one pass needs
+  const wam_config* cfg;
+  Geo g;
+  Layout L;
+  void* ws;
+  int n;        // chunks in this pass
+  int R, M;     // rows per branch, total rows
+  wam_kv_cache* kv;
+  const wam_ctx_kv* cx;
+  float* h;     // residual stream
+  const float* e6;
+  float2* rope;
+  hipStream_t s;
+};
+
+RowMap rowmap(const Pass& p) { return RowMap{p.R, p.g.Lq, p.g.Lv}; }
+
+GemmArgs gemm_args(const void* A, long lda, const void* W, long ldw, const void* bias, int M, int N, int K) {
+  GemmArgs a{};
+  a.A = A; a.lda = lda; a.W = W; a.ldw = ldw; a.bias = reinterpret_cast<const float*>(bias);
+  a.M = M; a.N = N; a.K = K;
+  return a;
+}
+
+// One block. kv_only: stop after the keys/values of this layer are in the cache.
+wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_only) {
+  const Geo& g = p.g;
+  const DType dt = g.dt;
+  const float eps = p.cfg->eps;
+  const RowMap rm = rowmap(p);
+  void* y = at<void>(p.ws, p.L.y);
+  void* qkv = at<void>(p.ws, p.L.qkv);
+  void* qh = at<void>(p.ws, p.L.qh);
+  void* attn = at<void>(p.ws, p.L.attn);
+  void* ffn = at<void>(p.ws, p.L.ffn);
+  const size_t cache_layer = (size_t)g.br * g.H * p.kv->capacity * g.d;
+  void* kc = layer_ptr<void>(p.kv->k, cache_layer, l, g.esz);
+  void* vc = layer_ptr<void>(p.kv->v, cache_layer, l, g.esz);
+  const int len = p.kv->length;
+  const float* mod = reinterpret_cast<const float*>(bw.mod);
+
+  // (1) y = LN(h) (1 + scale1) + shift1
+  NormArgs na{};
+  na.X = p.h; na.Y = y; na.M = p.M; na.D = g.D; na.eps = eps; na.mode = NORM_ADALN; na.rm = rm;
+  na.e6 = p.e6; na.mod = mod; na.shift_idx = 0; na.scale_idx = 1;
+  HIP_TRY(launch_norm(na, dt, p.s));
+  // (2) [q|k|v] = y Wqkv^T + b  (keys/values only for the last layer of an append)
+  {
+    const int col0 = kv_only ? g.D : 0;
+    GemmArgs ga = gemm_args(y, g.D, reinterpret_cast<const char*>(bw.w_qkv) + (size_t)col0 * g.D * g.esz, g.D,
+                            reinterpret_cast<const float*>(bw.b_qkv) + col0, p.M, 3 * g.D - col0, g.D);
+    ga.C = reinterpret_cast<char*>(qkv) + (size_t)col0 * g.esz;
+    ga.ldc = 3 * g.D;
+    HIP_TRY(launch_gemm(ga, dt, EPI_STORE, p.s));
+  }
+  // (3) RMSNorm + RoPE of q (head-major) and k (into the cache), values into the cache
+  QkNormArgs qa{};
+  qa.src = qkv; qa.src_ld = 3 * g.D; qa.M = p.M; qa.D = g.D; qa.H = g.H; qa.d = g.d; qa.rows_per_branch = p.R;
+  qa.eps = eps; qa.rope = p.rope; qa.rm = rm;
+  if (!kv_only) {
+    qa.src_col = 0; qa.gain = reinterpret_cast<const float*>(bw.g_q);
+    qa.dst = qh; qa.dst_bh_stride = (long)p.R * g.d; qa.dst_row0 = 0;
+    HIP_TRY(launch_qk_norm_rope(qa, dt, p.s));
+  }
+  qa.src_col = g.D; qa.gain = reinterpret_cast<const float*>(bw.g_k);
+  qa.dst = kc; qa.dst_bh_stride = (long)p.kv->capacity * g.d; qa.dst_row0 = len;
+  HIP_TRY(launch_qk_norm_rope(qa, dt, p.s));
+  VCacheArgs va{};
+  va.src = qkv; va.src_ld = 3 * g.D; va.src_col = 2 * g.D; va.dst = vc; va.dst_bh_stride = (long)g.d * p.kv->capacity;
+  va.dst_stride = p.kv->capacity; va.dst_col0 = len; va.rows_per_branch = p.R; va.br = g.br; va.H = g.H; va.d = g.d;
+  HIP_TRY(launch_v_to_cache(va, dt, p.s));
+  if (kv_only) return WAM_OK;
+
+  // (4) chunk-causal self-attention over [cache ; this pass]
+  AttnArgs aa{};
+  aa.Q = qh; aa.K = kc; aa.Vt = vc; aa.O = attn;
+  aa.q_bh_stride = (long)p.R * g.d; aa.k_bh_stride = (long)p.kv->capacity * g.d; aa.v_bh_stride = (long)g.d * p.kv->capacity;
+  aa.v_stride = p.kv->capacity; aa.Lq_total = p.R; aa.H = g.H; aa.d = g.d; aa.br = g.br;
+  aa.kv_base = len; aa.chunk_q = p.n > 1 ? g.Lq : 0; aa.kv_total = len + p.R;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
+  HIP_TRY(launch_attention(aa, dt, p.s));
+  // (5) h += gate1 * (o Wo^T + b)
+  {
+    GemmArgs ga = gemm_args(attn, g.D, bw.w_o, g.D, bw.b_o, p.M, g.D, g.D);
+    ga.H = p.h; ga.ldh = g.D; ga.rm = rm; ga.e6 = p.e6; ga.mod = mod; ga.gate_idx = 2; ga.D = g.D;
+    HIP_TRY(launch_gemm(ga, dt, EPI_RESID_GATED, p.s));
+  }
+  // (6) cross-attention: n3 = LN(h) w + b; qc = RMS(n3 Wcq^T + b) g
+  na.mode = NORM_AFFINE; na.w = reinterpret_cast<const float*>(bw.ln3_w); na.b = reinterpret_cast<const float*>(bw.ln3_b);
+  HIP_TRY(launch_norm(na, dt, p.s));
+  {
+    GemmArgs ga = gemm_args(y, g.D, bw.w_cq, g.D, bw.b_cq, p.M, g.D, g.D);
+    ga.C = qkv; ga.ldc = g.D;
+    HIP_TRY(launch_gemm(ga, dt, EPI_STORE, p.s));
+  }
+  qa.src_ld = g.D; qa.src_col = 0; qa.gain = reinterpret_cast<const float*>(bw.g_cq); qa.rope = nullptr;
+  qa.dst = qh; qa.dst_bh_stride = (long)p.R * g.d; qa.dst_row0 = 0;
+  HIP_TRY(launch_qk_norm_rope(qa, dt, p.s));
+  {
+    const size_t ck_layer = (size_t)g.br * g.H * g.Lc * g.d, cv_layer = (size_t)g.br * g.H * g.d * p.cx->ctx_stride;
+    AttnArgs ca{};
+    ca.Q = qh; ca.K = layer_ptr<void>(p.cx->k, ck_layer, l, g.esz); ca.Vt = layer_ptr<void>(p.cx->v, cv_layer, l, g.esz);
+    ca.O = attn; ca.q_bh_stride = (long)p.R * g.d; ca.k_bh_stride = (long)g.Lc * g.d;
+    ca.v_bh_stride = (long)g.d * p.cx->ctx_stride; ca.v_stride = p.cx->ctx_stride;
+    ca.Lq_total = p.R; ca.H = g.H; ca.d = g.d; ca.br = g.br; ca.kv_base = g.Lc; ca.chunk_q = 0; ca.kv_total = g.Lc;
+    ca.scale_log2 = aa.scale_log2;
+    HIP_TRY(launch_attention(ca, dt, p.s));
+  }
+  {
+    GemmArgs ga = gemm_args(attn, g.D, bw.w_co, g.D, bw.b_co, p.M, g.D, g.D);
+    ga.H = p.h; ga.ldh = g.D;
+    HIP_TRY(launch_gemm(ga, dt, EPI_RESID, p.s));
+  }
+  // (7) FFN: h += gate2 * (GELU(y2 W1^T + b1) W2^T + b2), y2 = LN(h) (1 + scale2) + shift2
+  na.mode = NORM_ADALN; na.shift_idx = 3; na.scale_idx = 4;
+  HIP_TRY(launch_norm(na, dt, p.s));
+  {
+    GemmArgs ga = gemm_args(y, g.D, bw.w_ff1, g.D, bw.b_ff1, p.M, g.F, g.D);
+    ga.C = ffn; ga.ldc = g.F;
+    HIP_TRY(launch_gemm(ga, dt, EPI_GELU, p.s));
+  }
+  {
+    GemmArgs ga = gemm_args(ffn, g.F, bw.w_ff2, g.F, bw.b_ff2, p.M, g.D, g.F);
+    ga.H = p.h; ga.ldh = g.D; ga.rm = rm; ga.e6 = p.e6; ga.mod = mod; ga.gate_idx = 5; ga.D = g.D;
+    HIP_TRY(launch_gemm(ga, dt, EPI_RESID_GATED, p.s));
+  }
+  return WAM_OK;
+}
+
+wam_status time_embed(const Pass& p, const wam_weights* w, const float* t, int G, float* e, float* e6) {
+  TimeArgs ta{};
+  for (int i = 0; i < G; ++i) ta.t[i] = t[i];
+  ta.G = G; ta.freq_dim = p.g.freq; ta.D = p.g.D;
+  ta.w1 = w->t_w1; ta.w2 = w->t_w2; ta.wp = w->t_wp;
+  ta.b1 = reinterpret_cast<const float*>(w->t_b1); ta.b2 = reinterpret_cast<const float*>(w->t_b2);
+  ta.bp = reinterpret_cast<const float*>(w->t_bp);
+  ta.emb = at<float>(p.ws, p.L.emb); ta.h1 = at<float>(p.ws, p.L.h1); ta.e = e; ta.e6 = e6;
+  HIP_TRY(launch_time_mlp(ta, p.g.dt, p.s));
+  return WAM_OK;
+}
+
+wam_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(WAM_E_ARG, "workspace is NULL");
+  if (ws_bytes < L.total) return fail(WAM_E_ARG, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(WAM_E_ARG, "workspace must be 256-byte aligned");
+  return WAM_OK;
+}
+
+#define CHECK(expr)                      \
+  do {                                   \
+    wam_status st_ = (expr);             \
+    if (st_ != WAM_OK) return st_;       \
+  } while (0)
+
+// the whole stack: time MLP, rotary table, embedding, blocks, heads (or only the K/V of an append)
+wam_status stack_pass(const wam_config* cfg, const wam_weights* w, wam_kv_cache* kv, const wam_ctx_kv* cx, int n,
+                      const float* xv, const float* xa, const float* tv, const float* ta, int start_frame,
+                      float* vv, float* va, void* ws, size_t ws_bytes, hipStream_t s, bool append) {
+  CHECK(check_cfg(cfg));
+  const Geo g = geo_of(*cfg);
+  if (n < 1 || n > kMaxChunks) return fail(WAM_E_SHAPE, "n_chunks must be in [1, %d]", kMaxChunks);
+  CHECK(check_weights(cfg, w, true));
+  CHECK(check_cache(g, kv, n * g.Lq));
+  CHECK(check_ctx(g, cx));
+  if (!xv || !xa) return fail(WAM_E_ARG, "latent pointers are NULL");
+  if (!append && (!vv || !va || !tv || !ta)) return fail(WAM_E_ARG, "output or timestep pointers are NULL");
+  if (start_frame < 0) return fail(WAM_E_ARG, "start_frame must be non-negative");
+  const Layout L = layout_of(g, n);
+  CHECK(check_ws(L, ws, ws_bytes));
+
+  Pass p{};
+  p.cfg = cfg; p.g = g; p.L = L; p.ws = ws; p.n = n; p.R = n * g.Lq; p.M = g.br * p.R; p.kv = kv; p.cx = cx;
+  p.h = at<float>(ws, L.h); p.e6 = at<float>(ws, L.e6); p.rope = at<float2>(ws, L.rope); p.s = s;
+
+  float tt[2 * kMaxChunks];
+  for (int c = 0; c < n; ++c) {
+    tt[2 * c] = append ? 1.f : tv[c];
+    tt[2 * c + 1] = append ? 1.f : ta[c];
+  }
+  CHECK(time_embed(p, w, tt, 2 * n, at<float>(ws, L.e), at<float>(ws, L.e6)));
+  HIP_TRY(launch_rope_table(p.rope, n, g.Lq, g.Lv, cfg->frames_per_chunk, cfg->grid_h, cfg->grid_w, start_frame, g.d,
+                            cfg->rope_theta, s));
+  EmbedArgs ea{};
+  ea.xv = xv; ea.xa = xa; ea.pe_w = w->pe_w; ea.pe_b = reinterpret_cast<const float*>(w->pe_b);
+  ea.ae_w = w->ae_w; ea.ae_b = reinterpret_cast<const float*>(w->ae_b); ea.H = p.h;
+  ea.n_chunks = n; ea.Lv = g.Lv; ea.La = g.La; ea.P = g.P; ea.A = g.A; ea.D = g.D; ea.br = g.br;
+  HIP_TRY(launch_embed(ea, g.dt, s));
+  for (int l = 0; l < g.L; ++l) CHECK(run_block(p, w->blocks[l], l, append && l == g.L - 1));
+  if (append) return WAM_OK;
+
+  // heads: n = LN(h) (1 + scale_h) + shift_h; v_video / v_action per token group
+  NormArgs na{};
+  na.X = p.h; na.Y = at<void>(ws, L.y); na.M = p.M; na.D = g.D; na.eps = cfg->eps; na.mode = NORM_HEAD;
+  na.rm = rowmap(p); na.e6 = at<float>(ws, L.e); na.mod = reinterpret_cast<const float*>(w->head_mod);
+  HIP_TRY(launch_norm(na, g.dt, s));
+  GemmArgs gv = gemm_args(at<void>(ws, L.y), g.D, w->vo_w, g.D, w->vo_b, p.M, g.P, g.D);
+  gv.C = vv; gv.ldc = g.P; gv.rm = rowmap(p); gv.sel_group = 0;
+  HIP_TRY(launch_gemm(gv, g.dt, EPI_ROWSEL_F32, s));
+  if (g.La > 0) {
+    GemmArgs ga = gemm_args(at<void>(ws, L.y), g.D, w->ao_w, g.D, w->ao_b, p.M, g.A, g.D);
+    ga.C = va; ga.ldc = g.A; ga.rm = rowmap(p); ga.sel_group = 1;
+    HIP_TRY(launch_gemm(ga, g.dt, EPI_ROWSEL_F32, s));
+  }
+  return WAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wam_workspace_bytes(const wam_config* cfg, int n_chunks) {
+  if (check_cfg(cfg) != WAM_OK || n_chunks < 1 || n_chunks > kMaxChunks) return 0;
+  return layout_of(geo_of(*cfg), n_chunks).total;
+}
+
+wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void* txt, const void* img, wam_ctx_kv* out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  const Geo g = geo_of(*cfg);
+  CHECK(check_weights(cfg, w, true));
+  CHECK(check_ctx(g, out));
+  if (!txt || !w->txt_w || !w->txt_b) return fail(WAM_E_ARG, "text features or text projection are NULL");
+  if (cfg->ctx_img_len > 0 && (!img || !w->img_w || !w->img_b)) return fail(WAM_E_ARG, "image features or projection are NULL");
+  const Layout L = layout_of(g, 1);
+  CHECK(check_ws(L, ws, ws_bytes));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ctx = at<void>(ws, L.ctx_a);
+  void* tmp = at<void>(ws, L.ctx_b);
+  const int Lt = cfg->ctx_text_len, Li = cfg->ctx_img_len;
+  for (int b = 0; b < g.br; ++b) {
+    GemmArgs gt = gemm_args(reinterpret_cast<const char*>(txt) + (size_t)b * Lt * g.Cin * g.esz, g.Cin, w->txt_w, g.Cin,
+                            w->txt_b, Lt, g.D, g.Cin);
+    gt.C = reinterpret_cast<char*>(ctx) + (size_t)b * g.Lc * g.D * g.esz; gt.ldc = g.D;
+    HIP_TRY(launch_gemm(gt, g.dt, EPI_STORE, s));
+    if (Li > 0) {
+      GemmArgs gi = gemm_args(img, g.Cin, w->img_w, g.Cin, w->img_b, Li, g.D, g.Cin);
+      gi.C = reinterpret_cast<char*>(ctx) + ((size_t)b * g.Lc + Lt) * g.D * g.esz; gi.ldc = g.D;
+      HIP_TRY(launch_gemm(gi, g.dt, EPI_STORE, s));
+    }
+  }
+  const int M = g.br * g.Lc;
+  const size_t ck_layer = (size_t)g.br * g.H * g.Lc * g.d, cv_layer = (size_t)g.br * g.H * g.d * out->ctx_stride;
+  for (int l = 0; l < g.L; ++l) {
+    const wam_block_weights& bw = w->blocks[l];
+    GemmArgs gk = gemm_args(ctx, g.D, bw.w_ck, g.D, bw.b_ck, M, g.D, g.D);
+    gk.C = tmp; gk.ldc = g.D;
+    HIP_TRY(launch_gemm(gk, g.dt, EPI_STORE, s));
+    QkNormArgs qa{};
+    qa.src = tmp; qa.src_ld = g.D; qa.src_col = 0; qa.gain = reinterpret_cast<const float*>(bw.g_ck);
+    qa.dst = layer_ptr<void>(out->k, ck_layer, l, g.esz); qa.dst_bh_stride = (long)g.Lc * g.d; qa.dst_row0 = 0;
+    qa.M = M; qa.D = g.D; qa.H = g.H; qa.d = g.d; qa.rows_per_branch = g.Lc; qa.eps = cfg->eps; qa.rope = nullptr;
+    qa.rm = RowMap{g.Lc, g.Lc, g.Lc};
+    HIP_TRY(launch_qk_norm_rope(qa, g.dt, s));
+    GemmArgs gv = gemm_args(ctx, g.D, bw.w_cv, g.D, bw.b_cv, M, g.D, g.D);
+    gv.C = tmp; gv.ldc = g.D;
+    HIP_TRY(launch_gemm(gv, g.dt, EPI_STORE, s));
+    VCacheArgs va{};
+    va.src = tmp; va.src_ld = g.D; va.src_col = 0; va.dst = layer_ptr<void>(out->v, cv_layer, l, g.esz);
+    va.dst_bh_stride = (long)g.d * out->ctx_stride; va.dst_stride = out->ctx_stride; va.dst_col0 = 0;
+    va.rows_per_branch = g.Lc; va.br = g.br; va.H = g.H; va.d = g.d;
+    HIP_TRY(launch_v_to_cache(va, g.dt, s));
+  }
+  return WAM_OK;
+}
+
+wam_status wam_time_embed(const wam_config* cfg, const wam_weights* w, const float* t, int n, float* e, float* e6,
+                          void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_weights(cfg, w, false));
+  if (!t || !e || !e6) return fail(WAM_E_ARG, "timestep or output pointers are NULL");
+  if (n < 1 || n > 2 * kMaxChunks) return fail(WAM_E_SHAPE, "n must be in [1, %d]", 2 * kMaxChunks);
+  Pass p{};
+  p.cfg = cfg; p.g = geo_of(*cfg); p.L = layout_of(p.g, kMaxChunks); p.ws = ws;
+  p.s = reinterpret_cast<hipStream_t>(stream);
+  const Layout need = layout_of(p.g, (n + 1) / 2);
+  CHECK(check_ws(need, ws, ws_bytes));
+  p.L = need;
+  return time_embed(p, w, t, n, e, e6);
+}
+
+wam_status wam_dit_stack_fwd(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache, const wam_ctx_kv* ctx,
+                             int n_chunks, const float* x_video, const float* x_action, const float* t_video,
+                             const float* t_action, int start_frame, float* v_video, float* v_action, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return stack_pass(cfg, w, cache, ctx, n_chunks, x_video, x_action, t_video, t_action, start_frame, v_video, v_action,
+                    ws, ws_bytes, reinterpret_cast<hipStream_t>(stream), false);
+}
+
+wam_status wam_kv_append(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache, const wam_ctx_kv* ctx,
+                         const float* x_video, const float* x_action, int start_frame, void* ws, size_t ws_bytes,
+                         void* stream) {
+  wam_status st = stack_pass(cfg, w, cache, ctx, 1, x_video, x_action, nullptr, nullptr, start_frame, nullptr, nullptr,
+                             ws, ws_bytes, reinterpret_cast<hipStream_t>(stream), true);
+  if (st == WAM_OK) cache->length += geo_of(*cfg).Lq;
+  return st;
+}
+
+wam_status wam_dit_block_fwd(const wam_config* cfg, const wam_block_weights* bw, int layer, wam_kv_cache* cache,
+                             const wam_ctx_kv* ctx, float* h, const float* e6, int n_chunks, int start_frame, void* ws,
+                             size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  const Geo g = geo_of(*cfg);
+  if (layer < 0 || layer >= g.L) return fail(WAM_E_ARG, "layer %d out of range", layer);
+  if (n_chunks < 1 || n_chunks > kMaxChunks) return fail(WAM_E_SHAPE, "n_chunks must be in [1, %d]", kMaxChunks);
+  CHECK(check_block(bw, layer));
+  CHECK(check_cache(g, cache, n_chunks * g.Lq));
+  CHECK(check_ctx(g, ctx));
+  if (!h || !e6) return fail(WAM_E_ARG, "h or e6 is NULL");
+  if (start_frame < 0) return fail(WAM_E_ARG, "start_frame must be non-negative");
+  const Layout L = layout_of(g, n_chunks);
+  CHECK(check_ws(L, ws, ws_bytes));
+  Pass p{};
+  p.cfg = cfg; p.g = g; p.L = L; p.ws = ws; p.n = n_chunks; p.R = n_chunks * g.Lq; p.M = g.br * p.R; p.kv = cache;
+  p.cx = ctx; p.h = h; p.e6 = e6; p.rope = at<float2>(ws, L.rope); p.s = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(launch_rope_table(p.rope, n_chunks, g.Lq, g.Lv, cfg->frames_per_chunk, cfg->grid_h, cfg->grid_w, start_frame,
+                            g.d, cfg->rope_theta, p.s));
+  return run_block(p, *bw, layer, false);
+}
+
+wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, const float* v_action, int branches,
+                         float guidance, int n_video, int n_action, float dt_video, float dt_action, float* g_video,
+                         float* g_action, const float* prev_video, float* cos_parts, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (branches != 1 && branches != 2) return fail(WAM_E_SHAPE, "branches must be 1 or 2");
+  if (n_video < 0 || n_action < 0) return fail(WAM_E_SHAPE, "negative sizes");
+  if ((n_video && (!x_video || !v_video)) || (n_action && (!x_action || !v_action)))
+    return fail(WAM_E_ARG, "latent or velocity pointers are NULL");
+  if (prev_video && !cos_parts) return fail(WAM_E_ARG, "prev_video given without cos_parts");
+  if (!std::isfinite(guidance) || !std::isfinite(dt_video) || !std::isfinite(dt_action))
+    return fail(WAM_E_ARG, "non-finite scalar");
+  const size_t need = 256 + 64 * 3 * 4;
+  if (prev_video && (!ws || ws_bytes < need)) return fail(WAM_E_ARG, "workspace too small for the cosine partials");
+  FlowArgs fa{};
+  fa.xv = x_video; fa.xa = x_action; fa.vv = v_video; fa.va = v_action; fa.br = branches; fa.w = guidance;
+  fa.nv = n_video; fa.na = n_action; fa.dtv = dt_video; fa.dta = dt_action; fa.gv = g_video; fa.ga = g_action;
+  fa.prev = prev_video; fa.partials = prev_video ? reinterpret_cast<float*>(ws) : nullptr; fa.cos_parts = cos_parts;
+  fa.nblocks = flow_partial_blocks(n_video);
+  HIP_TRY(launch_flow_step(fa, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
+wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W, int ldw, const float* bias, void* C,
+                         int ldc, int M, int N, int K, int act, void* stream) {
+  if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
+  if (!A || !W || !C) return fail(WAM_E_ARG, "NULL operand");
+  if (M < 0 || N < 0 || K <= 0 || K % 64) return fail(WAM_E_SHAPE, "K must be a positive multiple of 64");
+  if (lda < K || ldw < K || ldc < N) return fail(WAM_E_SHAPE, "leading dimensions too small");
+  const int epu = dtype == WAM_BF16 ? 8 : 4;
+  if (lda % epu || ldw % epu) return fail(WAM_E_SHAPE, "lda/ldw must keep rows 16-byte aligned");
+  if (act != 0 && act != 1) return fail(WAM_E_ARG, "act must be 0 or 1");
+  GemmArgs ga = gemm_args(A, lda, W, ldw, bias, M, N, K);
+  ga.C = C;
+  ga.ldc = ldc;
+  HIP_TRY(launch_gemm(ga, dtype == WAM_BF16 ? DT_BF16 : DT_F32, act ? EPI_GELU : EPI_STORE,
+                      reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
+wam_status wam_op_attention(wam_dtype dtype, const void* Q, const void* K, const void* Vt, void* O, int br, int heads,
+                            int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,
+                            void* stream) {
+  if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
+  if (!Q || !K || !Vt || !O) return fail(WAM_E_ARG, "NULL operand");
+  if (head_dim != 64 && head_dim != 128) return fail(WAM_E_SHAPE, "head_dim must be 64 or 128");
+  if (br <= 0 || heads <= 0 || Lq < 0 || kv_total <= 0 || kv_base < 0) return fail(WAM_E_SHAPE, "bad sizes");
+  if (k_rows < kv_total || v_stride < kv_total || v_stride % 8) return fail(WAM_E_SHAPE, "k_rows/v_stride too small");
+  AttnArgs a{};
+  a.Q = Q; a.K = K; a.Vt = Vt; a.O = O;
+  a.q_bh_stride = (long)Lq * head_dim; a.k_bh_stride = (long)k_rows * head_dim; a.v_bh_stride = (long)head_dim * v_stride;
+  a.v_stride = v_stride; a.Lq_total = Lq; a.H = heads; a.d = head_dim; a.br = br;
+  a.kv_base = kv_base; a.chunk_q = chunk_q; a.kv_total = kv_total;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  HIP_TRY(launch_attention(a, dtype == WAM_BF16 ? DT_BF16 : DT_F32, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
+void wam_kv_reset(wam_kv_cache* cache) {
+  if (cache) cache->length = 0;
+}
+
+const char* wam_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels of the chunk-causal DiT step.
+//
+// Element types: bf16 values are carried as raw 16-bit patterns (uint16_t) in memory and
+// converted with round-to-nearest-even; the fp32 debug build of every kernel uses float.
+// Matrix products go through the 32x32 MFMA family in "k16 chunks": a chunk of 16 consecutive
+// k-values, of which lane half h (lanes 32h..32h+31) supplies elements 8h..8h+7. For bf16 that is
+// one v_mfma_f32_32x32x16_bf16; for fp32 it is eight v_mfma_f32_32x32x2_f32, the t-th consuming
+// element t of each half's eight -- the same contraction with the k-order permuted identically on
+// both operands.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wam {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (bf16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Generic element access for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+  static __device__ __forceinline__ float to_f(bf16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ bf16_t from_f(float v) { return f32_to_bf16(v); }
+};
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ float to_f(float v) { return v; }
+  static __device__ __forceinline__ float from_f(float v) { return v; }
+};
+
+// A k16 fragment: the eight elements one lane contributes to a 32x32 MFMA chunk.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> { uint4 v; };            // 8 x bf16 = 16 bytes
+template <> struct Frag<float> { uint4 v[2]; };          // 8 x f32  = 32 bytes
+
+__device__ __forceinline__ void mfma_k16(floatx16& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  bf16x8_t av = __builtin_bit_cast(bf16x8_t, a.v);
+  bf16x8_t bv = __builtin_bit_cast(bf16x8_t, b.v);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mfma_k16(floatx16& acc, const Frag<float>& a, const Frag<float>& b) {
+  const float* af = reinterpret_cast<const float*>(&a.v[0]);
+  const float* bf = reinterpret_cast<const float*>(&b.v[0]);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[t], bf[t], acc, 0, 0, 0);
+}
+
+// Pack eight fp32 values (already in k order) into a fragment.
+__device__ __forceinline__ void pack_frag(Frag<bf16_t>& f, const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void pack_frag(Frag<float>& f, const float* x) {
+  f.v[0] = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
+  f.v[1] = make_uint4(__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7]));
+}
+
+// Output layout of a 32x32 MFMA accumulator: lane l, register r holds
+// row = 8*(r/4) + 4*(l/32) + (r%4), column = l%32.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Wave-wide (64 lanes) reductions by butterfly shuffles; every lane gets the result.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum for blockDim.x = NT threads (multiple of 64); deterministic order.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red /* >= NT/64 floats of LDS */) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += red[i];
+  return s;
+}
+
+__device__ __forceinline__ float gelu_tanh_f(float x) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * x * (1.f + tanhf(c * (x + 0.044715f * x * x * x)));
+}
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.f + expf(-x)); }
+
+}  // namespace wam

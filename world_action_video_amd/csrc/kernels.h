@@ -1,0 +1,141 @@
+// Launchers of the gfx950 kernels (host-callable, no torch types). Each returns the HIP status of
+// its launch; shapes are validated by the C-ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wam {
+
+enum DType { DT_BF16 = 0, DT_F32 = 1 };
+
+// ---- GEMM: C[m][n] = sum_k A[m][k] W[n][k] (+ bias[n]) followed by an epilogue ----------------
+enum Epi {
+  EPI_STORE = 0,        // C (element type T) = acc + bias
+  EPI_GELU = 1,         // C (T) = gelu_tanh(acc + bias)
+  EPI_RESID = 2,        // H (fp32) += acc + bias
+  EPI_RESID_GATED = 3,  // H (fp32) += gate[row group][n] * (acc + bias), gate = e6[chunk][group][gi] + mod[gi]
+  EPI_ROWSEL_F32 = 4,   // fp32 output of the rows of one token group, gathered per branch (output heads)
+};
+
+struct RowMap {       // how a GEMM row maps to (branch, chunk, token group)
+  int rows_per_branch;  // n_chunks * Lq
+  int Lq, Lv;           // tokens per chunk, video tokens per chunk
+};
+
+struct GemmArgs {
+  const void* A; long lda;   // [M][K], element type T
+  const void* W; long ldw;   // [N][K], element type T (nn.Linear layout)
+  const float* bias;         // [N] or nullptr
+  void* C; long ldc;         // EPI_STORE / EPI_GELU / EPI_ROWSEL_F32 output
+  float* H; long ldh;        // EPI_RESID* fp32 residual stream
+  int M, N, K;
+  RowMap rm;
+  const float* e6;           // EPI_RESID_GATED: [n_chunks][2][6][D]
+  const float* mod;          // EPI_RESID_GATED: [6][D]
+  int gate_idx, D;
+  int sel_group;             // EPI_ROWSEL_F32: 0 = video rows, 1 = action rows
+};
+
+hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s);
+
+// ---- attention ----------------------------------------------------------------------------------
+struct AttnArgs {
+  const void* Q;      // [br][H][Lq_total][d]
+  const void* K;      // [br][H][k_rows][d]     (k_rows = row capacity of one head's key block)
+  const void* Vt;     // [br][H][d][v_stride]   (values stored key-contiguous)
+  void* O;            // [br * Lq_total][H * d] row-major
+  long q_bh_stride, k_bh_stride, v_bh_stride;   // elements between consecutive (branch, head) blocks
+  int v_stride;       // keys per row of Vt
+  int Lq_total, H, d, br;
+  int kv_base;        // keys visible to every query (cached clean chunks)
+  int chunk_q;        // queries per chunk (for the chunk-causal limit); <= 0: no chunk limit
+  int kv_total;       // total keys present (kv_base + current keys)
+  float scale_log2;   // log2(e) / sqrt(d)
+};
+hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s);
+
+// ---- row-wise kernels -----------------------------------------------------------------------------
+enum NormMode {
+  NORM_ADALN = 0,       // LN(x) (1 + scale) + shift, scale/shift from e6 (+ layer offset)
+  NORM_AFFINE = 1,      // LN(x) w + b
+  NORM_HEAD = 2,        // LN(x) (1 + head_mod[1] + e) + head_mod[0] + e
+};
+struct NormArgs {
+  const float* X;       // [M][D] fp32 residual stream
+  void* Y;              // [M][D] T
+  int M, D;
+  float eps;
+  NormMode mode;
+  RowMap rm;
+  const float* e6;      // ADALN: [n_chunks][2][6][D]; HEAD: e [n_chunks][2][D]
+  const float* mod;     // ADALN: [6][D] layer offset; HEAD: head_mod [2][D]
+  int shift_idx, scale_idx;
+  const float* w;       // AFFINE
+  const float* b;
+};
+hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s);
+
+struct QkNormArgs {
+  const void* src; long src_ld;     // rows of the projection output ([M][src_ld], T)
+  int src_col;                      // first column of this tensor in a row
+  const float* gain;                // [D]
+  void* dst;                        // head-major destination [br][H][dst_rows][d]
+  long dst_bh_stride;               // elements between consecutive (branch, head) blocks
+  int dst_row0;                     // first destination row (cache length for keys)
+  int M, D, H, d;
+  int rows_per_branch;
+  float eps;
+  const float2* rope;               // [rows_per_branch][d/2] (cos, sin) or nullptr; rows of action tokens unused
+  RowMap rm;
+};
+hipError_t launch_qk_norm_rope(const QkNormArgs& a, DType dt, hipStream_t s);
+
+struct VCacheArgs {
+  const void* src; long src_ld; int src_col;   // v = src[row][src_col + h*d + j]
+  void* dst; long dst_bh_stride; int dst_stride; int dst_col0;   // Vt[b][h][j][dst_col0 + r]
+  int rows_per_branch, br, H, d;
+};
+hipError_t launch_v_to_cache(const VCacheArgs& a, DType dt, hipStream_t s);
+
+// rotary (cos, sin) table for the video tokens of n_chunks chunks, written for every row of a branch
+hipError_t launch_rope_table(float2* table, int n_chunks, int Lq, int Lv, int frames_per_chunk, int grid_h,
+                             int grid_w, int start_frame, int head_dim, float theta, hipStream_t s);
+
+// token embedding: h[b][row] = x_video/x_action row times the patch/action linear, for every branch
+struct EmbedArgs {
+  const float* xv; const float* xa;
+  const void* pe_w; const float* pe_b; const void* ae_w; const float* ae_b;
+  float* H;
+  int n_chunks, Lv, La, P, A, D, br;
+};
+hipError_t launch_embed(const EmbedArgs& a, DType dt, hipStream_t s);
+
+// small-batch matrix-vector products for the time embedding path
+struct TimeArgs {
+  float t[16];             // [G] timesteps, passed by value (host scalars)
+  int G, freq_dim, D;
+  const void *w1, *w2, *wp; const float *b1, *b2, *bp;
+  float* emb;              // [G][freq_dim] scratch
+  float* h1;               // [G][D] scratch
+  float* e;                // [G][D] out
+  float* e6;               // [G][6D] out
+};
+hipError_t launch_time_mlp(const TimeArgs& a, DType dt, hipStream_t s);
+
+struct FlowArgs {
+  float* xv; float* xa;
+  const float* vv; const float* va;   // [br][n]
+  int br; float w;
+  int nv, na;
+  float dtv, dta;
+  float* gv; float* ga;               // guided velocities out (optional)
+  const float* prev;                  // previous guided video velocity (optional)
+  float* partials;                    // [nblocks][3] scratch
+  float* cos_parts;                   // [3] out
+  int nblocks;
+};
+hipError_t launch_flow_step(const FlowArgs& a, hipStream_t s);
+int flow_partial_blocks(int nv);
+
+}  // namespace wam

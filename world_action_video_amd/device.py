@@ -1,0 +1,130 @@
+"""Device-side buffers for the C ABI: weights, caches and workspace as torch tensors on one GPU.
+
+torch is used here only to allocate device memory and to move the seeded inputs onto it; the
+library computes everything. Weight values come from the ``synth`` package (the same values the
+CPU oracle reads), so both sides see identical bf16-representable numbers.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+import synth
+from synth.workloads import Workload, draw, global_tensors, is_matrix, layer_tensors
+
+from . import (GLOBAL_FIELDS, WAM_BF16, WAM_F32, wam_block_weights, wam_config, wam_ctx_kv, wam_kv_cache,
+               wam_weights, wam_workspace_bytes)
+
+
+def make_config(w: Workload, dtype: str = "bf16", branches: int | None = None) -> wam_config:
+    c = wam_config()
+    for f in ("dim", "heads", "head_dim", "ffn_dim", "layers", "freq_dim", "patch_dim", "action_dim",
+              "action_tokens", "frames_per_chunk", "grid_h", "grid_w", "ctx_in_dim", "ctx_text_len", "ctx_img_len"):
+        setattr(c, f, int(getattr(w, f)))
+    c.branches = int(branches if branches is not None else w.branches)
+    c.rope_theta = float(w.rope_theta)
+    c.eps = float(w.eps)
+    c.dtype = WAM_BF16 if dtype == "bf16" else WAM_F32
+    return c
+
+
+def torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_device(arr_f32: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """float32 array of bf16-representable values -> device tensor in ``dtype`` (exact)."""
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(arr_f32)
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr_f32, dtype=np.float32)).to(device)
+
+
+def _upload(w: Workload, layer: int, spec, dtype: str, device) -> torch.Tensor:
+    name = spec[0]
+    if is_matrix(name) and dtype == "bf16":
+        bits = draw(w, layer, spec, "bf16")
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(draw(w, layer, spec, "f32")).to(device)
+
+
+class DeviceModel:
+    """All weights of a workload on the GPU plus the ``wam_weights`` struct pointing at them."""
+
+    def __init__(self, w: Workload, dtype: str = "bf16", device="cuda:0", overrides=None):
+        self.w, self.dtype, self.device = w, dtype, torch.device(device)
+        self.cfg = make_config(w, dtype)
+        overrides = overrides or {}
+        self.g = {}
+        for spec in global_tensors(w):
+            self.g[spec[0]] = self._get(-1, spec, overrides)
+        self.layers = []
+        for l in range(w.layers):
+            self.layers.append({spec[0]: self._get(l, spec, overrides) for spec in layer_tensors(w)})
+        self._build_structs()
+
+    def _get(self, layer, spec, overrides):
+        key = (layer, spec[0])
+        if key in overrides:
+            arr = np.ascontiguousarray(overrides[key], dtype=np.float32)
+            if is_matrix(spec[0]):
+                return to_device(arr, self.dtype, self.device)
+            return torch.from_numpy(arr).to(self.device)
+        return _upload(self.w, layer, spec, self.dtype, self.device)
+
+    def _build_structs(self):
+        # The library reads matrices in the model dtype and every other tensor as float32.
+        want = torch_dtype(self.dtype)
+        for name, t in list(self.g.items()) + [kv for lp in self.layers for kv in lp.items()]:
+            expect = want if is_matrix(name) else torch.float32
+            if t.dtype != expect or not t.is_contiguous():
+                raise TypeError("%s: %s (contiguous=%s), the library expects %s" % (name, t.dtype, t.is_contiguous(), expect))
+        self.blocks = (wam_block_weights * self.w.layers)()
+        for l, lp in enumerate(self.layers):
+            for name, t in lp.items():
+                setattr(self.blocks[l], name, t.data_ptr())
+        self.weights = wam_weights()
+        self.weights.blocks = ctypes.cast(self.blocks, ctypes.POINTER(wam_block_weights))
+        for name in GLOBAL_FIELDS:
+            t = self.g.get(name)
+            setattr(self.weights, name, t.data_ptr() if t is not None else None)
+
+
+class DeviceCache:
+    """Self-attention KV cache [layers][br][heads][cap][d] (keys) / [..][d][cap] (values)."""
+
+    def __init__(self, w: Workload, capacity: int, dtype: str = "bf16", device="cuda:0", branches=None):
+        br = branches if branches is not None else w.branches
+        cap = (capacity + 63) // 64 * 64
+        td = torch_dtype(dtype)
+        self.k = torch.zeros((w.layers, br, w.heads, cap, w.head_dim), dtype=td, device=device)
+        self.v = torch.zeros((w.layers, br, w.heads, w.head_dim, cap), dtype=td, device=device)
+        self.c = wam_kv_cache(self.k.data_ptr(), self.v.data_ptr(), br, cap, 0)
+
+    @property
+    def length(self) -> int:
+        return self.c.length
+
+
+class DeviceCtx:
+    """Cross-attention keys/values of the condition sequence for every layer."""
+
+    def __init__(self, w: Workload, dtype: str = "bf16", device="cuda:0", branches=None):
+        br = branches if branches is not None else w.branches
+        Lc = w.ctx_len
+        stride = (Lc + 63) // 64 * 64
+        td = torch_dtype(dtype)
+        self.k = torch.zeros((w.layers, br, w.heads, Lc, w.head_dim), dtype=td, device=device)
+        self.v = torch.zeros((w.layers, br, w.heads, w.head_dim, stride), dtype=td, device=device)
+        self.c = wam_ctx_kv(self.k.data_ptr(), self.v.data_ptr(), br, Lc, stride)
+
+
+def workspace(cfg: wam_config, n_chunks: int, device="cuda:0") -> torch.Tensor:
+    nbytes = wam_workspace_bytes(cfg, n_chunks)
+    if nbytes == 0:
+        raise ValueError("invalid configuration for a workspace")
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + nbytes]
