@@ -1,0 +1,253 @@
+"""Benchmark: one flow-matching denoising step of the 40-layer chunk-causal DiT, CFG as a batch of 2.
+
+Workload (Wan2.1-14B-shaped, synthetic): width 5120, 40 heads of 128, FFN 13824, 40 layers; one chunk
+of 2 latent frames x 11 x 20 patches + 24 action tokens (464 tokens) per branch, 2 branches
+(conditional / negative prompt); KV cache of 2 clean chunks (928 tokens); 769 condition tokens
+(512 text + 257 image). A step = time-embedding MLP -> token embedding -> 40 blocks -> output heads ->
+CFG + Euler + cosine partials, i.e. every kernel of the per-step path. The condition keys/values and
+the cached chunks are built once before timing (they are per request, not per step).
+
+Prints one JSON line (see the keys below). --gpus N > 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+WORKLOAD_ID = 3
+
+
+def step_flops(w) -> dict:
+    """Algorithmic FLOPs of one step (2*M*N*K per product; attention 4*br*H*Lq*Lk*d per self/cross)."""
+    br, D, F, L, H, d = w.branches, w.dim, w.ffn_dim, w.layers, w.heads, w.head_dim
+    Lq = w.chunk_tokens
+    M = br * Lq
+    Lk = w.cache_chunks * Lq + Lq
+    gemm_layer = 2 * M * D * (3 * D + D + D + D + F + F)          # qkv, o, cross-q, cross-o, ffn1, ffn2
+    attn_layer = 4 * br * H * Lq * d * (Lk + w.ctx_len)
+    head = 2 * br * (w.video_tokens * D * w.patch_dim + w.action_tokens * D * w.action_dim)
+    time_mlp = 2 * 2 * (D * w.freq_dim + D * D + 6 * D * D)
+    return {"gemm": L * gemm_layer, "attention": L * attn_layer, "other": head + time_mlp,
+            "total": L * (gemm_layer + attn_layer) + head + time_mlp}
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str, src_hash: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha256_16") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, timed_layers: int = 1) -> dict:
+    """The oracle as it stands, timed on this host on a bounded sample: ``timed_layers`` full-width
+    blocks of the same step (both CFG branches, 928 cached + 464 current tokens, 769 condition tokens),
+    scaled to ms per 40-layer step."""
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    m = O.load_model(w, layers=list(range(timed_layers)))
+    Lq, D = w.chunk_tokens, w.dim
+    T = Lq
+    br = w.branches
+    key = synth.tensor_key(w.id, -1, "cpu-baseline")
+    h = synth.fill((br, T, D), key, "normal", 1.0)
+    ctx_k = synth.fill((br, w.ctx_len, D), key + 1, "normal", 1.0)
+    ctx_v = synth.fill((br, w.ctx_len, D), key + 2, "normal", 1.0)
+    ck = synth.fill((br, w.cache_chunks * Lq, D), key + 3, "normal", 1.0)
+    cv = synth.fill((br, w.cache_chunks * Lq, D), key + 4, "normal", 1.0)
+    e6, _ = O.per_token_time(w, m.g, [0.5], [0.5], 1, np.float32)
+    pos = O.video_positions(w, 1, w.cache_chunks * w.frames_per_chunk)
+    t0 = time.perf_counter()
+    for lp in m.layers:
+        h, _, _ = O.block_forward(w, lp, h, e6, ctx_k, ctx_v, ck, cv, 1, pos)
+    dt = time.perf_counter() - t0
+    per_layer = dt / timed_layers
+    return {"value": round(per_layer * w.layers * 1e3, 1), "unit": "ms per 40-layer CFG step (extrapolated)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": "%d full-width block(s) of the step (CFG batch 2, 928 cached + 464 current tokens, 769 "
+                      "condition tokens), NumPy fp32, %.2f s per block, scaled x%d layers; time MLP and heads "
+                      "(<0.1%% of FLOPs) not timed" % (timed_layers, per_layer, w.layers)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="run only a 1 GiB copy and launches of the dominant kernel (for rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this path runs on one GPU; --gpus %d is not supported (run with --gpus 1)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import world_action_video_amd as wam
+    from synth.workloads import WORKLOADS, draw_named
+    from world_action_video_amd.device import DeviceCache, DeviceCtx, DeviceModel, to_device, workspace
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[WORKLOAD_ID]
+    Lq, Lv, La, D = w.chunk_tokens, w.video_tokens, w.action_tokens, w.dim
+    M = w.branches * Lq
+
+    if args.counters:
+        # calibration copy (known bytes) and launches of the dominant kernel at the step's shape
+        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.mul(x, 1.0, out=y)
+        a = torch.randn((M, D), device=dev).to(torch.bfloat16)
+        wq = (torch.randn((3 * D, D), device=dev) * 0.02).to(torch.bfloat16)
+        c = torch.empty((M, 3 * D), dtype=torch.bfloat16, device=dev)
+        for _ in range(5):
+            wam.wam_op_linear(wam.WAM_BF16, a, D, wq, D, None, c, 3 * D, M, 3 * D, D, 0)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4}))
+        return
+
+    def log(msg):
+        print("[bench] %s" % msg, file=sys.stderr, flush=True)
+
+    t_setup = time.perf_counter()
+    log("uploading %s weights" % w.name)
+    model = DeviceModel(w, "bf16", dev)
+    log("weights resident (%.1f s); building condition KV and %d cached chunks" % (time.perf_counter() - t_setup,
+                                                                                  w.cache_chunks))
+    ws = workspace(model.cfg, 1, dev)
+    ctx = DeviceCtx(w, "bf16", dev)
+    txt = draw_named(w, -1, "txt")
+    img = draw_named(w, -1, "img")
+    wam.wam_ctx_build(model.cfg, model.weights, to_device(txt, "bf16", dev), to_device(img, "bf16", dev), ctx.c, ws)
+    cache = DeviceCache(w, (w.cache_chunks + 1) * Lq, "bf16", dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)  # noqa: E731
+    for c in range(w.cache_chunks):
+        wam.wam_kv_append(model.cfg, model.weights, cache.c, ctx.c, f32(draw_named(w, -1, "x1_video_%d" % c)),
+                          f32(draw_named(w, -1, "x1_action_%d" % c)), c * w.frames_per_chunk, ws)
+    assert cache.length == w.cache_chunks * Lq
+    start_frame = w.cache_chunks * w.frames_per_chunk
+    xv = f32(draw_named(w, -1, "eps_video_%d" % w.cache_chunks))
+    xa = f32(draw_named(w, -1, "eps_action_%d" % w.cache_chunks))
+    vv = torch.empty((w.branches, Lv, w.patch_dim), device=dev)
+    va = torch.empty((w.branches, La, w.action_dim), device=dev)
+    gv = torch.zeros(Lv * w.patch_dim, device=dev)
+    ga = torch.zeros(La * w.action_dim, device=dev)
+    cos = torch.zeros(3, device=dev)
+    fws = torch.empty(4096, dtype=torch.uint8, device=dev)
+    ts = synth.workloads.timesteps(w, args.steps + args.warmup)
+    nv, na = Lv * w.patch_dim, La * w.action_dim
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def step(t):
+        wam.wam_dit_stack_fwd(model.cfg, model.weights, cache.c, ctx.c, 1, xv, xa, [t], [t], start_frame, vv, va, ws)
+        wam.wam_flow_step(xv, xa, vv, va, w.branches, w.guidance, nv, na, 1.0 / 16, 1.0 / 16, gv, ga, gv, cos, fws)
+
+    log("setup done (%.1f s); warmup %d, timed %d steps" % (setup_s, args.warmup, args.steps))
+    t_first = time.perf_counter()
+    step(float(ts[0]))
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t_first) * 1e3
+    for i in range(1, args.warmup):
+        step(float(ts[i]))
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(float(ts[args.warmup + i]))
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    finite = bool(torch.isfinite(vv).all().item() and torch.isfinite(va).all().item())
+
+    # dominant kernel: the QKV projection GEMM (bf16 MFMA, M = 928, N = 15360, K = 5120), same kernel and
+    # launch configuration as in the step, timed with HIP events on the library's stream
+    y = torch.randn((M, D), device=dev).to(torch.bfloat16)
+    cq = torch.empty((M, 3 * D), dtype=torch.bfloat16, device=dev)
+    wq, bq = model.layers[0]["w_qkv"], model.layers[0]["b_qkv"]
+    for _ in range(3):
+        wam.wam_op_linear(wam.WAM_BF16, y, D, wq, D, bq, cq, 3 * D, M, 3 * D, D, 0)
+    reps = 20
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        wam.wam_op_linear(wam.WAM_BF16, y, D, wq, D, bq, cq, 3 * D, M, 3 * D, D, 0)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / reps
+    gemm_flops = 2.0 * M * 3 * D * D
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    traffic = load_traffic("gemm_qkv_bf16_928x15360x5120", source_hash(os.path.join(ROOT, "world_action_video_amd", "csrc", "gemm.hip")))
+
+    fl = step_flops(w)
+    step_tflops = fl["total"] / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "ms per DiT denoise step (40L, CFG b=2)",
+        "value": round(ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latents/features)",
+        "config": {"workload": w.name, "layers": w.layers, "dim": w.dim, "heads": w.heads, "head_dim": w.head_dim,
+                   "ffn_dim": w.ffn_dim, "branches": w.branches, "chunk_tokens": Lq, "cached_tokens": cache.length,
+                   "ctx_tokens": w.ctx_len},
+        "step_tflop": round(fl["total"] / 1e12, 3),
+        "step_tflops": round(step_tflops, 1),
+        "step_mfma_frac": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+        "first_step_ms": round(first_ms, 1),
+        "setup_s": round(setup_s, 1),
+        "outputs_finite": finite,
+        "roofline": {"kernel": "gemm_kernel<bf16,256,256,128,64,8 waves,EPI_STORE> (QKV projection, 928x15360x5120)",
+                     "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "avg_launch_us": round(gemm_ms * 1e3, 2)},
+    }
+    log("step %.3f ms; QKV GEMM %.1f us (%.1f TFLOP/s)" % (ms, gemm_ms * 1e3, gemm_tflops))
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        del model, cache, ctx
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

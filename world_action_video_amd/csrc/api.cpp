@@ -65,7 +65,7 @@ wam_status check_cfg(const wam_config* c) {
   if (c->patch_dim <= 0 || c->action_dim <= 0 || c->action_tokens < 0) return fail(WAM_E_SHAPE, "bad token sizes");
   if (c->frames_per_chunk <= 0 || c->grid_h <= 0 || c->grid_w <= 0) return fail(WAM_E_SHAPE, "bad chunk geometry");
   const int lq = c->frames_per_chunk * c->grid_h * c->grid_w + c->action_tokens;
-  if (lq % 8) return fail(WAM_E_SHAPE, "tokens per chunk (%d) must be a multiple of 8", lq);
+  if (lq % 8 || lq < 32) return fail(WAM_E_SHAPE, "tokens per chunk (%d) must be a multiple of 8 and at least 32", lq);
   if (c->ctx_text_len <= 0 || c->ctx_img_len < 0) return fail(WAM_E_SHAPE, "bad condition lengths");
   if (c->branches != 1 && c->branches != 2) return fail(WAM_E_SHAPE, "branches must be 1 or 2");
   if (!(c->eps > 0.f) || !(c->rope_theta > 0.f)) return fail(WAM_E_ARG, "eps and rope_theta must be positive");

@@ -26,7 +26,7 @@ static constexpr int ATT_BQ = 128, ATT_BKV = 64;
 __device__ __forceinline__ int swap_bits_2_3(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_kernel(AttnArgs a) {
   constexpr int EPU = 16 / sizeof(T);
   constexpr int KU = D * (int)sizeof(T) / 16;          // 16-byte units per K row (D elements)
@@ -37,11 +37,26 @@ attn_kernel(AttnArgs a) {
   constexpr int DC = D / 16;                            // k16 chunks over the head dim
   constexpr int DB = D / 32;                            // 32-row blocks of the output O^T
   __shared__ uint4 smem[2][K_UNITS + V_UNITS];
+  // LDS swizzles (16-byte units XOR a row-dependent phase) chosen so that each 16-lane pass of a
+  // fragment read (16 rows, one logical unit) covers distinct banks: rows of 256 bytes or more
+  // take phase row mod 16; 128-byte rows take (row / 2) mod 8 (row pairs share a bank line).
+  auto kswz = [](int row) { return KU >= 16 ? (row & 15) : ((row >> 1) & 7); };
+  auto vswz = [](int row) { return VU >= 16 ? (row & 15) : ((row >> 1) & 7); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int qblk = blockIdx.x * ATT_BQ;
+  // XCD-aware order: workgroup w runs on XCD w mod 8; give each XCD a contiguous range of
+  // (branch, head, query tile) items, query tiles fastest, so the tiles that stream the same keys and
+  // values share one L2.
+  const int nq = (a.Lq_total + ATT_BQ - 1) / ATT_BQ;
+  const int items = nq * a.H * a.br;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per = items >> 3, rem = items & 7;
+  if (kx >= per + (xcd < rem ? 1 : 0)) return;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
+  const int qt = item % nq, bh_i = item / nq;
+  const int h = bh_i % a.H, b = bh_i / a.H;
+  const int qblk = qt * ATT_BQ;
   const long bh = (long)b * a.H + h;
   const T* Q = reinterpret_cast<const T*>(a.Q) + bh * a.q_bh_stride;
   const T* K = reinterpret_cast<const T*>(a.K) + bh * a.k_bh_stride;
@@ -63,6 +78,9 @@ attn_kernel(AttnArgs a) {
   const int q = qblk + wave * 32 + l32;
   const bool q_ok = q < a.Lq_total;
   const int my_lim = q_ok ? limit_of(q) : 0;
+  // smallest limit among this wave's valid queries (the first one); 0 if the wave has none
+  const int q_first = qblk + wave * 32;
+  const int wave_lim = q_first < a.Lq_total ? limit_of(q_first) : 0;
 
   // Q^T fragments (B operand of S^T = K Q^T): lane (query l32, half) holds Q[q][16c + 8 half .. +8]
   Frag<T> qf[DC];
@@ -106,12 +124,12 @@ attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
       const int u = tid + 256 * i, row = u / KU, unit = u % KU;
-      smem[st][row * KU + (unit ^ (row & 7))] = rk[i];
+      smem[st][row * KU + (unit ^ kswz(row))] = rk[i];
     }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
       const int u = tid + 256 * i, row = u / VU, unit = u % VU;
-      smem[st][K_UNITS + row * VU + (unit ^ (row & 7))] = rv[i];
+      smem[st][K_UNITS + row * VU + (unit ^ vswz(row))] = rv[i];
     }
   };
 
@@ -143,26 +161,37 @@ attn_kernel(AttnArgs a) {
         uint4* dst = reinterpret_cast<uint4*>(&kf);
         const int u0 = (c * 16 + half * 8) / EPU;
 #pragma unroll
-        for (int u = 0; u < UPF; ++u) dst[u] = sk[row * KU + ((u0 + u) ^ (row & 7))];
+        for (int u = 0; u < UPF; ++u) dst[u] = sk[row * KU + ((u0 + u) ^ kswz(row))];
         mfma_k16(s[kb], kf, qf[c]);
       }
     }
-    // register e of block kb holds key key0 + 32 kb + 16 (e / 8) + 8 half + (e % 8)
+    // register e of block kb holds key key0 + 32 kb + 16 (e / 8) + 8 half + (e % 8). Limits rise with
+    // the query index, so a tile entirely below the wave's first limit needs no mask.
     float tmax = -INFINITY;
+    if (key0 + ATT_BKV <= wave_lim) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + kb * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
-        const float v = key < my_lim ? s[kb][e] * a.scale_log2 : -INFINITY;
-        s[kb][e] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int e = 0; e < 16; ++e) {
+          s[kb][e] *= a.scale_log2;
+          tmax = fmaxf(tmax, s[kb][e]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = key0 + kb * 32 + 16 * (e >> 3) + 8 * half + (e & 7);
+          const float v = key < my_lim ? s[kb][e] * a.scale_log2 : -INFINITY;
+          s[kb][e] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
-    // a query with no visible key yet keeps m = -inf; its probabilities are 0 and alpha is 1
+    // a query with no visible key yet keeps m = -inf: its probabilities and alpha are 0 and o, l stay 0
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     float psum = 0.f;
     Frag<T> pf[2][2];
@@ -173,18 +202,10 @@ attn_kernel(AttnArgs a) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = exp2f(s[kb][8 * j + e] - m_use);
+          p[e] = __builtin_amdgcn_exp2f(s[kb][8 * j + e] - m_use);
+          psum += p[e];
         }
         pack_frag(pf[kb][j], p);
-        // the running sum adds the probabilities as the product sees them
-        if constexpr (sizeof(T) == 2) {
-          const bf16_t* pb = reinterpret_cast<const bf16_t*>(&pf[kb][j].v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) psum += bf16_to_f32(pb[e]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) psum += p[e];
-        }
       }
     l_run = l_run * alpha + psum;
 #pragma unroll
@@ -200,7 +221,7 @@ attn_kernel(AttnArgs a) {
           uint4* dst = reinterpret_cast<uint4*>(&vf);
           const int u0 = (kb * 32 + 16 * j + 8 * half) / EPU;
 #pragma unroll
-          for (int u = 0; u < UPF; ++u) dst[u] = sv[row * VU + ((u0 + u) ^ (row & 7))];
+          for (int u = 0; u < UPF; ++u) dst[u] = sv[row * VU + ((u0 + u) ^ vswz(row))];
           mfma_k16(o[db], vf, pf[kb][j]);
         }
     }
@@ -232,7 +253,8 @@ attn_kernel(AttnArgs a) {
 
 template <typename T, int D>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((a.Lq_total + ATT_BQ - 1) / ATT_BQ, a.H, a.br), block(256);
+  const int items = ((a.Lq_total + ATT_BQ - 1) / ATT_BQ) * a.H * a.br;
+  const dim3 grid(8 * ((items + 7) / 8)), block(256);
   hipLaunchKernelGGL((attn_kernel<T, D>), grid, block, 0, s, a);
   return hipGetLastError();
 }

@@ -20,11 +20,16 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (bf16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two fp32 -> packed bf16 pair (low half = a), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const float2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // Generic element access for the two storage types.
@@ -62,10 +67,7 @@ __device__ __forceinline__ void mfma_k16(floatx16& acc, const Frag<float>& a, co
 
 // Pack eight fp32 values (already in k order) into a fragment.
 __device__ __forceinline__ void pack_frag(Frag<bf16_t>& f, const float* x) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
-  f.v = make_uint4(w[0], w[1], w[2], w[3]);
+  f.v = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]), pack2_bf16(x[4], x[5]), pack2_bf16(x[6], x[7]));
 }
 __device__ __forceinline__ void pack_frag(Frag<float>& f, const float* x) {
   f.v[0] = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));

@@ -8,150 +8,177 @@
 namespace wam {
 
 // ------------------------------------------------------------------------------------------------
-// LayerNorm (+ modulation): one workgroup per row, D/4 float4 per row spread over 256 threads.
+// LayerNorm (+ modulation): one wave per row (4 rows per 256-thread workgroup). The row stays in
+// registers (VPL float4 per lane); mean and variance are two wave reductions, no LDS, no barrier.
 // ------------------------------------------------------------------------------------------------
-static constexpr int NORM_MAXV = 8;   // up to D = 8192
-
-template <typename T>
+template <typename T, int VPL>
 __global__ void __launch_bounds__(256) norm_kernel(NormArgs a) {
-  __shared__ float red[4];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;
   const float4* x4 = reinterpret_cast<const float4*>(a.X + (long)row * a.D);
   const int nv = a.D / 4;
-  float4 xv[NORM_MAXV];
+  float4 xv[VPL];
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < NORM_MAXV; ++k) {
-    const int i = tid + 256 * k;
-    if (i < nv) {
-      xv[k] = x4[i];
-      s += (xv[k].x + xv[k].y) + (xv[k].z + xv[k].w);
-    }
+  for (int k = 0; k < VPL; ++k) {
+    const int i = lane + 64 * k;
+    xv[k] = i < nv ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    s += (xv[k].x + xv[k].y) + (xv[k].z + xv[k].w);
   }
-  const float mean = block_sum<256>(s, red) / (float)a.D;
+  const float mean = wave_sum(s) / (float)a.D;
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < NORM_MAXV; ++k) {
-    const int i = tid + 256 * k;
+  for (int k = 0; k < VPL; ++k) {
+    const int i = lane + 64 * k;
     if (i < nv) {
       const float d0 = xv[k].x - mean, d1 = xv[k].y - mean, d2 = xv[k].z - mean, d3 = xv[k].w - mean;
       ss += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
     }
   }
-  const float var = block_sum<256>(ss, red) / (float)a.D;
-  const float rstd = 1.f / sqrtf(var + a.eps);
+  const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)a.D + a.eps);
 
-  const float* shift = nullptr;
-  const float* scale = nullptr;
-  const float* shift2 = nullptr;
-  const float* scale2 = nullptr;
+  const float4 *sh4 = nullptr, *sc4 = nullptr, *sh24 = nullptr, *sc24 = nullptr;
   if (a.mode != NORM_AFFINE) {
     const int rb = row % a.rm.rows_per_branch;
     const int ch = rb / a.rm.Lq, grp = (rb % a.rm.Lq) < a.rm.Lv ? 0 : 1;
     if (a.mode == NORM_ADALN) {
       const float* e6 = a.e6 + (long)(ch * 2 + grp) * 6 * a.D;
-      shift = e6 + (long)a.shift_idx * a.D;
-      scale = e6 + (long)a.scale_idx * a.D;
-      shift2 = a.mod + (long)a.shift_idx * a.D;
-      scale2 = a.mod + (long)a.scale_idx * a.D;
+      sh4 = reinterpret_cast<const float4*>(e6 + (long)a.shift_idx * a.D);
+      sc4 = reinterpret_cast<const float4*>(e6 + (long)a.scale_idx * a.D);
+      sh24 = reinterpret_cast<const float4*>(a.mod + (long)a.shift_idx * a.D);
+      sc24 = reinterpret_cast<const float4*>(a.mod + (long)a.scale_idx * a.D);
     } else {  // NORM_HEAD: e [n][2][D] + head_mod [2][D]
       const float* e = a.e6 + (long)(ch * 2 + grp) * a.D;
-      shift = e;
-      scale = e;
-      shift2 = a.mod;
-      scale2 = a.mod + a.D;
+      sh4 = sc4 = reinterpret_cast<const float4*>(e);
+      sh24 = reinterpret_cast<const float4*>(a.mod);
+      sc24 = reinterpret_cast<const float4*>(a.mod + a.D);
     }
   }
   T* y = reinterpret_cast<T*>(a.Y) + (long)row * a.D;
 #pragma unroll
-  for (int k = 0; k < NORM_MAXV; ++k) {
-    const int i = tid + 256 * k;
+  for (int k = 0; k < VPL; ++k) {
+    const int i = lane + 64 * k;
     if (i >= nv) continue;
-    float v[4] = {(xv[k].x - mean) * rstd, (xv[k].y - mean) * rstd, (xv[k].z - mean) * rstd, (xv[k].w - mean) * rstd};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int col = 4 * i + c;
-      if (a.mode == NORM_AFFINE) {
-        v[c] = v[c] * a.w[col] + a.b[col];
-      } else {
-        const float sh = shift[col] + shift2[col];
-        const float sc = scale[col] + scale2[col];
-        v[c] = v[c] * (1.f + sc) + sh;
-      }
+    float4 v = make_float4((xv[k].x - mean) * rstd, (xv[k].y - mean) * rstd, (xv[k].z - mean) * rstd,
+                           (xv[k].w - mean) * rstd);
+    if (a.mode == NORM_AFFINE) {
+      const float4 w = reinterpret_cast<const float4*>(a.w)[i], b = reinterpret_cast<const float4*>(a.b)[i];
+      v = make_float4(v.x * w.x + b.x, v.y * w.y + b.y, v.z * w.z + b.z, v.w * w.w + b.w);
+    } else {
+      const float4 p = sh4[i], q = sh24[i], r = sc4[i], t = sc24[i];
+      v = make_float4(v.x * (1.f + (r.x + t.x)) + (p.x + q.x), v.y * (1.f + (r.y + t.y)) + (p.y + q.y),
+                      v.z * (1.f + (r.z + t.z)) + (p.z + q.z), v.w * (1.f + (r.w + t.w)) + (p.w + q.w));
     }
     if constexpr (sizeof(T) == 2) {
-      const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-      reinterpret_cast<uint2*>(y)[i] = make_uint2(lo, hi);
+      reinterpret_cast<uint2*>(y)[i] = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
     } else {
-      reinterpret_cast<float4*>(y)[i] = make_float4(v[0], v[1], v[2], v[3]);
+      reinterpret_cast<float4*>(y)[i] = v;
     }
   }
+}
+
+template <typename T>
+static hipError_t launch_norm_t(const NormArgs& a, hipStream_t s) {
+  const dim3 grid((a.M + 3) / 4), block(256);
+  const int vpl = (a.D / 4 + 63) / 64;
+  if (vpl <= 4) hipLaunchKernelGGL((norm_kernel<T, 4>), grid, block, 0, s, a);
+  else if (vpl <= 8) hipLaunchKernelGGL((norm_kernel<T, 8>), grid, block, 0, s, a);
+  else if (vpl <= 20) hipLaunchKernelGGL((norm_kernel<T, 20>), grid, block, 0, s, a);
+  else if (vpl <= 32) hipLaunchKernelGGL((norm_kernel<T, 32>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  if (a.D % 4 || a.D > 4 * 256 * NORM_MAXV) return hipErrorInvalidValue;
-  if (dt == DT_BF16) hipLaunchKernelGGL(norm_kernel<bf16_t>, dim3(a.M), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(norm_kernel<float>, dim3(a.M), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (a.D % 4 || a.D > 8192) return hipErrorInvalidValue;
+  return dt == DT_BF16 ? launch_norm_t<bf16_t>(a, s) : launch_norm_t<float>(a, s);
 }
 
 // ------------------------------------------------------------------------------------------------
 // q/k RMSNorm over the full width + rotary embedding of video rows + scatter to head-major rows.
-// One workgroup per row; thread t handles channel pairs (2p, 2p+1), p = t + 256 k.
+// One wave per row; each lane owns groups of 8 consecutive channels (16-byte loads and stores; a
+// group never straddles a head since the head dim is a multiple of 8).
 // ------------------------------------------------------------------------------------------------
-static constexpr int QK_MAXP = 16;   // up to D = 8192
-
-template <typename T>
+template <typename T, int GPL>
 __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkNormArgs a) {
-  __shared__ float red[4];
-  const int row = blockIdx.x, tid = threadIdx.x;
+  constexpr int EPU = 16 / sizeof(T);            // elements per 16-byte unit
+  constexpr int UPG = 8 / EPU;                   // units per group of 8 channels
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.M) return;
   const T* src = reinterpret_cast<const T*>(a.src) + (long)row * a.src_ld + a.src_col;
-  const int np = a.D / 2;
-  float x0[QK_MAXP], x1[QK_MAXP];
+  const int ng = a.D / 8;
+  float x[GPL][8];
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < QK_MAXP; ++k) {
-    const int p = tid + 256 * k;
-    if (p < np) {
-      x0[k] = Elem<T>::load(src + 2 * p);
-      x1[k] = Elem<T>::load(src + 2 * p + 1);
-      ss += x0[k] * x0[k] + x1[k] * x1[k];
+  for (int k = 0; k < GPL; ++k) {
+    const int gi = lane + 64 * k;
+    if (gi < ng) {
+      uint4 u[UPG];
+#pragma unroll
+      for (int q = 0; q < UPG; ++q) u[q] = reinterpret_cast<const uint4*>(src + gi * 8)[q];
+      const T* e = reinterpret_cast<const T*>(u);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        x[k][c] = Elem<T>::to_f(e[c]);
+        ss += x[k][c] * x[k][c];
+      }
     }
   }
-  const float ms = block_sum<256>(ss, red) / (float)a.D;
-  const float rstd = 1.f / sqrtf(ms + a.eps);
+  const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)a.D + a.eps);
   const int b = row / a.rows_per_branch, rb = row % a.rows_per_branch;
   const bool video = (rb % a.rm.Lq) < a.rm.Lv;
   const int half_d = a.d / 2;
   T* dst = reinterpret_cast<T*>(a.dst);
 #pragma unroll
-  for (int k = 0; k < QK_MAXP; ++k) {
-    const int p = tid + 256 * k;
-    if (p >= np) continue;
-    float y0 = x0[k] * rstd * a.gain[2 * p];
-    float y1 = x1[k] * rstd * a.gain[2 * p + 1];
-    const int hh = (2 * p) / a.d, j = p % half_d;
+  for (int k = 0; k < GPL; ++k) {
+    const int gi = lane + 64 * k;
+    if (gi >= ng) continue;
+    const int ch0 = gi * 8;                       // first channel of the group
+    const int hh = ch0 / a.d, j0 = (ch0 % a.d) / 2;
+    float y[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) y[c] = x[k][c] * rstd * a.gain[ch0 + c];
     if (a.rope && video) {
-      const float2 cs = a.rope[(long)rb * half_d + j];
-      const float r0 = y0 * cs.x - y1 * cs.y;
-      const float r1 = y0 * cs.y + y1 * cs.x;
-      y0 = r0;
-      y1 = r1;
+      const float2* cs = a.rope + (long)rb * half_d + j0;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const float2 t = cs[pp];
+        const float r0 = y[2 * pp] * t.x - y[2 * pp + 1] * t.y;
+        const float r1 = y[2 * pp] * t.y + y[2 * pp + 1] * t.x;
+        y[2 * pp] = r0;
+        y[2 * pp + 1] = r1;
+      }
     }
-    T* o = dst + ((long)b * a.H + hh) * a.dst_bh_stride + (long)(a.dst_row0 + rb) * a.d + 2 * j;
-    o[0] = Elem<T>::from_f(y0);
-    o[1] = Elem<T>::from_f(y1);
+    T* o = dst + ((long)b * a.H + hh) * a.dst_bh_stride + (long)(a.dst_row0 + rb) * a.d + 2 * j0;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint4*>(o) = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
+                                                pack2_bf16(y[4], y[5]), pack2_bf16(y[6], y[7]));
+    } else {
+      reinterpret_cast<float4*>(o)[0] = make_float4(y[0], y[1], y[2], y[3]);
+      reinterpret_cast<float4*>(o)[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
   }
+}
+
+template <typename T>
+static hipError_t launch_qk_t(const QkNormArgs& a, hipStream_t s) {
+  const dim3 grid((a.M + 3) / 4), block(256);
+  const int gpl = (a.D / 8 + 63) / 64;
+  if (gpl <= 2) hipLaunchKernelGGL((qk_norm_rope_kernel<T, 2>), grid, block, 0, s, a);
+  else if (gpl <= 4) hipLaunchKernelGGL((qk_norm_rope_kernel<T, 4>), grid, block, 0, s, a);
+  else if (gpl <= 10) hipLaunchKernelGGL((qk_norm_rope_kernel<T, 10>), grid, block, 0, s, a);
+  else if (gpl <= 16) hipLaunchKernelGGL((qk_norm_rope_kernel<T, 16>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_qk_norm_rope(const QkNormArgs& a, DType dt, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  if (a.D % 2 || a.D > 2 * 256 * QK_MAXP) return hipErrorInvalidValue;
-  if (dt == DT_BF16) hipLaunchKernelGGL(qk_norm_rope_kernel<bf16_t>, dim3(a.M), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(qk_norm_rope_kernel<float>, dim3(a.M), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (a.D % 8 || a.D > 8192 || a.d % 8) return hipErrorInvalidValue;
+  return dt == DT_BF16 ? launch_qk_t<bf16_t>(a, s) : launch_qk_t<float>(a, s);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -233,37 +260,89 @@ hipError_t launch_rope_table(float2* table, int n_chunks, int Lq, int Lv, int Fc
 
 // ------------------------------------------------------------------------------------------------
 // Token embedding: per branch b and row r of chunk c, h = x W^T + bias with the patch linear for
-// video rows and the action linear for action rows. One thread per output column.
+// video rows and the action linear for action rows. A workgroup computes 16 rows x 256 columns:
+// the 16 input rows sit in LDS, each thread streams one weight row once and serves all 16 rows.
 // ------------------------------------------------------------------------------------------------
-template <typename T>
+static constexpr int EMB_ROWS = 16;
+
+// PC / AC > 0: compile-time patch / action widths (weights held in registers); 0: any width.
+template <typename T, int PC, int AC>
 __global__ void __launch_bounds__(256) embed_kernel(EmbedArgs a) {
-  extern __shared__ float xrow[];
-  const int rb = blockIdx.x, Lq = a.Lv + a.La;
-  const int ch = rb / Lq, loc = rb % Lq;
-  const bool video = loc < a.Lv;
-  const int K = video ? a.P : a.A;
-  const float* x = video ? a.xv + ((long)ch * a.Lv + loc) * a.P : a.xa + ((long)ch * a.La + (loc - a.Lv)) * a.A;
-  for (int k = threadIdx.x; k < K; k += blockDim.x) xrow[k] = x[k];
-  __syncthreads();
-  const T* Wm = reinterpret_cast<const T*>(video ? a.pe_w : a.ae_w);
-  const float* bias = video ? a.pe_b : a.ae_b;
-  const int R = a.n_chunks * Lq;
-  for (int n = blockIdx.y * blockDim.x + threadIdx.x; n < a.D; n += gridDim.y * blockDim.x) {
-    float acc = 0.f;
-    const T* wr = Wm + (long)n * K;
-    for (int k = 0; k < K; ++k) acc += xrow[k] * Elem<T>::load(wr + k);
-    acc += bias[n];
-    for (int b = 0; b < a.br; ++b) a.H[((long)b * R + rb) * a.D + n] = acc;
+  extern __shared__ float xs[];                      // [EMB_ROWS][Kmax]
+  const int Lq = a.Lv + a.La, R = a.n_chunks * Lq;
+  const int P = PC > 0 ? PC : a.P, A = AC > 0 ? AC : a.A;
+  const int Kmax = P > A ? P : A;
+  const int r0 = blockIdx.x * EMB_ROWS;
+  for (int e = threadIdx.x; e < EMB_ROWS * Kmax; e += 256) {
+    const int rr = e / Kmax, k = e % Kmax, rb = r0 + rr;
+    float v = 0.f;
+    if (rb < R) {
+      const int ch = rb / Lq, loc = rb % Lq;
+      if (loc < a.Lv) { if (k < P) v = a.xv[((long)ch * a.Lv + loc) * P + k]; }
+      else if (k < A) v = a.xa[((long)ch * a.La + (loc - a.Lv)) * A + k];
+    }
+    xs[e] = v;
   }
+  __syncthreads();
+  const int n = blockIdx.y * 256 + threadIdx.x;
+  if (n >= a.D) return;
+  const T* wpr = reinterpret_cast<const T*>(a.pe_w) + (long)n * P;
+  const T* war = reinterpret_cast<const T*>(a.ae_w) + (long)n * A;
+  const float bv = a.pe_b[n], ba = a.ae_b[n];
+  if constexpr (PC > 0 && AC > 0) {
+    float wv[PC], wa[AC];
+#pragma unroll
+    for (int k = 0; k < PC; ++k) wv[k] = Elem<T>::load(wpr + k);
+#pragma unroll
+    for (int k = 0; k < AC; ++k) wa[k] = Elem<T>::load(war + k);
+    for (int rr = 0; rr < EMB_ROWS; ++rr) {
+      const int rb = r0 + rr;
+      if (rb >= R) break;
+      const float* x = xs + rr * Kmax;
+      float acc = 0.f;
+      if ((rb % Lq) < a.Lv) {
+#pragma unroll
+        for (int k = 0; k < PC; ++k) acc += x[k] * wv[k];
+        acc += bv;
+      } else {
+#pragma unroll
+        for (int k = 0; k < AC; ++k) acc += x[k] * wa[k];
+        acc += ba;
+      }
+      for (int b = 0; b < a.br; ++b) a.H[((long)b * R + rb) * a.D + n] = acc;
+    }
+  } else {
+    for (int rr = 0; rr < EMB_ROWS; ++rr) {
+      const int rb = r0 + rr;
+      if (rb >= R) break;
+      const float* x = xs + rr * Kmax;
+      float acc = 0.f;
+      if ((rb % Lq) < a.Lv) {
+        for (int k = 0; k < P; ++k) acc += x[k] * Elem<T>::load(wpr + k);
+        acc += bv;
+      } else {
+        for (int k = 0; k < A; ++k) acc += x[k] * Elem<T>::load(war + k);
+        acc += ba;
+      }
+      for (int b = 0; b < a.br; ++b) a.H[((long)b * R + rb) * a.D + n] = acc;
+    }
+  }
+}
+
+template <typename T>
+static void launch_embed_t(const EmbedArgs& a, dim3 grid, size_t sh, hipStream_t s) {
+  if (a.P == 64 && a.A == 8) hipLaunchKernelGGL((embed_kernel<T, 64, 8>), grid, dim3(256), sh, s, a);
+  else hipLaunchKernelGGL((embed_kernel<T, 0, 0>), grid, dim3(256), sh, s, a);
 }
 
 hipError_t launch_embed(const EmbedArgs& a, DType dt, hipStream_t s) {
   const int R = a.n_chunks * (a.Lv + a.La);
   if (R <= 0) return hipSuccess;
-  const dim3 grid(R, (a.D + 255) / 256);
-  const size_t sh = sizeof(float) * (size_t)(a.P > a.A ? a.P : a.A);
-  if (dt == DT_BF16) hipLaunchKernelGGL(embed_kernel<bf16_t>, grid, dim3(256), sh, s, a);
-  else hipLaunchKernelGGL(embed_kernel<float>, grid, dim3(256), sh, s, a);
+  const dim3 grid((R + EMB_ROWS - 1) / EMB_ROWS, (a.D + 255) / 256);
+  const size_t sh = sizeof(float) * EMB_ROWS * (size_t)(a.P > a.A ? a.P : a.A);
+  if (sh > 48 * 1024) return hipErrorInvalidValue;
+  if (dt == DT_BF16) launch_embed_t<bf16_t>(a, grid, sh, s);
+  else launch_embed_t<float>(a, grid, sh, s);
   return hipGetLastError();
 }
 
@@ -328,11 +407,70 @@ __global__ void __launch_bounds__(256) gemv_kernel(const T* W, const float* bias
   }
 }
 
+// NR output rows per wave share each load of x; used for the common small batches (G <= 4).
+template <typename T, int G, int NR>
+__global__ void __launch_bounds__(256) gemv_rows_kernel(const T* W, const float* bias, const float* x, float* y, int N,
+                                                        int K, int silu_in, int silu_out) {
+  constexpr int EPU = 16 / sizeof(T);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * NR;
+  if (n0 >= N) return;
+  float acc[NR][G];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[r][g] = 0.f;
+  for (int k0 = lane * EPU; k0 < K; k0 += 64 * EPU) {
+    float xv[G][EPU];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float4* xp = reinterpret_cast<const float4*>(x + (long)g * K + k0);
+#pragma unroll
+      for (int q = 0; q < EPU / 4; ++q) {
+        const float4 t = xp[q];
+        xv[g][4 * q] = t.x; xv[g][4 * q + 1] = t.y; xv[g][4 * q + 2] = t.z; xv[g][4 * q + 3] = t.w;
+      }
+      if (silu_in) {
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) xv[g][e] = silu_f(xv[g][e]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (n0 + r >= N) break;
+      const uint4 raw = *reinterpret_cast<const uint4*>(W + (long)(n0 + r) * K + k0);
+      const T* we = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        const float wv = Elem<T>::to_f(we[e]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[r][g] += wv * xv[g][e];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float v = wave_sum(acc[r][g]);
+      if (lane == 0 && n0 + r < N) {
+        v += bias[n0 + r];
+        if (silu_out) v = silu_f(v);
+        y[(long)g * N + n0 + r] = v;
+      }
+    }
+  }
+}
+
 template <typename T>
 static void launch_gemv(const void* W, const float* b, const float* x, float* y, int N, int K, int G, int si, int so,
                         hipStream_t s) {
-  hipLaunchKernelGGL(gemv_kernel<T>, dim3((N + 3) / 4), dim3(256), 0, s, reinterpret_cast<const T*>(W), b, x, y, N, K, G,
-                     si, so);
+  const T* w = reinterpret_cast<const T*>(W);
+  constexpr int NR = 8;
+  const dim3 grid((N + 4 * NR - 1) / (4 * NR));
+  if (G == 2) hipLaunchKernelGGL((gemv_rows_kernel<T, 2, NR>), grid, dim3(256), 0, s, w, b, x, y, N, K, si, so);
+  else if (G == 4) hipLaunchKernelGGL((gemv_rows_kernel<T, 4, NR>), grid, dim3(256), 0, s, w, b, x, y, N, K, si, so);
+  else hipLaunchKernelGGL(gemv_kernel<T>, dim3((N + 3) / 4), dim3(256), 0, s, w, b, x, y, N, K, G, si, so);
 }
 
 hipError_t launch_time_mlp(const TimeArgs& a, DType dt, hipStream_t s) {
