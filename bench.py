@@ -235,7 +235,7 @@ def main():
         "first_step_ms": round(first_ms, 1),
         "setup_s": round(setup_s, 1),
         "outputs_finite": finite,
-        "roofline": {"kernel": "gemm_kernel<bf16,256,256,128,64,8 waves,EPI_STORE> (QKV projection, 928x15360x5120)",
+        "roofline": {"kernel": "gemm4_kernel<EPI_STORE> (bf16 256x256 tile, 4 waves; QKV projection, 928x15360x5120)",
                      "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2)},

@@ -186,9 +186,13 @@ wam_status wam_flow_step(float *x_video, float *x_action, const float *v_video, 
  *
  * Linear layer ([ARCH] §2.3: every projection of the block): C[m][n] = act(sum_k A[m][k] W[n][k] +
  * bias[n]) with A [M][lda], W [N][ldw], C [M][ldc] in `dtype`; bias float [N] or NULL; act 0 = none,
- * 1 = GELU (tanh approximation, the FFN's activation). K must be a multiple of 64. */
+ * 1 = GELU (tanh approximation, the FFN's activation). K must be a multiple of 64.
+ * ws / ws_bytes: optional device scratch (256-byte aligned) for split-K partial products; with
+ * NULL, or too little room, the product runs unsplit. A split product sums its fp32 partials in a
+ * fixed order, so results are deterministic, but they may differ from the unsplit product in the
+ * last bits. The stack and block calls use the split-K region of their own workspace. */
 wam_status wam_op_linear(wam_dtype dtype, const void *A, int lda, const void *W, int ldw, const float *bias, void *C,
-                         int ldc, int M, int N, int K, int act, void *stream);
+                         int ldc, int M, int N, int K, int act, void *ws, size_t ws_bytes, void *stream);
 
 /* Attention ([ARCH] §2.3 causal self-attention and cross-attention; [HYPER] 方法 mask):
  * for branch b, head h, query q < Lq: softmax over keys j < limit(q) of (Q.K_j) / sqrt(head_dim), times V,

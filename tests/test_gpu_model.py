@@ -160,20 +160,26 @@ def test_run_to_run_bitwise_determinism(gpu, tiny_oracle):
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
-def test_cfg_batch_equals_two_single_branch_calls(gpu, tiny_oracle):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cfg_batch_equals_two_single_branch_calls(gpu, tiny_oracle, dtype):
+    """CFG as batch 2 computes each branch exactly as a one-branch call would. Every row of the
+    step is independent of the other branch, so the fp32 path (one kernel configuration for any row
+    count) must agree bit for bit. In bf16 the row count picks the product kernel and may split a
+    product over K (different fp32 summation order, then bf16 rounding), so there the two agree to
+    within a few bf16 roundings: relative L2 <= 5e-3, a quarter of the oracle bar."""
     w, _, _ = tiny_oracle
     x1v, x1a, epv, epa = tiny_inputs(w)
-    rig2 = Rig(w, "bf16", gpu)
+    rig2 = Rig(w, dtype, gpu)
     dc = rig2.cache()
     rig2.append(dc, x1v[0], x1a[0], 0)
     both = rig2.step(dc, 1, epv[1], epa[1], [0.3], [0.3], w.frames_per_chunk)
     w1 = w.with_(branches=1)
     for b in range(2):
-        m1 = DeviceModel(w1, "bf16", gpu)
+        m1 = DeviceModel(w1, dtype, gpu)
         ws = workspace(m1.cfg, 1, gpu)
-        ctx1 = DeviceCtx(w1, "bf16", gpu)
-        wam.wam_ctx_build(m1.cfg, m1.weights, to_device(rig2.txt[b:b + 1], "bf16", gpu), None, ctx1.c, ws)
-        c1 = DeviceCache(w1, 2 * w.chunk_tokens, "bf16", gpu)
+        ctx1 = DeviceCtx(w1, dtype, gpu)
+        wam.wam_ctx_build(m1.cfg, m1.weights, to_device(rig2.txt[b:b + 1], dtype, gpu), None, ctx1.c, ws)
+        c1 = DeviceCache(w1, 2 * w.chunk_tokens, dtype, gpu)
         f32 = rig2.f32
         wam.wam_kv_append(m1.cfg, m1.weights, c1.c, ctx1.c, f32(x1v[0]), f32(x1a[0]), 0, ws)
         vv = torch.empty((1, w.video_tokens, w.patch_dim), device=gpu)
@@ -181,7 +187,13 @@ def test_cfg_batch_equals_two_single_branch_calls(gpu, tiny_oracle):
         wam.wam_dit_stack_fwd(m1.cfg, m1.weights, c1.c, ctx1.c, 1, f32(epv[1]), f32(epa[1]), [0.3], [0.3],
                               w.frames_per_chunk, vv, va, ws)
         torch.cuda.synchronize()
-        assert np.array_equal(vv.cpu().numpy()[0], both[0][b]) and np.array_equal(va.cpu().numpy()[0], both[1][b])
+        gv, ga = vv.cpu().numpy()[0], va.cpu().numpy()[0]
+        if dtype == "f32":
+            assert np.array_equal(gv, both[0][b]) and np.array_equal(ga, both[1][b])
+        else:
+            ev, ea = rel_l2(gv, both[0][b]), rel_l2(ga, both[1][b])
+            print("branch", b, "rel-L2 video %.2e action %.2e" % (ev, ea), flush=True)
+            assert ev <= 5e-3 and ea <= 5e-3
 
 
 def test_flow_step_matches_oracle(gpu):

@@ -35,14 +35,24 @@ def host(t):
     return t.float().cpu().numpy()
 
 
-LINEAR_CASES = [(1, 64, 64), (67, 200, 128), (300, 384, 512), (928, 1024, 256), (130, 96, 1024)]
+LINEAR_CASES = [(1, 64, 64), (67, 200, 128), (300, 384, 512), (928, 1024, 256), (130, 96, 1024), (300, 520, 1024),
+                (257, 260, 2048)]
+
+
+def split_ws(gpu, M, N):
+    """Scratch for up to four split-K partial products of an [M][N] output."""
+    return torch.empty(4 * M * N * 4 + 256, dtype=torch.uint8, device=gpu)[:4 * M * N * 4]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("M,N,K", LINEAR_CASES)
 @pytest.mark.parametrize("act", [0, 1])
-def test_op_linear_small(gpu, dtype, M, N, K, act):
-    print("linear", dtype, M, N, K, act, flush=True)
+@pytest.mark.parametrize("split", [False, True])
+def test_op_linear_small(gpu, dtype, M, N, K, act, split):
+    """With a workspace, bf16 products of fewer than 128 256x256 tiles split over K (M, N >= 256)."""
+    if split and dtype == "f32":
+        pytest.skip("split-K serves the bf16 path only")
+    print("linear", dtype, M, N, K, act, split, flush=True)
     a = draw((M, K), "a%d_%d_%d" % (M, N, K))
     w = draw((N, K), "w%d_%d_%d" % (M, N, K), 0.05)
     b = draw((N,), "b%d" % N, 0.1)
@@ -53,7 +63,7 @@ def test_op_linear_small(gpu, dtype, M, N, K, act):
     A, W = to_device(a, dtype, gpu), to_device(w, dtype, gpu)
     B = torch.from_numpy(b).to(gpu)
     C = torch.full((M, N), float("nan"), dtype=A.dtype, device=gpu)
-    wam.wam_op_linear(dt, A, K, W, K, B, C, N, M, N, K, act)
+    wam.wam_op_linear(dt, A, K, W, K, B, C, N, M, N, K, act, ws=split_ws(gpu, M, N) if split else None)
     torch.cuda.synchronize()
     out = host(C)
     if dtype == "bf16":
@@ -62,19 +72,28 @@ def test_op_linear_small(gpu, dtype, M, N, K, act):
         assert rel_l2(out, ref) <= 1e-5
 
 
-@pytest.mark.parametrize("M,N,K", [(928, 15360, 5120), (928, 5120, 13824), (1538, 5120, 1536), (2688, 5120, 5120)])
-def test_op_linear_full_size_sampled(gpu, M, N, K):
-    """The step's real projection shapes in bf16, checked on 4096 sampled outputs computed one by one."""
-    print("linear-full", M, N, K, flush=True)
+@pytest.mark.parametrize("M,N,K,split", [(928, 15360, 5120, False), (928, 5120, 13824, False), (928, 5120, 13824, True),
+                                         (928, 5120, 5120, True), (464, 15360, 5120, True), (1538, 5120, 1536, False),
+                                         (2688, 5120, 5120, False)])
+def test_op_linear_full_size_sampled(gpu, M, N, K, split):
+    """The step's real projection shapes in bf16 (split over K as the block splits them when a
+    workspace is given), checked on 4096 sampled outputs computed one by one."""
+    print("linear-full", M, N, K, split, flush=True)
     a = draw((M, K), "fa%d_%d" % (M, K))
     w = draw((N, K), "fw%d_%d" % (N, K), 0.02)
     b = draw((N,), "fb%d" % N, 0.02)
     A, W = to_device(a, "bf16", gpu), to_device(w, "bf16", gpu)
     B = torch.from_numpy(b).to(gpu)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=gpu)
-    wam.wam_op_linear(wam.WAM_BF16, A, K, W, K, B, C, N, M, N, K, 0)
+    ws = split_ws(gpu, M, N) if split else None
+    wam.wam_op_linear(wam.WAM_BF16, A, K, W, K, B, C, N, M, N, K, 0, ws=ws)
     torch.cuda.synchronize()
     out = host(C)
+    if split:   # the partials are summed in a fixed order: a second run is bit-identical
+        C2 = torch.empty_like(C)
+        wam.wam_op_linear(wam.WAM_BF16, A, K, W, K, B, C2, N, M, N, K, 0, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(C, C2)
     rng = np.random.default_rng(7)
     rows = np.concatenate([rng.integers(0, M, 4000), [0, M - 1] * 48])
     cols = np.concatenate([rng.integers(0, N, 4000), [0, N - 1, N - 1, 0] * 24])

@@ -83,7 +83,7 @@ def load(path: str = LIB_PATH):
         "wam_kv_append": (I, [CFG, W, KV, CX, P, P, I, P, S, P]),
         "wam_dit_block_fwd": (I, [CFG, ctypes.POINTER(wam_block_weights), I, KV, CX, P, P, I, I, P, S, P]),
         "wam_flow_step": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P, S, P]),
-        "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P]),
+        "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P]),
         "wam_kv_reset": (None, [KV]),
         "wam_last_error": (ctypes.c_char_p, []),
@@ -167,9 +167,11 @@ def wam_flow_step(x_video, x_action, v_video, v_action, branches, guidance, n_vi
                                 _stream(stream)))
 
 
-def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, stream=None):
+def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, ws=None, stream=None):
+    """``ws``: optional device scratch tensor for split-K partial products (None: no split)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().wam_op_linear(dtype, _ptr(A), lda, _ptr(W), ldw, _ptr(bias), _ptr(C), ldc, M, N, K, act,
-                                _stream(stream)))
+                                _ptr(ws), nbytes, _stream(stream)))
 
 
 def wam_op_attention(dtype, Q, K, Vt, O, br, heads, head_dim, Lq, k_rows, v_stride, kv_base, chunk_q, kv_total,

@@ -2,6 +2,7 @@
 // Every check happens before the first launch, so a non-OK status means nothing was enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -75,7 +76,8 @@ wam_status check_cfg(const wam_config* c) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t h, y, qkv, qh, attn, ffn, rope, emb, h1, e, e6, partials, ctx_a, ctx_b, total;
+  size_t h, y, qkv, qh, attn, ffn, rope, emb, h1, e, e6, partials, ctx_a, ctx_b, part, total;
+  long part_elems;   // fp32 capacity of the split-K partial products
 };
 
 Layout layout_of(const Geo& g, int n) {
@@ -100,7 +102,11 @@ Layout layout_of(const Geo& g, int n) {
   const size_t cb = align256((size_t)g.br * g.Lc * g.D * g.esz);
   L.ctx_a = 0;
   L.ctx_b = cb;
-  L.total = stack_total > 2 * cb ? stack_total : 2 * cb;
+  // split-K partial products (up to 4 splits of the widest D-column product), clear of both uses above
+  const size_t Mmax = std::max(M, (size_t)g.br * g.Lc);
+  L.part = align256(std::max(stack_total, 2 * cb));
+  L.part_elems = (long)(4 * Mmax * g.D);
+  L.total = L.part + align256((size_t)L.part_elems * 4);
   return L;
 }
 
@@ -174,10 +180,12 @@ struct Pass {   // everything one pass needs
 
 RowMap rowmap(const Pass& p) { return RowMap{p.R, p.g.Lq, p.g.Lv}; }
 
-GemmArgs gemm_args(const void* A, long lda, const void* W, long ldw, const void* bias, int M, int N, int K) {
+GemmArgs gemm_args(const void* A, long lda, const void* W, long ldw, const void* bias, int M, int N, int K,
+                   float* part = nullptr, long part_elems = 0) {
   GemmArgs a{};
   a.A = A; a.lda = lda; a.W = W; a.ldw = ldw; a.bias = reinterpret_cast<const float*>(bias);
   a.M = M; a.N = N; a.K = K;
+  a.part = part; a.part_elems = part_elems;
   return a;
 }
 
@@ -197,6 +205,8 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   void* vc = layer_ptr<void>(p.kv->v, cache_layer, l, g.esz);
   const int len = p.kv->length;
   const float* mod = reinterpret_cast<const float*>(bw.mod);
+  float* part = at<float>(p.ws, p.L.part);
+  const long part_n = p.L.part_elems;
 
   // (1) y = LN(h) (1 + scale1) + shift1
   NormArgs na{};
@@ -207,7 +217,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   {
     const int col0 = kv_only ? g.D : 0;
     GemmArgs ga = gemm_args(y, g.D, reinterpret_cast<const char*>(bw.w_qkv) + (size_t)col0 * g.D * g.esz, g.D,
-                            reinterpret_cast<const float*>(bw.b_qkv) + col0, p.M, 3 * g.D - col0, g.D);
+                            reinterpret_cast<const float*>(bw.b_qkv) + col0, p.M, 3 * g.D - col0, g.D, part, part_n);
     ga.C = reinterpret_cast<char*>(qkv) + (size_t)col0 * g.esz;
     ga.ldc = 3 * g.D;
     HIP_TRY(launch_gemm(ga, dt, EPI_STORE, p.s));
@@ -240,7 +250,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   HIP_TRY(launch_attention(aa, dt, p.s));
   // (5) h += gate1 * (o Wo^T + b)
   {
-    GemmArgs ga = gemm_args(attn, g.D, bw.w_o, g.D, bw.b_o, p.M, g.D, g.D);
+    GemmArgs ga = gemm_args(attn, g.D, bw.w_o, g.D, bw.b_o, p.M, g.D, g.D, part, part_n);
     ga.H = p.h; ga.ldh = g.D; ga.rm = rm; ga.e6 = p.e6; ga.mod = mod; ga.gate_idx = 2; ga.D = g.D;
     HIP_TRY(launch_gemm(ga, dt, EPI_RESID_GATED, p.s));
   }
@@ -248,7 +258,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   na.mode = NORM_AFFINE; na.w = reinterpret_cast<const float*>(bw.ln3_w); na.b = reinterpret_cast<const float*>(bw.ln3_b);
   HIP_TRY(launch_norm(na, dt, p.s));
   {
-    GemmArgs ga = gemm_args(y, g.D, bw.w_cq, g.D, bw.b_cq, p.M, g.D, g.D);
+    GemmArgs ga = gemm_args(y, g.D, bw.w_cq, g.D, bw.b_cq, p.M, g.D, g.D, part, part_n);
     ga.C = qkv; ga.ldc = g.D;
     HIP_TRY(launch_gemm(ga, dt, EPI_STORE, p.s));
   }
@@ -266,7 +276,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     HIP_TRY(launch_attention(ca, dt, p.s));
   }
   {
-    GemmArgs ga = gemm_args(attn, g.D, bw.w_co, g.D, bw.b_co, p.M, g.D, g.D);
+    GemmArgs ga = gemm_args(attn, g.D, bw.w_co, g.D, bw.b_co, p.M, g.D, g.D, part, part_n);
     ga.H = p.h; ga.ldh = g.D;
     HIP_TRY(launch_gemm(ga, dt, EPI_RESID, p.s));
   }
@@ -274,12 +284,12 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   na.mode = NORM_ADALN; na.shift_idx = 3; na.scale_idx = 4;
   HIP_TRY(launch_norm(na, dt, p.s));
   {
-    GemmArgs ga = gemm_args(y, g.D, bw.w_ff1, g.D, bw.b_ff1, p.M, g.F, g.D);
+    GemmArgs ga = gemm_args(y, g.D, bw.w_ff1, g.D, bw.b_ff1, p.M, g.F, g.D, part, part_n);
     ga.C = ffn; ga.ldc = g.F;
     HIP_TRY(launch_gemm(ga, dt, EPI_GELU, p.s));
   }
   {
-    GemmArgs ga = gemm_args(ffn, g.F, bw.w_ff2, g.F, bw.b_ff2, p.M, g.D, g.F);
+    GemmArgs ga = gemm_args(ffn, g.F, bw.w_ff2, g.F, bw.b_ff2, p.M, g.D, g.F, part, part_n);
     ga.H = p.h; ga.ldh = g.D; ga.rm = rm; ga.e6 = p.e6; ga.mod = mod; ga.gate_idx = 5; ga.D = g.D;
     HIP_TRY(launch_gemm(ga, dt, EPI_RESID_GATED, p.s));
   }
@@ -385,14 +395,16 @@ wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* ctx = at<void>(ws, L.ctx_a);
   void* tmp = at<void>(ws, L.ctx_b);
+  float* part = at<float>(ws, L.part);
+  const long part_n = L.part_elems;
   const int Lt = cfg->ctx_text_len, Li = cfg->ctx_img_len;
   for (int b = 0; b < g.br; ++b) {
     GemmArgs gt = gemm_args(reinterpret_cast<const char*>(txt) + (size_t)b * Lt * g.Cin * g.esz, g.Cin, w->txt_w, g.Cin,
-                            w->txt_b, Lt, g.D, g.Cin);
+                            w->txt_b, Lt, g.D, g.Cin, part, part_n);
     gt.C = reinterpret_cast<char*>(ctx) + (size_t)b * g.Lc * g.D * g.esz; gt.ldc = g.D;
     HIP_TRY(launch_gemm(gt, g.dt, EPI_STORE, s));
     if (Li > 0) {
-      GemmArgs gi = gemm_args(img, g.Cin, w->img_w, g.Cin, w->img_b, Li, g.D, g.Cin);
+      GemmArgs gi = gemm_args(img, g.Cin, w->img_w, g.Cin, w->img_b, Li, g.D, g.Cin, part, part_n);
       gi.C = reinterpret_cast<char*>(ctx) + ((size_t)b * g.Lc + Lt) * g.D * g.esz; gi.ldc = g.D;
       HIP_TRY(launch_gemm(gi, g.dt, EPI_STORE, s));
     }
@@ -401,7 +413,7 @@ wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void
   const size_t ck_layer = (size_t)g.br * g.H * g.Lc * g.d, cv_layer = (size_t)g.br * g.H * g.d * out->ctx_stride;
   for (int l = 0; l < g.L; ++l) {
     const wam_block_weights& bw = w->blocks[l];
-    GemmArgs gk = gemm_args(ctx, g.D, bw.w_ck, g.D, bw.b_ck, M, g.D, g.D);
+    GemmArgs gk = gemm_args(ctx, g.D, bw.w_ck, g.D, bw.b_ck, M, g.D, g.D, part, part_n);
     gk.C = tmp; gk.ldc = g.D;
     HIP_TRY(launch_gemm(gk, g.dt, EPI_STORE, s));
     QkNormArgs qa{};
@@ -410,7 +422,7 @@ wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void
     qa.M = M; qa.D = g.D; qa.H = g.H; qa.d = g.d; qa.rows_per_branch = g.Lc; qa.eps = cfg->eps; qa.rope = nullptr;
     qa.rm = RowMap{g.Lc, g.Lc, g.Lc};
     HIP_TRY(launch_qk_norm_rope(qa, g.dt, s));
-    GemmArgs gv = gemm_args(ctx, g.D, bw.w_cv, g.D, bw.b_cv, M, g.D, g.D);
+    GemmArgs gv = gemm_args(ctx, g.D, bw.w_cv, g.D, bw.b_cv, M, g.D, g.D, part, part_n);
     gv.C = tmp; gv.ldc = g.D;
     HIP_TRY(launch_gemm(gv, g.dt, EPI_STORE, s));
     VCacheArgs va{};
@@ -499,7 +511,7 @@ wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, 
 }
 
 wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W, int ldw, const float* bias, void* C,
-                         int ldc, int M, int N, int K, int act, void* stream) {
+                         int ldc, int M, int N, int K, int act, void* ws, size_t ws_bytes, void* stream) {
   if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
   if (!A || !W || !C) return fail(WAM_E_ARG, "NULL operand");
   if (M < 0 || N < 0 || K <= 0 || K % 64) return fail(WAM_E_SHAPE, "K must be a positive multiple of 64");
@@ -507,7 +519,9 @@ wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W,
   const int epu = dtype == WAM_BF16 ? 8 : 4;
   if (lda % epu || ldw % epu) return fail(WAM_E_SHAPE, "lda/ldw must keep rows 16-byte aligned");
   if (act != 0 && act != 1) return fail(WAM_E_ARG, "act must be 0 or 1");
-  GemmArgs ga = gemm_args(A, lda, W, ldw, bias, M, N, K);
+  if (ws && reinterpret_cast<uintptr_t>(ws) % 256) return fail(WAM_E_ARG, "workspace must be 256-byte aligned");
+  GemmArgs ga = gemm_args(A, lda, W, ldw, bias, M, N, K, ws ? reinterpret_cast<float*>(ws) : nullptr,
+                          ws ? (long)(ws_bytes / 4) : 0);
   ga.C = C;
   ga.ldc = ldc;
   HIP_TRY(launch_gemm(ga, dtype == WAM_BF16 ? DT_BF16 : DT_F32, act ? EPI_GELU : EPI_STORE,

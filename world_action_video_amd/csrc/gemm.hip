@@ -14,6 +14,7 @@
 // streamed operand) share one XCD's L2.
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace wam {
 
@@ -230,6 +231,349 @@ gemm_kernel(GemmArgs g) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// 256x256 bf16 tile on 4 waves (one per SIMD), 128x128 per wave (4x4 MFMA blocks): half the LDS
+// fragment traffic per MFMA of the 8-wave tile, which is what bounds the 8-wave kernel. Global data
+// for tile kt+3 is fetched while tile kt computes (two register sets), tile kt+1 is written to the
+// other LDS buffer one quarter per k16 chunk between the MFMA groups, and the workgroup synchronises
+// before the last chunk so the next tile's first fragments load under it.
+// Split-K: with `splits` > 1 each workgroup covers one contiguous range of k-tiles and writes fp32
+// partial products to g.part[split][M][N]; splitk_reduce_kernel sums them in split order (fixed,
+// deterministic) and applies the epilogue.
+// ------------------------------------------------------------------------------------------------
+static constexpr int EPI_PARTIAL = 16;   // internal: fp32 partial products of one split
+
+template <int EPI, bool IL = true>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm4_kernel(GemmArgs g, int splits) {
+  using T = bf16_t;
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 4, TN = 4;
+  constexpr int NT = 256, UNITS = 8, EPU = 8, BK = 64, CHUNKS = 4;
+  constexpr int PER_T = BM * UNITS / NT;   // 8 units of A and 8 of W per thread per tile
+  // Rows are padded to 9 units (144 bytes): row r's unit u sits in bank group (r + u) mod 8, so eight
+  // consecutive rows or eight units of one row never collide, and every fragment address of a chunk
+  // is one per-lane base plus a compile-time offset (no per-chunk swizzle registers).
+  constexpr int PITCH = UNITS + 1;
+  __shared__ uint4 smem[2][(BM + BN) * PITCH];
+
+  const int Mt = (g.M + BM - 1) / BM, Nt = (g.N + BN - 1) / BN;
+  const int items = Mt * Nt * splits;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per = items >> 3, rem = items & 7;
+  if (kx >= per + (xcd < rem ? 1 : 0)) return;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
+  const int mt = item % Mt, rest = item / Mt;
+  const int sp = rest % splits, nt = rest / splits;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KT_all = g.K / BK;
+  const int kb = (int)((long)sp * KT_all / splits), ke = (int)((long)(sp + 1) * KT_all / splits);
+  const int KT = ke - kb;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  const __amdgpu_buffer_rsrc_t ra_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), (short)0,
+                                                                       (int)((long)g.M * g.lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.W), (short)0,
+                                                                       (int)((long)g.N * g.ldw * 2), 0x00020000);
+  const int lrow = tid >> 3, lunit = tid & 7;
+  int offa[PER_T], offw[PER_T];
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    offa[i] = (int)(((long)(m0 + lrow + i * 32) * g.lda + lunit * EPU) * 2);
+    offw[i] = (int)(((long)(n0 + lrow + i * 32) * g.ldw + lunit * EPU) * 2);
+  }
+  const int sbase = lrow * PITCH + lunit;
+
+  uint4 rg[2][2 * PER_T];                  // [register set][A units 0..7, W units 8..15]
+  // quarter q of a tile: units 2q, 2q+1 of A and of W (rows 64q .. 64q+63)
+  auto gload_q = [&](int kt, int set, int q) {
+    const int koff = (kb + min(kt, KT - 1)) * BK * 2;   // prefetches past the split re-read its last tile
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * q + u;
+      rg[set][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_, offa[i], koff, 0));
+      rg[set][PER_T + i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw_, offw[i], koff, 0));
+    }
+  };
+  auto sstore_q = [&](int st, int set, int q) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * q + u;
+      smem[st][sbase + i * 32 * PITCH] = rg[set][i];
+      smem[st][BM * PITCH + sbase + i * 32 * PITCH] = rg[set][PER_T + i];
+    }
+  };
+  auto fload = [&](int st, int c, uint4* fa, uint4* fb) {
+    const uint4* sa = smem[st] + (wm * WM + l32) * PITCH + half;
+    const uint4* sb = smem[st] + (BM + wn * WN + l32) * PITCH + half;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = sa[i * 32 * PITCH + 2 * c];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = sb[j * 32 * PITCH + 2 * c];
+  };
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+
+  // The loop body has no data-dependent branches: loads past the split's last k-tile read other
+  // valid rows or fall outside the buffer range (returning zero), and stores/fragment loads into the
+  // idle LDS buffer after the last tile are never consumed. This keeps both register sets in
+  // registers instead of merging them through control flow.
+  uint4 fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_q(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_q(1, 1, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sstore_q(0, 0, q);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_q(2, 0, q);
+  fload(0, 0, fa[0], fb[0]);
+
+  // One k-tile from LDS buffer CUR; register set CUR^1 holds tile kt+1 and is refilled with kt+3.
+  // CUR is a compile-time constant so both register sets keep fixed registers.
+  auto mma = [&](int fc, int lo, int hi) {
+#pragma unroll
+    for (int q = lo; q < hi; ++q)
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[fc][q >> 2]),
+                                                                   __builtin_bit_cast(bf16x8_t, fb[fc][q & 3]),
+                                                                   acc[q >> 2][q & 3], 0, 0, 0);
+  };
+  // Scheduling groups: one MFMA, then one memory instruction of the given class, so the LDS and
+  // global traffic issues while the matrix core works instead of in a burst between MFMA groups.
+  constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
+  auto tile = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value, nset = cur ^ 1;
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int fc = c & 1;
+      if constexpr (IL) {
+        if (c + 1 < CHUNKS) {
+          fload(cur, c + 1, fa[fc ^ 1], fb[fc ^ 1]);
+          sstore_q(nset, nset, c);
+          gload_q(kt + 3, nset, c);
+          mma(fc, 0, 16);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          // last chunk: half of its MFMAs cover the tile's final LDS writes, the barrier sits in the
+          // middle, and the other half cover the first fragment loads of the next tile
+          sstore_q(nset, nset, c);
+          gload_q(kt + 3, nset, c);
+          mma(fc, 0, 8);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          __syncthreads();
+          fload(nset, 0, fa[fc ^ 1], fb[fc ^ 1]);
+          mma(fc, 8, 16);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        if (c + 1 < CHUNKS) fload(cur, c + 1, fa[fc ^ 1], fb[fc ^ 1]);
+        sstore_q(nset, nset, c);
+        gload_q(kt + 3, nset, c);
+        if (c + 1 == CHUNKS) {
+          __syncthreads();
+          fload(nset, 0, fa[fc ^ 1], fb[fc ^ 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fc, 0, 16);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>{});
+    tile(kt + 1, std::integral_constant<int, 1>{});
+  }
+  if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
+
+  // ---- epilogue
+  if constexpr (EPI == EPI_PARTIAL) {
+    float* part = g.part + (long)sp * g.M * g.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WN + j * 32 + l32;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WM + i * 32 + acc_row(r, lane);
+          if (row < g.M) part[(long)row * g.N + col] = acc[i][j][r];
+        }
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_GATED) {
+    // Residual updates read H (and the gate) before writing it: issue all loads of one 32-row block
+    // first, then update, so the load latency is paid once per block rather than once per element.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float hv[16][TN], gv[16][TN];
+      long hoff[16];
+      bool ok[16];
+      // (row within branch, chunk, position in chunk) of the block's first row: two divisions per
+      // 32-row block; the rows below it advance with at most one wrap each (32 < chunk length).
+      const int row0 = m0 + wm * WM + i * 32;
+      int rb0 = 0, ch0 = 0, loc0 = 0;
+      if constexpr (EPI == EPI_RESID_GATED) {
+        rb0 = row0 % g.rm.rows_per_branch;
+        ch0 = rb0 / g.rm.Lq;
+        loc0 = rb0 - ch0 * g.rm.Lq;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = acc_row(r, lane);
+        const int row = row0 + off;
+        ok[r] = row < g.M;
+        hoff[r] = (long)row * g.ldh;
+        const float* grow = nullptr;
+        if constexpr (EPI == EPI_RESID_GATED) {
+          int rb = rb0 + off, ch = ch0, loc = loc0 + off;
+          if (rb >= g.rm.rows_per_branch) { rb -= g.rm.rows_per_branch; ch = 0; loc = rb; }
+          else if (loc >= g.rm.Lq) { loc -= g.rm.Lq; ++ch; }
+          const int grp = loc < g.rm.Lv ? 0 : 1;
+          grow = g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + wn * WN + j * 32 + l32;
+          const bool v = ok[r] && col < g.N;
+          hv[r][j] = v ? g.H[hoff[r] + col] : 0.f;
+          if constexpr (EPI == EPI_RESID_GATED) gv[r][j] = v ? grow[col] + g.mod[g.gate_idx * g.D + col] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * WN + j * 32 + l32;
+        if (col >= g.N) continue;
+        const float bias = g.bias ? g.bias[col] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (!ok[r]) continue;
+          const float v = acc[i][j][r] + bias;
+          if constexpr (EPI == EPI_RESID_GATED) g.H[hoff[r] + col] = hv[r][j] + gv[r][j] * v;
+          else g.H[hoff[r] + col] = hv[r][j] + v;
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * WN + j * 32 + l32;
+    if (col >= g.N) continue;
+    const float bias = g.bias ? g.bias[col] : 0.f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WM + i * 32 + acc_row(r, lane);
+        if (row >= g.M) continue;
+        const float v = acc[i][j][r] + bias;
+        if constexpr (EPI == EPI_STORE) {
+          Elem<T>::store(reinterpret_cast<T*>(g.C) + (long)row * g.ldc + col, v);
+        } else if constexpr (EPI == EPI_GELU) {
+          Elem<T>::store(reinterpret_cast<T*>(g.C) + (long)row * g.ldc + col, gelu_tanh_f(v));
+        } else if constexpr (EPI == EPI_ROWSEL_F32) {
+          const int b = row / g.rm.rows_per_branch, rb_ = row % g.rm.rows_per_branch;
+          const int ch = rb_ / g.rm.Lq, loc = rb_ % g.rm.Lq;
+          const int La = g.rm.Lq - g.rm.Lv;
+          const int nch = g.rm.rows_per_branch / g.rm.Lq;
+          if (g.sel_group == 0 && loc < g.rm.Lv) {
+            reinterpret_cast<float*>(g.C)[((long)b * nch * g.rm.Lv + ch * g.rm.Lv + loc) * g.ldc + col] = v;
+          } else if (g.sel_group == 1 && loc >= g.rm.Lv) {
+            reinterpret_cast<float*>(g.C)[((long)b * nch * La + ch * La + (loc - g.rm.Lv)) * g.ldc + col] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+
+// Sum of the split partials in split order, plus bias, then the epilogue. One thread per 4 columns.
+template <typename T, int EPI>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs g, int splits) {
+  const int row = blockIdx.y;
+  const int c4 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c4 >= g.N) return;
+  float v[4];
+  {
+    const float4 p = *reinterpret_cast<const float4*>(g.part + (long)row * g.N + c4);
+    v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+  }
+  for (int s = 1; s < splits; ++s) {
+    const float4 p = *reinterpret_cast<const float4*>(g.part + ((long)s * g.M + row) * g.N + c4);
+    v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+  }
+  if (g.bias) {
+    const float4 b = *reinterpret_cast<const float4*>(g.bias + c4);
+    v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+  }
+  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
+    if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_f(v[e]);
+    }
+    T* out = reinterpret_cast<T*>(g.C) + (long)row * g.ldc + c4;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint2*>(out) = make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
+    } else {
+      *reinterpret_cast<float4*>(out) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  } else {
+    float4* h = reinterpret_cast<float4*>(g.H + (long)row * g.ldh + c4);
+    float4 hv = *h;
+    if constexpr (EPI == EPI_RESID_GATED) {
+      const int rb = row % g.rm.rows_per_branch;
+      const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
+      const float4 ge = *reinterpret_cast<const float4*>(g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D + c4);
+      const float4 gm = *reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D + c4);
+      hv.x += (ge.x + gm.x) * v[0]; hv.y += (ge.y + gm.y) * v[1]; hv.z += (ge.z + gm.z) * v[2]; hv.w += (ge.w + gm.w) * v[3];
+    } else {
+      hv.x += v[0]; hv.y += v[1]; hv.z += v[2]; hv.w += v[3];
+    }
+    *h = hv;
+  }
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int NW>
 static hipError_t launch_cfg(const GemmArgs& a, Epi epi, hipStream_t s) {
   if constexpr (BM * BN > 128 * 128) {
@@ -252,18 +596,66 @@ static hipError_t launch_cfg(const GemmArgs& a, Epi epi, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int EPI, bool IL = true>
+static void launch_g4(const GemmArgs& a, int splits, hipStream_t s) {
+  const int items = ((a.M + 255) / 256) * ((a.N + 255) / 256) * splits;
+  hipLaunchKernelGGL((gemm4_kernel<EPI, IL>), dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, a, splits);
+}
+
+// bf16 256x256 four-wave path: direct epilogue when there are enough tiles to occupy the CUs, else
+// split-K (about 240 workgroups) with a reduce; returns false when the shape does not suit it.
+static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err) {
+  if (epi == EPI_ROWSEL_F32 || a.M < 256 || a.N < 256) return false;
+  const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int KT = a.K / 64;
+  int splits = 1;
+  // the reduce moves four columns per thread: 16-byte aligned fp32 rows, 8-byte aligned bf16 rows
+  const bool vec_ok = a.N % 4 == 0 && (!a.bias || aligned16(a.bias)) &&
+                      (epi == EPI_STORE || epi == EPI_GELU ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
+                                                           : (aligned16(a.H) && a.ldh % 4 == 0)) &&
+                      (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
+  if (tiles < 128 && vec_ok && a.part) {
+    splits = (int)((240 + tiles - 1) / tiles);
+    if (splits > 4) splits = 4;
+    while (splits > 1 && (KT < 4 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
+  }
+  if (splits == 1) {
+    switch (epi) {
+      case EPI_STORE: launch_g4<EPI_STORE>(a, 1, s); break;
+      case EPI_GELU: launch_g4<EPI_GELU>(a, 1, s); break;
+      case EPI_RESID: launch_g4<EPI_RESID>(a, 1, s); break;
+      case EPI_RESID_GATED: launch_g4<EPI_RESID_GATED>(a, 1, s); break;
+      default: return false;
+    }
+  } else {
+    launch_g4<EPI_PARTIAL>(a, splits, s);
+    const dim3 grid((a.N / 4 + 255) / 256, a.M);
+    switch (epi) {
+      case EPI_STORE: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_STORE>), grid, dim3(256), 0, s, a, splits); break;
+      case EPI_GELU: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_GELU>), grid, dim3(256), 0, s, a, splits); break;
+      case EPI_RESID: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_RESID>), grid, dim3(256), 0, s, a, splits); break;
+      case EPI_RESID_GATED:
+        hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_RESID_GATED>), grid, dim3(256), 0, s, a, splits);
+        break;
+      default: return false;
+    }
+  }
+  *err = hipGetLastError();
+  return true;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   // buffer descriptors address each operand with 32-bit byte offsets
   const long esz = dt == DT_BF16 ? 2 : 4;
   if ((long)a.M * a.lda * esz >= (1L << 31) || (long)a.N * a.ldw * esz >= (1L << 31)) return hipErrorInvalidValue;
-  // Tile choice (measured on MI355X over the step's shapes): the 256x256 tile with 8 waves (128x64 per
-  // wave) when it yields enough tiles to cover most of the 256 CUs; otherwise 256x128 / 128x256 tiles
-  // with 8 waves of 64x64, which double the tile count at M = 928 or 464; smaller tiles for tiny shapes.
+  // Tile choice (measured on MI355X over the step's shapes): bf16 products with M, N >= 256 take the
+  // four-wave 256x256 kernel (split over K when it has fewer than 128 tiles); the rest take 256x128 /
+  // 128x256 tiles with 8 waves of 64x64, and smaller tiles for tiny shapes.
   if (dt == DT_BF16) {
-    const long t256 = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (epi != EPI_ROWSEL_F32 && a.M >= 256 && a.N >= 256 && t256 >= 192)
-      return launch_cfg<bf16_t, 256, 256, 128, 64, 8>(a, epi, s);
+    hipError_t e4;
+    if (try_gemm4(a, epi, s, &e4)) return e4;
     if (epi != EPI_ROWSEL_F32 && a.M >= 256 && a.N >= 128) return launch_cfg<bf16_t, 256, 128, 64, 64, 8>(a, epi, s);
     if (epi != EPI_ROWSEL_F32 && a.M >= 128 && a.N >= 256) return launch_cfg<bf16_t, 128, 256, 64, 64, 8>(a, epi, s);
     if (a.N >= 128 && a.M >= 128) return launch_cfg<bf16_t, 128, 128, 64, 64, 4>(a, epi, s);

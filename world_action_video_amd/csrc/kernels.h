@@ -35,6 +35,8 @@ struct GemmArgs {
   const float* mod;          // EPI_RESID_GATED: [6][D]
   int gate_idx, D;
   int sel_group;             // EPI_ROWSEL_F32: 0 = video rows, 1 = action rows
+  float* part;               // split-K scratch: [splits][M][N] fp32 partial products (nullptr: no split)
+  long part_elems;           // capacity of `part` in floats
 };
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s);
