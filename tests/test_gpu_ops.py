@@ -36,7 +36,7 @@ def host(t):
 
 
 LINEAR_CASES = [(1, 64, 64), (67, 200, 128), (300, 384, 512), (928, 1024, 256), (130, 96, 1024), (300, 520, 1024),
-                (257, 260, 2048)]
+                (257, 260, 2048), (260, 258, 192)]
 
 
 def split_ws(gpu, M, N):

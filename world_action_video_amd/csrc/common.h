@@ -104,9 +104,13 @@ __device__ __forceinline__ float block_sum(float v, float* red /* >= NT/64 float
   return s;
 }
 
+// GELU, tanh form: 0.5 x (1 + tanh(u)) with u = sqrt(2/pi) (x + 0.044715 x^3), evaluated through the
+// identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)): one v_exp_f32 and one v_rcp_f32 (about 1e-7
+// relative). Saturates correctly: exp -> inf gives 0, exp -> 0 gives x.
 __device__ __forceinline__ float gelu_tanh_f(float x) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * x * (1.f + tanhf(c * (x + 0.044715f * x * x * x)));
+  const float c2 = -2.f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float e = __builtin_amdgcn_exp2f(c2 * (x + 0.044715f * x * x * x));
+  return x * __builtin_amdgcn_rcpf(1.f + e);
 }
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.f + expf(-x)); }

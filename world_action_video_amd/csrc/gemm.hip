@@ -338,11 +338,13 @@ gemm4_kernel(GemmArgs g, int splits) {
 
   // One k-tile from LDS buffer CUR; register set CUR^1 holds tile kt+1 and is refilled with kt+3.
   // CUR is a compile-time constant so both register sets keep fixed registers.
+  // acc[i][j] holds the transposed 32x32 block (W rows x A rows): lane l then owns output row
+  // m = .. + l % 32 and four runs of four consecutive columns, which the epilogue stores as vectors.
   auto mma = [&](int fc, int lo, int hi) {
 #pragma unroll
     for (int q = lo; q < hi; ++q)
-      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[fc][q >> 2]),
-                                                                   __builtin_bit_cast(bf16x8_t, fb[fc][q & 3]),
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fb[fc][q & 3]),
+                                                                   __builtin_bit_cast(bf16x8_t, fa[fc][q >> 2]),
                                                                    acc[q >> 2][q & 3], 0, 0, 0);
   };
   // Scheduling groups: one MFMA, then one memory instruction of the given class, so the LDS and
@@ -423,104 +425,108 @@ gemm4_kernel(GemmArgs g, int splits) {
   }
   if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
 
-  // ---- epilogue
+  // ---- epilogue: lane (l32, half) holds, for block (i, j), output row m = mb + 32 i and columns
+  // nb + 32 j + 8 g + 0..3 in acc[i][j][4 g .. 4 g + 3] (g = 0..3). N % 4 == 0 (checked at launch), so
+  // a run is either wholly inside the matrix or wholly outside.
+  const int mb = m0 + wm * WM + l32, nb = n0 + wn * WN + 4 * half;
+  auto run = [&](int i, int j, int gq) {
+    return make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+  };
   if constexpr (EPI == EPI_PARTIAL) {
     float* part = g.part + (long)sp * g.M * g.N;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WN + j * 32 + l32;
-      if (col >= g.N) continue;
+    for (int i = 0; i < TM; ++i) {
+      const int m = mb + 32 * i;
+      if (m >= g.M) continue;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WM + i * 32 + acc_row(r, lane);
-          if (row < g.M) part[(long)row * g.N + col] = acc[i][j][r];
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          if (n < g.N) *reinterpret_cast<float4*>(part + (long)m * g.N + n) = run(i, j, gq);
         }
     }
     return;
   }
-  if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_GATED) {
-    // Residual updates read H (and the gate) before writing it: issue all loads of one 32-row block
-    // first, then update, so the load latency is paid once per block rather than once per element.
+  float4 bias[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int n = nb + 32 * j + 8 * gq;
+      bias[j][gq] = (g.bias && n < g.N) ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      float hv[16][TN], gv[16][TN];
-      long hoff[16];
-      bool ok[16];
-      // (row within branch, chunk, position in chunk) of the block's first row: two divisions per
-      // 32-row block; the rows below it advance with at most one wrap each (32 < chunk length).
-      const int row0 = m0 + wm * WM + i * 32;
-      int rb0 = 0, ch0 = 0, loc0 = 0;
+      const int m = mb + 32 * i;
+      if (m >= g.M) continue;
+      bf16_t* crow = reinterpret_cast<bf16_t*>(g.C) + (long)m * g.ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          if (n >= g.N) continue;
+          float4 v = run(i, j, gq);
+          const float4 b = bias[j][gq];
+          v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+          if constexpr (EPI == EPI_GELU) {
+            v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
+          }
+          *reinterpret_cast<uint2*>(crow + n) = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+        }
+    }
+  } else {   // EPI_RESID, EPI_RESID_GATED: fp32 residual rows, read-modify-write per run of four
+    float4 gm[TN][4];
+    if constexpr (EPI == EPI_RESID_GATED) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          gm[j][gq] = n < g.N ? *reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D + n)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mb + 32 * i;
+      if (m >= g.M) continue;
+      float* hrow = g.H + (long)m * g.ldh;
+      const float* grow = nullptr;
       if constexpr (EPI == EPI_RESID_GATED) {
-        rb0 = row0 % g.rm.rows_per_branch;
-        ch0 = rb0 / g.rm.Lq;
-        loc0 = rb0 - ch0 * g.rm.Lq;
+        const int rb = m % g.rm.rows_per_branch;
+        const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
+        grow = g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D;
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = acc_row(r, lane);
-        const int row = row0 + off;
-        ok[r] = row < g.M;
-        hoff[r] = (long)row * g.ldh;
-        const float* grow = nullptr;
-        if constexpr (EPI == EPI_RESID_GATED) {
-          int rb = rb0 + off, ch = ch0, loc = loc0 + off;
-          if (rb >= g.rm.rows_per_branch) { rb -= g.rm.rows_per_branch; ch = 0; loc = rb; }
-          else if (loc >= g.rm.Lq) { loc -= g.rm.Lq; ++ch; }
-          const int grp = loc < g.rm.Lv ? 0 : 1;
-          grow = g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D;
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn * WN + j * 32 + l32;
-          const bool v = ok[r] && col < g.N;
-          hv[r][j] = v ? g.H[hoff[r] + col] : 0.f;
-          if constexpr (EPI == EPI_RESID_GATED) gv[r][j] = v ? grow[col] + g.mod[g.gate_idx * g.D + col] : 0.f;
-        }
-      }
+      // per block: the four runs' loads first, then the updates
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wn * WN + j * 32 + l32;
-        if (col >= g.N) continue;
-        const float bias = g.bias ? g.bias[col] : 0.f;
+        float4 hv[4], gv[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (!ok[r]) continue;
-          const float v = acc[i][j][r] + bias;
-          if constexpr (EPI == EPI_RESID_GATED) g.H[hoff[r] + col] = hv[r][j] + gv[r][j] * v;
-          else g.H[hoff[r] + col] = hv[r][j] + v;
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          const bool ok = n < g.N;
+          hv[gq] = ok ? *reinterpret_cast<const float4*>(hrow + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+          if constexpr (EPI == EPI_RESID_GATED)
+            gv[gq] = ok ? *reinterpret_cast<const float4*>(grow + n) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-      }
-    }
-    return;
-  }
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WN + j * 32 + l32;
-    if (col >= g.N) continue;
-    const float bias = g.bias ? g.bias[col] : 0.f;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WM + i * 32 + acc_row(r, lane);
-        if (row >= g.M) continue;
-        const float v = acc[i][j][r] + bias;
-        if constexpr (EPI == EPI_STORE) {
-          Elem<T>::store(reinterpret_cast<T*>(g.C) + (long)row * g.ldc + col, v);
-        } else if constexpr (EPI == EPI_GELU) {
-          Elem<T>::store(reinterpret_cast<T*>(g.C) + (long)row * g.ldc + col, gelu_tanh_f(v));
-        } else if constexpr (EPI == EPI_ROWSEL_F32) {
-          const int b = row / g.rm.rows_per_branch, rb_ = row % g.rm.rows_per_branch;
-          const int ch = rb_ / g.rm.Lq, loc = rb_ % g.rm.Lq;
-          const int La = g.rm.Lq - g.rm.Lv;
-          const int nch = g.rm.rows_per_branch / g.rm.Lq;
-          if (g.sel_group == 0 && loc < g.rm.Lv) {
-            reinterpret_cast<float*>(g.C)[((long)b * nch * g.rm.Lv + ch * g.rm.Lv + loc) * g.ldc + col] = v;
-          } else if (g.sel_group == 1 && loc >= g.rm.Lv) {
-            reinterpret_cast<float*>(g.C)[((long)b * nch * La + ch * La + (loc - g.rm.Lv)) * g.ldc + col] = v;
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          if (n >= g.N) continue;
+          float4 v = run(i, j, gq);
+          const float4 b = bias[j][gq];
+          v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+          float4 h = hv[gq];
+          if constexpr (EPI == EPI_RESID_GATED) {
+            const float4 ge = gv[gq], gmm = gm[j][gq];
+            h.x += (ge.x + gmm.x) * v.x; h.y += (ge.y + gmm.y) * v.y; h.z += (ge.z + gmm.z) * v.z; h.w += (ge.w + gmm.w) * v.w;
+          } else {
+            h.x += v.x; h.y += v.y; h.z += v.z; h.w += v.w;
           }
+          *reinterpret_cast<float4*>(hrow + n) = h;
         }
       }
     }
@@ -615,7 +621,8 @@ static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err
                       (epi == EPI_STORE || epi == EPI_GELU ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
                                                            : (aligned16(a.H) && a.ldh % 4 == 0)) &&
                       (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
-  if (tiles < 128 && vec_ok && a.part) {
+  if (!vec_ok) return false;
+  if (tiles < 128 && a.part) {
     splits = (int)((240 + tiles - 1) / tiles);
     if (splits > 4) splits = 4;
     while (splits > 1 && (KT < 4 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
