@@ -189,8 +189,28 @@ GemmArgs gemm_args(const void* A, long lda, const void* W, long ldw, const void*
   return a;
 }
 
-// One block. kv_only: stop after the keys/values of this layer are in the cache.
-wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_only) {
+// AdaLN norm of a block input: y = LN(h) (1 + scale) + shift, rows modulated per chunk and token group
+NormArgs adaln_args(const Pass& p, const float* mod, int shift_idx, int scale_idx) {
+  NormArgs na{};
+  na.X = p.h; na.Y = at<void>(p.ws, p.L.y); na.M = p.M; na.D = p.g.D; na.eps = p.cfg->eps; na.mode = NORM_ADALN;
+  na.rm = rowmap(p); na.e6 = p.e6; na.mod = mod; na.shift_idx = shift_idx; na.scale_idx = scale_idx;
+  return na;
+}
+
+// Output-head norm: y = LN(h) (1 + scale_h) + shift_h
+NormArgs head_norm_args(const Pass& p, const wam_weights* w) {
+  NormArgs na{};
+  na.X = p.h; na.Y = at<void>(p.ws, p.L.y); na.M = p.M; na.D = p.g.D; na.eps = p.cfg->eps; na.mode = NORM_HEAD;
+  na.rm = rowmap(p); na.e6 = at<float>(p.ws, p.L.e); na.mod = reinterpret_cast<const float*>(w->head_mod);
+  return na;
+}
+
+// One block. kv_only: stop after the keys/values of this layer are in the cache. pre_normed: y
+// already holds this block's first AdaLN norm (written by the previous block's last product).
+// after: the row stage that follows this block (the next block's first norm or the head norm), run
+// together with the block's last product; nullptr for none.
+wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_only, bool pre_normed,
+                     const PostArgs* after) {
   const Geo& g = p.g;
   const DType dt = g.dt;
   const float eps = p.cfg->eps;
@@ -209,10 +229,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   const long part_n = p.L.part_elems;
 
   // (1) y = LN(h) (1 + scale1) + shift1
-  NormArgs na{};
-  na.X = p.h; na.Y = y; na.M = p.M; na.D = g.D; na.eps = eps; na.mode = NORM_ADALN; na.rm = rm;
-  na.e6 = p.e6; na.mod = mod; na.shift_idx = 0; na.scale_idx = 1;
-  HIP_TRY(launch_norm(na, dt, p.s));
+  if (!pre_normed) HIP_TRY(launch_norm(adaln_args(p, mod, 0, 1), dt, p.s));
   // (2) [q|k|v] = y Wqkv^T + b  (keys/values only for the last layer of an append)
   {
     const int col0 = kv_only ? g.D : 0;
@@ -248,23 +265,28 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   aa.kv_base = len; aa.chunk_q = p.n > 1 ? g.Lq : 0; aa.kv_total = len + p.R;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
   HIP_TRY(launch_attention(aa, dt, p.s));
-  // (5) h += gate1 * (o Wo^T + b)
+  // (5) h += gate1 * (o Wo^T + b), then (6) n3 = LN(h) w + b for the cross-attention queries
   {
     GemmArgs ga = gemm_args(attn, g.D, bw.w_o, g.D, bw.b_o, p.M, g.D, g.D, part, part_n);
     ga.H = p.h; ga.ldh = g.D; ga.rm = rm; ga.e6 = p.e6; ga.mod = mod; ga.gate_idx = 2; ga.D = g.D;
-    HIP_TRY(launch_gemm(ga, dt, EPI_RESID_GATED, p.s));
+    PostArgs post{};
+    post.mode = POST_NORM;
+    post.na = adaln_args(p, mod, 0, 1);
+    post.na.mode = NORM_AFFINE; post.na.w = reinterpret_cast<const float*>(bw.ln3_w);
+    post.na.b = reinterpret_cast<const float*>(bw.ln3_b);
+    HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID_GATED, post, p.s));
   }
-  // (6) cross-attention: n3 = LN(h) w + b; qc = RMS(n3 Wcq^T + b) g
-  na.mode = NORM_AFFINE; na.w = reinterpret_cast<const float*>(bw.ln3_w); na.b = reinterpret_cast<const float*>(bw.ln3_b);
-  HIP_TRY(launch_norm(na, dt, p.s));
+  // qc = RMS(n3 Wcq^T + b) g, head-major
   {
     GemmArgs ga = gemm_args(y, g.D, bw.w_cq, g.D, bw.b_cq, p.M, g.D, g.D, part, part_n);
     ga.C = qkv; ga.ldc = g.D;
-    HIP_TRY(launch_gemm(ga, dt, EPI_STORE, p.s));
+    PostArgs post{};
+    post.mode = POST_QK;
+    post.qa = qa;
+    post.qa.src_ld = g.D; post.qa.src_col = 0; post.qa.gain = reinterpret_cast<const float*>(bw.g_cq); post.qa.rope = nullptr;
+    post.qa.dst = qh; post.qa.dst_bh_stride = (long)p.R * g.d; post.qa.dst_row0 = 0;
+    HIP_TRY(launch_gemm_post(ga, dt, EPI_STORE, post, p.s));
   }
-  qa.src_ld = g.D; qa.src_col = 0; qa.gain = reinterpret_cast<const float*>(bw.g_cq); qa.rope = nullptr;
-  qa.dst = qh; qa.dst_bh_stride = (long)p.R * g.d; qa.dst_row0 = 0;
-  HIP_TRY(launch_qk_norm_rope(qa, dt, p.s));
   {
     const size_t ck_layer = (size_t)g.br * g.H * g.Lc * g.d, cv_layer = (size_t)g.br * g.H * g.d * p.cx->ctx_stride;
     AttnArgs ca{};
@@ -275,14 +297,16 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     ca.scale_log2 = aa.scale_log2;
     HIP_TRY(launch_attention(ca, dt, p.s));
   }
+  // h += o Wco^T + b, then (7) y2 = LN(h) (1 + scale2) + shift2
   {
     GemmArgs ga = gemm_args(attn, g.D, bw.w_co, g.D, bw.b_co, p.M, g.D, g.D, part, part_n);
     ga.H = p.h; ga.ldh = g.D;
-    HIP_TRY(launch_gemm(ga, dt, EPI_RESID, p.s));
+    PostArgs post{};
+    post.mode = POST_NORM;
+    post.na = adaln_args(p, mod, 3, 4);
+    HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID, post, p.s));
   }
-  // (7) FFN: h += gate2 * (GELU(y2 W1^T + b1) W2^T + b2), y2 = LN(h) (1 + scale2) + shift2
-  na.mode = NORM_ADALN; na.shift_idx = 3; na.scale_idx = 4;
-  HIP_TRY(launch_norm(na, dt, p.s));
+  // FFN: h += gate2 * (GELU(y2 W1^T + b1) W2^T + b2)
   {
     GemmArgs ga = gemm_args(y, g.D, bw.w_ff1, g.D, bw.b_ff1, p.M, g.F, g.D, part, part_n);
     ga.C = ffn; ga.ldc = g.F;
@@ -291,7 +315,9 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   {
     GemmArgs ga = gemm_args(ffn, g.F, bw.w_ff2, g.F, bw.b_ff2, p.M, g.D, g.F, part, part_n);
     ga.H = p.h; ga.ldh = g.D; ga.rm = rm; ga.e6 = p.e6; ga.mod = mod; ga.gate_idx = 5; ga.D = g.D;
-    HIP_TRY(launch_gemm(ga, dt, EPI_RESID_GATED, p.s));
+    PostArgs none{};
+    none.mode = POST_NONE;
+    HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID_GATED, after ? *after : none, p.s));
   }
   return WAM_OK;
 }
@@ -354,14 +380,26 @@ wam_status stack_pass(const wam_config* cfg, const wam_weights* w, wam_kv_cache*
   ea.ae_w = w->ae_w; ea.ae_b = reinterpret_cast<const float*>(w->ae_b); ea.H = p.h;
   ea.n_chunks = n; ea.Lv = g.Lv; ea.La = g.La; ea.P = g.P; ea.A = g.A; ea.D = g.D; ea.br = g.br;
   HIP_TRY(launch_embed(ea, g.dt, s));
-  for (int l = 0; l < g.L; ++l) CHECK(run_block(p, w->blocks[l], l, append && l == g.L - 1));
+  // Each block's first norm runs with the previous block's last product (the first one on its own);
+  // the last block's product also runs the output-head norm.
+  HIP_TRY(launch_norm(adaln_args(p, reinterpret_cast<const float*>(w->blocks[0].mod), 0, 1), g.dt, s));
+  for (int l = 0; l < g.L; ++l) {
+    PostArgs after{};
+    const PostArgs* ap = nullptr;
+    if (l + 1 < g.L) {
+      after.mode = POST_NORM;
+      after.na = adaln_args(p, reinterpret_cast<const float*>(w->blocks[l + 1].mod), 0, 1);
+      ap = &after;
+    } else if (!append) {
+      after.mode = POST_NORM;
+      after.na = head_norm_args(p, w);
+      ap = &after;
+    }
+    CHECK(run_block(p, w->blocks[l], l, append && l == g.L - 1, true, ap));
+  }
   if (append) return WAM_OK;
 
-  // heads: n = LN(h) (1 + scale_h) + shift_h; v_video / v_action per token group
-  NormArgs na{};
-  na.X = p.h; na.Y = at<void>(ws, L.y); na.M = p.M; na.D = g.D; na.eps = cfg->eps; na.mode = NORM_HEAD;
-  na.rm = rowmap(p); na.e6 = at<float>(ws, L.e); na.mod = reinterpret_cast<const float*>(w->head_mod);
-  HIP_TRY(launch_norm(na, g.dt, s));
+  // heads: v_video / v_action per token group from y = LN(h) (1 + scale_h) + shift_h
   GemmArgs gv = gemm_args(at<void>(ws, L.y), g.D, w->vo_w, g.D, w->vo_b, p.M, g.P, g.D);
   gv.C = vv; gv.ldc = g.P; gv.rm = rowmap(p); gv.sel_group = 0;
   HIP_TRY(launch_gemm(gv, g.dt, EPI_ROWSEL_F32, s));
@@ -485,7 +523,7 @@ wam_status wam_dit_block_fwd(const wam_config* cfg, const wam_block_weights* bw,
   p.cx = ctx; p.h = h; p.e6 = e6; p.rope = at<float2>(ws, L.rope); p.s = reinterpret_cast<hipStream_t>(stream);
   HIP_TRY(launch_rope_table(p.rope, n_chunks, g.Lq, g.Lv, cfg->frames_per_chunk, cfg->grid_h, cfg->grid_w, start_frame,
                             g.d, cfg->rope_theta, p.s));
-  return run_block(p, *bw, layer, false);
+  return run_block(p, *bw, layer, false, false, nullptr);
 }
 
 wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, const float* v_action, int branches,

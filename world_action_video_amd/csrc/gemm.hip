@@ -609,44 +609,59 @@ static void launch_g4(const GemmArgs& a, int splits, hipStream_t s) {
 }
 
 // bf16 256x256 four-wave path: direct epilogue when there are enough tiles to occupy the CUs, else
-// split-K (about 240 workgroups) with a reduce; returns false when the shape does not suit it.
+// split-K (about 240 workgroups) with a finishing row kernel. Returns 0 when the shape does not suit
+// the kernel (the caller falls back to the 8-wave tiles), 1 for a direct launch, else the split count.
 static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
-static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err) {
-  if (epi == EPI_ROWSEL_F32 || a.M < 256 || a.N < 256) return false;
-  const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  const int KT = a.K / 64;
-  int splits = 1;
-  // the reduce moves four columns per thread: 16-byte aligned fp32 rows, 8-byte aligned bf16 rows
+static int g4_plan(const GemmArgs& a, Epi epi) {
+  if (epi == EPI_ROWSEL_F32 || a.M < 256 || a.N < 256) return 0;
+  // vector epilogues: runs of four columns, 16-byte aligned fp32 rows, 8-byte aligned bf16 rows
   const bool vec_ok = a.N % 4 == 0 && (!a.bias || aligned16(a.bias)) &&
                       (epi == EPI_STORE || epi == EPI_GELU ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
                                                            : (aligned16(a.H) && a.ldh % 4 == 0)) &&
                       (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
-  if (!vec_ok) return false;
+  if (!vec_ok) return 0;
+  const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int KT = a.K / 64;
+  int splits = 1;
   if (tiles < 128 && a.part) {
     splits = (int)((240 + tiles - 1) / tiles);
     if (splits > 4) splits = 4;
     while (splits > 1 && (KT < 4 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
   }
-  if (splits == 1) {
-    switch (epi) {
-      case EPI_STORE: launch_g4<EPI_STORE>(a, 1, s); break;
-      case EPI_GELU: launch_g4<EPI_GELU>(a, 1, s); break;
-      case EPI_RESID: launch_g4<EPI_RESID>(a, 1, s); break;
-      case EPI_RESID_GATED: launch_g4<EPI_RESID_GATED>(a, 1, s); break;
-      default: return false;
-    }
+  return splits;
+}
+
+static void launch_g4_direct(const GemmArgs& a, Epi epi, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: launch_g4<EPI_STORE>(a, 1, s); break;
+    case EPI_GELU: launch_g4<EPI_GELU>(a, 1, s); break;
+    case EPI_RESID: launch_g4<EPI_RESID>(a, 1, s); break;
+    case EPI_RESID_GATED: launch_g4<EPI_RESID_GATED>(a, 1, s); break;
+    default: break;
+  }
+}
+
+static void launch_reduce(const GemmArgs& a, Epi epi, int splits, hipStream_t s) {
+  const dim3 grid((a.N / 4 + 255) / 256, a.M);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_STORE>), grid, dim3(256), 0, s, a, splits); break;
+    case EPI_GELU: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_GELU>), grid, dim3(256), 0, s, a, splits); break;
+    case EPI_RESID: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_RESID>), grid, dim3(256), 0, s, a, splits); break;
+    case EPI_RESID_GATED:
+      hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_RESID_GATED>), grid, dim3(256), 0, s, a, splits);
+      break;
+    default: break;
+  }
+}
+
+static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err) {
+  const int plan = g4_plan(a, epi);
+  if (plan == 0) return false;
+  if (plan == 1) {
+    launch_g4_direct(a, epi, s);
   } else {
-    launch_g4<EPI_PARTIAL>(a, splits, s);
-    const dim3 grid((a.N / 4 + 255) / 256, a.M);
-    switch (epi) {
-      case EPI_STORE: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_STORE>), grid, dim3(256), 0, s, a, splits); break;
-      case EPI_GELU: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_GELU>), grid, dim3(256), 0, s, a, splits); break;
-      case EPI_RESID: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_RESID>), grid, dim3(256), 0, s, a, splits); break;
-      case EPI_RESID_GATED:
-        hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_RESID_GATED>), grid, dim3(256), 0, s, a, splits);
-        break;
-      default: return false;
-    }
+    launch_g4<EPI_PARTIAL>(a, plan, s);
+    launch_reduce(a, epi, plan, s);
   }
   *err = hipGetLastError();
   return true;
@@ -670,6 +685,153 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s) {
   }
   if (a.N >= 128 && a.M >= 128) return launch_cfg<float, 128, 128, 64, 64, 4>(a, epi, s);
   return launch_cfg<float, 64, 64, 32, 32, 4>(a, epi, s);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Split-K finish fused with the row stage that follows the product: one workgroup (256 threads) per
+// output row sums the fp32 partials in split order, adds the bias, applies the epilogue and then, with
+// the whole row in registers, the LayerNorm (POST_NORM) or the q/k RMSNorm with head-major scatter
+// (POST_QK). Row statistics are block reductions in a fixed order (deterministic).
+// ------------------------------------------------------------------------------------------------
+constexpr int FIN_G = 8;   // float4 groups per thread: rows of up to 8192 columns
+
+template <int EPI, int POST>
+__global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, int splits, PostArgs p) {
+  __shared__ float red[4];
+  const int m = blockIdx.x, t = threadIdx.x;
+  const int nv = g.N / 4;
+  const long pstride = (long)g.M * g.N;
+  float4 v[FIN_G];
+#pragma unroll
+  for (int k = 0; k < FIN_G; ++k) {
+    const int q = t + 256 * k;
+    v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (q >= nv) continue;
+    const float* pp = g.part + (long)m * g.N + 4 * q;
+    float4 a = *reinterpret_cast<const float4*>(pp);
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 b = *reinterpret_cast<const float4*>(pp + sp * pstride);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    if (g.bias) {
+      const float4 b = *reinterpret_cast<const float4*>(g.bias + 4 * q);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    if constexpr (EPI == EPI_STORE) {
+      // the stage reads what the unfused path would have stored: bf16-rounded outputs
+      a.x = bf16_to_f32(f32_to_bf16(a.x)); a.y = bf16_to_f32(f32_to_bf16(a.y));
+      a.z = bf16_to_f32(f32_to_bf16(a.z)); a.w = bf16_to_f32(f32_to_bf16(a.w));
+    } else {
+      float4* hp = reinterpret_cast<float4*>(g.H + (long)m * g.ldh + 4 * q);
+      float4 h = *hp;
+      if constexpr (EPI == EPI_RESID_GATED) {
+        const int rb = m % g.rm.rows_per_branch;
+        const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
+        const float4 ge = *reinterpret_cast<const float4*>(g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D + 4 * q);
+        const float4 gm = *reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D + 4 * q);
+        h.x += (ge.x + gm.x) * a.x; h.y += (ge.y + gm.y) * a.y; h.z += (ge.z + gm.z) * a.z; h.w += (ge.w + gm.w) * a.w;
+      } else {
+        h.x += a.x; h.y += a.y; h.z += a.z; h.w += a.w;
+      }
+      *hp = h;
+      a = h;
+    }
+    v[k] = a;
+  }
+  if constexpr (POST == POST_NORM) {
+    const NormArgs& na = p.na;
+    float s1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < FIN_G; ++k) s1 += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+    const float mean = block_sum<256>(s1, red) / (float)g.N;
+    float s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < FIN_G; ++k) {
+      if (t + 256 * k >= nv) continue;
+      const float d0 = v[k].x - mean, d1 = v[k].y - mean, d2 = v[k].z - mean, d3 = v[k].w - mean;
+      s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+    }
+    const float rstd = 1.f / sqrtf(block_sum<256>(s2, red) / (float)g.N + na.eps);
+    const float4 *sh = nullptr, *sc = nullptr, *sh2 = nullptr, *sc2 = nullptr;
+    if (na.mode != NORM_AFFINE) {
+      const int rb = m % na.rm.rows_per_branch;
+      const int ch = rb / na.rm.Lq, grp = (rb % na.rm.Lq) < na.rm.Lv ? 0 : 1;
+      if (na.mode == NORM_ADALN) {
+        const float* e6 = na.e6 + (long)(ch * 2 + grp) * 6 * na.D;
+        sh = reinterpret_cast<const float4*>(e6 + (long)na.shift_idx * na.D);
+        sc = reinterpret_cast<const float4*>(e6 + (long)na.scale_idx * na.D);
+        sh2 = reinterpret_cast<const float4*>(na.mod + (long)na.shift_idx * na.D);
+        sc2 = reinterpret_cast<const float4*>(na.mod + (long)na.scale_idx * na.D);
+      } else {
+        const float* e = na.e6 + (long)(ch * 2 + grp) * na.D;
+        sh = sc = reinterpret_cast<const float4*>(e);
+        sh2 = reinterpret_cast<const float4*>(na.mod);
+        sc2 = reinterpret_cast<const float4*>(na.mod + na.D);
+      }
+    }
+    bf16_t* y = reinterpret_cast<bf16_t*>(na.Y) + (long)m * na.D;
+#pragma unroll
+    for (int k = 0; k < FIN_G; ++k) {
+      const int q = t + 256 * k;
+      if (q >= nv) continue;
+      float4 o = make_float4((v[k].x - mean) * rstd, (v[k].y - mean) * rstd, (v[k].z - mean) * rstd, (v[k].w - mean) * rstd);
+      if (na.mode == NORM_AFFINE) {
+        const float4 w = reinterpret_cast<const float4*>(na.w)[q], b = reinterpret_cast<const float4*>(na.b)[q];
+        o = make_float4(o.x * w.x + b.x, o.y * w.y + b.y, o.z * w.z + b.z, o.w * w.w + b.w);
+      } else {
+        const float4 pa = sh[q], pb = sh2[q], ra = sc[q], rb2 = sc2[q];
+        o = make_float4(o.x * (1.f + (ra.x + rb2.x)) + (pa.x + pb.x), o.y * (1.f + (ra.y + rb2.y)) + (pa.y + pb.y),
+                        o.z * (1.f + (ra.z + rb2.z)) + (pa.z + pb.z), o.w * (1.f + (ra.w + rb2.w)) + (pa.w + pb.w));
+      }
+      reinterpret_cast<uint2*>(y)[q] = make_uint2(pack2_bf16(o.x, o.y), pack2_bf16(o.z, o.w));
+    }
+  } else {   // POST_QK
+    const QkNormArgs& qa = p.qa;
+    float s2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < FIN_G; ++k) s2 += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
+    const float rstd = 1.f / sqrtf(block_sum<256>(s2, red) / (float)g.N + qa.eps);
+    const int b = m / qa.rows_per_branch, rb = m % qa.rows_per_branch;
+    bf16_t* dst = reinterpret_cast<bf16_t*>(qa.dst);
+#pragma unroll
+    for (int k = 0; k < FIN_G; ++k) {
+      const int q = t + 256 * k;
+      if (q >= nv) continue;
+      const int c0 = 4 * q, hh = c0 / qa.d, j = c0 % qa.d;
+      const float4 gn = *reinterpret_cast<const float4*>(qa.gain + c0);
+      bf16_t* o = dst + (long)(b * qa.H + hh) * qa.dst_bh_stride + (long)(qa.dst_row0 + rb) * qa.d + j;
+      *reinterpret_cast<uint2*>(o) = make_uint2(pack2_bf16(v[k].x * rstd * gn.x, v[k].y * rstd * gn.y),
+                                                pack2_bf16(v[k].z * rstd * gn.z, v[k].w * rstd * gn.w));
+    }
+  }
+}
+
+hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs& post, hipStream_t s) {
+  if (post.mode == POST_NONE || a.M <= 0 || a.N <= 0) return launch_gemm(a, dt, epi, s);
+  bool fused = dt == DT_BF16 && a.N <= 256 * 4 * FIN_G;
+  if (post.mode == POST_NORM)
+    fused = fused && (epi == EPI_RESID || epi == EPI_RESID_GATED) && post.na.X == a.H && post.na.D == a.N &&
+            post.na.M == a.M && aligned16(post.na.Y) && (post.na.mode != NORM_AFFINE || (aligned16(post.na.w) && aligned16(post.na.b))) &&
+            (post.na.mode == NORM_AFFINE || (aligned16(post.na.e6) && aligned16(post.na.mod)));
+  else
+    fused = fused && epi == EPI_STORE && post.qa.rope == nullptr && post.qa.D == a.N && post.qa.M == a.M &&
+            post.qa.d % 4 == 0 && aligned16(post.qa.gain) && reinterpret_cast<uintptr_t>(post.qa.dst) % 8 == 0;
+  const int plan = fused ? g4_plan(a, epi) : 0;
+  if (plan > 1) {
+    launch_g4<EPI_PARTIAL>(a, plan, s);
+    if (post.mode == POST_NORM) {
+      if (epi == EPI_RESID)
+        hipLaunchKernelGGL((splitk_finish_kernel<EPI_RESID, POST_NORM>), dim3(a.M), dim3(256), 0, s, a, plan, post);
+      else
+        hipLaunchKernelGGL((splitk_finish_kernel<EPI_RESID_GATED, POST_NORM>), dim3(a.M), dim3(256), 0, s, a, plan, post);
+    } else {
+      hipLaunchKernelGGL((splitk_finish_kernel<EPI_STORE, POST_QK>), dim3(a.M), dim3(256), 0, s, a, plan, post);
+    }
+    return hipGetLastError();
+  }
+  hipError_t e = launch_gemm(a, dt, epi, s);
+  if (e != hipSuccess) return e;
+  return post.mode == POST_NORM ? launch_norm(post.na, dt, s) : launch_qk_norm_rope(post.qa, dt, s);
 }
 
 }  // namespace wam

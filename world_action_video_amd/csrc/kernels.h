@@ -93,6 +93,18 @@ struct QkNormArgs {
 };
 hipError_t launch_qk_norm_rope(const QkNormArgs& a, DType dt, hipStream_t s);
 
+// Row stage that follows a product. POST_NORM: the LayerNorm `na` of the product's updated residual
+// rows (na.X is the product's H); POST_QK: the q/k RMSNorm `qa` of the product's output rows (qa.src
+// is the product's C; no rotary embedding). When the product is split over K, the stage runs in the
+// kernel that sums the partials (one workgroup per row), otherwise as its own launch afterwards.
+enum PostMode { POST_NONE = 0, POST_NORM = 1, POST_QK = 2 };
+struct PostArgs {
+  PostMode mode;
+  NormArgs na;
+  QkNormArgs qa;
+};
+hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs& post, hipStream_t s);
+
 struct VCacheArgs {
   const void* src; long src_ld; int src_col;   // v = src[row][src_col + h*d + j]
   void* dst; long dst_bh_stride; int dst_stride; int dst_col0;   // Vt[b][h][j][dst_col0 + r]
