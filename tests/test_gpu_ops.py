@@ -102,9 +102,10 @@ def test_op_linear_full_size_sampled(gpu, M, N, K, split):
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-3)
 
 
-def _attn_case(gpu, dtype, br, H, d, Lq, kv_base, chunk_q, kv_total, tag):
+def _attn_case(gpu, dtype, br, H, d, Lq, kv_base, chunk_q, kv_total, tag, v_stride=None):
     k_rows = ((kv_total + 63) // 64) * 64 + 64
-    v_stride = ((kv_total + 63) // 64) * 64
+    if v_stride is None:
+        v_stride = ((kv_total + 63) // 64) * 64
     q = draw((br, H, Lq, d), "q" + tag)
     k = draw((br, H, k_rows, d), "k" + tag)
     v = draw((br, H, kv_total, d), "v" + tag)
@@ -144,6 +145,22 @@ def test_op_attention(gpu, dtype, d, Lq, kv_base, chunk_q, kv_total):
     out, ref = _attn_case(gpu, dtype, 2, 3, d, Lq, kv_base, chunk_q, kv_total, "%d_%d_%d_%d_%d" % (d, Lq, kv_base, chunk_q, kv_total))
     assert np.all(np.isfinite(out))
     assert rel_l2(out, ref) <= (1e-2 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Lq,kv_base,chunk_q,kv_total,v_stride", [
+    (100, 0, 0, 100, 104),     # value rows shorter than whole 32-key tiles: register-staged kernel
+    (130, 0, 0, 769, 776),
+    (96, 32, 40, 249, 256),    # rows hold whole tiles: copy kernel, tail keys past kv_total poisoned
+])
+def test_op_attention_value_row_pitch(gpu, d, Lq, kv_base, chunk_q, kv_total, v_stride):
+    """bf16 value rows of tight pitch: both attention kernels (selected by whether a row holds whole
+    32-key tiles) against the oracle, with stale keys and values past kv_total set to NaN."""
+    print("attention-pitch", d, Lq, kv_base, chunk_q, kv_total, v_stride, flush=True)
+    out, ref = _attn_case(gpu, "bf16", 2, 3, d, Lq, kv_base, chunk_q, kv_total, "p%d_%d_%d" % (d, kv_total, v_stride),
+                          v_stride=v_stride)
+    assert np.all(np.isfinite(out))
+    assert rel_l2(out, ref) <= 1e-2
 
 
 def test_op_attention_full_shape_bf16(gpu):

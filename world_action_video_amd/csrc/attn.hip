@@ -19,6 +19,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is written by the LDS-copy assembly
+
 namespace wam {
 
 static constexpr int ATT_BQ = 128, ATT_BKV = 64;
@@ -251,6 +253,283 @@ attn_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// bf16 kernel with 32-key tiles copied global -> LDS by the buffer unit (buffer_load ... lds), in a
+// ring of NS stages: tile t+NS-1 is requested while tile t computes, so about NS-1 tiles of compute
+// cover the memory latency and no registers stage the copies. Each 1 KB copy instruction writes
+// 64 lanes x 16 bytes contiguously; which 16-byte unit a lane fetches implements the XOR swizzle.
+// The copies are issued from inline assembly (M0 holds the LDS destination) and waited for with
+// explicit vmcnt counts before the barrier that hands a stage over, so the compiler neither drains
+// them at barriers nor waits for them before unrelated LDS reads.
+//
+// Softmax bookkeeping follows the online (running max) formulation with a lazy reference: the
+// running max used as the exponent offset is raised (and the output rescaled) only when a tile's max
+// exceeds it by more than 2^8 for some query of the wave; otherwise probabilities up to 2^8 are
+// accumulated against the old reference. The final normalisation divides by the sum accumulated
+// against the same reference, so the result is the exact softmax (rescaling is exact up to
+// rounding). The score scale is folded into the exponent: p = exp2(s c - m), c = log2(e)/sqrt(d).
+//
+// Keys at or past kv_total read as zero (the copy's buffer range ends there) and are masked; values
+// past kv_total are zeroed in LDS once their tile has landed, so stale rows never meet a zero
+// probability as 0 * inf or 0 * NaN.
+// ------------------------------------------------------------------------------------------------
+static constexpr int AT3_BKV = 32;
+
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+__device__ __forceinline__ void lds_copy16(int lds_addr, int voffset, __amdgpu_buffer_rsrc_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
+}
+
+template <int D, int NS, int QA, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn3_kernel(AttnArgs a) {
+  constexpr int BQ = 32 * NW;                    // queries per workgroup
+  using T = bf16_t;
+  constexpr int KU = D / 8;                      // 16-byte units per K row
+  constexpr int K_ROWS_I = 64 / KU;              // K rows per 1 KB copy
+  constexpr int K_INSTR = AT3_BKV / K_ROWS_I;    // copies per K tile
+  constexpr int V_INSTR = D / 16;                // copies per V^T tile (16 rows of 64 bytes each)
+  constexpr int PER_WAVE = (K_INSTR + V_INSTR) / NW;
+  static_assert((K_INSTR + V_INSTR) % NW == 0, "copies split evenly over the waves");
+  constexpr int KB = AT3_BKV * D * 2, SB = KB + D * AT3_BKV * 2;   // K block, stage bytes
+  constexpr int DC = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint4 smem[NS * SB / 16];
+  char* lds = reinterpret_cast<char*>(smem);
+  const int lds_base = (int)(uintptr_t)lds;      // low 32 bits of a generic LDS pointer: its LDS address
+  auto kswz = [](int row) { return KU >= 16 ? (row & 15) : ((row >> 1) & 7); };
+  auto vswz = [](int row) { return (row >> 2) & 3; };   // 64-byte rows: four rows share a bank line
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int nq = (a.Lq_total + BQ - 1) / BQ;
+  const int items = nq * a.H * a.br;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per = items >> 3, rem = items & 7;
+  if (kx >= per + (xcd < rem ? 1 : 0)) return;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
+  const int qt = item % nq, bh_i = item / nq;
+  const int h = bh_i % a.H, b = bh_i / a.H;
+  const int qblk = qt * BQ;
+  const long bh = (long)b * a.H + h;
+  const T* Q = reinterpret_cast<const T*>(a.Q) + bh * a.q_bh_stride;
+
+  auto limit_of = [&](int q) {
+    int lim = a.kv_total;
+    if (a.chunk_q > 0) {
+      const int c = a.kv_base + (q / a.chunk_q + 1) * a.chunk_q;
+      lim = c < lim ? c : lim;
+    }
+    return lim;
+  };
+  const int q_last = min(qblk + BQ, a.Lq_total) - 1;
+  const int n_tiles = (limit_of(q_last) + AT3_BKV - 1) / AT3_BKV;
+  const int q = qblk + wave * 32 + l32;
+  const bool q_ok = q < a.Lq_total;
+  const int my_lim = q_ok ? limit_of(q) : 0;
+  const int q_first = qblk + wave * 32;
+  const int wave_lim = q_first < a.Lq_total ? limit_of(q_first) : 0;
+
+  // buffer ranges: keys of this (branch, head) up to kv_total; all value rows of its block
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(reinterpret_cast<const T*>(a.K) + bh * a.k_bh_stride), (short)0, a.kv_total * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(reinterpret_cast<const T*>(a.Vt) + bh * a.v_bh_stride), (short)0, D * a.v_stride * 2, 0x00020000);
+  // Copies of a tile: waves 0 .. K_INSTR/PER_WAVE - 1 move the K block, the others the V^T block, so
+  // each wave has one source (no branches). Lane offsets for tile 0; tile t adds t * tile_stride.
+  static_assert(K_INSTR % PER_WAVE == 0, "a wave copies either keys or values");
+  const bool kwave = wave * PER_WAVE < K_INSTR;
+  const __amdgpu_buffer_rsrc_t rsrc = kwave ? rk : rv;
+  const int tile_stride = kwave ? AT3_BKV * D * 2 : AT3_BKV * 2;
+  int voff[PER_WAVE], ldst[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int i = wave * PER_WAVE + j;           // copy index within the tile
+    const int ki = i, vi = i - K_INSTR;
+    const int krow = ki * K_ROWS_I + lane / KU, vrow = vi * 16 + (lane >> 2);
+    voff[j] = kwave ? krow * D * 2 + ((lane % KU) ^ kswz(krow)) * 16
+                    : vrow * a.v_stride * 2 + ((lane & 3) ^ vswz(vrow)) * 16;
+    ldst[j] = kwave ? ki * 1024 : KB + vi * 1024;
+  }
+  auto copy_tile = [&](int t, int stage) {
+    const int toff = min(t, n_tiles - 1) * tile_stride;   // past the end: refetch the last tile into a free stage
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) lds_copy16(lds_base + stage * SB + ldst[j], voff[j] + toff, rsrc);
+  };
+  // values past kv_total in the tile that holds kv_total (once it has landed) become zero
+  const int tail_tile = (a.kv_total % AT3_BKV) ? a.kv_total / AT3_BKV : -1;
+  auto zero_tail = [&](int stage) {
+    char* vb = lds + stage * SB + KB;
+    const int k0 = tail_tile * AT3_BKV;
+    for (int x = tid; x < D * 4; x += NW * 64) {
+      const int row = x >> 2, u = x & 3;
+      const int kfirst = k0 + u * 8;
+      if (kfirst + 8 <= a.kv_total) continue;
+      uint4* p = reinterpret_cast<uint4*>(vb + row * 64 + ((u ^ vswz(row)) * 16));
+      uint4 v = *p;
+      T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (kfirst + k >= a.kv_total) e[k] = T(0);
+      *p = v;
+    }
+  };
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  uint4 qf[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c)
+    qf[c] = q_ok ? *reinterpret_cast<const uint4*>(Q + (long)q * D + c * 16 + half * 8) : make_uint4(0, 0, 0, 0);
+
+  floatx16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = floatx16{};
+  float m_ref = -INFINITY, l_run = 0.f;   // m_ref in scaled (log2) units
+  const float c = a.scale_log2;
+
+  // Software pipeline per tile kt: scores from K fragments already in registers, value fragments
+  // requested, stage hand-over (tile kt+1 visible, stage of tile kt-1 free), copy of tile kt+NS-1
+  // requested, K fragments of tile kt+1 requested, then the softmax and the value product, so LDS
+  // latency hides behind matrix and vector work. Tile kt+1's copies were requested NS-3 tiles earlier.
+  static_assert(NS >= 4, "the hand-over waits for copies issued NS-3 tiles ahead");
+  const int srow = swap_bits_2_3(l32);
+  uint4 kf[DC];
+  auto load_kf = [&](int stage) {
+    const char* sk = lds + stage * SB + srow * (D * 2);
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc) kf[cc] = *reinterpret_cast<const uint4*>(sk + (((2 * cc + half) ^ kswz(srow)) * 16));
+  };
+  auto hand_over = [&]() {   // copies land in LDS without LDS-counter traffic: only vmcnt and the barrier
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) copy_tile(t, t);
+    vmcnt_wait<PER_WAVE * (NS - 2)>();
+    hand_over();
+    if (tail_tile == 0) {
+      zero_tail(0);
+      barrier();
+    }
+    load_kf(0);
+  }
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int st = kt % NS;
+    const char* sb = lds + st * SB;
+    // (1) S^T = K Q^T for 32 keys (rows permuted) x this wave's 32 queries
+    floatx16 s = floatx16{};
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[cc]), __builtin_bit_cast(bf16x8_t, qf[cc]), s,
+                                                  0, 0, 0);
+    // (2) value fragments of this tile
+    uint4 vf[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int row = db * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        vf[db][j] = *reinterpret_cast<const uint4*>(sb + KB + row * 64 + (((2 * j + half) ^ vswz(row)) * 16));
+    }
+    // (3) hand-over: this wave's copies of tile kt+1 have landed, then everyone's
+    vmcnt_wait<PER_WAVE * (NS - 3)>();
+    hand_over();
+    if (kt + 1 == tail_tile) {
+      zero_tail((kt + 1) % NS);
+      barrier();
+    }
+    // (4) request tile kt+NS-1 into the stage of tile kt-1; (5) next tile's key fragments
+    copy_tile(kt + NS - 1, (kt + NS - 1) % NS);
+    load_kf((kt + 1) % NS);
+    // (6) softmax; register e of s holds key kt*32 + 16 (e / 8) + 8 half + (e % 8)
+    const int key0 = kt * AT3_BKV;
+    float tmax = -INFINITY;
+    if (key0 + AT3_BKV <= wave_lim) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s[e], s[e + 1]));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + 16 * (e >> 3) + 8 * half + (e & 7);
+        s[e] = key < my_lim ? s[e] : -INFINITY;
+        tmax = fmaxf(tmax, s[e]);
+      }
+    }
+    {   // max with the partner lane (l xor 32) holding the query's other 16 keys
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+    }
+    if (__any(tmax > m_ref + 8.f)) {
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    }
+    // a query with no visible key yet keeps m_ref = -inf and must produce p = 0, not NaN
+    const float moff = m_ref == -INFINITY ? 0.f : m_ref;
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -moff));
+      l_run += p[e];
+    }
+    uint4 pf[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pf[j] = make_uint4(pack2_bf16(p[8 * j], p[8 * j + 1]), pack2_bf16(p[8 * j + 2], p[8 * j + 3]),
+                         pack2_bf16(p[8 * j + 4], p[8 * j + 5]), pack2_bf16(p[8 * j + 6], p[8 * j + 7]));
+    // (7) O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[db][j]),
+                                                         __builtin_bit_cast(bf16x8_t, pf[j]), o[db], 0, 0, 0);
+  }
+  vmcnt_wait<0>();
+  barrier();
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  constexpr int SROW = D + 8;
+  static_assert(NW * 32 * SROW * 2 <= NS * SB, "staging fits in LDS");
+  T* stage = reinterpret_cast<T*>(smem) + wave * 32 * SROW;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) stage[l32 * SROW + db * 32 + acc_row(e, lane)] = f32_to_bf16(o[db][e] * inv);
+  __syncthreads();
+  constexpr int ROW_UNITS = D / 8;
+  T* O = reinterpret_cast<T*>(a.O);
+  for (int u = lane; u < 32 * ROW_UNITS; u += 64) {
+    const int r = u / ROW_UNITS, cu = u % ROW_UNITS;
+    const int qq = qblk + wave * 32 + r;
+    if (qq < a.Lq_total)
+      *reinterpret_cast<uint4*>(O + ((long)b * a.Lq_total + qq) * ((long)a.H * D) + (long)h * D + cu * 8) =
+          reinterpret_cast<const uint4*>(stage + r * SROW)[cu];
+  }
+}
+
+template <int D, int NS = 4, int QA = 1, int NW = 4>
+static hipError_t launch_attn3(const AttnArgs& a, hipStream_t s) {
+  const int items = ((a.Lq_total + 32 * NW - 1) / (32 * NW)) * a.H * a.br;
+  hipLaunchKernelGGL((attn3_kernel<D, NS, QA, NW>), dim3(8 * ((items + 7) / 8)), dim3(NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   const int items = ((a.Lq_total + ATT_BQ - 1) / ATT_BQ) * a.H * a.br;
@@ -262,6 +541,15 @@ static hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s) {
   if (a.Lq_total <= 0) return hipSuccess;
   if (dt == DT_BF16) {
+    // the copy kernel reads whole 32-key tiles of every value row: rows must hold them, and the
+    // 32-bit buffer offsets must cover the head's block
+    const long tiles_end = ((long)a.kv_total + 31) / 32 * 32;
+    const bool copy_ok = a.v_stride >= tiles_end && a.v_stride % 8 == 0 &&
+                         (long)a.d * a.v_stride * 2 < (1L << 31) && (long)a.kv_total * a.d * 2 < (1L << 31) &&
+                         reinterpret_cast<uintptr_t>(a.K) % 16 == 0 && reinterpret_cast<uintptr_t>(a.Vt) % 16 == 0 &&
+                         (a.k_bh_stride * 2) % 16 == 0 && (a.v_bh_stride * 2) % 16 == 0;
+    if (copy_ok && a.d == 128) return launch_attn3<128>(a, s);
+    if (copy_ok && a.d == 64) return launch_attn3<64>(a, s);
     if (a.d == 128) return launch_t<bf16_t, 128>(a, s);
     if (a.d == 64) return launch_t<bf16_t, 64>(a, s);
   } else {
