@@ -243,18 +243,15 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   QkNormArgs qa{};
   qa.src = qkv; qa.src_ld = 3 * g.D; qa.M = p.M; qa.D = g.D; qa.H = g.H; qa.d = g.d; qa.rows_per_branch = p.R;
   qa.eps = eps; qa.rope = p.rope; qa.rm = rm;
-  if (!kv_only) {
-    qa.src_col = 0; qa.gain = reinterpret_cast<const float*>(bw.g_q);
-    qa.dst = qh; qa.dst_bh_stride = (long)p.R * g.d; qa.dst_row0 = 0;
-    HIP_TRY(launch_qk_norm_rope(qa, dt, p.s));
-  }
-  qa.src_col = g.D; qa.gain = reinterpret_cast<const float*>(bw.g_k);
-  qa.dst = kc; qa.dst_bh_stride = (long)p.kv->capacity * g.d; qa.dst_row0 = len;
-  HIP_TRY(launch_qk_norm_rope(qa, dt, p.s));
+  qa.src_col = 0; qa.gain = reinterpret_cast<const float*>(bw.g_q);
+  qa.dst = qh; qa.dst_bh_stride = (long)p.R * g.d; qa.dst_row0 = 0;
+  QkNormArgs ka = qa;
+  ka.src_col = g.D; ka.gain = reinterpret_cast<const float*>(bw.g_k);
+  ka.dst = kc; ka.dst_bh_stride = (long)p.kv->capacity * g.d; ka.dst_row0 = len;
   VCacheArgs va{};
   va.src = qkv; va.src_ld = 3 * g.D; va.src_col = 2 * g.D; va.dst = vc; va.dst_bh_stride = (long)g.d * p.kv->capacity;
   va.dst_stride = p.kv->capacity; va.dst_col0 = len; va.rows_per_branch = p.R; va.br = g.br; va.H = g.H; va.d = g.d;
-  HIP_TRY(launch_v_to_cache(va, dt, p.s));
+  HIP_TRY(launch_qkv_cache(kv_only ? nullptr : &qa, ka, va, dt, p.s));
   if (kv_only) return WAM_OK;
 
   // (4) chunk-causal self-attention over [cache ; this pass]

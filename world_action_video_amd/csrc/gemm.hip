@@ -693,23 +693,31 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s) {
 // the whole row in registers, the LayerNorm (POST_NORM) or the q/k RMSNorm with head-major scatter
 // (POST_QK). Row statistics are block reductions in a fixed order (deterministic).
 // ------------------------------------------------------------------------------------------------
-constexpr int FIN_G = 8;   // float4 groups per thread: rows of up to 8192 columns
+constexpr int FIN_G = 8;   // float4 groups per thread (template G <= FIN_G): rows of up to 8192 columns
 
-template <int EPI, int POST>
-__global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, int splits, PostArgs p) {
+template <int EPI, int POST, int SPLITS, int G>
+__global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs p) {
   __shared__ float red[4];
   const int m = blockIdx.x, t = threadIdx.x;
   const int nv = g.N / 4;
   const long pstride = (long)g.M * g.N;
-  float4 v[FIN_G];
+  // all loads of the row first (partials, residual, gate), then the arithmetic and the stores
+  float4 v[G], hv[G], gv[G];
+  const float* grow = nullptr;
+  if constexpr (EPI == EPI_RESID_GATED) {
+    const int rb = m % g.rm.rows_per_branch;
+    const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
+    grow = g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D;
+  }
 #pragma unroll
-  for (int k = 0; k < FIN_G; ++k) {
+  for (int k = 0; k < G; ++k) {
     const int q = t + 256 * k;
-    v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    v[k] = hv[k] = gv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (q >= nv) continue;
     const float* pp = g.part + (long)m * g.N + 4 * q;
     float4 a = *reinterpret_cast<const float4*>(pp);
-    for (int sp = 1; sp < splits; ++sp) {
+#pragma unroll
+    for (int sp = 1; sp < SPLITS; ++sp) {
       const float4 b = *reinterpret_cast<const float4*>(pp + sp * pstride);
       a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
     }
@@ -717,23 +725,32 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, int spli
       const float4 b = *reinterpret_cast<const float4*>(g.bias + 4 * q);
       a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
     }
+    v[k] = a;
+    if constexpr (EPI != EPI_STORE) hv[k] = *reinterpret_cast<const float4*>(g.H + (long)m * g.ldh + 4 * q);
+    if constexpr (EPI == EPI_RESID_GATED) {
+      const float4 ge = *reinterpret_cast<const float4*>(grow + 4 * q);
+      const float4 gm = *reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D + 4 * q);
+      gv[k] = make_float4(ge.x + gm.x, ge.y + gm.y, ge.z + gm.z, ge.w + gm.w);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const int q = t + 256 * k;
+    if (q >= nv) continue;
+    float4 a = v[k];
     if constexpr (EPI == EPI_STORE) {
       // the stage reads what the unfused path would have stored: bf16-rounded outputs
       a.x = bf16_to_f32(f32_to_bf16(a.x)); a.y = bf16_to_f32(f32_to_bf16(a.y));
       a.z = bf16_to_f32(f32_to_bf16(a.z)); a.w = bf16_to_f32(f32_to_bf16(a.w));
     } else {
-      float4* hp = reinterpret_cast<float4*>(g.H + (long)m * g.ldh + 4 * q);
-      float4 h = *hp;
+      float4 h = hv[k];
       if constexpr (EPI == EPI_RESID_GATED) {
-        const int rb = m % g.rm.rows_per_branch;
-        const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
-        const float4 ge = *reinterpret_cast<const float4*>(g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D + 4 * q);
-        const float4 gm = *reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D + 4 * q);
-        h.x += (ge.x + gm.x) * a.x; h.y += (ge.y + gm.y) * a.y; h.z += (ge.z + gm.z) * a.z; h.w += (ge.w + gm.w) * a.w;
+        const float4 gg = gv[k];
+        h.x += gg.x * a.x; h.y += gg.y * a.y; h.z += gg.z * a.z; h.w += gg.w * a.w;
       } else {
         h.x += a.x; h.y += a.y; h.z += a.z; h.w += a.w;
       }
-      *hp = h;
+      *reinterpret_cast<float4*>(g.H + (long)m * g.ldh + 4 * q) = h;
       a = h;
     }
     v[k] = a;
@@ -742,11 +759,11 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, int spli
     const NormArgs& na = p.na;
     float s1 = 0.f;
 #pragma unroll
-    for (int k = 0; k < FIN_G; ++k) s1 += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+    for (int k = 0; k < G; ++k) s1 += (v[k].x + v[k].y) + (v[k].z + v[k].w);
     const float mean = block_sum<256>(s1, red) / (float)g.N;
     float s2 = 0.f;
 #pragma unroll
-    for (int k = 0; k < FIN_G; ++k) {
+    for (int k = 0; k < G; ++k) {
       if (t + 256 * k >= nv) continue;
       const float d0 = v[k].x - mean, d1 = v[k].y - mean, d2 = v[k].z - mean, d3 = v[k].w - mean;
       s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
@@ -771,7 +788,7 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, int spli
     }
     bf16_t* y = reinterpret_cast<bf16_t*>(na.Y) + (long)m * na.D;
 #pragma unroll
-    for (int k = 0; k < FIN_G; ++k) {
+    for (int k = 0; k < G; ++k) {
       const int q = t + 256 * k;
       if (q >= nv) continue;
       float4 o = make_float4((v[k].x - mean) * rstd, (v[k].y - mean) * rstd, (v[k].z - mean) * rstd, (v[k].w - mean) * rstd);
@@ -789,12 +806,12 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, int spli
     const QkNormArgs& qa = p.qa;
     float s2 = 0.f;
 #pragma unroll
-    for (int k = 0; k < FIN_G; ++k) s2 += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
+    for (int k = 0; k < G; ++k) s2 += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
     const float rstd = 1.f / sqrtf(block_sum<256>(s2, red) / (float)g.N + qa.eps);
     const int b = m / qa.rows_per_branch, rb = m % qa.rows_per_branch;
     bf16_t* dst = reinterpret_cast<bf16_t*>(qa.dst);
 #pragma unroll
-    for (int k = 0; k < FIN_G; ++k) {
+    for (int k = 0; k < G; ++k) {
       const int q = t + 256 * k;
       if (q >= nv) continue;
       const int c0 = 4 * q, hh = c0 / qa.d, j = c0 % qa.d;
@@ -819,14 +836,29 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
   const int plan = fused ? g4_plan(a, epi) : 0;
   if (plan > 1) {
     launch_g4<EPI_PARTIAL>(a, plan, s);
+    const dim3 grid(a.M), block(256);
+    const int groups = (a.N / 4 + 255) / 256;   // float4 groups per thread
+#define WAM_FINISH_G(E, P, S)                                                                              \
+  if (groups <= 1) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 1>), grid, block, 0, s, a, post);      \
+  else if (groups <= 5) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 5>), grid, block, 0, s, a, post); \
+  else hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, FIN_G>), grid, block, 0, s, a, post);
+#define WAM_FINISH(E, P)                  \
+  switch (plan) {                         \
+    case 2: WAM_FINISH_G(E, P, 2) break;  \
+    case 3: WAM_FINISH_G(E, P, 3) break;  \
+    default: WAM_FINISH_G(E, P, 4) break; \
+  }
     if (post.mode == POST_NORM) {
-      if (epi == EPI_RESID)
-        hipLaunchKernelGGL((splitk_finish_kernel<EPI_RESID, POST_NORM>), dim3(a.M), dim3(256), 0, s, a, plan, post);
-      else
-        hipLaunchKernelGGL((splitk_finish_kernel<EPI_RESID_GATED, POST_NORM>), dim3(a.M), dim3(256), 0, s, a, plan, post);
+      if (epi == EPI_RESID) {
+        WAM_FINISH(EPI_RESID, POST_NORM)
+      } else {
+        WAM_FINISH(EPI_RESID_GATED, POST_NORM)
+      }
     } else {
-      hipLaunchKernelGGL((splitk_finish_kernel<EPI_STORE, POST_QK>), dim3(a.M), dim3(256), 0, s, a, plan, post);
+      WAM_FINISH(EPI_STORE, POST_QK)
     }
+#undef WAM_FINISH
+#undef WAM_FINISH_G
     return hipGetLastError();
   }
   hipError_t e = launch_gemm(a, dt, epi, s);

@@ -111,6 +111,9 @@ struct VCacheArgs {
   int rows_per_branch, br, H, d;
 };
 hipError_t launch_v_to_cache(const VCacheArgs& a, DType dt, hipStream_t s);
+// q (optional) and k norms plus the value transpose in one launch (bf16; other cases run the three
+// launches above)
+hipError_t launch_qkv_cache(const QkNormArgs* q, const QkNormArgs& k, const VCacheArgs& v, DType dt, hipStream_t s);
 
 // rotary (cos, sin) table for the video tokens of n_chunks chunks, written for every row of a branch
 hipError_t launch_rope_table(float2* table, int n_chunks, int Lq, int Lv, int frames_per_chunk, int grid_h,

@@ -102,12 +102,9 @@ hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s) {
 // group never straddles a head since the head dim is a multiple of 8).
 // ------------------------------------------------------------------------------------------------
 template <typename T, int GPL>
-__global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkNormArgs a) {
+__device__ __forceinline__ void qk_row(const QkNormArgs& a, int row, int lane) {
   constexpr int EPU = 16 / sizeof(T);            // elements per 16-byte unit
   constexpr int UPG = 8 / EPU;                   // units per group of 8 channels
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.M) return;
   const T* src = reinterpret_cast<const T*>(a.src) + (long)row * a.src_ld + a.src_col;
   const int ng = a.D / 8;
   float x[GPL][8];
@@ -163,6 +160,12 @@ __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkNormArgs a) {
   }
 }
 
+template <typename T, int GPL>
+__global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkNormArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row < a.M) qk_row<T, GPL>(a, row, threadIdx.x & 63);
+}
+
 template <typename T>
 static hipError_t launch_qk_t(const QkNormArgs& a, hipStream_t s) {
   const dim3 grid((a.M + 3) / 4), block(256);
@@ -203,6 +206,90 @@ __global__ void __launch_bounds__(256) v_to_cache_kernel(VCacheArgs a) {
     const int rr = r0 + r;
     if (rr < a.rows_per_branch) dst[(long)j * a.dst_stride + a.dst_col0 + rr] = tile[r * PITCH + j];
   }
+}
+
+// ------------------------------------------------------------------------------------------------
+// One launch for everything that follows the QKV projection (bf16): q RMSNorm + RoPE to head-major
+// rows, k RMSNorm + RoPE into the key cache, v transposed into the value cache. Block ranges of the
+// 1-D grid select the part, so the three run side by side. The value part moves 8x8 element blocks
+// through registers: each thread reads 8 rows x 16 bytes (one head's 8 channels) and writes 8 cache
+// rows x 16 bytes (8 consecutive keys), so both sides are 16-byte accesses.
+// ------------------------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void v_block_bf16(const VCacheArgs& a, int blk) {
+  constexpr int CB = D / 8;                      // 8-channel column blocks per head
+  constexpr int RB = 256 / CB;                   // 8-row blocks per workgroup
+  const int R = a.rows_per_branch;
+  const int nrb = (R + RB * 8 - 1) / (RB * 8);
+  const int rblk = blk % nrb, h = (blk / nrb) % a.H, b = blk / (nrb * a.H);
+  const int cb = threadIdx.x % CB, rbk = threadIdx.x / CB;
+  const int r0 = rblk * RB * 8 + rbk * 8;        // rows per branch are a multiple of 8
+  if (r0 >= R) return;
+  const bf16_t* src = reinterpret_cast<const bf16_t*>(a.src) + ((long)b * R + r0) * a.src_ld + a.src_col + h * D + cb * 8;
+  uint4 x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = *reinterpret_cast<const uint4*>(src + (long)i * a.src_ld);
+  bf16_t* dst = reinterpret_cast<bf16_t*>(a.dst) + ((long)b * a.H + h) * a.dst_bh_stride + (long)(cb * 8) * a.dst_stride +
+                a.dst_col0 + r0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    // channel c of the 8 rows: element c of each row's unit
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (reinterpret_cast<const uint32_t*>(&x[2 * i])[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu;
+      const uint32_t hi = (reinterpret_cast<const uint32_t*>(&x[2 * i + 1])[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu;
+      w[i] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + (long)c * a.dst_stride) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <int GPL, int D>
+__global__ void __launch_bounds__(256) qkv_cache_kernel(QkNormArgs q, QkNormArgs k, VCacheArgs v, int nq_blk, int nk_blk) {
+  int blk = blockIdx.x;
+  const int row4 = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (blk < nk_blk) {
+    const int row = blk * 4 + row4;
+    if (row < k.M) qk_row<bf16_t, GPL>(k, row, lane);
+    return;
+  }
+  blk -= nk_blk;
+  if (blk < nq_blk) {
+    const int row = blk * 4 + row4;
+    if (row < q.M) qk_row<bf16_t, GPL>(q, row, lane);
+    return;
+  }
+  v_block_bf16<D>(v, blk - nq_blk);
+}
+
+hipError_t launch_qkv_cache(const QkNormArgs* q, const QkNormArgs& k, const VCacheArgs& v, DType dt, hipStream_t s) {
+  if (k.M <= 0) return hipSuccess;
+  const bool fused = dt == DT_BF16 && (v.d == 128 || v.d == 64) && v.rows_per_branch % 8 == 0 && v.dst_col0 % 8 == 0 &&
+                     v.dst_stride % 8 == 0 && v.src_ld % 8 == 0 && v.src_col % 8 == 0 && k.D % 8 == 0 &&
+                     k.D <= 8192 && k.d % 8 == 0 && (!q || (q->D == k.D && q->M == k.M));
+  if (!fused) {
+    hipError_t e = hipSuccess;
+    if (q) e = launch_qk_norm_rope(*q, dt, s);
+    if (e == hipSuccess) e = launch_qk_norm_rope(k, dt, s);
+    if (e == hipSuccess) e = launch_v_to_cache(v, dt, s);
+    return e;
+  }
+  const int nk_blk = (k.M + 3) / 4, nq_blk = q ? (q->M + 3) / 4 : 0;
+  const int rows_per_wg = 8 * (256 / (v.d / 8));
+  const int nv_blk = (v.rows_per_branch + rows_per_wg - 1) / rows_per_wg * v.H * v.br;
+  const dim3 grid(nk_blk + nq_blk + nv_blk), block(256);
+  const QkNormArgs qq = q ? *q : k;
+  const int gpl = (k.D / 8 + 63) / 64;
+#define WAM_QKV(G)                                                                                              \
+  if (v.d == 128) hipLaunchKernelGGL((qkv_cache_kernel<G, 128>), grid, block, 0, s, qq, k, v, nq_blk, nk_blk); \
+  else hipLaunchKernelGGL((qkv_cache_kernel<G, 64>), grid, block, 0, s, qq, k, v, nq_blk, nk_blk);
+  if (gpl <= 2) { WAM_QKV(2) }
+  else if (gpl <= 4) { WAM_QKV(4) }
+  else if (gpl <= 10) { WAM_QKV(10) }
+  else { WAM_QKV(16) }
+#undef WAM_QKV
+  return hipGetLastError();
 }
 
 hipError_t launch_v_to_cache(const VCacheArgs& a, DType dt, hipStream_t s) {
