@@ -60,6 +60,48 @@ def load_traffic(kernel_key: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
+TRAFFIC_KEY = "gemm_qkv_bf16_928x15360x5120"
+
+
+def summarize_counters(fetch_db: str, write_db: str):
+    """HBM bytes per launch of the QKV product from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by the ratio of known bytes to counted bytes of the 1 GiB copy in the same run."""
+    import sqlite3
+
+    def per_dispatch(db, counter):
+        if not os.path.isfile(db):
+            raise SystemExit("no such database: %s" % db)
+        cur = sqlite3.connect("file:%s?mode=ro" % db, uri=True).cursor()
+        cols = [r[1] for r in cur.execute("pragma table_info(counters_collection)")]
+        name_col = "kernel_name" if "kernel_name" in cols else "name"
+        rows = cur.execute("select %s, counter_name, value from counters_collection" % name_col).fetchall()
+        return [(n, v) for n, c, v in rows if c.startswith(counter)]
+
+    out = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        rows = per_dispatch(db, counter)
+        copy = max((v for n, v in rows if "elementwise" in n), default=None)
+        gemm = [v for n, v in rows if "gemm4_kernel<0" in n]
+        if copy is None or not gemm:
+            raise SystemExit("counters not found in %s" % db)
+        known = float(1 << 30)   # the copy moves 2^28 floats each way
+        out[counter] = {"copy_kib": copy, "factor": known / (copy * 1024.0), "gemm_kib_mean": sum(gemm) / len(gemm),
+                        "gemm_launches": len(gemm)}
+    fetch = out["FETCH_SIZE"]["gemm_kib_mean"] * 1024.0 * out["FETCH_SIZE"]["factor"]
+    write = out["WRITE_SIZE"]["gemm_kib_mean"] * 1024.0 * out["WRITE_SIZE"]["factor"]
+    rec = {"bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write, "counters": out,
+           "source_sha256_16": source_hash(os.path.join(ROOT, "world_action_video_amd", "csrc", "gemm.hip")),
+           "commands": ["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run -- python bench.py --counters",
+                        "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run -- python bench.py --counters",
+                        "python bench.py --summarize-counters <fetch db> <write db>"]}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[TRAFFIC_KEY] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps({TRAFFIC_KEY: {"bytes_per_launch": rec["bytes_per_launch"]}}))
+
+
 def cpu_baseline(w, timed_layers: int = 1) -> dict:
     """The oracle as it stands, timed on this host on a bounded sample: ``timed_layers`` full-width
     blocks of the same step (both CFG branches, 928 cached + 464 current tokens, 769 condition tokens),
@@ -104,7 +146,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="run only a 1 GiB copy and launches of the dominant kernel (for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="turn the two rocprofv3 --pmc databases of a --counters run (FETCH_SIZE, WRITE_SIZE) "
+                         "into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print("bench.py: this path runs on one GPU; --gpus %d is not supported (run with --gpus 1)" % args.gpus,
               file=sys.stderr)
@@ -209,7 +257,7 @@ def main():
     gemm_ms = e0.elapsed_time(e1) / reps
     gemm_flops = 2.0 * M * 3 * D * D
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    traffic = load_traffic("gemm_qkv_bf16_928x15360x5120", source_hash(os.path.join(ROOT, "world_action_video_amd", "csrc", "gemm.hip")))
+    traffic = load_traffic(TRAFFIC_KEY, source_hash(os.path.join(ROOT, "world_action_video_amd", "csrc", "gemm.hip")))
 
     fl = step_flops(w)
     step_tflops = fl["total"] / (ms * 1e-3) / 1e12
