@@ -182,6 +182,27 @@ wam_status wam_flow_step(float *x_video, float *x_action, const float *v_video, 
                          float *g_video, float *g_action, const float *prev_video, float *cos_parts, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* One chunk's denoising loop ([N569] dynamic DiT caching; [WS1] dynamic16 scheduler): n_steps Euler
+ * steps over the host times grid[0..n_steps] (both token groups at grid[k]), CFG with `guidance`,
+ * with velocity reuse: steps 0 and 1 always run the DiT; at step k >= 2, if the cosine similarity of
+ * the two most recent DiT-computed guided video velocities exceeds tau (and fewer than
+ * max_consecutive_reuse steps in a row were reused; negative = no limit), the DiT is skipped and
+ * the latest computed guided velocities drive the Euler update.
+ *   x_video [Lv * P], x_action [La * A] (float, device): updated in place
+ *   v_video [branches][Lv][P], v_action [branches][La][A] (float, device): scratch for the DiT output
+ *   g_video [Lv * P], g_action [La * A] (float, device): the latest computed guided velocities (out)
+ *   cos_parts (float[3], device): scratch for the similarity partial sums
+ *   dit_calls (host, may be NULL): DiT passes run; reused (host, n_steps bytes, may be NULL): 1 where
+ *   a step reused the velocity
+ * The decision needs the similarity on the host: with tau <= 1 the call synchronises `stream` once
+ * per DiT pass (12 bytes read back); with tau > 1 reuse is impossible and nothing synchronises.
+ * Workspace: wam_workspace_bytes(cfg, 1). The cache is read, not committed (use wam_kv_append). */
+wam_status wam_denoise_chunk(const wam_config *cfg, const wam_weights *w, wam_kv_cache *cache, const wam_ctx_kv *ctx,
+                             float *x_video, float *x_action, const float *grid, int n_steps, float guidance, float tau,
+                             int max_consecutive_reuse, int start_frame, float *v_video, float *v_action,
+                             float *g_video, float *g_action, float *cos_parts, void *ws, size_t ws_bytes,
+                             void *stream, int *dit_calls, unsigned char *reused);
+
 /* Kernel-level calls, exposed so each kernel can be verified on its own (same kernels as above).
  *
  * Linear layer ([ARCH] §2.3: every projection of the block): C[m][n] = act(sum_k A[m][k] W[n][k] +

@@ -116,3 +116,22 @@ def test_kv_reset_is_host_only():
     kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 512, 464)
     wam.wam_kv_reset(kv)
     assert kv.length == 0
+
+
+def test_denoise_chunk_validation():
+    """The denoising loop checks its own arguments, and its first DiT pass checks the rest, before
+    anything is enqueued."""
+    lib = _lib()
+    c = _cfg(1)
+    F = ctypes.c_float
+    grid = (F * 3)(0.0, 0.5, 1.0)
+    P = 0x1000
+    args = lambda g, n, gv=P, cosp=P: (ctypes.byref(c), None, None, None, P, P, g, n, F(5.0), F(2.0), -1, 0, P, P,  # noqa
+                                       gv, P, cosp, P, 1 << 30, None, None, None)
+    assert lib.wam_denoise_chunk(*args(None, 2)) == wam.WAM_E_ARG and "grid" in wam.wam_last_error()
+    assert lib.wam_denoise_chunk(*args(grid, 0)) == wam.WAM_E_ARG
+    nan_grid = (F * 3)(0.0, float("nan"), 1.0)
+    assert lib.wam_denoise_chunk(*args(nan_grid, 2)) == wam.WAM_E_ARG and "non-finite" in wam.wam_last_error()
+    assert lib.wam_denoise_chunk(*args(grid, 2, gv=None)) == wam.WAM_E_ARG
+    # valid loop arguments: the first DiT pass rejects the missing weights
+    assert lib.wam_denoise_chunk(*args(grid, 2)) == wam.WAM_E_ARG and "weights" in wam.wam_last_error()

@@ -196,6 +196,50 @@ def test_cfg_batch_equals_two_single_branch_calls(gpu, tiny_oracle, dtype):
             assert ev <= 5e-3 and ea <= 5e-3
 
 
+_DENOISE_REF = {}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("tau,max_reuse,calls_expected", [(1.5, -1, 16), (-1.5, -1, 2), (-1.5, 1, 9)])
+def test_denoise_chunk_matches_oracle(gpu, tiny_oracle, dtype, tau, max_reuse, calls_expected):
+    """The library's 16-step Euler loop with velocity reuse (wam_denoise_chunk) against the oracle's
+    loop on the same DiT: same call count and reuse pattern (the thresholds are far from any cosine,
+    so the decisions cannot differ), final latents within the stack tolerance."""
+    w, m, ckv = tiny_oracle
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    grid = [k / 16 for k in range(17)]
+    key = (tau, max_reuse)
+    if key not in _DENOISE_REF:
+        cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+        O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+
+        def dit(xv, xa, t):
+            vb, ab = O.stack_forward(m, cache, ckv, xv, xa, [t], [t], 1, w.frames_per_chunk)
+            return O.cfg_combine(vb, w.guidance), O.cfg_combine(ab, w.guidance)
+        _DENOISE_REF[key] = O.denoise_chunk(dit, epv[1], epa[1], grid, tau, None if max_reuse < 0 else max_reuse)
+    ref_v, ref_a, n_ref, flags_ref = _DENOISE_REF[key]
+    print("denoise", dtype, tau, max_reuse, flush=True)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    xv, xa = rig.f32(epv[1]), rig.f32(epa[1])
+    br = rig.m.cfg.branches
+    vv = torch.empty((br, w.video_tokens, w.patch_dim), device=gpu)
+    va = torch.empty((br, w.action_tokens, w.action_dim), device=gpu)
+    gv = torch.empty(w.video_tokens * w.patch_dim, device=gpu)
+    ga = torch.empty(w.action_tokens * w.action_dim, device=gpu)
+    cosp = torch.empty(3, device=gpu)
+    calls, flags = wam.wam_denoise_chunk(rig.m.cfg, rig.m.weights, dc.c, rig.ctx.c, xv, xa, grid, w.guidance, tau, vv, va,
+                                         gv, ga, cosp, rig.ws, start_frame=w.frames_per_chunk,
+                                         max_consecutive_reuse=max_reuse)
+    torch.cuda.synchronize()
+    assert calls == n_ref == calls_expected
+    assert flags == list(flags_ref)
+    ev, ea = rel_l2(xv.cpu().numpy(), ref_v), rel_l2(xa.cpu().numpy(), ref_a)
+    print("rel-L2 video %.2e action %.2e" % (ev, ea), flush=True)
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
 def test_flow_step_matches_oracle(gpu):
     nv, na = 28160, 192
     rng = synth.tensor_key(101, 0, "flow")

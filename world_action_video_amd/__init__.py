@@ -17,7 +17,7 @@ WAM_OK, WAM_E_ARG, WAM_E_SHAPE, WAM_E_CAPACITY, WAM_E_HIP, WAM_E_UNSUPPORTED = 0
 WAM_BF16, WAM_F32 = 0, 1
 
 EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
-           "wam_dit_block_fwd", "wam_flow_step", "wam_op_linear", "wam_op_attention", "wam_kv_reset",
+           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_op_linear", "wam_op_attention", "wam_kv_reset",
            "wam_last_error")
 
 
@@ -83,6 +83,7 @@ def load(path: str = LIB_PATH):
         "wam_kv_append": (I, [CFG, W, KV, CX, P, P, I, P, S, P]),
         "wam_dit_block_fwd": (I, [CFG, ctypes.POINTER(wam_block_weights), I, KV, CX, P, P, I, I, P, S, P]),
         "wam_flow_step": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P, S, P]),
+        "wam_denoise_chunk": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, P, P, P, P, P, P, S, P, P, P]),
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P]),
         "wam_kv_reset": (None, [KV]),
@@ -165,6 +166,23 @@ def wam_flow_step(x_video, x_action, v_video, v_action, branches, guidance, n_vi
                                 float(guidance), n_video, n_action, float(dt_video), float(dt_action), _ptr(g_video),
                                 _ptr(g_action), _ptr(prev_video), _ptr(cos_parts), _ptr(ws), _nbytes(ws),
                                 _stream(stream)))
+
+
+def wam_denoise_chunk(cfg, weights, cache, ctx, x_video, x_action, grid, guidance, tau, v_video, v_action, g_video,
+                      g_action, cos_parts, ws, start_frame=0, max_consecutive_reuse=-1, stream=None):
+    """Returns (number of DiT passes, list of per-step reuse flags). ``grid`` is a host sequence of
+    n_steps + 1 times."""
+    n = len(grid) - 1
+    g = (ctypes.c_float * (n + 1))(*[float(t) for t in grid])
+    calls = ctypes.c_int(0)
+    flags = (ctypes.c_ubyte * max(n, 1))()
+    _check(load().wam_denoise_chunk(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(ctx),
+                                    _ptr(x_video), _ptr(x_action), ctypes.cast(g, ctypes.c_void_p), n, float(guidance),
+                                    float(tau), int(max_consecutive_reuse), int(start_frame), _ptr(v_video),
+                                    _ptr(v_action), _ptr(g_video), _ptr(g_action), _ptr(cos_parts), _ptr(ws),
+                                    _nbytes(ws), _stream(stream), ctypes.cast(ctypes.byref(calls), ctypes.c_void_p),
+                                    ctypes.cast(flags, ctypes.c_void_p)))
+    return calls.value, [bool(flags[i]) for i in range(n)]
 
 
 def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, ws=None, stream=None):

@@ -545,6 +545,58 @@ wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, 
   return WAM_OK;
 }
 
+wam_status wam_denoise_chunk(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache, const wam_ctx_kv* ctx,
+                             float* x_video, float* x_action, const float* grid, int n_steps, float guidance, float tau,
+                             int max_consecutive_reuse, int start_frame, float* v_video, float* v_action, float* g_video,
+                             float* g_action, float* cos_parts, void* ws, size_t ws_bytes, void* stream, int* dit_calls,
+                             unsigned char* reused) {
+  CHECK(check_cfg(cfg));
+  if (!grid || n_steps < 1) return fail(WAM_E_ARG, "grid must hold n_steps + 1 >= 2 times");
+  for (int k = 0; k <= n_steps; ++k)
+    if (!std::isfinite(grid[k])) return fail(WAM_E_ARG, "non-finite time in the grid");
+  if (!g_video || !g_action || !cos_parts) return fail(WAM_E_ARG, "guided-velocity or cosine buffers are NULL");
+  if (!std::isfinite(tau) && !std::isinf(tau)) return fail(WAM_E_ARG, "tau is NaN");
+  const Geo g = geo_of(*cfg);
+  const int nv = g.Lv * g.P, na = g.La * g.A;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // reuse needs cos > tau with cos <= 1: a tau above 1 can never trigger it (no host read-back then)
+  const bool may_reuse = tau <= 1.f;
+  int computed = 0, consecutive = 0, calls = 0;
+  double cos_last = -2.0;   // cosine of the two most recent DiT-computed guided video velocities
+  for (int k = 0; k < n_steps; ++k) {
+    const float t = grid[k], dt = grid[k + 1] - grid[k];
+    bool reuse = false;
+    if (may_reuse && k >= 2 && computed >= 2 &&
+        (max_consecutive_reuse < 0 || consecutive < max_consecutive_reuse))
+      reuse = cos_last > (double)tau;
+    if (reuse) {
+      // Euler step with the latest computed guided velocities
+      CHECK(wam_flow_step(x_video, x_action, g_video, g_action, 1, 1.f, nv, na, dt, dt, nullptr, nullptr, nullptr,
+                          nullptr, ws, ws_bytes, stream));
+      ++consecutive;
+    } else {
+      CHECK(wam_dit_stack_fwd(cfg, w, cache, ctx, 1, x_video, x_action, &t, &t, start_frame, v_video, v_action, ws,
+                              ws_bytes, stream));
+      // guided velocities replace the previous computed ones; the cosine compares new and previous
+      CHECK(wam_flow_step(x_video, x_action, v_video, v_action, g.br, guidance, nv, na, dt, dt, g_video, g_action,
+                          computed >= 1 ? g_video : nullptr, cos_parts, ws, ws_bytes, stream));
+      ++computed;
+      ++calls;
+      consecutive = 0;
+      if (may_reuse && computed >= 2 && k + 1 < n_steps) {
+        float parts[3];
+        HIP_TRY(hipMemcpyAsync(parts, cos_parts, sizeof(parts), hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        const double den = std::sqrt((double)parts[1] * (double)parts[2]);
+        cos_last = den > 0.0 ? (double)parts[0] / den : 0.0;
+      }
+    }
+    if (reused) reused[k] = reuse ? 1 : 0;
+  }
+  if (dit_calls) *dit_calls = calls;
+  return WAM_OK;
+}
+
 wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W, int ldw, const float* bias, void* C,
                          int ldc, int M, int N, int K, int act, void* ws, size_t ws_bytes, void* stream) {
   if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
