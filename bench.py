@@ -12,6 +12,7 @@ Prints one JSON line (see the keys below). --gpus N > 1 is refused: this path ru
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -144,6 +145,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
+                    help="3: the step metric (default); 2: one full-width block (br = 2 and B = 1); 4: four chunks "
+                         "of 16 Euler steps plus KV appends; 5: three-view long context, 16-step loop with reuse")
     ap.add_argument("--counters", action="store_true",
                     help="run only a 1 GiB copy and launches of the dominant kernel (for rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -167,6 +171,9 @@ def main():
     from world_action_video_amd.device import DeviceCache, DeviceCtx, DeviceModel, to_device, workspace
 
     dev = torch.device("cuda:0")
+    if args.workload != WORKLOAD_ID and not args.counters:
+        extra_workload(args, dev)
+        return
     w = WORKLOADS[WORKLOAD_ID]
     Lq, Lv, La, D = w.chunk_tokens, w.video_tokens, w.action_tokens, w.dim
     M = w.branches * Lq
@@ -294,6 +301,144 @@ def main():
         del model, cache, ctx
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+
+
+def extra_workload(args, dev):
+    """The other measured configurations (one JSON line each; the step metric is workload 3)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import world_action_video_amd as wam
+    from synth.workloads import WORKLOADS, draw_named
+    from world_action_video_amd.device import DeviceCache, DeviceCtx, DeviceModel, to_device, workspace
+
+    w = WORKLOADS[args.workload]
+    Lq, Lv, La = w.chunk_tokens, w.video_tokens, w.action_tokens
+
+    def log(msg):
+        print("[bench] %s" % msg, file=sys.stderr, flush=True)
+
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)  # noqa: E731
+    log("uploading %s weights" % w.name)
+    model = DeviceModel(w, "bf16", dev)
+    ctx = DeviceCtx(w, "bf16", dev)
+    ws = workspace(model.cfg, 1, dev)
+    img = draw_named(w, -1, "img") if w.ctx_img_len else None
+    wam.wam_ctx_build(model.cfg, model.weights, to_device(draw_named(w, -1, "txt"), "bf16", dev),
+                      to_device(img, "bf16", dev) if img is not None else None, ctx.c, ws)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    base = {"n_gpus": 1, "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latents/features)",
+            "config": {"workload": w.name, "layers": w.layers, "dim": w.dim, "branches": w.branches,
+                       "chunk_tokens": Lq}}
+
+    if args.workload == 2:
+        # one block on the residual stream, CFG batch 2 and the B = 1 per-GPU share of a branch split
+        res = {}
+        for br in (2, 1):
+            cfg = wam.wam_config.from_buffer_copy(model.cfg)
+            cfg.branches = br
+            cache = DeviceCache(w, 2 * Lq, "bf16", dev, branches=br)
+            cx = DeviceCtx(w, "bf16", dev, branches=br)
+            wsb = workspace(cfg, 1, dev)
+            wam.wam_ctx_build(cfg, model.weights, to_device(draw_named(w, -1, "txt")[:br], "bf16", dev),
+                              to_device(img, "bf16", dev), cx.c, wsb)
+            wam.wam_kv_append(cfg, model.weights, cache.c, cx.c, f32(draw_named(w, -1, "x1_video_0")),
+                              f32(draw_named(w, -1, "x1_action_0")), 0, wsb)
+            h = torch.randn((br, Lq, w.dim), device=dev)
+            e = torch.empty((2, w.dim), device=dev)
+            e6 = torch.empty((2, 6, w.dim), device=dev)
+            wam.wam_time_embed(cfg, model.weights, [0.4, 0.4], e, e6, wsb)
+            blk = model.blocks[0]
+            run = lambda: wam.wam_dit_block_fwd(cfg, blk, 0, cache.c, cx.c, h, e6, 1, w.frames_per_chunk, wsb)  # noqa
+            for _ in range(args.warmup):
+                run()
+            a, b = ev(), ev()
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(args.steps):
+                run()
+            b.record()
+            torch.cuda.synchronize()
+            res["br%d" % br] = round(a.elapsed_time(b) / args.steps, 3)
+        out = dict(base, metric="ms per DiT block", value=res["br2"], unit="ms", higher_is_better=False,
+                   ms_per_block={"cfg_batch_2": res["br2"], "B_1": res["br1"]})
+        print(json.dumps(out))
+        return
+
+    n_new = 4 if args.workload == 4 else 1
+    cache = DeviceCache(w, (w.cache_chunks + n_new) * Lq, "bf16", dev)
+    for c in range(w.cache_chunks):
+        wam.wam_kv_append(model.cfg, model.weights, cache.c, ctx.c, f32(draw_named(w, -1, "x1_video_%d" % c, n_chunks=8)),
+                          f32(draw_named(w, -1, "x1_action_%d" % c, n_chunks=8)), c * w.frames_per_chunk, ws)
+    vv = torch.empty((w.branches, Lv, w.patch_dim), device=dev)
+    va = torch.empty((w.branches, La, w.action_dim), device=dev)
+    gv = torch.empty(Lv * w.patch_dim, device=dev)
+    ga = torch.empty(La * w.action_dim, device=dev)
+    cos = torch.empty(3, device=dev)
+    grid = [k / 16 for k in range(17)]
+    torch.cuda.synchronize()
+
+    if args.workload == 4:
+        # four chunks: 16 Euler steps from noise, then the chunk is committed with a fresh video
+        # observation and its own denoised actions
+        times, calls = [], []
+        xv0 = f32(draw_named(w, -1, "eps_video_1", n_chunks=8))
+        xa0 = f32(draw_named(w, -1, "eps_action_1", n_chunks=8))
+        xv, xa = xv0.clone(), xa0.clone()
+        wam.wam_denoise_chunk(model.cfg, model.weights, cache.c, ctx.c, xv, xa, grid, w.guidance, 2.0, vv, va, gv, ga,
+                              cos, ws, start_frame=w.frames_per_chunk)   # warm-up, cache untouched
+        for c in range(1, 5):
+            xv = f32(draw_named(w, -1, "eps_video_%d" % c, n_chunks=8))
+            xa = f32(draw_named(w, -1, "eps_action_%d" % c, n_chunks=8))
+            obs = f32(draw_named(w, -1, "x1_video_%d" % c, n_chunks=8))
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record()
+            n, _ = wam.wam_denoise_chunk(model.cfg, model.weights, cache.c, ctx.c, xv, xa, grid, w.guidance, 2.0, vv, va,
+                                         gv, ga, cos, ws, start_frame=c * w.frames_per_chunk)
+            wam.wam_kv_append(model.cfg, model.weights, cache.c, ctx.c, obs, xa, c * w.frames_per_chunk, ws)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(round(a.elapsed_time(b), 2))
+            calls.append(n)
+        finite = bool(torch.isfinite(xv).all().item() and torch.isfinite(xa).all().item())
+        out = dict(base, metric="ms per chunk (16 Euler steps + KV append)", value=round(sum(times) / 4, 2), unit="ms",
+                   higher_is_better=False, per_chunk_ms=times, total_ms=round(sum(times), 1), dit_calls=calls,
+                   cache_rows_final=cache.length, outputs_finite=finite)
+        print(json.dumps(out))
+        return
+
+    # workload 5: one step with decoupled timesteps, then a 16-step loop with velocity reuse
+    start = w.cache_chunks * w.frames_per_chunk
+    xv = f32(draw_named(w, -1, "eps_video_%d" % w.cache_chunks, n_chunks=8))
+    xa = f32(draw_named(w, -1, "eps_action_%d" % w.cache_chunks, n_chunks=8))
+    u = synth.uniform01(2 * (args.steps + args.warmup), synth.tensor_key(w.id, -1, "timesteps"), stream=2)
+    tv = 1.0 - np.sqrt(u[0::2])          # sigma = 1 - t_v ~ Beta(2, 1): inverse CDF of x^2
+    ta = u[1::2]
+    for i in range(args.warmup):
+        wam.wam_dit_stack_fwd(model.cfg, model.weights, cache.c, ctx.c, 1, xv, xa, [tv[i]], [ta[i]], start, vv, va, ws)
+    a, b = ev(), ev()
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(args.steps):
+        j = args.warmup + i
+        wam.wam_dit_stack_fwd(model.cfg, model.weights, cache.c, ctx.c, 1, xv, xa, [tv[j]], [ta[j]], start, vv, va, ws)
+    b.record()
+    torch.cuda.synchronize()
+    step_ms = a.elapsed_time(b) / args.steps
+    a, b = ev(), ev()
+    a.record()
+    n, flags = wam.wam_denoise_chunk(model.cfg, model.weights, cache.c, ctx.c, xv, xa, grid, w.guidance, 0.99, vv, va,
+                                     gv, ga, cos, ws, start_frame=start)
+    b.record()
+    torch.cuda.synchronize()
+    loop_ms = a.elapsed_time(b)
+    finite = bool(torch.isfinite(xv).all().item() and torch.isfinite(xa).all().item())
+    out = dict(base, metric="ms per DiT denoise step (40L, CFG b=2, 8064 cached tokens)", value=round(step_ms, 3),
+               unit="ms", higher_is_better=False, loop_16_steps_ms=round(loop_ms, 1), dit_calls=n,
+               reused_steps=[k for k, f in enumerate(flags) if f], cached_tokens=cache.length, outputs_finite=finite)
     print(json.dumps(out))
 
 
