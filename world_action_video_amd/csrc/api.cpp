@@ -64,6 +64,7 @@ wam_status check_cfg(const wam_config* c) {
   if (c->dim > 8192) return fail(WAM_E_SHAPE, "dim above 8192 is not supported");
   if (c->freq_dim % 8) return fail(WAM_E_SHAPE, "freq_dim must be a multiple of 8");
   if (c->patch_dim <= 0 || c->action_dim <= 0 || c->action_tokens < 0) return fail(WAM_E_SHAPE, "bad token sizes");
+  if (c->patch_dim > 64 || c->action_dim > 64) return fail(WAM_E_SHAPE, "patch_dim and action_dim must be <= 64");
   if (c->frames_per_chunk <= 0 || c->grid_h <= 0 || c->grid_w <= 0) return fail(WAM_E_SHAPE, "bad chunk geometry");
   const int lq = c->frames_per_chunk * c->grid_h * c->grid_w + c->action_tokens;
   if (lq % 8 || lq < 32) return fail(WAM_E_SHAPE, "tokens per chunk (%d) must be a multiple of 8 and at least 32", lq);
@@ -397,14 +398,14 @@ wam_status stack_pass(const wam_config* cfg, const wam_weights* w, wam_kv_cache*
   if (append) return WAM_OK;
 
   // heads: v_video / v_action per token group from y = LN(h) (1 + scale_h) + shift_h
-  GemmArgs gv = gemm_args(at<void>(ws, L.y), g.D, w->vo_w, g.D, w->vo_b, p.M, g.P, g.D);
-  gv.C = vv; gv.ldc = g.P; gv.rm = rowmap(p); gv.sel_group = 0;
-  HIP_TRY(launch_gemm(gv, g.dt, EPI_ROWSEL_F32, s));
-  if (g.La > 0) {
-    GemmArgs ga = gemm_args(at<void>(ws, L.y), g.D, w->ao_w, g.D, w->ao_b, p.M, g.A, g.D);
-    ga.C = va; ga.ldc = g.A; ga.rm = rowmap(p); ga.sel_group = 1;
-    HIP_TRY(launch_gemm(ga, g.dt, EPI_ROWSEL_F32, s));
-  }
+  HeadArgs hd{};
+  hd.Y = at<void>(ws, L.y); hd.M = p.M; hd.D = g.D;
+  hd.wv = w->vo_w; hd.bv = reinterpret_cast<const float*>(w->vo_b); hd.P = g.P;
+  hd.wa = w->ao_w; hd.ba = reinterpret_cast<const float*>(w->ao_b); hd.A = g.A;
+  hd.vv = vv; hd.va = va; hd.rm = rowmap(p);
+  hd.part = at<float>(ws, L.part);
+  hd.splits = g.D % 512 == 0 && g.D >= 2048 ? 8 : 1;   // 8 x M x 64 partials fit the split-K region
+  HIP_TRY(launch_head(hd, g.dt, s));
   return WAM_OK;
 }
 

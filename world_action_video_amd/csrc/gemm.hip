@@ -243,7 +243,7 @@ gemm_kernel(GemmArgs g) {
 // ------------------------------------------------------------------------------------------------
 static constexpr int EPI_PARTIAL = 16;   // internal: fp32 partial products of one split
 
-template <int EPI, bool IL = true>
+template <int EPI, int IL = 1>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm4_kernel(GemmArgs g, int splits) {
   using T = bf16_t;
@@ -361,20 +361,67 @@ gemm4_kernel(GemmArgs g, int splits) {
           sstore_q(nset, nset, c);
           gload_q(kt + 3, nset, c);
           mma(fc, 0, 16);
+          if constexpr (IL == 2) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
-          }
+            for (int k = 0; k < 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 2, 0);
+            }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
-          }
+            for (int k = 0; k < 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            for (int k = 0; k < 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+          } else if constexpr (IL == 3) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+            }
+          } else if constexpr (IL == 4) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         } else {
@@ -602,7 +649,7 @@ static hipError_t launch_cfg(const GemmArgs& a, Epi epi, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, bool IL = true>
+template <int EPI, int IL = 1>
 static void launch_g4(const GemmArgs& a, int splits, hipStream_t s) {
   const int items = ((a.M + 255) / 256) * ((a.N + 255) / 256) * splits;
   hipLaunchKernelGGL((gemm4_kernel<EPI, IL>), dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, a, splits);

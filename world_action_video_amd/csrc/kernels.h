@@ -153,6 +153,19 @@ struct FlowArgs {
   int nblocks;
 };
 hipError_t launch_flow_step(const FlowArgs& a, hipStream_t s);
+
+// Output heads: video rows (first Lv of each chunk) -> Wv [P][D], action rows -> Wa [A][D], written
+// token-major per branch to vv [br][n*Lv][P] and va [br][n*La][A]. K is split `splits` ways into
+// fp32 partials part[splits][M][64] (summed in order by the second kernel). P, A <= 64.
+struct HeadArgs {
+  const void* Y; int M, D;
+  const void* wv; const float* bv; int P;
+  const void* wa; const float* ba; int A;
+  float* vv; float* va;
+  RowMap rm;
+  float* part; int splits;
+};
+hipError_t launch_head(const HeadArgs& a, DType dt, hipStream_t s);
 int flow_partial_blocks(int nv);
 
 }  // namespace wam

@@ -640,4 +640,68 @@ hipError_t launch_flow_step(const FlowArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------------
+// Output heads. One wave per (row, K split); lane n accumulates output n (fp32, k in order) from
+// 8-element vectors of the row and of weight row n. The second kernel sums the splits in order, adds
+// the bias and writes the row to its token-group output.
+// ------------------------------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) head_partial_kernel(HeadArgs a) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), n = threadIdx.x & 63, sp = blockIdx.y;
+  if (m >= a.M) return;
+  const int loc = (m % a.rm.rows_per_branch) % a.rm.Lq;
+  const bool video = loc < a.rm.Lv;
+  const int nout = video ? a.P : a.A;
+  if (n >= nout) return;
+  const T* w = reinterpret_cast<const T*>(video ? a.wv : a.wa) + (long)n * a.D;
+  const T* y = reinterpret_cast<const T*>(a.Y) + (long)m * a.D;
+  const int kspan = a.D / a.splits, k0 = sp * kspan;
+  constexpr int EPU = 16 / sizeof(T);
+  float acc = 0.f;
+  for (int k = k0; k < k0 + kspan; k += 8) {
+    float yv[8], wv[8];
+#pragma unroll
+    for (int u = 0; u < 8 / EPU; ++u) {
+      const uint4 yy = *reinterpret_cast<const uint4*>(y + k + u * EPU);
+      const uint4 ww = *reinterpret_cast<const uint4*>(w + k + u * EPU);
+      const T* ye = reinterpret_cast<const T*>(&yy);
+      const T* we = reinterpret_cast<const T*>(&ww);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        yv[u * EPU + e] = Elem<T>::to_f(ye[e]);
+        wv[u * EPU + e] = Elem<T>::to_f(we[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(yv[e], wv[e], acc);
+  }
+  a.part[((long)sp * a.M + m) * 64 + n] = acc;
+}
+
+__global__ void __launch_bounds__(256) head_reduce_kernel(HeadArgs a) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), n = threadIdx.x & 63;
+  if (m >= a.M) return;
+  const int b = m / a.rm.rows_per_branch, rb = m % a.rm.rows_per_branch;
+  const int ch = rb / a.rm.Lq, loc = rb % a.rm.Lq;
+  const int nch = a.rm.rows_per_branch / a.rm.Lq, La = a.rm.Lq - a.rm.Lv;
+  const bool video = loc < a.rm.Lv;
+  const int nout = video ? a.P : a.A;
+  if (n >= nout) return;
+  float v = 0.f;
+  for (int sp = 0; sp < a.splits; ++sp) v += a.part[((long)sp * a.M + m) * 64 + n];
+  v += video ? a.bv[n] : a.ba[n];
+  if (video) a.vv[((long)(b * nch + ch) * a.rm.Lv + loc) * a.P + n] = v;
+  else a.va[((long)(b * nch + ch) * La + (loc - a.rm.Lv)) * a.A + n] = v;
+}
+
+hipError_t launch_head(const HeadArgs& a, DType dt, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  if (a.P > 64 || a.A > 64 || a.splits < 1 || a.D % (8 * a.splits)) return hipErrorInvalidValue;
+  const dim3 grid((a.M + 3) / 4, a.splits), block(256);
+  if (dt == DT_BF16) hipLaunchKernelGGL(head_partial_kernel<bf16_t>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(head_partial_kernel<float>, grid, block, 0, s, a);
+  hipLaunchKernelGGL(head_reduce_kernel, dim3((a.M + 3) / 4), block, 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace wam
