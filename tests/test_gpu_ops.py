@@ -163,6 +163,20 @@ def test_op_attention_value_row_pitch(gpu, d, Lq, kv_base, chunk_q, kv_total, v_
     assert rel_l2(out, ref) <= 1e-2
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Lq,kv_base,chunk_q,kv_total", [
+    (1024, 2053, 0, 3077),     # incremental, ragged last tile
+    (1100, 2000, 550, 3100),   # two query chunks over a long cache, chunk-causal
+])
+def test_op_attention_long_ranges(gpu, d, Lq, kv_base, chunk_q, kv_total):
+    """Query and key ranges of the long-context workload's order (1024+ queries over 3072+ keys, many
+    tiles per workgroup); one branch and two heads keep the oracle fast."""
+    print("attention-long", d, Lq, kv_base, chunk_q, kv_total, flush=True)
+    out, ref = _attn_case(gpu, "bf16", 1, 2, d, Lq, kv_base, chunk_q, kv_total, "l%d_%d_%d" % (d, Lq, kv_total))
+    assert np.all(np.isfinite(out))
+    assert rel_l2(out, ref) <= 1e-2
+
+
 def test_op_attention_full_shape_bf16(gpu):
     """Config-3 self-attention geometry: 928 cached + 464 current keys, 40 heads of 128, 2 branches."""
     print("attention-full", flush=True)

@@ -257,10 +257,9 @@ attn_kernel(AttnArgs a) {
 // bf16 kernel with 32-key tiles copied global -> LDS by the buffer unit (buffer_load ... lds), in a
 // ring of NS stages: tile t+NS-1 is requested while tile t computes, so about NS-1 tiles of compute
 // cover the memory latency and no registers stage the copies. Each 1 KB copy instruction writes
-// 64 lanes x 16 bytes contiguously; which 16-byte unit a lane fetches implements the XOR swizzle.
-// The copies are issued from inline assembly (M0 holds the LDS destination) and waited for with
-// explicit vmcnt counts before the barrier that hands a stage over, so the compiler neither drains
-// them at barriers nor waits for them before unrelated LDS reads.
+// 64 lanes x 16 bytes contiguously; which 16-byte unit a lane fetches implements the XOR swizzle. The copies are issued from inline assembly (M0 holds the LDS destination) and
+// waited for with explicit vmcnt counts before the barrier that hands a stage over, so the compiler
+// neither drains them at barriers nor waits for them before unrelated LDS reads.
 //
 // Softmax bookkeeping follows the online (running max) formulation with a lazy reference: the
 // running max used as the exponent offset is raised (and the output rescaled) only when a tile's max
@@ -273,7 +272,7 @@ attn_kernel(AttnArgs a) {
 // past kv_total are zeroed in LDS once their tile has landed, so stale rows never meet a zero
 // probability as 0 * inf or 0 * NaN.
 // ------------------------------------------------------------------------------------------------
-static constexpr int AT3_BKV = 32;
+static constexpr int AT3_BKV = 32;   // keys per tile
 
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
@@ -283,148 +282,239 @@ __device__ __forceinline__ void lds_copy16(int lds_addr, int voffset, __amdgpu_b
                :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
 }
 
-template <int D, int NS, int QA, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn3_kernel(AttnArgs a) {
-  constexpr int BQ = 32 * NW;                    // queries per workgroup
-  using T = bf16_t;
-  constexpr int KU = D / 8;                      // 16-byte units per K row
-  constexpr int K_ROWS_I = 64 / KU;              // K rows per 1 KB copy
-  constexpr int K_INSTR = AT3_BKV / K_ROWS_I;    // copies per K tile
-  constexpr int V_INSTR = D / 16;                // copies per V^T tile (16 rows of 64 bytes each)
-  constexpr int PER_WAVE = (K_INSTR + V_INSTR) / NW;
-  static_assert((K_INSTR + V_INSTR) % NW == 0, "copies split evenly over the waves");
-  constexpr int KB = AT3_BKV * D * 2, SB = KB + D * AT3_BKV * 2;   // K block, stage bytes
-  constexpr int DC = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint4 smem[NS * SB / 16];
-  char* lds = reinterpret_cast<char*>(smem);
-  const int lds_base = (int)(uintptr_t)lds;      // low 32 bits of a generic LDS pointer: its LDS address
-  auto kswz = [](int row) { return KU >= 16 ? (row & 15) : ((row >> 1) & 7); };
-  auto vswz = [](int row) { return (row >> 2) & 3; };   // 64-byte rows: four rows share a bank line
+// The compiler cannot see the lds_copy16 loads, so a wait it places for its own loads in a loop
+// header would also drain every copy in flight. Consuming the query fragments once before the loop
+// moves that wait out of the loop.
+__device__ __forceinline__ void settle(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5, l32 = lane & 31;
-  const int nq = (a.Lq_total + BQ - 1) / BQ;
-  const int items = nq * a.H * a.br;
-  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
-  const int per = items >> 3, rem = items & 7;
-  if (kx >= per + (xcd < rem ? 1 : 0)) return;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
-  const int qt = item % nq, bh_i = item / nq;
-  const int h = bh_i % a.H, b = bh_i / a.H;
-  const int qblk = qt * BQ;
-  const long bh = (long)b * a.H + h;
-  const T* Q = reinterpret_cast<const T*>(a.Q) + bh * a.q_bh_stride;
+// copies land in LDS without LDS-counter traffic: handing a stage over needs only vmcnt and a barrier
+__device__ __forceinline__ void lds_hand_over() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-  auto limit_of = [&](int q) {
+// One workgroup's share: NW waves x 32 queries of one (branch, head), taken in XCD-aware order
+// (consecutive query blocks of a head share one XCD's L2), with each query's chunk-causal key limit.
+template <int NW>
+struct AttnItem {
+  static constexpr int BQ = 32 * NW;
+  bool valid = false, q_ok = false;
+  int b = 0, h = 0, qblk = 0, n_tiles = 0, q = 0, my_lim = 0, wave_lim = 0;
+  long bh = 0;
+  __device__ __forceinline__ static int limit_of(const AttnArgs& a, int q) {
     int lim = a.kv_total;
     if (a.chunk_q > 0) {
       const int c = a.kv_base + (q / a.chunk_q + 1) * a.chunk_q;
       lim = c < lim ? c : lim;
     }
     return lim;
-  };
-  const int q_last = min(qblk + BQ, a.Lq_total) - 1;
-  const int n_tiles = (limit_of(q_last) + AT3_BKV - 1) / AT3_BKV;
-  const int q = qblk + wave * 32 + l32;
-  const bool q_ok = q < a.Lq_total;
-  const int my_lim = q_ok ? limit_of(q) : 0;
-  const int q_first = qblk + wave * 32;
-  const int wave_lim = q_first < a.Lq_total ? limit_of(q_first) : 0;
-
-  // buffer ranges: keys of this (branch, head) up to kv_total; all value rows of its block
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(reinterpret_cast<const T*>(a.K) + bh * a.k_bh_stride), (short)0, a.kv_total * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(reinterpret_cast<const T*>(a.Vt) + bh * a.v_bh_stride), (short)0, D * a.v_stride * 2, 0x00020000);
-  // Copies of a tile: waves 0 .. K_INSTR/PER_WAVE - 1 move the K block, the others the V^T block, so
-  // each wave has one source (no branches). Lane offsets for tile 0; tile t adds t * tile_stride.
-  static_assert(K_INSTR % PER_WAVE == 0, "a wave copies either keys or values");
-  const bool kwave = wave * PER_WAVE < K_INSTR;
-  const __amdgpu_buffer_rsrc_t rsrc = kwave ? rk : rv;
-  const int tile_stride = kwave ? AT3_BKV * D * 2 : AT3_BKV * 2;
-  int voff[PER_WAVE], ldst[PER_WAVE];
-#pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int i = wave * PER_WAVE + j;           // copy index within the tile
-    const int ki = i, vi = i - K_INSTR;
-    const int krow = ki * K_ROWS_I + lane / KU, vrow = vi * 16 + (lane >> 2);
-    voff[j] = kwave ? krow * D * 2 + ((lane % KU) ^ kswz(krow)) * 16
-                    : vrow * a.v_stride * 2 + ((lane & 3) ^ vswz(vrow)) * 16;
-    ldst[j] = kwave ? ki * 1024 : KB + vi * 1024;
   }
-  auto copy_tile = [&](int t, int stage) {
-    const int toff = min(t, n_tiles - 1) * tile_stride;   // past the end: refetch the last tile into a free stage
+  __device__ __forceinline__ AttnItem(const AttnArgs& a, int wave, int l32) {
+    const int nq = (a.Lq_total + BQ - 1) / BQ;
+    const int items = nq * a.H * a.br;
+    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+    const int per = items >> 3, rem = items & 7;
+    if (kx >= per + (xcd < rem ? 1 : 0)) return;
+    valid = true;
+    const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
+    const int qt = item % nq, bh_i = item / nq;
+    h = bh_i % a.H;
+    b = bh_i / a.H;
+    qblk = qt * BQ;
+    bh = (long)b * a.H + h;
+    const int q_last = min(qblk + BQ, a.Lq_total) - 1;
+    n_tiles = (limit_of(a, q_last) + AT3_BKV - 1) / AT3_BKV;
+    q = qblk + wave * 32 + l32;
+    q_ok = q < a.Lq_total;
+    my_lim = q_ok ? limit_of(a, q) : 0;
+    const int q_first = qblk + wave * 32;   // the limit grows with the query: the wave's first is its least
+    wave_lim = q_first < a.Lq_total ? limit_of(a, q_first) : 0;
+  }
+};
+
+// The LDS ring. Stage s holds the K block of a 32-key tile (32 rows of D bf16, 16-byte units XOR
+// swizzled by row) followed by its V^T block (D rows of 32 keys, 64 bytes each). Waves
+// 0 .. K_INSTR/PER_WAVE - 1 copy the K block and the others the V^T block, so each wave has a single
+// source and no branches. Lane offsets are for tile 0; tile t adds t * tile_stride. Requests past
+// the last tile refetch the last tile into a free stage.
+template <int D, int NS, int NW>
+struct KvRing {
+  static constexpr int KU = D / 8;                      // 16-byte units per K row
+  static constexpr int K_ROWS_I = 64 / KU;              // K rows per 1 KB copy
+  static constexpr int K_INSTR = AT3_BKV / K_ROWS_I;    // copies per K tile
+  static constexpr int V_INSTR = D / 16;                // copies per V^T tile (16 rows each)
+  static constexpr int PER_WAVE = (K_INSTR + V_INSTR) / NW;
+  static constexpr int KB = AT3_BKV * D * 2, SB = KB + D * AT3_BKV * 2;   // K block, stage bytes
+  static_assert((K_INSTR + V_INSTR) % NW == 0, "copies split evenly over the waves");
+  static_assert(K_INSTR % PER_WAVE == 0, "a wave copies either keys or values");
+  __device__ __forceinline__ static int kswz(int row) { return KU >= 16 ? (row & 15) : ((row >> 1) & 7); }
+  __device__ __forceinline__ static int vswz(int row) { return (row >> 2) & 3; }   // four 64-B rows share a bank line
+
+  int lds_base, tile_stride, last;
+  int voff[PER_WAVE], ldst[PER_WAVE];
+  __amdgpu_buffer_rsrc_t rsrc;
+
+  __device__ __forceinline__ KvRing(const AttnArgs& a, long bh, const char* lds, int wave, int lane, int n_tiles) {
+    using T = bf16_t;
+    lds_base = (int)(uintptr_t)lds;   // low 32 bits of a generic LDS pointer: its LDS address
+    last = n_tiles - 1;
+    // buffer ranges: keys of this (branch, head) up to kv_total; all value rows of its block
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(reinterpret_cast<const T*>(a.K) + bh * a.k_bh_stride), (short)0, a.kv_total * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(reinterpret_cast<const T*>(a.Vt) + bh * a.v_bh_stride), (short)0, D * a.v_stride * 2, 0x00020000);
+    const bool kwave = wave * PER_WAVE < K_INSTR;
+    rsrc = kwave ? rk : rv;
+    tile_stride = kwave ? AT3_BKV * D * 2 : AT3_BKV * 2;
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) lds_copy16(lds_base + stage * SB + ldst[j], voff[j] + toff, rsrc);
-  };
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int i = wave * PER_WAVE + j;   // copy index within the tile
+      const int ki = i, vi = i - K_INSTR;
+      const int krow = ki * K_ROWS_I + lane / KU, vrow = vi * 16 + (lane >> 2);
+      voff[j] = kwave ? krow * D * 2 + ((lane % KU) ^ kswz(krow)) * 16
+                      : vrow * a.v_stride * 2 + ((lane & 3) ^ vswz(vrow)) * 16;
+      ldst[j] = kwave ? ki * 1024 : KB + vi * 1024;
+    }
+  }
+  __device__ __forceinline__ void copy(int t, int stage) const {
+    const int toff = min(t, last) * tile_stride;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j)   // the LDS address is wave-uniform (M0 takes a scalar)
+      lds_copy16(__builtin_amdgcn_readfirstlane(lds_base + stage * SB + ldst[j]), voff[j] + toff, rsrc);
+  }
   // values past kv_total in the tile that holds kv_total (once it has landed) become zero
-  const int tail_tile = (a.kv_total % AT3_BKV) ? a.kv_total / AT3_BKV : -1;
-  auto zero_tail = [&](int stage) {
+  __device__ __forceinline__ static void zero_tail(char* lds, int stage, int tail_tile, int kv_total, int tid) {
+    using T = bf16_t;
     char* vb = lds + stage * SB + KB;
     const int k0 = tail_tile * AT3_BKV;
     for (int x = tid; x < D * 4; x += NW * 64) {
       const int row = x >> 2, u = x & 3;
       const int kfirst = k0 + u * 8;
-      if (kfirst + 8 <= a.kv_total) continue;
+      if (kfirst + 8 <= kv_total) continue;
       uint4* p = reinterpret_cast<uint4*>(vb + row * 64 + ((u ^ vswz(row)) * 16));
       uint4 v = *p;
       T* e = reinterpret_cast<T*>(&v);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (kfirst + k >= a.kv_total) e[k] = T(0);
+        if (kfirst + k >= kv_total) e[k] = T(0);
       *p = v;
     }
-  };
-  auto barrier = [&]() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
+  }
+};
+
+// Query fragments of the 32x32x16 products: lane l holds query l % 32, head-dim elements
+// 16 c + 8 (l / 32) .. + 8. Lanes past the last query read the last query's row (no branch around
+// the loads); their results are never stored.
+template <int D, int NW>
+__device__ __forceinline__ void load_q_frags(const AttnArgs& a, const AttnItem<NW>& it, int half, uint4 (&qf)[D / 16]) {
+  const bf16_t* Q = reinterpret_cast<const bf16_t*>(a.Q) + it.bh * a.q_bh_stride;
+  const int q_row = it.q_ok ? it.q : a.Lq_total - 1;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) qf[c] = *reinterpret_cast<const uint4*>(Q + (long)q_row * D + c * 16 + half * 8);
+}
+
+// Normalise, stage each wave's 32 x D block through LDS and write whole 16-byte row pieces.
+// The caller has drained every copy and synchronised the workgroup (the ring is reused).
+template <int D, int NW>
+__device__ __forceinline__ void store_output(uint4* smem, const floatx16 (&o)[D / 32], float l_run, const AttnArgs& a,
+                                             const AttnItem<NW>& it, int wave, int lane) {
+  using T = bf16_t;
+  const int l32 = lane & 31;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  constexpr int SROW = D + 8;
+  T* stage = reinterpret_cast<T*>(smem) + wave * 32 * SROW;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) stage[l32 * SROW + db * 32 + acc_row(e, lane)] = f32_to_bf16(o[db][e] * inv);
+  __syncthreads();
+  constexpr int ROW_UNITS = D / 8;
+  T* O = reinterpret_cast<T*>(a.O);
+  for (int u = lane; u < 32 * ROW_UNITS; u += 64) {
+    const int r = u / ROW_UNITS, cu = u % ROW_UNITS;
+    const int qq = it.qblk + wave * 32 + r;
+    if (qq < a.Lq_total)
+      *reinterpret_cast<uint4*>(O + ((long)it.b * a.Lq_total + qq) * ((long)a.H * D) + (long)it.h * D + cu * 8) =
+          reinterpret_cast<const uint4*>(stage + r * SROW)[cu];
+  }
+}
+
+// Lazy softmax reference update for one tile (tmax already in log2 units): raise the reference and
+// rescale only when some query of the wave exceeds it by more than 2^8.
+template <int DB>
+__device__ __forceinline__ void raise_reference(float tmax, float& m_ref, float& l_run, floatx16 (&o)[DB]) {
+  if (__any(tmax > m_ref + 8.f)) {
+    const float m_new = fmaxf(m_ref, tmax);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    m_ref = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+  }
+}
+
+// Per tile kt: scores from K fragments already in registers, value fragments requested, stage
+// hand-over (tile kt+1 visible, stage of tile kt-1 free), copy of tile kt+NS-1 requested, K
+// fragments of tile kt+1 requested, then the softmax and the value product, so LDS latency hides
+// behind matrix and vector work. Tile kt+1's copies were requested NS-3 tiles earlier.
+template <int D, int NS, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn3_kernel(AttnArgs a) {
+  using Ring = KvRing<D, NS, NW>;
+  constexpr int KB = Ring::KB, SB = Ring::SB, DC = D / 16, DB = D / 32;
+  static_assert(NS >= 4, "the hand-over waits for copies issued NS-3 tiles ahead");
+  static_assert(NW * 32 * (D + 8) * 2 <= NS * SB, "output staging fits in LDS");
+  __shared__ __attribute__((aligned(1024))) uint4 smem[NS * SB / 16];
+  char* lds = reinterpret_cast<char*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const AttnItem<NW> it(a, wave, l32);
+  if (!it.valid) return;
+  const int n_tiles = it.n_tiles;
+  const Ring ring(a, it.bh, lds, wave, lane, n_tiles);
+  const int tail_tile = (a.kv_total % AT3_BKV) ? a.kv_total / AT3_BKV : -1;
 
   uint4 qf[DC];
-#pragma unroll
-  for (int c = 0; c < DC; ++c)
-    qf[c] = q_ok ? *reinterpret_cast<const uint4*>(Q + (long)q * D + c * 16 + half * 8) : make_uint4(0, 0, 0, 0);
-
+  load_q_frags<D, NW>(a, it, half, qf);
   floatx16 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = floatx16{};
   float m_ref = -INFINITY, l_run = 0.f;   // m_ref in scaled (log2) units
   const float c = a.scale_log2;
 
-  // Software pipeline per tile kt: scores from K fragments already in registers, value fragments
-  // requested, stage hand-over (tile kt+1 visible, stage of tile kt-1 free), copy of tile kt+NS-1
-  // requested, K fragments of tile kt+1 requested, then the softmax and the value product, so LDS
-  // latency hides behind matrix and vector work. Tile kt+1's copies were requested NS-3 tiles earlier.
-  static_assert(NS >= 4, "the hand-over waits for copies issued NS-3 tiles ahead");
   const int srow = swap_bits_2_3(l32);
   uint4 kf[DC];
   auto load_kf = [&](int stage) {
     const char* sk = lds + stage * SB + srow * (D * 2);
 #pragma unroll
-    for (int cc = 0; cc < DC; ++cc) kf[cc] = *reinterpret_cast<const uint4*>(sk + (((2 * cc + half) ^ kswz(srow)) * 16));
-  };
-  auto hand_over = [&]() {   // copies land in LDS without LDS-counter traffic: only vmcnt and the barrier
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    for (int cc = 0; cc < DC; ++cc) kf[cc] = *reinterpret_cast<const uint4*>(sk + (((2 * cc + half) ^ Ring::kswz(srow)) * 16));
   };
   if (n_tiles > 0) {
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t) copy_tile(t, t);
-    vmcnt_wait<PER_WAVE * (NS - 2)>();
-    hand_over();
+    for (int t = 0; t < NS - 1; ++t) ring.copy(t, t);
+    vmcnt_wait<Ring::PER_WAVE * (NS - 2)>();
+    lds_hand_over();
     if (tail_tile == 0) {
-      zero_tail(0);
-      barrier();
+      Ring::zero_tail(lds, 0, tail_tile, a.kv_total, tid);
+      lds_barrier();
     }
     load_kf(0);
   }
+#pragma unroll
+  for (int cc = 0; cc < DC; ++cc) settle(qf[cc]);
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const int st = kt % NS;
-    const char* sb = lds + st * SB;
+    const char* sb = lds + (kt % NS) * SB;
     // (1) S^T = K Q^T for 32 keys (rows permuted) x this wave's 32 queries
     floatx16 s = floatx16{};
 #pragma unroll
@@ -438,29 +528,29 @@ attn3_kernel(AttnArgs a) {
       const int row = db * 32 + l32;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        vf[db][j] = *reinterpret_cast<const uint4*>(sb + KB + row * 64 + (((2 * j + half) ^ vswz(row)) * 16));
+        vf[db][j] = *reinterpret_cast<const uint4*>(sb + KB + row * 64 + (((2 * j + half) ^ Ring::vswz(row)) * 16));
     }
     // (3) hand-over: this wave's copies of tile kt+1 have landed, then everyone's
-    vmcnt_wait<PER_WAVE * (NS - 3)>();
-    hand_over();
+    vmcnt_wait<Ring::PER_WAVE * (NS - 3)>();
+    lds_hand_over();
     if (kt + 1 == tail_tile) {
-      zero_tail((kt + 1) % NS);
-      barrier();
+      Ring::zero_tail(lds, (kt + 1) % NS, tail_tile, a.kv_total, tid);
+      lds_barrier();
     }
     // (4) request tile kt+NS-1 into the stage of tile kt-1; (5) next tile's key fragments
-    copy_tile(kt + NS - 1, (kt + NS - 1) % NS);
+    ring.copy(kt + NS - 1, (kt + NS - 1) % NS);
     load_kf((kt + 1) % NS);
     // (6) softmax; register e of s holds key kt*32 + 16 (e / 8) + 8 half + (e % 8)
     const int key0 = kt * AT3_BKV;
     float tmax = -INFINITY;
-    if (key0 + AT3_BKV <= wave_lim) {
+    if (key0 + AT3_BKV <= it.wave_lim) {
 #pragma unroll
       for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s[e], s[e + 1]));
     } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = key0 + 16 * (e >> 3) + 8 * half + (e & 7);
-        s[e] = key < my_lim ? s[e] : -INFINITY;
+        s[e] = key < it.my_lim ? s[e] : -INFINITY;
         tmax = fmaxf(tmax, s[e]);
       }
     }
@@ -468,16 +558,7 @@ attn3_kernel(AttnArgs a) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
     }
-    if (__any(tmax > m_ref + 8.f)) {
-      const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-    }
+    raise_reference(tmax, m_ref, l_run, o);
     // a query with no visible key yet keeps m_ref = -inf and must produce p = 0, not NaN
     const float moff = m_ref == -INFINITY ? 0.f : m_ref;
     float p[16];
@@ -500,33 +581,14 @@ attn3_kernel(AttnArgs a) {
                                                          __builtin_bit_cast(bf16x8_t, pf[j]), o[db], 0, 0, 0);
   }
   vmcnt_wait<0>();
-  barrier();
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  constexpr int SROW = D + 8;
-  static_assert(NW * 32 * SROW * 2 <= NS * SB, "staging fits in LDS");
-  T* stage = reinterpret_cast<T*>(smem) + wave * 32 * SROW;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) stage[l32 * SROW + db * 32 + acc_row(e, lane)] = f32_to_bf16(o[db][e] * inv);
-  __syncthreads();
-  constexpr int ROW_UNITS = D / 8;
-  T* O = reinterpret_cast<T*>(a.O);
-  for (int u = lane; u < 32 * ROW_UNITS; u += 64) {
-    const int r = u / ROW_UNITS, cu = u % ROW_UNITS;
-    const int qq = qblk + wave * 32 + r;
-    if (qq < a.Lq_total)
-      *reinterpret_cast<uint4*>(O + ((long)b * a.Lq_total + qq) * ((long)a.H * D) + (long)h * D + cu * 8) =
-          reinterpret_cast<const uint4*>(stage + r * SROW)[cu];
-  }
+  lds_barrier();
+  store_output<D, NW>(smem, o, l_run, a, it, wave, lane);
 }
 
-template <int D, int NS = 4, int QA = 1, int NW = 4>
+template <int D, int NS = 4, int NW = 4>
 static hipError_t launch_attn3(const AttnArgs& a, hipStream_t s) {
   const int items = ((a.Lq_total + 32 * NW - 1) / (32 * NW)) * a.H * a.br;
-  hipLaunchKernelGGL((attn3_kernel<D, NS, QA, NW>), dim3(8 * ((items + 7) / 8)), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((attn3_kernel<D, NS, NW>), dim3(8 * ((items + 7) / 8)), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
