@@ -93,6 +93,11 @@ def test_validation_rejects_before_launch():
     st = lib.wam_kv_append(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(cx), 0x1000, 0x1000, 0,
                            0x1000, 16, None)
     assert st == wam.WAM_E_ARG and "workspace" in wam.wam_last_error() and kv.length == 0
+    blocks[c.layers - 1].g_q = 0x1008   # the kernels read vectors with 16-byte loads
+    st = lib.wam_kv_append(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(cx), 0x1000, 0x1000, 0,
+                           0x1000, 1 << 30, None)
+    assert st == wam.WAM_E_ARG and "g_q is not 16-byte aligned" in wam.wam_last_error() and kv.length == 0
+    blocks[c.layers - 1].g_q = 0x1000
     blocks[c.layers - 1].w_ff2 = None
     st = lib.wam_kv_append(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(cx), 0x1000, 0x1000, 0,
                            0x1000, 1 << 30, None)

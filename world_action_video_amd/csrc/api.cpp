@@ -117,11 +117,15 @@ const char* const kBlockNames[] = {"mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o",
                                    "w_cq", "b_cq", "g_cq", "w_ck", "b_ck", "g_ck", "w_cv", "b_cv", "w_co",
                                    "b_co", "w_ff1", "b_ff1", "w_ff2", "b_ff2"};
 
+bool unaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
+
 wam_status check_block(const wam_block_weights* b, int l) {
   if (!b) return fail(WAM_E_ARG, "block weights of layer %d are NULL", l);
   const void* const* p = reinterpret_cast<const void* const*>(b);
-  for (int i = 0; i < (int)(sizeof(wam_block_weights) / sizeof(void*)); ++i)
+  for (int i = 0; i < (int)(sizeof(wam_block_weights) / sizeof(void*)); ++i) {
     if (!p[i]) return fail(WAM_E_ARG, "layer %d: %s is NULL", l, kBlockNames[i]);
+    if (unaligned16(p[i])) return fail(WAM_E_ARG, "layer %d: %s is not 16-byte aligned", l, kBlockNames[i]);
+  }
   return WAM_OK;
 }
 
@@ -131,6 +135,9 @@ wam_status check_weights(const wam_config* c, const wam_weights* w, bool need_bl
     return fail(WAM_E_ARG, "time-embedding weights are NULL");
   if (!w->pe_w || !w->pe_b || !w->ae_w || !w->ae_b) return fail(WAM_E_ARG, "token-embedding weights are NULL");
   if (!w->head_mod || !w->vo_w || !w->vo_b || !w->ao_w || !w->ao_b) return fail(WAM_E_ARG, "head weights are NULL");
+  for (const void* q : {w->t_w1, w->t_b1, w->t_w2, w->t_b2, w->t_wp, w->t_bp, w->pe_w, w->pe_b, w->ae_w, w->ae_b,
+                        w->head_mod, w->vo_w, w->vo_b, w->ao_w, w->ao_b})
+    if (unaligned16(q)) return fail(WAM_E_ARG, "a global weight tensor is not 16-byte aligned");
   if (need_blocks) {
     if (!w->blocks) return fail(WAM_E_ARG, "blocks array is NULL");
     for (int l = 0; l < c->layers; ++l) {
@@ -143,6 +150,7 @@ wam_status check_weights(const wam_config* c, const wam_weights* w, bool need_bl
 
 wam_status check_cache(const Geo& g, const wam_kv_cache* kv, int rows) {
   if (!kv || !kv->k || !kv->v) return fail(WAM_E_ARG, "KV cache pointers are NULL");
+  if (unaligned16(kv->k) || unaligned16(kv->v)) return fail(WAM_E_ARG, "KV cache pointers are not 16-byte aligned");
   if (kv->branches != g.br) return fail(WAM_E_SHAPE, "cache branches %d != config branches %d", kv->branches, g.br);
   if (kv->capacity <= 0 || kv->capacity % 64) return fail(WAM_E_SHAPE, "cache capacity must be a positive multiple of 64");
   if (kv->length < 0 || kv->length % 8) return fail(WAM_E_SHAPE, "cache length must be a non-negative multiple of 8");
@@ -153,6 +161,7 @@ wam_status check_cache(const Geo& g, const wam_kv_cache* kv, int rows) {
 
 wam_status check_ctx(const Geo& g, const wam_ctx_kv* cx) {
   if (!cx || !cx->k || !cx->v) return fail(WAM_E_ARG, "condition KV pointers are NULL");
+  if (unaligned16(cx->k) || unaligned16(cx->v)) return fail(WAM_E_ARG, "condition KV pointers are not 16-byte aligned");
   if (cx->branches != g.br) return fail(WAM_E_SHAPE, "condition KV branches != config branches");
   if (cx->ctx_len != g.Lc) return fail(WAM_E_SHAPE, "condition length %d != %d", cx->ctx_len, g.Lc);
   if (cx->ctx_stride < g.Lc || cx->ctx_stride % 64) return fail(WAM_E_SHAPE, "ctx_stride must be a multiple of 64 >= ctx_len");

@@ -99,7 +99,10 @@ hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s) {
 // ------------------------------------------------------------------------------------------------
 // q/k RMSNorm over the full width + rotary embedding of video rows + scatter to head-major rows.
 // One wave per row; each lane owns groups of 8 consecutive channels (16-byte loads and stores; a
-// group never straddles a head since the head dim is a multiple of 8).
+// group never straddles a head since the head dim is a multiple of 8). The gain and the rotation are
+// linear, so they are applied to the raw row while the sum of squares is still being reduced:
+// y = rstd * R(x * g). Every load of the row (values, gain, rotation table) is then issued in one
+// round trip, and only the final scaling waits for the reduction.
 // ------------------------------------------------------------------------------------------------
 template <typename T, int GPL>
 __device__ __forceinline__ void qk_row(const QkNormArgs& a, int row, int lane) {
@@ -107,55 +110,57 @@ __device__ __forceinline__ void qk_row(const QkNormArgs& a, int row, int lane) {
   constexpr int UPG = 8 / EPU;                   // units per group of 8 channels
   const T* src = reinterpret_cast<const T*>(a.src) + (long)row * a.src_ld + a.src_col;
   const int ng = a.D / 8;
-  float x[GPL][8];
+  const int b = row / a.rows_per_branch, rb = row % a.rows_per_branch;
+  const bool rotate = a.rope && (rb % a.rm.Lq) < a.rm.Lv;   // video rows only
+  const int half_d = a.d / 2;
+  float y[GPL][8];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < GPL; ++k) {
     const int gi = lane + 64 * k;
-    if (gi < ng) {
-      uint4 u[UPG];
+    if (gi >= ng) continue;
+    const int ch0 = gi * 8;
+    uint4 u[UPG];
 #pragma unroll
-      for (int q = 0; q < UPG; ++q) u[q] = reinterpret_cast<const uint4*>(src + gi * 8)[q];
-      const T* e = reinterpret_cast<const T*>(u);
+    for (int q = 0; q < UPG; ++q) u[q] = reinterpret_cast<const uint4*>(src + ch0)[q];
+    const float4 g0 = reinterpret_cast<const float4*>(a.gain + ch0)[0], g1 = reinterpret_cast<const float4*>(a.gain + ch0)[1];
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const T* e = reinterpret_cast<const T*>(u);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        x[k][c] = Elem<T>::to_f(e[c]);
-        ss += x[k][c] * x[k][c];
+    for (int c = 0; c < 8; ++c) {
+      const float x = Elem<T>::to_f(e[c]);
+      ss += x * x;
+      y[k][c] = x * g[c];
+    }
+    if (rotate) {
+      const float2* cs = a.rope + (long)rb * half_d + (ch0 % a.d) / 2;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const float2 t = cs[pp];
+        const float r0 = y[k][2 * pp] * t.x - y[k][2 * pp + 1] * t.y;
+        const float r1 = y[k][2 * pp] * t.y + y[k][2 * pp + 1] * t.x;
+        y[k][2 * pp] = r0;
+        y[k][2 * pp + 1] = r1;
       }
     }
   }
   const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)a.D + a.eps);
-  const int b = row / a.rows_per_branch, rb = row % a.rows_per_branch;
-  const bool video = (rb % a.rm.Lq) < a.rm.Lv;
-  const int half_d = a.d / 2;
   T* dst = reinterpret_cast<T*>(a.dst);
 #pragma unroll
   for (int k = 0; k < GPL; ++k) {
     const int gi = lane + 64 * k;
     if (gi >= ng) continue;
-    const int ch0 = gi * 8;                       // first channel of the group
-    const int hh = ch0 / a.d, j0 = (ch0 % a.d) / 2;
-    float y[8];
+    const int ch0 = gi * 8, hh = ch0 / a.d;
+    T* o = dst + ((long)b * a.H + hh) * a.dst_bh_stride + (long)(a.dst_row0 + rb) * a.d + ch0 % a.d;
+    float v[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) y[c] = x[k][c] * rstd * a.gain[ch0 + c];
-    if (a.rope && video) {
-      const float2* cs = a.rope + (long)rb * half_d + j0;
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const float2 t = cs[pp];
-        const float r0 = y[2 * pp] * t.x - y[2 * pp + 1] * t.y;
-        const float r1 = y[2 * pp] * t.y + y[2 * pp + 1] * t.x;
-        y[2 * pp] = r0;
-        y[2 * pp + 1] = r1;
-      }
-    }
-    T* o = dst + ((long)b * a.H + hh) * a.dst_bh_stride + (long)(a.dst_row0 + rb) * a.d + 2 * j0;
+    for (int c = 0; c < 8; ++c) v[c] = y[k][c] * rstd;
     if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<uint4*>(o) = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
-                                                pack2_bf16(y[4], y[5]), pack2_bf16(y[6], y[7]));
+      *reinterpret_cast<uint4*>(o) = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]),
+                                                pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
     } else {
-      reinterpret_cast<float4*>(o)[0] = make_float4(y[0], y[1], y[2], y[3]);
-      reinterpret_cast<float4*>(o)[1] = make_float4(y[4], y[5], y[6], y[7]);
+      reinterpret_cast<float4*>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+      reinterpret_cast<float4*>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
     }
   }
 }
