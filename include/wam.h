@@ -219,10 +219,16 @@ wam_status wam_op_linear(wam_dtype dtype, const void *A, int lda, const void *W,
  * for branch b, head h, query q < Lq: softmax over keys j < limit(q) of (Q.K_j) / sqrt(head_dim), times V,
  * limit(q) = kv_total, or min(kv_total, kv_base + (q / chunk_q + 1) * chunk_q) when chunk_q > 0.
  *   Q  [br][H][Lq][d], K [br][H][k_rows][d] (k_rows >= kv_total), Vt [br][H][d][v_stride]
- *   (v_stride multiple of 8, >= kv_total), O [br*Lq][H*d]; all in dtype; d = 64 or 128. */
+ *   (v_stride multiple of 8, >= kv_total), O [br*Lq][H*d]; all in dtype; d = 64 or 128.
+ * ws / ws_bytes: optional device scratch (256-byte aligned). When the query blocks of 128 would fill
+ * fewer than half of the GPU's CUs and there are at least 8 key tiles of 32, bf16 attention splits
+ * each block's keys into up to 8 ranges (flash-decoding style) if the scratch holds their partial
+ * outputs (66 x 64 fp32 per 32 queries and range); the ranges are merged in a fixed order, so the
+ * result is deterministic, and equals the unsplit result up to rounding. Without scratch (NULL, or
+ * too small) nothing is split. The stack and block calls use their own workspace. */
 wam_status wam_op_attention(wam_dtype dtype, const void *Q, const void *K, const void *Vt, void *O, int br, int heads,
                             int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,
-                            void *stream);
+                            void *ws, size_t ws_bytes, void *stream);
 
 /* Host-side: forget every committed row ([WS1] continuous requests: at a window boundary the
  * old KV is released and the frame position restarts). No device work. */

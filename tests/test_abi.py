@@ -108,8 +108,12 @@ def test_op_validation():
     lib = _lib()
     assert lib.wam_op_linear(0, 0x1000, 64, 0x1000, 64, None, 0x1000, 64, 4, 4, 60, 0, None, 0, None) == wam.WAM_E_SHAPE
     assert lib.wam_op_linear(0, None, 64, 0x1000, 64, None, 0x1000, 64, 4, 4, 64, 0, None, 0, None) == wam.WAM_E_ARG
-    assert lib.wam_op_attention(0, 0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 96, 8, 8, 8, 0, 0, 8, None) == wam.WAM_E_SHAPE
-    assert lib.wam_op_attention(0, 0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 64, 8, 8, 12, 0, 0, 12, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_attention(0, 0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 96, 8, 8, 8, 0, 0, 8, None, 0,
+                                None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_attention(0, 0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 64, 8, 8, 12, 0, 0, 12, None, 0,
+                                None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_attention(0, 0x1000, 0x1000, 0x1000, 0x1000, 1, 1, 64, 8, 8, 8, 0, 0, 8, 0x1010, 4096,
+                                None) == wam.WAM_E_ARG
     assert lib.wam_flow_step(0x1000, 0x1000, 0x1000, 0x1000, 3, 5.0, 4, 4, 0.1, 0.1, None, None, None, None, None, 0,
                              None) == wam.WAM_E_SHAPE
     assert lib.wam_flow_step(0x1000, 0x1000, 0x1000, 0x1000, 2, 5.0, 4, 4, 0.1, 0.1, None, None, 0x1000, None, None, 0,

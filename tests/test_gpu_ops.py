@@ -102,7 +102,7 @@ def test_op_linear_full_size_sampled(gpu, M, N, K, split):
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-3)
 
 
-def _attn_case(gpu, dtype, br, H, d, Lq, kv_base, chunk_q, kv_total, tag, v_stride=None):
+def _attn_case(gpu, dtype, br, H, d, Lq, kv_base, chunk_q, kv_total, tag, v_stride=None, ws=None, runs=1):
     k_rows = ((kv_total + 63) // 64) * 64 + 64
     if v_stride is None:
         v_stride = ((kv_total + 63) // 64) * 64
@@ -116,11 +116,14 @@ def _attn_case(gpu, dtype, br, H, d, Lq, kv_base, chunk_q, kv_total, tag, v_stri
         vt[..., kv_total:] = np.nan
     k[:, :, kv_total:] = np.nan
     Q, K, VT = (to_device(x, dtype, gpu) for x in (q, k, vt))
-    Ot = torch.full((br * Lq, H * d), float("nan"), dtype=Q.dtype, device=gpu)
     dt = wam.WAM_BF16 if dtype == "bf16" else wam.WAM_F32
-    wam.wam_op_attention(dt, Q, K, VT, Ot, br, H, d, Lq, k_rows, v_stride, kv_base, chunk_q, kv_total)
-    torch.cuda.synchronize()
-    out = host(Ot).reshape(br, Lq, H, d).transpose(0, 2, 1, 3)
+    outs = []
+    for _ in range(runs):
+        Ot = torch.full((br * Lq, H * d), float("nan"), dtype=Q.dtype, device=gpu)
+        wam.wam_op_attention(dt, Q, K, VT, Ot, br, H, d, Lq, k_rows, v_stride, kv_base, chunk_q, kv_total, ws=ws)
+        torch.cuda.synchronize()
+        outs.append(host(Ot).reshape(br, Lq, H, d).transpose(0, 2, 1, 3))
+    out = outs[0] if runs == 1 else outs
     lim = np.full(Lq, kv_total)
     if chunk_q > 0:
         lim = np.minimum(kv_total, kv_base + (np.arange(Lq) // chunk_q + 1) * chunk_q)
@@ -175,6 +178,26 @@ def test_op_attention_long_ranges(gpu, d, Lq, kv_base, chunk_q, kv_total):
     out, ref = _attn_case(gpu, "bf16", 1, 2, d, Lq, kv_base, chunk_q, kv_total, "l%d_%d_%d" % (d, Lq, kv_total))
     assert np.all(np.isfinite(out))
     assert rel_l2(out, ref) <= 1e-2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Lq,kv_base,chunk_q,kv_total", [
+    (100, 1900, 0, 2000),      # few query blocks over a long cache: eight key ranges
+    (512, 0, 64, 512),         # full-sequence chunk-causal: some ranges hold no visible key for some queries
+    (300, 1500, 100, 1800),    # chunk-causal over a cache, ragged last tile
+])
+def test_op_attention_key_split(gpu, d, Lq, kv_base, chunk_q, kv_total):
+    """With scratch and few query blocks, bf16 attention splits the keys into ranges and merges them:
+    against the oracle, bit-identical across runs, and equal to the unsplit kernel up to rounding."""
+    print("attention-split", d, Lq, kv_base, chunk_q, kv_total, flush=True)
+    tag = "s%d_%d_%d_%d" % (d, Lq, chunk_q, kv_total)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=gpu)
+    (o1, o2), ref = _attn_case(gpu, "bf16", 1, 2, d, Lq, kv_base, chunk_q, kv_total, tag, ws=ws, runs=2)
+    plain, _ = _attn_case(gpu, "bf16", 1, 2, d, Lq, kv_base, chunk_q, kv_total, tag)
+    assert np.all(np.isfinite(o1))
+    assert rel_l2(o1, ref) <= 1e-2
+    assert np.array_equal(o1, o2)
+    assert rel_l2(o1, plain) <= 1e-2
 
 
 def test_op_attention_full_shape_bf16(gpu):

@@ -85,7 +85,7 @@ def load(path: str = LIB_PATH):
         "wam_flow_step": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P, S, P]),
         "wam_denoise_chunk": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, P, P, P, P, P, P, S, P, P, P]),
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
-        "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P]),
+        "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P, S, P]),
         "wam_kv_reset": (None, [KV]),
         "wam_last_error": (ctypes.c_char_p, []),
     }
@@ -193,9 +193,11 @@ def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, ws=None, 
 
 
 def wam_op_attention(dtype, Q, K, Vt, O, br, heads, head_dim, Lq, k_rows, v_stride, kv_base, chunk_q, kv_total,
-                     stream=None):
+                     ws=None, stream=None):
+    """``ws``: optional device scratch tensor for key-split partial outputs (None: no split)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().wam_op_attention(dtype, _ptr(Q), _ptr(K), _ptr(Vt), _ptr(O), br, heads, head_dim, Lq, k_rows,
-                                   v_stride, kv_base, chunk_q, kv_total, _stream(stream)))
+                                   v_stride, kv_base, chunk_q, kv_total, _ptr(ws), nbytes, _stream(stream)))
 
 
 def wam_kv_reset(cache: wam_kv_cache):

@@ -103,10 +103,13 @@ Layout layout_of(const Geo& g, int n) {
   const size_t cb = align256((size_t)g.br * g.Lc * g.D * g.esz);
   L.ctx_a = 0;
   L.ctx_b = cb;
-  // split-K partial products (up to 4 splits of the widest D-column product), clear of both uses above
+  // split-K partial products (up to 4 splits of the widest D-column product), clear of both uses above;
+  // the attention's key-split partials reuse the region (never live at the same time as a product's)
   const size_t Mmax = std::max(M, (size_t)g.br * g.Lc);
   L.part = align256(std::max(stack_total, 2 * cb));
   L.part_elems = (long)(4 * Mmax * g.D);
+  if (g.dt == DT_BF16)   // the largest split any key count can take for this many query rows
+    L.part_elems = std::max(L.part_elems, attn_split_floats((int)R, g.H, g.br, 1 << 28));
   L.total = L.part + align256((size_t)L.part_elems * 4);
   return L;
 }
@@ -271,6 +274,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   aa.v_stride = p.kv->capacity; aa.Lq_total = p.R; aa.H = g.H; aa.d = g.d; aa.br = g.br;
   aa.kv_base = len; aa.chunk_q = p.n > 1 ? g.Lq : 0; aa.kv_total = len + p.R;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
+  aa.part = part; aa.part_elems = part_n;
   HIP_TRY(launch_attention(aa, dt, p.s));
   // (5) h += gate1 * (o Wo^T + b), then (6) n3 = LN(h) w + b for the cross-attention queries
   {
@@ -302,6 +306,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     ca.v_bh_stride = (long)g.d * p.cx->ctx_stride; ca.v_stride = p.cx->ctx_stride;
     ca.Lq_total = p.R; ca.H = g.H; ca.d = g.d; ca.br = g.br; ca.kv_base = g.Lc; ca.chunk_q = 0; ca.kv_total = g.Lc;
     ca.scale_log2 = aa.scale_log2;
+    ca.part = part; ca.part_elems = part_n;
     HIP_TRY(launch_attention(ca, dt, p.s));
   }
   // h += o Wco^T + b, then (7) y2 = LN(h) (1 + scale2) + shift2
@@ -628,18 +633,20 @@ wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W,
 
 wam_status wam_op_attention(wam_dtype dtype, const void* Q, const void* K, const void* Vt, void* O, int br, int heads,
                             int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,
-                            void* stream) {
+                            void* ws, size_t ws_bytes, void* stream) {
   if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
   if (!Q || !K || !Vt || !O) return fail(WAM_E_ARG, "NULL operand");
   if (head_dim != 64 && head_dim != 128) return fail(WAM_E_SHAPE, "head_dim must be 64 or 128");
   if (br <= 0 || heads <= 0 || Lq < 0 || kv_total <= 0 || kv_base < 0) return fail(WAM_E_SHAPE, "bad sizes");
   if (k_rows < kv_total || v_stride < kv_total || v_stride % 8) return fail(WAM_E_SHAPE, "k_rows/v_stride too small");
+  if (ws && reinterpret_cast<uintptr_t>(ws) % 256) return fail(WAM_E_ARG, "workspace must be 256-byte aligned");
   AttnArgs a{};
   a.Q = Q; a.K = K; a.Vt = Vt; a.O = O;
   a.q_bh_stride = (long)Lq * head_dim; a.k_bh_stride = (long)k_rows * head_dim; a.v_bh_stride = (long)head_dim * v_stride;
   a.v_stride = v_stride; a.Lq_total = Lq; a.H = heads; a.d = head_dim; a.br = br;
   a.kv_base = kv_base; a.chunk_q = chunk_q; a.kv_total = kv_total;
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  a.part = reinterpret_cast<float*>(ws); a.part_elems = ws ? (long)(ws_bytes / 4) : 0;
   HIP_TRY(launch_attention(a, dtype == WAM_BF16 ? DT_BF16 : DT_F32, reinterpret_cast<hipStream_t>(stream)));
   return WAM_OK;
 }

@@ -19,6 +19,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 is written by the LDS-copy assembly
 
 namespace wam {
@@ -273,6 +275,8 @@ attn_kernel(AttnArgs a) {
 // probability as 0 * inf or 0 * NaN.
 // ------------------------------------------------------------------------------------------------
 static constexpr int AT3_BKV = 32;   // keys per tile
+static constexpr int AT3_NW = 4;     // waves (x 32 queries) per workgroup
+static constexpr int AT3_PART = 66 * 64;   // floats of one wave's key-split partial: up to 64 accumulators, max, sum
 
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
@@ -301,11 +305,13 @@ __device__ __forceinline__ void lds_barrier() {
 
 // One workgroup's share: NW waves x 32 queries of one (branch, head), taken in XCD-aware order
 // (consecutive query blocks of a head share one XCD's L2), with each query's chunk-causal key limit.
+// With `splits` > 1 each query block is a unit of `splits` workgroups, one per contiguous range of
+// its key tiles; the units of one block are consecutive, so they also share an XCD.
 template <int NW>
 struct AttnItem {
   static constexpr int BQ = 32 * NW;
   bool valid = false, q_ok = false;
-  int b = 0, h = 0, qblk = 0, n_tiles = 0, q = 0, my_lim = 0, wave_lim = 0;
+  int item = 0, split = 0, b = 0, h = 0, qblk = 0, n_tiles = 0, q = 0, my_lim = 0, wave_lim = 0;
   long bh = 0;
   __device__ __forceinline__ static int limit_of(const AttnArgs& a, int q) {
     int lim = a.kv_total;
@@ -315,15 +321,29 @@ struct AttnItem {
     }
     return lim;
   }
-  __device__ __forceinline__ AttnItem(const AttnArgs& a, int wave, int l32) {
-    const int nq = (a.Lq_total + BQ - 1) / BQ;
-    const int items = nq * a.H * a.br;
+  __device__ __forceinline__ static int blocks(const AttnArgs& a) { return (a.Lq_total + BQ - 1) / BQ * a.H * a.br; }
+  // the workgroup's unit from its index in XCD order
+  __device__ __forceinline__ AttnItem(const AttnArgs& a, int wave, int l32, int splits) {
+    const int units = blocks(a) * splits;
     const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
-    const int per = items >> 3, rem = items & 7;
+    const int per = units >> 3, rem = units & 7;
     if (kx >= per + (xcd < rem ? 1 : 0)) return;
+    const int unit = xcd * per + (xcd < rem ? xcd : rem) + kx;
+    init(a, unit / splits, wave, l32);
+    split = unit % splits;
+  }
+  // query block `it` directly (the merge of key-split partials)
+  __device__ __forceinline__ static AttnItem block(const AttnArgs& a, int it, int wave, int l32) {
+    AttnItem r;
+    r.init(a, it, wave, l32);
+    return r;
+  }
+  AttnItem() = default;
+  __device__ __forceinline__ void init(const AttnArgs& a, int it, int wave, int l32) {
     valid = true;
-    const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
-    const int qt = item % nq, bh_i = item / nq;
+    item = it;
+    const int nq = (a.Lq_total + BQ - 1) / BQ;
+    const int qt = it % nq, bh_i = it / nq;
     h = bh_i % a.H;
     b = bh_i / a.H;
     qblk = qt * BQ;
@@ -479,10 +499,12 @@ attn3_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  const AttnItem<NW> it(a, wave, l32);
+  const AttnItem<NW> it(a, wave, l32, a.kv_splits);
   if (!it.valid) return;
-  const int n_tiles = it.n_tiles;
-  const Ring ring(a, it.bh, lds, wave, lane, n_tiles);
+  // this workgroup's key tiles [t0, t1): all of them, or one contiguous range of a key split
+  const int t0 = it.split * it.n_tiles / a.kv_splits, t1 = (it.split + 1) * it.n_tiles / a.kv_splits;
+  const int nt = t1 - t0;
+  const Ring ring(a, it.bh, lds, wave, lane, t1);
   const int tail_tile = (a.kv_total % AT3_BKV) ? a.kv_total / AT3_BKV : -1;
 
   uint4 qf[DC];
@@ -500,12 +522,13 @@ attn3_kernel(AttnArgs a) {
 #pragma unroll
     for (int cc = 0; cc < DC; ++cc) kf[cc] = *reinterpret_cast<const uint4*>(sk + (((2 * cc + half) ^ Ring::kswz(srow)) * 16));
   };
-  if (n_tiles > 0) {
+  // stage of the range's tile t0 + i is i % NS
+  if (nt > 0) {
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t) ring.copy(t, t);
+    for (int t = 0; t < NS - 1; ++t) ring.copy(t0 + t, t);
     vmcnt_wait<Ring::PER_WAVE * (NS - 2)>();
     lds_hand_over();
-    if (tail_tile == 0) {
+    if (tail_tile == t0) {
       Ring::zero_tail(lds, 0, tail_tile, a.kv_total, tid);
       lds_barrier();
     }
@@ -513,8 +536,9 @@ attn3_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int cc = 0; cc < DC; ++cc) settle(qf[cc]);
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const char* sb = lds + (kt % NS) * SB;
+  for (int i = 0; i < nt; ++i) {
+    const int kt = t0 + i;
+    const char* sb = lds + (i % NS) * SB;
     // (1) S^T = K Q^T for 32 keys (rows permuted) x this wave's 32 queries
     floatx16 s = floatx16{};
 #pragma unroll
@@ -534,12 +558,12 @@ attn3_kernel(AttnArgs a) {
     vmcnt_wait<Ring::PER_WAVE * (NS - 3)>();
     lds_hand_over();
     if (kt + 1 == tail_tile) {
-      Ring::zero_tail(lds, (kt + 1) % NS, tail_tile, a.kv_total, tid);
+      Ring::zero_tail(lds, (i + 1) % NS, tail_tile, a.kv_total, tid);
       lds_barrier();
     }
     // (4) request tile kt+NS-1 into the stage of tile kt-1; (5) next tile's key fragments
-    ring.copy(kt + NS - 1, (kt + NS - 1) % NS);
-    load_kf((kt + 1) % NS);
+    ring.copy(kt + NS - 1, (i + NS - 1) % NS);
+    load_kf((i + 1) % NS);
     // (6) softmax; register e of s holds key kt*32 + 16 (e / 8) + 8 half + (e % 8)
     const int key0 = kt * AT3_BKV;
     float tmax = -INFINITY;
@@ -582,14 +606,86 @@ attn3_kernel(AttnArgs a) {
   }
   vmcnt_wait<0>();
   lds_barrier();
-  store_output<D, NW>(smem, o, l_run, a, it, wave, lane);
+  if (a.kv_splits == 1) {
+    store_output<D, NW>(smem, o, l_run, a, it, wave, lane);
+  } else {   // unnormalised partial of this key range: accumulators (float4 q of lane l at (q*64 + l)*4),
+             // then the reference max and the row-sum share of each lane
+    float* dst = a.part + ((long)(it.item * a.kv_splits + it.split) * NW + wave) * AT3_PART;
+#pragma unroll
+    for (int q = 0; q < DB * 4; ++q)
+      reinterpret_cast<float4*>(dst)[q * 64 + lane] =
+          make_float4(o[q >> 2][4 * (q & 3)], o[q >> 2][4 * (q & 3) + 1], o[q >> 2][4 * (q & 3) + 2], o[q >> 2][4 * (q & 3) + 3]);
+    dst[64 * 64 + lane] = m_ref;
+    dst[65 * 64 + lane] = l_run;
+  }
 }
 
-template <int D, int NS = 4, int NW = 4>
+// Merge of the key-split partials of one query block (one workgroup): every lane combines the
+// values it held in each range, p-weighted by 2^(m_s - M) with M the largest reference, in range
+// order (deterministic), then normalises and stores like the unsplit kernel. A range with no
+// visible key for a query (reference -inf) contributes nothing.
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) attn_merge_kernel(AttnArgs a) {
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint4 smem[NW * 32 * (D + 8) * 2 / 16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const AttnItem<NW> it = AttnItem<NW>::block(a, (int)blockIdx.x, wave, lane & 31);
+  const int S = a.kv_splits;
+  const float* base = a.part + ((long)it.item * S * NW + wave) * AT3_PART;
+  constexpr long SPLIT = (long)NW * AT3_PART;
+  float m = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) m = fmaxf(m, base[sp * SPLIT + 64 * 64 + lane]);
+  floatx16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = floatx16{};
+  float l = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    const float* p = base + sp * SPLIT;
+    float4 v[DB * 4];   // all of the range's values requested before any is used
+#pragma unroll
+    for (int q = 0; q < DB * 4; ++q) v[q] = reinterpret_cast<const float4*>(p)[q * 64 + lane];
+    const float ms = p[64 * 64 + lane], ls = p[65 * 64 + lane];
+    const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+    l += f * ls;
+#pragma unroll
+    for (int q = 0; q < DB * 4; ++q) {
+      floatx16& acc = o[q >> 2];
+      const int e = 4 * (q & 3);
+      acc[e] += f * v[q].x;
+      acc[e + 1] += f * v[q].y;
+      acc[e + 2] += f * v[q].z;
+      acc[e + 3] += f * v[q].w;
+    }
+  }
+  store_output<D, NW>(smem, o, l, a, it, wave, lane);
+}
+
+// a.kv_splits ranges per query block; above one, the merge kernel follows
+template <int D, int NS = 4, int NW = AT3_NW>
 static hipError_t launch_attn3(const AttnArgs& a, hipStream_t s) {
-  const int items = ((a.Lq_total + 32 * NW - 1) / (32 * NW)) * a.H * a.br;
-  hipLaunchKernelGGL((attn3_kernel<D, NS, NW>), dim3(8 * ((items + 7) / 8)), dim3(NW * 64), 0, s, a);
+  const int blocks = ((a.Lq_total + 32 * NW - 1) / (32 * NW)) * a.H * a.br;
+  const int units = blocks * a.kv_splits;
+  hipLaunchKernelGGL((attn3_kernel<D, NS, NW>), dim3(8 * ((units + 7) / 8)), dim3(NW * 64), 0, s, a);
+  if (a.kv_splits > 1) hipLaunchKernelGGL((attn_merge_kernel<D, NW>), dim3(blocks), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
+}
+
+// Key split (flash-decoding style): only when the query blocks fill fewer than half of the 256 CUs
+// and every range keeps at least four tiles; ranges up to the CU count, at most eight.
+int attn_kv_splits(int Lq_total, int H, int br, int kv_total) {
+  const int blocks = (Lq_total + 32 * AT3_NW - 1) / (32 * AT3_NW) * H * br;
+  const int n_tiles = (kv_total + AT3_BKV - 1) / AT3_BKV;
+  if (blocks <= 0 || blocks >= 128 || n_tiles < 8) return 1;
+  const int sp = std::min(std::min(8, (256 + blocks - 1) / blocks), n_tiles / 4);
+  return sp >= 2 ? sp : 1;
+}
+
+long attn_split_floats(int Lq_total, int H, int br, int kv_total) {
+  const int sp = attn_kv_splits(Lq_total, H, br, kv_total);
+  if (sp == 1) return 0;
+  const long blocks = (Lq_total + 32 * AT3_NW - 1) / (32 * AT3_NW) * (long)H * br;
+  return blocks * sp * AT3_NW * AT3_PART;
 }
 
 template <typename T, int D>
@@ -610,8 +706,12 @@ hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s) {
                          (long)a.d * a.v_stride * 2 < (1L << 31) && (long)a.kv_total * a.d * 2 < (1L << 31) &&
                          reinterpret_cast<uintptr_t>(a.K) % 16 == 0 && reinterpret_cast<uintptr_t>(a.Vt) % 16 == 0 &&
                          (a.k_bh_stride * 2) % 16 == 0 && (a.v_bh_stride * 2) % 16 == 0;
-    if (copy_ok && a.d == 128) return launch_attn3<128>(a, s);
-    if (copy_ok && a.d == 64) return launch_attn3<64>(a, s);
+    AttnArgs b = a;
+    b.kv_splits = attn_kv_splits(a.Lq_total, a.H, a.br, a.kv_total);
+    if (b.kv_splits > 1 && (!a.part || a.part_elems < attn_split_floats(a.Lq_total, a.H, a.br, a.kv_total)))
+      b.kv_splits = 1;   // no scratch for the partials: one range per block
+    if (copy_ok && a.d == 128) return launch_attn3<128>(b, s);
+    if (copy_ok && a.d == 64) return launch_attn3<64>(b, s);
     if (a.d == 128) return launch_t<bf16_t, 128>(a, s);
     if (a.d == 64) return launch_t<bf16_t, 64>(a, s);
   } else {

@@ -54,8 +54,15 @@ struct AttnArgs {
   int chunk_q;        // queries per chunk (for the chunk-causal limit); <= 0: no chunk limit
   int kv_total;       // total keys present (kv_base + current keys)
   float scale_log2;   // log2(e) / sqrt(d)
+  float* part;        // scratch for key-split partial outputs (nullptr: never split)
+  long part_elems;    // capacity of `part` in floats
+  int kv_splits;      // set by launch_attention: key ranges per query block (1 = no split)
 };
 hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s);
+// Key ranges per query block the bf16 kernel takes for these sizes (flash-decoding-style split when
+// the query blocks alone would leave most CUs idle), and the scratch floats that split needs.
+int attn_kv_splits(int Lq_total, int H, int br, int kv_total);
+long attn_split_floats(int Lq_total, int H, int br, int kv_total);
 
 // ---- row-wise kernels -----------------------------------------------------------------------------
 enum NormMode {
