@@ -230,6 +230,20 @@ wam_status wam_op_attention(wam_dtype dtype, const void *Q, const void *K, const
                             int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,
                             void *ws, size_t ws_bytes, void *stream);
 
+/* Sliding attention window ([WS1] continuous requests: the attention window releases old KV and
+ * the frame position restarts; [HYPER] 方法: cached clean chunks are the only past a chunk sees).
+ * Drops the oldest `drop_rows` committed rows of every layer and branch (whole chunks: a multiple
+ * of the tokens per chunk, at most cache->length) and moves the kept chunks' frame positions back by
+ * `frame_shift` frames: the frame-axis rotary pairs of their video keys are rotated by
+ * -frame_shift * freq(j) (rotations compose, so a key rotated for frame f becomes the key of frame
+ * f - frame_shift); values and action keys only move. The rows are moved in place, on `stream`; on
+ * success cache->length -= drop_rows, and the next chunk should be appended / denoised with its start
+ * frame lowered by frame_shift (frame_shift = dropped chunks x frames_per_chunk restarts the window's
+ * positions at its first kept chunk). drop_rows = 0 does nothing. Errors: WAM_E_ARG (NULL or
+ * misaligned pointers), WAM_E_SHAPE (drop_rows not whole chunks or above the length; cache
+ * geometry); nothing is enqueued then. */
+wam_status wam_kv_evict(const wam_config *cfg, wam_kv_cache *cache, int drop_rows, int frame_shift, void *stream);
+
 /* Host-side: forget every committed row ([WS1] continuous requests: at a window boundary the
  * old KV is released and the frame position restarts). No device work. */
 void wam_kv_reset(wam_kv_cache *cache);

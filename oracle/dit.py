@@ -434,6 +434,28 @@ def kv_append(model: Model, cache: KVCache, ctx_kv, x_video: Array, x_action: Ar
     stack_forward(model, cache, ctx_kv, x_video, x_action, [1.0], [1.0], 1, start_frame, dt, commit=True)
 
 
+def kv_evict(w, cache: KVCache, drop_rows: int, frame_shift: int) -> None:
+    """Slide the attention window ([WS1] continuous requests: the window releases old KV and the
+    frame position restarts): drop the oldest ``drop_rows`` cached rows (whole chunks) and move the
+    kept chunks' frame positions back by ``frame_shift``. Cached keys are stored after RoPE, so the
+    video keys are rotated once more with position (-frame_shift, 0, 0): the frame-axis pairs turn
+    by -frame_shift * freq, the row and column pairs by zero. Values and action keys only move."""
+    Lq, Lv = w.chunk_tokens, w.video_tokens
+    assert 0 <= drop_rows <= cache.length and drop_rows % Lq == 0
+    keep = cache.length - drop_rows
+    is_video = (np.arange(keep) % Lq) < Lv
+    H, d = w.heads, w.head_dim
+    pos = np.tile(np.array([[-frame_shift, 0, 0]], dtype=np.int64), (int(is_video.sum()), 1))
+    for l in range(len(cache.k)):
+        k = cache.k[l][:, drop_rows:].copy()
+        for b in range(k.shape[0]):
+            kb = k[b].reshape(keep, H, d)
+            kb[is_video] = apply_rope(kb[is_video], pos, d, w.rope_theta)
+            k[b] = kb.reshape(keep, H * d)
+        cache.k[l] = k
+        cache.v[l] = cache.v[l][:, drop_rows:].copy()
+
+
 # ----------------------------------------------------------------------------------------------
 # Guidance, Euler update, velocity reuse ([N569] real-time optimisations; BASELINE Euler reading)
 # ----------------------------------------------------------------------------------------------

@@ -144,3 +144,18 @@ def test_denoise_chunk_validation():
     assert lib.wam_denoise_chunk(*args(grid, 2, gv=None)) == wam.WAM_E_ARG
     # valid loop arguments: the first DiT pass rejects the missing weights
     assert lib.wam_denoise_chunk(*args(grid, 2)) == wam.WAM_E_ARG and "weights" in wam.wam_last_error()
+
+
+def test_kv_evict_validation():
+    """Eviction keeps whole chunks and rejects bad requests on the host; nothing changes then."""
+    lib = _lib()
+    c = _cfg(1)
+    lq = WORKLOADS[1].chunk_tokens
+    kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 512, 2 * lq)
+    assert lib.wam_kv_evict(ctypes.byref(c), ctypes.byref(kv), lq - 8, 2, None) == wam.WAM_E_SHAPE
+    assert kv.length == 2 * lq
+    assert lib.wam_kv_evict(ctypes.byref(c), ctypes.byref(kv), 3 * lq, 2, None) == wam.WAM_E_SHAPE
+    assert lib.wam_kv_evict(ctypes.byref(c), None, lq, 2, None) == wam.WAM_E_ARG
+    bad = wam.wam_kv_cache(0x1008, 0x1000, 2, 512, 2 * lq)
+    assert lib.wam_kv_evict(ctypes.byref(c), ctypes.byref(bad), lq, 2, None) == wam.WAM_E_ARG
+    assert lib.wam_kv_evict(ctypes.byref(c), ctypes.byref(kv), 0, 2, None) == wam.WAM_OK and kv.length == 2 * lq

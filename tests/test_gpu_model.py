@@ -274,6 +274,57 @@ def test_flow_step_matches_oracle(gpu):
     assert np.array_equal(Gv2.cpu().numpy(), vv[0])
 
 
+def cache_host(dc, length):
+    """Device cache -> the oracle's layout: per layer [br, length, H*d] keys and values (float32)."""
+    k = dc.k[..., :length, :].float().cpu().numpy()    # [L, br, H, len, d]
+    v = dc.v[..., :length].float().cpu().numpy()       # [L, br, H, d, len]
+    L, br, H, n, d = k.shape
+    return O.KVCache([k[l].transpose(0, 2, 1, 3).reshape(br, n, H * d) for l in range(L)],
+                     [v[l].transpose(0, 3, 1, 2).reshape(br, n, H * d) for l in range(L)])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kv_evict_matches_oracle(gpu, tiny_oracle, dtype):
+    """Window eviction on the GPU (one of three cached chunks dropped, positions moved back by one
+    chunk of frames) against the oracle's eviction of the same cache contents, then a denoising
+    step on the evicted cache against the oracle's step on its own evicted cache."""
+    w, m, ckv = tiny_oracle
+    Lq, Fc = w.chunk_tokens, w.frames_per_chunk
+    print("kv-evict", dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache(4)
+    for c in range(3):
+        rig.append(dc, x1v[c], x1a[c], c * Fc)
+    torch.cuda.synchronize()
+    before = cache_host(dc, 3 * Lq)
+    ref = O.KVCache([k.astype(np.float64) for k in before.k], [v.astype(np.float64) for v in before.v])
+    O.kv_evict(w, ref, Lq, Fc)
+    wam.wam_kv_evict(rig.m.cfg, dc.c, Lq, Fc)
+    torch.cuda.synchronize()
+    assert dc.length == 2 * Lq
+    after = cache_host(dc, 2 * Lq)
+    for l in range(w.layers):
+        assert np.array_equal(after.v[l], ref.v[l])          # values only move
+        scale = np.abs(before.k[l]).max()
+        if dtype == "f32":
+            assert np.abs(after.k[l] - ref.k[l]).max() <= 1e-6 * scale
+        else:   # one rounding of the rotated key to bf16
+            assert np.all(np.abs(after.k[l] - ref.k[l]) <= np.abs(ref.k[l]) * 2.0 ** -8 + 1e-6 * scale)
+    # the next chunk, denoised at its position lowered by the shift
+    xv = O.interpolate(x1v[2], epv[2], 0.4)
+    xa = O.interpolate(x1a[2], epa[2], 0.4)
+    gv, ga = rig.step(dc, 1, xv, xa, [0.4], [0.4], 2 * Fc)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    for c in range(3):
+        O.kv_append(m, cache, ckv, x1v[c], x1a[c], c * Fc)
+    O.kv_evict(w, cache, Lq, Fc)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, xv, xa, [0.4], [0.4], 1, 2 * Fc)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
 @pytest.mark.timeout(900)
 def test_full_width_block_bf16(gpu):
     """One Wan-14B-sized block (width 5120, 40 heads of 128, FFN 13824), 769 condition tokens, one cached

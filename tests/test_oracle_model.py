@@ -198,3 +198,49 @@ def test_workload_shapes_match_pages():
     # 320x176 frames, 8x spatial VAE compression, 2x2 patches -> 20 x 11 patch grid
     assert (vals["frame_w"] // vals["vae_spatial"] // 2, vals["frame_h"] // vals["vae_spatial"] // 2) == (w.grid_w, w.grid_h)
     assert synth.BASE_SEED == vals["seed"]
+
+
+def test_kv_evict_equals_appending_at_shifted_frames(tiny):
+    # Layer-0 keys and values of a chunk depend on its own tokens and frame positions only (no
+    # attention precedes them). So after evicting the first of three cached chunks and moving the
+    # window back by one chunk of frames, the layer-0 rows of the two kept chunks must equal those
+    # of the same chunks appended to an empty cache at frames lowered by that shift: keys up to the
+    # rounding of one extra rotation, values exactly. Action rows are never rotated.
+    w, m, _, ckv, x1v, x1a, _, _ = tiny
+    Lq, Fc = w.chunk_tokens, w.frames_per_chunk
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    for c in range(3):
+        O.kv_append(m, cache, ckv, x1v[c], x1a[c], c * Fc)
+    ref = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    for c in (1, 2):
+        O.kv_append(m, ref, ckv, x1v[c], x1a[c], (c - 1) * Fc)
+    O.kv_evict(w, cache, Lq, Fc)
+    assert cache.length == 2 * Lq
+    assert np.array_equal(cache.v[0], ref.v[0])
+    scale = np.abs(ref.k[0]).max()
+    assert np.abs(cache.k[0] - ref.k[0]).max() <= 1e-5 * scale
+    video = (np.arange(2 * Lq) % Lq) < w.video_tokens
+    assert np.array_equal(cache.k[0][:, ~video], ref.k[0][:, ~video])
+
+
+def test_kv_evict_without_shift_only_drops_rows(tiny):
+    w, m, _, ckv, x1v, x1a, _, _ = tiny
+    Lq, Fc = w.chunk_tokens, w.frames_per_chunk
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    for c in range(2):
+        O.kv_append(m, cache, ckv, x1v[c], x1a[c], c * Fc)
+    before = [k.copy() for k in cache.k], [v.copy() for v in cache.v]
+    O.kv_evict(w, cache, Lq, 0)
+    for l in range(len(m.layers)):
+        assert np.array_equal(cache.k[l], before[0][l][:, Lq:])
+        assert np.array_equal(cache.v[l], before[1][l][:, Lq:])
+
+
+def test_rotary_composition_is_a_position_shift():
+    # The eviction's extra rotation by (-s, 0, 0) equals rotating at the shifted position once.
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((40, 4, 64))
+    pos = np.stack([rng.integers(0, 30, 40), rng.integers(0, 8, 40), rng.integers(0, 8, 40)], 1)
+    twice = O.apply_rope(O.apply_rope(x, pos, 64, 1e4), np.tile([[-7, 0, 0]], (40, 1)), 64, 1e4)
+    once = O.apply_rope(x, pos - np.array([7, 0, 0]), 64, 1e4)
+    assert np.abs(twice - once).max() <= 1e-12

@@ -17,7 +17,7 @@ WAM_OK, WAM_E_ARG, WAM_E_SHAPE, WAM_E_CAPACITY, WAM_E_HIP, WAM_E_UNSUPPORTED = 0
 WAM_BF16, WAM_F32 = 0, 1
 
 EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
-           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_op_linear", "wam_op_attention", "wam_kv_reset",
+           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_op_linear", "wam_op_attention", "wam_kv_evict", "wam_kv_reset",
            "wam_last_error")
 
 
@@ -86,6 +86,7 @@ def load(path: str = LIB_PATH):
         "wam_denoise_chunk": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, P, P, P, P, P, P, S, P, P, P]),
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P, S, P]),
+        "wam_kv_evict": (I, [CFG, KV, I, I, P]),
         "wam_kv_reset": (None, [KV]),
         "wam_last_error": (ctypes.c_char_p, []),
     }
@@ -198,6 +199,10 @@ def wam_op_attention(dtype, Q, K, Vt, O, br, heads, head_dim, Lq, k_rows, v_stri
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().wam_op_attention(dtype, _ptr(Q), _ptr(K), _ptr(Vt), _ptr(O), br, heads, head_dim, Lq, k_rows,
                                    v_stride, kv_base, chunk_q, kv_total, _ptr(ws), nbytes, _stream(stream)))
+
+
+def wam_kv_evict(cfg, cache: wam_kv_cache, drop_rows: int, frame_shift: int, stream=None):
+    _check(load().wam_kv_evict(ctypes.byref(cfg), ctypes.byref(cache), drop_rows, frame_shift, _stream(stream)))
 
 
 def wam_kv_reset(cache: wam_kv_cache):

@@ -651,6 +651,33 @@ wam_status wam_op_attention(wam_dtype dtype, const void* Q, const void* K, const
   return WAM_OK;
 }
 
+wam_status wam_kv_evict(const wam_config* cfg, wam_kv_cache* cache, int drop_rows, int frame_shift, void* stream) {
+  CHECK(check_cfg(cfg));
+  const Geo g = geo_of(*cfg);
+  if (!cache || !cache->k || !cache->v) return fail(WAM_E_ARG, "KV cache pointers are NULL");
+  if (unaligned16(cache->k) || unaligned16(cache->v)) return fail(WAM_E_ARG, "KV cache pointers are not 16-byte aligned");
+  if (cache->branches != g.br) return fail(WAM_E_SHAPE, "cache branches %d != config branches %d", cache->branches, g.br);
+  if (cache->capacity <= 0 || cache->capacity % 64) return fail(WAM_E_SHAPE, "cache capacity must be a positive multiple of 64");
+  if (drop_rows < 0 || drop_rows % g.Lq || drop_rows > cache->length)
+    return fail(WAM_E_SHAPE, "drop_rows (%d) must be whole chunks of %d rows, at most the length %d", drop_rows, g.Lq,
+                cache->length);
+  if (drop_rows == 0) return WAM_OK;
+  KvEvictArgs a{};
+  a.k = cache->k; a.v = cache->v;
+  a.blocks = g.L * g.br * g.H; a.cap = cache->capacity; a.d = g.d; a.len = cache->length; a.drop = drop_rows;
+  a.Lq = g.Lq; a.Lv = g.Lv;
+  // frame axis: the first d_t / 2 pairs of a head, d_t = d - 2 * 2 floor(d / 6), freq theta^(-2j / d_t)
+  const int dh = 2 * (g.d / 6), dt = g.d - 2 * dh;
+  a.frame_pairs = dt / 2;
+  for (int j = 0; j < a.frame_pairs; ++j) {
+    const double ang = -(double)frame_shift * std::pow((double)cfg->rope_theta, -2.0 * j / (double)dt);
+    a.cs[j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+  }
+  HIP_TRY(launch_kv_evict(a, g.dt, reinterpret_cast<hipStream_t>(stream)));
+  cache->length -= drop_rows;
+  return WAM_OK;
+}
+
 void wam_kv_reset(wam_kv_cache* cache) {
   if (cache) cache->length = 0;
 }

@@ -122,6 +122,18 @@ hipError_t launch_v_to_cache(const VCacheArgs& a, DType dt, hipStream_t s);
 // launches above)
 hipError_t launch_qkv_cache(const QkNormArgs* q, const QkNormArgs& k, const VCacheArgs& v, DType dt, hipStream_t s);
 
+// Sliding-window eviction: keep rows [drop, len) of every (layer, branch, head) block, moved to the
+// front, with the frame-axis pairs of video keys rotated by (cos, sin) = cs[j] (j < frame_pairs).
+struct KvEvictArgs {
+  void* k;            // [blocks][cap][d]
+  void* v;            // [blocks][d][cap]
+  int blocks, cap, d, len, drop;
+  int Lq, Lv;         // rows per cached chunk, video rows first (drop is a multiple of Lq)
+  int frame_pairs;    // channel pairs (2j, 2j+1) of a head on the frame axis
+  float2 cs[64];
+};
+hipError_t launch_kv_evict(const KvEvictArgs& a, DType dt, hipStream_t s);
+
 // rotary (cos, sin) table for the video tokens of n_chunks chunks, written for every row of a branch
 hipError_t launch_rope_table(float2* table, int n_chunks, int Lq, int Lv, int frames_per_chunk, int grid_h,
                              int grid_w, int start_frame, int head_dim, float theta, hipStream_t s);

@@ -351,6 +351,94 @@ hipError_t launch_rope_table(float2* table, int n_chunks, int Lq, int Lv, int Fc
 }
 
 // ------------------------------------------------------------------------------------------------
+// Sliding attention window ([WS1] continuous requests: the attention window releases old KV and
+// the frame position restarts). Every (layer, branch, head) block keeps rows [drop, len), moved to
+// [0, len - drop); keys of video rows get their frame-axis pairs rotated by -shift * freq(j) on the
+// way: rotations compose, so a key rotated for frame f becomes the key of frame f - shift. Values
+// move along their key-contiguous rows. One workgroup per block moves it front to back in rounds:
+// a round's data are in registers before any of it is stored (the barrier sits between), and later
+// rounds read only rows past every row written so far, so the overlapping in-place move is safe.
+// ------------------------------------------------------------------------------------------------
+static constexpr int EVICT_PER = 4;   // 16-byte units per thread per round
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) kv_evict_k_kernel(KvEvictArgs a) {
+  constexpr int EPU = 16 / sizeof(T), U = D / EPU, ROWS = 256 * EVICT_PER / U;
+  T* base = reinterpret_cast<T*>(a.k) + (long)blockIdx.x * a.cap * D;
+  const int keep = a.len - a.drop;
+  for (int r0 = 0; r0 < keep; r0 += ROWS) {
+    uint4 v[EVICT_PER];
+#pragma unroll
+    for (int i = 0; i < EVICT_PER; ++i) {
+      const int x = threadIdx.x + 256 * i, row = r0 + x / U, u = x % U;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (row >= keep) continue;
+      v[i] = reinterpret_cast<const uint4*>(base + (long)(row + a.drop) * D)[u];
+      const int j0 = u * EPU / 2;   // first channel pair of the unit
+      if ((row % a.Lq) >= a.Lv || j0 >= a.frame_pairs) continue;
+      T* e = reinterpret_cast<T*>(&v[i]);
+#pragma unroll
+      for (int pp = 0; pp < EPU / 2; ++pp) {
+        if (j0 + pp >= a.frame_pairs) break;
+        const float2 t = a.cs[j0 + pp];
+        const float x0 = Elem<T>::to_f(e[2 * pp]), x1 = Elem<T>::to_f(e[2 * pp + 1]);
+        e[2 * pp] = Elem<T>::from_f(x0 * t.x - x1 * t.y);
+        e[2 * pp + 1] = Elem<T>::from_f(x0 * t.y + x1 * t.x);
+      }
+    }
+    // every thread's loads have returned before any store of the round
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < EVICT_PER; ++i) {
+      const int x = threadIdx.x + 256 * i, row = r0 + x / U, u = x % U;
+      if (row < keep) reinterpret_cast<uint4*>(base + (long)row * D)[u] = v[i];
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) kv_evict_v_kernel(KvEvictArgs a) {
+  constexpr int EPU = 16 / sizeof(T), KU = 256 * EVICT_PER / D;   // key units per row per round
+  T* base = reinterpret_cast<T*>(a.v) + (long)blockIdx.x * D * a.cap;
+  const int keep = a.len - a.drop;   // a multiple of 8 keys, so of EPU
+  for (int k0 = 0; k0 < keep; k0 += KU * EPU) {
+    uint4 v[EVICT_PER];
+#pragma unroll
+    for (int i = 0; i < EVICT_PER; ++i) {
+      const int x = threadIdx.x + 256 * i, j = x / KU, key = k0 + (x % KU) * EPU;
+      v[i] = key < keep ? *reinterpret_cast<const uint4*>(base + (long)j * a.cap + a.drop + key) : make_uint4(0, 0, 0, 0);
+    }
+    // every thread's loads have returned before any store of the round
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < EVICT_PER; ++i) {
+      const int x = threadIdx.x + 256 * i, j = x / KU, key = k0 + (x % KU) * EPU;
+      if (key < keep) *reinterpret_cast<uint4*>(base + (long)j * a.cap + key) = v[i];
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_kv_evict(const KvEvictArgs& a, DType dt, hipStream_t s) {
+  if (a.len - a.drop <= 0 || a.drop <= 0 || a.blocks <= 0) return hipSuccess;
+  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  const dim3 grid(a.blocks), block(256);
+#define WAM_EVICT(T, D)                                                  \
+  hipLaunchKernelGGL((kv_evict_k_kernel<T, D>), grid, block, 0, s, a); \
+  hipLaunchKernelGGL((kv_evict_v_kernel<T, D>), grid, block, 0, s, a);
+  if (dt == DT_BF16) {
+    if (a.d == 128) { WAM_EVICT(bf16_t, 128) } else { WAM_EVICT(bf16_t, 64) }
+  } else {
+    if (a.d == 128) { WAM_EVICT(float, 128) } else { WAM_EVICT(float, 64) }
+  }
+#undef WAM_EVICT
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
 // Token embedding: per branch b and row r of chunk c, h = x W^T + bias with the patch linear for
 // video rows and the action linear for action rows. A workgroup computes 16 rows x 256 columns:
 // the 16 input rows sit in LDS, each thread streams one weight row once and serves all 16 rows.
