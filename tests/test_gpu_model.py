@@ -97,6 +97,30 @@ def test_stack_tiny_matches_oracle(gpu, tiny_oracle, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_three_camera_grid(gpu, tiny_oracle, dtype):
+    """The three-camera 352 x 640 input of the single-GPU inference docs: 22 x 40 patches per frame
+    (880 tokens), 1784 tokens per chunk with the actions, rotary rows and columns up to 21 and 39,
+    one cached chunk, on the tiny width."""
+    w0, m0, ckv = tiny_oracle
+    w = w0.with_(grid_h=22, grid_w=40)
+    m = O.Model(w, m0.g, m0.layers)
+    print("three-camera grid", dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    xv1 = O.interpolate(x1v[1], epv[1], 0.5)
+    xa1 = O.interpolate(x1a[1], epa[1], 0.5)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, xv1, xa1, [0.5], [0.5], 1, w.frames_per_chunk)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache(2)
+    rig.append(dc, x1v[0], x1a[0], 0)
+    gv, ga = rig.step(dc, 1, xv1, xa1, [0.5], [0.5], w.frames_per_chunk)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decoupled_timesteps_and_frames(gpu, tiny_oracle, dtype):
     """Different video/action timesteps and a non-zero window offset, two cached chunks."""
     w, m, ckv = tiny_oracle
