@@ -13,3 +13,4 @@ weights, which is *parity unpinned*: no checkpoint and no worked numerical
 example exist on the pages.
 """
 from .dit import *  # noqa: F401,F403
+from .unipc import denoise_chunk_unipc, exp_neg_h, step_order, update_weights  # noqa: F401
