@@ -203,6 +203,25 @@ wam_status wam_denoise_chunk(const wam_config *cfg, const wam_weights *w, wam_kv
                              float *g_video, float *g_action, float *cos_parts, void *ws, size_t ws_bytes,
                              void *stream, int *dit_calls, unsigned char *reused);
 
+/* The same loop with the UniPC solver in place of Euler ([WS1] names UniPC as the scheduler's
+ * solver; no formula on the pages: the published predictor UniP-p / corrector UniC-p in
+ * data-prediction form with B(h) = e^h - 1, for alpha_t = t, sigma_t = 1 - t, lambda_t =
+ * log(alpha_t / sigma_t), data prediction m = x + sigma_t g). Arguments as wam_denoise_chunk, plus:
+ *   order 1..3: predictor order; steps from t = 0, to t = 1 and the step after one from t = 0 run
+ *     at order 1 (lambda is infinite at the ends; the order-1 predictor is the Euler step)
+ *   corrector != 0: after each DiT pass, the previous step is corrected with the fresh output
+ *     (same order as its predictor); skipped after a reused velocity
+ *   state: device scratch of 5 * (Lv * P + La * A) floats (data predictions and the previous
+ *     state), owned by the caller, contents irrelevant on entry
+ * The grid must increase strictly within [0, 1]. Errors as wam_denoise_chunk, plus WAM_E_ARG for
+ * an order outside 1..3, a NULL state or a bad grid. */
+wam_status wam_denoise_chunk_unipc(const wam_config *cfg, const wam_weights *w, wam_kv_cache *cache,
+                                   const wam_ctx_kv *ctx, float *x_video, float *x_action, const float *grid,
+                                   int n_steps, float guidance, float tau, int max_consecutive_reuse, int start_frame,
+                                   int order, int corrector, float *v_video, float *v_action, float *g_video,
+                                   float *g_action, float *cos_parts, float *state, void *ws, size_t ws_bytes,
+                                   void *stream, int *dit_calls, unsigned char *reused);
+
 /* Kernel-level calls, exposed so each kernel can be verified on its own (same kernels as above).
  *
  * Linear layer ([ARCH] §2.3: every projection of the block): C[m][n] = act(sum_k A[m][k] W[n][k] +

@@ -159,3 +159,25 @@ def test_kv_evict_validation():
     bad = wam.wam_kv_cache(0x1008, 0x1000, 2, 512, 2 * lq)
     assert lib.wam_kv_evict(ctypes.byref(c), ctypes.byref(bad), lq, 2, None) == wam.WAM_E_ARG
     assert lib.wam_kv_evict(ctypes.byref(c), ctypes.byref(kv), 0, 2, None) == wam.WAM_OK and kv.length == 2 * lq
+
+
+def test_denoise_chunk_unipc_validation():
+    """The UniPC loop checks its order, state and grid before anything is enqueued."""
+    lib = _lib()
+    c = _cfg(1)
+    F = ctypes.c_float
+    P = 0x1000
+    grid = (F * 3)(0.0, 0.5, 1.0)
+
+    def call(g, order, state=P):
+        return lib.wam_denoise_chunk_unipc(ctypes.byref(c), None, None, None, P, P, g, 2, F(5.0), F(2.0), -1, 0, order,
+                                           1, P, P, P, P, P, state, P, 1 << 30, None, None, None)
+    assert call(grid, 0) == wam.WAM_E_ARG and "order" in wam.wam_last_error()
+    assert call(grid, 4) == wam.WAM_E_ARG and "order" in wam.wam_last_error()
+    assert call(grid, 2, state=None) == wam.WAM_E_ARG and "state" in wam.wam_last_error()
+    flat = (F * 3)(0.0, 0.5, 0.5)
+    assert call(flat, 2) == wam.WAM_E_ARG and "increase" in wam.wam_last_error()
+    outside = (F * 3)(0.0, 0.5, 1.5)
+    assert call(outside, 2) == wam.WAM_E_ARG
+    # valid loop arguments: the first DiT pass rejects the missing weights
+    assert call(grid, 2) == wam.WAM_E_ARG and "weights" in wam.wam_last_error()

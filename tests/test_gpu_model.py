@@ -264,6 +264,54 @@ def test_denoise_chunk_matches_oracle(gpu, tiny_oracle, dtype, tau, max_reuse, c
     assert ev <= TOL[dtype] and ea <= TOL[dtype]
 
 
+_UNIPC_REF = {}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("order,corrector,tau,max_reuse", [(2, True, 1.5, -1), (3, True, 1.5, -1),
+                                                           (2, False, 1.5, -1), (1, True, 1.5, -1),
+                                                           (2, True, -1.5, 1)])
+def test_denoise_chunk_unipc_matches_oracle(gpu, tiny_oracle, dtype, order, corrector, tau, max_reuse):
+    """The library's 16-step UniPC loop (wam_denoise_chunk_unipc) against the oracle's UniPC loop on
+    the same DiT: same calls and reuse pattern, final latents within the stack tolerance."""
+    w, m, ckv = tiny_oracle
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    grid = [k / 16 for k in range(17)]
+    key = (order, corrector, tau, max_reuse)
+    if key not in _UNIPC_REF:
+        cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+        O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+
+        def dit(xv, xa, t):
+            vb, ab = O.stack_forward(m, cache, ckv, xv, xa, [t], [t], 1, w.frames_per_chunk)
+            return O.cfg_combine(vb, w.guidance), O.cfg_combine(ab, w.guidance)
+        _UNIPC_REF[key] = O.denoise_chunk_unipc(dit, epv[1], epa[1], grid, tau, None if max_reuse < 0 else max_reuse,
+                                                order=order, corrector=corrector)
+    ref_v, ref_a, n_ref, flags_ref = _UNIPC_REF[key]
+    print("unipc", dtype, key, flush=True)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    xv, xa = rig.f32(epv[1]), rig.f32(epa[1])
+    br = rig.m.cfg.branches
+    n = w.video_tokens * w.patch_dim + w.action_tokens * w.action_dim
+    vv = torch.empty((br, w.video_tokens, w.patch_dim), device=gpu)
+    va = torch.empty((br, w.action_tokens, w.action_dim), device=gpu)
+    gv = torch.empty(w.video_tokens * w.patch_dim, device=gpu)
+    ga = torch.empty(w.action_tokens * w.action_dim, device=gpu)
+    cosp = torch.empty(3, device=gpu)
+    state = torch.full((5 * n,), float("nan"), device=gpu)   # contents on entry must not matter
+    calls, flags = wam.wam_denoise_chunk_unipc(rig.m.cfg, rig.m.weights, dc.c, rig.ctx.c, xv, xa, grid, w.guidance, tau,
+                                               vv, va, gv, ga, cosp, state, rig.ws, order=order, corrector=corrector,
+                                               start_frame=w.frames_per_chunk, max_consecutive_reuse=max_reuse)
+    torch.cuda.synchronize()
+    assert calls == n_ref
+    assert flags == list(flags_ref)
+    ev, ea = rel_l2(xv.cpu().numpy(), ref_v), rel_l2(xa.cpu().numpy(), ref_a)
+    print("rel-L2 video %.2e action %.2e" % (ev, ea), flush=True)
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
 def test_flow_step_matches_oracle(gpu):
     nv, na = 28160, 192
     rng = synth.tensor_key(101, 0, "flow")

@@ -17,7 +17,7 @@ WAM_OK, WAM_E_ARG, WAM_E_SHAPE, WAM_E_CAPACITY, WAM_E_HIP, WAM_E_UNSUPPORTED = 0
 WAM_BF16, WAM_F32 = 0, 1
 
 EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
-           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_op_linear", "wam_op_attention", "wam_kv_evict", "wam_kv_reset",
+           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear", "wam_op_attention", "wam_kv_evict", "wam_kv_reset",
            "wam_last_error")
 
 
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH):
         "wam_dit_block_fwd": (I, [CFG, ctypes.POINTER(wam_block_weights), I, KV, CX, P, P, I, I, P, S, P]),
         "wam_flow_step": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P, S, P]),
         "wam_denoise_chunk": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, P, P, P, P, P, P, S, P, P, P]),
+        "wam_denoise_chunk_unipc": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, I, I, P, P, P, P, P, P, P, S, P, P,
+                                        P]),
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P, S, P]),
         "wam_kv_evict": (I, [CFG, KV, I, I, P]),
@@ -183,6 +185,23 @@ def wam_denoise_chunk(cfg, weights, cache, ctx, x_video, x_action, grid, guidanc
                                     _ptr(v_action), _ptr(g_video), _ptr(g_action), _ptr(cos_parts), _ptr(ws),
                                     _nbytes(ws), _stream(stream), ctypes.cast(ctypes.byref(calls), ctypes.c_void_p),
                                     ctypes.cast(flags, ctypes.c_void_p)))
+    return calls.value, [bool(flags[i]) for i in range(n)]
+
+
+def wam_denoise_chunk_unipc(cfg, weights, cache, ctx, x_video, x_action, grid, guidance, tau, v_video, v_action,
+                            g_video, g_action, cos_parts, state, ws, order=2, corrector=True, start_frame=0,
+                            max_consecutive_reuse=-1, stream=None):
+    """UniPC variant of ``wam_denoise_chunk``; ``state`` holds 5 x (video + action) floats."""
+    n = len(grid) - 1
+    g = (ctypes.c_float * (n + 1))(*[float(t) for t in grid])
+    calls = ctypes.c_int(0)
+    flags = (ctypes.c_ubyte * max(n, 1))()
+    _check(load().wam_denoise_chunk_unipc(
+        ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(ctx), _ptr(x_video),
+        _ptr(x_action), ctypes.cast(g, ctypes.c_void_p), n, float(guidance), float(tau), int(max_consecutive_reuse),
+        int(start_frame), int(order), 1 if corrector else 0, _ptr(v_video), _ptr(v_action), _ptr(g_video),
+        _ptr(g_action), _ptr(cos_parts), _ptr(state), _ptr(ws), _nbytes(ws), _stream(stream),
+        ctypes.cast(ctypes.byref(calls), ctypes.c_void_p), ctypes.cast(flags, ctypes.c_void_p)))
     return calls.value, [bool(flags[i]) for i in range(n)]
 
 

@@ -560,23 +560,111 @@ wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, 
   return WAM_OK;
 }
 
-wam_status wam_denoise_chunk(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache, const wam_ctx_kv* ctx,
-                             float* x_video, float* x_action, const float* grid, int n_steps, float guidance, float tau,
-                             int max_consecutive_reuse, int start_frame, float* v_video, float* v_action, float* g_video,
-                             float* g_action, float* cos_parts, void* ws, size_t ws_bytes, void* stream, int* dit_calls,
-                             unsigned char* reused) {
+// ---- solvers of the denoising loop ------------------------------------------------------------------
+// UniPC ([WS1] names it as the scheduler's solver; the published predictor UniP-p / corrector
+// UniC-p in data-prediction form with B(h) = e^h - 1), for alpha_t = t, sigma_t = 1 - t,
+// lambda_t = log(alpha_t / sigma_t): from s to t with h = lambda_t - lambda_s, earlier outputs at
+// r_j = (lambda_j - lambda_s) / h (the corrector's new output at r = 1), D_j = (m_j - m_s) / r_j,
+// h_phi_1 = e^{-h} - 1, h_phi_{k+1} = h_phi_k / (-h) - 1/k!, sum_j rho_j r_j^k = h_phi_{k+2} (k+1)! / B_h,
+// x_t = (sigma_t / sigma_s) x_s - alpha_t h_phi_1 m_s - alpha_t B_h sum_j rho_j D_j.
+// Weights are formed in double: x_new = a x_s + w[0] m_s + sum_j w[j] m_j (new output last).
+struct UniUpdate {
+  double a = 0.0;
+  double w[5] = {0, 0, 0, 0, 0};
+  int n = 0;   // entries of w used
+};
+
+static double half_log_snr(double t) { return std::log(t / (1.0 - t)); }
+
+static UniUpdate unipc_update(double t_t, const double* hist, int order, bool corrector) {
+  UniUpdate u;
+  const double ts = hist[0];
+  const double e = (ts * (1.0 - t_t)) / ((1.0 - ts) * t_t);   // e^{-h}: 0 from t = 0 or to t = 1
+  const double z = e > 0.0 ? std::log(e) : -INFINITY;         // -h
+  double hphi[6];                                             // hphi[k] = h_phi_{k+1}
+  hphi[0] = e - 1.0;
+  double fact = 1.0;
+  for (int k = 1; k < 6; ++k) {
+    fact *= k;
+    hphi[k] = hphi[k - 1] / z - 1.0 / fact;
+  }
+  const double b_h = e - 1.0;
+  double r[4];
+  int nr = 0;
+  for (int j = 1; j < order; ++j) r[nr++] = (half_log_snr(hist[j]) - half_log_snr(ts)) / -z;
+  if (corrector) r[nr++] = 1.0;
+  u.a = (1.0 - t_t) / (1.0 - ts);
+  u.n = 1 + nr;
+  u.w[0] = -t_t * hphi[0];
+  if (nr == 0) return u;
+  // Vandermonde system, Gaussian elimination with partial pivoting (nr <= 4)
+  double A[4][5];
+  fact = 1.0;
+  for (int k = 0; k < nr; ++k) {
+    fact *= (k + 1);
+    for (int j = 0; j < nr; ++j) A[k][j] = std::pow(r[j], k);
+    A[k][nr] = hphi[k + 1] * fact / b_h;
+  }
+  for (int c = 0; c < nr; ++c) {
+    int piv = c;
+    for (int i = c + 1; i < nr; ++i)
+      if (std::fabs(A[i][c]) > std::fabs(A[piv][c])) piv = i;
+    for (int j = 0; j <= nr; ++j) std::swap(A[c][j], A[piv][j]);
+    for (int i = c + 1; i < nr; ++i) {
+      const double f = A[i][c] / A[c][c];
+      for (int j = c; j <= nr; ++j) A[i][j] -= f * A[c][j];
+    }
+  }
+  double rho[4];
+  for (int i = nr - 1; i >= 0; --i) {
+    double acc = A[i][nr];
+    for (int j = i + 1; j < nr; ++j) acc -= A[i][j] * rho[j];
+    rho[i] = acc / A[i][i];
+  }
+  for (int j = 0; j < nr; ++j) {
+    const double c = -t_t * b_h * rho[j] / r[j];
+    u.w[j + 1] += c;
+    u.w[0] -= c;
+  }
+  return u;
+}
+
+// predictor order of step k: 1 from t = 0, to t = 1 and after a step from t = 0 (lambda infinite)
+static int unipc_order(const float* grid, int k, int order) {
+  if (grid[k] <= 0.f || grid[k + 1] >= 1.f) return 1;
+  int u = 1;
+  while (u < order && k - u >= 0 && grid[k - u] > 0.f) ++u;
+  return u;
+}
+
+// The chunk's denoising loop with CFG and velocity reuse; order 0 = Euler, 1..3 = UniPC.
+static wam_status denoise_loop(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache, const wam_ctx_kv* ctx,
+                               float* x_video, float* x_action, const float* grid, int n_steps, float guidance,
+                               float tau, int max_consecutive_reuse, int start_frame, int order, bool corrector,
+                               float* v_video, float* v_action, float* g_video, float* g_action, float* cos_parts,
+                               float* state, void* ws, size_t ws_bytes, void* stream, int* dit_calls,
+                               unsigned char* reused) {
   CHECK(check_cfg(cfg));
   if (!grid || n_steps < 1) return fail(WAM_E_ARG, "grid must hold n_steps + 1 >= 2 times");
   for (int k = 0; k <= n_steps; ++k)
     if (!std::isfinite(grid[k])) return fail(WAM_E_ARG, "non-finite time in the grid");
   if (!g_video || !g_action || !cos_parts) return fail(WAM_E_ARG, "guided-velocity or cosine buffers are NULL");
   if (!std::isfinite(tau) && !std::isinf(tau)) return fail(WAM_E_ARG, "tau is NaN");
+  if (order > 0) {
+    if (order > 3) return fail(WAM_E_ARG, "UniPC order must be 1, 2 or 3");
+    if (!state) return fail(WAM_E_ARG, "UniPC state buffer is NULL");
+    if (grid[0] < 0.f || grid[n_steps] > 1.f) return fail(WAM_E_ARG, "UniPC times must lie in [0, 1]");
+    for (int k = 0; k < n_steps; ++k)
+      if (!(grid[k + 1] > grid[k])) return fail(WAM_E_ARG, "UniPC times must increase strictly");
+    const size_t need = 256 + 64 * 3 * 4;
+    if (!ws || ws_bytes < need) return fail(WAM_E_ARG, "workspace too small");
+  }
   const Geo g = geo_of(*cfg);
   const int nv = g.Lv * g.P, na = g.La * g.A;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // reuse needs cos > tau with cos <= 1: a tau above 1 can never trigger it (no host read-back then)
   const bool may_reuse = tau <= 1.f;
-  int computed = 0, consecutive = 0, calls = 0;
+  int computed = 0, consecutive = 0, calls = 0, prev_order = 0;
   double cos_last = -2.0;   // cosine of the two most recent DiT-computed guided video velocities
   for (int k = 0; k < n_steps; ++k) {
     const float t = grid[k], dt = grid[k + 1] - grid[k];
@@ -584,17 +672,54 @@ wam_status wam_denoise_chunk(const wam_config* cfg, const wam_weights* w, wam_kv
     if (may_reuse && k >= 2 && computed >= 2 &&
         (max_consecutive_reuse < 0 || consecutive < max_consecutive_reuse))
       reuse = cos_last > (double)tau;
-    if (reuse) {
-      // Euler step with the latest computed guided velocities
-      CHECK(wam_flow_step(x_video, x_action, g_video, g_action, 1, 1.f, nv, na, dt, dt, nullptr, nullptr, nullptr,
-                          nullptr, ws, ws_bytes, stream));
-      ++consecutive;
-    } else {
+    if (!reuse)
       CHECK(wam_dit_stack_fwd(cfg, w, cache, ctx, 1, x_video, x_action, &t, &t, start_frame, v_video, v_action, ws,
                               ws_bytes, stream));
-      // guided velocities replace the previous computed ones; the cosine compares new and previous
-      CHECK(wam_flow_step(x_video, x_action, v_video, v_action, g.br, guidance, nv, na, dt, dt, g_video, g_action,
-                          computed >= 1 ? g_video : nullptr, cos_parts, ws, ws_bytes, stream));
+    // reused: the latest computed guided velocities; computed: guided velocities replace the previous
+    // ones and the cosine compares new and previous
+    const float* src_v = reuse ? g_video : v_video;
+    const float* src_a = reuse ? g_action : v_action;
+    const int br = reuse ? 1 : g.br;
+    const float wgt = reuse ? 1.f : guidance;
+    float* out_v = reuse ? nullptr : g_video;
+    float* out_a = reuse ? nullptr : g_action;
+    const float* prev = !reuse && computed >= 1 ? g_video : nullptr;
+    if (order == 0) {
+      CHECK(wam_flow_step(x_video, x_action, src_v, src_a, br, wgt, nv, na, dt, dt, out_v, out_a, prev,
+                          prev ? cos_parts : nullptr, ws, ws_bytes, stream));
+    } else {
+      UnipcArgs ua{};
+      ua.xv = x_video; ua.xa = x_action; ua.vv = src_v; ua.va = src_a; ua.br = br; ua.w = wgt;
+      ua.nv = nv; ua.na = na; ua.sigma = 1.f - t; ua.gv = out_v; ua.ga = out_a; ua.prev = prev;
+      ua.partials = reinterpret_cast<float*>(ws); ua.cos_parts = prev ? cos_parts : nullptr;
+      ua.state = state;
+      const int slots = order + 1;
+      ua.slot_new = k % slots;
+      if (corrector && k >= 1 && !reuse) {   // the previous step's corrector with this fresh output
+        double hist[3];
+        for (int j = 0; j < prev_order; ++j) hist[j] = grid[k - 1 - j];
+        const UniUpdate c = unipc_update(t, hist, prev_order, true);
+        ua.corr = 1; ua.cn = prev_order; ua.ca = (float)c.a; ua.ct = (float)c.w[c.n - 1];
+        for (int j = 0; j < prev_order; ++j) {
+          ua.cw[j] = (float)c.w[j];
+          ua.cslot[j] = (k - 1 - j) % slots;
+        }
+      }
+      const int p = unipc_order(grid, k, order);
+      double hist[3];
+      for (int j = 0; j < p; ++j) hist[j] = grid[k - j];
+      const UniUpdate pu = unipc_update(grid[k + 1], hist, p, false);
+      ua.pn = p; ua.pa = (float)pu.a;
+      for (int j = 0; j < p; ++j) {
+        ua.pw[j] = (float)pu.w[j];
+        ua.pslot[j] = (k - j) % slots;
+      }
+      HIP_TRY(launch_unipc_step(ua, s));
+      prev_order = p;
+    }
+    if (reuse) {
+      ++consecutive;
+    } else {
       ++computed;
       ++calls;
       consecutive = 0;
@@ -610,6 +735,28 @@ wam_status wam_denoise_chunk(const wam_config* cfg, const wam_weights* w, wam_kv
   }
   if (dit_calls) *dit_calls = calls;
   return WAM_OK;
+}
+
+wam_status wam_denoise_chunk(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache, const wam_ctx_kv* ctx,
+                             float* x_video, float* x_action, const float* grid, int n_steps, float guidance, float tau,
+                             int max_consecutive_reuse, int start_frame, float* v_video, float* v_action, float* g_video,
+                             float* g_action, float* cos_parts, void* ws, size_t ws_bytes, void* stream, int* dit_calls,
+                             unsigned char* reused) {
+  return denoise_loop(cfg, w, cache, ctx, x_video, x_action, grid, n_steps, guidance, tau, max_consecutive_reuse,
+                      start_frame, 0, false, v_video, v_action, g_video, g_action, cos_parts, nullptr, ws, ws_bytes,
+                      stream, dit_calls, reused);
+}
+
+wam_status wam_denoise_chunk_unipc(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache,
+                                   const wam_ctx_kv* ctx, float* x_video, float* x_action, const float* grid,
+                                   int n_steps, float guidance, float tau, int max_consecutive_reuse, int start_frame,
+                                   int order, int corrector, float* v_video, float* v_action, float* g_video,
+                                   float* g_action, float* cos_parts, float* state, void* ws, size_t ws_bytes,
+                                   void* stream, int* dit_calls, unsigned char* reused) {
+  if (order < 1) return fail(WAM_E_ARG, "UniPC order must be 1, 2 or 3");
+  return denoise_loop(cfg, w, cache, ctx, x_video, x_action, grid, n_steps, guidance, tau, max_consecutive_reuse,
+                      start_frame, order, corrector != 0, v_video, v_action, g_video, g_action, cos_parts, state, ws,
+                      ws_bytes, stream, dit_calls, reused);
 }
 
 wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W, int ldw, const float* bias, void* C,

@@ -173,6 +173,27 @@ struct FlowArgs {
 };
 hipError_t launch_flow_step(const FlowArgs& a, hipStream_t s);
 
+// One UniPC step on the concatenated [video | action] latent (n = nv + na): the guided velocity g
+// (as in the flow step), the data prediction m = x + sigma g, optionally the previous step's
+// corrector xs = ca x_prev + sum_j cw[j] m_{cslot[j]} + ct m, then the predictor
+// x_next = pa xs + pw[0] m + sum_{j>=1} pw[j] m_{pslot[j]}. `state` holds `slots` data predictions
+// of n floats each followed by x_prev; m goes to slot `slot_new`, xs to x_prev.
+struct UnipcArgs {
+  float* xv; float* xa;
+  const float* vv; const float* va;   // [br][n] model outputs, or a reused guided velocity (br = 1, w = 1)
+  int br; float w;
+  int nv, na;
+  float sigma;
+  float* gv; float* ga;               // guided velocities out (optional)
+  const float* prev;                  // previous guided video velocity (optional, cosine partials)
+  float* partials; float* cos_parts;
+  float* state;
+  int slot_new;
+  int corr, cn; float ca, ct; float cw[4]; int cslot[4];
+  int pn; float pa; float pw[4]; int pslot[4];
+};
+hipError_t launch_unipc_step(const UnipcArgs& a, hipStream_t s);
+
 // Output heads: video rows (first Lv of each chunk) -> Wv [P][D], action rows -> Wa [A][D], written
 // token-major per branch to vv [br][n*Lv][P] and va [br][n*La][A]. K is split `splits` ways into
 // fp32 partials part[splits][M][64] (summed in order by the second kernel). P, A <= 64.

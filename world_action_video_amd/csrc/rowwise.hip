@@ -734,6 +734,68 @@ hipError_t launch_flow_step(const FlowArgs& a, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// UniPC step ([WS1] names UniPC as the scheduler's solver; the published predictor-corrector in
+// data-prediction form). Elementwise over the concatenated latent with weights from the host; the
+// cosine partials of the guided video velocity are reduced exactly as in the flow step.
+// ------------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) unipc_kernel(UnipcArgs a) {
+  __shared__ float red[4];
+  const float wc = a.w, wu = 1.f - a.w;
+  float dot = 0.f, gg = 0.f, pp = 0.f;
+  const int n = a.nv + a.na;
+  float* xprev = a.state + (long)4 * n;   // after the four data-prediction slots
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += FLOW_BLOCKS * 256) {
+    const bool video = i < a.nv;
+    const int k = video ? i : i - a.nv;
+    const float* v = video ? a.vv : a.va;
+    const int nn = video ? a.nv : a.na;
+    float g = v[k];
+    if (a.br == 2) g = wc * v[k] + wu * v[nn + k];
+    float* xp = video ? a.xv + k : a.xa + k;
+    const float x = *xp;
+    const float m = x + a.sigma * g;
+    float xs = x;
+    if (a.corr) {
+      xs = a.ca * xprev[i];
+      for (int j = 0; j < a.cn; ++j) xs += a.cw[j] * a.state[(long)a.cslot[j] * n + i];
+      xs += a.ct * m;
+    }
+    float xn = a.pa * xs + a.pw[0] * m;
+    for (int j = 1; j < a.pn; ++j) xn += a.pw[j] * a.state[(long)a.pslot[j] * n + i];
+    a.state[(long)a.slot_new * n + i] = m;
+    xprev[i] = xs;
+    *xp = xn;
+    if (video) {
+      if (a.prev) {
+        const float p = a.prev[k];
+        dot += g * p;
+        gg += g * g;
+        pp += p * p;
+      }
+      if (a.gv) a.gv[k] = g;
+    } else if (a.ga) {
+      a.ga[k] = g;
+    }
+  }
+  if (a.prev) {
+    dot = block_sum<256>(dot, red);
+    gg = block_sum<256>(gg, red);
+    pp = block_sum<256>(pp, red);
+    if (threadIdx.x == 0) {
+      a.partials[blockIdx.x * 3 + 0] = dot;
+      a.partials[blockIdx.x * 3 + 1] = gg;
+      a.partials[blockIdx.x * 3 + 2] = pp;
+    }
+  }
+}
+
+hipError_t launch_unipc_step(const UnipcArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(unipc_kernel, dim3(FLOW_BLOCKS), dim3(256), 0, s, a);
+  if (a.prev && a.cos_parts) hipLaunchKernelGGL(flow_reduce_kernel, dim3(1), dim3(64), 0, s, a.partials, a.cos_parts);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
 // Output heads. One wave per (row, K split); lane n accumulates output n (fp32, k in order) from
 // 8-element vectors of the row and of weight row n. The second kernel sums the splits in order, adds
 // the bias and writes the row to its token-group output.
