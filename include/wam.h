@@ -62,7 +62,13 @@ typedef struct {
   int branches;            /* 1, or 2 = CFG batch (branch 0 conditional, branch 1 negative prompt) */
   float rope_theta, eps;   /* 10000, 1e-6 */
   wam_dtype dtype;
+  int variant;             /* 0, or WAM_VARIANT_* bits (architectural variants of [ARCH] §2.3) */
 } wam_config;
+
+/* Architectural variants drawn on the architecture page next to the adopted readings.
+ * FRAME_CAUSAL: inside a chunk a video token sees the video tokens of its own and earlier frames
+ *   and an action token the whole chunk (cached chunks and earlier chunks of a pass stay visible). */
+enum { WAM_VARIANT_FRAME_CAUSAL = 1 };
 
 /* One block's parameters ([ARCH] §2.3 single causal block). Matrices [out][in] in dtype;
  * everything else float. mod: [6][D] per-layer offset added to the shared time modulation

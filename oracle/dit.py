@@ -271,6 +271,25 @@ def token_layout(w, n_chunks: int) -> Tuple[Array, Array, Array]:
     return np.array(chunk), np.array(group), np.array(local)
 
 
+def visibility(w, chunk: Array, group: Array, cached: int) -> Array:
+    """[T, cached + T] mask of the self-attention (reading R7): a query sees every cached clean key
+    and the keys of earlier chunks of the pass; inside its own chunk it sees every token
+    (bidirectional), or, with the frame-causal variant of [ARCH] §2.3 causal mask, a video token sees
+    the video tokens of its own and earlier frames of the chunk and an action token the whole chunk."""
+    T = chunk.size
+    pos = np.zeros(T, dtype=np.int64)                  # index inside the chunk: video first, then actions
+    for i in range(1, T):
+        pos[i] = pos[i - 1] + 1 if chunk[i] == chunk[i - 1] else 0
+    if getattr(w, "variant", 0) & 1:
+        hw = w.grid_h * w.grid_w
+        inside = np.where(group == 0, (pos // hw + 1) * hw, w.chunk_tokens)
+    else:
+        inside = np.full(T, w.chunk_tokens)
+    same = chunk[None, :] == chunk[:, None]
+    vis_pass = (chunk[None, :] < chunk[:, None]) | (same & (pos[None, :] < inside[:, None]))
+    return np.concatenate([np.ones((T, cached), dtype=bool), vis_pass], axis=1)
+
+
 @dataclass
 class KVCache:
     """Per layer, per branch: keys (after RMSNorm and RoPE) and values of clean chunks.
@@ -314,9 +333,7 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
     chunk, group, _ = token_layout(w, n_chunks)
     is_video = group == 0
     L0 = cache_k.shape[1]
-    # key j is visible to query i if it is cached (a clean earlier chunk) or its chunk <= i's chunk
-    key_chunk = np.concatenate([np.full(L0, -1), chunk])
-    visible = key_chunk[None, :] <= chunk[:, None]
+    visible = visibility(w, chunk, group, L0)
     oc_all = np.empty_like(h)
     k_new = np.empty_like(h)
     v_new = np.empty_like(h)

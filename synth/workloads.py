@@ -42,6 +42,7 @@ class Workload:
     eps: float = 1e-6
     rope_theta: float = 10000.0
     guidance: float = 5.0
+    variant: int = 0        # architectural variants of the pages (bit flags, see VARIANT_* below)
 
     @property
     def video_tokens(self) -> int:
@@ -58,6 +59,11 @@ class Workload:
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
 
+
+# Variants drawn on the architecture page next to the adopted readings (bit flags):
+VARIANT_FRAME_CAUSAL = 1   # inside a chunk a frame sees earlier and its own frames; actions see the chunk
+VARIANT_RMS_NORM = 2       # RMSNorm in place of the block and head LayerNorms
+VARIANT_SWIGLU = 4         # SwiGLU feed-forward: SiLU(gate) * up with interleaved [gate, up] rows
 
 WORKLOADS = {
     # Tiny single block: width 256, 4 heads of 64, FFN 1024, 2 frames of 8x8 patches + 24 action tokens,

@@ -121,6 +121,39 @@ def test_three_camera_grid(gpu, tiny_oracle, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_frame_causal_variant(gpu, tiny_oracle, dtype):
+    """Frame-causal mask inside the chunk (architecture page's causal-mask drawing): against the
+    oracle; on the GPU, the second frame and the action tokens cannot reach the first frame's
+    outputs, bit for bit; incremental equals full-sequence."""
+    w0, m0, ckv = tiny_oracle
+    w = w0.with_(variant=synth.workloads.VARIANT_FRAME_CAUSAL)
+    m = O.Model(w, m0.g, m0.layers)
+    hw, Lv, La, Fc = w.grid_h * w.grid_w, w.video_tokens, w.action_tokens, w.frames_per_chunk
+    print("frame-causal", dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.4], [0.4], 1, Fc)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    gv, ga = rig.step(dc, 1, epv[1], epa[1], [0.4], [0.4], Fc)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+    xv2 = epv[1].copy()
+    xv2[hw:] = xv2[hw:] * 3 - 1
+    pv, pa = rig.step(dc, 1, xv2, epa[1], [0.4], [0.4], Fc)
+    assert np.array_equal(pv[:, :hw], gv[:, :hw]) and not np.array_equal(pa, ga)
+    qv, qa = rig.step(dc, 1, epv[1], -epa[1], [0.4], [0.4], Fc)
+    assert np.array_equal(qv, gv) and not np.array_equal(qa, ga)
+    fv, fa = rig.step(rig.cache(), 2, np.concatenate([x1v[0], epv[1]]), np.concatenate([x1a[0], epa[1]]),
+                      [1.0, 0.4], [1.0, 0.4], 0)
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    assert rel_l2(fv[:, Lv:], gv) <= tol and rel_l2(fa[:, La:], ga) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decoupled_timesteps_and_frames(gpu, tiny_oracle, dtype):
     """Different video/action timesteps and a non-zero window offset, two cached chunks."""
     w, m, ckv = tiny_oracle

@@ -244,3 +244,44 @@ def test_rotary_composition_is_a_position_shift():
     twice = O.apply_rope(O.apply_rope(x, pos, 64, 1e4), np.tile([[-7, 0, 0]], (40, 1)), 64, 1e4)
     once = O.apply_rope(x, pos - np.array([7, 0, 0]), 64, 1e4)
     assert np.abs(twice - once).max() <= 1e-12
+
+
+def _frame_causal(tiny):
+    w, m = tiny[0], tiny[1]
+    wf = w.with_(variant=synth.workloads.VARIANT_FRAME_CAUSAL)
+    return wf, O.Model(wf, m.g, m.layers)
+
+
+def test_frame_causal_mask_hides_later_frames_and_actions(tiny):
+    # Frame-causal variant ([ARCH] §2.3 causal mask): inside a chunk, changing the second frame's
+    # tokens cannot reach the first frame's outputs, and changing the action tokens cannot reach any
+    # video output; both reach the action outputs. Under the adopted chunk-level mask they do reach.
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    wf, mf = _frame_causal(tiny)
+    hw = w.grid_h * w.grid_w
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    O.kv_append(mf, cache, ckv, x1v[0], x1a[0], 0)
+    base = O.stack_forward(mf, cache, ckv, epv[1], epa[1], [0.4], [0.4], 1, w.frames_per_chunk)
+    xv2 = epv[1].copy()
+    xv2[hw:] = xv2[hw:] * 3 - 1                       # second frame only
+    f2 = O.stack_forward(mf, cache, ckv, xv2, epa[1], [0.4], [0.4], 1, w.frames_per_chunk)
+    assert np.array_equal(base[0][:, :hw], f2[0][:, :hw])
+    assert not np.array_equal(base[0][:, hw:], f2[0][:, hw:]) and not np.array_equal(base[1], f2[1])
+    a2 = O.stack_forward(mf, cache, ckv, epv[1], -epa[1], [0.4], [0.4], 1, w.frames_per_chunk)
+    assert np.array_equal(base[0], a2[0]) and not np.array_equal(base[1], a2[1])
+    cache0 = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    O.kv_append(m, cache0, ckv, x1v[0], x1a[0], 0)
+    c1 = O.stack_forward(m, cache0, ckv, epv[1], epa[1], [0.4], [0.4], 1, w.frames_per_chunk)
+    c2 = O.stack_forward(m, cache0, ckv, xv2, epa[1], [0.4], [0.4], 1, w.frames_per_chunk)
+    assert not np.array_equal(c1[0][:, :hw], c2[0][:, :hw])
+
+
+def test_frame_causal_incremental_equals_full_sequence(tiny):
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    wf, mf = _frame_causal(tiny)
+    Lv, La, Fc = w.video_tokens, w.action_tokens, w.frames_per_chunk
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    O.kv_append(mf, cache, ckv, x1v[0], x1a[0], 0)
+    iv, ia = O.stack_forward(mf, cache, ckv, epv[1], epa[1], [0.3], [0.6], 1, Fc)
+    fv, fa = _full(wf, mf, ckv, [x1v[0], epv[1]], [x1a[0], epa[1]], [1, 0.3], [1, 0.6])
+    assert np.abs(fv[:, Lv:] - iv).max() <= 1e-5 and np.abs(fa[:, La:] - ia).max() <= 1e-5

@@ -32,7 +32,8 @@ class wam_config(ctypes.Structure):
                                              "patch_dim", "action_dim", "action_tokens", "frames_per_chunk",
                                              "grid_h", "grid_w", "ctx_in_dim", "ctx_text_len", "ctx_img_len",
                                              "branches")] + \
-              [("rope_theta", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+              [("rope_theta", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int),
+               ("variant", ctypes.c_int)]
 
 
 BLOCK_FIELDS = ("mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "ln3_w", "ln3_b", "w_cq", "b_cq", "g_cq",

@@ -71,6 +71,7 @@ wam_status check_cfg(const wam_config* c) {
   if (c->ctx_text_len <= 0 || c->ctx_img_len < 0) return fail(WAM_E_SHAPE, "bad condition lengths");
   if (c->branches != 1 && c->branches != 2) return fail(WAM_E_SHAPE, "branches must be 1 or 2");
   if (!(c->eps > 0.f) || !(c->rope_theta > 0.f)) return fail(WAM_E_ARG, "eps and rope_theta must be positive");
+  if (c->variant & ~WAM_VARIANT_FRAME_CAUSAL) return fail(WAM_E_UNSUPPORTED, "unknown variant bits 0x%x", c->variant);
   return WAM_OK;
 }
 
@@ -272,7 +273,9 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   aa.Q = qh; aa.K = kc; aa.Vt = vc; aa.O = attn;
   aa.q_bh_stride = (long)p.R * g.d; aa.k_bh_stride = (long)p.kv->capacity * g.d; aa.v_bh_stride = (long)g.d * p.kv->capacity;
   aa.v_stride = p.kv->capacity; aa.Lq_total = p.R; aa.H = g.H; aa.d = g.d; aa.br = g.br;
-  aa.kv_base = len; aa.chunk_q = p.n > 1 ? g.Lq : 0; aa.kv_total = len + p.R;
+  const bool frame_causal = (p.cfg->variant & WAM_VARIANT_FRAME_CAUSAL) != 0;
+  aa.kv_base = len; aa.chunk_q = p.n > 1 || frame_causal ? g.Lq : 0; aa.kv_total = len + p.R;
+  aa.frame_tokens = frame_causal ? p.cfg->grid_h * p.cfg->grid_w : 0; aa.video_tokens = g.Lv;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)g.d));
   aa.part = part; aa.part_elems = part_n;
   HIP_TRY(launch_attention(aa, dt, p.s));

@@ -13,9 +13,10 @@
 //
 // Masking is by select: a score whose key is at or beyond the query's limit becomes -inf before the
 // max, so its probability is exactly 0 and hidden keys cannot influence the result. The limit of
-// query q is min(kv_total, kv_base + (q / chunk_q + 1) * chunk_q): cached clean chunks are always
-// visible, current-chunk keys up to the end of the query's own chunk (bidirectional inside a chunk),
-// never later chunks. Value rows past kv_total are zero-filled in LDS.
+// query q (attn_limit) is min(kv_total, kv_base + (q / chunk_q + 1) * chunk_q): cached clean chunks
+// are always visible, current-chunk keys up to the end of the query's own chunk (bidirectional
+// inside a chunk), never later chunks; with the frame-causal variant a video query's limit ends at
+// its own frame instead. Limits never decrease with q. Value rows past kv_total are zero-filled in LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -66,14 +67,7 @@ attn_kernel(AttnArgs a) {
   const T* K = reinterpret_cast<const T*>(a.K) + bh * a.k_bh_stride;
   const T* Vt = reinterpret_cast<const T*>(a.Vt) + bh * a.v_bh_stride;
 
-  auto limit_of = [&](int q) {
-    int lim = a.kv_total;
-    if (a.chunk_q > 0) {
-      const int c = a.kv_base + (q / a.chunk_q + 1) * a.chunk_q;
-      lim = c < lim ? c : lim;
-    }
-    return lim;
-  };
+  auto limit_of = [&](int q) { return attn_limit(a, q); };
   const int q_last = min(qblk + ATT_BQ, a.Lq_total) - 1;
   const int kv_wg = limit_of(q_last);                   // limits grow with q: the last query sees most
   const int n_tiles = (kv_wg + ATT_BKV - 1) / ATT_BKV;
@@ -313,14 +307,7 @@ struct AttnItem {
   bool valid = false, q_ok = false;
   int item = 0, split = 0, b = 0, h = 0, qblk = 0, n_tiles = 0, q = 0, my_lim = 0, wave_lim = 0;
   long bh = 0;
-  __device__ __forceinline__ static int limit_of(const AttnArgs& a, int q) {
-    int lim = a.kv_total;
-    if (a.chunk_q > 0) {
-      const int c = a.kv_base + (q / a.chunk_q + 1) * a.chunk_q;
-      lim = c < lim ? c : lim;
-    }
-    return lim;
-  }
+  __device__ __forceinline__ static int limit_of(const AttnArgs& a, int q) { return attn_limit(a, q); }
   __device__ __forceinline__ static int blocks(const AttnArgs& a) { return (a.Lq_total + BQ - 1) / BQ * a.H * a.br; }
   // the workgroup's unit from its index in XCD order
   __device__ __forceinline__ AttnItem(const AttnArgs& a, int wave, int l32, int splits) {

@@ -57,7 +57,23 @@ struct AttnArgs {
   float* part;        // scratch for key-split partial outputs (nullptr: never split)
   long part_elems;    // capacity of `part` in floats
   int kv_splits;      // set by launch_attention: key ranges per query block (1 = no split)
+  int frame_tokens;   // > 0 (with chunk_q > 0): frame-causal inside a chunk, frames of this many tokens
+  int video_tokens;   // video tokens at the start of each chunk (frame-causal only)
 };
+// Keys visible to query q: a prefix [0, limit) of the key rows. Cached keys (below kv_base) are
+// always visible; inside the pass, keys up to the end of the query's chunk (chunk_q > 0), or with
+// frame_tokens > 0 up to the end of the query's frame for video queries.
+__host__ __device__ inline int attn_limit(const AttnArgs& a, int q) {
+  int lim = a.kv_total;
+  if (a.chunk_q > 0) {
+    const int loc = q % a.chunk_q;
+    int inside = a.chunk_q;
+    if (a.frame_tokens > 0 && loc < a.video_tokens) inside = (loc / a.frame_tokens + 1) * a.frame_tokens;
+    const int c = a.kv_base + (q - loc) + inside;
+    lim = c < lim ? c : lim;
+  }
+  return lim;
+}
 hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s);
 // Key ranges per query block the bf16 kernel takes for these sizes (flash-decoding-style split when
 // the query blocks alone would leave most CUs idle), and the scratch floats that split needs.

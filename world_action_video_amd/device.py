@@ -27,6 +27,7 @@ def make_config(w: Workload, dtype: str = "bf16", branches: int | None = None) -
     c.rope_theta = float(w.rope_theta)
     c.eps = float(w.eps)
     c.dtype = WAM_BF16 if dtype == "bf16" else WAM_F32
+    c.variant = int(w.variant)
     return c
 
 
