@@ -67,8 +67,10 @@ typedef struct {
 
 /* Architectural variants drawn on the architecture page next to the adopted readings.
  * FRAME_CAUSAL: inside a chunk a video token sees the video tokens of its own and earlier frames
- *   and an action token the whole chunk (cached chunks and earlier chunks of a pass stay visible). */
-enum { WAM_VARIANT_FRAME_CAUSAL = 1 };
+ *   and an action token the whole chunk (cached chunks and earlier chunks of a pass stay visible).
+ * RMS_NORM: the block norms (both modulated norms and the affine norm before cross-attention) and
+ *   the output-head norm divide by the root mean square without subtracting the mean. */
+enum { WAM_VARIANT_FRAME_CAUSAL = 1, WAM_VARIANT_RMS_NORM = 2 };
 
 /* One block's parameters ([ARCH] §2.3 single causal block). Matrices [out][in] in dtype;
  * everything else float. mod: [6][D] per-layer offset added to the shared time modulation

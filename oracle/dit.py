@@ -92,10 +92,17 @@ def linear(x: Array, w: Array, b: Optional[Array] = None) -> Array:
     return y
 
 
-def modulated_norm(x: Array, shift: Array, scale: Array, eps: float) -> Array:
+def modulated_norm(x: Array, shift: Array, scale: Array, eps: float, rms: bool = False) -> Array:
     """adaLN: LN(x) (1 + scale) + shift ([ARCH] §2.3 single block: the normed input is modulated
-    by shift and scale from the time embedding; reading R3: scale enters as 1 + scale)."""
-    return layer_norm(x, eps) * (x.dtype.type(1) + scale) + shift
+    by shift and scale from the time embedding; reading R3: scale enters as 1 + scale). With
+    ``rms`` (the RMSNorm variant drawn on [ARCH] §2.3) the normalisation is RMSNorm."""
+    n = rms_norm(x, eps) if rms else layer_norm(x, eps)
+    return n * (x.dtype.type(1) + scale) + shift
+
+
+def uses_rms(w) -> bool:
+    """The RMSNorm variant: every block norm and the head norm normalise by the RMS (no mean)."""
+    return bool(getattr(w, "variant", 0) & 2)
 
 
 def softmax_rows(s: Array) -> Array:
@@ -340,7 +347,7 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
     # --- self-attention sub-layer
     o_all = np.empty_like(h)
     for b in range(br):
-        y = modulated_norm(h[b], shift1, scale1, w.eps)
+        y = modulated_norm(h[b], shift1, scale1, w.eps, uses_rms(w))
         qkv = linear(y, lp["w_qkv"], lp["b_qkv"])
         q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
         q = rms_norm(q, w.eps, lp["g_q"]).reshape(T, H, d)
@@ -356,7 +363,8 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
     h = h + gate1[None] * linear(o_all, lp["w_o"], lp["b_o"])
     # --- cross-attention sub-layer (no mask, no RoPE, no modulation)
     for b in range(br):
-        n3 = layer_norm(h[b], w.eps, lp["ln3_w"], lp["ln3_b"])
+        n3 = (rms_norm(h[b], w.eps) * lp["ln3_w"] + lp["ln3_b"] if uses_rms(w)
+              else layer_norm(h[b], w.eps, lp["ln3_w"], lp["ln3_b"]))
         qc = rms_norm(linear(n3, lp["w_cq"], lp["b_cq"]), w.eps, lp["g_cq"]).reshape(T, H, d)
         kc = ctx_k[b].reshape(-1, H, d).transpose(1, 0, 2)
         vc = ctx_v[b].reshape(-1, H, d).transpose(1, 0, 2)
@@ -364,7 +372,7 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
         oc_all[b] = oc
     h = h + linear(oc_all, lp["w_co"], lp["b_co"])
     # --- feed-forward sub-layer
-    y2 = modulated_norm(h, shift2[None], scale2[None], w.eps)
+    y2 = modulated_norm(h, shift2[None], scale2[None], w.eps, uses_rms(w))
     f = linear(gelu_tanh(linear(y2, lp["w_ff1"], lp["b_ff1"])), lp["w_ff2"], lp["b_ff2"])
     h = h + gate2[None] * f
     return h, k_new, v_new
@@ -391,7 +399,7 @@ def head_forward(w, g: Dict[str, Array], h: Array, e: Array, n_chunks: int) -> T
     v_video = n_video W_vo^T + b, v_action = n_action W_ao^T + b."""
     shift = g["head_mod"][0][None] + e
     scale = g["head_mod"][1][None] + e
-    n = modulated_norm(h, shift[None], scale[None], w.eps)
+    n = modulated_norm(h, shift[None], scale[None], w.eps, uses_rms(w))
     _, group, _ = token_layout(w, n_chunks)
     vv = linear(n[:, group == 0], g["vo_w"], g["vo_b"])
     va = linear(n[:, group == 1], g["ao_w"], g["ao_b"])

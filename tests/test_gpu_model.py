@@ -154,6 +154,29 @@ def test_frame_causal_variant(gpu, tiny_oracle, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", [synth.workloads.VARIANT_RMS_NORM,
+                                     synth.workloads.VARIANT_RMS_NORM | synth.workloads.VARIANT_FRAME_CAUSAL])
+def test_variant_stack_matches_oracle(gpu, tiny_oracle, dtype, variant):
+    """Architectural variants (RMSNorm block and head norms, alone and with the frame-causal mask):
+    one cached chunk and a step, against the oracle with the same variant."""
+    w0, m0, ckv = tiny_oracle
+    w = w0.with_(variant=variant)
+    m = O.Model(w, m0.g, m0.layers)
+    print("variant", variant, dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.35], [0.55], 1, w.frames_per_chunk)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    gv, ga = rig.step(dc, 1, epv[1], epa[1], [0.35], [0.55], w.frames_per_chunk)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decoupled_timesteps_and_frames(gpu, tiny_oracle, dtype):
     """Different video/action timesteps and a non-zero window offset, two cached chunks."""
     w, m, ckv = tiny_oracle

@@ -54,6 +54,20 @@ def test_modulated_norm_statistics():
     np.testing.assert_allclose(y.std(axis=1), 1.0 + scale[:, 0], rtol=1e-9)
 
 
+def test_modulated_rms_norm_matches_torch():
+    # The RMSNorm variant of the block norms: torch's rms_norm, then the same (1 + scale), shift; the
+    # result differs from the LayerNorm form exactly when the rows have a non-zero mean.
+    x = _r(5, 768, dt=np.float64) * 4 - 1.5
+    shift = _r(1, 768, dt=np.float64) - 0.5
+    scale = _r(1, 768, dt=np.float64) - 0.5
+    ref = F.rms_norm(torch.from_numpy(x), (768,), eps=1e-6).numpy() * (1 + scale) + shift
+    np.testing.assert_allclose(O.modulated_norm(x, shift, scale, 1e-6, rms=True), ref, rtol=1e-12, atol=1e-12)
+    xc = x - x.mean(axis=1, keepdims=True)
+    np.testing.assert_allclose(O.modulated_norm(xc, shift, scale, 1e-6, rms=True),
+                               O.modulated_norm(xc, shift, scale, 1e-6), rtol=1e-9, atol=1e-9)
+    assert np.abs(O.modulated_norm(x, shift, scale, 1e-6, rms=True) - O.modulated_norm(x, shift, scale, 1e-6)).max() > 0.1
+
+
 def test_linear_brute_force():
     x, w, b = _r(3, 5, dt=np.float64), _r(4, 5, dt=np.float64), _r(4, dt=np.float64)
     y = O.linear(x, w, b)

@@ -71,7 +71,8 @@ wam_status check_cfg(const wam_config* c) {
   if (c->ctx_text_len <= 0 || c->ctx_img_len < 0) return fail(WAM_E_SHAPE, "bad condition lengths");
   if (c->branches != 1 && c->branches != 2) return fail(WAM_E_SHAPE, "branches must be 1 or 2");
   if (!(c->eps > 0.f) || !(c->rope_theta > 0.f)) return fail(WAM_E_ARG, "eps and rope_theta must be positive");
-  if (c->variant & ~WAM_VARIANT_FRAME_CAUSAL) return fail(WAM_E_UNSUPPORTED, "unknown variant bits 0x%x", c->variant);
+  if (c->variant & ~(WAM_VARIANT_FRAME_CAUSAL | WAM_VARIANT_RMS_NORM))
+    return fail(WAM_E_UNSUPPORTED, "unknown variant bits 0x%x", c->variant);
   return WAM_OK;
 }
 
@@ -208,6 +209,7 @@ NormArgs adaln_args(const Pass& p, const float* mod, int shift_idx, int scale_id
   NormArgs na{};
   na.X = p.h; na.Y = at<void>(p.ws, p.L.y); na.M = p.M; na.D = p.g.D; na.eps = p.cfg->eps; na.mode = NORM_ADALN;
   na.rm = rowmap(p); na.e6 = p.e6; na.mod = mod; na.shift_idx = shift_idx; na.scale_idx = scale_idx;
+  na.rms = (p.cfg->variant & WAM_VARIANT_RMS_NORM) != 0;
   return na;
 }
 
@@ -216,6 +218,7 @@ NormArgs head_norm_args(const Pass& p, const wam_weights* w) {
   NormArgs na{};
   na.X = p.h; na.Y = at<void>(p.ws, p.L.y); na.M = p.M; na.D = p.g.D; na.eps = p.cfg->eps; na.mode = NORM_HEAD;
   na.rm = rowmap(p); na.e6 = at<float>(p.ws, p.L.e); na.mod = reinterpret_cast<const float*>(w->head_mod);
+  na.rms = (p.cfg->variant & WAM_VARIANT_RMS_NORM) != 0;
   return na;
 }
 

@@ -807,7 +807,7 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
     float s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < G; ++k) s1 += (v[k].x + v[k].y) + (v[k].z + v[k].w);
-    const float mean = block_sum<256>(s1, red) / (float)g.N;
+    const float mean = na.rms ? 0.f : block_sum<256>(s1, red) / (float)g.N;
     float s2 = 0.f;
 #pragma unroll
     for (int k = 0; k < G; ++k) {

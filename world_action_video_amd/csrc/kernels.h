@@ -98,6 +98,7 @@ struct NormArgs {
   int shift_idx, scale_idx;
   const float* w;       // AFFINE
   const float* b;
+  int rms;              // RMSNorm (no mean subtraction) in place of LayerNorm
 };
 hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s);
 

@@ -10,6 +10,7 @@ namespace wam {
 // ------------------------------------------------------------------------------------------------
 // LayerNorm (+ modulation): one wave per row (4 rows per 256-thread workgroup). The row stays in
 // registers (VPL float4 per lane); mean and variance are two wave reductions, no LDS, no barrier.
+// With a.rms the mean is taken as zero: RMSNorm.
 // ------------------------------------------------------------------------------------------------
 template <typename T, int VPL>
 __global__ void __launch_bounds__(256) norm_kernel(NormArgs a) {
@@ -26,7 +27,7 @@ __global__ void __launch_bounds__(256) norm_kernel(NormArgs a) {
     xv[k] = i < nv ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     s += (xv[k].x + xv[k].y) + (xv[k].z + xv[k].w);
   }
-  const float mean = wave_sum(s) / (float)a.D;
+  const float mean = a.rms ? 0.f : wave_sum(s) / (float)a.D;
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
