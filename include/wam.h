@@ -69,8 +69,10 @@ typedef struct {
  * FRAME_CAUSAL: inside a chunk a video token sees the video tokens of its own and earlier frames
  *   and an action token the whole chunk (cached chunks and earlier chunks of a pass stay visible).
  * RMS_NORM: the block norms (both modulated norms and the affine norm before cross-attention) and
- *   the output-head norm divide by the root mean square without subtracting the mean. */
-enum { WAM_VARIANT_FRAME_CAUSAL = 1, WAM_VARIANT_RMS_NORM = 2 };
+ *   the output-head norm divide by the root mean square without subtracting the mean.
+ * SWIGLU: the feed-forward is (SiLU(y W_g^T + b_g) * (y W_u^T + b_u)) W_2^T + b_2 with w_ff1 [2F][D]
+ *   and b_ff1 [2F] holding the gate and up rows interleaved (row 2j gate j, row 2j+1 up j). */
+enum { WAM_VARIANT_FRAME_CAUSAL = 1, WAM_VARIANT_RMS_NORM = 2, WAM_VARIANT_SWIGLU = 4 };
 
 /* One block's parameters ([ARCH] §2.3 single causal block). Matrices [out][in] in dtype;
  * everything else float. mod: [6][D] per-layer offset added to the shared time modulation
@@ -85,7 +87,7 @@ typedef struct {
   const void *w_ck, *b_ck, *g_ck;
   const void *w_cv, *b_cv;
   const void *w_co, *b_co;
-  const void *w_ff1, *b_ff1;   /* [F][D], [F] */
+  const void *w_ff1, *b_ff1;   /* [F][D], [F] (SwiGLU variant: [2F][D], [2F], see below) */
   const void *w_ff2, *b_ff2;   /* [D][F], [D] */
 } wam_block_weights;
 
@@ -234,7 +236,8 @@ wam_status wam_denoise_chunk_unipc(const wam_config *cfg, const wam_weights *w, 
  *
  * Linear layer ([ARCH] §2.3: every projection of the block): C[m][n] = act(sum_k A[m][k] W[n][k] +
  * bias[n]) with A [M][lda], W [N][ldw], C [M][ldc] in `dtype`; bias float [N] or NULL; act 0 = none,
- * 1 = GELU (tanh approximation, the FFN's activation). K must be a multiple of 64.
+ * 1 = GELU (tanh approximation, the FFN's activation), 2 = SwiGLU pairs (N even: C[m][j] =
+ * SiLU(z[m][2j]) * z[m][2j+1] with z = A W^T + bias, so C has N / 2 columns). K must be a multiple of 64.
  * ws / ws_bytes: optional device scratch (256-byte aligned) for split-K partial products; with
  * NULL, or too little room, the product runs unsplit. A split product sums its fp32 partials in a
  * fixed order, so results are deterministic, but they may differ from the unsplit product in the

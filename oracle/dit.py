@@ -278,6 +278,18 @@ def token_layout(w, n_chunks: int) -> Tuple[Array, Array, Array]:
     return np.array(chunk), np.array(group), np.array(local)
 
 
+def feed_forward(w, lp: Dict[str, Array], y: Array) -> Array:
+    """GELU_tanh(y W1^T + b1) W2^T + b2 (reading R6); with the SwiGLU variant drawn on [ARCH] §2.3,
+    (SiLU(y Wg^T + bg) * (y Wu^T + bu)) W2^T + b2 where rows 2j / 2j+1 of W1 (and entries of b1)
+    are the gate / up rows of hidden unit j."""
+    u = linear(y, lp["w_ff1"], lp["b_ff1"])
+    if getattr(w, "variant", 0) & 4:
+        act = silu(u[..., 0::2]) * u[..., 1::2]
+    else:
+        act = gelu_tanh(u)
+    return linear(act, lp["w_ff2"], lp["b_ff2"])
+
+
 def visibility(w, chunk: Array, group: Array, cached: int) -> Array:
     """[T, cached + T] mask of the self-attention (reading R7): a query sees every cached clean key
     and the keys of earlier chunks of the pass; inside its own chunk it sees every token
@@ -373,8 +385,7 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
     h = h + linear(oc_all, lp["w_co"], lp["b_co"])
     # --- feed-forward sub-layer
     y2 = modulated_norm(h, shift2[None], scale2[None], w.eps, uses_rms(w))
-    f = linear(gelu_tanh(linear(y2, lp["w_ff1"], lp["b_ff1"])), lp["w_ff2"], lp["b_ff2"])
-    h = h + gate2[None] * f
+    h = h + gate2[None] * feed_forward(w, lp, y2)
     return h, k_new, v_new
 
 

@@ -107,6 +107,7 @@ def global_tensors(w: Workload):
 def layer_tensors(w: Workload):
     """(name, shape, kind, sigma_or_value) of one layer's tensors (Linear weights are [out, in])."""
     D, F = w.dim, w.ffn_dim
+    F1 = 2 * F if w.variant & VARIANT_SWIGLU else F   # SwiGLU: interleaved gate and up rows
     n = lambda name, shape: (name, shape, "normal", 0.02)  # noqa: E731
     c = lambda name, shape, v: (name, shape, "const", v)  # noqa: E731
     return [
@@ -118,7 +119,7 @@ def layer_tensors(w: Workload):
         n("w_ck", (D, D)), n("b_ck", (D,)), c("g_ck", (D,), 1.0),
         n("w_cv", (D, D)), n("b_cv", (D,)),
         n("w_co", (D, D)), n("b_co", (D,)),
-        n("w_ff1", (F, D)), n("b_ff1", (F,)),
+        n("w_ff1", (F1, D)), n("b_ff1", (F1,)),
         n("w_ff2", (D, F)), n("b_ff2", (D,)),
     ]
 

@@ -155,13 +155,17 @@ def test_frame_causal_variant(gpu, tiny_oracle, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("variant", [synth.workloads.VARIANT_RMS_NORM,
-                                     synth.workloads.VARIANT_RMS_NORM | synth.workloads.VARIANT_FRAME_CAUSAL])
+                                     synth.workloads.VARIANT_RMS_NORM | synth.workloads.VARIANT_FRAME_CAUSAL,
+                                     synth.workloads.VARIANT_SWIGLU,
+                                     synth.workloads.VARIANT_SWIGLU | synth.workloads.VARIANT_RMS_NORM
+                                     | synth.workloads.VARIANT_FRAME_CAUSAL])
 def test_variant_stack_matches_oracle(gpu, tiny_oracle, dtype, variant):
-    """Architectural variants (RMSNorm block and head norms, alone and with the frame-causal mask):
-    one cached chunk and a step, against the oracle with the same variant."""
+    """Architectural variants (RMSNorm block and head norms, SwiGLU feed-forward, combined with the
+    frame-causal mask): one cached chunk and a step, against the oracle with the same variant."""
     w0, m0, ckv = tiny_oracle
     w = w0.with_(variant=variant)
-    m = O.Model(w, m0.g, m0.layers)
+    # SwiGLU draws a wider first feed-forward matrix; every other tensor is drawn identically
+    m = O.load_model(w) if variant & synth.workloads.VARIANT_SWIGLU else O.Model(w, m0.g, m0.layers)
     print("variant", variant, dtype, flush=True)
     x1v, x1a, epv, epa = tiny_inputs(w)
     cache = O.KVCache.empty(w.layers, w.branches, w.dim)

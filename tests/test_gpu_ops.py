@@ -46,7 +46,7 @@ def split_ws(gpu, M, N):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("M,N,K", LINEAR_CASES)
-@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("act", [0, 1, 2])
 @pytest.mark.parametrize("split", [False, True])
 def test_op_linear_small(gpu, dtype, M, N, K, act, split):
     """With a workspace, bf16 products of fewer than 128 256x256 tiles split over K (M, N >= 256)."""
@@ -57,13 +57,15 @@ def test_op_linear_small(gpu, dtype, M, N, K, act, split):
     w = draw((N, K), "w%d_%d_%d" % (M, N, K), 0.05)
     b = draw((N,), "b%d" % N, 0.1)
     ref = a.astype(np.float64) @ w.astype(np.float64).T + b
-    if act:
+    if act == 1:
         ref = O.gelu_tanh(ref)
+    elif act == 2:   # SwiGLU pairs: SiLU(gate column 2j) * up column 2j+1
+        ref = O.silu(ref[:, 0::2]) * ref[:, 1::2]
     dt = wam.WAM_BF16 if dtype == "bf16" else wam.WAM_F32
     A, W = to_device(a, dtype, gpu), to_device(w, dtype, gpu)
     B = torch.from_numpy(b).to(gpu)
-    C = torch.full((M, N), float("nan"), dtype=A.dtype, device=gpu)
-    wam.wam_op_linear(dt, A, K, W, K, B, C, N, M, N, K, act, ws=split_ws(gpu, M, N) if split else None)
+    C = torch.full((M, N // 2 if act == 2 else N), float("nan"), dtype=A.dtype, device=gpu)
+    wam.wam_op_linear(dt, A, K, W, K, B, C, C.shape[1], M, N, K, act, ws=split_ws(gpu, M, N) if split else None)
     torch.cuda.synchronize()
     out = host(C)
     if dtype == "bf16":

@@ -199,3 +199,37 @@ def test_cosine_fp64():
     assert abs(O.cosine_fp64(a, a) - 1.0) < 1e-14
     assert abs(O.cosine_fp64(a, -a) + 1.0) < 1e-14
     assert abs(O.cosine_fp64(np.array([1.0, 0.0]), np.array([0.0, 2.0]))) == 0.0
+
+
+def test_swiglu_feed_forward_structure():
+    # SwiGLU variant: the up rows (odd rows of W1) enter linearly, the gate rows through SiLU. Scaling
+    # the up rows and biases by a scales the product by a; a zero gate leaves only b2; an up path
+    # fixed at 1 leaves a SiLU feed-forward, checked against torch.
+    from types import SimpleNamespace
+    rng = np.random.default_rng(11)
+    D, Fh = 32, 24
+    w = SimpleNamespace(variant=4)
+    lp = {"w_ff1": rng.standard_normal((2 * Fh, D)) * 0.3, "b_ff1": rng.standard_normal(2 * Fh) * 0.1,
+          "w_ff2": rng.standard_normal((D, Fh)) * 0.3, "b_ff2": rng.standard_normal(D) * 0.1}
+    y = rng.standard_normal((7, D))
+    base = O.feed_forward(w, lp, y)
+    lp2 = dict(lp, w_ff1=lp["w_ff1"].copy(), b_ff1=lp["b_ff1"].copy())
+    lp2["w_ff1"][1::2] *= 2.5
+    lp2["b_ff1"][1::2] *= 2.5
+    np.testing.assert_allclose(O.feed_forward(w, lp2, y) - lp["b_ff2"], 2.5 * (base - lp["b_ff2"]), rtol=1e-12, atol=1e-12)
+    lp3 = dict(lp, w_ff1=lp["w_ff1"].copy(), b_ff1=lp["b_ff1"].copy())
+    lp3["w_ff1"][0::2] = 0.0
+    lp3["b_ff1"][0::2] = 0.0
+    np.testing.assert_array_equal(O.feed_forward(w, lp3, y), np.broadcast_to(lp["b_ff2"], (7, D)))
+    lp4 = dict(lp, w_ff1=lp["w_ff1"].copy(), b_ff1=lp["b_ff1"].copy())
+    lp4["w_ff1"][1::2] = 0.0
+    lp4["b_ff1"][1::2] = 1.0
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+    ref = F.linear(F.silu(F.linear(t(y), t(lp["w_ff1"][0::2]), t(lp["b_ff1"][0::2]))), t(lp["w_ff2"]), t(lp["b_ff2"]))
+    np.testing.assert_allclose(O.feed_forward(w, lp4, y), ref.numpy(), rtol=1e-12, atol=1e-12)
+    # the adopted GELU-tanh feed-forward against torch
+    w0 = SimpleNamespace(variant=0)
+    lp0 = dict(lp, w_ff1=lp["w_ff1"][:Fh], b_ff1=lp["b_ff1"][:Fh])
+    ref0 = F.linear(F.gelu(F.linear(t(y), t(lp0["w_ff1"]), t(lp0["b_ff1"])), approximate="tanh"), t(lp["w_ff2"]),
+                    t(lp["b_ff2"]))
+    np.testing.assert_allclose(O.feed_forward(w0, lp0, y), ref0.numpy(), rtol=1e-9, atol=1e-9)

@@ -71,7 +71,7 @@ wam_status check_cfg(const wam_config* c) {
   if (c->ctx_text_len <= 0 || c->ctx_img_len < 0) return fail(WAM_E_SHAPE, "bad condition lengths");
   if (c->branches != 1 && c->branches != 2) return fail(WAM_E_SHAPE, "branches must be 1 or 2");
   if (!(c->eps > 0.f) || !(c->rope_theta > 0.f)) return fail(WAM_E_ARG, "eps and rope_theta must be positive");
-  if (c->variant & ~(WAM_VARIANT_FRAME_CAUSAL | WAM_VARIANT_RMS_NORM))
+  if (c->variant & ~(WAM_VARIANT_FRAME_CAUSAL | WAM_VARIANT_RMS_NORM | WAM_VARIANT_SWIGLU))
     return fail(WAM_E_UNSUPPORTED, "unknown variant bits 0x%x", c->variant);
   return WAM_OK;
 }
@@ -324,11 +324,13 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     post.na = adaln_args(p, mod, 3, 4);
     HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID, post, p.s));
   }
-  // FFN: h += gate2 * (GELU(y2 W1^T + b1) W2^T + b2)
+  // FFN: h += gate2 * (GELU(y2 W1^T + b1) W2^T + b2); SwiGLU variant: W1 has 2F interleaved
+  // [gate, up] rows and the product's epilogue writes SiLU(gate) * up
   {
-    GemmArgs ga = gemm_args(y, g.D, bw.w_ff1, g.D, bw.b_ff1, p.M, g.F, g.D, part, part_n);
+    const bool swiglu = (p.cfg->variant & WAM_VARIANT_SWIGLU) != 0;
+    GemmArgs ga = gemm_args(y, g.D, bw.w_ff1, g.D, bw.b_ff1, p.M, swiglu ? 2 * g.F : g.F, g.D, part, part_n);
     ga.C = ffn; ga.ldc = g.F;
-    HIP_TRY(launch_gemm(ga, dt, EPI_GELU, p.s));
+    HIP_TRY(launch_gemm(ga, dt, swiglu ? EPI_SWIGLU : EPI_GELU, p.s));
   }
   {
     GemmArgs ga = gemm_args(ffn, g.F, bw.w_ff2, g.F, bw.b_ff2, p.M, g.D, g.F, part, part_n);
@@ -770,16 +772,17 @@ wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W,
   if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
   if (!A || !W || !C) return fail(WAM_E_ARG, "NULL operand");
   if (M < 0 || N < 0 || K <= 0 || K % 64) return fail(WAM_E_SHAPE, "K must be a positive multiple of 64");
-  if (lda < K || ldw < K || ldc < N) return fail(WAM_E_SHAPE, "leading dimensions too small");
+  if (lda < K || ldw < K || ldc < (act == 2 ? N / 2 : N)) return fail(WAM_E_SHAPE, "leading dimensions too small");
   const int epu = dtype == WAM_BF16 ? 8 : 4;
   if (lda % epu || ldw % epu) return fail(WAM_E_SHAPE, "lda/ldw must keep rows 16-byte aligned");
-  if (act != 0 && act != 1) return fail(WAM_E_ARG, "act must be 0 or 1");
+  if (act < 0 || act > 2) return fail(WAM_E_ARG, "act must be 0, 1 or 2");
+  if (act == 2 && N % 2) return fail(WAM_E_SHAPE, "SwiGLU needs an even N");
   if (ws && reinterpret_cast<uintptr_t>(ws) % 256) return fail(WAM_E_ARG, "workspace must be 256-byte aligned");
   GemmArgs ga = gemm_args(A, lda, W, ldw, bias, M, N, K, ws ? reinterpret_cast<float*>(ws) : nullptr,
                           ws ? (long)(ws_bytes / 4) : 0);
   ga.C = C;
   ga.ldc = ldc;
-  HIP_TRY(launch_gemm(ga, dtype == WAM_BF16 ? DT_BF16 : DT_F32, act ? EPI_GELU : EPI_STORE,
+  HIP_TRY(launch_gemm(ga, dtype == WAM_BF16 ? DT_BF16 : DT_F32, act == 2 ? EPI_SWIGLU : act ? EPI_GELU : EPI_STORE,
                       reinterpret_cast<hipStream_t>(stream)));
   return WAM_OK;
 }

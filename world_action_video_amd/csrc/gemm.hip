@@ -213,6 +213,11 @@ gemm_kernel(GemmArgs g) {
         const float v = acc[i][j][r] + bias;
         if constexpr (EPI == EPI_STORE) {
           Elem<T>::store(reinterpret_cast<T*>(g.C) + (long)row * g.ldc + col, v);
+        } else if constexpr (EPI == EPI_SWIGLU) {
+          // gate column 2j in an even lane, its up column 2j+1 in the next lane (N even: both or neither
+          // lane of a pair is past the edge, and both hold the same row)
+          const float up = __shfl_xor(v, 1, 64);
+          if (!(l32 & 1)) Elem<T>::store(reinterpret_cast<T*>(g.C) + (long)row * g.ldc + col / 2, silu_f(v) * up);
         } else if constexpr (EPI == EPI_GELU) {
           Elem<T>::store(reinterpret_cast<T*>(g.C) + (long)row * g.ldc + col, gelu_tanh_f(v));
         } else if constexpr (EPI == EPI_ROWSEL_F32) {
@@ -503,7 +508,7 @@ gemm4_kernel(GemmArgs g, int splits) {
       const int n = nb + 32 * j + 8 * gq;
       bias[j][gq] = (g.bias && n < g.N) ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = mb + 32 * i;
@@ -518,6 +523,10 @@ gemm4_kernel(GemmArgs g, int splits) {
           float4 v = run(i, j, gq);
           const float4 b = bias[j][gq];
           v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+          if constexpr (EPI == EPI_SWIGLU) {   // columns (n, n+1), (n+2, n+3): two outputs at n / 2
+            *reinterpret_cast<uint32_t*>(crow + n / 2) = pack2_bf16(silu_f(v.x) * v.y, silu_f(v.z) * v.w);
+            continue;
+          }
           if constexpr (EPI == EPI_GELU) {
             v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
           }
@@ -600,7 +609,11 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs g, int spli
     const float4 b = *reinterpret_cast<const float4*>(g.bias + c4);
     v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
   }
-  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    T* out = reinterpret_cast<T*>(g.C) + (long)row * g.ldc + c4 / 2;
+    Elem<T>::store(out, silu_f(v[0]) * v[1]);
+    Elem<T>::store(out + 1, silu_f(v[2]) * v[3]);
+  } else if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
     if constexpr (EPI == EPI_GELU) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_f(v[e]);
@@ -637,6 +650,7 @@ static hipError_t launch_cfg(const GemmArgs& a, Epi epi, hipStream_t s) {
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, EPI_STORE>), grid, block, 0, s, a); break;
     case EPI_GELU: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, EPI_GELU>), grid, block, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, EPI_SWIGLU>), grid, block, 0, s, a); break;
     case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, EPI_RESID>), grid, block, 0, s, a); break;
     case EPI_RESID_GATED:
       hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, NW, EPI_RESID_GATED>), grid, block, 0, s, a);
@@ -663,7 +677,8 @@ static int g4_plan(const GemmArgs& a, Epi epi) {
   if (epi == EPI_ROWSEL_F32 || a.M < 256 || a.N < 256) return 0;
   // vector epilogues: runs of four columns, 16-byte aligned fp32 rows, 8-byte aligned bf16 rows
   const bool vec_ok = a.N % 4 == 0 && (!a.bias || aligned16(a.bias)) &&
-                      (epi == EPI_STORE || epi == EPI_GELU ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
+                      (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_SWIGLU
+                           ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
                                                            : (aligned16(a.H) && a.ldh % 4 == 0)) &&
                       (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
   if (!vec_ok) return 0;
@@ -682,6 +697,7 @@ static void launch_g4_direct(const GemmArgs& a, Epi epi, hipStream_t s) {
   switch (epi) {
     case EPI_STORE: launch_g4<EPI_STORE>(a, 1, s); break;
     case EPI_GELU: launch_g4<EPI_GELU>(a, 1, s); break;
+    case EPI_SWIGLU: launch_g4<EPI_SWIGLU>(a, 1, s); break;
     case EPI_RESID: launch_g4<EPI_RESID>(a, 1, s); break;
     case EPI_RESID_GATED: launch_g4<EPI_RESID_GATED>(a, 1, s); break;
     default: break;
@@ -693,6 +709,9 @@ static void launch_reduce(const GemmArgs& a, Epi epi, int splits, hipStream_t s)
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_STORE>), grid, dim3(256), 0, s, a, splits); break;
     case EPI_GELU: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_GELU>), grid, dim3(256), 0, s, a, splits); break;
+    case EPI_SWIGLU:
+      hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_SWIGLU>), grid, dim3(256), 0, s, a, splits);
+      break;
     case EPI_RESID: hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_RESID>), grid, dim3(256), 0, s, a, splits); break;
     case EPI_RESID_GATED:
       hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, EPI_RESID_GATED>), grid, dim3(256), 0, s, a, splits);
@@ -716,6 +735,7 @@ static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (epi == EPI_SWIGLU && a.N % 2) return hipErrorInvalidValue;   // (gate, up) column pairs
   // buffer descriptors address each operand with 32-bit byte offsets
   const long esz = dt == DT_BF16 ? 2 : 4;
   if ((long)a.M * a.lda * esz >= (1L << 31) || (long)a.N * a.ldw * esz >= (1L << 31)) return hipErrorInvalidValue;

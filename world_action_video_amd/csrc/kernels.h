@@ -16,6 +16,7 @@ enum Epi {
   EPI_RESID = 2,        // H (fp32) += acc + bias
   EPI_RESID_GATED = 3,  // H (fp32) += gate[row group][n] * (acc + bias), gate = e6[chunk][group][gi] + mod[gi]
   EPI_ROWSEL_F32 = 4,   // fp32 output of the rows of one token group, gathered per branch (output heads)
+  EPI_SWIGLU = 5,       // C[m][j] (T) = silu(acc[m][2j] + bias[2j]) * (acc[m][2j+1] + bias[2j+1]), N even
 };
 
 struct RowMap {       // how a GEMM row maps to (branch, chunk, token group)
