@@ -1,0 +1,86 @@
+"""MXFP8 quantisation (oracle) for the low-precision projections.
+
+TEST INFRASTRUCTURE ONLY: see ``oracle/__init__.py`` for who may import it.
+
+[N569] (real-time optimisations) and the single-GPU docs quantise the projections to low-precision
+floats; the format here is the OCP microscaling one that gfx950's scaled matrix instructions read:
+fp8 e4m3 elements (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; subnormals; largest
+finite 448; no infinities) sharing one power-of-two scale per 32 consecutive elements of a row.
+Reading (the pages name only the element formats): shared exponent e = floor(log2(amax)) - 8,
+8 being the exponent of e4m3's largest power of two, clamped to >= -127 (e8m0 byte e + 127);
+elements x / 2^e saturated to +-448 and rounded to nearest, ties to even.
+"""
+from __future__ import annotations
+
+import math
+from typing import Tuple
+
+import numpy as np
+
+Array = np.ndarray
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: Array) -> Array:
+    """Real value of e4m3 codes (no NaN codes expected)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+    return sign * mag
+
+
+def e4m3_encode(x: Array) -> Array:
+    """Round float64 values with |x| <= 448 to e4m3 codes, nearest with ties to even.
+
+    Magnitudes below 2^-6 are on the subnormal grid of spacing 2^-9; above, the grid spacing is
+    2^(floor(log2|x|) - 3). The sign bit follows the sign of x (negative zero keeps it).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sub = a < 2.0 ** -6
+    e = np.where(sub, -6, np.floor(np.log2(np.where(a > 0, a, 1.0)))).astype(np.int64)
+    step = np.ldexp(1.0, np.where(sub, -9, e - 3))
+    q = np.rint(a / step)                                   # ties to even
+    # sub: code = q (q = 8 is the smallest normal); normal: q in [8, 16], 16 carries into the exponent
+    carry = (~sub) & (q == 16)
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 8, q)
+    code = np.where(sub, q, ((e + 7) << 3) + (q - 8)).astype(np.int64)
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def mx_quantize(x: Array, block: int = 32) -> Tuple[Array, Array]:
+    """Quantise the last axis in blocks of ``block``: (e4m3 codes, e8m0 scale bytes)."""
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] % block == 0
+    xb = x.reshape(x.shape[:-1] + (x.shape[-1] // block, block))
+    amax = np.abs(xb).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    e = np.maximum(e, -127).astype(np.int64)
+    y = np.clip(xb / np.ldexp(1.0, e)[..., None], -E4M3_MAX, E4M3_MAX)
+    codes = e4m3_encode(y).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes: Array, scales: Array, block: int = 32) -> Array:
+    v = e4m3_value(codes)
+    vb = v.reshape(v.shape[:-1] + (v.shape[-1] // block, block))
+    return (vb * np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]).reshape(v.shape)
+
+
+def mx_linear(a_codes: Array, a_scales: Array, w_codes: Array, w_scales: Array, bias=None) -> Array:
+    """y = dequant(A) dequant(W)^T (+ b) in float64: what the scaled matrix instruction computes
+    before the fp32 rounding of its accumulation."""
+    y = mx_dequantize(a_codes, a_scales) @ mx_dequantize(w_codes, w_scales).T
+    return y if bias is None else y + bias
+
+
+def relative_error_bound() -> float:
+    """Largest relative error of one element in the normal range: half a unit in the last of 3
+    mantissa bits."""
+    return math.ldexp(1.0, -4)

@@ -1,0 +1,82 @@
+"""Pins of the oracle's MXFP8 quantisation against the format's closed forms.
+
+* e4m3 code values: 448 = 1.75 x 2^8 is the largest finite value, 2^-6 the smallest normal, 2^-9
+  the smallest subnormal, 1.0 has exponent field 7 (bias 7).
+* Every finite code round-trips; midpoints between neighbouring codes go to the even code (ties to
+  even), values just above a midpoint go up; encoding is monotone.
+* Blocks: the block maximum lands in [256, 448] (the scale is the largest power of two with that
+  property, except when saturating above 448); all-zero blocks get code 0 and the smallest scale;
+  the dequantised error stays within half a unit in the last place of the element grid.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+
+
+def _finite_codes():
+    return np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def test_e4m3_closed_forms():
+    v = O.e4m3_value(np.array([0x7E, 0x08, 0x01, 0x38, 0xB8, 0x00, 0x80, 0x07], dtype=np.uint8))
+    assert list(v[:5]) == [448.0, 2.0 ** -6, 2.0 ** -9, 1.0, -1.0]
+    assert v[5] == 0.0 and v[6] == 0.0 and np.signbit(v[6])
+    assert v[7] == 7 * 2.0 ** -9                      # largest subnormal
+
+
+def test_round_trip_ties_and_monotonicity():
+    codes = _finite_codes()
+    vals = O.e4m3_value(codes)
+    np.testing.assert_array_equal(O.e4m3_encode(vals), codes)
+    pos = np.sort(O.e4m3_value(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = 0.5 * (pos[:-1] + pos[1:])
+    lo_codes = O.e4m3_encode(pos[:-1])
+    hi_codes = O.e4m3_encode(pos[1:])
+    got = O.e4m3_encode(mids)
+    even = np.where(lo_codes % 2 == 0, lo_codes, hi_codes)
+    np.testing.assert_array_equal(got, even)
+    np.testing.assert_array_equal(O.e4m3_encode(np.nextafter(mids, np.inf)), hi_codes)
+    np.testing.assert_array_equal(O.e4m3_encode(np.nextafter(mids, -np.inf)), lo_codes)
+    sweep = np.linspace(-448, 448, 20001)
+    assert np.all(np.diff(O.e4m3_value(O.e4m3_encode(sweep))) >= 0)
+
+
+@pytest.mark.parametrize("p", [-20, -3, 0, 5, 40])
+def test_block_scale_places_the_maximum(p):
+    rng = np.random.default_rng(p + 50)
+    x = rng.uniform(-1, 1, (3, 64)) * 2.0 ** p
+    x[:, 7] = 2.0 ** p                                  # block 0 maximum is a power of two
+    codes, scales = O.mx_quantize(x)
+    assert np.all(scales[:, 0] == p - 8 + 127)
+    assert np.all(O.e4m3_value(codes[:, 7]) == 256.0)
+    y = np.abs(x.reshape(3, 2, 32)) / np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]
+    assert np.all(y.max(axis=-1) >= 256.0) and np.all(y.max(axis=-1) < 512.0)
+
+
+def test_zero_block_and_error_bound():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((16, 256)) * np.exp(rng.uniform(-8, 8, (16, 1)))
+    x[3, 32:64] = 0.0
+    codes, scales = O.mx_quantize(x)
+    assert scales[3, 1] == 0 and np.all(codes[3, 32:64] == 0)
+    xq = O.mx_dequantize(codes, scales)
+    X = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+    y = np.abs(x) / X
+    normal = (y >= 2.0 ** -6) & (y <= 448.0)
+    assert np.all(np.abs(xq - x)[normal] <= O.mx.relative_error_bound() * np.abs(x)[normal])
+    small = y < 2.0 ** -6
+    assert np.all(np.abs(xq - x)[small] <= 2.0 ** -10 * X[small])
+    over = y > 448.0                                    # saturation to the largest finite value
+    assert np.all(np.abs(xq[over]) == 448.0 * X[over])
+
+
+def test_mx_linear_is_the_product_of_dequantised_operands():
+    rng = np.random.default_rng(4)
+    a, w = rng.standard_normal((5, 64)), rng.standard_normal((3, 64))
+    ac, asc = O.mx_quantize(a)
+    wc, wsc = O.mx_quantize(w)
+    ref = np.einsum("ik,jk->ij", O.mx_dequantize(ac, asc), O.mx_dequantize(wc, wsc))
+    np.testing.assert_allclose(O.mx_linear(ac, asc, wc, wsc), ref, rtol=1e-13, atol=1e-13)
+    # quantisation error of the product stays at the element level: ~2^-4 relative per element
+    assert np.abs(O.mx_linear(ac, asc, wc, wsc) - a @ w.T).max() < 0.15 * np.abs(a @ w.T).max()
