@@ -245,6 +245,24 @@ wam_status wam_denoise_chunk_unipc(const wam_config *cfg, const wam_weights *w, 
 wam_status wam_op_linear(wam_dtype dtype, const void *A, int lda, const void *W, int ldw, const float *bias, void *C,
                          int ldc, int M, int N, int K, int act, void *ws, size_t ws_bytes, void *stream);
 
+/* Low-precision projections ([N569] real-time optimisations: quantised projections) in the OCP
+ * microscaling format that gfx950's scaled matrix instructions read (MXFP8): fp8 e4m3 codes (bias
+ * 7, subnormals, largest finite 448) sharing one e8m0 power-of-two scale per 32 consecutive elements
+ * of a row. Quantisation: per block e = max(floor(log2(amax)) - 8, -127), scale byte e + 127, codes
+ * = e4m3 of x * 2^-e saturated to +-448, rounded to nearest even (deterministic, bit-exact).
+ *   wam_mx_quantize: src [rows][ld] (bf16 or float, dtype) -> codes [rows][ldq] bytes (ldq multiple
+ *   of 16), scales [rows][cols / 32] bytes; cols multiple of 32.
+ *   wam_op_linear_mx: C[m][n] = act(sum_k dequant(A)[m][k] dequant(W)[n][k] + bias[n]) with A codes
+ *   [M][lda] and scales [M][K/32], W codes [N][ldw] and scales [N][K/32], fp32 accumulation, C bf16
+ *   [M][ldc]; act as wam_op_linear; K multiple of 128, N multiple of 4, lda / ldw multiples of 16,
+ *   codes 16-byte and scales 4-byte aligned. Errors: WAM_E_SHAPE / WAM_E_ARG, nothing launched.
+ *   ws: optional scratch for split-K partials (as wam_op_linear). */
+wam_status wam_mx_quantize(wam_dtype dtype, const void *src, int ld, int rows, int cols, void *codes, int ldq,
+                           void *scales, void *stream);
+wam_status wam_op_linear_mx(const void *A, const void *A_scales, int lda, const void *W, const void *W_scales, int ldw,
+                            const float *bias, void *C, int ldc, int M, int N, int K, int act, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /* Attention ([ARCH] §2.3 causal self-attention and cross-attention; [HYPER] 方法 mask):
  * for branch b, head h, query q < Lq: softmax over keys j < limit(q) of (Q.K_j) / sqrt(head_dim), times V,
  * limit(q) = kv_total, or min(kv_total, kv_base + (q / chunk_q + 1) * chunk_q) when chunk_q > 0.

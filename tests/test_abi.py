@@ -120,6 +120,27 @@ def test_op_validation():
                              None) == wam.WAM_E_ARG
 
 
+def test_mx_validation():
+    """MXFP8 entry points reject bad shapes and alignment on the host (fake pointers, nothing launched)."""
+    lib = _lib()
+    P = 0x1000
+    # quantiser: cols not a multiple of 32, ldq not a multiple of 16, src misaligned, unknown dtype
+    assert lib.wam_mx_quantize(0, P, 48, 4, 48, P, 48, P, None) == wam.WAM_E_SHAPE
+    assert lib.wam_mx_quantize(0, P, 64, 4, 64, P, 72, P, None) == wam.WAM_E_SHAPE
+    assert lib.wam_mx_quantize(1, P + 4, 64, 4, 64, P, 64, P, None) == wam.WAM_E_ARG
+    assert lib.wam_mx_quantize(7, P, 64, 4, 64, P, 64, P, None) == wam.WAM_E_ARG
+    # product: K not a multiple of 128, N not a multiple of 4, odd SwiGLU pitch, scale misaligned, NULL operand
+    args = lambda **kw: [kw.get(n, d) for n, d in (  # noqa: E731
+        ("A", P), ("As", P), ("lda", 256), ("W", P), ("Ws", P), ("ldw", 256), ("bias", None), ("C", P), ("ldc", 64),
+        ("M", 8), ("N", 64), ("K", 256), ("act", 0), ("ws", None), ("wsb", 0), ("s", None))]
+    assert lib.wam_op_linear_mx(*args(K=192, lda=192, ldw=192)) == wam.WAM_E_SHAPE
+    assert lib.wam_op_linear_mx(*args(N=62)) == wam.WAM_E_SHAPE
+    assert lib.wam_op_linear_mx(*args(N=60, act=2, ldc=30)) == wam.WAM_E_SHAPE
+    assert lib.wam_op_linear_mx(*args(Ws=P + 2)) == wam.WAM_E_ARG
+    assert lib.wam_op_linear_mx(*args(As=None)) == wam.WAM_E_ARG
+    assert lib.wam_op_linear_mx(*args(act=3)) == wam.WAM_E_ARG
+
+
 def test_kv_reset_is_host_only():
     _lib()
     kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 512, 464)

@@ -17,7 +17,7 @@ WAM_OK, WAM_E_ARG, WAM_E_SHAPE, WAM_E_CAPACITY, WAM_E_HIP, WAM_E_UNSUPPORTED = 0
 WAM_BF16, WAM_F32 = 0, 1
 
 EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
-           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear", "wam_op_attention", "wam_kv_evict", "wam_kv_reset",
+           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear", "wam_mx_quantize", "wam_op_linear_mx", "wam_op_attention", "wam_kv_evict", "wam_kv_reset",
            "wam_last_error")
 
 
@@ -88,6 +88,8 @@ def load(path: str = LIB_PATH):
         "wam_denoise_chunk_unipc": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, I, I, P, P, P, P, P, P, P, S, P, P,
                                         P]),
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
+        "wam_mx_quantize": (I, [I, P, I, I, I, P, I, P, P]),
+        "wam_op_linear_mx": (I, [P, P, I, P, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P, S, P]),
         "wam_kv_evict": (I, [CFG, KV, I, I, P]),
         "wam_kv_reset": (None, [KV]),
@@ -211,6 +213,17 @@ def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, ws=None, 
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().wam_op_linear(dtype, _ptr(A), lda, _ptr(W), ldw, _ptr(bias), _ptr(C), ldc, M, N, K, act,
                                 _ptr(ws), nbytes, _stream(stream)))
+
+
+def wam_mx_quantize(dtype, src, ld, rows, cols, codes, ldq, scales, stream=None):
+    _check(load().wam_mx_quantize(dtype, _ptr(src), ld, rows, cols, _ptr(codes), ldq, _ptr(scales), _stream(stream)))
+
+
+def wam_op_linear_mx(A, A_scales, lda, W, W_scales, ldw, bias, C, ldc, M, N, K, act=0, ws=None, stream=None):
+    """MXFP8 product: uint8 code / scale tensors in, bf16 C out."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().wam_op_linear_mx(_ptr(A), _ptr(A_scales), lda, _ptr(W), _ptr(W_scales), ldw, _ptr(bias), _ptr(C), ldc,
+                                   M, N, K, act, _ptr(ws), nbytes, _stream(stream)))
 
 
 def wam_op_attention(dtype, Q, K, Vt, O, br, heads, head_dim, Lq, k_rows, v_stride, kv_base, chunk_q, kv_total,

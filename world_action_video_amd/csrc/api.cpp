@@ -787,6 +787,43 @@ wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W,
   return WAM_OK;
 }
 
+wam_status wam_mx_quantize(wam_dtype dtype, const void* src, int ld, int rows, int cols, void* codes, int ldq,
+                           void* scales, void* stream) {
+  if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
+  if (!src || !codes || !scales) return fail(WAM_E_ARG, "NULL buffer");
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(WAM_E_SHAPE, "cols must be a positive multiple of 32");
+  if (ld < cols || ldq < cols || ldq % 16 || ld % (dtype == WAM_BF16 ? 8 : 4))
+    return fail(WAM_E_SHAPE, "ld must keep rows 16-byte aligned and ldq be a multiple of 16, both >= cols");
+  if (unaligned16(src) || unaligned16(codes)) return fail(WAM_E_ARG, "src and codes must be 16-byte aligned");
+  HIP_TRY(launch_mx_quantize(src, ld, dtype == WAM_BF16 ? DT_BF16 : DT_F32, rows, cols, reinterpret_cast<uint8_t*>(codes),
+                             ldq, reinterpret_cast<uint8_t*>(scales), reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
+wam_status wam_op_linear_mx(const void* A, const void* A_scales, int lda, const void* W, const void* W_scales, int ldw,
+                            const float* bias, void* C, int ldc, int M, int N, int K, int act, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!A || !A_scales || !W || !W_scales || !C) return fail(WAM_E_ARG, "NULL operand");
+  if (M < 0 || N <= 0 || K <= 0 || K % 128) return fail(WAM_E_SHAPE, "K must be a positive multiple of 128");
+  if (N % 4) return fail(WAM_E_SHAPE, "N must be a multiple of 4");
+  if (act < 0 || act > 2) return fail(WAM_E_ARG, "act must be 0, 1 or 2");
+  if (lda < K || ldw < K || lda % 16 || ldw % 16) return fail(WAM_E_SHAPE, "lda/ldw must be multiples of 16, >= K");
+  if (ldc < (act == 2 ? N / 2 : N) || ldc % 4) return fail(WAM_E_SHAPE, "ldc too small or not a multiple of 4");
+  if (unaligned16(A) || unaligned16(W) || reinterpret_cast<uintptr_t>(C) % 8 || (bias && unaligned16(bias)))
+    return fail(WAM_E_ARG, "A, W (16 bytes), C (8 bytes) and bias (16 bytes) alignment");
+  if (reinterpret_cast<uintptr_t>(A_scales) % 4 || reinterpret_cast<uintptr_t>(W_scales) % 4)
+    return fail(WAM_E_ARG, "scale arrays must be 4-byte aligned");
+  if (ws && reinterpret_cast<uintptr_t>(ws) % 256) return fail(WAM_E_ARG, "workspace must be 256-byte aligned");
+  GemmArgs ga = gemm_args(A, lda, W, ldw, bias, M, N, K, ws ? reinterpret_cast<float*>(ws) : nullptr,
+                          ws ? (long)(ws_bytes / 4) : 0);
+  ga.C = C;
+  ga.ldc = ldc;
+  ga.As = reinterpret_cast<const uint8_t*>(A_scales);
+  ga.Ws = reinterpret_cast<const uint8_t*>(W_scales);
+  HIP_TRY(launch_gemm_mx(ga, act == 2 ? EPI_SWIGLU : act ? EPI_GELU : EPI_STORE, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
 wam_status wam_op_attention(wam_dtype dtype, const void* Q, const void* K, const void* Vt, void* O, int br, int heads,
                             int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,
                             void* ws, size_t ws_bytes, void* stream) {

@@ -248,6 +248,123 @@ gemm_kernel(GemmArgs g) {
 // ------------------------------------------------------------------------------------------------
 static constexpr int EPI_PARTIAL = 16;   // internal: fp32 partial products of one split
 
+// Epilogue of the 256x256 four-wave tiles (bf16 and MXFP8 operands alike).
+template <int EPI>
+__device__ __forceinline__ void g4_epilogue(const GemmArgs& g, const floatx16 (&acc)[4][4], int m0, int n0, int sp,
+                                            int wm, int wn, int l32, int half) {
+  constexpr int TM = 4, TN = 4, WM = 128, WN = 128;
+  // ---- epilogue: lane (l32, half) holds, for block (i, j), output row m = mb + 32 i and columns
+  // nb + 32 j + 8 g + 0..3 in acc[i][j][4 g .. 4 g + 3] (g = 0..3). N % 4 == 0 (checked at launch), so
+  // a run is either wholly inside the matrix or wholly outside.
+  const int mb = m0 + wm * WM + l32, nb = n0 + wn * WN + 4 * half;
+  auto run = [&](int i, int j, int gq) {
+    return make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+  };
+  if constexpr (EPI == EPI_PARTIAL) {
+    float* part = g.part + (long)sp * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mb + 32 * i;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          if (n < g.N) *reinterpret_cast<float4*>(part + (long)m * g.N + n) = run(i, j, gq);
+        }
+    }
+    return;
+  }
+  float4 bias[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int n = nb + 32 * j + 8 * gq;
+      bias[j][gq] = (g.bias && n < g.N) ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mb + 32 * i;
+      if (m >= g.M) continue;
+      bf16_t* crow = reinterpret_cast<bf16_t*>(g.C) + (long)m * g.ldc;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          if (n >= g.N) continue;
+          float4 v = run(i, j, gq);
+          const float4 b = bias[j][gq];
+          v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+          if constexpr (EPI == EPI_SWIGLU) {   // columns (n, n+1), (n+2, n+3): two outputs at n / 2
+            *reinterpret_cast<uint32_t*>(crow + n / 2) = pack2_bf16(silu_f(v.x) * v.y, silu_f(v.z) * v.w);
+            continue;
+          }
+          if constexpr (EPI == EPI_GELU) {
+            v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
+          }
+          *reinterpret_cast<uint2*>(crow + n) = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+        }
+    }
+  } else {   // EPI_RESID, EPI_RESID_GATED: fp32 residual rows, read-modify-write per run of four
+    float4 gm[TN][4];
+    if constexpr (EPI == EPI_RESID_GATED) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          gm[j][gq] = n < g.N ? *reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D + n)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mb + 32 * i;
+      if (m >= g.M) continue;
+      float* hrow = g.H + (long)m * g.ldh;
+      const float* grow = nullptr;
+      if constexpr (EPI == EPI_RESID_GATED) {
+        const int rb = m % g.rm.rows_per_branch;
+        const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
+        grow = g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D;
+      }
+      // per block: the four runs' loads first, then the updates
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float4 hv[4], gv[4];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          const bool ok = n < g.N;
+          hv[gq] = ok ? *reinterpret_cast<const float4*>(hrow + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+          if constexpr (EPI == EPI_RESID_GATED)
+            gv[gq] = ok ? *reinterpret_cast<const float4*>(grow + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nb + 32 * j + 8 * gq;
+          if (n >= g.N) continue;
+          float4 v = run(i, j, gq);
+          const float4 b = bias[j][gq];
+          v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+          float4 h = hv[gq];
+          if constexpr (EPI == EPI_RESID_GATED) {
+            const float4 ge = gv[gq], gmm = gm[j][gq];
+            h.x += (ge.x + gmm.x) * v.x; h.y += (ge.y + gmm.y) * v.y; h.z += (ge.z + gmm.z) * v.z; h.w += (ge.w + gmm.w) * v.w;
+          } else {
+            h.x += v.x; h.y += v.y; h.z += v.z; h.w += v.w;
+          }
+          *reinterpret_cast<float4*>(hrow + n) = h;
+        }
+      }
+    }
+  }
+}
+
 template <int EPI, int IL = 1>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm4_kernel(GemmArgs g, int splits) {
@@ -477,118 +594,179 @@ gemm4_kernel(GemmArgs g, int splits) {
   }
   if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
 
-  // ---- epilogue: lane (l32, half) holds, for block (i, j), output row m = mb + 32 i and columns
-  // nb + 32 j + 8 g + 0..3 in acc[i][j][4 g .. 4 g + 3] (g = 0..3). N % 4 == 0 (checked at launch), so
-  // a run is either wholly inside the matrix or wholly outside.
-  const int mb = m0 + wm * WM + l32, nb = n0 + wn * WN + 4 * half;
-  auto run = [&](int i, int j, int gq) {
-    return make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-  };
-  if constexpr (EPI == EPI_PARTIAL) {
-    float* part = g.part + (long)sp * g.M * g.N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = mb + 32 * i;
-      if (m >= g.M) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = nb + 32 * j + 8 * gq;
-          if (n < g.N) *reinterpret_cast<float4*>(part + (long)m * g.N + n) = run(i, j, gq);
-        }
-    }
-    return;
-  }
-  float4 bias[TN][4];
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int n = nb + 32 * j + 8 * gq;
-      bias[j][gq] = (g.bias && n < g.N) ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = mb + 32 * i;
-      if (m >= g.M) continue;
-      bf16_t* crow = reinterpret_cast<bf16_t*>(g.C) + (long)m * g.ldc;
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = nb + 32 * j + 8 * gq;
-          if (n >= g.N) continue;
-          float4 v = run(i, j, gq);
-          const float4 b = bias[j][gq];
-          v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-          if constexpr (EPI == EPI_SWIGLU) {   // columns (n, n+1), (n+2, n+3): two outputs at n / 2
-            *reinterpret_cast<uint32_t*>(crow + n / 2) = pack2_bf16(silu_f(v.x) * v.y, silu_f(v.z) * v.w);
-            continue;
-          }
-          if constexpr (EPI == EPI_GELU) {
-            v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
-          }
-          *reinterpret_cast<uint2*>(crow + n) = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
-        }
-    }
-  } else {   // EPI_RESID, EPI_RESID_GATED: fp32 residual rows, read-modify-write per run of four
-    float4 gm[TN][4];
-    if constexpr (EPI == EPI_RESID_GATED) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = nb + 32 * j + 8 * gq;
-          gm[j][gq] = n < g.N ? *reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D + n)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = mb + 32 * i;
-      if (m >= g.M) continue;
-      float* hrow = g.H + (long)m * g.ldh;
-      const float* grow = nullptr;
-      if constexpr (EPI == EPI_RESID_GATED) {
-        const int rb = m % g.rm.rows_per_branch;
-        const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
-        grow = g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D;
-      }
-      // per block: the four runs' loads first, then the updates
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        float4 hv[4], gv[4];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = nb + 32 * j + 8 * gq;
-          const bool ok = n < g.N;
-          hv[gq] = ok ? *reinterpret_cast<const float4*>(hrow + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-          if constexpr (EPI == EPI_RESID_GATED)
-            gv[gq] = ok ? *reinterpret_cast<const float4*>(grow + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = nb + 32 * j + 8 * gq;
-          if (n >= g.N) continue;
-          float4 v = run(i, j, gq);
-          const float4 b = bias[j][gq];
-          v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
-          float4 h = hv[gq];
-          if constexpr (EPI == EPI_RESID_GATED) {
-            const float4 ge = gv[gq], gmm = gm[j][gq];
-            h.x += (ge.x + gmm.x) * v.x; h.y += (ge.y + gmm.y) * v.y; h.z += (ge.z + gmm.z) * v.z; h.w += (ge.w + gmm.w) * v.w;
-          } else {
-            h.x += v.x; h.y += v.y; h.z += v.z; h.w += v.w;
-          }
-          *reinterpret_cast<float4*>(hrow + n) = h;
-        }
-      }
-    }
-  }
+  g4_epilogue<EPI>(g, acc, m0, n0, sp, wm, wn, l32, half);
 }
 
+
+// ------------------------------------------------------------------------------------------------
+// MXFP8 256x256 four-wave product. Operands are fp8 e4m3 codes with one e8m0 (power-of-two) scale per
+// 32 consecutive k of a row; v_mfma_scale_f32_32x32x64_f8f6f4 applies the scales in the product.
+// A k-tile is 128 codes = 128 bytes per row, exactly the bytes of a bf16 k-tile, so the tile's LDS
+// layout (144-byte padded rows) and the global -> register -> LDS staging are those of gemm4_kernel;
+// one register set (the tile after next is requested while the next one is written to LDS).
+// Per tile: two k64 steps, each as two chunks of 8 MFMAs (row blocks 0-1, then 2-3). Operand lanes
+// (measured): lane l holds row l % 32; bytes 0-15 are k 16 h .. 16 h + 15 and bytes 16-31 are
+// k 32 + 16 h .. (h = l / 32) of the step, i.e. both 32-k scale blocks, and lane l supplies the scale
+// of block h of its row. The W block goes first (transposed accumulators, as in gemm4_kernel).
+// ------------------------------------------------------------------------------------------------
+typedef int int8v_t __attribute__((ext_vector_type(8)));
+
+template <int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm4mx_kernel(GemmArgs g, int splits) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 4, TN = 4;
+  constexpr int NT = 256, UNITS = 8, BK = 128, PER_T = BM * UNITS / NT, PITCH = UNITS + 1;
+  __shared__ uint4 smem[2][(BM + BN) * PITCH];
+
+  const int Mt = (g.M + BM - 1) / BM, Nt = (g.N + BN - 1) / BN;
+  const int items = Mt * Nt * splits;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per = items >> 3, rem = items & 7;
+  if (kx >= per + (xcd < rem ? 1 : 0)) return;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
+  const int mt = item % Mt, rest = item / Mt;
+  const int sp = rest % splits, nt = rest / splits;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KT_all = g.K / BK;
+  const int kb = (int)((long)sp * KT_all / splits), ke = (int)((long)(sp + 1) * KT_all / splits);
+  const int KT = ke - kb;
+  const int kblocks = g.K / 32;   // scale bytes per row
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  const __amdgpu_buffer_rsrc_t ra_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), (short)0,
+                                                                       (int)((long)g.M * g.lda), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.W), (short)0,
+                                                                       (int)((long)g.N * g.ldw), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.As), (short)0,
+                                                                        (int)((long)g.M * kblocks), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsw_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.Ws), (short)0,
+                                                                        (int)((long)g.N * kblocks), 0x00020000);
+  const int lrow = tid >> 3, lunit = tid & 7;
+  int offa[PER_T], offw[PER_T];
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    offa[i] = (int)((long)(m0 + lrow + i * 32) * g.lda + lunit * 16);
+    offw[i] = (int)((long)(n0 + lrow + i * 32) * g.ldw + lunit * 16);
+  }
+  // this lane's scale rows: row block i of the wave's A rows, column block j of its W rows
+  int soff_a[TM], soff_w[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) soff_a[i] = (m0 + wm * WM + i * 32 + l32) * kblocks;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) soff_w[j] = (n0 + wn * WN + j * 32 + l32) * kblocks;
+  const int sbase = lrow * PITCH + lunit;
+
+  uint4 rg[2 * PER_T];
+  auto gload_q = [&](int kt, int q) {
+    const int koff = (kb + min(kt, KT - 1)) * BK;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * q + u;
+      rg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_, offa[i], koff, 0));
+      rg[PER_T + i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw_, offw[i], koff, 0));
+    }
+  };
+  auto sstore_q = [&](int st, int q) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * q + u;
+      smem[st][sbase + i * 32 * PITCH] = rg[i];
+      smem[st][BM * PITCH + sbase + i * 32 * PITCH] = rg[PER_T + i];
+    }
+  };
+  // the four 32-k scale bytes of tile kt for this lane's rows (one dword per row block)
+  uint32_t sca[2][TM], scw[2][TN];
+  auto sload = [&](int kt, uint32_t* a_, uint32_t* w_) {
+    const int koff = (kb + min(kt, KT - 1)) * 4;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a_[i] = __builtin_amdgcn_raw_buffer_load_b32(rsa_, soff_a[i], koff, 0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) w_[j] = __builtin_amdgcn_raw_buffer_load_b32(rsw_, soff_w[j], koff, 0);
+  };
+  // fragments of chunk c: step s = c / 2, A row blocks 2 (c % 2), +1; W column blocks with the step
+  uint4 fa[2][2][2], fb[2][TN][2];
+  auto fload_a = [&](int st, int c, uint4 (&f)[2][2]) {
+    const int s_ = c >> 1, i0 = 2 * (c & 1);
+    const uint4* sa = smem[st] + (wm * WM + l32) * PITCH + half;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      f[ii][0] = sa[(i0 + ii) * 32 * PITCH + 4 * s_];
+      f[ii][1] = sa[(i0 + ii) * 32 * PITCH + 4 * s_ + 2];
+    }
+  };
+  auto fload_w = [&](int st, int s_, uint4 (&f)[TN][2]) {
+    const uint4* sb = smem[st] + (BM + wn * WN + l32) * PITCH + half;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      f[j][0] = sb[j * 32 * PITCH + 4 * s_];
+      f[j][1] = sb[j * 32 * PITCH + 4 * s_ + 2];
+    }
+  };
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_q(0, q);
+  sload(0, sca[0], scw[0]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sstore_q(0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_q(1, q);
+  __syncthreads();
+  fload_a(0, 0, fa[0]);
+  fload_w(0, 0, fb[0]);
+
+  // tile kt from LDS buffer CUR with scale set CUR; rg holds tile kt+1, written to the other buffer
+  // quarter by quarter and refilled with tile kt+2; scales of kt+1 are requested into the other set.
+  auto tile = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
+    sload(kt + 1, sca[nxt], scw[nxt]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int s_ = c >> 1, i0 = 2 * (c & 1);
+      const int fc = c & 1, fs = s_ & 1;
+      if (c + 1 < 4) {
+        fload_a(cur, c + 1, fa[fc ^ 1]);
+        if (c == 1) fload_w(cur, 1, fb[fs ^ 1]);
+      }
+      sstore_q(nxt, c);
+      gload_q(kt + 2, c);
+      if (c + 1 == 4) {
+        __syncthreads();
+        fload_a(nxt, 0, fa[fc ^ 1]);
+        fload_w(nxt, 0, fb[fs ^ 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = i0 + ii;
+        const int sa_ = (int)(sca[cur][i] >> (8 * (2 * s_ + half)));
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int sw_ = (int)(scw[cur][j] >> (8 * (2 * s_ + half)));
+          const int8v_t wv = __builtin_bit_cast(int8v_t, fb[fs][j]);
+          const int8v_t av = __builtin_bit_cast(int8v_t, fa[fc][ii]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 0, 0, 0, sw_, 0, sa_);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>{});
+    tile(kt + 1, std::integral_constant<int, 1>{});
+  }
+  if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
+  g4_epilogue<EPI>(g, acc, m0, n0, sp, wm, wn, l32, half);
+}
 
 // Sum of the split partials in split order, plus bias, then the epilogue. One thread per 4 columns.
 template <typename T, int EPI>
@@ -931,6 +1109,115 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
   hipError_t e = launch_gemm(a, dt, epi, s);
   if (e != hipSuccess) return e;
   return post.mode == POST_NORM ? launch_norm(post.na, dt, s) : launch_qk_norm_rope(post.qa, dt, s);
+}
+
+// MXFP8 quantisation (OCP microscaling, 32-element blocks along a row): shared exponent
+// e = floor(log2(amax)) - 8 (8 = exponent of e4m3's largest power of two), clamped to >= -127; the
+// codes are e4m3 of x * 2^-e (exact scaling) saturated to +-448 and rounded to nearest even by the
+// conversion instruction; the scale byte is e + 127. One thread per block.
+template <typename T>
+__global__ void __launch_bounds__(256) mx_quantize_kernel(const T* src, long ld, int rows, int cols, uint8_t* codes,
+                                                          long ldq, uint8_t* scales) {
+  const long blk = (long)blockIdx.x * 256 + threadIdx.x;
+  const int nb = cols / 32;
+  if (blk >= (long)rows * nb) return;
+  const int r = (int)(blk / nb), b = (int)(blk % nb);
+  const T* x = src + (long)r * ld + b * 32;
+  float v[32];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 w = reinterpret_cast<const uint4*>(x)[u];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * u + 2 * k] = __uint_as_float(ww[k] << 16);
+        v[8 * u + 2 * k + 1] = __uint_as_float(ww[k] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 w = reinterpret_cast<const float4*>(x)[u];
+      v[4 * u] = w.x; v[4 * u + 1] = w.y; v[4 * u + 2] = w.z; v[4 * u + 3] = w.w;
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xff);   // 0 for zero and fp32 subnormals
+  const int e = ebits == 0 ? -127 : max(ebits - 127 - 8, -127);
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, e in [-127, 119]
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float q[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) q[t] = fminf(fmaxf(v[4 * k + t] * inv, -448.f), 448.f);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+    w[k] = (uint32_t)lo;
+  }
+  uint4* out = reinterpret_cast<uint4*>(codes + (long)r * ldq + b * 32);
+  out[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  out[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  scales[(long)r * nb + b] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_mx_quantize(const void* src, long ld_src, DType dt, int rows, int cols, uint8_t* codes, long ldq,
+                              uint8_t* scales, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (cols % 32 || ldq % 16 || reinterpret_cast<uintptr_t>(codes) % 16 || reinterpret_cast<uintptr_t>(src) % 16 ||
+      ld_src % (dt == DT_BF16 ? 8 : 4))
+    return hipErrorInvalidValue;
+  const long blocks = (long)rows * (cols / 32);
+  const dim3 grid((unsigned)((blocks + 255) / 256)), block(256);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL((mx_quantize_kernel<bf16_t>), grid, block, 0, s, reinterpret_cast<const bf16_t*>(src), ld_src,
+                       rows, cols, codes, ldq, scales);
+  else
+    hipLaunchKernelGGL((mx_quantize_kernel<float>), grid, block, 0, s, reinterpret_cast<const float*>(src), ld_src,
+                       rows, cols, codes, ldq, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K % 128 || a.N % 4 || !a.As || !a.Ws || epi == EPI_ROWSEL_F32) return hipErrorInvalidValue;
+  if (epi == EPI_SWIGLU && a.N % 2) return hipErrorInvalidValue;
+  if ((long)a.M * a.lda >= (1L << 31) || (long)a.N * a.ldw >= (1L << 31) || a.lda % 16 || a.ldw % 16 ||
+      reinterpret_cast<uintptr_t>(a.A) % 16 || reinterpret_cast<uintptr_t>(a.W) % 16)
+    return hipErrorInvalidValue;
+  const bool vec_ok = (!a.bias || aligned16(a.bias)) &&
+                      (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_SWIGLU
+                           ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
+                           : (aligned16(a.H) && a.ldh % 4 == 0)) &&
+                      (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
+  if (!vec_ok) return hipErrorInvalidValue;
+  const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int KT = a.K / 128;
+  int splits = 1;
+  if (tiles < 128 && a.part) {   // as the bf16 product: about 240 workgroups, fp32 partials summed in order
+    splits = (int)((240 + tiles - 1) / tiles);
+    if (splits > 4) splits = 4;
+    while (splits > 1 && (KT < 2 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
+  }
+  const int units = (int)tiles * splits;
+  const dim3 grid(8 * ((units + 7) / 8)), block(256);
+  if (splits > 1) {
+    hipLaunchKernelGGL((gemm4mx_kernel<EPI_PARTIAL>), grid, block, 0, s, a, splits);
+    launch_reduce(a, epi, splits, s);
+    return hipGetLastError();
+  }
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL((gemm4mx_kernel<EPI_STORE>), grid, block, 0, s, a, 1); break;
+    case EPI_GELU: hipLaunchKernelGGL((gemm4mx_kernel<EPI_GELU>), grid, block, 0, s, a, 1); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm4mx_kernel<EPI_SWIGLU>), grid, block, 0, s, a, 1); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm4mx_kernel<EPI_RESID>), grid, block, 0, s, a, 1); break;
+    case EPI_RESID_GATED: hipLaunchKernelGGL((gemm4mx_kernel<EPI_RESID_GATED>), grid, block, 0, s, a, 1); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace wam

@@ -38,9 +38,19 @@ struct GemmArgs {
   int sel_group;             // EPI_ROWSEL_F32: 0 = video rows, 1 = action rows
   float* part;               // split-K scratch: [splits][M][N] fp32 partial products (nullptr: no split)
   long part_elems;           // capacity of `part` in floats
+  const uint8_t* As;         // MXFP8 operands only: e8m0 scales of A [M][K/32] and of W [N][K/32]
+  const uint8_t* Ws;         //   (A and W then hold fp8 e4m3 codes, lda / ldw in bytes)
 };
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s);
+// MXFP8 product ([N569] real-time optimisations: quantised projections; the OCP microscaling format
+// that gfx950's scaled MFMA reads): A, W fp8 e4m3 with one power-of-two scale per 32 consecutive k,
+// fp32 accumulation, the same epilogues as the bf16 product (bf16 outputs). K % 128 == 0, N % 4 == 0.
+hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s);
+// Quantise rows of a bf16 / fp32 matrix to MXFP8: codes [rows][cols] (row stride ldq bytes) and scales
+// [rows][cols/32]; cols % 32 == 0.
+hipError_t launch_mx_quantize(const void* src, long ld_src, DType dt, int rows, int cols, uint8_t* codes, long ldq,
+                              uint8_t* scales, hipStream_t s);
 
 // ---- attention ----------------------------------------------------------------------------------
 struct AttnArgs {
