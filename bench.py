@@ -24,6 +24,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the MXFP8 scaled instructions run at this rate)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WORKLOAD_ID = 3
 
@@ -148,6 +149,9 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
                     help="3: the step metric (default); 2: one full-width block (br = 2 and B = 1); 4: four chunks "
                          "of 16 Euler steps plus KV appends; 5: three-view long context, 16-step loop with reuse")
+    ap.add_argument("--precision", choices=("bf16", "mxfp8"), default="bf16",
+                    help="bf16 (the metric); mxfp8: the six block projections quantised to MXFP8, reported "
+                         "separately (its own dtype and workload name)")
     ap.add_argument("--counters", action="store_true",
                     help="run only a 1 GiB copy and launches of the dominant kernel (for rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -175,6 +179,9 @@ def main():
         extra_workload(args, dev)
         return
     w = WORKLOADS[WORKLOAD_ID]
+    mx = args.precision == "mxfp8"
+    if mx:
+        w = w.with_(precision=synth.workloads.PRECISION_MXFP8)
     Lq, Lv, La, D = w.chunk_tokens, w.video_tokens, w.action_tokens, w.dim
     M = w.branches * Lq
 
@@ -246,25 +253,37 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     finite = bool(torch.isfinite(vv).all().item() and torch.isfinite(va).all().item())
 
-    # dominant kernel: the QKV projection GEMM (bf16 MFMA, M = 928, N = 15360, K = 5120), same kernel and
-    # launch configuration as in the step, timed with HIP events on the library's stream
+    # dominant kernel: the QKV projection GEMM (M = 928, N = 15360, K = 5120; bf16 MFMA, or the scaled fp8
+    # MFMA on the packed weights of layer 0), same kernel and launch configuration as in the step, timed
+    # with HIP events on the library's stream
     y = torch.randn((M, D), device=dev).to(torch.bfloat16)
     cq = torch.empty((M, 3 * D), dtype=torch.bfloat16, device=dev)
     wq, bq = model.layers[0]["w_qkv"], model.layers[0]["b_qkv"]
+    if mx:
+        yq = torch.empty((M, D), dtype=torch.uint8, device=dev)
+        ys = torch.empty((M, D // 32), dtype=torch.uint8, device=dev)
+        wam.wam_mx_quantize(wam.WAM_BF16, y, D, M, D, yq, D, ys)
+        arena = model.blocks[0].mx   # w_qkv codes [3D][D] at offset 0, its scales after them (256-aligned)
+        wq_s = arena + ((3 * D * D + 255) // 256) * 256
+        qkv_op = lambda: wam.wam_op_linear_mx(yq, ys, D, arena, wq_s, D, bq, cq, 3 * D, M, 3 * D, D, 0)  # noqa: E731
+    else:
+        qkv_op = lambda: wam.wam_op_linear(wam.WAM_BF16, y, D, wq, D, bq, cq, 3 * D, M, 3 * D, D, 0)  # noqa: E731
     for _ in range(3):
-        wam.wam_op_linear(wam.WAM_BF16, y, D, wq, D, bq, cq, 3 * D, M, 3 * D, D, 0)
+        qkv_op()
     reps = 20
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        wam.wam_op_linear(wam.WAM_BF16, y, D, wq, D, bq, cq, 3 * D, M, 3 * D, D, 0)
+        qkv_op()
     e1.record()
     torch.cuda.synchronize()
     gemm_ms = e0.elapsed_time(e1) / reps
     gemm_flops = 2.0 * M * 3 * D * D
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    traffic = load_traffic(TRAFFIC_KEY, source_hash(os.path.join(ROOT, "world_action_video_amd", "csrc", "gemm.hip")))
+    traffic = None if mx else load_traffic(TRAFFIC_KEY, source_hash(os.path.join(ROOT, "world_action_video_amd", "csrc",
+                                                                                  "gemm.hip")))
+    peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
 
     fl = step_flops(w)
     step_tflops = fl["total"] / (ms * 1e-3) / 1e12
@@ -279,9 +298,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8 projections, bf16 elsewhere" if mx else "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latents/features)",
-        "config": {"workload": w.name, "layers": w.layers, "dim": w.dim, "heads": w.heads, "head_dim": w.head_dim,
+        "config": {"workload": w.name + ("+mxfp8-projections" if mx else ""), "layers": w.layers, "dim": w.dim, "heads": w.heads, "head_dim": w.head_dim,
                    "ffn_dim": w.ffn_dim, "branches": w.branches, "chunk_tokens": Lq, "cached_tokens": cache.length,
                    "ctx_tokens": w.ctx_len},
         "step_tflop": round(fl["total"] / 1e12, 3),
@@ -290,13 +309,14 @@ def main():
         "first_step_ms": round(first_ms, 1),
         "setup_s": round(setup_s, 1),
         "outputs_finite": finite,
-        "roofline": {"kernel": "gemm4_kernel<EPI_STORE> (bf16 256x256 tile, 4 waves; QKV projection, 928x15360x5120)",
-                     "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+        "roofline": {"kernel": ("gemm4mx_kernel<EPI_STORE> (MXFP8 scaled MFMA" if mx else
+                                "gemm4_kernel<EPI_STORE> (bf16") + " 256x256 tile, 4 waves; QKV projection, 928x15360x5120)",
+                     "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / peak, 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2)},
     }
     log("step %.3f ms; QKV GEMM %.1f us (%.1f TFLOP/s)" % (ms, gemm_ms * 1e3, gemm_tflops))
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not mx:
         log("timing the oracle on the host")
         del model, cache, ctx
         torch.cuda.empty_cache()

@@ -63,7 +63,17 @@ typedef struct {
   float rope_theta, eps;   /* 10000, 1e-6 */
   wam_dtype dtype;
   int variant;             /* 0, or WAM_VARIANT_* bits (architectural variants of [ARCH] §2.3) */
+  int precision;           /* WAM_PRECISION_NATIVE (0) or WAM_PRECISION_MXFP8 (see below) */
 } wam_config;
+
+/* Arithmetic of the six block projections (w_qkv, w_o, w_cq, w_co, w_ff1, w_ff2).
+ * NATIVE: in dtype. MXFP8 ([N569] real-time optimisations: low-precision projections; bf16 dtype
+ *   only, dim and ffn_dim multiples of 128): each projection's input rows are quantised to MXFP8
+ *   (see wam_mx_quantize) and multiplied with the layer's packed MXFP8 weights (wam_mx_pack_block)
+ *   by the scaled matrix instructions, fp32 accumulation; outputs, epilogues and every other
+ *   operation as NATIVE. The condition projections (wam_ctx_build), embeddings and heads stay in
+ *   dtype. */
+enum { WAM_PRECISION_NATIVE = 0, WAM_PRECISION_MXFP8 = 1 };
 
 /* Architectural variants drawn on the architecture page next to the adopted readings.
  * FRAME_CAUSAL: inside a chunk a video token sees the video tokens of its own and earlier frames
@@ -89,6 +99,8 @@ typedef struct {
   const void *w_co, *b_co;
   const void *w_ff1, *b_ff1;   /* [F][D], [F] (SwiGLU variant: [2F][D], [2F], see below) */
   const void *w_ff2, *b_ff2;   /* [D][F], [D] */
+  const void *mx;              /* MXFP8 precision only (else ignored): this layer's packed projections,
+                                  wam_mx_block_bytes(cfg) bytes written by wam_mx_pack_block, 256-aligned */
 } wam_block_weights;
 
 typedef struct {
@@ -274,6 +286,16 @@ wam_status wam_op_linear_mx(const void *A, const void *A_scales, int lda, const 
  * outputs (66 x 64 fp32 per 32 queries and range); the ranges are merged in a fixed order, so the
  * result is deterministic, and equals the unsplit result up to rounding. Without scratch (NULL, or
  * too small) nothing is split. The stack and block calls use their own workspace. */
+/* Packed MXFP8 projections of one layer for WAM_PRECISION_MXFP8. Layout (each region 256-byte
+ * aligned, in this order for w_qkv, w_o, w_cq, w_co, w_ff1, w_ff2): e4m3 codes [N][K] then e8m0 scales
+ * [N][K/32] of the [N][K] matrix. wam_mx_block_bytes: the arena size (0 for a configuration the
+ * format cannot serve: dtype not bf16, dim or ffn_dim not multiples of 128). wam_mx_pack_block
+ * quantises bw's bf16 matrices into dst (device, 256-byte aligned, dst_bytes >= the arena size); run
+ * once per layer after the weights are loaded. Errors: WAM_E_ARG / WAM_E_SHAPE, nothing launched. */
+size_t wam_mx_block_bytes(const wam_config *cfg);
+wam_status wam_mx_pack_block(const wam_config *cfg, const wam_block_weights *bw, void *dst, size_t dst_bytes,
+                             void *stream);
+
 wam_status wam_op_attention(wam_dtype dtype, const void *Q, const void *K, const void *Vt, void *O, int br, int heads,
                             int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,
                             void *ws, size_t ws_bytes, void *stream);

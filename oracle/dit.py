@@ -92,6 +92,21 @@ def linear(x: Array, w: Array, b: Optional[Array] = None) -> Array:
     return y
 
 
+def project(w, x: Array, W: Array, b: Optional[Array] = None) -> Array:
+    """A block projection y = x W^T + b. With MXFP8 precision (the low-precision projections of
+    [N569] real-time optimisations; format and block rule in ``oracle.mx``) the rows of x and of W
+    are first quantised along the input features and the product is taken of the quantised values,
+    exactly (then cast back to the dtype of x)."""
+    if getattr(w, "precision", 0) != 1:
+        return linear(x, W, b)
+    from .mx import mx_linear, mx_quantize
+    lead = x.shape[:-1]
+    xc, xs = mx_quantize(x.reshape(-1, x.shape[-1]).astype(np.float64))
+    wc, ws = mx_quantize(W.astype(np.float64))
+    y = mx_linear(xc, xs, wc, ws, None if b is None else b.astype(np.float64))
+    return y.reshape(lead + (W.shape[0],)).astype(x.dtype)
+
+
 def modulated_norm(x: Array, shift: Array, scale: Array, eps: float, rms: bool = False) -> Array:
     """adaLN: LN(x) (1 + scale) + shift ([ARCH] §2.3 single block: the normed input is modulated
     by shift and scale from the time embedding; reading R3: scale enters as 1 + scale). With
@@ -282,12 +297,12 @@ def feed_forward(w, lp: Dict[str, Array], y: Array) -> Array:
     """GELU_tanh(y W1^T + b1) W2^T + b2 (reading R6); with the SwiGLU variant drawn on [ARCH] §2.3,
     (SiLU(y Wg^T + bg) * (y Wu^T + bu)) W2^T + b2 where rows 2j / 2j+1 of W1 (and entries of b1)
     are the gate / up rows of hidden unit j."""
-    u = linear(y, lp["w_ff1"], lp["b_ff1"])
+    u = project(w, y, lp["w_ff1"], lp["b_ff1"])
     if getattr(w, "variant", 0) & 4:
         act = silu(u[..., 0::2]) * u[..., 1::2]
     else:
         act = gelu_tanh(u)
-    return linear(act, lp["w_ff2"], lp["b_ff2"])
+    return project(w, act, lp["w_ff2"], lp["b_ff2"])
 
 
 def visibility(w, chunk: Array, group: Array, cached: int) -> Array:
@@ -360,7 +375,7 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
     o_all = np.empty_like(h)
     for b in range(br):
         y = modulated_norm(h[b], shift1, scale1, w.eps, uses_rms(w))
-        qkv = linear(y, lp["w_qkv"], lp["b_qkv"])
+        qkv = project(w, y, lp["w_qkv"], lp["b_qkv"])
         q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
         q = rms_norm(q, w.eps, lp["g_q"]).reshape(T, H, d)
         k = rms_norm(k, w.eps, lp["g_k"]).reshape(T, H, d)
@@ -372,17 +387,17 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
         vv = np.concatenate([cache_v[b], v_new[b]], axis=0).reshape(-1, H, d).transpose(1, 0, 2)
         o = attention(q.transpose(1, 0, 2), kk, vv, visible)      # [H, T, d]
         o_all[b] = o.transpose(1, 0, 2).reshape(T, D)
-    h = h + gate1[None] * linear(o_all, lp["w_o"], lp["b_o"])
+    h = h + gate1[None] * project(w, o_all, lp["w_o"], lp["b_o"])
     # --- cross-attention sub-layer (no mask, no RoPE, no modulation)
     for b in range(br):
         n3 = (rms_norm(h[b], w.eps) * lp["ln3_w"] + lp["ln3_b"] if uses_rms(w)
               else layer_norm(h[b], w.eps, lp["ln3_w"], lp["ln3_b"]))
-        qc = rms_norm(linear(n3, lp["w_cq"], lp["b_cq"]), w.eps, lp["g_cq"]).reshape(T, H, d)
+        qc = rms_norm(project(w, n3, lp["w_cq"], lp["b_cq"]), w.eps, lp["g_cq"]).reshape(T, H, d)
         kc = ctx_k[b].reshape(-1, H, d).transpose(1, 0, 2)
         vc = ctx_v[b].reshape(-1, H, d).transpose(1, 0, 2)
         oc = attention(qc.transpose(1, 0, 2), kc, vc, None).transpose(1, 0, 2).reshape(T, D)
         oc_all[b] = oc
-    h = h + linear(oc_all, lp["w_co"], lp["b_co"])
+    h = h + project(w, oc_all, lp["w_co"], lp["b_co"])
     # --- feed-forward sub-layer
     y2 = modulated_norm(h, shift2[None], scale2[None], w.eps, uses_rms(w))
     h = h + gate2[None] * feed_forward(w, lp, y2)

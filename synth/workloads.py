@@ -43,6 +43,7 @@ class Workload:
     rope_theta: float = 10000.0
     guidance: float = 5.0
     variant: int = 0        # architectural variants of the pages (bit flags, see VARIANT_* below)
+    precision: int = 0      # arithmetic of the block projections: 0 the model dtype, PRECISION_MXFP8
 
     @property
     def video_tokens(self) -> int:
@@ -64,6 +65,10 @@ class Workload:
 VARIANT_FRAME_CAUSAL = 1   # inside a chunk a frame sees earlier and its own frames; actions see the chunk
 VARIANT_RMS_NORM = 2       # RMSNorm in place of the block and head LayerNorms
 VARIANT_SWIGLU = 4         # SwiGLU feed-forward: SiLU(gate) * up with interleaved [gate, up] rows
+
+# Low-precision block projections: inputs and weights quantised to MXFP8 (fp8 e4m3 codes with one
+# power-of-two scale per 32 consecutive input features)
+PRECISION_MXFP8 = 1
 
 WORKLOADS = {
     # Tiny single block: width 256, 4 heads of 64, FFN 1024, 2 frames of 8x8 patches + 24 action tokens,

@@ -180,6 +180,40 @@ def test_variant_stack_matches_oracle(gpu, tiny_oracle, dtype, variant):
     assert ev <= TOL[dtype] and ea <= TOL[dtype]
 
 
+# MXFP8 projections against the oracle taking the same quantised projections. Both sides quantise
+# the same activations except that the library stores them in bf16 first: about 1% of the codes then
+# round to the neighbouring fp8 value (the bf16 half-ulp, 2^-9, against an fp8 spacing of 2^-4 to
+# 2^-3), a relative change near 1e-2 of each projection input; on top of the bf16 path's 2e-2.
+MX_TOL = 5e-2
+
+
+@pytest.mark.parametrize("variant", [0, synth.workloads.VARIANT_SWIGLU | synth.workloads.VARIANT_RMS_NORM])
+def test_mxfp8_stack_matches_oracle(gpu, tiny_oracle, variant):
+    """One cached chunk and a step with the six block projections in MXFP8, against the oracle with
+    the same quantised projections; the distance to the unquantised model is printed (quality)."""
+    w0, m0, ckv = tiny_oracle
+    w = w0.with_(variant=variant, precision=synth.workloads.PRECISION_MXFP8)
+    m = O.load_model(w) if variant & synth.workloads.VARIANT_SWIGLU else O.Model(w, m0.g, m0.layers)
+    print("mxfp8 stack, variant", variant, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.35], [0.55], 1, w.frames_per_chunk)
+    wn = w.with_(precision=0)
+    mn = O.Model(wn, m.g, m.layers)
+    cn = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(mn, cn, ckv, x1v[0], x1a[0], 0)
+    nat_v, nat_a = O.stack_forward(mn, cn, ckv, epv[1], epa[1], [0.35], [0.55], 1, w.frames_per_chunk)
+    rig = Rig(w, "bf16", gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    gv, ga = rig.step(dc, 1, epv[1], epa[1], [0.35], [0.55], w.frames_per_chunk)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 to the MXFP8 oracle: video %.3e action %.3e; oracle MXFP8 to unquantised: video %.3e "
+          "action %.3e" % (ev, ea, rel_l2(ref_v, nat_v), rel_l2(ref_a, nat_a)), flush=True)
+    assert ev <= MX_TOL and ea <= MX_TOL
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decoupled_timesteps_and_frames(gpu, tiny_oracle, dtype):
     """Different video/action timesteps and a non-zero window offset, two cached chunks."""

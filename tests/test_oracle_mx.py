@@ -80,3 +80,63 @@ def test_mx_linear_is_the_product_of_dequantised_operands():
     np.testing.assert_allclose(O.mx_linear(ac, asc, wc, wsc), ref, rtol=1e-13, atol=1e-13)
     # quantisation error of the product stays at the element level: ~2^-4 relative per element
     assert np.abs(O.mx_linear(ac, asc, wc, wsc) - a @ w.T).max() < 0.15 * np.abs(a @ w.T).max()
+
+
+def _proj_inputs(seed=3):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((6, 128))
+    W = rng.standard_normal((10, 128)) * 0.05
+    b = rng.standard_normal(10) * 0.1
+    return x, W, b
+
+
+class _W:
+    precision = 1
+
+
+def test_projection_native_is_linear():
+    x, W, b = _proj_inputs()
+    class W0:
+        precision = 0
+    assert np.array_equal(O.project(W0, x, W, b), O.linear(x, W, b))
+
+
+def test_projection_mx_exact_on_representable_operands():
+    """Operands already on the MXFP8 grid (small-integer mantissas, one binade span per block) are
+    unchanged by quantisation, so the projection is the plain product."""
+    rng = np.random.default_rng(4)
+    # multiples of 1/8 up to 14/8 are e4m3 values; with block amax 1.75 the block exponent is -8 and
+    # 1.75 * 2^8 = 448, the largest code, so nothing saturates (amax 1.875 would: 480 > 448)
+    x = rng.integers(-14, 15, size=(5, 64)) / 8.0
+    x[:, ::32] = 1.75
+    W = rng.integers(-14, 15, size=(7, 64)) / 4.0
+    W[:, ::32] = 3.5
+    got = O.project(_W, x, W, None)
+    assert np.array_equal(got, x @ W.T)
+
+
+def test_projection_mx_quantises_along_input_features():
+    """Blocks run along the input features of each row: scaling one row of x (or one output row of
+    W) by a power of two scales exactly that output row (column) and changes nothing else."""
+    x, W, b = _proj_inputs()
+    base = O.project(_W, x, W, None)
+    x2 = x.copy()
+    x2[2] *= 2.0 ** 5
+    y2 = O.project(_W, x2, W, None)
+    assert np.array_equal(np.delete(y2, 2, axis=0), np.delete(base, 2, axis=0))
+    assert np.array_equal(y2[2], base[2] * 2.0 ** 5)
+    W2 = W.copy()
+    W2[4] *= 2.0 ** -7
+    y3 = O.project(_W, x, W2, None)
+    assert np.array_equal(np.delete(y3, 4, axis=1), np.delete(base, 4, axis=1))
+    assert np.array_equal(y3[:, 4], base[:, 4] * 2.0 ** -7)
+
+
+def test_projection_mx_error_is_that_of_the_format():
+    """Quantising both operands of a 128-term product: relative L2 error of a few percent, between the
+    per-element e4m3 bound 2^-4 / sqrt(3)-ish and twice the bound."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 512))
+    W = rng.standard_normal((96, 512))
+    err = np.linalg.norm(O.project(_W, x, W, None) - x @ W.T) / np.linalg.norm(x @ W.T)
+    assert 0.01 < err < 2 * O.relative_error_bound()

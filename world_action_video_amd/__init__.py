@@ -15,9 +15,10 @@ LIB_PATH = os.path.join(_HERE, "libwam.so")
 
 WAM_OK, WAM_E_ARG, WAM_E_SHAPE, WAM_E_CAPACITY, WAM_E_HIP, WAM_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 WAM_BF16, WAM_F32 = 0, 1
+WAM_PRECISION_NATIVE, WAM_PRECISION_MXFP8 = 0, 1
 
 EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
-           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear", "wam_mx_quantize", "wam_op_linear_mx", "wam_op_attention", "wam_kv_evict", "wam_kv_reset",
+           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear", "wam_mx_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block", "wam_op_attention", "wam_kv_evict", "wam_kv_reset",
            "wam_last_error")
 
 
@@ -33,7 +34,7 @@ class wam_config(ctypes.Structure):
                                              "grid_h", "grid_w", "ctx_in_dim", "ctx_text_len", "ctx_img_len",
                                              "branches")] + \
               [("rope_theta", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int),
-               ("variant", ctypes.c_int)]
+               ("variant", ctypes.c_int), ("precision", ctypes.c_int)]
 
 
 BLOCK_FIELDS = ("mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "ln3_w", "ln3_b", "w_cq", "b_cq", "g_cq",
@@ -43,7 +44,7 @@ GLOBAL_FIELDS = ("t_w1", "t_b1", "t_w2", "t_b2", "t_wp", "t_bp", "pe_w", "pe_b",
 
 
 class wam_block_weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_FIELDS] + [("mx", ctypes.c_void_p)]
 
 
 class wam_weights(ctypes.Structure):
@@ -89,6 +90,8 @@ def load(path: str = LIB_PATH):
                                         P]),
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_mx_quantize": (I, [I, P, I, I, I, P, I, P, P]),
+        "wam_mx_block_bytes": (S, [CFG]),
+        "wam_mx_pack_block": (I, [CFG, ctypes.POINTER(wam_block_weights), P, S, P]),
         "wam_op_linear_mx": (I, [P, P, I, P, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P, S, P]),
         "wam_kv_evict": (I, [CFG, KV, I, I, P]),
@@ -217,6 +220,15 @@ def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, ws=None, 
 
 def wam_mx_quantize(dtype, src, ld, rows, cols, codes, ldq, scales, stream=None):
     _check(load().wam_mx_quantize(dtype, _ptr(src), ld, rows, cols, _ptr(codes), ldq, _ptr(scales), _stream(stream)))
+
+
+def wam_mx_block_bytes(cfg: wam_config) -> int:
+    return int(load().wam_mx_block_bytes(ctypes.byref(cfg)))
+
+
+def wam_mx_pack_block(cfg: wam_config, bw: wam_block_weights, dst, stream=None):
+    nbytes = dst.numel() * dst.element_size()
+    _check(load().wam_mx_pack_block(ctypes.byref(cfg), ctypes.byref(bw), _ptr(dst), nbytes, _stream(stream)))
 
 
 def wam_op_linear_mx(A, A_scales, lda, W, W_scales, ldw, bias, C, ldc, M, N, K, act=0, ws=None, stream=None):

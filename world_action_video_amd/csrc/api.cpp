@@ -39,6 +39,8 @@ struct Geo {
   int D, H, d, F, L, P, A, La, Lv, Lq, Lc, Cin, br, freq;
   size_t esz;
   DType dt;
+  bool mx;     // MXFP8 block projections
+  int F1;      // rows of w_ff1 (2F for the SwiGLU variant)
 };
 
 Geo geo_of(const wam_config& c) {
@@ -49,7 +51,30 @@ Geo geo_of(const wam_config& c) {
   g.freq = c.freq_dim;
   g.dt = c.dtype == WAM_BF16 ? DT_BF16 : DT_F32;
   g.esz = c.dtype == WAM_BF16 ? 2 : 4;
+  g.mx = c.precision == WAM_PRECISION_MXFP8;
+  g.F1 = (c.variant & WAM_VARIANT_SWIGLU) ? 2 * c.ffn_dim : c.ffn_dim;
   return g;
+}
+
+// Packed MXFP8 projections of one layer: codes [N][K] then scales [N][K/32] per matrix, 256-aligned.
+enum { MX_QKV, MX_O, MX_CQ, MX_CO, MX_FF1, MX_FF2, MX_MATS };
+struct MxMat { size_t codes, scales; int N, K; };
+struct MxBlock { MxMat m[MX_MATS]; size_t total; };
+
+MxBlock mx_block_of(const Geo& g) {
+  MxBlock b{};
+  const int NK[MX_MATS][2] = {{3 * g.D, g.D}, {g.D, g.D}, {g.D, g.D}, {g.D, g.D}, {g.F1, g.D}, {g.D, g.F}};
+  size_t off = 0;
+  for (int i = 0; i < MX_MATS; ++i) {
+    b.m[i].N = NK[i][0];
+    b.m[i].K = NK[i][1];
+    b.m[i].codes = off;
+    off += ((size_t)b.m[i].N * b.m[i].K + 255) & ~size_t(255);
+    b.m[i].scales = off;
+    off += ((size_t)b.m[i].N * (b.m[i].K / 32) + 255) & ~size_t(255);
+  }
+  b.total = off;
+  return b;
 }
 
 wam_status check_cfg(const wam_config* c) {
@@ -73,13 +98,17 @@ wam_status check_cfg(const wam_config* c) {
   if (!(c->eps > 0.f) || !(c->rope_theta > 0.f)) return fail(WAM_E_ARG, "eps and rope_theta must be positive");
   if (c->variant & ~(WAM_VARIANT_FRAME_CAUSAL | WAM_VARIANT_RMS_NORM | WAM_VARIANT_SWIGLU))
     return fail(WAM_E_UNSUPPORTED, "unknown variant bits 0x%x", c->variant);
+  if (c->precision != WAM_PRECISION_NATIVE && c->precision != WAM_PRECISION_MXFP8)
+    return fail(WAM_E_UNSUPPORTED, "unknown precision %d", c->precision);
+  if (c->precision == WAM_PRECISION_MXFP8 && (c->dtype != WAM_BF16 || c->dim % 128 || c->ffn_dim % 128))
+    return fail(WAM_E_UNSUPPORTED, "MXFP8 projections need dtype bf16 and dim, ffn_dim multiples of 128");
   return WAM_OK;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t h, y, qkv, qh, attn, ffn, rope, emb, h1, e, e6, partials, ctx_a, ctx_b, part, total;
+  size_t h, y, qkv, qh, attn, ffn, rope, emb, h1, e, e6, partials, xq, xs, ctx_a, ctx_b, part, total;
   long part_elems;   // fp32 capacity of the split-K partial products
 };
 
@@ -100,6 +129,11 @@ Layout layout_of(const Geo& g, int n) {
   L.e = take(G * g.D * 4);
   L.e6 = take(G * 6 * g.D * 4);
   L.partials = take(64 * 3 * 4);
+  if (g.mx) {   // MXFP8 codes and scales of one projection input (up to ffn_dim columns)
+    const size_t kmax = std::max(g.D, g.F);
+    L.xq = take(M * kmax);
+    L.xs = take(M * (kmax / 32));
+  }
   size_t stack_total = off;
   // condition build (never concurrent with a pass on the same workspace): two [br*Lc][D] buffers
   const size_t cb = align256((size_t)g.br * g.Lc * g.D * g.esz);
@@ -124,10 +158,12 @@ const char* const kBlockNames[] = {"mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o",
 
 bool unaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
 
-wam_status check_block(const wam_block_weights* b, int l) {
+wam_status check_block(const wam_block_weights* b, int l, bool mx) {
   if (!b) return fail(WAM_E_ARG, "block weights of layer %d are NULL", l);
+  if (mx && (!b->mx || reinterpret_cast<uintptr_t>(b->mx) % 256))
+    return fail(WAM_E_ARG, "layer %d: MXFP8 precision needs the packed projections (mx, 256-byte aligned)", l);
   const void* const* p = reinterpret_cast<const void* const*>(b);
-  for (int i = 0; i < (int)(sizeof(wam_block_weights) / sizeof(void*)); ++i) {
+  for (int i = 0; i < (int)(sizeof(kBlockNames) / sizeof(kBlockNames[0])); ++i) {
     if (!p[i]) return fail(WAM_E_ARG, "layer %d: %s is NULL", l, kBlockNames[i]);
     if (unaligned16(p[i])) return fail(WAM_E_ARG, "layer %d: %s is not 16-byte aligned", l, kBlockNames[i]);
   }
@@ -146,7 +182,7 @@ wam_status check_weights(const wam_config* c, const wam_weights* w, bool need_bl
   if (need_blocks) {
     if (!w->blocks) return fail(WAM_E_ARG, "blocks array is NULL");
     for (int l = 0; l < c->layers; ++l) {
-      wam_status st = check_block(&w->blocks[l], l);
+      wam_status st = check_block(&w->blocks[l], l, c->precision == WAM_PRECISION_MXFP8);
       if (st != WAM_OK) return st;
     }
   }
@@ -222,6 +258,23 @@ NormArgs head_norm_args(const Pass& p, const wam_weights* w) {
   return na;
 }
 
+// MXFP8 projections: quantise the product's input rows (bf16 [M][K]) into the workspace, then point
+// the product at them and at the layer's packed weights, matrix rows from row0 on.
+hipError_t mx_operands(const Pass& p, const wam_block_weights& bw, GemmArgs& ga, const void* src, int mat, int row0) {
+  const MxMat mm = mx_block_of(p.g).m[mat];
+  uint8_t* xq = at<uint8_t>(p.ws, p.L.xq);
+  uint8_t* xs = at<uint8_t>(p.ws, p.L.xs);
+  const hipError_t e = launch_mx_quantize(src, mm.K, DT_BF16, p.M, mm.K, xq, mm.K, xs, p.s);
+  const char* base = reinterpret_cast<const char*>(bw.mx);
+  ga.A = xq;
+  ga.lda = mm.K;
+  ga.As = xs;
+  ga.W = base + mm.codes + (size_t)row0 * mm.K;
+  ga.ldw = mm.K;
+  ga.Ws = reinterpret_cast<const uint8_t*>(base + mm.scales + (size_t)row0 * (mm.K / 32));
+  return e;
+}
+
 // One block. kv_only: stop after the keys/values of this layer are in the cache. pre_normed: y
 // already holds this block's first AdaLN norm (written by the previous block's last product).
 // after: the row stage that follows this block (the next block's first norm or the head norm), run
@@ -254,6 +307,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
                             reinterpret_cast<const float*>(bw.b_qkv) + col0, p.M, 3 * g.D - col0, g.D, part, part_n);
     ga.C = reinterpret_cast<char*>(qkv) + (size_t)col0 * g.esz;
     ga.ldc = 3 * g.D;
+    if (g.mx) HIP_TRY(mx_operands(p, bw, ga, y, MX_QKV, col0));
     HIP_TRY(launch_gemm(ga, dt, EPI_STORE, p.s));
   }
   // (3) RMSNorm + RoPE of q (head-major) and k (into the cache), values into the cache
@@ -291,6 +345,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     post.na = adaln_args(p, mod, 0, 1);
     post.na.mode = NORM_AFFINE; post.na.w = reinterpret_cast<const float*>(bw.ln3_w);
     post.na.b = reinterpret_cast<const float*>(bw.ln3_b);
+    if (g.mx) HIP_TRY(mx_operands(p, bw, ga, attn, MX_O, 0));
     HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID_GATED, post, p.s));
   }
   // qc = RMS(n3 Wcq^T + b) g, head-major
@@ -302,6 +357,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     post.qa = qa;
     post.qa.src_ld = g.D; post.qa.src_col = 0; post.qa.gain = reinterpret_cast<const float*>(bw.g_cq); post.qa.rope = nullptr;
     post.qa.dst = qh; post.qa.dst_bh_stride = (long)p.R * g.d; post.qa.dst_row0 = 0;
+    if (g.mx) HIP_TRY(mx_operands(p, bw, ga, y, MX_CQ, 0));
     HIP_TRY(launch_gemm_post(ga, dt, EPI_STORE, post, p.s));
   }
   {
@@ -322,6 +378,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     PostArgs post{};
     post.mode = POST_NORM;
     post.na = adaln_args(p, mod, 3, 4);
+    if (g.mx) HIP_TRY(mx_operands(p, bw, ga, attn, MX_CO, 0));
     HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID, post, p.s));
   }
   // FFN: h += gate2 * (GELU(y2 W1^T + b1) W2^T + b2); SwiGLU variant: W1 has 2F interleaved
@@ -330,6 +387,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     const bool swiglu = (p.cfg->variant & WAM_VARIANT_SWIGLU) != 0;
     GemmArgs ga = gemm_args(y, g.D, bw.w_ff1, g.D, bw.b_ff1, p.M, swiglu ? 2 * g.F : g.F, g.D, part, part_n);
     ga.C = ffn; ga.ldc = g.F;
+    if (g.mx) HIP_TRY(mx_operands(p, bw, ga, y, MX_FF1, 0));
     HIP_TRY(launch_gemm(ga, dt, swiglu ? EPI_SWIGLU : EPI_GELU, p.s));
   }
   {
@@ -337,6 +395,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     ga.H = p.h; ga.ldh = g.D; ga.rm = rm; ga.e6 = p.e6; ga.mod = mod; ga.gate_idx = 5; ga.D = g.D;
     PostArgs none{};
     none.mode = POST_NONE;
+    if (g.mx) HIP_TRY(mx_operands(p, bw, ga, ffn, MX_FF2, 0));
     HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID_GATED, after ? *after : none, p.s));
   }
   return WAM_OK;
@@ -531,7 +590,7 @@ wam_status wam_dit_block_fwd(const wam_config* cfg, const wam_block_weights* bw,
   const Geo g = geo_of(*cfg);
   if (layer < 0 || layer >= g.L) return fail(WAM_E_ARG, "layer %d out of range", layer);
   if (n_chunks < 1 || n_chunks > kMaxChunks) return fail(WAM_E_SHAPE, "n_chunks must be in [1, %d]", kMaxChunks);
-  CHECK(check_block(bw, layer));
+  CHECK(check_block(bw, layer, g.mx));
   CHECK(check_cache(g, cache, n_chunks * g.Lq));
   CHECK(check_ctx(g, ctx));
   if (!h || !e6) return fail(WAM_E_ARG, "h or e6 is NULL");
@@ -821,6 +880,37 @@ wam_status wam_op_linear_mx(const void* A, const void* A_scales, int lda, const 
   ga.As = reinterpret_cast<const uint8_t*>(A_scales);
   ga.Ws = reinterpret_cast<const uint8_t*>(W_scales);
   HIP_TRY(launch_gemm_mx(ga, act == 2 ? EPI_SWIGLU : act ? EPI_GELU : EPI_STORE, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
+size_t wam_mx_block_bytes(const wam_config* cfg) {
+  if (check_cfg(cfg) != WAM_OK) return 0;
+  const Geo g = geo_of(*cfg);
+  if (g.dt != DT_BF16 || g.D % 128 || g.F % 128) return 0;
+  return mx_block_of(g).total;
+}
+
+wam_status wam_mx_pack_block(const wam_config* cfg, const wam_block_weights* bw, void* dst, size_t dst_bytes,
+                             void* stream) {
+  CHECK(check_cfg(cfg));
+  const Geo g = geo_of(*cfg);
+  if (g.dt != DT_BF16 || g.D % 128 || g.F % 128)
+    return fail(WAM_E_UNSUPPORTED, "MXFP8 packing needs dtype bf16 and dim, ffn_dim multiples of 128");
+  if (!bw) return fail(WAM_E_ARG, "block weights are NULL");
+  const MxBlock b = mx_block_of(g);
+  if (!dst || reinterpret_cast<uintptr_t>(dst) % 256) return fail(WAM_E_ARG, "dst must be a 256-byte aligned buffer");
+  if (dst_bytes < b.total) return fail(WAM_E_ARG, "dst holds %zu bytes, the packed layer needs %zu", dst_bytes, b.total);
+  const void* W[MX_MATS] = {bw->w_qkv, bw->w_o, bw->w_cq, bw->w_co, bw->w_ff1, bw->w_ff2};
+  const char* names[MX_MATS] = {"w_qkv", "w_o", "w_cq", "w_co", "w_ff1", "w_ff2"};
+  for (int i = 0; i < MX_MATS; ++i)
+    if (!W[i] || unaligned16(W[i])) return fail(WAM_E_ARG, "%s is NULL or not 16-byte aligned", names[i]);
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(dst);
+  for (int i = 0; i < MX_MATS; ++i) {
+    const MxMat& m = b.m[i];
+    HIP_TRY(launch_mx_quantize(W[i], m.K, DT_BF16, m.N, m.K, reinterpret_cast<uint8_t*>(base + m.codes), m.K,
+                               reinterpret_cast<uint8_t*>(base + m.scales), s));
+  }
   return WAM_OK;
 }
 

@@ -913,6 +913,7 @@ static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.As) return dt == DT_BF16 ? launch_gemm_mx(a, epi, s) : hipErrorInvalidValue;   // MXFP8 operands
   if (epi == EPI_SWIGLU && a.N % 2) return hipErrorInvalidValue;   // (gate, up) column pairs
   // buffer descriptors address each operand with 32-bit byte offsets
   const long esz = dt == DT_BF16 ? 2 : 4;
@@ -1068,6 +1069,10 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
   }
 }
 
+static int mx_splits(const GemmArgs& a);
+static bool mx_operands_ok(const GemmArgs& a);
+static void launch_g4mx_partial(const GemmArgs& a, int splits, hipStream_t s);
+
 hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs& post, hipStream_t s) {
   if (post.mode == POST_NONE || a.M <= 0 || a.N <= 0) return launch_gemm(a, dt, epi, s);
   bool fused = dt == DT_BF16 && a.N <= 256 * 4 * FIN_G;
@@ -1078,9 +1083,12 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
   else
     fused = fused && epi == EPI_STORE && post.qa.rope == nullptr && post.qa.D == a.N && post.qa.M == a.M &&
             post.qa.d % 4 == 0 && aligned16(post.qa.gain) && reinterpret_cast<uintptr_t>(post.qa.dst) % 8 == 0;
-  const int plan = fused ? g4_plan(a, epi) : 0;
+  const int plan = !fused ? 0 : a.As ? (mx_operands_ok(a) ? mx_splits(a) : 0) : g4_plan(a, epi);
   if (plan > 1) {
-    launch_g4<EPI_PARTIAL>(a, plan, s);
+    if (a.As)
+      launch_g4mx_partial(a, plan, s);
+    else
+      launch_g4<EPI_PARTIAL>(a, plan, s);
     const dim3 grid(a.M), block(256);
     const int groups = (a.N / 4 + 255) / 256;   // float4 groups per thread
 #define WAM_FINISH_G(E, P, S)                                                                              \
@@ -1181,13 +1189,36 @@ hipError_t launch_mx_quantize(const void* src, long ld_src, DType dt, int rows, 
   return hipGetLastError();
 }
 
+// Splits over K of the MXFP8 product: as the bf16 product, about 240 workgroups when there are fewer
+// than 128 tiles and a partial buffer, each split at least two 128-k tiles.
+static int mx_splits(const GemmArgs& a) {
+  const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int KT = a.K / 128;
+  int splits = 1;
+  if (tiles < 128 && a.part) {
+    splits = (int)((240 + tiles - 1) / tiles);
+    if (splits > 4) splits = 4;
+    while (splits > 1 && (KT < 2 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
+  }
+  return splits;
+}
+
+static bool mx_operands_ok(const GemmArgs& a) {
+  return a.K % 128 == 0 && a.N % 4 == 0 && a.As && a.Ws && (long)a.M * a.lda < (1L << 31) &&
+         (long)a.N * a.ldw < (1L << 31) && a.lda % 16 == 0 && a.ldw % 16 == 0 && aligned16(a.A) && aligned16(a.W) &&
+         reinterpret_cast<uintptr_t>(a.As) % 4 == 0 && reinterpret_cast<uintptr_t>(a.Ws) % 4 == 0;
+}
+
+static void launch_g4mx_partial(const GemmArgs& a, int splits, hipStream_t s) {
+  const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int units = (int)tiles * splits;
+  hipLaunchKernelGGL((gemm4mx_kernel<EPI_PARTIAL>), dim3(8 * ((units + 7) / 8)), dim3(256), 0, s, a, splits);
+}
+
 hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.K % 128 || a.N % 4 || !a.As || !a.Ws || epi == EPI_ROWSEL_F32) return hipErrorInvalidValue;
+  if (!mx_operands_ok(a) || epi == EPI_ROWSEL_F32) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU && a.N % 2) return hipErrorInvalidValue;
-  if ((long)a.M * a.lda >= (1L << 31) || (long)a.N * a.ldw >= (1L << 31) || a.lda % 16 || a.ldw % 16 ||
-      reinterpret_cast<uintptr_t>(a.A) % 16 || reinterpret_cast<uintptr_t>(a.W) % 16)
-    return hipErrorInvalidValue;
   const bool vec_ok = (!a.bias || aligned16(a.bias)) &&
                       (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_SWIGLU
                            ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
@@ -1195,20 +1226,13 @@ hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s) {
                       (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
   if (!vec_ok) return hipErrorInvalidValue;
   const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  const int KT = a.K / 128;
-  int splits = 1;
-  if (tiles < 128 && a.part) {   // as the bf16 product: about 240 workgroups, fp32 partials summed in order
-    splits = (int)((240 + tiles - 1) / tiles);
-    if (splits > 4) splits = 4;
-    while (splits > 1 && (KT < 2 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
-  }
-  const int units = (int)tiles * splits;
-  const dim3 grid(8 * ((units + 7) / 8)), block(256);
-  if (splits > 1) {
-    hipLaunchKernelGGL((gemm4mx_kernel<EPI_PARTIAL>), grid, block, 0, s, a, splits);
+  const int splits = mx_splits(a);
+  if (splits > 1) {   // fp32 partials summed in split order
+    launch_g4mx_partial(a, splits, s);
     launch_reduce(a, epi, splits, s);
     return hipGetLastError();
   }
+  const dim3 grid(8 * (((int)tiles + 7) / 8)), block(256);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((gemm4mx_kernel<EPI_STORE>), grid, block, 0, s, a, 1); break;
     case EPI_GELU: hipLaunchKernelGGL((gemm4mx_kernel<EPI_GELU>), grid, block, 0, s, a, 1); break;

@@ -14,8 +14,8 @@ import torch
 import synth
 from synth.workloads import Workload, draw, global_tensors, is_matrix, layer_tensors
 
-from . import (GLOBAL_FIELDS, WAM_BF16, WAM_F32, wam_block_weights, wam_config, wam_ctx_kv, wam_kv_cache,
-               wam_weights, wam_workspace_bytes)
+from . import (GLOBAL_FIELDS, WAM_BF16, WAM_F32, WAM_PRECISION_MXFP8, wam_block_weights, wam_config, wam_ctx_kv,
+               wam_kv_cache, wam_mx_block_bytes, wam_mx_pack_block, wam_weights, wam_workspace_bytes)
 
 
 def make_config(w: Workload, dtype: str = "bf16", branches: int | None = None) -> wam_config:
@@ -28,6 +28,7 @@ def make_config(w: Workload, dtype: str = "bf16", branches: int | None = None) -
     c.eps = float(w.eps)
     c.dtype = WAM_BF16 if dtype == "bf16" else WAM_F32
     c.variant = int(w.variant)
+    c.precision = int(w.precision)
     return c
 
 
@@ -86,6 +87,18 @@ class DeviceModel:
         for l, lp in enumerate(self.layers):
             for name, t in lp.items():
                 setattr(self.blocks[l], name, t.data_ptr())
+        self.mx = []
+        if self.cfg.precision == WAM_PRECISION_MXFP8:   # the library packs each layer's projections once
+            nbytes = wam_mx_block_bytes(self.cfg)
+            if nbytes == 0:
+                raise ValueError("configuration cannot take MXFP8 projections")
+            for l in range(self.w.layers):
+                buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+                off = (-buf.data_ptr()) % 256
+                arena = buf[off:off + nbytes]
+                wam_mx_pack_block(self.cfg, self.blocks[l], arena)
+                self.blocks[l].mx = arena.data_ptr()
+                self.mx.append(buf)
         self.weights = wam_weights()
         self.weights.blocks = ctypes.cast(self.blocks, ctypes.POINTER(wam_block_weights))
         for name in GLOBAL_FIELDS:
