@@ -246,6 +246,10 @@ NormArgs adaln_args(const Pass& p, const float* mod, int shift_idx, int scale_id
   na.X = p.h; na.Y = at<void>(p.ws, p.L.y); na.M = p.M; na.D = p.g.D; na.eps = p.cfg->eps; na.mode = NORM_ADALN;
   na.rm = rowmap(p); na.e6 = p.e6; na.mod = mod; na.shift_idx = shift_idx; na.scale_idx = scale_idx;
   na.rms = (p.cfg->variant & WAM_VARIANT_RMS_NORM) != 0;
+  if (p.g.mx) {   // the block norms feed MXFP8 projections: they also write the quantised rows
+    na.mxq = at<uint8_t>(p.ws, p.L.xq);
+    na.mxs = at<uint8_t>(p.ws, p.L.xs);
+  }
   return na;
 }
 
@@ -258,13 +262,15 @@ NormArgs head_norm_args(const Pass& p, const wam_weights* w) {
   return na;
 }
 
-// MXFP8 projections: quantise the product's input rows (bf16 [M][K]) into the workspace, then point
-// the product at them and at the layer's packed weights, matrix rows from row0 on.
+// MXFP8 projections: point the product at the quantised input rows in the workspace (quantising the
+// bf16 rows src [M][K] first unless the block norm that wrote them already did) and at the layer's
+// packed weights, matrix rows from row0 on.
 hipError_t mx_operands(const Pass& p, const wam_block_weights& bw, GemmArgs& ga, const void* src, int mat, int row0) {
   const MxMat mm = mx_block_of(p.g).m[mat];
   uint8_t* xq = at<uint8_t>(p.ws, p.L.xq);
   uint8_t* xs = at<uint8_t>(p.ws, p.L.xs);
-  const hipError_t e = launch_mx_quantize(src, mm.K, DT_BF16, p.M, mm.K, xq, mm.K, xs, p.s);
+  const bool from_norm = mat == MX_QKV || mat == MX_CQ || mat == MX_FF1;
+  const hipError_t e = from_norm ? hipSuccess : launch_mx_quantize(src, mm.K, DT_BF16, p.M, mm.K, xq, mm.K, xs, p.s);
   const char* base = reinterpret_cast<const char*>(bw.mx);
   ga.A = xq;
   ga.lda = mm.K;

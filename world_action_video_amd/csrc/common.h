@@ -32,6 +32,44 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// ---- MXFP8 (OCP microscaling: fp8 e4m3 codes, one e8m0 scale per 32 consecutive values of a row) ----
+// Shared exponent e = floor(log2(amax)) - 8 (8 = exponent of e4m3's largest power of two), clamped to
+// >= -127; codes = e4m3(x * 2^-e) saturated to +-448, nearest even; scale byte e + 127.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xff);   // 0 for zero and fp32 subnormals
+  return ebits == 0 ? -127 : max(ebits - 127 - 8, -127);
+}
+
+__device__ __forceinline__ float mx_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// four values (already multiplied by 2^-e) -> four e4m3 bytes, little-endian in one word
+__device__ __forceinline__ uint32_t mx_pack4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ float bf16_round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+
+// Columns 4q .. 4q+3 of a row, held by one lane; the 8 lanes of an aligned group hold one 32-column
+// block and share its scale (butterfly maximum). Every lane of the wave calls this (act = the lane
+// holds data); codes / scales point at the row.
+__device__ __forceinline__ void mx_store_quad(float4 o, bool act, uint8_t* codes, uint8_t* scales, int q) {
+  float amax = act ? fmaxf(fmaxf(fabsf(o.x), fabsf(o.y)), fmaxf(fabsf(o.z), fabsf(o.w))) : 0.f;
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  if (!act) return;
+  const int e = mx_block_exponent(amax);
+  const float inv = mx_inv_scale(e);
+  reinterpret_cast<uint32_t*>(codes)[q] = mx_pack4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if ((q & 7) == 0) scales[q >> 3] = (uint8_t)(e + 127);
+}
+
 // Generic element access for the two storage types.
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {

@@ -1036,6 +1036,24 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
 #pragma unroll
     for (int k = 0; k < G; ++k) {
       const int q = t + 256 * k;
+      if (na.mxq && 256 * k < nv) {   // MXFP8 copy of the stored (bf16-rounded) row; whole waves call it
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q < nv) {
+          o = make_float4((v[k].x - mean) * rstd, (v[k].y - mean) * rstd, (v[k].z - mean) * rstd, (v[k].w - mean) * rstd);
+          if (na.mode == NORM_AFFINE) {
+            const float4 w = reinterpret_cast<const float4*>(na.w)[q], b = reinterpret_cast<const float4*>(na.b)[q];
+            o = make_float4(o.x * w.x + b.x, o.y * w.y + b.y, o.z * w.z + b.z, o.w * w.w + b.w);
+          } else {
+            const float4 pa = sh[q], pb = sh2[q], ra = sc[q], rb2 = sc2[q];
+            o = make_float4(o.x * (1.f + (ra.x + rb2.x)) + (pa.x + pb.x), o.y * (1.f + (ra.y + rb2.y)) + (pa.y + pb.y),
+                            o.z * (1.f + (ra.z + rb2.z)) + (pa.z + pb.z), o.w * (1.f + (ra.w + rb2.w)) + (pa.w + pb.w));
+          }
+          reinterpret_cast<uint2*>(y)[q] = make_uint2(pack2_bf16(o.x, o.y), pack2_bf16(o.z, o.w));
+          o = make_float4(bf16_round(o.x), bf16_round(o.y), bf16_round(o.z), bf16_round(o.w));
+        }
+        mx_store_quad(o, q < nv, na.mxq + (long)m * na.D, na.mxs + (long)m * (na.D / 32), q);
+        continue;
+      }
       if (q >= nv) continue;
       float4 o = make_float4((v[k].x - mean) * rstd, (v[k].y - mean) * rstd, (v[k].z - mean) * rstd, (v[k].w - mean) * rstd);
       if (na.mode == NORM_AFFINE) {
@@ -1122,54 +1140,52 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
 // MXFP8 quantisation (OCP microscaling, 32-element blocks along a row): shared exponent
 // e = floor(log2(amax)) - 8 (8 = exponent of e4m3's largest power of two), clamped to >= -127; the
 // codes are e4m3 of x * 2^-e (exact scaling) saturated to +-448 and rounded to nearest even by the
-// conversion instruction; the scale byte is e + 127. One thread per block.
+// conversion instruction; the scale byte is e + 127. LPB lanes share a block, each with 16 bytes of
+// it (8 bf16 or 4 float values), so a wave's loads and stores cover contiguous bytes; the block
+// maximum is a butterfly over the LPB lanes.
 template <typename T>
 __global__ void __launch_bounds__(256) mx_quantize_kernel(const T* src, long ld, int rows, int cols, uint8_t* codes,
                                                           long ldq, uint8_t* scales) {
-  const long blk = (long)blockIdx.x * 256 + threadIdx.x;
+  constexpr int LPB = sizeof(T) == 2 ? 4 : 8, VALS = 32 / LPB;
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long blk = gid / LPB;
+  const int part = (int)(gid % LPB);
   const int nb = cols / 32;
-  if (blk >= (long)rows * nb) return;
-  const int r = (int)(blk / nb), b = (int)(blk % nb);
-  const T* x = src + (long)r * ld + b * 32;
-  float v[32];
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint4 w = reinterpret_cast<const uint4*>(x)[u];
+  const bool live = blk < (long)rows * nb;   // whole groups of LPB lanes agree (LPB divides 256)
+  const int r = live ? (int)(blk / nb) : 0, b = live ? (int)(blk % nb) : 0;
+  float v[VALS];
+  if (live) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src + (long)r * ld + b * 32 + part * VALS);
+    if constexpr (sizeof(T) == 2) {
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        v[8 * u + 2 * k] = __uint_as_float(ww[k] << 16);
-        v[8 * u + 2 * k + 1] = __uint_as_float(ww[k] & 0xffff0000u);
+        v[2 * k] = __uint_as_float(ww[k] << 16);
+        v[2 * k + 1] = __uint_as_float(ww[k] & 0xffff0000u);
       }
+    } else {
+      v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y); v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float4 w = reinterpret_cast<const float4*>(x)[u];
-      v[4 * u] = w.x; v[4 * u + 1] = w.y; v[4 * u + 2] = w.z; v[4 * u + 3] = w.w;
-    }
+    for (int i = 0; i < VALS; ++i) v[i] = 0.f;
   }
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xff);   // 0 for zero and fp32 subnormals
-  const int e = ebits == 0 ? -127 : max(ebits - 127 - 8, -127);
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, e in [-127, 119]
-  uint32_t w[8];
+  for (int i = 0; i < VALS; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    float q[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) q[t] = fminf(fmaxf(v[4 * k + t] * inv, -448.f), 448.f);
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
-    w[k] = (uint32_t)lo;
+  for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (!live) return;
+  const int e = mx_block_exponent(amax);
+  const float inv = mx_inv_scale(e);
+  uint8_t* out = codes + (long)r * ldq + b * 32 + part * VALS;
+  if constexpr (VALS == 8) {
+    *reinterpret_cast<uint2*>(out) = make_uint2(mx_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
+                                                mx_pack4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv));
+  } else {
+    *reinterpret_cast<uint32_t*>(out) = mx_pack4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
   }
-  uint4* out = reinterpret_cast<uint4*>(codes + (long)r * ldq + b * 32);
-  out[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  out[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  scales[(long)r * nb + b] = (uint8_t)(e + 127);
+  if (part == 0) scales[(long)r * nb + b] = (uint8_t)(e + 127);
 }
 
 hipError_t launch_mx_quantize(const void* src, long ld_src, DType dt, int rows, int cols, uint8_t* codes, long ldq,
@@ -1178,8 +1194,8 @@ hipError_t launch_mx_quantize(const void* src, long ld_src, DType dt, int rows, 
   if (cols % 32 || ldq % 16 || reinterpret_cast<uintptr_t>(codes) % 16 || reinterpret_cast<uintptr_t>(src) % 16 ||
       ld_src % (dt == DT_BF16 ? 8 : 4))
     return hipErrorInvalidValue;
-  const long blocks = (long)rows * (cols / 32);
-  const dim3 grid((unsigned)((blocks + 255) / 256)), block(256);
+  const long lanes = (long)rows * (cols / 32) * (dt == DT_BF16 ? 4 : 8);
+  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
   if (dt == DT_BF16)
     hipLaunchKernelGGL((mx_quantize_kernel<bf16_t>), grid, block, 0, s, reinterpret_cast<const bf16_t*>(src), ld_src,
                        rows, cols, codes, ldq, scales);

@@ -110,6 +110,8 @@ struct NormArgs {
   const float* w;       // AFFINE
   const float* b;
   int rms;              // RMSNorm (no mean subtraction) in place of LayerNorm
+  uint8_t* mxq;         // bf16 only, optional: MXFP8 copy of Y, codes [M][D] and scales [M][D/32]
+  uint8_t* mxs;         //   (D % 32 == 0), quantised from the stored bf16 values
 };
 hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s);
 

@@ -60,6 +60,27 @@ __global__ void __launch_bounds__(256) norm_kernel(NormArgs a) {
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     const int i = lane + 64 * k;
+    if constexpr (sizeof(T) == 2) {
+      if (a.mxq && 64 * k < nv) {   // MXFP8 copy of the stored (bf16-rounded) row; the whole wave calls it
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < nv) {
+          v = make_float4((xv[k].x - mean) * rstd, (xv[k].y - mean) * rstd, (xv[k].z - mean) * rstd,
+                          (xv[k].w - mean) * rstd);
+          if (a.mode == NORM_AFFINE) {
+            const float4 w = reinterpret_cast<const float4*>(a.w)[i], b = reinterpret_cast<const float4*>(a.b)[i];
+            v = make_float4(v.x * w.x + b.x, v.y * w.y + b.y, v.z * w.z + b.z, v.w * w.w + b.w);
+          } else {
+            const float4 p = sh4[i], q = sh24[i], r = sc4[i], t = sc24[i];
+            v = make_float4(v.x * (1.f + (r.x + t.x)) + (p.x + q.x), v.y * (1.f + (r.y + t.y)) + (p.y + q.y),
+                            v.z * (1.f + (r.z + t.z)) + (p.z + q.z), v.w * (1.f + (r.w + t.w)) + (p.w + q.w));
+          }
+          reinterpret_cast<uint2*>(y)[i] = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+          v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
+        }
+        mx_store_quad(v, i < nv, a.mxq + (long)row * a.D, a.mxs + (long)row * (a.D / 32), i);
+        continue;
+      }
+    }
     if (i >= nv) continue;
     float4 v = make_float4((xv[k].x - mean) * rstd, (xv[k].y - mean) * rstd, (xv[k].z - mean) * rstd,
                            (xv[k].w - mean) * rstd);
