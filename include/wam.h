@@ -103,6 +103,14 @@ typedef struct {
                                   wam_mx_block_bytes(cfg) bytes written by wam_mx_pack_block, 256-aligned */
 } wam_block_weights;
 
+/* Action encoder and decoder of one embodiment ([ARCH] §2.4: each robot body has its own linear from
+ * its action space to the width and back, the shared DiT in between, routed by the embodiment id).
+ * Shapes as ae_* / ao_* of wam_weights: every embodiment's actions are padded to cfg->action_dim. */
+typedef struct {
+  const void *ae_w, *ae_b;   /* [D][action_dim], [D] */
+  const void *ao_w, *ao_b;   /* [action_dim][D], [action_dim] */
+} wam_action_io;
+
 typedef struct {
   const wam_block_weights *blocks;           /* host array [layers] */
   const void *t_w1, *t_b1, *t_w2, *t_b2;     /* time MLP: [D][freq_dim], [D]; [D][D], [D] */
@@ -114,7 +122,15 @@ typedef struct {
   const void *ao_w, *ao_b;                   /* action head [action_dim][D], [action_dim] */
   const void *txt_w, *txt_b;                 /* text features -> width [D][ctx_in_dim], [D] */
   const void *img_w, *img_b;                 /* image features -> width (NULL when ctx_img_len = 0) */
+  const wam_action_io *embodiments;          /* optional host array [n_embodiments] (see below) */
+  int n_embodiments;
 } wam_weights;
+
+/* Routing by embodiment id ([ARCH] §2.4): *out = *w with ae_* / ao_* taken from w->embodiments[id].
+ * Every call then runs that embodiment's action encoder and decoder (one request, both CFG branches,
+ * is one embodiment). Host only, nothing launched; out may alias w. Errors: WAM_E_ARG (id outside
+ * [0, n_embodiments), NULL table or matrices). */
+wam_status wam_weights_for_embodiment(const wam_weights *w, int id, wam_weights *out);
 
 /* Self-attention KV cache of clean chunks ([WS1] architecture: the DiT runner keeps the KV;
  * [HYPER] 方法: executed chunks are replaced by real observations). Keys after RMSNorm and RoPE.

@@ -419,6 +419,18 @@ def per_token_time(w, g: Dict[str, Array], t_video: Sequence[float], t_action: S
     return e6, e
 
 
+def embodiment_params(g: Dict[str, Array], e: int) -> Dict[str, Array]:
+    """Global parameters routed to embodiment e ([ARCH] §2.4: each robot body has its own action
+    encoder and decoder linear around the shared DiT, chosen by the embodiment id): ae_* / ao_* are
+    replaced by that embodiment's (embodiment 0 keeps the defaults); everything else is shared."""
+    if e == 0:
+        return g
+    out = dict(g)
+    for name in ("ae_w", "ae_b", "ao_w", "ao_b"):
+        out[name] = g["%s_%d" % (name, e)]
+    return out
+
+
 def head_forward(w, g: Dict[str, Array], h: Array, e: Array, n_chunks: int) -> Tuple[Array, Array]:
     """Output split ([ARCH] §2.3 output decoding, §2.4 per-embodiment decoder):
     n = LN(h)(1 + scale_h) + shift_h with (shift_h, scale_h) = head_mod + e;

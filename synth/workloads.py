@@ -44,6 +44,7 @@ class Workload:
     guidance: float = 5.0
     variant: int = 0        # architectural variants of the pages (bit flags, see VARIANT_* below)
     precision: int = 0      # arithmetic of the block projections: 0 the model dtype, PRECISION_MXFP8
+    embodiments: int = 1    # action encoder / decoder pairs; embodiment 0 is ae_* / ao_*, e >= 1 ae_*_e / ao_*_e
 
     @property
     def video_tokens(self) -> int:
@@ -106,6 +107,9 @@ def global_tensors(w: Workload):
     ]
     if w.ctx_img_len > 0:
         out += [("img_w", (D, C), "normal", 0.02), ("img_b", (D,), "normal", 0.02)]
+    for e in range(1, w.embodiments):
+        out += [("ae_w_%d" % e, (D, A), "normal", 0.02), ("ae_b_%d" % e, (D,), "normal", 0.02),
+                ("ao_w_%d" % e, (A, D), "normal", 0.02), ("ao_b_%d" % e, (A,), "normal", 0.02)]
     return out
 
 
@@ -153,7 +157,7 @@ MATRIX_NAMES = frozenset({
 def is_matrix(name: str) -> bool:
     """Linear weights ([out, in]) are the tensors a bf16 path stores in bf16; every other tensor
     (biases, gains, LayerNorm affine vectors, modulation tables) stays float32."""
-    return name in MATRIX_NAMES
+    return name in MATRIX_NAMES or name.rsplit("_", 1)[0] in ("ae_w", "ao_w")
 
 
 def draw(w: Workload, layer: int, spec, fmt: str = "f32"):

@@ -141,6 +141,32 @@ def test_mx_validation():
     assert lib.wam_op_linear_mx(*args(act=3)) == wam.WAM_E_ARG
 
 
+def test_embodiment_routing_is_host_only():
+    """wam_weights_for_embodiment swaps the action encoder / decoder pointers and nothing else."""
+    _lib()
+    w = wam.wam_weights()
+    for i, name in enumerate(wam.GLOBAL_FIELDS):
+        setattr(w, name, 0x1000 + 0x100 * i)
+    table = (wam.wam_action_io * 2)()
+    for e in range(2):
+        for j, name in enumerate(("ae_w", "ae_b", "ao_w", "ao_b")):
+            setattr(table[e], name, 0x900000 + 0x1000 * e + 0x10 * j)
+    w.embodiments = ctypes.cast(table, ctypes.POINTER(wam.wam_action_io))
+    w.n_embodiments = 2
+    r = wam.wam_weights_for_embodiment(w, 1)
+    for name in wam.GLOBAL_FIELDS:
+        want = getattr(table[1], name) if name in ("ae_w", "ae_b", "ao_w", "ao_b") else getattr(w, name)
+        assert getattr(r, name) == want, name
+    assert r.n_embodiments == 2
+    with pytest.raises(wam.WamError, match="embodiment 2"):
+        wam.wam_weights_for_embodiment(w, 2)
+    with pytest.raises(wam.WamError):
+        wam.wam_weights_for_embodiment(w, -1)
+    w.n_embodiments = 0
+    with pytest.raises(wam.WamError):
+        wam.wam_weights_for_embodiment(w, 0)
+
+
 def test_kv_reset_is_host_only():
     _lib()
     kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 512, 464)

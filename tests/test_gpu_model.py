@@ -215,6 +215,38 @@ def test_mxfp8_stack_matches_oracle(gpu, tiny_oracle, variant):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_embodiment_routing(gpu, tiny_oracle, dtype):
+    """Three embodiments in one model: each request routed by id runs that embodiment's action encoder
+    and decoder (append and step), against the oracle with the same routing; the default weights
+    stay embodiment 0's."""
+    w0, m0, ckv = tiny_oracle
+    w = w0.with_(embodiments=3)
+    m = O.load_model(w)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    rig = Rig(w, dtype, gpu)
+    outs = []
+    for e in (2, 0, 1):
+        me = O.Model(w, O.embodiment_params(m.g, e), m.layers)
+        cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+        O.kv_append(me, cache, ckv, x1v[0], x1a[0], 0)
+        ref_v, ref_a = O.stack_forward(me, cache, ckv, epv[1], epa[1], [0.4], [0.4], 1, w.frames_per_chunk)
+        rig.m.weights_routed = rig.m.for_embodiment(e)
+        default = rig.m.weights
+        rig.m.weights = rig.m.weights_routed
+        try:
+            dc = rig.cache()
+            rig.append(dc, x1v[0], x1a[0], 0)
+            gv, ga = rig.step(dc, 1, epv[1], epa[1], [0.4], [0.4], w.frames_per_chunk)
+        finally:
+            rig.m.weights = default
+        ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+        print("embodiment %d: rel-L2 video %.3e action %.3e" % (e, ev, ea), flush=True)
+        assert ev <= TOL[dtype] and ea <= TOL[dtype]
+        outs.append(ga)
+    assert not np.allclose(outs[0], outs[1]) and not np.allclose(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decoupled_timesteps_and_frames(gpu, tiny_oracle, dtype):
     """Different video/action timesteps and a non-zero window offset, two cached chunks."""
     w, m, ckv = tiny_oracle

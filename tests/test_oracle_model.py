@@ -285,3 +285,35 @@ def test_frame_causal_incremental_equals_full_sequence(tiny):
     iv, ia = O.stack_forward(mf, cache, ckv, epv[1], epa[1], [0.3], [0.6], 1, Fc)
     fv, fa = _full(wf, mf, ckv, [x1v[0], epv[1]], [x1a[0], epa[1]], [1, 0.3], [1, 0.6])
     assert np.abs(fv[:, Lv:] - iv).max() <= 1e-5 and np.abs(fa[:, La:] - ia).max() <= 1e-5
+
+
+def _embodiment_step(w, g, layers, ckv, x1v, x1a, epv, epa, e):
+    me = O.Model(w, O.embodiment_params(g, e), layers)
+    cache = O.KVCache.empty(len(layers), w.branches, w.dim)
+    O.kv_append(me, cache, ckv, x1v[0], x1a[0], 0)
+    return O.stack_forward(me, cache, ckv, epv[1], epa[1], [0.4], [0.4], 1, w.frames_per_chunk)
+
+
+def test_embodiment_routing_encoder_and_decoder(tiny):
+    """Architecture page §2.4: per-embodiment action encoder / decoder around a shared DiT. Embodiment
+    0 is the default weights; a decoder-only difference leaves the video output bit-identical (the
+    decoder runs after the DiT) and changes the action output; an encoder difference reaches the
+    video rows through attention."""
+    w, m, _, ckv, x1v, x1a, epv, epa = tiny
+    assert O.embodiment_params(m.g, 0) is m.g
+    rng = np.random.default_rng(11)
+    g = dict(m.g)
+    A, D = w.action_dim, w.dim
+    # embodiment 1: own decoder, shared encoder; embodiment 2: own encoder, shared decoder
+    g["ae_w_1"], g["ae_b_1"] = m.g["ae_w"], m.g["ae_b"]
+    g["ao_w_1"] = (rng.standard_normal((A, D)) * 0.02).astype(np.float32)
+    g["ao_b_1"] = (rng.standard_normal(A) * 0.02).astype(np.float32)
+    g["ae_w_2"] = (rng.standard_normal((D, A)) * 0.02).astype(np.float32)
+    g["ae_b_2"] = (rng.standard_normal(D) * 0.02).astype(np.float32)
+    g["ao_w_2"], g["ao_b_2"] = m.g["ao_w"], m.g["ao_b"]
+    v0, a0 = _embodiment_step(w, g, m.layers, ckv, x1v, x1a, epv, epa, 0)
+    v1, a1 = _embodiment_step(w, g, m.layers, ckv, x1v, x1a, epv, epa, 1)
+    v2, a2 = _embodiment_step(w, g, m.layers, ckv, x1v, x1a, epv, epa, 2)
+    assert np.array_equal(v0, v1)
+    assert not np.allclose(a0, a1)
+    assert not np.array_equal(v0, v2) and not np.allclose(a0, a2)

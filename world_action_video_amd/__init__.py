@@ -18,8 +18,9 @@ WAM_BF16, WAM_F32 = 0, 1
 WAM_PRECISION_NATIVE, WAM_PRECISION_MXFP8 = 0, 1
 
 EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
-           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear", "wam_mx_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block", "wam_op_attention", "wam_kv_evict", "wam_kv_reset",
-           "wam_last_error")
+           "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear",
+           "wam_mx_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
+           "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error")
 
 
 class WamError(RuntimeError):
@@ -47,8 +48,13 @@ class wam_block_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_FIELDS] + [("mx", ctypes.c_void_p)]
 
 
+class wam_action_io(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("ae_w", "ae_b", "ao_w", "ao_b")]
+
+
 class wam_weights(ctypes.Structure):
-    _fields_ = [("blocks", ctypes.POINTER(wam_block_weights))] + [(n, ctypes.c_void_p) for n in GLOBAL_FIELDS]
+    _fields_ = [("blocks", ctypes.POINTER(wam_block_weights))] + [(n, ctypes.c_void_p) for n in GLOBAL_FIELDS] + \
+               [("embodiments", ctypes.POINTER(wam_action_io)), ("n_embodiments", ctypes.c_int)]
 
 
 class wam_kv_cache(ctypes.Structure):
@@ -91,6 +97,7 @@ def load(path: str = LIB_PATH):
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_mx_quantize": (I, [I, P, I, I, I, P, I, P, P]),
         "wam_mx_block_bytes": (S, [CFG]),
+        "wam_weights_for_embodiment": (I, [ctypes.POINTER(wam_weights), I, ctypes.POINTER(wam_weights)]),
         "wam_mx_pack_block": (I, [CFG, ctypes.POINTER(wam_block_weights), P, S, P]),
         "wam_op_linear_mx": (I, [P, P, I, P, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P, S, P]),
@@ -220,6 +227,12 @@ def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, ws=None, 
 
 def wam_mx_quantize(dtype, src, ld, rows, cols, codes, ldq, scales, stream=None):
     _check(load().wam_mx_quantize(dtype, _ptr(src), ld, rows, cols, _ptr(codes), ldq, _ptr(scales), _stream(stream)))
+
+
+def wam_weights_for_embodiment(w: wam_weights, id: int) -> wam_weights:
+    out = wam_weights()
+    _check(load().wam_weights_for_embodiment(ctypes.byref(w), id, ctypes.byref(out)))
+    return out
 
 
 def wam_mx_block_bytes(cfg: wam_config) -> int:

@@ -889,6 +889,21 @@ wam_status wam_op_linear_mx(const void* A, const void* A_scales, int lda, const 
   return WAM_OK;
 }
 
+wam_status wam_weights_for_embodiment(const wam_weights* w, int id, wam_weights* out) {
+  if (!w || !out) return fail(WAM_E_ARG, "weights or out is NULL");
+  if (!w->embodiments || id < 0 || id >= w->n_embodiments)
+    return fail(WAM_E_ARG, "embodiment %d outside the table of %d", id, w->embodiments ? w->n_embodiments : 0);
+  const wam_action_io& e = w->embodiments[id];
+  if (!e.ae_w || !e.ae_b || !e.ao_w || !e.ao_b) return fail(WAM_E_ARG, "embodiment %d: action matrices are NULL", id);
+  wam_weights r = *w;
+  r.ae_w = e.ae_w;
+  r.ae_b = e.ae_b;
+  r.ao_w = e.ao_w;
+  r.ao_b = e.ao_b;
+  *out = r;
+  return WAM_OK;
+}
+
 size_t wam_mx_block_bytes(const wam_config* cfg) {
   if (check_cfg(cfg) != WAM_OK) return 0;
   const Geo g = geo_of(*cfg);

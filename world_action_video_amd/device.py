@@ -14,8 +14,9 @@ import torch
 import synth
 from synth.workloads import Workload, draw, global_tensors, is_matrix, layer_tensors
 
-from . import (GLOBAL_FIELDS, WAM_BF16, WAM_F32, WAM_PRECISION_MXFP8, wam_block_weights, wam_config, wam_ctx_kv,
-               wam_kv_cache, wam_mx_block_bytes, wam_mx_pack_block, wam_weights, wam_workspace_bytes)
+from . import (GLOBAL_FIELDS, WAM_BF16, WAM_F32, WAM_PRECISION_MXFP8, wam_action_io, wam_block_weights, wam_config,
+               wam_ctx_kv, wam_kv_cache, wam_mx_block_bytes, wam_mx_pack_block, wam_weights, wam_weights_for_embodiment,
+               wam_workspace_bytes)
 
 
 def make_config(w: Workload, dtype: str = "bf16", branches: int | None = None) -> wam_config:
@@ -104,6 +105,18 @@ class DeviceModel:
         for name in GLOBAL_FIELDS:
             t = self.g.get(name)
             setattr(self.weights, name, t.data_ptr() if t is not None else None)
+        E = self.w.embodiments
+        self.embodiments = (wam_action_io * E)()
+        for e in range(E):
+            suffix = "" if e == 0 else "_%d" % e
+            for name in ("ae_w", "ae_b", "ao_w", "ao_b"):
+                setattr(self.embodiments[e], name, self.g[name + suffix].data_ptr())
+        self.weights.embodiments = ctypes.cast(self.embodiments, ctypes.POINTER(wam_action_io))
+        self.weights.n_embodiments = E
+
+    def for_embodiment(self, e: int) -> wam_weights:
+        """The weights routed to embodiment e (its action encoder and decoder), as the library builds them."""
+        return wam_weights_for_embodiment(self.weights, e)
 
 
 class DeviceCache:
