@@ -81,8 +81,13 @@ enum { WAM_PRECISION_NATIVE = 0, WAM_PRECISION_MXFP8 = 1 };
  * RMS_NORM: the block norms (both modulated norms and the affine norm before cross-attention) and
  *   the output-head norm divide by the root mean square without subtracting the mean.
  * SWIGLU: the feed-forward is (SiLU(y W_g^T + b_g) * (y W_u^T + b_u)) W_2^T + b_2 with w_ff1 [2F][D]
- *   and b_ff1 [2F] holding the gate and up rows interleaved (row 2j gate j, row 2j+1 up j). */
-enum { WAM_VARIANT_FRAME_CAUSAL = 1, WAM_VARIANT_RMS_NORM = 2, WAM_VARIANT_SWIGLU = 4 };
+ *   and b_ff1 [2F] holding the gate and up rows interleaved (row 2j gate j, row 2j+1 up j).
+ * IMG_XATTN: the image part of the condition sequence gets its own key / value projections
+ *   (w_cki, b_cki, g_cki, w_cvi, b_cvi of the block) and its own softmax: the cross-attention output
+ *   is attn(q, K_txt, V_txt) + attn(q, K_img, V_img) before W_co (the backbone's image-to-video
+ *   layout). Needs ctx_img_len > 0, ctx_text_len a multiple of 8, and ctx_stride of the condition
+ *   KV >= ctx_text_len + ctx_img_len rounded up to 32. */
+enum { WAM_VARIANT_FRAME_CAUSAL = 1, WAM_VARIANT_RMS_NORM = 2, WAM_VARIANT_SWIGLU = 4, WAM_VARIANT_IMG_XATTN = 8 };
 
 /* One block's parameters ([ARCH] §2.3 single causal block). Matrices [out][in] in dtype;
  * everything else float. mod: [6][D] per-layer offset added to the shared time modulation
@@ -101,6 +106,8 @@ typedef struct {
   const void *w_ff2, *b_ff2;   /* [D][F], [D] */
   const void *mx;              /* MXFP8 precision only (else ignored): this layer's packed projections,
                                   wam_mx_block_bytes(cfg) bytes written by wam_mx_pack_block, 256-aligned */
+  const void *w_cki, *b_cki, *g_cki;   /* IMG_XATTN only (else ignored): image keys [D][D], [D], RMSNorm gain [D] */
+  const void *w_cvi, *b_cvi;           /* IMG_XATTN only: image values [D][D], [D] */
 } wam_block_weights;
 
 /* Action encoder and decoder of one embodiment ([ARCH] §2.4: each robot body has its own linear from

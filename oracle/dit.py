@@ -262,7 +262,21 @@ def context_kv(w, lp: Dict[str, Array], ctx: Array) -> Tuple[Array, Array]:
     """
     kc = rms_norm(linear(ctx, lp["w_ck"], lp["b_ck"]), w.eps, lp["g_ck"])
     vc = linear(ctx, lp["w_cv"], lp["b_cv"])
+    if separate_image_attention(w):
+        # image rows (after the text rows) through their own key / value projections and gain
+        Lt = w.ctx_text_len
+        kc = kc.copy()
+        vc = vc.copy()
+        kc[..., Lt:, :] = rms_norm(linear(ctx[..., Lt:, :], lp["w_cki"], lp["b_cki"]), w.eps, lp["g_cki"])
+        vc[..., Lt:, :] = linear(ctx[..., Lt:, :], lp["w_cvi"], lp["b_cvi"])
     return kc, vc
+
+
+def separate_image_attention(w) -> bool:
+    """Variant drawn for the image-to-video backbone the architecture page builds on: the image part
+    of the condition sequence has its own key / value projections and its own softmax, and the two
+    attention outputs are summed before the output projection (bit 8 of ``variant``)."""
+    return bool(getattr(w, "variant", 0) & 8)
 
 
 def embed_tokens(g: Dict[str, Array], x_video: Array, x_action: Array, w, n_chunks: int) -> Array:
@@ -395,7 +409,13 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
         qc = rms_norm(project(w, n3, lp["w_cq"], lp["b_cq"]), w.eps, lp["g_cq"]).reshape(T, H, d)
         kc = ctx_k[b].reshape(-1, H, d).transpose(1, 0, 2)
         vc = ctx_v[b].reshape(-1, H, d).transpose(1, 0, 2)
-        oc = attention(qc.transpose(1, 0, 2), kc, vc, None).transpose(1, 0, 2).reshape(T, D)
+        if separate_image_attention(w):
+            Lt = w.ctx_text_len
+            oc = (attention(qc.transpose(1, 0, 2), kc[:, :Lt], vc[:, :Lt], None)
+                  + attention(qc.transpose(1, 0, 2), kc[:, Lt:], vc[:, Lt:], None))
+            oc = oc.transpose(1, 0, 2).reshape(T, D)
+        else:
+            oc = attention(qc.transpose(1, 0, 2), kc, vc, None).transpose(1, 0, 2).reshape(T, D)
         oc_all[b] = oc
     h = h + project(w, oc_all, lp["w_co"], lp["b_co"])
     # --- feed-forward sub-layer

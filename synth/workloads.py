@@ -66,6 +66,7 @@ class Workload:
 VARIANT_FRAME_CAUSAL = 1   # inside a chunk a frame sees earlier and its own frames; actions see the chunk
 VARIANT_RMS_NORM = 2       # RMSNorm in place of the block and head LayerNorms
 VARIANT_SWIGLU = 4         # SwiGLU feed-forward: SiLU(gate) * up with interleaved [gate, up] rows
+VARIANT_IMG_XATTN = 8      # image condition tokens: own key / value projections and their own softmax
 
 # Low-precision block projections: inputs and weights quantised to MXFP8 (fp8 e4m3 codes with one
 # power-of-two scale per 32 consecutive input features)
@@ -130,7 +131,8 @@ def layer_tensors(w: Workload):
         n("w_co", (D, D)), n("b_co", (D,)),
         n("w_ff1", (F1, D)), n("b_ff1", (F1,)),
         n("w_ff2", (D, F)), n("b_ff2", (D,)),
-    ]
+    ] + ([n("w_cki", (D, D)), n("b_cki", (D,)), c("g_cki", (D,), 1.0), n("w_cvi", (D, D)), n("b_cvi", (D,))]
+         if w.variant & VARIANT_IMG_XATTN else [])
 
 
 def input_tensors(w: Workload, n_chunks: int):
@@ -150,7 +152,7 @@ def input_tensors(w: Workload, n_chunks: int):
 
 MATRIX_NAMES = frozenset({
     "t_w1", "t_w2", "t_wp", "pe_w", "ae_w", "txt_w", "img_w", "vo_w", "ao_w",
-    "w_qkv", "w_o", "w_cq", "w_ck", "w_cv", "w_co", "w_ff1", "w_ff2",
+    "w_qkv", "w_o", "w_cq", "w_ck", "w_cv", "w_co", "w_ff1", "w_ff2", "w_cki", "w_cvi",
 })
 
 

@@ -141,6 +141,19 @@ def test_mx_validation():
     assert lib.wam_op_linear_mx(*args(act=3)) == wam.WAM_E_ARG
 
 
+def test_image_cross_attention_validation():
+    """The separate image cross-attention variant needs image tokens, the image projections and a
+    condition value stride that holds the image key tiles (checked before anything runs)."""
+    lib = _lib()
+    from world_action_video_amd.device import make_config
+    w = WORKLOADS[1].with_(ctx_img_len=0, variant=8)
+    c = make_config(w, "f32")
+    assert lib.wam_workspace_bytes(ctypes.byref(c), 1) == 0
+    assert "image" in wam.wam_last_error()
+    c = make_config(WORKLOADS[1].with_(ctx_img_len=16, variant=8), "f32")
+    assert lib.wam_workspace_bytes(ctypes.byref(c), 1) > 0
+
+
 def test_embodiment_routing_is_host_only():
     """wam_weights_for_embodiment swaps the action encoder / decoder pointers and nothing else."""
     _lib()

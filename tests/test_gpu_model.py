@@ -215,6 +215,30 @@ def test_mxfp8_stack_matches_oracle(gpu, tiny_oracle, variant):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", [synth.workloads.VARIANT_IMG_XATTN,
+                                     synth.workloads.VARIANT_IMG_XATTN | synth.workloads.VARIANT_FRAME_CAUSAL])
+def test_separate_image_attention(gpu, dtype, variant):
+    """Image condition tokens with their own key / value projections and softmax (16 image tokens after
+    32 text tokens): condition build, one cached chunk and a step, against the oracle."""
+    w = WORKLOADS[1].with_(layers=2, ctx_img_len=16, variant=variant)
+    m = O.load_model(w)
+    ctx = O.build_context(w, m.g, draw_named(w, -1, "txt"), draw_named(w, -1, "img"))
+    ckv = [O.context_kv(w, lp, ctx) for lp in m.layers]
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.3], [0.6], 1, w.frames_per_chunk)
+    print("image cross-attention", variant, dtype, flush=True)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    gv, ga = rig.step(dc, 1, epv[1], epa[1], [0.3], [0.6], w.frames_per_chunk)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_embodiment_routing(gpu, tiny_oracle, dtype):
     """Three embodiments in one model: each request routed by id runs that embodiment's action encoder
     and decoder (append and step), against the oracle with the same routing; the default weights

@@ -317,3 +317,42 @@ def test_embodiment_routing_encoder_and_decoder(tiny):
     assert np.array_equal(v0, v1)
     assert not np.allclose(a0, a1)
     assert not np.array_equal(v0, v2) and not np.allclose(a0, a2)
+
+
+def _img_setup(variant):
+    w = WORKLOADS[1].with_(layers=2, ctx_img_len=16, variant=variant)
+    m = O.load_model(w)
+    txt = draw_named(w, -1, "txt")
+    img = draw_named(w, -1, "img")
+    return w, m, txt, img
+
+
+def _step_with_ctx(w, m, ctx, x1v, x1a, epv, epa):
+    ckv = [O.context_kv(w, lp, ctx) for lp in m.layers]
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    return O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.4], [0.4], 1, w.frames_per_chunk)
+
+
+def test_separate_image_attention_pins(tiny):
+    """Image cross-attention variant (own image key / value projections, own softmax, outputs summed):
+    with the image value projection zero the image branch adds exactly nothing, so the step equals the
+    text-only model bit for bit; the image tokens form a set (permuting them changes nothing beyond
+    rounding); and the variant differs from one softmax over the concatenated sequence."""
+    _, _, _, _, x1v, x1a, epv, epa = tiny
+    w, m, txt, img = _img_setup(8)
+    layers0 = [dict(lp, w_cvi=np.zeros_like(lp["w_cvi"]), b_cvi=np.zeros_like(lp["b_cvi"])) for lp in m.layers]
+    m0 = O.Model(w, m.g, layers0)
+    v_zero, a_zero = _step_with_ctx(w, m0, O.build_context(w, m.g, txt, img), x1v, x1a, epv, epa)
+    wt = w.with_(ctx_img_len=0, variant=0)
+    mt = O.Model(wt, m.g, m.layers)
+    v_txt, a_txt = _step_with_ctx(wt, mt, O.build_context(wt, m.g, txt, None), x1v, x1a, epv, epa)
+    assert np.array_equal(v_zero, v_txt) and np.array_equal(a_zero, a_txt)
+    v1, a1 = _step_with_ctx(w, m, O.build_context(w, m.g, txt, img), x1v, x1a, epv, epa)
+    perm = np.random.default_rng(2).permutation(img.shape[0])
+    v2, a2 = _step_with_ctx(w, m, O.build_context(w, m.g, txt, img[perm]), x1v, x1a, epv, epa)
+    assert np.allclose(v1, v2, rtol=0, atol=1e-5 * np.abs(v1).max()) and np.allclose(a1, a2, rtol=0,
+                                                                                    atol=1e-5 * np.abs(a1).max())
+    wc = w.with_(variant=0)
+    vc, ac = _step_with_ctx(wc, O.Model(wc, m.g, m.layers), O.build_context(wc, m.g, txt, img), x1v, x1a, epv, epa)
+    assert not np.allclose(v1, vc, rtol=0, atol=1e-4 * np.abs(v1).max())

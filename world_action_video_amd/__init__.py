@@ -40,12 +40,14 @@ class wam_config(ctypes.Structure):
 
 BLOCK_FIELDS = ("mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "ln3_w", "ln3_b", "w_cq", "b_cq", "g_cq",
                 "w_ck", "b_ck", "g_ck", "w_cv", "b_cv", "w_co", "b_co", "w_ff1", "b_ff1", "w_ff2", "b_ff2")
+IMG_XATTN_FIELDS = ("w_cki", "b_cki", "g_cki", "w_cvi", "b_cvi")
 GLOBAL_FIELDS = ("t_w1", "t_b1", "t_w2", "t_b2", "t_wp", "t_bp", "pe_w", "pe_b", "ae_w", "ae_b", "head_mod",
                  "vo_w", "vo_b", "ao_w", "ao_b", "txt_w", "txt_b", "img_w", "img_b")
 
 
 class wam_block_weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_FIELDS] + [("mx", ctypes.c_void_p)]
+    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_FIELDS] + [("mx", ctypes.c_void_p)] + \
+               [(n, ctypes.c_void_p) for n in IMG_XATTN_FIELDS]
 
 
 class wam_action_io(ctypes.Structure):

@@ -41,6 +41,8 @@ struct Geo {
   DType dt;
   bool mx;     // MXFP8 block projections
   int F1;      // rows of w_ff1 (2F for the SwiGLU variant)
+  int Lt;      // text rows of the condition sequence (the image rows follow)
+  bool img_x;  // image rows with their own projections and softmax (IMG_XATTN variant)
 };
 
 Geo geo_of(const wam_config& c) {
@@ -53,6 +55,8 @@ Geo geo_of(const wam_config& c) {
   g.esz = c.dtype == WAM_BF16 ? 2 : 4;
   g.mx = c.precision == WAM_PRECISION_MXFP8;
   g.F1 = (c.variant & WAM_VARIANT_SWIGLU) ? 2 * c.ffn_dim : c.ffn_dim;
+  g.Lt = c.ctx_text_len;
+  g.img_x = (c.variant & WAM_VARIANT_IMG_XATTN) != 0;
   return g;
 }
 
@@ -96,8 +100,10 @@ wam_status check_cfg(const wam_config* c) {
   if (c->ctx_text_len <= 0 || c->ctx_img_len < 0) return fail(WAM_E_SHAPE, "bad condition lengths");
   if (c->branches != 1 && c->branches != 2) return fail(WAM_E_SHAPE, "branches must be 1 or 2");
   if (!(c->eps > 0.f) || !(c->rope_theta > 0.f)) return fail(WAM_E_ARG, "eps and rope_theta must be positive");
-  if (c->variant & ~(WAM_VARIANT_FRAME_CAUSAL | WAM_VARIANT_RMS_NORM | WAM_VARIANT_SWIGLU))
+  if (c->variant & ~(WAM_VARIANT_FRAME_CAUSAL | WAM_VARIANT_RMS_NORM | WAM_VARIANT_SWIGLU | WAM_VARIANT_IMG_XATTN))
     return fail(WAM_E_UNSUPPORTED, "unknown variant bits 0x%x", c->variant);
+  if ((c->variant & WAM_VARIANT_IMG_XATTN) && (c->ctx_img_len <= 0 || c->ctx_text_len % 8))
+    return fail(WAM_E_SHAPE, "separate image cross-attention needs image tokens and ctx_text_len a multiple of 8");
   if (c->precision != WAM_PRECISION_NATIVE && c->precision != WAM_PRECISION_MXFP8)
     return fail(WAM_E_UNSUPPORTED, "unknown precision %d", c->precision);
   if (c->precision == WAM_PRECISION_MXFP8 && (c->dtype != WAM_BF16 || c->dim % 128 || c->ffn_dim % 128))
@@ -158,8 +164,14 @@ const char* const kBlockNames[] = {"mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o",
 
 bool unaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
 
-wam_status check_block(const wam_block_weights* b, int l, bool mx) {
+wam_status check_block(const wam_block_weights* b, int l, bool mx, bool img_x) {
   if (!b) return fail(WAM_E_ARG, "block weights of layer %d are NULL", l);
+  if (img_x) {
+    const void* q[5] = {b->w_cki, b->b_cki, b->g_cki, b->w_cvi, b->b_cvi};
+    for (const void* x : q)
+      if (!x || unaligned16(x))
+        return fail(WAM_E_ARG, "layer %d: image key / value projections NULL or not 16-byte aligned", l);
+  }
   if (mx && (!b->mx || reinterpret_cast<uintptr_t>(b->mx) % 256))
     return fail(WAM_E_ARG, "layer %d: MXFP8 precision needs the packed projections (mx, 256-byte aligned)", l);
   const void* const* p = reinterpret_cast<const void* const*>(b);
@@ -182,7 +194,8 @@ wam_status check_weights(const wam_config* c, const wam_weights* w, bool need_bl
   if (need_blocks) {
     if (!w->blocks) return fail(WAM_E_ARG, "blocks array is NULL");
     for (int l = 0; l < c->layers; ++l) {
-      wam_status st = check_block(&w->blocks[l], l, c->precision == WAM_PRECISION_MXFP8);
+      wam_status st = check_block(&w->blocks[l], l, c->precision == WAM_PRECISION_MXFP8,
+                                  (c->variant & WAM_VARIANT_IMG_XATTN) != 0);
       if (st != WAM_OK) return st;
     }
   }
@@ -206,6 +219,9 @@ wam_status check_ctx(const Geo& g, const wam_ctx_kv* cx) {
   if (cx->branches != g.br) return fail(WAM_E_SHAPE, "condition KV branches != config branches");
   if (cx->ctx_len != g.Lc) return fail(WAM_E_SHAPE, "condition length %d != %d", cx->ctx_len, g.Lc);
   if (cx->ctx_stride < g.Lc || cx->ctx_stride % 64) return fail(WAM_E_SHAPE, "ctx_stride must be a multiple of 64 >= ctx_len");
+  // the image attention reads whole 32-key tiles of value rows that start at column Lt
+  if (g.img_x && cx->ctx_stride < g.Lt + (g.Lc - g.Lt + 31) / 32 * 32)
+    return fail(WAM_E_SHAPE, "ctx_stride must hold ctx_text_len + ctx_img_len rounded up to 32");
   return WAM_OK;
 }
 
@@ -375,7 +391,20 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     ca.Lq_total = p.R; ca.H = g.H; ca.d = g.d; ca.br = g.br; ca.kv_base = g.Lc; ca.chunk_q = 0; ca.kv_total = g.Lc;
     ca.scale_log2 = aa.scale_log2;
     ca.part = part; ca.part_elems = part_n;
-    HIP_TRY(launch_attention(ca, dt, p.s));
+    if (!g.img_x) {
+      HIP_TRY(launch_attention(ca, dt, p.s));
+    } else {   // text rows and image rows, each with its own softmax; the outputs are summed
+      const int Li = g.Lc - g.Lt;
+      ca.kv_base = ca.kv_total = g.Lt;
+      HIP_TRY(launch_attention(ca, dt, p.s));
+      AttnArgs ci = ca;
+      ci.K = reinterpret_cast<const char*>(ca.K) + (size_t)g.Lt * g.d * g.esz;
+      ci.Vt = reinterpret_cast<const char*>(ca.Vt) + (size_t)g.Lt * g.esz;
+      ci.kv_base = ci.kv_total = Li;
+      ci.O = qkv;   // free here: the cross queries are already in qh
+      HIP_TRY(launch_attention(ci, dt, p.s));
+      HIP_TRY(launch_add(attn, qkv, (long)p.M * g.D, dt, p.s));
+    }
   }
   // h += o Wco^T + b, then (7) y2 = LN(h) (1 + scale2) + shift2
   {
@@ -553,6 +582,27 @@ wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void
     va.dst_bh_stride = (long)g.d * out->ctx_stride; va.dst_stride = out->ctx_stride; va.dst_col0 = 0;
     va.rows_per_branch = g.Lc; va.br = g.br; va.H = g.H; va.d = g.d;
     HIP_TRY(launch_v_to_cache(va, g.dt, s));
+    if (g.img_x) {   // image rows of each branch again, with the image projections and gain
+      const int Li = g.Lc - g.Lt;
+      for (int b = 0; b < g.br; ++b) {
+        const char* src = reinterpret_cast<const char*>(ctx) + ((size_t)b * g.Lc + g.Lt) * g.D * g.esz;
+        GemmArgs ik = gemm_args(src, g.D, bw.w_cki, g.D, bw.b_cki, Li, g.D, g.D, part, part_n);
+        ik.C = tmp; ik.ldc = g.D;
+        HIP_TRY(launch_gemm(ik, g.dt, EPI_STORE, s));
+        QkNormArgs iq = qa;
+        iq.src = tmp; iq.gain = reinterpret_cast<const float*>(bw.g_cki); iq.M = Li; iq.rows_per_branch = Li;
+        iq.dst = layer_ptr<char>(out->k, ck_layer, l, g.esz) + (size_t)b * g.H * g.Lc * g.d * g.esz;
+        iq.dst_row0 = g.Lt; iq.rm = RowMap{Li, Li, Li};
+        HIP_TRY(launch_qk_norm_rope(iq, g.dt, s));
+        GemmArgs iv = gemm_args(src, g.D, bw.w_cvi, g.D, bw.b_cvi, Li, g.D, g.D, part, part_n);
+        iv.C = tmp; iv.ldc = g.D;
+        HIP_TRY(launch_gemm(iv, g.dt, EPI_STORE, s));
+        VCacheArgs ia = va;
+        ia.src = tmp; ia.dst = layer_ptr<char>(out->v, cv_layer, l, g.esz) + (size_t)b * g.H * g.d * out->ctx_stride * g.esz;
+        ia.dst_col0 = g.Lt; ia.rows_per_branch = Li; ia.br = 1;
+        HIP_TRY(launch_v_to_cache(ia, g.dt, s));
+      }
+    }
   }
   return WAM_OK;
 }
@@ -596,7 +646,7 @@ wam_status wam_dit_block_fwd(const wam_config* cfg, const wam_block_weights* bw,
   const Geo g = geo_of(*cfg);
   if (layer < 0 || layer >= g.L) return fail(WAM_E_ARG, "layer %d out of range", layer);
   if (n_chunks < 1 || n_chunks > kMaxChunks) return fail(WAM_E_SHAPE, "n_chunks must be in [1, %d]", kMaxChunks);
-  CHECK(check_block(bw, layer, g.mx));
+  CHECK(check_block(bw, layer, g.mx, g.img_x));
   CHECK(check_cache(g, cache, n_chunks * g.Lq));
   CHECK(check_ctx(g, ctx));
   if (!h || !e6) return fail(WAM_E_ARG, "h or e6 is NULL");

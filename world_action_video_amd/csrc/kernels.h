@@ -114,6 +114,8 @@ struct NormArgs {
   uint8_t* mxs;         //   (D % 32 == 0), quantised from the stored bf16 values
 };
 hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s);
+// dst[i] += src[i] for i < n (elements of the storage type; n % 8 == 0, 16-byte aligned pointers)
+hipError_t launch_add(void* dst, const void* src, long n, DType dt, hipStream_t s);
 
 struct QkNormArgs {
   const void* src; long src_ld;     // rows of the projection output ([M][src_ld], T)

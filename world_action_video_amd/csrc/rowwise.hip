@@ -100,6 +100,44 @@ __global__ void __launch_bounds__(256) norm_kernel(NormArgs a) {
   }
 }
 
+// dst += src elementwise, eight elements (bf16) or four (fp32) per 16-byte access; sums in fp32
+template <typename T>
+__global__ void __launch_bounds__(256) add_kernel(T* dst, const T* src, long n16) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  uint4 a = reinterpret_cast<const uint4*>(dst)[i];
+  const uint4 b = reinterpret_cast<const uint4*>(src)[i];
+  uint32_t* pa = reinterpret_cast<uint32_t*>(&a);
+  const uint32_t* pb = reinterpret_cast<const uint32_t*>(&b);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (sizeof(T) == 2) {
+      const float lo = __uint_as_float(pa[k] << 16) + __uint_as_float(pb[k] << 16);
+      const float hi = __uint_as_float(pa[k] & 0xffff0000u) + __uint_as_float(pb[k] & 0xffff0000u);
+      pa[k] = pack2_bf16(lo, hi);
+    } else {
+      pa[k] = __float_as_uint(__uint_as_float(pa[k]) + __uint_as_float(pb[k]));
+    }
+  }
+  reinterpret_cast<uint4*>(dst)[i] = a;
+}
+
+hipError_t launch_add(void* dst, const void* src, long n, DType dt, hipStream_t s) {
+  const long per = dt == DT_BF16 ? 8 : 4;
+  if (n <= 0) return hipSuccess;
+  if (n % per || reinterpret_cast<uintptr_t>(dst) % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return hipErrorInvalidValue;
+  const long n16 = n / per;
+  const dim3 grid((unsigned)((n16 + 255) / 256)), block(256);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL((add_kernel<bf16_t>), grid, block, 0, s, reinterpret_cast<bf16_t*>(dst),
+                       reinterpret_cast<const bf16_t*>(src), n16);
+  else
+    hipLaunchKernelGGL((add_kernel<float>), grid, block, 0, s, reinterpret_cast<float*>(dst),
+                       reinterpret_cast<const float*>(src), n16);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_norm_t(const NormArgs& a, hipStream_t s) {
   const dim3 grid((a.M + 3) / 4), block(256);
