@@ -152,6 +152,9 @@ def main():
     ap.add_argument("--precision", choices=("bf16", "mxfp8"), default="bf16",
                     help="bf16 (the metric); mxfp8: the six block projections quantised to MXFP8, reported "
                          "separately (its own dtype and workload name)")
+    ap.add_argument("--variant", type=int, default=0,
+                    help="architectural variant bits of the step (1 frame-causal, 2 RMSNorm, 4 SwiGLU, 8 separate "
+                         "image cross-attention); non-zero values are reported under their own workload name")
     ap.add_argument("--counters", action="store_true",
                     help="run only a 1 GiB copy and launches of the dominant kernel (for rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -182,6 +185,8 @@ def main():
     mx = args.precision == "mxfp8"
     if mx:
         w = w.with_(precision=synth.workloads.PRECISION_MXFP8)
+    if args.variant:
+        w = w.with_(variant=args.variant)
     Lq, Lv, La, D = w.chunk_tokens, w.video_tokens, w.action_tokens, w.dim
     M = w.branches * Lq
 
@@ -300,7 +305,8 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp8 projections, bf16 elsewhere" if mx else "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latents/features)",
-        "config": {"workload": w.name + ("+mxfp8-projections" if mx else ""), "layers": w.layers, "dim": w.dim, "heads": w.heads, "head_dim": w.head_dim,
+        "config": {"workload": w.name + ("+mxfp8-projections" if mx else "") +
+                               ("+variant%d" % args.variant if args.variant else ""), "layers": w.layers, "dim": w.dim, "heads": w.heads, "head_dim": w.head_dim,
                    "ffn_dim": w.ffn_dim, "branches": w.branches, "chunk_tokens": Lq, "cached_tokens": cache.length,
                    "ctx_tokens": w.ctx_len},
         "step_tflop": round(fl["total"] / 1e12, 3),
@@ -316,7 +322,7 @@ def main():
                      "avg_launch_us": round(gemm_ms * 1e3, 2)},
     }
     log("step %.3f ms; QKV GEMM %.1f us (%.1f TFLOP/s)" % (ms, gemm_ms * 1e3, gemm_tflops))
-    if not args.no_cpu_baseline and not mx:
+    if not args.no_cpu_baseline and not mx and not args.variant:
         log("timing the oracle on the host")
         del model, cache, ctx
         torch.cuda.empty_cache()
