@@ -93,17 +93,19 @@ def linear(x: Array, w: Array, b: Optional[Array] = None) -> Array:
 
 
 def project(w, x: Array, W: Array, b: Optional[Array] = None) -> Array:
-    """A block projection y = x W^T + b. With MXFP8 precision (the low-precision projections of
-    [N569] real-time optimisations; format and block rule in ``oracle.mx``) the rows of x and of W
+    """A block projection y = x W^T + b. With MXFP8 precision (1; the low-precision projections of
+    [N569] real-time optimisations; formats and block rule in ``oracle.mx``) the rows of x and of W
     are first quantised along the input features and the product is taken of the quantised values,
-    exactly (then cast back to the dtype of x)."""
-    if getattr(w, "precision", 0) != 1:
+    exactly (then cast back to the dtype of x); precision 2 quantises W to MXFP4 instead."""
+    prec = getattr(w, "precision", 0)
+    if prec not in (1, 2):
         return linear(x, W, b)
     from .mx import mx_linear, mx_quantize
+    w_fmt = "e2m1" if prec == 2 else "e4m3"   # precision 2: MXFP4 weights, MXFP8 activations
     lead = x.shape[:-1]
     xc, xs = mx_quantize(x.reshape(-1, x.shape[-1]).astype(np.float64))
-    wc, ws = mx_quantize(W.astype(np.float64))
-    y = mx_linear(xc, xs, wc, ws, None if b is None else b.astype(np.float64))
+    wc, ws = mx_quantize(W.astype(np.float64), fmt=w_fmt)
+    y = mx_linear(xc, xs, wc, ws, None if b is None else b.astype(np.float64), w_fmt=w_fmt)
     return y.reshape(lead + (W.shape[0],)).astype(x.dtype)
 
 

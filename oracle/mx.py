@@ -1,4 +1,4 @@
-"""MXFP8 quantisation (oracle) for the low-precision projections.
+"""MXFP8 / MXFP4 quantisation (oracle) for the low-precision projections.
 
 TEST INFRASTRUCTURE ONLY: see ``oracle/__init__.py`` for who may import it.
 
@@ -9,6 +9,10 @@ finite 448; no infinities) sharing one power-of-two scale per 32 consecutive ele
 Reading (the pages name only the element formats): shared exponent e = floor(log2(amax)) - 8,
 8 being the exponent of e4m3's largest power of two, clamped to >= -127 (e8m0 byte e + 127);
 elements x / 2^e saturated to +-448 and rounded to nearest, ties to even.
+
+MXFP4 (weights only): fp4 e2m1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; values
+0, 0.5, 1, 1.5, 2, 3, 4, 6), the same 32-element blocks and block rule with e2m1's largest exponent 2:
+e = floor(log2(amax)) - 2, elements x / 2^e saturated to +-6, nearest with ties to even.
 """
 from __future__ import annotations
 
@@ -53,30 +57,66 @@ def e4m3_encode(x: Array) -> Array:
     return (code | sign).astype(np.uint8)
 
 
-def mx_quantize(x: Array, block: int = 32) -> Tuple[Array, Array]:
-    """Quantise the last axis in blocks of ``block``: (e4m3 codes, e8m0 scale bytes)."""
+E2M1_MAX = 6.0
+
+
+def e2m1_value(code: Array) -> Array:
+    """Real value of e2m1 codes (low 4 bits)."""
+    c = np.asarray(code, dtype=np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = c & 1
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 2.0, e - 1), m / 2.0)
+    return sign * mag
+
+
+def e2m1_encode(x: Array) -> Array:
+    """Round float64 values with |x| <= 6 to e2m1 codes, nearest with ties to even: below 1 the grid
+    spacing is 1/2 (subnormal 0.5 and zero), above it 2^(floor(log2|x|) - 1)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sub = a < 1.0
+    e = np.where(sub, 0, np.floor(np.log2(np.where(a > 0, a, 1.0)))).astype(np.int64)
+    step = np.ldexp(1.0, np.where(sub, -1, e - 1))
+    q = np.rint(a / step)                                   # ties to even
+    # sub: code = q (q = 2 is 1.0, the smallest normal); normal: q in [2, 4], 4 carries into the exponent
+    carry = (~sub) & (q == 4)
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 2, q)
+    code = np.where(sub, q, ((e + 1) << 1) + (q - 2)).astype(np.int64)
+    sign = np.signbit(x).astype(np.int64) << 3
+    return (code | sign).astype(np.uint8)
+
+
+_FORMATS = {"e4m3": (8, E4M3_MAX, e4m3_encode, e4m3_value), "e2m1": (2, E2M1_MAX, e2m1_encode, e2m1_value)}
+
+
+def mx_quantize(x: Array, block: int = 32, fmt: str = "e4m3") -> Tuple[Array, Array]:
+    """Quantise the last axis in blocks of ``block``: (element codes, e8m0 scale bytes). e2m1 codes
+    are returned one per element (low 4 bits), not packed."""
+    emax, vmax, encode, _ = _FORMATS[fmt]
     x = np.asarray(x, dtype=np.float64)
     assert x.shape[-1] % block == 0
     xb = x.reshape(x.shape[:-1] + (x.shape[-1] // block, block))
     amax = np.abs(xb).max(axis=-1)
     with np.errstate(divide="ignore"):
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - emax, -127)
     e = np.maximum(e, -127).astype(np.int64)
-    y = np.clip(xb / np.ldexp(1.0, e)[..., None], -E4M3_MAX, E4M3_MAX)
-    codes = e4m3_encode(y).reshape(x.shape)
+    y = np.clip(xb / np.ldexp(1.0, e)[..., None], -vmax, vmax)
+    codes = encode(y).reshape(x.shape)
     return codes, (e + 127).astype(np.uint8)
 
 
-def mx_dequantize(codes: Array, scales: Array, block: int = 32) -> Array:
-    v = e4m3_value(codes)
+def mx_dequantize(codes: Array, scales: Array, block: int = 32, fmt: str = "e4m3") -> Array:
+    v = _FORMATS[fmt][3](codes)
     vb = v.reshape(v.shape[:-1] + (v.shape[-1] // block, block))
     return (vb * np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]).reshape(v.shape)
 
 
-def mx_linear(a_codes: Array, a_scales: Array, w_codes: Array, w_scales: Array, bias=None) -> Array:
+def mx_linear(a_codes: Array, a_scales: Array, w_codes: Array, w_scales: Array, bias=None, w_fmt: str = "e4m3") -> Array:
     """y = dequant(A) dequant(W)^T (+ b) in float64: what the scaled matrix instruction computes
-    before the fp32 rounding of its accumulation."""
-    y = mx_dequantize(a_codes, a_scales) @ mx_dequantize(w_codes, w_scales).T
+    before the fp32 rounding of its accumulation (A e4m3; W e4m3 or e2m1)."""
+    y = mx_dequantize(a_codes, a_scales) @ mx_dequantize(w_codes, w_scales, fmt=w_fmt).T
     return y if bias is None else y + bias
 
 

@@ -140,3 +140,72 @@ def test_projection_mx_error_is_that_of_the_format():
     W = rng.standard_normal((96, 512))
     err = np.linalg.norm(O.project(_W, x, W, None) - x @ W.T) / np.linalg.norm(x @ W.T)
     assert 0.01 < err < 2 * O.relative_error_bound()
+
+
+# ---- MXFP4 (e2m1 elements) ------------------------------------------------------------------------
+
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # the format's eight magnitudes, codes 0..7
+
+
+def test_e2m1_code_table_and_round_trip():
+    codes = np.arange(16)
+    vals = O.e2m1_value(codes)
+    assert list(vals[:8]) == E2M1_TABLE
+    assert list(-vals[8:]) == E2M1_TABLE and all(np.signbit(vals[8:]))
+    assert np.array_equal(O.e2m1_encode(vals), codes)
+
+
+def test_e2m1_ties_to_even_and_nearest():
+    # midpoints between neighbours go to the neighbour with an even code (mantissa bit 0)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    want = np.array([0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0])
+    assert np.array_equal(O.e2m1_value(O.e2m1_encode(mids)), want)
+    assert np.array_equal(O.e2m1_value(O.e2m1_encode(-mids)), -want)
+    # just off the midpoints: plain nearest
+    eps = 1e-9
+    assert np.array_equal(O.e2m1_value(O.e2m1_encode(mids + eps)), np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]))
+    assert np.array_equal(O.e2m1_value(O.e2m1_encode(mids - eps)), np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0]))
+
+
+def test_mxfp4_block_rule_and_saturation():
+    x = np.zeros((1, 64))
+    x[0, 0] = 1.0                                          # amax 1: e = 0 - 2, scaled amax 4 (code 6)
+    x[0, 1] = 0.3                                          # 0.3 * 4 = 1.2 -> 1.0
+    x[0, 32] = 7.0                                         # amax 7: e = 2 - 2 = 0, 7 > 6 saturates
+    x[0, 33] = -2.9                                        # -> -3
+    codes, scales = O.mx_quantize(x, fmt="e2m1")
+    assert list(scales[0]) == [125, 127]
+    assert codes[0, 0] == 6 and codes[0, 1] == 2 and codes[0, 32] == 7 and codes[0, 33] == 13
+    back = O.mx_dequantize(codes, scales, fmt="e2m1")
+    assert back[0, 0] == 1.0 and back[0, 1] == 0.25 and back[0, 32] == 6.0 and back[0, 33] == -3.0
+
+
+def test_mxfp4_error_is_that_of_the_format():
+    """One mantissa bit: relative error of a normal element at most 1/4 (1.25 -> 1); relative L2 of
+    Gaussian blocks between 5% and 20%."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((64, 256))
+    codes, scales = O.mx_quantize(x, fmt="e2m1")
+    back = O.mx_dequantize(codes, scales, fmt="e2m1")
+    err = np.linalg.norm(back - x) / np.linalg.norm(x)
+    assert 0.05 < err < 0.2
+    # elements at least a quarter of the block maximum sit in e2m1's normal range: error <= 1/4
+    xb = x.reshape(64, 8, 32)
+    big = np.abs(xb) >= np.abs(xb).max(axis=-1, keepdims=True) / 4
+    bb = back.reshape(64, 8, 32)
+    sat = np.abs(xb) > 6 * np.ldexp(1.0, scales.astype(int) - 127)[..., None]
+    rel = np.abs(bb - xb) / np.abs(xb)
+    assert rel[big & ~sat].max() <= 0.25 + 1e-12
+
+
+def test_projection_mxfp4_weights():
+    """Precision 2: activations MXFP8, weights MXFP4 -- the plain product of the two dequantised operands."""
+    class W2:
+        precision = 2
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 64))
+    W = rng.standard_normal((7, 64))
+    xc, xs = O.mx_quantize(x)
+    wc, ws = O.mx_quantize(W, fmt="e2m1")
+    want = O.mx_dequantize(xc, xs) @ O.mx_dequantize(wc, ws, fmt="e2m1").T
+    assert np.array_equal(O.project(W2, x, W, None), want)
