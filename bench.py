@@ -149,9 +149,9 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
                     help="3: the step metric (default); 2: one full-width block (br = 2 and B = 1); 4: four chunks "
                          "of 16 Euler steps plus KV appends; 5: three-view long context, 16-step loop with reuse")
-    ap.add_argument("--precision", choices=("bf16", "mxfp8"), default="bf16",
-                    help="bf16 (the metric); mxfp8: the six block projections quantised to MXFP8, reported "
-                         "separately (its own dtype and workload name)")
+    ap.add_argument("--precision", choices=("bf16", "mxfp8", "mxfp4w"), default="bf16",
+                    help="bf16 (the metric); mxfp8: the six block projections quantised to MXFP8; mxfp4w: their "
+                         "weights MXFP4, activations MXFP8 -- reported separately (own dtype and workload name)")
     ap.add_argument("--variant", type=int, default=0,
                     help="architectural variant bits of the step (1 frame-causal, 2 RMSNorm, 4 SwiGLU, 8 separate "
                          "image cross-attention); non-zero values are reported under their own workload name")
@@ -182,9 +182,10 @@ def main():
         extra_workload(args, dev)
         return
     w = WORKLOADS[WORKLOAD_ID]
-    mx = args.precision == "mxfp8"
+    mx = args.precision != "bf16"
+    w4 = args.precision == "mxfp4w"
     if mx:
-        w = w.with_(precision=synth.workloads.PRECISION_MXFP8)
+        w = w.with_(precision=synth.workloads.PRECISION_MXFP4W if w4 else synth.workloads.PRECISION_MXFP8)
     if args.variant:
         w = w.with_(variant=args.variant)
     Lq, Lv, La, D = w.chunk_tokens, w.video_tokens, w.action_tokens, w.dim
@@ -268,9 +269,11 @@ def main():
         yq = torch.empty((M, D), dtype=torch.uint8, device=dev)
         ys = torch.empty((M, D // 32), dtype=torch.uint8, device=dev)
         wam.wam_mx_quantize(wam.WAM_BF16, y, D, M, D, yq, D, ys)
-        arena = model.blocks[0].mx   # w_qkv codes [3D][D] at offset 0, its scales after them (256-aligned)
-        wq_s = arena + ((3 * D * D + 255) // 256) * 256
-        qkv_op = lambda: wam.wam_op_linear_mx(yq, ys, D, arena, wq_s, D, bq, cq, 3 * D, M, 3 * D, D, 0)  # noqa: E731
+        arena = model.blocks[0].mx   # w_qkv codes [3D][D] (or [3D][D/2] packed e2m1) at 0, its scales after them
+        wrow = D // 2 if w4 else D
+        wq_s = arena + ((3 * D * wrow + 255) // 256) * 256
+        qkv_op = lambda: wam.wam_op_linear_mx(yq, ys, D, arena, wq_s, wrow, bq, cq, 3 * D, M, 3 * D, D, 0,  # noqa: E731
+                                              w_format=wam.WAM_MX_E2M1 if w4 else wam.WAM_MX_E4M3)
     else:
         qkv_op = lambda: wam.wam_op_linear(wam.WAM_BF16, y, D, wq, D, bq, cq, 3 * D, M, 3 * D, D, 0)  # noqa: E731
     for _ in range(3):
@@ -303,9 +306,10 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 projections, bf16 elsewhere" if mx else "bf16",
+        "dtype": ("mxfp4 weights x mxfp8 activations in the projections, bf16 elsewhere" if w4 else
+                  "mxfp8 projections, bf16 elsewhere") if mx else "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latents/features)",
-        "config": {"workload": w.name + ("+mxfp8-projections" if mx else "") +
+        "config": {"workload": w.name + (("+mxfp4w-projections" if w4 else "+mxfp8-projections") if mx else "") +
                                ("+variant%d" % args.variant if args.variant else ""), "layers": w.layers, "dim": w.dim, "heads": w.heads, "head_dim": w.head_dim,
                    "ffn_dim": w.ffn_dim, "branches": w.branches, "chunk_tokens": Lq, "cached_tokens": cache.length,
                    "ctx_tokens": w.ctx_len},
@@ -315,7 +319,8 @@ def main():
         "first_step_ms": round(first_ms, 1),
         "setup_s": round(setup_s, 1),
         "outputs_finite": finite,
-        "roofline": {"kernel": ("gemm4mx_kernel<EPI_STORE> (MXFP8 scaled MFMA" if mx else
+        "roofline": {"kernel": ("gemm4mx_kernel<EPI_STORE, W4> (MXFP4 x MXFP8 scaled MFMA" if w4 else
+                                "gemm4mx_kernel<EPI_STORE> (MXFP8 scaled MFMA" if mx else
                                 "gemm4_kernel<EPI_STORE> (bf16") + " 256x256 tile, 4 waves; QKV projection, 928x15360x5120)",
                      "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / peak, 4), "traffic": traffic,

@@ -73,7 +73,9 @@ typedef struct {
  *   by the scaled matrix instructions, fp32 accumulation; outputs, epilogues and every other
  *   operation as NATIVE. The condition projections (wam_ctx_build), embeddings and heads stay in
  *   dtype. */
-enum { WAM_PRECISION_NATIVE = 0, WAM_PRECISION_MXFP8 = 1 };
+enum { WAM_PRECISION_NATIVE = 0, WAM_PRECISION_MXFP8 = 1, WAM_PRECISION_MXFP4W = 2 };
+/* MXFP4W: as MXFP8, but the packed weights are MXFP4 (e2m1 elements, see wam_mx4_quantize); the
+ * activations stay MXFP8 and the instructions take one fp8 and one fp4 operand. */
 
 /* Architectural variants drawn on the architecture page next to the adopted readings.
  * FRAME_CAUSAL: inside a chunk a video token sees the video tokens of its own and earlier frames
@@ -289,13 +291,22 @@ wam_status wam_op_linear(wam_dtype dtype, const void *A, int lda, const void *W,
  *   of 16), scales [rows][cols / 32] bytes; cols multiple of 32.
  *   wam_op_linear_mx: C[m][n] = act(sum_k dequant(A)[m][k] dequant(W)[n][k] + bias[n]) with A codes
  *   [M][lda] and scales [M][K/32], W codes [N][ldw] and scales [N][K/32], fp32 accumulation, C bf16
- *   [M][ldc]; act as wam_op_linear; K multiple of 128, N multiple of 4, lda / ldw multiples of 16,
+ *   [M][ldc] (W MXFP8, or MXFP4 with w_format below); act as wam_op_linear; K multiple of 128, N
+ *   multiple of 4, lda / ldw multiples of 16,
  *   codes 16-byte and scales 4-byte aligned. Errors: WAM_E_SHAPE / WAM_E_ARG, nothing launched.
  *   ws: optional scratch for split-K partials (as wam_op_linear). */
 wam_status wam_mx_quantize(wam_dtype dtype, const void *src, int ld, int rows, int cols, void *codes, int ldq,
                            void *scales, void *stream);
+/* MXFP4 (weights): e2m1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit: 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6), block exponent e = max(floor(log2(amax)) - 2, -127), codes = e2m1 of x * 2^-e
+ * saturated to +-6, nearest even; two codes per byte, low nibble first (k even), codes [rows][ldq]
+ * bytes with ldq >= cols / 2 a multiple of 16; scales as wam_mx_quantize. */
+wam_status wam_mx4_quantize(wam_dtype dtype, const void *src, int ld, int rows, int cols, void *codes, int ldq,
+                            void *scales, void *stream);
+enum { WAM_MX_E4M3 = 0, WAM_MX_E2M1 = 1 };
+/* w_format: WAM_MX_E4M3 (W codes [N][ldw] bytes, ldw >= K) or WAM_MX_E2M1 (packed nibbles, ldw >= K/2). */
 wam_status wam_op_linear_mx(const void *A, const void *A_scales, int lda, const void *W, const void *W_scales, int ldw,
-                            const float *bias, void *C, int ldc, int M, int N, int K, int act, void *ws,
+                            int w_format, const float *bias, void *C, int ldc, int M, int N, int K, int act, void *ws,
                             size_t ws_bytes, void *stream);
 
 /* Attention ([ARCH] §2.3 causal self-attention and cross-attention; [HYPER] 方法 mask):
@@ -309,9 +320,9 @@ wam_status wam_op_linear_mx(const void *A, const void *A_scales, int lda, const 
  * outputs (66 x 64 fp32 per 32 queries and range); the ranges are merged in a fixed order, so the
  * result is deterministic, and equals the unsplit result up to rounding. Without scratch (NULL, or
  * too small) nothing is split. The stack and block calls use their own workspace. */
-/* Packed MXFP8 projections of one layer for WAM_PRECISION_MXFP8. Layout (each region 256-byte
- * aligned, in this order for w_qkv, w_o, w_cq, w_co, w_ff1, w_ff2): e4m3 codes [N][K] then e8m0 scales
- * [N][K/32] of the [N][K] matrix. wam_mx_block_bytes: the arena size (0 for a configuration the
+/* Packed projections of one layer for WAM_PRECISION_MXFP8 / MXFP4W. Layout (each region 256-byte
+ * aligned, in this order for w_qkv, w_o, w_cq, w_co, w_ff1, w_ff2): codes (e4m3 [N][K], or e2m1
+ * [N][K/2] packed for MXFP4W) then e8m0 scales [N][K/32] of the [N][K] matrix. wam_mx_block_bytes: the arena size (0 for a configuration the
  * format cannot serve: dtype not bf16, dim or ffn_dim not multiples of 128). wam_mx_pack_block
  * quantises bw's bf16 matrices into dst (device, 256-byte aligned, dst_bytes >= the arena size); run
  * once per layer after the weights are loaded. Errors: WAM_E_ARG / WAM_E_SHAPE, nothing launched. */

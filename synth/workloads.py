@@ -71,6 +71,7 @@ VARIANT_IMG_XATTN = 8      # image condition tokens: own key / value projections
 # Low-precision block projections: inputs and weights quantised to MXFP8 (fp8 e4m3 codes with one
 # power-of-two scale per 32 consecutive input features)
 PRECISION_MXFP8 = 1
+PRECISION_MXFP4W = 2       # weights MXFP4 (fp4 e2m1 codes, same block scales), activations MXFP8
 
 WORKLOADS = {
     # Tiny single block: width 256, 4 heads of 64, FFN 1024, 2 frames of 8x8 patches + 24 action tokens,

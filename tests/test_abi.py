@@ -131,7 +131,8 @@ def test_mx_validation():
     assert lib.wam_mx_quantize(7, P, 64, 4, 64, P, 64, P, None) == wam.WAM_E_ARG
     # product: K not a multiple of 128, N not a multiple of 4, odd SwiGLU pitch, scale misaligned, NULL operand
     args = lambda **kw: [kw.get(n, d) for n, d in (  # noqa: E731
-        ("A", P), ("As", P), ("lda", 256), ("W", P), ("Ws", P), ("ldw", 256), ("bias", None), ("C", P), ("ldc", 64),
+        ("A", P), ("As", P), ("lda", 256), ("W", P), ("Ws", P), ("ldw", 256), ("wf", 0), ("bias", None), ("C", P),
+        ("ldc", 64),
         ("M", 8), ("N", 64), ("K", 256), ("act", 0), ("ws", None), ("wsb", 0), ("s", None))]
     assert lib.wam_op_linear_mx(*args(K=192, lda=192, ldw=192)) == wam.WAM_E_SHAPE
     assert lib.wam_op_linear_mx(*args(N=62)) == wam.WAM_E_SHAPE
@@ -139,6 +140,9 @@ def test_mx_validation():
     assert lib.wam_op_linear_mx(*args(Ws=P + 2)) == wam.WAM_E_ARG
     assert lib.wam_op_linear_mx(*args(As=None)) == wam.WAM_E_ARG
     assert lib.wam_op_linear_mx(*args(act=3)) == wam.WAM_E_ARG
+    assert lib.wam_op_linear_mx(*args(wf=2)) == wam.WAM_E_ARG
+    assert lib.wam_op_linear_mx(*args(wf=1, ldw=112)) == wam.WAM_E_SHAPE     # e2m1 rows need K / 2 = 128 bytes
+    assert lib.wam_mx4_quantize(0, P, 64, 4, 64, P, 16, P, None) == wam.WAM_E_SHAPE   # ldq < cols / 2
 
 
 def test_image_cross_attention_validation():

@@ -187,14 +187,17 @@ def test_variant_stack_matches_oracle(gpu, tiny_oracle, dtype, variant):
 MX_TOL = 5e-2
 
 
+@pytest.mark.parametrize("precision", [synth.workloads.PRECISION_MXFP8, synth.workloads.PRECISION_MXFP4W])
 @pytest.mark.parametrize("variant", [0, synth.workloads.VARIANT_SWIGLU | synth.workloads.VARIANT_RMS_NORM])
-def test_mxfp8_stack_matches_oracle(gpu, tiny_oracle, variant):
-    """One cached chunk and a step with the six block projections in MXFP8, against the oracle with
-    the same quantised projections; the distance to the unquantised model is printed (quality)."""
+def test_mxfp8_stack_matches_oracle(gpu, tiny_oracle, variant, precision):
+    """One cached chunk and a step with the six block projections in MXFP8 (or MXFP4 weights with
+    MXFP8 activations), against the oracle with the same quantised projections; the distance to the
+    unquantised model is printed (quality). The weights are quantised identically on both sides (the
+    quantisers are bit-exact), so the bound is the MXFP8 one."""
     w0, m0, ckv = tiny_oracle
-    w = w0.with_(variant=variant, precision=synth.workloads.PRECISION_MXFP8)
+    w = w0.with_(variant=variant, precision=precision)
     m = O.load_model(w) if variant & synth.workloads.VARIANT_SWIGLU else O.Model(w, m0.g, m0.layers)
-    print("mxfp8 stack, variant", variant, flush=True)
+    print("low-precision stack, precision", precision, "variant", variant, flush=True)
     x1v, x1a, epv, epa = tiny_inputs(w)
     cache = O.KVCache.empty(w.layers, w.branches, w.dim)
     O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)

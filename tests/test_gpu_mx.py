@@ -297,3 +297,139 @@ def test_op_linear_mx_exact_sum_rows(gpu):
         assert np.all(got[r] == got[r, 0])
         if exact:
             assert got[r, 0] == ex[r, 0], (r, got[r, 0], ex[r, 0])
+
+
+# ---- MXFP4 weights (e2m1 codes, two per byte, low nibble first) -----------------------------------
+
+def unpack_e2m1(packed, cols):
+    p = np.asarray(packed, dtype=np.uint8)[:, :cols // 2]
+    out = np.empty((p.shape[0], cols), dtype=np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def pack_e2m1(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.ascontiguousarray((c[:, 0::2] & 0xF) | ((c[:, 1::2] & 0xF) << 4))
+
+
+def quantise4_on_gpu(gpu, x, dtype):
+    rows, cols = x.shape
+    X = to_device(np.ascontiguousarray(x, dtype=np.float32), dtype, gpu)
+    ldq = cols // 2 + 16
+    codes = torch.full((rows, ldq), 0x5A, dtype=torch.uint8, device=gpu)
+    scales = torch.full((rows, cols // 32), 0x5A, dtype=torch.uint8, device=gpu)
+    wam.wam_mx4_quantize(wam.WAM_BF16 if dtype == "bf16" else wam.WAM_F32, X, cols, rows, cols, codes, ldq, scales)
+    torch.cuda.synchronize()
+    c = codes.cpu().numpy()
+    assert np.all(c[:, cols // 2:] == 0x5A), "row padding written"
+    return unpack_e2m1(c, cols), scales.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (67, 256), (300, 1024), (5, 5120)])
+def test_mx4_quantize_bit_exact(gpu, dtype, rows, cols):
+    print("mx4_quantize", dtype, rows, cols, flush=True)
+    x = draw((rows, cols), "q4_%d_%d" % (rows, cols))
+    mag = np.ldexp(1.0, (np.arange(rows * (cols // 32)) % 25 - 12)).reshape(rows, cols // 32)
+    x = (x.reshape(rows, cols // 32, 32) * mag[..., None]).reshape(rows, cols).astype(np.float32)
+    if dtype == "bf16":
+        x = synth.round_bf16(x)
+    codes, scales = quantise4_on_gpu(gpu, x, dtype)
+    rc, rs = O.mx_quantize(x.astype(np.float64), fmt="e2m1")
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mx4_quantize_special_blocks(gpu, dtype):
+    """Zero and negative-zero blocks, every e2m1 midpoint (ties to even), saturation above 6, large and
+    small exponents."""
+    blocks = [np.zeros(32), np.where(np.arange(32) % 2 == 0, -0.0, 0.0)]
+    b = np.full(32, 0.5)
+    b[0] = 4.0                                                   # amax 4: e = 0, scaled = x
+    b[1:15] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, 0.3, 3.4]
+    blocks.append(b)
+    b = np.linspace(-1.0, 1.0, 32) * 7.5                         # amax 7.5: e = 0, |x| > 6 saturates
+    blocks.append(b)
+    b = np.full(32, 1.0)
+    b[3] = 5.0                                                   # tie 5 -> 4 with amax 5 (e = 0)
+    blocks.append(b)
+    blocks.append(np.linspace(-1.0, 1.0, 32) * 2.0 ** 40)
+    blocks.append(np.linspace(-1.0, 1.0, 32) * 2.0 ** -120)
+    row = np.concatenate(blocks)
+    x = np.stack([row, -row, np.roll(row, 32)]).astype(np.float32)
+    if dtype == "bf16":
+        x = synth.round_bf16(x)
+    codes, scales = quantise4_on_gpu(gpu, x, dtype)
+    rc, rs = O.mx_quantize(x.astype(np.float64), fmt="e2m1")
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc)
+
+
+def draw_codes4(rows, cols, name):
+    u = synth.uniform01(rows * cols, key(name + "_c4"))
+    codes = np.floor(u * 16).astype(np.uint8).reshape(rows, cols)
+    s = synth.uniform01(rows * cols // 32, key(name + "_s4"))
+    scales = (123 + np.floor(s * 9)).astype(np.uint8).reshape(rows, cols // 32)
+    return codes, scales
+
+
+@pytest.mark.parametrize("M,N,K", MX_CASES)
+@pytest.mark.parametrize("act", [0, 1, 2])
+@pytest.mark.parametrize("split", [False, True])
+def test_op_linear_mx4(gpu, M, N, K, act, split):
+    """MXFP8 activations times MXFP4 weights, same bound as the MXFP8 product (the fp8 x fp4 products
+    are exact; the accumulation is the same instruction's)."""
+    if act == 2 and (N // 2) % 4:
+        pytest.skip("SwiGLU output pitch N/2 must be a multiple of 4 (rejection covered by the MXFP8 test)")
+    print("linear_mx4", M, N, K, act, split, flush=True)
+    ac, as_ = draw_codes(M, K, "a4%d_%d_%d" % (M, N, K))
+    wc, ws_ = draw_codes4(N, K, "w4%d_%d_%d" % (M, N, K))
+    if act == 1:
+        as_ = np.minimum(as_, 120).astype(np.uint8)
+    da, dw = O.mx_dequantize(ac, as_), O.mx_dequantize(wc, ws_, fmt="e2m1")
+    pre = da @ dw.T
+    b = (draw((N,), "b4%d" % N) * np.sqrt(np.mean(pre ** 2))).astype(np.float32)
+    A, AS, W, WS = dev_u8(ac, gpu), dev_u8(as_, gpu), dev_u8(pack_e2m1(wc), gpu), dev_u8(ws_, gpu)
+    B = torch.from_numpy(b).to(gpu)
+    C = torch.full((M, N // 2 if act == 2 else N), float("nan"), dtype=torch.bfloat16, device=gpu)
+    wsb = torch.empty(4 * M * N * 4, dtype=torch.uint8, device=gpu) if split else None
+    wam.wam_op_linear_mx(A, AS, K, W, WS, K // 2, B, C, C.shape[1], M, N, K, act, ws=wsb, w_format=wam.WAM_MX_E2M1)
+    torch.cuda.synchronize()
+    out = C.float().cpu().numpy()
+    pre = pre + b
+    t = acc_bound(da, dw)
+    ref, tol = _tolerance(pre, t, act)
+    _check_bound(out, ref, tol, t if act == 0 else None)
+    assert rel_l2(out, ref) <= 1e-2
+
+
+def test_op_linear_mx4_full_size_end_to_end(gpu):
+    """928 x 15360 x 5120 (QKV shape): bf16 activations quantised to MXFP8 and bf16 weights to MXFP4 on
+    each side independently, rows sampled; and the MXFP4-weight error against the unquantised product."""
+    M, N, K = 928, 15360, 5120
+    x = synth.round_bf16(draw((M, K), "e2e4_x"))
+    w = synth.round_bf16(draw((N, K), "e2e4_w", 0.02))
+    X, Wt = to_device(x, "bf16", gpu), to_device(w, "bf16", gpu)
+    AQ = torch.empty((M, K), dtype=torch.uint8, device=gpu)
+    AS = torch.empty((M, K // 32), dtype=torch.uint8, device=gpu)
+    WQ = torch.empty((N, K // 2), dtype=torch.uint8, device=gpu)
+    WS = torch.empty((N, K // 32), dtype=torch.uint8, device=gpu)
+    wam.wam_mx_quantize(wam.WAM_BF16, X, K, M, K, AQ, K, AS)
+    wam.wam_mx4_quantize(wam.WAM_BF16, Wt, K, N, K, WQ, K // 2, WS)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=gpu)
+    wam.wam_op_linear_mx(AQ, AS, K, WQ, WS, K // 2, None, C, N, M, N, K, 0, w_format=wam.WAM_MX_E2M1)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, M, 29), np.arange(M - 4, M)]))
+    out = C.float().cpu().numpy()[rows]
+    rc, rs = O.mx_quantize(x[rows].astype(np.float64))
+    wc, wsc = O.mx_quantize(w.astype(np.float64), fmt="e2m1")
+    ref = O.mx_linear(rc, rs, wc, wsc, w_fmt="e2m1")
+    t = acc_bound(O.mx_dequantize(rc, rs), O.mx_dequantize(wc, wsc, fmt="e2m1"))
+    _check_bound(out, ref, 2.0 ** -8 * (np.abs(ref) + t) + t, t)
+    exact = x[rows].astype(np.float64) @ w.astype(np.float64).T
+    err = rel_l2(out, exact)
+    print("MXFP4-weight relative L2 against the unquantised product: %.4f" % err, flush=True)
+    assert err <= 0.2

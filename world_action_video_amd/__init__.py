@@ -15,11 +15,12 @@ LIB_PATH = os.path.join(_HERE, "libwam.so")
 
 WAM_OK, WAM_E_ARG, WAM_E_SHAPE, WAM_E_CAPACITY, WAM_E_HIP, WAM_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 WAM_BF16, WAM_F32 = 0, 1
-WAM_PRECISION_NATIVE, WAM_PRECISION_MXFP8 = 0, 1
+WAM_PRECISION_NATIVE, WAM_PRECISION_MXFP8, WAM_PRECISION_MXFP4W = 0, 1, 2
+WAM_MX_E4M3, WAM_MX_E2M1 = 0, 1
 
 EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
            "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear",
-           "wam_mx_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
+           "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error")
 
 
@@ -98,10 +99,11 @@ def load(path: str = LIB_PATH):
                                         P]),
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_mx_quantize": (I, [I, P, I, I, I, P, I, P, P]),
+        "wam_mx4_quantize": (I, [I, P, I, I, I, P, I, P, P]),
         "wam_mx_block_bytes": (S, [CFG]),
         "wam_weights_for_embodiment": (I, [ctypes.POINTER(wam_weights), I, ctypes.POINTER(wam_weights)]),
         "wam_mx_pack_block": (I, [CFG, ctypes.POINTER(wam_block_weights), P, S, P]),
-        "wam_op_linear_mx": (I, [P, P, I, P, P, I, P, P, I, I, I, I, I, P, S, P]),
+        "wam_op_linear_mx": (I, [P, P, I, P, P, I, I, P, P, I, I, I, I, I, P, S, P]),
         "wam_op_attention": (I, [I, P, P, P, P, I, I, I, I, I, I, I, I, I, P, S, P]),
         "wam_kv_evict": (I, [CFG, KV, I, I, P]),
         "wam_kv_reset": (None, [KV]),
@@ -246,10 +248,16 @@ def wam_mx_pack_block(cfg: wam_config, bw: wam_block_weights, dst, stream=None):
     _check(load().wam_mx_pack_block(ctypes.byref(cfg), ctypes.byref(bw), _ptr(dst), nbytes, _stream(stream)))
 
 
-def wam_op_linear_mx(A, A_scales, lda, W, W_scales, ldw, bias, C, ldc, M, N, K, act=0, ws=None, stream=None):
+def wam_mx4_quantize(dtype, src, ld, rows, cols, codes, ldq, scales, stream=None):
+    _check(load().wam_mx4_quantize(dtype, _ptr(src), ld, rows, cols, _ptr(codes), ldq, _ptr(scales), _stream(stream)))
+
+
+def wam_op_linear_mx(A, A_scales, lda, W, W_scales, ldw, bias, C, ldc, M, N, K, act=0, ws=None, stream=None,
+                     w_format=WAM_MX_E4M3):
     """MXFP8 product: uint8 code / scale tensors in, bf16 C out."""
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(load().wam_op_linear_mx(_ptr(A), _ptr(A_scales), lda, _ptr(W), _ptr(W_scales), ldw, _ptr(bias), _ptr(C), ldc,
+    _check(load().wam_op_linear_mx(_ptr(A), _ptr(A_scales), lda, _ptr(W), _ptr(W_scales), ldw, w_format, _ptr(bias),
+                                   _ptr(C), ldc,
                                    M, N, K, act, _ptr(ws), nbytes, _stream(stream)))
 
 

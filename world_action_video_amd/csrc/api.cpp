@@ -39,7 +39,8 @@ struct Geo {
   int D, H, d, F, L, P, A, La, Lv, Lq, Lc, Cin, br, freq;
   size_t esz;
   DType dt;
-  bool mx;     // MXFP8 block projections
+  bool mx;     // MXFP8 block projections (activations; weights too unless w4)
+  bool w4;     // MXFP4 weights of the block projections
   int F1;      // rows of w_ff1 (2F for the SwiGLU variant)
   int Lt;      // text rows of the condition sequence (the image rows follow)
   bool img_x;  // image rows with their own projections and softmax (IMG_XATTN variant)
@@ -53,7 +54,8 @@ Geo geo_of(const wam_config& c) {
   g.freq = c.freq_dim;
   g.dt = c.dtype == WAM_BF16 ? DT_BF16 : DT_F32;
   g.esz = c.dtype == WAM_BF16 ? 2 : 4;
-  g.mx = c.precision == WAM_PRECISION_MXFP8;
+  g.mx = c.precision == WAM_PRECISION_MXFP8 || c.precision == WAM_PRECISION_MXFP4W;
+  g.w4 = c.precision == WAM_PRECISION_MXFP4W;
   g.F1 = (c.variant & WAM_VARIANT_SWIGLU) ? 2 * c.ffn_dim : c.ffn_dim;
   g.Lt = c.ctx_text_len;
   g.img_x = (c.variant & WAM_VARIANT_IMG_XATTN) != 0;
@@ -73,7 +75,7 @@ MxBlock mx_block_of(const Geo& g) {
     b.m[i].N = NK[i][0];
     b.m[i].K = NK[i][1];
     b.m[i].codes = off;
-    off += ((size_t)b.m[i].N * b.m[i].K + 255) & ~size_t(255);
+    off += ((size_t)b.m[i].N * (g.w4 ? b.m[i].K / 2 : b.m[i].K) + 255) & ~size_t(255);
     b.m[i].scales = off;
     off += ((size_t)b.m[i].N * (b.m[i].K / 32) + 255) & ~size_t(255);
   }
@@ -104,10 +106,11 @@ wam_status check_cfg(const wam_config* c) {
     return fail(WAM_E_UNSUPPORTED, "unknown variant bits 0x%x", c->variant);
   if ((c->variant & WAM_VARIANT_IMG_XATTN) && (c->ctx_img_len <= 0 || c->ctx_text_len % 8))
     return fail(WAM_E_SHAPE, "separate image cross-attention needs image tokens and ctx_text_len a multiple of 8");
-  if (c->precision != WAM_PRECISION_NATIVE && c->precision != WAM_PRECISION_MXFP8)
+  if (c->precision != WAM_PRECISION_NATIVE && c->precision != WAM_PRECISION_MXFP8 &&
+      c->precision != WAM_PRECISION_MXFP4W)
     return fail(WAM_E_UNSUPPORTED, "unknown precision %d", c->precision);
-  if (c->precision == WAM_PRECISION_MXFP8 && (c->dtype != WAM_BF16 || c->dim % 128 || c->ffn_dim % 128))
-    return fail(WAM_E_UNSUPPORTED, "MXFP8 projections need dtype bf16 and dim, ffn_dim multiples of 128");
+  if (c->precision != WAM_PRECISION_NATIVE && (c->dtype != WAM_BF16 || c->dim % 128 || c->ffn_dim % 128))
+    return fail(WAM_E_UNSUPPORTED, "MXFP8 / MXFP4 projections need dtype bf16 and dim, ffn_dim multiples of 128");
   return WAM_OK;
 }
 
@@ -194,7 +197,7 @@ wam_status check_weights(const wam_config* c, const wam_weights* w, bool need_bl
   if (need_blocks) {
     if (!w->blocks) return fail(WAM_E_ARG, "blocks array is NULL");
     for (int l = 0; l < c->layers; ++l) {
-      wam_status st = check_block(&w->blocks[l], l, c->precision == WAM_PRECISION_MXFP8,
+      wam_status st = check_block(&w->blocks[l], l, c->precision != WAM_PRECISION_NATIVE,
                                   (c->variant & WAM_VARIANT_IMG_XATTN) != 0);
       if (st != WAM_OK) return st;
     }
@@ -291,8 +294,10 @@ hipError_t mx_operands(const Pass& p, const wam_block_weights& bw, GemmArgs& ga,
   ga.A = xq;
   ga.lda = mm.K;
   ga.As = xs;
-  ga.W = base + mm.codes + (size_t)row0 * mm.K;
-  ga.ldw = mm.K;
+  const int wrow = p.g.w4 ? mm.K / 2 : mm.K;   // bytes of one packed weight row
+  ga.W = base + mm.codes + (size_t)row0 * wrow;
+  ga.ldw = wrow;
+  ga.w_fp4 = p.g.w4;
   ga.Ws = reinterpret_cast<const uint8_t*>(base + mm.scales + (size_t)row0 * (mm.K / 32));
   return e;
 }
@@ -915,14 +920,31 @@ wam_status wam_mx_quantize(wam_dtype dtype, const void* src, int ld, int rows, i
   return WAM_OK;
 }
 
+wam_status wam_mx4_quantize(wam_dtype dtype, const void* src, int ld, int rows, int cols, void* codes, int ldq,
+                            void* scales, void* stream) {
+  if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
+  if (!src || !codes || !scales) return fail(WAM_E_ARG, "NULL buffer");
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(WAM_E_SHAPE, "cols must be a positive multiple of 32");
+  if (ld < cols || ldq < cols / 2 || ldq % 16 || ld % (dtype == WAM_BF16 ? 8 : 4))
+    return fail(WAM_E_SHAPE, "ld must keep rows 16-byte aligned and be >= cols; ldq a multiple of 16, >= cols / 2");
+  if (unaligned16(src) || unaligned16(codes)) return fail(WAM_E_ARG, "src and codes must be 16-byte aligned");
+  HIP_TRY(launch_mx4_quantize(src, ld, dtype == WAM_BF16 ? DT_BF16 : DT_F32, rows, cols,
+                              reinterpret_cast<uint8_t*>(codes), ldq, reinterpret_cast<uint8_t*>(scales),
+                              reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
 wam_status wam_op_linear_mx(const void* A, const void* A_scales, int lda, const void* W, const void* W_scales, int ldw,
-                            const float* bias, void* C, int ldc, int M, int N, int K, int act, void* ws,
+                            int w_format, const float* bias, void* C, int ldc, int M, int N, int K, int act, void* ws,
                             size_t ws_bytes, void* stream) {
   if (!A || !A_scales || !W || !W_scales || !C) return fail(WAM_E_ARG, "NULL operand");
   if (M < 0 || N <= 0 || K <= 0 || K % 128) return fail(WAM_E_SHAPE, "K must be a positive multiple of 128");
   if (N % 4) return fail(WAM_E_SHAPE, "N must be a multiple of 4");
   if (act < 0 || act > 2) return fail(WAM_E_ARG, "act must be 0, 1 or 2");
-  if (lda < K || ldw < K || lda % 16 || ldw % 16) return fail(WAM_E_SHAPE, "lda/ldw must be multiples of 16, >= K");
+  if (w_format != WAM_MX_E4M3 && w_format != WAM_MX_E2M1) return fail(WAM_E_ARG, "unknown weight format");
+  const int wbytes = w_format == WAM_MX_E2M1 ? K / 2 : K;
+  if (lda < K || ldw < wbytes || lda % 16 || ldw % 16)
+    return fail(WAM_E_SHAPE, "lda / ldw must be multiples of 16 holding a row (K codes, K / 2 bytes for e2m1)");
   if (ldc < (act == 2 ? N / 2 : N) || ldc % 4) return fail(WAM_E_SHAPE, "ldc too small or not a multiple of 4");
   if (unaligned16(A) || unaligned16(W) || reinterpret_cast<uintptr_t>(C) % 8 || (bias && unaligned16(bias)))
     return fail(WAM_E_ARG, "A, W (16 bytes), C (8 bytes) and bias (16 bytes) alignment");
@@ -935,6 +957,7 @@ wam_status wam_op_linear_mx(const void* A, const void* A_scales, int lda, const 
   ga.ldc = ldc;
   ga.As = reinterpret_cast<const uint8_t*>(A_scales);
   ga.Ws = reinterpret_cast<const uint8_t*>(W_scales);
+  ga.w_fp4 = w_format == WAM_MX_E2M1;
   HIP_TRY(launch_gemm_mx(ga, act == 2 ? EPI_SWIGLU : act ? EPI_GELU : EPI_STORE, reinterpret_cast<hipStream_t>(stream)));
   return WAM_OK;
 }
@@ -979,8 +1002,12 @@ wam_status wam_mx_pack_block(const wam_config* cfg, const wam_block_weights* bw,
   char* base = reinterpret_cast<char*>(dst);
   for (int i = 0; i < MX_MATS; ++i) {
     const MxMat& m = b.m[i];
-    HIP_TRY(launch_mx_quantize(W[i], m.K, DT_BF16, m.N, m.K, reinterpret_cast<uint8_t*>(base + m.codes), m.K,
-                               reinterpret_cast<uint8_t*>(base + m.scales), s));
+    uint8_t* codes = reinterpret_cast<uint8_t*>(base + m.codes);
+    uint8_t* scales = reinterpret_cast<uint8_t*>(base + m.scales);
+    if (g.w4)
+      HIP_TRY(launch_mx4_quantize(W[i], m.K, DT_BF16, m.N, m.K, codes, m.K / 2, scales, s));
+    else
+      HIP_TRY(launch_mx_quantize(W[i], m.K, DT_BF16, m.N, m.K, codes, m.K, scales, s));
   }
   return WAM_OK;
 }

@@ -608,15 +608,20 @@ gemm4_kernel(GemmArgs g, int splits) {
 // (measured): lane l holds row l % 32; bytes 0-15 are k 16 h .. 16 h + 15 and bytes 16-31 are
 // k 32 + 16 h .. (h = l / 32) of the step, i.e. both 32-k scale blocks, and lane l supplies the scale
 // of block h of its row. The W block goes first (transposed accumulators, as in gemm4_kernel).
+// W4: W holds MXFP4 (e2m1 nibbles, two k per byte, low nibble first): a k-tile is 64 bytes per row,
+// and in the fp4 operand lane l holds k 32 h .. 32 h + 31 of the step as 16 contiguous bytes
+// (measured), which is unit 2 s + h of the row's tile; the A (fp8) operand and the scales are as above.
 // ------------------------------------------------------------------------------------------------
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 
-template <int EPI>
+template <int EPI, bool W4 = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm4mx_kernel(GemmArgs g, int splits) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 4, TN = 4;
   constexpr int NT = 256, UNITS = 8, BK = 128, PER_T = BM * UNITS / NT, PITCH = UNITS + 1;
-  __shared__ uint4 smem[2][(BM + BN) * PITCH];
+  constexpr int UNITS_W = W4 ? 4 : 8, PITCH_W = UNITS_W + 1, PER_TW = BN * UNITS_W / NT, BKW = W4 ? 64 : 128;
+  constexpr int WROWS = NT / UNITS_W;   // W rows one pass of the workgroup's loads covers
+  __shared__ uint4 smem[2][BM * PITCH + BN * PITCH_W];
 
   const int Mt = (g.M + BM - 1) / BM, Nt = (g.N + BN - 1) / BN;
   const int items = Mt * Nt * splits;
@@ -645,12 +650,12 @@ gemm4mx_kernel(GemmArgs g, int splits) {
   const __amdgpu_buffer_rsrc_t rsw_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.Ws), (short)0,
                                                                         (int)((long)g.N * kblocks), 0x00020000);
   const int lrow = tid >> 3, lunit = tid & 7;
-  int offa[PER_T], offw[PER_T];
+  const int lroww = tid / UNITS_W, lunitw = tid % UNITS_W;
+  int offa[PER_T], offw[PER_TW];
 #pragma unroll
-  for (int i = 0; i < PER_T; ++i) {
-    offa[i] = (int)((long)(m0 + lrow + i * 32) * g.lda + lunit * 16);
-    offw[i] = (int)((long)(n0 + lrow + i * 32) * g.ldw + lunit * 16);
-  }
+  for (int i = 0; i < PER_T; ++i) offa[i] = (int)((long)(m0 + lrow + i * 32) * g.lda + lunit * 16);
+#pragma unroll
+  for (int i = 0; i < PER_TW; ++i) offw[i] = (int)((long)(n0 + lroww + i * WROWS) * g.ldw + lunitw * 16);
   // this lane's scale rows: row block i of the wave's A rows, column block j of its W rows
   int soff_a[TM], soff_w[TN];
 #pragma unroll
@@ -658,15 +663,21 @@ gemm4mx_kernel(GemmArgs g, int splits) {
 #pragma unroll
   for (int j = 0; j < TN; ++j) soff_w[j] = (n0 + wn * WN + j * 32 + l32) * kblocks;
   const int sbase = lrow * PITCH + lunit;
+  const int sbasew = BM * PITCH + lroww * PITCH_W + lunitw;
 
-  uint4 rg[2 * PER_T];
+  constexpr int QW = PER_TW / 4;   // W units per quarter: 2 (fp8) or 1 (fp4)
+  uint4 rg[PER_T], rgw[PER_TW];
   auto gload_q = [&](int kt, int q) {
-    const int koff = (kb + min(kt, KT - 1)) * BK;
+    const int kc = kb + min(kt, KT - 1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = 2 * q + u;
-      rg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_, offa[i], koff, 0));
-      rg[PER_T + i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw_, offw[i], koff, 0));
+      rg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_, offa[i], kc * BK, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < QW; ++u) {
+      const int i = QW * q + u;
+      rgw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw_, offw[i], kc * BKW, 0));
     }
   };
   auto sstore_q = [&](int st, int q) {
@@ -674,7 +685,11 @@ gemm4mx_kernel(GemmArgs g, int splits) {
     for (int u = 0; u < 2; ++u) {
       const int i = 2 * q + u;
       smem[st][sbase + i * 32 * PITCH] = rg[i];
-      smem[st][BM * PITCH + sbase + i * 32 * PITCH] = rg[PER_T + i];
+    }
+#pragma unroll
+    for (int u = 0; u < QW; ++u) {
+      const int i = QW * q + u;
+      smem[st][sbasew + i * WROWS * PITCH_W] = rgw[i];
     }
   };
   // the four 32-k scale bytes of tile kt for this lane's rows (one dword per row block)
@@ -698,11 +713,15 @@ gemm4mx_kernel(GemmArgs g, int splits) {
     }
   };
   auto fload_w = [&](int st, int s_, uint4 (&f)[TN][2]) {
-    const uint4* sb = smem[st] + (BM + wn * WN + l32) * PITCH + half;
+    const uint4* sb = smem[st] + BM * PITCH + (wn * WN + l32) * PITCH_W + half;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      f[j][0] = sb[j * 32 * PITCH + 4 * s_];
-      f[j][1] = sb[j * 32 * PITCH + 4 * s_ + 2];
+      if constexpr (W4) {
+        f[j][0] = sb[j * 32 * PITCH_W + 2 * s_];
+      } else {
+        f[j][0] = sb[j * 32 * PITCH_W + 4 * s_];
+        f[j][1] = sb[j * 32 * PITCH_W + 4 * s_ + 2];
+      }
     }
   };
 
@@ -751,9 +770,15 @@ gemm4mx_kernel(GemmArgs g, int splits) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int sw_ = (int)(scw[cur][j] >> (8 * (2 * s_ + half)));
-          const int8v_t wv = __builtin_bit_cast(int8v_t, fb[fs][j]);
           const int8v_t av = __builtin_bit_cast(int8v_t, fa[fc][ii]);
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 0, 0, 0, sw_, 0, sa_);
+          if constexpr (W4) {   // first operand e2m1 (format 4): its low four registers
+            const uint4 w4 = fb[fs][j][0];
+            const int8v_t wv = {(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w, 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 4, 0, 0, sw_, 0, sa_);
+          } else {
+            const int8v_t wv = __builtin_bit_cast(int8v_t, fb[fs][j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 0, 0, 0, sw_, 0, sa_);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1188,6 +1213,81 @@ __global__ void __launch_bounds__(256) mx_quantize_kernel(const T* src, long ld,
   if (part == 0) scales[(long)r * nb + b] = (uint8_t)(e + 127);
 }
 
+// e2m1 code of |y| <= 6 (y already scaled), nearest with ties to even: the midpoints 0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5 go to the neighbour with mantissa bit 0
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
+  return m | (__float_as_uint(y) >> 31 << 3);
+}
+
+// MXFP4 weights: as mx_quantize_kernel with the block exponent floor(log2 amax) - 2 (2 = exponent of
+// e2m1's largest power of two), values saturated to +-6; each lane packs its values two per byte.
+template <typename T>
+__global__ void __launch_bounds__(256) mx4_quantize_kernel(const T* src, long ld, int rows, int cols, uint8_t* codes,
+                                                           long ldq, uint8_t* scales) {
+  constexpr int LPB = sizeof(T) == 2 ? 4 : 8, VALS = 32 / LPB;
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long blk = gid / LPB;
+  const int part = (int)(gid % LPB);
+  const int nb = cols / 32;
+  const bool live = blk < (long)rows * nb;
+  const int r = live ? (int)(blk / nb) : 0, b = live ? (int)(blk % nb) : 0;
+  float v[VALS];
+  if (live) {
+    const uint4 w = *reinterpret_cast<const uint4*>(src + (long)r * ld + b * 32 + part * VALS);
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(ww[k] << 16);
+        v[2 * k + 1] = __uint_as_float(ww[k] & 0xffff0000u);
+      }
+    } else {
+      v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y); v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < VALS; ++i) v[i] = 0.f;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < VALS; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (!live) return;
+  const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xff);
+  const int e = ebits == 0 ? -127 : max(ebits - 127 - 2, -127);
+  const float inv = mx_inv_scale(e);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < VALS; ++i) word |= e2m1_code(fminf(fmaxf(v[i] * inv, -6.f), 6.f)) << (4 * i);
+  uint8_t* out = codes + (long)r * ldq + b * 16 + part * (VALS / 2);
+  if constexpr (VALS == 8)
+    *reinterpret_cast<uint32_t*>(out) = word;
+  else
+    *reinterpret_cast<uint16_t*>(out) = (uint16_t)word;
+  if (part == 0) scales[(long)r * nb + b] = (uint8_t)(e + 127);
+}
+
+hipError_t launch_mx4_quantize(const void* src, long ld_src, DType dt, int rows, int cols, uint8_t* codes, long ldq,
+                               uint8_t* scales, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (cols % 32 || ldq % 16 || ldq < cols / 2 || reinterpret_cast<uintptr_t>(codes) % 16 ||
+      reinterpret_cast<uintptr_t>(src) % 16 || ld_src % (dt == DT_BF16 ? 8 : 4))
+    return hipErrorInvalidValue;
+  const long lanes = (long)rows * (cols / 32) * (dt == DT_BF16 ? 4 : 8);
+  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL((mx4_quantize_kernel<bf16_t>), grid, block, 0, s, reinterpret_cast<const bf16_t*>(src), ld_src,
+                       rows, cols, codes, ldq, scales);
+  else
+    hipLaunchKernelGGL((mx4_quantize_kernel<float>), grid, block, 0, s, reinterpret_cast<const float*>(src), ld_src,
+                       rows, cols, codes, ldq, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_quantize(const void* src, long ld_src, DType dt, int rows, int cols, uint8_t* codes, long ldq,
                               uint8_t* scales, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
@@ -1228,7 +1328,10 @@ static bool mx_operands_ok(const GemmArgs& a) {
 static void launch_g4mx_partial(const GemmArgs& a, int splits, hipStream_t s) {
   const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
   const int units = (int)tiles * splits;
-  hipLaunchKernelGGL((gemm4mx_kernel<EPI_PARTIAL>), dim3(8 * ((units + 7) / 8)), dim3(256), 0, s, a, splits);
+  if (a.w_fp4)
+    hipLaunchKernelGGL((gemm4mx_kernel<EPI_PARTIAL, true>), dim3(8 * ((units + 7) / 8)), dim3(256), 0, s, a, splits);
+  else
+    hipLaunchKernelGGL((gemm4mx_kernel<EPI_PARTIAL>), dim3(8 * ((units + 7) / 8)), dim3(256), 0, s, a, splits);
 }
 
 hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s) {
@@ -1249,14 +1352,20 @@ hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s) {
     return hipGetLastError();
   }
   const dim3 grid(8 * (((int)tiles + 7) / 8)), block(256);
+#define WAM_MX_CASE(E)                                                                             \
+  case E:                                                                                          \
+    if (a.w_fp4) hipLaunchKernelGGL((gemm4mx_kernel<E, true>), grid, block, 0, s, a, 1);           \
+    else hipLaunchKernelGGL((gemm4mx_kernel<E>), grid, block, 0, s, a, 1);                         \
+    break;
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm4mx_kernel<EPI_STORE>), grid, block, 0, s, a, 1); break;
-    case EPI_GELU: hipLaunchKernelGGL((gemm4mx_kernel<EPI_GELU>), grid, block, 0, s, a, 1); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm4mx_kernel<EPI_SWIGLU>), grid, block, 0, s, a, 1); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm4mx_kernel<EPI_RESID>), grid, block, 0, s, a, 1); break;
-    case EPI_RESID_GATED: hipLaunchKernelGGL((gemm4mx_kernel<EPI_RESID_GATED>), grid, block, 0, s, a, 1); break;
+    WAM_MX_CASE(EPI_STORE)
+    WAM_MX_CASE(EPI_GELU)
+    WAM_MX_CASE(EPI_SWIGLU)
+    WAM_MX_CASE(EPI_RESID)
+    WAM_MX_CASE(EPI_RESID_GATED)
     default: return hipErrorInvalidValue;
   }
+#undef WAM_MX_CASE
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ struct GemmArgs {
   long part_elems;           // capacity of `part` in floats
   const uint8_t* As;         // MXFP8 operands only: e8m0 scales of A [M][K/32] and of W [N][K/32]
   const uint8_t* Ws;         //   (A and W then hold fp8 e4m3 codes, lda / ldw in bytes)
+  int w_fp4;                 // MXFP8 operands only: W holds e2m1 nibbles (two k per byte, low first)
 };
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s);
@@ -51,6 +52,10 @@ hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s);
 // [rows][cols/32]; cols % 32 == 0.
 hipError_t launch_mx_quantize(const void* src, long ld_src, DType dt, int rows, int cols, uint8_t* codes, long ldq,
                               uint8_t* scales, hipStream_t s);
+// The same for MXFP4 (e2m1 elements, block exponent floor(log2 amax) - 2): codes two per byte, low
+// nibble first, [rows][ldq] bytes with ldq >= cols / 2.
+hipError_t launch_mx4_quantize(const void* src, long ld_src, DType dt, int rows, int cols, uint8_t* codes, long ldq,
+                               uint8_t* scales, hipStream_t s);
 
 // ---- attention ----------------------------------------------------------------------------------
 struct AttnArgs {

@@ -14,7 +14,7 @@ import torch
 import synth
 from synth.workloads import Workload, draw, global_tensors, is_matrix, layer_tensors
 
-from . import (GLOBAL_FIELDS, WAM_BF16, WAM_F32, WAM_PRECISION_MXFP8, wam_action_io, wam_block_weights, wam_config,
+from . import (GLOBAL_FIELDS, WAM_BF16, WAM_F32, wam_action_io, wam_block_weights, wam_config,
                wam_ctx_kv, wam_kv_cache, wam_mx_block_bytes, wam_mx_pack_block, wam_weights, wam_weights_for_embodiment,
                wam_workspace_bytes)
 
@@ -89,7 +89,7 @@ class DeviceModel:
             for name, t in lp.items():
                 setattr(self.blocks[l], name, t.data_ptr())
         self.mx = []
-        if self.cfg.precision == WAM_PRECISION_MXFP8:   # the library packs each layer's projections once
+        if self.cfg.precision != 0:   # MXFP8 / MXFP4 weights: the library packs each layer's projections once
             nbytes = wam_mx_block_bytes(self.cfg)
             if nbytes == 0:
                 raise ValueError("configuration cannot take MXFP8 projections")
