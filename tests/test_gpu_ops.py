@@ -202,6 +202,22 @@ def test_op_attention_key_split(gpu, d, Lq, kv_base, chunk_q, kv_total):
     assert rel_l2(o1, plain) <= 1e-2
 
 
+@pytest.mark.parametrize("H,Lq,kv_base,chunk_q,kv_total", [
+    (33, 400, 100, 136, 500),   # chunk-causal over a cache, ragged last block
+    (40, 464, 0, 0, 769),       # cross-attention geometry
+    (33, 480, 0, 160, 480),     # full-sequence pass of three chunks
+    (36, 385, 0, 0, 1000),      # last block of 65 queries: waves 2-4 hold (almost) none
+])
+def test_op_attention_five_wave_blocks(gpu, H, Lq, kv_base, chunk_q, kv_total):
+    """Shapes whose 128-query blocks overflow the 256 CUs while 160-query blocks fit in one round take
+    five-wave workgroups (the fifth wave only computes): against the oracle."""
+    print("attention-five-wave", H, Lq, kv_base, chunk_q, kv_total, flush=True)
+    assert -(-Lq // 128) * 2 * H > 256 and -(-Lq // 160) * 2 * H <= 256
+    out, ref = _attn_case(gpu, "bf16", 2, H, 128, Lq, kv_base, chunk_q, kv_total, "w5_%d_%d_%d" % (H, Lq, kv_total))
+    assert np.all(np.isfinite(out))
+    assert rel_l2(out, ref) <= 1e-2
+
+
 def test_op_attention_full_shape_bf16(gpu):
     """Config-3 self-attention geometry: 928 cached + 464 current keys, 40 heads of 128, 2 branches."""
     print("attention-full", flush=True)

@@ -356,14 +356,18 @@ struct KvRing {
   static constexpr int K_ROWS_I = 64 / KU;              // K rows per 1 KB copy
   static constexpr int K_INSTR = AT3_BKV / K_ROWS_I;    // copies per K tile
   static constexpr int V_INSTR = D / 16;                // copies per V^T tile (16 rows each)
-  static constexpr int PER_WAVE = (K_INSTR + V_INSTR) / NW;
+  // waves that copy: all when the copies split evenly over them, else the first four (the others
+  // only compute; their vmcnt waits are then trivially met)
+  static constexpr int COPY_WAVES = (K_INSTR + V_INSTR) % NW == 0 ? NW : 4;
+  static constexpr int PER_WAVE = (K_INSTR + V_INSTR) / COPY_WAVES;
   static constexpr int KB = AT3_BKV * D * 2, SB = KB + D * AT3_BKV * 2;   // K block, stage bytes
-  static_assert((K_INSTR + V_INSTR) % NW == 0, "copies split evenly over the waves");
+  static_assert((K_INSTR + V_INSTR) % COPY_WAVES == 0 && COPY_WAVES <= NW, "copies split evenly over the copy waves");
   static_assert(K_INSTR % PER_WAVE == 0, "a wave copies either keys or values");
   __device__ __forceinline__ static int kswz(int row) { return KU >= 16 ? (row & 15) : ((row >> 1) & 7); }
   __device__ __forceinline__ static int vswz(int row) { return (row >> 2) & 3; }   // four 64-B rows share a bank line
 
   int lds_base, tile_stride, last;
+  bool copier;
   int voff[PER_WAVE], ldst[PER_WAVE];
   __amdgpu_buffer_rsrc_t rsrc;
 
@@ -376,12 +380,13 @@ struct KvRing {
         const_cast<T*>(reinterpret_cast<const T*>(a.K) + bh * a.k_bh_stride), (short)0, a.kv_total * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T*>(reinterpret_cast<const T*>(a.Vt) + bh * a.v_bh_stride), (short)0, D * a.v_stride * 2, 0x00020000);
+    copier = wave < COPY_WAVES;
     const bool kwave = wave * PER_WAVE < K_INSTR;
     rsrc = kwave ? rk : rv;
     tile_stride = kwave ? AT3_BKV * D * 2 : AT3_BKV * 2;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int i = wave * PER_WAVE + j;   // copy index within the tile
+      const int i = min(wave * PER_WAVE + j, K_INSTR + V_INSTR - 1);   // copy index within the tile
       const int ki = i, vi = i - K_INSTR;
       const int krow = ki * K_ROWS_I + lane / KU, vrow = vi * 16 + (lane >> 2);
       voff[j] = kwave ? krow * D * 2 + ((lane % KU) ^ kswz(krow)) * 16
@@ -390,6 +395,8 @@ struct KvRing {
     }
   }
   __device__ __forceinline__ void copy(int t, int stage) const {
+    if constexpr (COPY_WAVES < NW)
+      if (!copier) return;   // wave-uniform
     const int toff = min(t, last) * tile_stride;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j)   // the LDS address is wave-uniform (M0 takes a scalar)
@@ -697,6 +704,11 @@ hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s) {
     b.kv_splits = attn_kv_splits(a.Lq_total, a.H, a.br, a.kv_total);
     if (b.kv_splits > 1 && (!a.part || a.part_elems < attn_split_floats(a.Lq_total, a.H, a.br, a.kv_total)))
       b.kv_splits = 1;   // no scratch for the partials: one range per block
+    // five waves (160 queries) per block when four-wave blocks would overflow the 256 CUs and
+    // five-wave blocks fit them in one round (e.g. 2 x 40 heads x 464 queries: 320 -> 240 blocks)
+    const long heads = (long)a.H * a.br;
+    const bool five = b.kv_splits == 1 && (a.Lq_total + 127) / 128 * heads > 256 && (a.Lq_total + 159) / 160 * heads <= 256;
+    if (copy_ok && a.d == 128 && five) return launch_attn3<128, 4, 5>(b, s);
     if (copy_ok && a.d == 128) return launch_attn3<128>(b, s);
     if (copy_ok && a.d == 64) return launch_attn3<64>(b, s);
     if (a.d == 128) return launch_t<bf16_t, 128>(a, s);
