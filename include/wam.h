@@ -274,7 +274,9 @@ wam_status wam_denoise_chunk_unipc(const wam_config *cfg, const wam_weights *w, 
  * Linear layer ([ARCH] §2.3: every projection of the block): C[m][n] = act(sum_k A[m][k] W[n][k] +
  * bias[n]) with A [M][lda], W [N][ldw], C [M][ldc] in `dtype`; bias float [N] or NULL; act 0 = none,
  * 1 = GELU (tanh approximation, the FFN's activation), 2 = SwiGLU pairs (N even: C[m][j] =
- * SiLU(z[m][2j]) * z[m][2j+1] with z = A W^T + bias, so C has N / 2 columns). K must be a multiple of 64.
+ * SiLU(z[m][2j]) * z[m][2j+1] with z = A W^T + bias, so C has N / 2 columns). K must be a multiple of 64;
+ * A and W must each stay below 2 GiB (the kernels address them with 32-bit buffer offsets), else
+ * WAM_E_SHAPE. M = 0 launches nothing and returns WAM_OK.
  * ws / ws_bytes: optional device scratch (256-byte aligned) for split-K partial products; with
  * NULL, or too little room, the product runs unsplit. A split product sums its fp32 partials in a
  * fixed order, so results are deterministic, but they may differ from the unsplit product in the

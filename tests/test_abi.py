@@ -184,6 +184,21 @@ def test_embodiment_routing_is_host_only():
         wam.wam_weights_for_embodiment(w, 0)
 
 
+def test_empty_and_oversized_products():
+    """M = 0 launches nothing and succeeds; operands past the 32-bit buffer offsets are rejected as a
+    shape error before anything runs (fake pointers, no GPU needed)."""
+    lib = _lib()
+    P = 0x1000
+    assert lib.wam_op_linear(0, P, 64, P, 64, None, P, 64, 0, 64, 64, 0, None, 0, None) == wam.WAM_OK
+    assert lib.wam_op_linear(0, P, 8192, P, 8192, None, P, 64, 300000, 64, 8192, 0, None, 0, None) == wam.WAM_E_SHAPE
+    assert "2 GiB" in wam.wam_last_error()
+    assert lib.wam_op_linear(1, P, 8192, P, 8192, None, P, 300000, 64, 300000, 8192, 0, None, 0, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_linear_mx(P, P, 256, P, P, 256, 0, None, P, 64, 0, 64, 256, 0, None, 0, None) == wam.WAM_OK
+    assert lib.wam_op_linear_mx(P, P, 16384, P, P, 16384, 0, None, P, 64, 140000, 64, 16384, 0, None, 0,
+                                None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_attention(0, P, P, P, P, 1, 1, 64, 0, 64, 64, 0, 0, 8, None, 0, None) == wam.WAM_OK
+
+
 def test_kv_reset_is_host_only():
     _lib()
     kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 512, 464)

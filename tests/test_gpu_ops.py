@@ -218,6 +218,40 @@ def test_op_attention_five_wave_blocks(gpu, H, Lq, kv_base, chunk_q, kv_total):
     assert rel_l2(out, ref) <= 1e-2
 
 
+@pytest.mark.timeout(600)
+def test_op_attention_long_context_full_size_sampled(gpu):
+    """Three-view long-context geometry at full size, as the step launches it (workspace given): 2
+    branches x 40 heads of 128, a chunk of 1344 queries over 6 cached chunks + itself (9408 keys).
+    The oracle computes 48 sampled query rows one by one."""
+    br, H, d, Lq, kv_base = 2, 40, 128, 1344, 8064
+    kv_total = kv_base + Lq
+    print("attention-long-context-full", flush=True)
+    k_rows = ((kv_total + 63) // 64) * 64 + 64
+    v_stride = ((kv_total + 63) // 64) * 64
+    q = draw((br, H, Lq, d), "lcq")
+    k = draw((br, H, k_rows, d), "lck")
+    v = draw((br, H, kv_total, d), "lcv")
+    vt = np.zeros((br, H, d, v_stride), np.float32)
+    vt[..., :kv_total] = np.swapaxes(v, -1, -2)
+    Q, K, VT = (to_device(x, "bf16", gpu) for x in (q, k, vt))
+    q = synth.round_bf16(q)
+    k = synth.round_bf16(k)
+    v = synth.round_bf16(v)
+    Ot = torch.full((br * Lq, H * d), float("nan"), dtype=torch.bfloat16, device=gpu)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=gpu)
+    wam.wam_op_attention(wam.WAM_BF16, Q, K, VT, Ot, br, H, d, Lq, k_rows, v_stride, kv_base, 0, kv_total, ws=ws)
+    torch.cuda.synchronize()
+    out = host(Ot).reshape(br, Lq, H, d)
+    assert np.all(np.isfinite(out))
+    u = synth.uniform01(3 * 48, synth.tensor_key(100, 0, "lc_samples"))
+    picks = [(int(u[3 * i] * br), int(u[3 * i + 1] * H), int(u[3 * i + 2] * Lq)) for i in range(48)]
+    picks += [(br - 1, H - 1, Lq - 1), (0, 0, 0)]
+    got = np.stack([out[b, qi, h] for b, h, qi in picks])
+    ref = np.stack([O.attention(q[b, h, qi:qi + 1].astype(np.float64), k[b, h, :kv_total].astype(np.float64),
+                                v[b, h].astype(np.float64), None)[0] for b, h, qi in picks])
+    assert rel_l2(got, ref) <= 1e-2
+
+
 def test_op_attention_full_shape_bf16(gpu):
     """Config-3 self-attention geometry: 928 cached + 464 current keys, 40 heads of 128, 2 branches."""
     print("attention-full", flush=True)

@@ -897,6 +897,9 @@ wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W,
   if (lda % epu || ldw % epu) return fail(WAM_E_SHAPE, "lda/ldw must keep rows 16-byte aligned");
   if (act < 0 || act > 2) return fail(WAM_E_ARG, "act must be 0, 1 or 2");
   if (act == 2 && N % 2) return fail(WAM_E_SHAPE, "SwiGLU needs an even N");
+  const long esz = dtype == WAM_BF16 ? 2 : 4;
+  if ((long)M * lda * esz >= (1L << 31) || (long)N * ldw * esz >= (1L << 31))
+    return fail(WAM_E_SHAPE, "A and W must each stay below 2 GiB (32-bit buffer offsets): split the product");
   if (ws && reinterpret_cast<uintptr_t>(ws) % 256) return fail(WAM_E_ARG, "workspace must be 256-byte aligned");
   GemmArgs ga = gemm_args(A, lda, W, ldw, bias, M, N, K, ws ? reinterpret_cast<float*>(ws) : nullptr,
                           ws ? (long)(ws_bytes / 4) : 0);
@@ -946,6 +949,8 @@ wam_status wam_op_linear_mx(const void* A, const void* A_scales, int lda, const 
   if (lda < K || ldw < wbytes || lda % 16 || ldw % 16)
     return fail(WAM_E_SHAPE, "lda / ldw must be multiples of 16 holding a row (K codes, K / 2 bytes for e2m1)");
   if (ldc < (act == 2 ? N / 2 : N) || ldc % 4) return fail(WAM_E_SHAPE, "ldc too small or not a multiple of 4");
+  if ((long)M * lda >= (1L << 31) || (long)N * ldw >= (1L << 31))
+    return fail(WAM_E_SHAPE, "A and W codes must each stay below 2 GiB (32-bit buffer offsets): split the product");
   if (unaligned16(A) || unaligned16(W) || reinterpret_cast<uintptr_t>(C) % 8 || (bias && unaligned16(bias)))
     return fail(WAM_E_ARG, "A, W (16 bytes), C (8 bytes) and bias (16 bytes) alignment");
   if (reinterpret_cast<uintptr_t>(A_scales) % 4 || reinterpret_cast<uintptr_t>(W_scales) % 4)
