@@ -744,25 +744,28 @@ gemm4mx_kernel(GemmArgs g, int splits) {
 
   // tile kt from LDS buffer CUR with scale set CUR; rg holds tile kt+1, written to the other buffer
   // quarter by quarter and refilled with tile kt+2; scales of kt+1 are requested into the other set.
+  // Scheduling groups (chunks 0-2): the chunk's LDS reads go out between its first four MFMAs, its
+  // LDS writes and global loads between the last four, so they issue while the matrix core works.
+  constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
   auto tile = [&](int kt, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
     sload(kt + 1, sca[nxt], scw[nxt]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    auto chunk = [&](auto c_c) {
+      constexpr int c = decltype(c_c)::value;
       const int s_ = c >> 1, i0 = 2 * (c & 1);
       const int fc = c & 1, fs = s_ & 1;
-      if (c + 1 < 4) {
+      if constexpr (c + 1 < 4) {
         fload_a(cur, c + 1, fa[fc ^ 1]);
-        if (c == 1) fload_w(cur, 1, fb[fs ^ 1]);
+        if constexpr (c == 1) fload_w(cur, 1, fb[fs ^ 1]);
       }
       sstore_q(nxt, c);
       gload_q(kt + 2, c);
-      if (c + 1 == 4) {
+      if constexpr (c + 1 == 4) {
         __syncthreads();
         fload_a(nxt, 0, fa[fc ^ 1]);
         fload_w(nxt, 0, fb[fs ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         const int i = i0 + ii;
@@ -781,8 +784,26 @@ gemm4mx_kernel(GemmArgs g, int splits) {
           }
         }
       }
+      if constexpr (c + 1 < 4) {
+        constexpr int RD = c == 1 ? (W4 ? 2 : 3) : 1;   // LDS reads per early MFMA (4, 8 or 12 in all)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    chunk(std::integral_constant<int, 0>{});
+    chunk(std::integral_constant<int, 1>{});
+    chunk(std::integral_constant<int, 2>{});
+    chunk(std::integral_constant<int, 3>{});
   };
   int kt = 0;
   for (; kt + 1 < KT; kt += 2) {
