@@ -764,7 +764,6 @@ gemm4mx_kernel(GemmArgs g, int splits) {
         __syncthreads();
         fload_a(nxt, 0, fa[fc ^ 1]);
         fload_w(nxt, 0, fb[fs ^ 1]);
-        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
@@ -783,6 +782,15 @@ gemm4mx_kernel(GemmArgs g, int splits) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wv, av, acc[i][j], 0, 0, 0, sw_, 0, sa_);
           }
         }
+      }
+      if constexpr (c + 1 == 4) {   // the next tile's first fragments go out between this chunk's MFMAs
+        constexpr int RD = W4 ? 1 : 2;                    // 8 or 12 reads over six MFMAs
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_RD, RD, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
       }
       if constexpr (c + 1 < 4) {
         constexpr int RD = c == 1 ? (W4 ? 2 : 3) : 1;   // LDS reads per early MFMA (4, 8 or 12 in all)
