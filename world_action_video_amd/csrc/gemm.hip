@@ -365,7 +365,7 @@ __device__ __forceinline__ void g4_epilogue(const GemmArgs& g, const floatx16 (&
   }
 }
 
-template <int EPI, int IL = 1>
+template <int EPI>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm4_kernel(GemmArgs g, int splits) {
   using T = bf16_t;
@@ -477,112 +477,52 @@ gemm4_kernel(GemmArgs g, int splits) {
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
       const int fc = c & 1;
-      if constexpr (IL) {
-        if (c + 1 < CHUNKS) {
-          fload(cur, c + 1, fa[fc ^ 1], fb[fc ^ 1]);
-          sstore_q(nset, nset, c);
-          gload_q(kt + 3, nset, c);
-          mma(fc, 0, 16);
-          if constexpr (IL == 2) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 2, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
-          } else if constexpr (IL == 3) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
-            }
-          } else if constexpr (IL == 4) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-            }
-          } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        } else {
-          // last chunk: half of its MFMAs cover the tile's final LDS writes, the barrier sits in the
-          // middle, and the other half cover the first fragment loads of the next tile
-          sstore_q(nset, nset, c);
-          gload_q(kt + 3, nset, c);
-          mma(fc, 0, 8);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          __syncthreads();
-          fload(nset, 0, fa[fc ^ 1], fb[fc ^ 1]);
-          mma(fc, 8, 16);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-        if (c + 1 < CHUNKS) fload(cur, c + 1, fa[fc ^ 1], fb[fc ^ 1]);
+      if (c + 1 < CHUNKS) {
+        fload(cur, c + 1, fa[fc ^ 1], fb[fc ^ 1]);
         sstore_q(nset, nset, c);
         gload_q(kt + 3, nset, c);
-        if (c + 1 == CHUNKS) {
-          __syncthreads();
-          fload(nset, 0, fa[fc ^ 1], fb[fc ^ 1]);
+        mma(fc, 0, 16);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mma(fc, 0, 16);
+      } else {
+        // last chunk: half of its MFMAs cover the tile's final LDS writes, the barrier sits in the
+        // middle, and the other half cover the first fragment loads of the next tile
+        sstore_q(nset, nset, c);
+        gload_q(kt + 3, nset, c);
+        mma(fc, 0, 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fload(nset, 0, fa[fc ^ 1], fb[fc ^ 1]);
+        mma(fc, 8, 16);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -895,10 +835,10 @@ static hipError_t launch_cfg(const GemmArgs& a, Epi epi, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, int IL = 1>
+template <int EPI>
 static void launch_g4(const GemmArgs& a, int splits, hipStream_t s) {
   const int items = ((a.M + 255) / 256) * ((a.N + 255) / 256) * splits;
-  hipLaunchKernelGGL((gemm4_kernel<EPI, IL>), dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, a, splits);
+  hipLaunchKernelGGL((gemm4_kernel<EPI>), dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, a, splits);
 }
 
 // bf16 256x256 four-wave path: direct epilogue when there are enough tiles to occupy the CUs, else
