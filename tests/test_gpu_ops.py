@@ -36,7 +36,8 @@ def host(t):
 
 
 LINEAR_CASES = [(1, 64, 64), (67, 200, 128), (300, 384, 512), (928, 1024, 256), (130, 96, 1024), (300, 520, 1024),
-                (257, 260, 2048), (260, 258, 192)]
+                (257, 260, 2048), (260, 258, 192),
+                (520, 16380, 320)]   # 192 tiles of 256 x 256 -> 222 of 256 x 224 (ragged M and N)
 
 
 def split_ws(gpu, M, N):
@@ -78,9 +79,19 @@ def test_op_linear_small(gpu, dtype, M, N, K, act, split):
                                          (928, 5120, 5120, True), (464, 15360, 5120, True), (1538, 5120, 1536, False),
                                          (2688, 5120, 5120, False)])
 def test_op_linear_full_size_sampled(gpu, M, N, K, split):
+    _linear_full(gpu, M, N, K, split, 0)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_op_linear_ffn_up_full_size_sampled(gpu, act):
+    """FFN-up shape 928 x 13824 x 5120 (256 x 224 tiles: 248 workgroups), plain and with GELU."""
+    _linear_full(gpu, 928, 13824, 5120, False, act)
+
+
+def _linear_full(gpu, M, N, K, split, act):
     """The step's real projection shapes in bf16 (split over K as the block splits them when a
     workspace is given), checked on 4096 sampled outputs computed one by one."""
-    print("linear-full", M, N, K, split, flush=True)
+    print("linear-full", M, N, K, split, act, flush=True)
     a = draw((M, K), "fa%d_%d" % (M, K))
     w = draw((N, K), "fw%d_%d" % (N, K), 0.02)
     b = draw((N,), "fb%d" % N, 0.02)
@@ -88,18 +99,22 @@ def test_op_linear_full_size_sampled(gpu, M, N, K, split):
     B = torch.from_numpy(b).to(gpu)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=gpu)
     ws = split_ws(gpu, M, N) if split else None
-    wam.wam_op_linear(wam.WAM_BF16, A, K, W, K, B, C, N, M, N, K, 0, ws=ws)
+    wam.wam_op_linear(wam.WAM_BF16, A, K, W, K, B, C, N, M, N, K, act, ws=ws)
     torch.cuda.synchronize()
     out = host(C)
     if split:   # the partials are summed in a fixed order: a second run is bit-identical
         C2 = torch.empty_like(C)
-        wam.wam_op_linear(wam.WAM_BF16, A, K, W, K, B, C2, N, M, N, K, 0, ws=ws)
+        wam.wam_op_linear(wam.WAM_BF16, A, K, W, K, B, C2, N, M, N, K, act, ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(C, C2)
     rng = np.random.default_rng(7)
     rows = np.concatenate([rng.integers(0, M, 4000), [0, M - 1] * 48])
     cols = np.concatenate([rng.integers(0, N, 4000), [0, N - 1, N - 1, 0] * 24])
-    ref = np.einsum("ik,ik->i", a[rows].astype(np.float64), w[cols].astype(np.float64)) + b[cols]
+    a_bf = synth.round_bf16(a).astype(np.float64)
+    w_bf = synth.round_bf16(w).astype(np.float64)
+    ref = np.einsum("ik,ik->i", a_bf[rows], w_bf[cols]) + b[cols]
+    if act == 1:
+        ref = O.gelu_tanh(ref)
     got = out[rows, cols]
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-3)
 

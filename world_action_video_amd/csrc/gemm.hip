@@ -249,14 +249,14 @@ gemm_kernel(GemmArgs g) {
 static constexpr int EPI_PARTIAL = 16;   // internal: fp32 partial products of one split
 
 // Epilogue of the 256x256 four-wave tiles (bf16 and MXFP8 operands alike).
-template <int EPI>
-__device__ __forceinline__ void g4_epilogue(const GemmArgs& g, const floatx16 (&acc)[4][4], int m0, int n0, int sp,
-                                            int wm, int wn, int l32, int half) {
-  constexpr int TM = 4, TN = 4, WM = 128, WN = 128;
-  // ---- epilogue: lane (l32, half) holds, for block (i, j), output row m = mb + 32 i and columns
+// Epilogue of a wave's TM x TN blocks of 32 x 32 whose first row / column are wrow / wcol.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void g4_epilogue_t(const GemmArgs& g, const floatx16 (&acc)[TM][TN], int wrow, int wcol,
+                                              int sp, int l32, int half) {
+  // ---- lane (l32, half) holds, for block (i, j), output row m = mb + 32 i and columns
   // nb + 32 j + 8 g + 0..3 in acc[i][j][4 g .. 4 g + 3] (g = 0..3). N % 4 == 0 (checked at launch), so
   // a run is either wholly inside the matrix or wholly outside.
-  const int mb = m0 + wm * WM + l32, nb = n0 + wn * WN + 4 * half;
+  const int mb = wrow + l32, nb = wcol + 4 * half;
   auto run = [&](int i, int j, int gq) {
     return make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
   };
@@ -363,6 +363,13 @@ __device__ __forceinline__ void g4_epilogue(const GemmArgs& g, const floatx16 (&
       }
     }
   }
+}
+
+// the 2 x 2 waves of 128 x 128 of the 256 x 256 tiles
+template <int EPI>
+__device__ __forceinline__ void g4_epilogue(const GemmArgs& g, const floatx16 (&acc)[4][4], int m0, int n0, int sp,
+                                            int wm, int wn, int l32, int half) {
+  g4_epilogue_t<EPI, 4, 4>(g, acc, m0 + wm * 128, n0 + wn * 128, sp, l32, half);
 }
 
 template <int EPI>
@@ -537,6 +544,171 @@ gemm4_kernel(GemmArgs g, int splits) {
   g4_epilogue<EPI>(g, acc, m0, n0, sp, wm, wn, l32, half);
 }
 
+
+// ------------------------------------------------------------------------------------------------
+// 256 x 224 four-wave product: the waves stacked along M (64 rows x 224 columns each, 2 x 7 blocks of
+// 32 x 32), the loads, LDS layout and pipeline of gemm4_kernel. For products whose 256-wide tiles
+// leave CUs idle in their single round while 224-wide tiles still fit in one (e.g. 928 x 13824:
+// 216 -> 248 workgroups, each with 7/8 of the work).
+// ------------------------------------------------------------------------------------------------
+template <int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm4w_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 224, WM = 64, TM = 2, TN = 7;
+  constexpr int NT = 256, UNITS = 8, EPU = 8, BK = 64, CHUNKS = 4, PITCH = UNITS + 1;
+  constexpr int PER_A = BM * UNITS / NT, PER_W = BN * UNITS / NT;   // 8 and 7 units per thread per tile
+  __shared__ uint4 smem[2][(BM + BN) * PITCH];
+
+  const int Mt = (g.M + BM - 1) / BM, Nt = (g.N + BN - 1) / BN;
+  const int items = Mt * Nt;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per = items >> 3, rem = items & 7;
+  if (kx >= per + (xcd < rem ? 1 : 0)) return;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
+  const int mt = item % Mt, nt = item / Mt;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KT = g.K / BK;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  const __amdgpu_buffer_rsrc_t ra_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), (short)0,
+                                                                       (int)((long)g.M * g.lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.W), (short)0,
+                                                                       (int)((long)g.N * g.ldw * 2), 0x00020000);
+  const int lrow = tid >> 3, lunit = tid & 7;
+  int offa[PER_A], offw[PER_W];
+#pragma unroll
+  for (int i = 0; i < PER_A; ++i) offa[i] = (int)(((long)(m0 + lrow + i * 32) * g.lda + lunit * EPU) * 2);
+#pragma unroll
+  for (int i = 0; i < PER_W; ++i) offw[i] = (int)(((long)(n0 + lrow + i * 32) * g.ldw + lunit * EPU) * 2);
+  const int sbase = lrow * PITCH + lunit;
+
+  uint4 rg[2][PER_A + PER_W];   // [register set][A units 0..7, W units 8..14]
+  // quarter q of a tile: A units 2q, 2q+1 and W units 2q, 2q+1 (quarter 3 has one W unit)
+  auto gload_q = [&](int kt, int set, int q) {
+    const int koff = min(kt, KT - 1) * BK * 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * q + u;
+      rg[set][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_, offa[i], koff, 0));
+      if (i < PER_W)
+        rg[set][PER_A + i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw_, offw[i], koff, 0));
+    }
+  };
+  auto sstore_q = [&](int st, int set, int q) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * q + u;
+      smem[st][sbase + i * 32 * PITCH] = rg[set][i];
+      if (i < PER_W) smem[st][BM * PITCH + sbase + i * 32 * PITCH] = rg[set][PER_A + i];
+    }
+  };
+  auto fload = [&](int st, int c, uint4* fa, uint4* fb) {
+    const uint4* sa = smem[st] + (wave * WM + l32) * PITCH + half;
+    const uint4* sb = smem[st] + (BM + l32) * PITCH + half;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = sa[i * 32 * PITCH + 2 * c];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = sb[j * 32 * PITCH + 2 * c];
+  };
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+
+  uint4 fa[2][TM], fb[2][TN];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_q(0, 0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_q(1, 1, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sstore_q(0, 0, q);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_q(2, 0, q);
+  fload(0, 0, fa[0], fb[0]);
+
+  auto mma = [&](int fc, int lo, int hi) {
+#pragma unroll
+    for (int q = lo; q < hi; ++q)
+      acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fb[fc][q % TN]),
+                                                                    __builtin_bit_cast(bf16x8_t, fa[fc][q / TN]),
+                                                                    acc[q / TN][q % TN], 0, 0, 0);
+  };
+  constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
+  auto tile = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value, nset = cur ^ 1;
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int fc = c & 1;
+      if (c + 1 < CHUNKS) {
+        fload(cur, c + 1, fa[fc ^ 1], fb[fc ^ 1]);
+        sstore_q(nset, nset, c);
+        gload_q(kt + 3, nset, c);
+        mma(fc, 0, TM * TN);
+        // 14 MFMAs: the 9 fragment reads between the first seven, then the writes and loads
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 2, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // last chunk: half of its MFMAs cover the tile's final LDS writes, the barrier sits in the
+        // middle, and the other half cover the first fragment loads of the next tile
+        sstore_q(nset, nset, c);
+        gload_q(kt + 3, nset, c);
+        mma(fc, 0, 7);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fload(nset, 0, fa[fc ^ 1], fb[fc ^ 1]);
+        mma(fc, 7, TM * TN);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 3, 0);
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>{});
+    tile(kt + 1, std::integral_constant<int, 1>{});
+  }
+  if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
+
+  g4_epilogue_t<EPI, TM, TN>(g, acc, m0 + wave * WM, n0, 0, l32, half);
+}
 
 // ------------------------------------------------------------------------------------------------
 // MXFP8 256x256 four-wave product. Operands are fp8 e4m3 codes with one e8m0 (power-of-two) scale per
@@ -892,10 +1064,26 @@ static void launch_reduce(const GemmArgs& a, Epi epi, int splits, hipStream_t s)
   }
 }
 
+// 224-wide tiles when the 256-wide ones fill between half and all of the CUs in one round and the
+// 224-wide ones still fit in one round: every workgroup then has 7/8 of the work
+static bool use_wide_rows(const GemmArgs& a, Epi epi) {
+  if (epi != EPI_STORE && epi != EPI_GELU) return false;
+  const long mt = (a.M + 255) / 256;
+  const long t256 = mt * ((a.N + 255) / 256), t224 = mt * ((a.N + 223) / 224);
+  return t256 >= 128 && t256 < 256 && t224 <= 256;
+}
+
 static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err) {
   const int plan = g4_plan(a, epi);
   if (plan == 0) return false;
-  if (plan == 1) {
+  if (plan == 1 && use_wide_rows(a, epi)) {
+    const long items = (long)((a.M + 255) / 256) * ((a.N + 223) / 224);
+    const dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(256);
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL((gemm4w_kernel<EPI_GELU>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm4w_kernel<EPI_STORE>), grid, block, 0, s, a);
+  } else if (plan == 1) {
     launch_g4_direct(a, epi, s);
   } else {
     launch_g4<EPI_PARTIAL>(a, plan, s);
