@@ -242,19 +242,28 @@ def cast_params(p: Dict[str, Array], dt) -> Dict[str, Array]:
     return {k: np.asarray(v, dtype=dt) for k, v in p.items()}
 
 
-def build_context(w, g: Dict[str, Array], txt: Array, img: Optional[Array]) -> Array:
-    """Condition sequence per CFG branch: [txt_b W_txt^T + b ; img W_img^T + b]  -> [br, Lc, D].
+def build_context(w, g: Dict[str, Array], txt: Array, img: Optional[Array], state: Optional[Array] = None) -> Array:
+    """Condition sequence per CFG branch: [txt_b W_txt^T + b ; img W_img^T + b ; state W_st^T + b]
+    -> [br, Lc, D].
 
     [ARCH] §2.1: image and text features (1536-d) are concatenated into one condition sequence;
     reading R12: one Linear per modality to the model width. Branch 1 carries the negative
     (null) prompt ([WS1] request format); the image features are shared by both branches.
+    State rows (reading R23): the walk-throughs name a state encoder next to the text encoder
+    whose output is fused into the DiT; here each proprioceptive state vector [state_dim] goes
+    through its own Linear to one condition row after the image rows, shared by the branches.
     """
     ctx_t = linear(txt, g["txt_w"], g["txt_b"])                   # [br, Lt, D]
-    if img is None or w.ctx_img_len == 0:
-        return ctx_t
-    ctx_i = linear(img, g["img_w"], g["img_b"])                   # [Li, D]
-    ctx_i = np.broadcast_to(ctx_i[None], (ctx_t.shape[0],) + ctx_i.shape)
-    return np.concatenate([ctx_t, ctx_i], axis=1)
+    parts = [ctx_t]
+    br = ctx_t.shape[0]
+    if img is not None and w.ctx_img_len > 0:
+        ctx_i = linear(img, g["img_w"], g["img_b"])               # [Li, D]
+        parts.append(np.broadcast_to(ctx_i[None], (br,) + ctx_i.shape))
+    if getattr(w, "ctx_state_len", 0) > 0:
+        assert state is not None and state.shape == (w.ctx_state_len, w.state_dim)
+        ctx_s = linear(state, g["st_w"], g["st_b"])               # [Ls, D]
+        parts.append(np.broadcast_to(ctx_s[None], (br,) + ctx_s.shape))
+    return parts[0] if len(parts) == 1 else np.concatenate(parts, axis=1)
 
 
 def context_kv(w, lp: Dict[str, Array], ctx: Array) -> Tuple[Array, Array]:

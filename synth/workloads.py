@@ -45,6 +45,8 @@ class Workload:
     variant: int = 0        # architectural variants of the pages (bit flags, see VARIANT_* below)
     precision: int = 0      # arithmetic of the block projections: 0 the model dtype, PRECISION_MXFP8
     embodiments: int = 1    # action encoder / decoder pairs; embodiment 0 is ae_* / ao_*, e >= 1 ae_*_e / ao_*_e
+    ctx_state_len: int = 0  # proprioceptive state rows appended to the condition sequence (0: none)
+    state_dim: int = 64     # width of one (normalised, padded) state vector
 
     @property
     def video_tokens(self) -> int:
@@ -56,7 +58,7 @@ class Workload:
 
     @property
     def ctx_len(self) -> int:
-        return self.ctx_text_len + self.ctx_img_len
+        return self.ctx_text_len + self.ctx_img_len + self.ctx_state_len
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -109,6 +111,8 @@ def global_tensors(w: Workload):
     ]
     if w.ctx_img_len > 0:
         out += [("img_w", (D, C), "normal", 0.02), ("img_b", (D,), "normal", 0.02)]
+    if w.ctx_state_len > 0:
+        out += [("st_w", (D, w.state_dim), "normal", 0.02), ("st_b", (D,), "normal", 0.02)]
     for e in range(1, w.embodiments):
         out += [("ae_w_%d" % e, (D, A), "normal", 0.02), ("ae_b_%d" % e, (D,), "normal", 0.02),
                 ("ao_w_%d" % e, (A, D), "normal", 0.02), ("ao_b_%d" % e, (A,), "normal", 0.02)]
@@ -141,6 +145,8 @@ def input_tensors(w: Workload, n_chunks: int):
     out = [("txt", (w.branches, w.ctx_text_len, w.ctx_in_dim), "normal", 1.0)]
     if w.ctx_img_len > 0:
         out.append(("img", (w.ctx_img_len, w.ctx_in_dim), "normal", 1.0))
+    for c in range(n_chunks if w.ctx_state_len > 0 else 0):   # the observed state of each chunk
+        out.append(("state_%d" % c, (w.ctx_state_len, w.state_dim), "normal", 1.0))
     for c in range(n_chunks):
         out += [
             ("x1_video_%d" % c, (w.video_tokens, w.patch_dim), "normal", 1.0),
@@ -152,7 +158,7 @@ def input_tensors(w: Workload, n_chunks: int):
 
 
 MATRIX_NAMES = frozenset({
-    "t_w1", "t_w2", "t_wp", "pe_w", "ae_w", "txt_w", "img_w", "vo_w", "ao_w",
+    "t_w1", "t_w2", "t_wp", "pe_w", "ae_w", "txt_w", "img_w", "vo_w", "ao_w", "st_w",
     "w_qkv", "w_o", "w_cq", "w_ck", "w_cv", "w_co", "w_ff1", "w_ff2", "w_cki", "w_cvi",
 })
 

@@ -356,3 +356,39 @@ def test_separate_image_attention_pins(tiny):
     wc = w.with_(variant=0)
     vc, ac = _step_with_ctx(wc, O.Model(wc, m.g, m.layers), O.build_context(wc, m.g, txt, img), x1v, x1a, epv, epa)
     assert not np.allclose(v1, vc, rtol=0, atol=1e-4 * np.abs(v1).max())
+
+
+def test_state_rows_in_the_condition_sequence(tiny):
+    """State rows (reading: one encoder Linear, rows appended to the condition sequence): cross
+    attention treats the condition tokens as a set, so moving the state row to the front of the
+    sequence changes nothing beyond rounding; a different observed state changes the step; a
+    sequence whose last text row equals the state row's embedding (text made one row shorter) gives
+    the same result as the state-row model."""
+    _, _, _, _, x1v, x1a, epv, epa = tiny
+    w = WORKLOADS[1].with_(layers=2, ctx_state_len=1)
+    m = O.load_model(w)
+    txt = draw_named(w, -1, "txt")
+    st0, st1 = draw_named(w, -1, "state_0"), draw_named(w, -1, "state_1")
+
+    def step(ctx, ww=w):
+        ckv = [O.context_kv(ww, lp, ctx) for lp in m.layers]
+        cache = O.KVCache.empty(ww.layers, ww.branches, ww.dim)
+        O.kv_append(O.Model(ww, m.g, m.layers), cache, ckv, x1v[0], x1a[0], 0)
+        return O.stack_forward(O.Model(ww, m.g, m.layers), cache, ckv, epv[1], epa[1], [0.4], [0.4], 1,
+                               ww.frames_per_chunk)
+
+    ctx = O.build_context(w, m.g, txt, None, st0)
+    assert ctx.shape == (w.branches, w.ctx_len, w.dim)
+    v0, a0 = step(ctx)
+    front = np.concatenate([ctx[:, -1:], ctx[:, :-1]], axis=1)
+    vf, af = step(front)
+    assert np.allclose(v0, vf, rtol=0, atol=1e-5 * np.abs(v0).max()) and np.allclose(a0, af, rtol=0,
+                                                                                    atol=1e-5 * np.abs(a0).max())
+    v1, _ = step(O.build_context(w, m.g, txt, None, st1))
+    assert not np.allclose(v0, v1, rtol=0, atol=1e-4 * np.abs(v0).max())
+    # the state row is one more condition row: a text-only model with that row in place of its last
+    # text row (text one shorter) is the same computation
+    wt = w.with_(ctx_state_len=0, ctx_text_len=w.ctx_text_len + 1)
+    ctx_t = np.concatenate([ctx[:, :-1], ctx[:, -1:]], axis=1)
+    vt, at = step(ctx_t, wt)
+    assert np.array_equal(v0, vt) and np.array_equal(a0, at)
