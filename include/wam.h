@@ -64,6 +64,8 @@ typedef struct {
   wam_dtype dtype;
   int variant;             /* 0, or WAM_VARIANT_* bits (architectural variants of [ARCH] §2.3) */
   int precision;           /* WAM_PRECISION_NATIVE (0) or WAM_PRECISION_MXFP8 (see below) */
+  int ctx_state_len;       /* proprioceptive state rows at the end of the condition sequence (0: none) */
+  int state_dim;           /* width of one state vector (multiple of 64) when ctx_state_len > 0 */
 } wam_config;
 
 /* Arithmetic of the six block projections (w_qkv, w_o, w_cq, w_co, w_ff1, w_ff2).
@@ -133,6 +135,7 @@ typedef struct {
   const void *img_w, *img_b;                 /* image features -> width (NULL when ctx_img_len = 0) */
   const wam_action_io *embodiments;          /* optional host array [n_embodiments] (see below) */
   int n_embodiments;
+  const void *st_w, *st_b;                   /* state encoder [D][state_dim], [D] (NULL when ctx_state_len = 0) */
 } wam_weights;
 
 /* Routing by embodiment id ([ARCH] §2.4): *out = *w with ae_* / ao_* taken from w->embodiments[id].
@@ -168,12 +171,22 @@ typedef struct {
 size_t wam_workspace_bytes(const wam_config *cfg, int n_chunks);
 
 /* Condition build ([ARCH] §2.1: text and image features concatenated into one condition
- * sequence; §4: encoded once). ctx_b = [txt_b W_txt^T + b ; img W_img^T + b] per branch, then per
- * layer Kc = RMSNorm(ctx Wck^T + b) g_ck and Vc = ctx Wcv^T + b into `out`.
- *   txt: [branches][ctx_text_len][ctx_in_dim] dtype (branch 1 = negative prompt features)
- *   img: [ctx_img_len][ctx_in_dim] dtype, shared by the branches (NULL when ctx_img_len = 0) */
+ * sequence; §4: encoded once). ctx_b = [txt_b W_txt^T + b ; img W_img^T + b ; state W_st^T + b] per
+ * branch, then per layer Kc = RMSNorm(ctx Wck^T + b) g_ck and Vc = ctx Wcv^T + b into `out`.
+ *   txt:   [branches][ctx_text_len][ctx_in_dim] dtype (branch 1 = negative prompt features)
+ *   img:   [ctx_img_len][ctx_in_dim] dtype, shared by the branches (NULL when ctx_img_len = 0)
+ *   state: [ctx_state_len][state_dim] dtype, the observed proprioceptive state shared by the
+ *          branches (NULL when ctx_state_len = 0). The walk-throughs name a state encoder beside the
+ *          text encoder, fused into the DiT; here it is one Linear whose rows join the condition
+ *          sequence after the image rows. */
 wam_status wam_ctx_build(const wam_config *cfg, const wam_weights *w, const void *txt, const void *img,
-                         wam_ctx_kv *out, void *ws, size_t ws_bytes, void *stream);
+                         const void *state, wam_ctx_kv *out, void *ws, size_t ws_bytes, void *stream);
+
+/* New observation: recompute only the state rows of every layer's condition keys / values (the
+ * text and image rows built by wam_ctx_build are kept). state as in wam_ctx_build. Errors:
+ * WAM_E_ARG / WAM_E_SHAPE (no state rows configured), nothing launched. */
+wam_status wam_ctx_set_state(const wam_config *cfg, const wam_weights *w, const void *state, wam_ctx_kv *ctx,
+                             void *ws, size_t ws_bytes, void *stream);
 
 /* Shared time modulation for `n` timesteps t[0..n) (host floats, n <= 16): e [n][D] and
  * e6 [n][6][D] (device float). [ARCH] §2.3: sinusoidal time embedding; the modulation's shift and

@@ -158,6 +158,24 @@ def test_image_cross_attention_validation():
     assert lib.wam_workspace_bytes(ctypes.byref(c), 1) > 0
 
 
+def test_state_rows_validation():
+    """State rows: state_dim a multiple of 64, no combination with the separate image attention,
+    and wam_ctx_set_state refused without state rows (checked before anything runs)."""
+    lib = _lib()
+    from world_action_video_amd.device import make_config
+    c = make_config(WORKLOADS[1].with_(ctx_state_len=1), "f32")
+    assert lib.wam_workspace_bytes(ctypes.byref(c), 1) > 0
+    c = make_config(WORKLOADS[1].with_(ctx_state_len=1, state_dim=40), "f32")
+    assert lib.wam_workspace_bytes(ctypes.byref(c), 1) == 0 and "state_dim" in wam.wam_last_error()
+    c = make_config(WORKLOADS[1].with_(ctx_state_len=1, ctx_img_len=16, variant=8), "f32")
+    assert lib.wam_workspace_bytes(ctypes.byref(c), 1) == 0 and "state rows" in wam.wam_last_error()
+    c = make_config(WORKLOADS[1], "f32")
+    w = wam.wam_weights()
+    cx = wam.wam_ctx_kv(0x1000, 0x1000, 2, 32, 64)
+    assert lib.wam_ctx_set_state(ctypes.byref(c), ctypes.byref(w), 0x1000, ctypes.byref(cx), 0x1000, 1 << 30,
+                                 None) == wam.WAM_E_SHAPE
+
+
 def test_embodiment_routing_is_host_only():
     """wam_weights_for_embodiment swaps the action encoder / decoder pointers and nothing else."""
     _lib()

@@ -33,8 +33,10 @@ class Rig:
         self.txt = draw_named(w, -1, "txt")
         self.img = draw_named(w, -1, "img") if w.ctx_img_len else None
         self.ctx = DeviceCtx(w, dtype, device)
+        self.state = draw_named(w, -1, "state_0") if w.ctx_state_len else None
         wam.wam_ctx_build(self.m.cfg, self.m.weights, to_device(self.txt, dtype, device),
-                          to_device(self.img, dtype, device) if self.img is not None else None, self.ctx.c, self.ws)
+                          to_device(self.img, dtype, device) if self.img is not None else None, self.ctx.c, self.ws,
+                          state=to_device(self.state, dtype, device) if self.state is not None else None)
 
     def cache(self, chunks=3):
         return DeviceCache(self.w, chunks * self.w.chunk_tokens, self.dtype, self.dev)
@@ -239,6 +241,33 @@ def test_separate_image_attention(gpu, dtype, variant):
     ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
     print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
     assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_rows(gpu, tiny_oracle, dtype):
+    """Proprioceptive state rows in the condition sequence: built with the first observed state, a
+    step against the oracle; then the state rows alone updated to a new observation
+    (wam_ctx_set_state) and the step again, against the oracle rebuilt with the new state."""
+    _, _, _ = tiny_oracle
+    w = WORKLOADS[1].with_(layers=2, ctx_state_len=1)
+    m = O.load_model(w)
+    txt = draw_named(w, -1, "txt")
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    rig = Rig(w, dtype, gpu)
+    for c in (0, 1):
+        st = draw_named(w, -1, "state_%d" % c)
+        if c == 1:
+            wam.wam_ctx_set_state(rig.m.cfg, rig.m.weights, to_device(st, dtype, gpu), rig.ctx.c, rig.ws)
+        ckv = [O.context_kv(w, lp, O.build_context(w, m.g, txt, None, st)) for lp in m.layers]
+        cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+        O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+        ref_v, ref_a = O.stack_forward(m, cache, ckv, epv[1], epa[1], [0.45], [0.45], 1, w.frames_per_chunk)
+        dc = rig.cache()
+        rig.append(dc, x1v[0], x1a[0], 0)
+        gv, ga = rig.step(dc, 1, epv[1], epa[1], [0.45], [0.45], w.frames_per_chunk)
+        ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+        print("state %d %s: rel-L2 video %.3e action %.3e" % (c, dtype, ev, ea), flush=True)
+        assert ev <= TOL[dtype] and ea <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -18,7 +18,7 @@ WAM_BF16, WAM_F32 = 0, 1
 WAM_PRECISION_NATIVE, WAM_PRECISION_MXFP8, WAM_PRECISION_MXFP4W = 0, 1, 2
 WAM_MX_E4M3, WAM_MX_E2M1 = 0, 1
 
-EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
+EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
            "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear",
            "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error")
@@ -36,7 +36,8 @@ class wam_config(ctypes.Structure):
                                              "grid_h", "grid_w", "ctx_in_dim", "ctx_text_len", "ctx_img_len",
                                              "branches")] + \
               [("rope_theta", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int),
-               ("variant", ctypes.c_int), ("precision", ctypes.c_int)]
+               ("variant", ctypes.c_int), ("precision", ctypes.c_int), ("ctx_state_len", ctypes.c_int),
+               ("state_dim", ctypes.c_int)]
 
 
 BLOCK_FIELDS = ("mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "ln3_w", "ln3_b", "w_cq", "b_cq", "g_cq",
@@ -57,7 +58,8 @@ class wam_action_io(ctypes.Structure):
 
 class wam_weights(ctypes.Structure):
     _fields_ = [("blocks", ctypes.POINTER(wam_block_weights))] + [(n, ctypes.c_void_p) for n in GLOBAL_FIELDS] + \
-               [("embodiments", ctypes.POINTER(wam_action_io)), ("n_embodiments", ctypes.c_int)]
+               [("embodiments", ctypes.POINTER(wam_action_io)), ("n_embodiments", ctypes.c_int),
+                ("st_w", ctypes.c_void_p), ("st_b", ctypes.c_void_p)]
 
 
 class wam_kv_cache(ctypes.Structure):
@@ -88,7 +90,8 @@ def load(path: str = LIB_PATH):
     CX = ctypes.POINTER(wam_ctx_kv)
     sig = {
         "wam_workspace_bytes": (S, [CFG, I]),
-        "wam_ctx_build": (I, [CFG, W, P, P, CX, P, S, P]),
+        "wam_ctx_build": (I, [CFG, W, P, P, P, CX, P, S, P]),
+        "wam_ctx_set_state": (I, [CFG, W, P, CX, P, S, P]),
         "wam_time_embed": (I, [CFG, W, P, I, P, P, P, S, P]),
         "wam_dit_stack_fwd": (I, [CFG, W, KV, CX, I, P, P, P, P, I, P, P, P, S, P]),
         "wam_kv_append": (I, [CFG, W, KV, CX, P, P, I, P, S, P]),
@@ -147,9 +150,14 @@ def wam_workspace_bytes(cfg: wam_config, n_chunks: int) -> int:
     return int(load().wam_workspace_bytes(ctypes.byref(cfg), n_chunks))
 
 
-def wam_ctx_build(cfg, w, txt, img, ctx: wam_ctx_kv, ws, stream=None):
-    _check(load().wam_ctx_build(ctypes.byref(cfg), ctypes.byref(w), _ptr(txt), _ptr(img), ctypes.byref(ctx),
-                                _ptr(ws), _nbytes(ws), _stream(stream)))
+def wam_ctx_set_state(cfg, w, state, ctx: wam_ctx_kv, ws, stream=None):
+    _check(load().wam_ctx_set_state(ctypes.byref(cfg), ctypes.byref(w), _ptr(state), ctypes.byref(ctx), _ptr(ws),
+                                    _nbytes(ws), _stream(stream)))
+
+
+def wam_ctx_build(cfg, w, txt, img, ctx: wam_ctx_kv, ws, stream=None, state=None):
+    _check(load().wam_ctx_build(ctypes.byref(cfg), ctypes.byref(w), _ptr(txt), _ptr(img), _ptr(state),
+                                ctypes.byref(ctx), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def wam_time_embed(cfg, w, t, e, e6, ws, stream=None):

@@ -42,7 +42,8 @@ struct Geo {
   bool mx;     // MXFP8 block projections (activations; weights too unless w4)
   bool w4;     // MXFP4 weights of the block projections
   int F1;      // rows of w_ff1 (2F for the SwiGLU variant)
-  int Lt;      // text rows of the condition sequence (the image rows follow)
+  int Lt;      // text rows of the condition sequence (the image rows follow, then the state rows)
+  int Li, Ls, Sd;   // image rows, state rows, state width
   bool img_x;  // image rows with their own projections and softmax (IMG_XATTN variant)
 };
 
@@ -50,7 +51,9 @@ Geo geo_of(const wam_config& c) {
   Geo g;
   g.D = c.dim; g.H = c.heads; g.d = c.head_dim; g.F = c.ffn_dim; g.L = c.layers; g.P = c.patch_dim;
   g.A = c.action_dim; g.La = c.action_tokens; g.Lv = c.frames_per_chunk * c.grid_h * c.grid_w;
-  g.Lq = g.Lv + g.La; g.Lc = c.ctx_text_len + c.ctx_img_len; g.Cin = c.ctx_in_dim; g.br = c.branches;
+  g.Lq = g.Lv + g.La; g.Lc = c.ctx_text_len + c.ctx_img_len + c.ctx_state_len; g.Cin = c.ctx_in_dim;
+  g.br = c.branches;
+  g.Li = c.ctx_img_len; g.Ls = c.ctx_state_len; g.Sd = c.state_dim;
   g.freq = c.freq_dim;
   g.dt = c.dtype == WAM_BF16 ? DT_BF16 : DT_F32;
   g.esz = c.dtype == WAM_BF16 ? 2 : 4;
@@ -106,6 +109,11 @@ wam_status check_cfg(const wam_config* c) {
     return fail(WAM_E_UNSUPPORTED, "unknown variant bits 0x%x", c->variant);
   if ((c->variant & WAM_VARIANT_IMG_XATTN) && (c->ctx_img_len <= 0 || c->ctx_text_len % 8))
     return fail(WAM_E_SHAPE, "separate image cross-attention needs image tokens and ctx_text_len a multiple of 8");
+  if (c->ctx_state_len < 0 || c->ctx_state_len > 64) return fail(WAM_E_SHAPE, "ctx_state_len must be in [0, 64]");
+  if (c->ctx_state_len > 0 && (c->state_dim <= 0 || c->state_dim % 64 || c->state_dim > 4096))
+    return fail(WAM_E_SHAPE, "state_dim must be a positive multiple of 64 (at most 4096)");
+  if (c->ctx_state_len > 0 && (c->variant & WAM_VARIANT_IMG_XATTN))
+    return fail(WAM_E_UNSUPPORTED, "state rows and the separate image cross-attention are not combined");
   if (c->precision != WAM_PRECISION_NATIVE && c->precision != WAM_PRECISION_MXFP8 &&
       c->precision != WAM_PRECISION_MXFP4W)
     return fail(WAM_E_UNSUPPORTED, "unknown precision %d", c->precision);
@@ -194,6 +202,8 @@ wam_status check_weights(const wam_config* c, const wam_weights* w, bool need_bl
   for (const void* q : {w->t_w1, w->t_b1, w->t_w2, w->t_b2, w->t_wp, w->t_bp, w->pe_w, w->pe_b, w->ae_w, w->ae_b,
                         w->head_mod, w->vo_w, w->vo_b, w->ao_w, w->ao_b})
     if (unaligned16(q)) return fail(WAM_E_ARG, "a global weight tensor is not 16-byte aligned");
+  if (c->ctx_state_len > 0 && (!w->st_w || !w->st_b || unaligned16(w->st_w) || unaligned16(w->st_b)))
+    return fail(WAM_E_ARG, "state encoder weights are NULL or not 16-byte aligned");
   if (need_blocks) {
     if (!w->blocks) return fail(WAM_E_ARG, "blocks array is NULL");
     for (int l = 0; l < c->layers; ++l) {
@@ -223,7 +233,7 @@ wam_status check_ctx(const Geo& g, const wam_ctx_kv* cx) {
   if (cx->ctx_len != g.Lc) return fail(WAM_E_SHAPE, "condition length %d != %d", cx->ctx_len, g.Lc);
   if (cx->ctx_stride < g.Lc || cx->ctx_stride % 64) return fail(WAM_E_SHAPE, "ctx_stride must be a multiple of 64 >= ctx_len");
   // the image attention reads whole 32-key tiles of value rows that start at column Lt
-  if (g.img_x && cx->ctx_stride < g.Lt + (g.Lc - g.Lt + 31) / 32 * 32)
+  if (g.img_x && cx->ctx_stride < g.Lt + (g.Li + 31) / 32 * 32)
     return fail(WAM_E_SHAPE, "ctx_stride must hold ctx_text_len + ctx_img_len rounded up to 32");
   return WAM_OK;
 }
@@ -399,7 +409,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     if (!g.img_x) {
       HIP_TRY(launch_attention(ca, dt, p.s));
     } else {   // text rows and image rows, each with its own softmax; the outputs are summed
-      const int Li = g.Lc - g.Lt;
+      const int Li = g.Li;
       ca.kv_base = ca.kv_total = g.Lt;
       HIP_TRY(launch_attention(ca, dt, p.s));
       AttnArgs ci = ca;
@@ -539,14 +549,15 @@ size_t wam_workspace_bytes(const wam_config* cfg, int n_chunks) {
   return layout_of(geo_of(*cfg), n_chunks).total;
 }
 
-wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void* txt, const void* img, wam_ctx_kv* out,
-                         void* ws, size_t ws_bytes, void* stream) {
+wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void* txt, const void* img,
+                         const void* state, wam_ctx_kv* out, void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_cfg(cfg));
   const Geo g = geo_of(*cfg);
   CHECK(check_weights(cfg, w, true));
   CHECK(check_ctx(g, out));
   if (!txt || !w->txt_w || !w->txt_b) return fail(WAM_E_ARG, "text features or text projection are NULL");
   if (cfg->ctx_img_len > 0 && (!img || !w->img_w || !w->img_b)) return fail(WAM_E_ARG, "image features or projection are NULL");
+  if (cfg->ctx_state_len > 0 && (!state || unaligned16(state))) return fail(WAM_E_ARG, "state is NULL or not 16-byte aligned");
   const Layout L = layout_of(g, 1);
   CHECK(check_ws(L, ws, ws_bytes));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -564,6 +575,11 @@ wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void
       GemmArgs gi = gemm_args(img, g.Cin, w->img_w, g.Cin, w->img_b, Li, g.D, g.Cin, part, part_n);
       gi.C = reinterpret_cast<char*>(ctx) + ((size_t)b * g.Lc + Lt) * g.D * g.esz; gi.ldc = g.D;
       HIP_TRY(launch_gemm(gi, g.dt, EPI_STORE, s));
+    }
+    if (g.Ls > 0) {   // state rows after the image rows
+      GemmArgs gs = gemm_args(state, g.Sd, w->st_w, g.Sd, w->st_b, g.Ls, g.D, g.Sd, part, part_n);
+      gs.C = reinterpret_cast<char*>(ctx) + ((size_t)b * g.Lc + Lt + Li) * g.D * g.esz; gs.ldc = g.D;
+      HIP_TRY(launch_gemm(gs, g.dt, EPI_STORE, s));
     }
   }
   const int M = g.br * g.Lc;
@@ -588,7 +604,7 @@ wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void
     va.rows_per_branch = g.Lc; va.br = g.br; va.H = g.H; va.d = g.d;
     HIP_TRY(launch_v_to_cache(va, g.dt, s));
     if (g.img_x) {   // image rows of each branch again, with the image projections and gain
-      const int Li = g.Lc - g.Lt;
+      const int Li = g.Li;
       for (int b = 0; b < g.br; ++b) {
         const char* src = reinterpret_cast<const char*>(ctx) + ((size_t)b * g.Lc + g.Lt) * g.D * g.esz;
         GemmArgs ik = gemm_args(src, g.D, bw.w_cki, g.D, bw.b_cki, Li, g.D, g.D, part, part_n);
@@ -607,6 +623,55 @@ wam_status wam_ctx_build(const wam_config* cfg, const wam_weights* w, const void
         ia.dst_col0 = g.Lt; ia.rows_per_branch = Li; ia.br = 1;
         HIP_TRY(launch_v_to_cache(ia, g.dt, s));
       }
+    }
+  }
+  return WAM_OK;
+}
+
+wam_status wam_ctx_set_state(const wam_config* cfg, const wam_weights* w, const void* state, wam_ctx_kv* ctx,
+                             void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  const Geo g = geo_of(*cfg);
+  if (g.Ls <= 0) return fail(WAM_E_SHAPE, "the configuration has no state rows (ctx_state_len = 0)");
+  CHECK(check_weights(cfg, w, true));
+  CHECK(check_ctx(g, ctx));
+  if (!state || unaligned16(state)) return fail(WAM_E_ARG, "state is NULL or not 16-byte aligned");
+  const Layout L = layout_of(g, 1);
+  CHECK(check_ws(L, ws, ws_bytes));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* emb = at<void>(ws, L.ctx_a);   // [Ls][D]
+  void* tmp = at<void>(ws, L.ctx_b);   // [Ls][D]
+  float* part = at<float>(ws, L.part);
+  const long part_n = L.part_elems;
+  GemmArgs gs = gemm_args(state, g.Sd, w->st_w, g.Sd, w->st_b, g.Ls, g.D, g.Sd, part, part_n);
+  gs.C = emb; gs.ldc = g.D;
+  HIP_TRY(launch_gemm(gs, g.dt, EPI_STORE, s));
+  const int row0 = g.Lt + g.Li;
+  const size_t ck_layer = (size_t)g.br * g.H * g.Lc * g.d, cv_layer = (size_t)g.br * g.H * g.d * ctx->ctx_stride;
+  for (int l = 0; l < g.L; ++l) {   // the rows are the same for both branches: project once, write per branch
+    const wam_block_weights& bw = w->blocks[l];
+    GemmArgs gk = gemm_args(emb, g.D, bw.w_ck, g.D, bw.b_ck, g.Ls, g.D, g.D, part, part_n);
+    gk.C = tmp; gk.ldc = g.D;
+    HIP_TRY(launch_gemm(gk, g.dt, EPI_STORE, s));
+    for (int b = 0; b < g.br; ++b) {
+      QkNormArgs qa{};
+      qa.src = tmp; qa.src_ld = g.D; qa.src_col = 0; qa.gain = reinterpret_cast<const float*>(bw.g_ck);
+      qa.dst = layer_ptr<char>(ctx->k, ck_layer, l, g.esz) + (size_t)b * g.H * g.Lc * g.d * g.esz;
+      qa.dst_bh_stride = (long)g.Lc * g.d; qa.dst_row0 = row0;
+      qa.M = g.Ls; qa.D = g.D; qa.H = g.H; qa.d = g.d; qa.rows_per_branch = g.Ls; qa.eps = cfg->eps; qa.rope = nullptr;
+      qa.rm = RowMap{g.Ls, g.Ls, g.Ls};
+      HIP_TRY(launch_qk_norm_rope(qa, g.dt, s));
+    }
+    GemmArgs gv = gemm_args(emb, g.D, bw.w_cv, g.D, bw.b_cv, g.Ls, g.D, g.D, part, part_n);
+    gv.C = tmp; gv.ldc = g.D;
+    HIP_TRY(launch_gemm(gv, g.dt, EPI_STORE, s));
+    for (int b = 0; b < g.br; ++b) {
+      VCacheArgs va{};
+      va.src = tmp; va.src_ld = g.D; va.src_col = 0;
+      va.dst = layer_ptr<char>(ctx->v, cv_layer, l, g.esz) + (size_t)b * g.H * g.d * ctx->ctx_stride * g.esz;
+      va.dst_bh_stride = (long)g.d * ctx->ctx_stride; va.dst_stride = ctx->ctx_stride; va.dst_col0 = row0;
+      va.rows_per_branch = g.Ls; va.br = 1; va.H = g.H; va.d = g.d;
+      HIP_TRY(launch_v_to_cache(va, g.dt, s));
     }
   }
   return WAM_OK;

@@ -30,6 +30,8 @@ def make_config(w: Workload, dtype: str = "bf16", branches: int | None = None) -
     c.dtype = WAM_BF16 if dtype == "bf16" else WAM_F32
     c.variant = int(w.variant)
     c.precision = int(w.precision)
+    c.ctx_state_len = int(w.ctx_state_len)
+    c.state_dim = int(w.state_dim)
     return c
 
 
@@ -103,6 +105,9 @@ class DeviceModel:
         self.weights = wam_weights()
         self.weights.blocks = ctypes.cast(self.blocks, ctypes.POINTER(wam_block_weights))
         for name in GLOBAL_FIELDS:
+            t = self.g.get(name)
+            setattr(self.weights, name, t.data_ptr() if t is not None else None)
+        for name in ("st_w", "st_b"):
             t = self.g.get(name)
             setattr(self.weights, name, t.data_ptr() if t is not None else None)
         E = self.w.embodiments
