@@ -249,9 +249,11 @@ def build_context(w, g: Dict[str, Array], txt: Array, img: Optional[Array], stat
     [ARCH] §2.1: image and text features (1536-d) are concatenated into one condition sequence;
     reading R12: one Linear per modality to the model width. Branch 1 carries the negative
     (null) prompt ([WS1] request format); the image features are shared by both branches.
-    State rows (reading R23): the walk-throughs name a state encoder next to the text encoder
-    whose output is fused into the DiT; here each proprioceptive state vector [state_dim] goes
-    through its own Linear to one condition row after the image rows, shared by the branches.
+    State rows: [HYPER] 方法 has proprioception pass a state encoder beside the text encoder
+    before the modalities are fused into the causal DiT, and [N569] (architecture) counts that
+    encoder among the few parameters added to the backbone. Here each proprioceptive feature
+    vector [state_dim] goes through one Linear to one condition row after the image rows, shared
+    by the branches; any featurisation of joint readings before it is the caller's.
     """
     ctx_t = linear(txt, g["txt_w"], g["txt_b"])                   # [br, Lt, D]
     parts = [ctx_t]

@@ -244,12 +244,14 @@ def test_separate_image_attention(gpu, dtype, variant):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_state_rows(gpu, tiny_oracle, dtype):
+@pytest.mark.parametrize("n_state", [1, 3, 6])
+def test_state_rows(gpu, tiny_oracle, dtype, n_state):
     """Proprioceptive state rows in the condition sequence: built with the first observed state, a
     step against the oracle; then the state rows alone updated to a new observation
-    (wam_ctx_set_state) and the step again, against the oracle rebuilt with the new state."""
+    (wam_ctx_set_state) and the step again, against the oracle rebuilt with the new state. Up to
+    four rows take the row-parallel product, more the tiled GEMM."""
     _, _, _ = tiny_oracle
-    w = WORKLOADS[1].with_(layers=2, ctx_state_len=1)
+    w = WORKLOADS[1].with_(layers=2, ctx_state_len=n_state)
     m = O.load_model(w)
     txt = draw_named(w, -1, "txt")
     x1v, x1a, epv, epa = tiny_inputs(w)
@@ -266,7 +268,7 @@ def test_state_rows(gpu, tiny_oracle, dtype):
         rig.append(dc, x1v[0], x1a[0], 0)
         gv, ga = rig.step(dc, 1, epv[1], epa[1], [0.45], [0.45], w.frames_per_chunk)
         ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
-        print("state %d %s: rel-L2 video %.3e action %.3e" % (c, dtype, ev, ea), flush=True)
+        print("state %d x%d %s: rel-L2 video %.3e action %.3e" % (c, n_state, dtype, ev, ea), flush=True)
         assert ev <= TOL[dtype] and ea <= TOL[dtype]
 
 

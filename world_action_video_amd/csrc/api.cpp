@@ -643,16 +643,20 @@ wam_status wam_ctx_set_state(const wam_config* cfg, const wam_weights* w, const 
   void* tmp = at<void>(ws, L.ctx_b);   // [Ls][D]
   float* part = at<float>(ws, L.part);
   const long part_n = L.part_elems;
-  GemmArgs gs = gemm_args(state, g.Sd, w->st_w, g.Sd, w->st_b, g.Ls, g.D, g.Sd, part, part_n);
-  gs.C = emb; gs.ldc = g.D;
-  HIP_TRY(launch_gemm(gs, g.dt, EPI_STORE, s));
+  // a few rows: each projection as a row-parallel product over N / 32 workgroups
+  const bool gemv = g.Ls <= 4;
+  auto project = [&](const void* x, const void* W, const void* b, int K, void* y) -> hipError_t {
+    if (gemv) return launch_gemv_store(W, reinterpret_cast<const float*>(b), x, K, y, g.D, g.Ls, g.D, K, g.dt, s);
+    GemmArgs ga = gemm_args(x, K, W, K, b, g.Ls, g.D, K, part, part_n);
+    ga.C = y; ga.ldc = g.D;
+    return launch_gemm(ga, g.dt, EPI_STORE, s);
+  };
+  HIP_TRY(project(state, w->st_w, w->st_b, g.Sd, emb));
   const int row0 = g.Lt + g.Li;
   const size_t ck_layer = (size_t)g.br * g.H * g.Lc * g.d, cv_layer = (size_t)g.br * g.H * g.d * ctx->ctx_stride;
   for (int l = 0; l < g.L; ++l) {   // the rows are the same for both branches: project once, write per branch
     const wam_block_weights& bw = w->blocks[l];
-    GemmArgs gk = gemm_args(emb, g.D, bw.w_ck, g.D, bw.b_ck, g.Ls, g.D, g.D, part, part_n);
-    gk.C = tmp; gk.ldc = g.D;
-    HIP_TRY(launch_gemm(gk, g.dt, EPI_STORE, s));
+    HIP_TRY(project(emb, bw.w_ck, bw.b_ck, g.D, tmp));
     for (int b = 0; b < g.br; ++b) {
       QkNormArgs qa{};
       qa.src = tmp; qa.src_ld = g.D; qa.src_col = 0; qa.gain = reinterpret_cast<const float*>(bw.g_ck);
@@ -662,9 +666,7 @@ wam_status wam_ctx_set_state(const wam_config* cfg, const wam_weights* w, const 
       qa.rm = RowMap{g.Ls, g.Ls, g.Ls};
       HIP_TRY(launch_qk_norm_rope(qa, g.dt, s));
     }
-    GemmArgs gv = gemm_args(emb, g.D, bw.w_cv, g.D, bw.b_cv, g.Ls, g.D, g.D, part, part_n);
-    gv.C = tmp; gv.ldc = g.D;
-    HIP_TRY(launch_gemm(gv, g.dt, EPI_STORE, s));
+    HIP_TRY(project(emb, bw.w_cv, bw.b_cv, g.D, tmp));
     for (int b = 0; b < g.br; ++b) {
       VCacheArgs va{};
       va.src = tmp; va.src_ld = g.D; va.src_col = 0;

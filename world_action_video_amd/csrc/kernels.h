@@ -119,6 +119,10 @@ struct NormArgs {
   uint8_t* mxs;         //   (D % 32 == 0), quantised from the stored bf16 values
 };
 hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s);
+// y[g][n] = x[g] . W[n] + bias[n] for g < G <= 4 rows (storage type in and out, fp32 sums; bias may be
+// NULL); K and ldx multiples of 16 bytes' worth of elements, 16-byte aligned W and x.
+hipError_t launch_gemv_store(const void* W, const float* bias, const void* x, long ldx, void* y, long ldy, int G, int N,
+                             int K, DType dt, hipStream_t s);
 // dst[i] += src[i] for i < n (elements of the storage type; n % 8 == 0, 16-byte aligned pointers)
 hipError_t launch_add(void* dst, const void* src, long n, DType dt, hipStream_t s);
 

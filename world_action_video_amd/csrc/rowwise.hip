@@ -702,6 +702,72 @@ __global__ void __launch_bounds__(256) gemv_rows_kernel(const T* W, const float*
   }
 }
 
+// y[g][n] = sum_k x[g][k] W[n][k] + bias[n] for a few rows g < G of x, in the storage type: the one-row
+// products of a state update spread over N / 32 workgroups instead of a handful of GEMM tiles.
+template <typename T, int G, int NR>
+__global__ void __launch_bounds__(256) gemv_store_kernel(const T* W, const float* bias, const T* x, long ldx, T* y,
+                                                         long ldy, int N, int K) {
+  constexpr int EPU = 16 / sizeof(T);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * NR;
+  if (n0 >= N) return;
+  float acc[NR][G];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[r][g] = 0.f;
+  for (int k0 = lane * EPU; k0 < K; k0 += 64 * EPU) {
+    float xv[G][EPU];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(x + (long)g * ldx + k0);
+      const T* xe = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) xv[g][e] = Elem<T>::to_f(xe[e]);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (n0 + r >= N) break;
+      const uint4 raw = *reinterpret_cast<const uint4*>(W + (long)(n0 + r) * K + k0);
+      const T* we = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        const float wv = Elem<T>::to_f(we[e]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[r][g] += wv * xv[g][e];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float v = wave_sum(acc[r][g]);
+      if (lane == 0 && n0 + r < N) Elem<T>::store(y + (long)g * ldy + n0 + r, v + (bias ? bias[n0 + r] : 0.f));
+    }
+  }
+}
+
+hipError_t launch_gemv_store(const void* W, const float* bias, const void* x, long ldx, void* y, long ldy, int G, int N,
+                             int K, DType dt, hipStream_t s) {
+  if (G <= 0 || N <= 0) return hipSuccess;
+  const int epu = dt == DT_BF16 ? 8 : 4;
+  if (G > 4 || K % epu || ldx % epu || reinterpret_cast<uintptr_t>(W) % 16 || reinterpret_cast<uintptr_t>(x) % 16)
+    return hipErrorInvalidValue;
+  constexpr int NR = 2;
+  const dim3 grid((N + 4 * NR - 1) / (4 * NR)), block(256);
+#define WAM_GEMV(T, GG)                                                                                         \
+  hipLaunchKernelGGL((gemv_store_kernel<T, GG, NR>), grid, block, 0, s, reinterpret_cast<const T*>(W), bias,  \
+                     reinterpret_cast<const T*>(x), ldx, reinterpret_cast<T*>(y), ldy, N, K)
+  if (dt == DT_BF16) {
+    if (G == 1) WAM_GEMV(bf16_t, 1); else if (G == 2) WAM_GEMV(bf16_t, 2); else if (G == 3) WAM_GEMV(bf16_t, 3); else WAM_GEMV(bf16_t, 4);
+  } else {
+    if (G == 1) WAM_GEMV(float, 1); else if (G == 2) WAM_GEMV(float, 2); else if (G == 3) WAM_GEMV(float, 3); else WAM_GEMV(float, 4);
+  }
+#undef WAM_GEMV
+  return hipGetLastError();
+}
+
 template <typename T>
 static void launch_gemv(const void* W, const float* b, const float* x, float* y, int N, int K, int G, int si, int so,
                         hipStream_t s) {
