@@ -157,6 +157,10 @@ def main():
                          "image cross-attention); non-zero values are reported under their own workload name")
     ap.add_argument("--counters", action="store_true",
                     help="run only a 1 GiB copy and launches of the dominant kernel (for rocprofv3 --pmc)")
+    ap.add_argument("--elementwise", action="store_true",
+                    help="HBM-bound kernels: the flow update from the step's size to a >1 GB footprint (buffers "
+                         "rotated through a 1.5 GiB pool, past the 256 MB Infinity Cache) beside a 1 GiB copy, and one "
+                         "config-3 block over 1 and 8 chunks (for a kernel trace of its row kernels)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="turn the two rocprofv3 --pmc databases of a --counters run (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/hbm_traffic.json")
@@ -178,6 +182,9 @@ def main():
     from world_action_video_amd.device import DeviceCache, DeviceCtx, DeviceModel, to_device, workspace
 
     dev = torch.device("cuda:0")
+    if args.elementwise:
+        elementwise(args, dev)
+        return
     if args.workload != WORKLOAD_ID and not args.counters:
         extra_workload(args, dev)
         return
@@ -333,6 +340,112 @@ def main():
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
+
+
+def elementwise(args, dev):
+    """HBM-bound kernels at the step's size and past the Infinity Cache (one JSON line).
+
+    Flow update (guidance + Euler + cosine partials, 2 branches): 24 bytes per latent element (reads x,
+    v_cond, v_uncond, prev; writes x, g). Guidance 1 and dt 0 keep every value bounded while the kernel
+    still moves all of them. "resident" reuses one buffer set per call; "rotated" walks the calls through a
+    1.5 GiB pool so that consecutive calls touch new memory. The copy is torch's device copy of 1 GiB
+    between two rotated pairs (2 GiB moved per call), the practical HBM ceiling next to the 8 TB/s
+    nominal figure. The block pass runs one config-3 block (layer 0) over 1 and 8 chunks: its split-K
+    finishes and q/k/v kernel then see 105 MB and 840 MB footprints, timed per kernel by a trace."""
+    import torch
+
+    import world_action_video_amd as wam
+    from synth.workloads import WORKLOADS, draw_named
+    from world_action_video_amd.device import DeviceCache, DeviceCtx, DeviceModel, to_device, workspace
+
+    def log(msg):
+        print("[bench] %s" % msg, file=sys.stderr, flush=True)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, reps):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    pool_floats = 384 << 20                                  # 1.5 GiB
+    pool = torch.randn(pool_floats, device=dev)
+    na = 192
+    cos = torch.zeros(3, device=dev)
+    fws = torch.empty(32768, dtype=torch.uint8, device=dev)
+    flow = []
+    for nv in (28160, 1 << 20, 1 << 22, 1 << 24, 50 << 20):
+        n = nv + na
+        span = (5 * n + 63) // 64 * 64                       # x, v (2 branches), prev, g
+        sets = max(1, pool_floats // span)
+        nbytes = 24 * n
+
+        base = pool.data_ptr()
+
+        def call(i, rot):
+            # one set: x [nv | na], v [2][nv] then [2][na], prev [nv], g [nv | na] (raw pointers keep the
+            # host side of a call short)
+            o = base + 4 * ((i % sets) * span if rot else 0)
+            x, v, pv, g = o, o + 4 * n, o + 12 * n, o + 16 * n
+            wam.wam_flow_step(x, x + 4 * nv, v, v + 8 * nv, 2, 1.0, nv, na, 0.0, 0.0, g, g + 4 * nv, pv, cos, fws)
+
+        reps = min(4000, max(20, 2 * sets)) if sets > 1 else 10
+        for rot in (False, True):
+            call(0, rot)
+        res = timed(lambda i: call(i, False), 20 if nv > (1 << 22) else 200)
+        rot = timed(lambda i: call(i, True), reps)
+        flow.append({"n": n, "bytes": nbytes, "resident_us": round(res * 1e3, 2),
+                     "resident_GBps": round(nbytes / (res * 1e-3) / 1e9, 1),
+                     "rotated_us": round(rot * 1e3, 2), "rotated_GBps": round(nbytes / (rot * 1e-3) / 1e9, 1),
+                     "rotated_hbm_frac": round(nbytes / (rot * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+        log("flow n=%d: resident %.2f us, rotated %.2f us (%.0f GB/s)" % (n, res * 1e3, rot * 1e3,
+                                                                          nbytes / (rot * 1e-3) / 1e9))
+    del pool
+    torch.cuda.empty_cache()
+    src = [torch.ones(1 << 28, device=dev) for _ in range(2)]
+    dst = [torch.empty(1 << 28, device=dev) for _ in range(2)]
+    dst[0].copy_(src[0])
+    copy_ms = timed(lambda i: dst[i % 2].copy_(src[i % 2]), 20)
+    copy_gbps = 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9
+    log("copy 1 GiB: %.1f us, %.0f GB/s" % (copy_ms * 1e3, copy_gbps))
+    del src, dst
+    torch.cuda.empty_cache()
+
+    w = WORKLOADS[WORKLOAD_ID].with_(layers=1)
+    Lq = w.chunk_tokens
+    model = DeviceModel(w, "bf16", dev)
+    ctx = DeviceCtx(w, "bf16", dev)
+    blocks = {}
+    n_max = 8
+    ws = workspace(model.cfg, n_max, dev)
+    img = draw_named(w, -1, "img")
+    wam.wam_ctx_build(model.cfg, model.weights, to_device(draw_named(w, -1, "txt"), "bf16", dev),
+                      to_device(img, "bf16", dev), ctx.c, ws)
+    cache = DeviceCache(w, (w.cache_chunks + n_max) * Lq, "bf16", dev)
+    f32 = lambda a: torch.from_numpy(a.astype("float32")).to(dev)  # noqa: E731
+    for c in range(w.cache_chunks):
+        wam.wam_kv_append(model.cfg, model.weights, cache.c, ctx.c, f32(draw_named(w, -1, "x1_video_%d" % c)),
+                          f32(draw_named(w, -1, "x1_action_%d" % c)), c * w.frames_per_chunk, ws)
+    for n_chunks in (1, n_max):
+        h = torch.randn((w.branches, n_chunks * Lq, w.dim), device=dev)
+        e = torch.empty((2 * n_chunks, w.dim), device=dev)
+        e6 = torch.empty((2 * n_chunks, 6, w.dim), device=dev)
+        wam.wam_time_embed(model.cfg, model.weights, [0.4] * (2 * n_chunks), e, e6, ws)
+        run = lambda i: wam.wam_dit_block_fwd(model.cfg, model.blocks[0], 0, cache.c, ctx.c, h, e6, n_chunks,  # noqa
+                                              w.cache_chunks * w.frames_per_chunk, ws)
+        run(0)
+        blocks["chunks_%d" % n_chunks] = round(timed(run, 3), 3)
+        log("block over %d chunk(s): %.3f ms" % (n_chunks, blocks["chunks_%d" % n_chunks]))
+    print(json.dumps({"metric": "HBM-bound kernels (flow update sweep, 1 GiB copy, block passes)",
+                      "unit": "GB/s", "n_gpus": 1, "dtype": "f32", "data": "synthetic",
+                      "config": {"workload": "flow update 2 branches, 24 B per element; config-3 block over 1 and 8 chunks"},
+                      "hbm_peak_GBps": PEAK_HBM_GBS, "copy_1GiB_GBps": round(copy_gbps, 1),
+                      "copy_frac": round(copy_gbps / PEAK_HBM_GBS, 3), "flow": flow, "block_ms": blocks}))
 
 
 def extra_workload(args, dev):

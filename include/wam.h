@@ -235,8 +235,10 @@ wam_status wam_dit_block_fwd(const wam_config *cfg, const wam_block_weights *bw,
  *   x_video += dt_video * g_video; x_action += dt_action * g_action
  *   g_video / g_action (optional, may be NULL): the guided velocities; g_video may alias prev_video
  *   prev_video (optional): if given, cos_parts[0..3) = (<g,prev>, |g|^2, |prev|^2) over the video
- *   part, fp32 partial sums in a fixed order (deterministic). cos_parts is device memory.
- * Needs wam_workspace_bytes(cfg, 1) of workspace (only a few hundred bytes are used). */
+ *   part, fp32 partial sums in a fixed order for given sizes (deterministic). cos_parts is device
+ *   memory.
+ * With prev_video, ws must hold 12 * min(512, max(1, ceil((n_video + n_action) / 4096))) bytes
+ * (at most 6 KB; wam_workspace_bytes(cfg, 1) always suffices), else WAM_E_ARG. */
 wam_status wam_flow_step(float *x_video, float *x_action, const float *v_video, const float *v_action, int branches,
                          float guidance, int n_video, int n_action, float dt_video, float dt_action,
                          float *g_video, float *g_action, const float *prev_video, float *cos_parts, void *ws,

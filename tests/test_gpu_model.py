@@ -496,8 +496,10 @@ def test_denoise_chunk_unipc_matches_oracle(gpu, tiny_oracle, dtype, order, corr
     assert ev <= TOL[dtype] and ea <= TOL[dtype]
 
 
-def test_flow_step_matches_oracle(gpu):
-    nv, na = 28160, 192
+@pytest.mark.parametrize("nv,na", [(28160, 192), (28161, 193), (9_000_000, 4096)])
+def test_flow_step_matches_oracle(gpu, nv, na):
+    """The config-3 sizes (float4 path), odd sizes (scalar path) and a large latent whose grid reaches
+    the 512-workgroup limit."""
     rng = synth.tensor_key(101, 0, "flow")
     v = synth.fill((2, nv + na), rng, "normal", 1.0)
     xv = synth.fill((nv,), rng + 1, "normal", 1.0)
@@ -508,7 +510,7 @@ def test_flow_step_matches_oracle(gpu):
     Xv, Xa, Prev = d(xv), d(xa), d(prev)
     Gv, Ga = torch.empty(nv, device=gpu), torch.empty(na, device=gpu)
     cos = torch.empty(3, device=gpu)
-    ws = torch.empty(4096, dtype=torch.uint8, device=gpu)
+    ws = torch.empty(32768, dtype=torch.uint8, device=gpu)
     wam.wam_flow_step(Xv, Xa, d(vv), d(va), 2, 5.0, nv, na, 1 / 16, 0.25, Gv, Ga, Prev, cos, ws)
     torch.cuda.synchronize()
     gv = O.cfg_combine(vv, 5.0)

@@ -744,13 +744,14 @@ wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, 
   if (prev_video && !cos_parts) return fail(WAM_E_ARG, "prev_video given without cos_parts");
   if (!std::isfinite(guidance) || !std::isfinite(dt_video) || !std::isfinite(dt_action))
     return fail(WAM_E_ARG, "non-finite scalar");
-  const size_t need = 256 + 64 * 3 * 4;
+  const int nblocks = flow_partial_blocks(n_video, n_action);
+  const size_t need = (size_t)nblocks * 3 * 4;
   if (prev_video && (!ws || ws_bytes < need)) return fail(WAM_E_ARG, "workspace too small for the cosine partials");
   FlowArgs fa{};
   fa.xv = x_video; fa.xa = x_action; fa.vv = v_video; fa.va = v_action; fa.br = branches; fa.w = guidance;
   fa.nv = n_video; fa.na = n_action; fa.dtv = dt_video; fa.dta = dt_action; fa.gv = g_video; fa.ga = g_action;
   fa.prev = prev_video; fa.partials = prev_video ? reinterpret_cast<float*>(ws) : nullptr; fa.cos_parts = cos_parts;
-  fa.nblocks = flow_partial_blocks(n_video);
+  fa.nblocks = nblocks;
   HIP_TRY(launch_flow_step(fa, reinterpret_cast<hipStream_t>(stream)));
   return WAM_OK;
 }

@@ -247,6 +247,7 @@ struct HeadArgs {
   float* part; int splits;
 };
 hipError_t launch_head(const HeadArgs& a, DType dt, hipStream_t s);
-int flow_partial_blocks(int nv);
+// workgroups (and [3] partial-sum slots) of the flow step for these sizes: 1 .. 512
+int flow_partial_blocks(int nv, int na);
 
 }  // namespace wam
