@@ -106,8 +106,8 @@ def summarize_counters(fetch_db: str, write_db: str):
 
 def cpu_baseline(w, timed_layers: int = 1) -> dict:
     """The oracle as it stands, timed on this host on a bounded sample: ``timed_layers`` full-width
-    blocks of the same step (both CFG branches, 928 cached + 464 current tokens, 769 condition tokens),
-    scaled to ms per 40-layer step."""
+    blocks of the workload's step (both CFG branches, its cached, current and condition tokens),
+    scaled to ms per step of all its layers."""
     import numpy as np
     import oracle as O
     import synth
@@ -133,11 +133,13 @@ def cpu_baseline(w, timed_layers: int = 1) -> dict:
         h, _, _ = O.block_forward(w, lp, h, e6, ctx_k, ctx_v, ck, cv, 1, pos)
     dt = time.perf_counter() - t0
     per_layer = dt / timed_layers
-    return {"value": round(per_layer * w.layers * 1e3, 1), "unit": "ms per 40-layer CFG step (extrapolated)",
+    return {"value": round(per_layer * w.layers * 1e3, 1),
+            "unit": "ms per %d-layer CFG step (extrapolated)" % w.layers if w.layers > 1 else "ms per block",
             "cores": int(threads), "kind": "oracle",
-            "sample": "%d full-width block(s) of the step (CFG batch 2, 928 cached + 464 current tokens, 769 "
+            "sample": "%d full-width block(s) of the step (CFG batch %d, %d cached + %d current tokens, %d "
                       "condition tokens), NumPy fp32, %.2f s per block, scaled x%d layers; time MLP and heads "
-                      "(<0.1%% of FLOPs) not timed" % (timed_layers, per_layer, w.layers)}
+                      "(<0.1%% of FLOPs) not timed" % (timed_layers, br, w.cache_chunks * Lq, Lq, w.ctx_len,
+                                                       per_layer, w.layers)}
 
 
 def main():
@@ -508,6 +510,9 @@ def extra_workload(args, dev):
             res["br%d" % br] = round(a.elapsed_time(b) / args.steps, 3)
         out = dict(base, metric="ms per DiT block", value=res["br2"], unit="ms", higher_is_better=False,
                    ms_per_block={"cfg_batch_2": res["br2"], "B_1": res["br1"]})
+        if not args.no_cpu_baseline:
+            log("timing the oracle on the host")
+            out["cpu_baseline"] = cpu_baseline(w.with_(layers=1))
         print(json.dumps(out))
         return
 
@@ -551,6 +556,14 @@ def extra_workload(args, dev):
         out = dict(base, metric="ms per chunk (16 Euler steps + KV append)", value=round(sum(times) / 4, 2), unit="ms",
                    higher_is_better=False, per_chunk_ms=times, total_ms=round(sum(times), 1), dit_calls=calls,
                    cache_rows_final=cache.length, outputs_finite=finite)
+        if not args.no_cpu_baseline:
+            log("timing the oracle on the host")
+            cb = cpu_baseline(w)
+            cb["sample"] += ("; one chunk extrapolated as 17 steps at the first chunk's cache (16 DiT calls plus "
+                             "the append's pass), not run")
+            cb["value"] = round(cb["value"] * 17, 1)
+            cb["unit"] = "ms per chunk (extrapolated)"
+            out["cpu_baseline"] = cb
         print(json.dumps(out))
         return
 
@@ -583,6 +596,9 @@ def extra_workload(args, dev):
     out = dict(base, metric="ms per DiT denoise step (40L, CFG b=2, 8064 cached tokens)", value=round(step_ms, 3),
                unit="ms", higher_is_better=False, loop_16_steps_ms=round(loop_ms, 1), dit_calls=n,
                reused_steps=[k for k, f in enumerate(flags) if f], cached_tokens=cache.length, outputs_finite=finite)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
 
 
