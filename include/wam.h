@@ -372,6 +372,19 @@ void wam_kv_reset(wam_kv_cache *cache);
 /* Text of the last non-OK status returned on this thread (empty string if none). */
 const char *wam_last_error(void);
 
+/* Measurement hook for the QKV projection (the largest product of a block): while enabled, every
+ * pass that runs block `layer` with full q/k/v records a HIP event pair around that product on its
+ * stream, up to `max_samples` pairs (1..4096, else WAM_E_ARG). layer < 0 disables and frees the
+ * events. The events are created on the current device, which the timed passes must use. One
+ * process-wide timer, not thread-safe. Events are host-side objects: no device memory is
+ * allocated. */
+wam_status wam_qkv_timer_config(int layer, int max_samples);
+
+/* Durations (ms) of the recorded samples, oldest first: ms[0 .. min(*n, cap)), *n = the number
+ * recorded since the last read (which restarts the count). Waits for the recorded events: the one
+ * call of this library that blocks the host. ms is a HOST array (may be NULL when cap = 0). */
+wam_status wam_qkv_timer_read(float *ms, int cap, int *n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -120,6 +120,20 @@ def test_op_validation():
                              None) == wam.WAM_E_ARG
 
 
+def test_qkv_timer_host_side():
+    """The measurement hook's host-side paths: disabling, bad sample counts and reads with nothing
+    recorded make no HIP call (enabling creates events, which needs a GPU)."""
+    lib = _lib()
+    assert lib.wam_qkv_timer_config(-1, 0) == wam.WAM_OK
+    assert lib.wam_qkv_timer_config(3, 0) == wam.WAM_E_ARG and "max_samples" in wam.wam_last_error()
+    assert lib.wam_qkv_timer_config(3, 5000) == wam.WAM_E_ARG
+    n = ctypes.c_int(-1)
+    assert lib.wam_qkv_timer_read(None, 0, ctypes.byref(n)) == wam.WAM_OK and n.value == 0
+    assert lib.wam_qkv_timer_read(None, 4, ctypes.byref(n)) == wam.WAM_E_ARG
+    assert lib.wam_qkv_timer_read(None, 0, None) == wam.WAM_E_ARG
+    assert wam.wam_qkv_timer_read(8) == []
+
+
 def test_mx_validation():
     """MXFP8 entry points reject bad shapes and alignment on the host (fake pointers, nothing launched)."""
     lib = _lib()

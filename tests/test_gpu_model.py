@@ -243,6 +243,30 @@ def test_separate_image_attention(gpu, dtype, variant):
     assert ev <= TOL[dtype] and ea <= TOL[dtype]
 
 
+def test_qkv_timer(gpu, tiny_oracle):
+    """The QKV measurement hook: one sample per pass through the chosen layer (none from the key/value
+    only product of an append's last layer, none past max_samples), positive durations, and the
+    read restarts the count; disabled, nothing is recorded."""
+    w0, _, _ = tiny_oracle
+    w = w0.with_(layers=2)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    rig = Rig(w, "bf16", gpu)
+    dc = rig.cache()
+    wam.wam_qkv_timer_config(1, 2)
+    try:
+        rig.append(dc, x1v[0], x1a[0], 0)          # layer 1 is the last: keys/values only
+        assert wam.wam_qkv_timer_read() == []
+        for _ in range(3):
+            rig.step(dc, 1, epv[1], epa[1], [0.5], [0.5], w.frames_per_chunk)
+        ms = wam.wam_qkv_timer_read()
+        assert len(ms) == 2 and all(0.0 < t < 100.0 for t in ms)
+        assert wam.wam_qkv_timer_read() == []
+    finally:
+        wam.wam_qkv_timer_config(-1)
+    rig.step(dc, 1, epv[1], epa[1], [0.5], [0.5], w.frames_per_chunk)
+    assert wam.wam_qkv_timer_read() == []
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("n_state", [1, 3, 6])
 def test_state_rows(gpu, tiny_oracle, dtype, n_state):

@@ -21,7 +21,8 @@ WAM_MX_E4M3, WAM_MX_E2M1 = 0, 1
 EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_time_embed", "wam_dit_stack_fwd", "wam_kv_append",
            "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear",
            "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
-           "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error")
+           "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error",
+           "wam_qkv_timer_config", "wam_qkv_timer_read")
 
 
 class WamError(RuntimeError):
@@ -111,6 +112,8 @@ def load(path: str = LIB_PATH):
         "wam_kv_evict": (I, [CFG, KV, I, I, P]),
         "wam_kv_reset": (None, [KV]),
         "wam_last_error": (ctypes.c_char_p, []),
+        "wam_qkv_timer_config": (I, [I, I]),
+        "wam_qkv_timer_read": (I, [ctypes.POINTER(ctypes.c_float), I, ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -287,6 +290,19 @@ def wam_kv_reset(cache: wam_kv_cache):
 
 def wam_last_error() -> str:
     return load().wam_last_error().decode()
+
+
+def wam_qkv_timer_config(layer: int, max_samples: int = 1):
+    """Record HIP events around block ``layer``'s QKV product in later passes (layer < 0: off)."""
+    _check(load().wam_qkv_timer_config(layer, max_samples))
+
+
+def wam_qkv_timer_read(cap: int = 4096):
+    """Durations in ms of the samples recorded since the last read (waits for their events)."""
+    buf = (ctypes.c_float * max(cap, 1))()
+    n = ctypes.c_int(0)
+    _check(load().wam_qkv_timer_read(buf, cap, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(min(n.value, cap))]
 
 
 def _nbytes(ws):

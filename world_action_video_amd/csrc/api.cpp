@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "../../include/wam.h"
 #include "kernels.h"
@@ -16,6 +17,20 @@ using namespace wam;
 namespace {
 
 thread_local std::string g_err;
+
+// Event pairs around the QKV product of one layer, recorded on the pass's stream (process-wide, one
+// user at a time).
+struct QkvTimer {
+  int layer = -1, n = 0;
+  std::vector<hipEvent_t> ev;   // start, stop per sample
+  void clear() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+    layer = -1;
+    n = 0;
+  }
+};
+QkvTimer g_qkv_timer;
 
 wam_status fail(wam_status st, const char* fmt, ...) {
   char buf[512];
@@ -345,7 +360,14 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     ga.C = reinterpret_cast<char*>(qkv) + (size_t)col0 * g.esz;
     ga.ldc = 3 * g.D;
     if (g.mx) HIP_TRY(mx_operands(p, bw, ga, y, MX_QKV, col0));
+    QkvTimer& tm = g_qkv_timer;
+    const bool timed = tm.layer == l && !kv_only && 2 * tm.n < (int)tm.ev.size();
+    if (timed) HIP_TRY(hipEventRecord(tm.ev[2 * tm.n], p.s));
     HIP_TRY(launch_gemm(ga, dt, EPI_STORE, p.s));
+    if (timed) {
+      HIP_TRY(hipEventRecord(tm.ev[2 * tm.n + 1], p.s));
+      ++tm.n;
+    }
   }
   // (3) RMSNorm + RoPE of q (head-major) and k (into the cache), values into the cache
   QkNormArgs qa{};
@@ -1137,5 +1159,35 @@ void wam_kv_reset(wam_kv_cache* cache) {
 }
 
 const char* wam_last_error(void) { return g_err.c_str(); }
+
+wam_status wam_qkv_timer_config(int layer, int max_samples) {
+  g_qkv_timer.clear();
+  if (layer < 0) return WAM_OK;
+  if (max_samples < 1 || max_samples > 4096) return fail(WAM_E_ARG, "max_samples must be in [1, 4096]");
+  for (int i = 0; i < 2 * max_samples; ++i) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      g_qkv_timer.clear();
+      return fail(WAM_E_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+    }
+    g_qkv_timer.ev.push_back(e);
+  }
+  g_qkv_timer.layer = layer;
+  return WAM_OK;
+}
+
+wam_status wam_qkv_timer_read(float* ms, int cap, int* n) {
+  if (!n || (cap > 0 && !ms) || cap < 0) return fail(WAM_E_ARG, "n is NULL, or ms is NULL with cap > 0");
+  QkvTimer& tm = g_qkv_timer;
+  *n = tm.n;
+  for (int i = 0; i < tm.n && i < cap; ++i) {
+    hipError_t err = hipEventSynchronize(tm.ev[2 * i + 1]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms[i], tm.ev[2 * i], tm.ev[2 * i + 1]);
+    if (err != hipSuccess) return fail(WAM_E_HIP, "timer event: %s", hipGetErrorString(err));
+  }
+  tm.n = 0;
+  return WAM_OK;
+}
 
 }  // extern "C"
