@@ -14,5 +14,5 @@ example exist on the pages.
 """
 from .dit import *  # noqa: F401,F403
 from .unipc import denoise_chunk_unipc, exp_neg_h, step_order, update_weights  # noqa: F401
-from .mx import (e2m1_encode, e2m1_value, e4m3_encode, e4m3_value, mx_dequantize, mx_linear, mx_quantize,  # noqa: F401
-                 relative_error_bound)  # noqa: F401
+from .mx import (e2m1_encode, e2m1_value, e4m3_encode, e4m3_value, mx_attention, mx_dequantize, mx_linear,  # noqa: F401
+                 mx_quantize, relative_error_bound)  # noqa: F401

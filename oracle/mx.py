@@ -124,3 +124,40 @@ def relative_error_bound() -> float:
     """Largest relative error of one element in the normal range: half a unit in the last of 3
     mantissa bits."""
     return math.ldexp(1.0, -4)
+
+
+def mx_attention(q_codes: Array, q_scales: Array, k_codes: Array, k_scales: Array, vt_codes: Array,
+                 vt_scales: Array, limits: Array, ref_offset: int = 0) -> Array:
+    """Attention on MXFP8 operands with MXFP8 probabilities, per head, in float64.
+
+    [N569] (implementation-level optimisations, mixed precision) keeps the softmax in fp8 e4m3
+    beside the fp8 QKV projection. Reading: the probabilities are quantised with the same MX rule
+    as the operands, in blocks of 32 consecutive keys of a query's row, before the product with the
+    values; the normaliser is the sum of the unquantised probabilities.
+      q [H, Lq, d], k [H, Lk, d]: MXFP8 along d (blocks of 32); vt [H, d, Lk]: MXFP8 along keys.
+      limits [Lq]: query i sees keys j < limits[i] (a prefix, as the chunk-causal mask gives).
+    S = dequant(q) dequant(k)^T / sqrt(d); with M the smallest integer >= every visible S log2(e)
+    of the row, p_j = 2^(S_j log2(e) - M) for visible keys, 0 otherwise; l = sum_j p_j;
+    o = dequant(mx_quantize(p)) dequant(vt)^T / l  -> [H, Lq, d].
+    Scaling p by 2^k (integer k) shifts every block's shared exponent by k and leaves the codes
+    alone, so any integer reference gives the same o; ``ref_offset`` adds k to M to show it.
+    """
+    qd = mx_dequantize(q_codes, q_scales)
+    kd = mx_dequantize(k_codes, k_scales)
+    vd = mx_dequantize(vt_codes, vt_scales)               # [H, d, Lk_pad]
+    H, Lq, d = qd.shape
+    Lk = kd.shape[1]
+    s = (qd @ np.swapaxes(kd, -1, -2)) * (math.log2(math.e) / math.sqrt(d))   # log2 units
+    vis = np.arange(Lk)[None, :] < np.asarray(limits)[:, None]
+    s = np.where(vis[None], s, -np.inf)
+    with np.errstate(invalid="ignore"):
+        m = np.ceil(s.max(axis=-1, keepdims=True))
+    m = np.where(np.isfinite(m), m, 0.0) + ref_offset
+    p = np.where(vis[None], np.exp2(s - m), 0.0)
+    l = p.sum(axis=-1, keepdims=True)
+    pad = (-Lk) % 32
+    pp = np.concatenate([p, np.zeros((H, Lq, pad))], axis=-1) if pad else p
+    pq = mx_dequantize(*mx_quantize(pp))[..., :Lk]
+    o = pq @ np.swapaxes(vd[..., :Lk], -1, -2)
+    return np.where(l > 0, o / np.where(l > 0, l, 1.0), 0.0)
+

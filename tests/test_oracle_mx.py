@@ -209,3 +209,90 @@ def test_projection_mxfp4_weights():
     wc, ws = O.mx_quantize(W, fmt="e2m1")
     want = O.mx_dequantize(xc, xs) @ O.mx_dequantize(wc, ws, fmt="e2m1").T
     assert np.array_equal(O.project(W2, x, W, None), want)
+
+
+# ---- MXFP8 attention (probabilities quantised in blocks of 32 keys) ----------------------------------
+
+def _mx_attn_inputs(H, Lq, Lk, d, seed, qscale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((H, Lq, d)) * qscale
+    k = rng.standard_normal((H, Lk, d))
+    v = rng.standard_normal((H, Lk, d))
+    pad = (-Lk) % 64
+    vt = np.concatenate([np.swapaxes(v, 1, 2), np.zeros((H, d, pad))], axis=-1)
+    return O.mx_quantize(q), O.mx_quantize(k), O.mx_quantize(vt)
+
+
+def test_mx_attention_uniform_scores_average_the_values():
+    """Zero queries: every visible key scores 0, each probability is exactly 1 (representable), so
+    the output is the plain mean of the visible dequantised values."""
+    (qc, qs), kq, vq = _mx_attn_inputs(2, 5, 70, 64, 1)
+    qc = np.zeros_like(qc)
+    limits = np.array([1, 17, 32, 33, 70])
+    o = O.mx_attention(qc, qs, *kq, *vq, limits)
+    vd = O.mx_dequantize(*vq)
+    for i, lim in enumerate(limits):
+        np.testing.assert_allclose(o[:, i], vd[:, :, :lim].mean(axis=-1), rtol=1e-13, atol=1e-13)
+
+
+def test_mx_attention_dominant_key():
+    """One key far above the others (2^-40 and below after the reference): the output is that key's
+    value row times one common factor q(p)/p, the rounding of its probability over the unquantised
+    normaliser, within e4m3's 2^-4; the rest reaches it only through probabilities below 2^-40."""
+    H, Lk, d = 1, 96, 64
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((H, Lk, d)) * 0.01
+    k[0, 37] = 1.0
+    q = np.full((H, 1, d), 4.0)      # score of key 37: 4 d / sqrt(d) = 32; log2 units 46
+    vt = rng.standard_normal((H, d, Lk))
+    o = O.mx_attention(*O.mx_quantize(q), *O.mx_quantize(k), *O.mx_quantize(vt), np.array([Lk]))
+    v37 = O.mx_dequantize(*O.mx_quantize(vt))[0, :, 37]
+    c = o[0, 0] @ v37 / (v37 @ v37)
+    assert abs(c - 1.0) <= 2.0 ** -4 and c != 1.0
+    np.testing.assert_allclose(o[0, 0], c * v37, rtol=0, atol=1e-9 * np.abs(v37).max())
+
+
+def test_mx_attention_integer_reference_is_irrelevant():
+    """Probabilities scaled by 2^k quantise to the same codes with shifted block exponents, so the
+    output does not depend on the integer reference: equal up to exp2's own rounding (a different
+    argument), far below the 2^-4 steps a changed code would make."""
+    qq, kq, vq = _mx_attn_inputs(3, 9, 100, 128, 3, qscale=2.0)
+    limits = np.array([3, 10, 31, 32, 33, 64, 65, 99, 100])
+    o0 = O.mx_attention(*qq, *kq, *vq, limits)
+    for off in (-3, 1, 7):
+        np.testing.assert_allclose(O.mx_attention(*qq, *kq, *vq, limits, ref_offset=off), o0, rtol=1e-12, atol=1e-14)
+    pc, ps = O.mx_quantize(np.random.default_rng(4).random((5, 64)))
+    pc2, ps2 = O.mx_quantize(np.ldexp(O.mx_dequantize(pc, ps), -5))
+    assert np.array_equal(pc2, pc) and np.array_equal(ps2.astype(int), ps.astype(int) - 5)
+
+
+@pytest.mark.parametrize("Lk", [32, 77, 130])
+def test_mx_attention_within_the_probability_rounding_bound(Lk):
+    """Against exact attention on the same dequantised operands (the model's attention function with
+    the prefix mask). With the block scale 2^e (e = floor(log2 of the block's largest probability)
+    - 8) an e4m3 probability is off by at most: half a unit in its last place, 2^-4 of itself, in
+    the normal range; p - 448 2^e where the block's top values saturate at 448; 2^-10 2^e (half
+    the subnormal step) below the normal range. So |o - o_exact| <= sum_j b_j |v_j| / l per
+    output element, b_j = max(2^-4 p_j, p_j - 448 2^e) + 2^-10 2^e."""
+    H, Lq, d = 2, 7, 64
+    qq, kq, vq = _mx_attn_inputs(H, Lq, Lk, d, 10 + Lk, qscale=1.5)
+    limits = np.minimum(np.array([1, 5, 31, 32, 33, 60, Lk]), Lk)
+    o = O.mx_attention(*qq, *kq, *vq, limits)
+    qd, kd = O.mx_dequantize(*qq), O.mx_dequantize(*kq)
+    vd = np.swapaxes(O.mx_dequantize(*vq)[..., :Lk], 1, 2)          # [H, Lk, d]
+    vis = np.arange(Lk)[None, :] < limits[:, None]
+    exact = O.attention(qd, kd, vd, vis)
+    # probabilities on the oracle's own scale: 2^(S log2 e - M), M the row's ceiling in log2 units
+    s = qd @ np.swapaxes(kd, 1, 2) * (np.log2(np.e) / np.sqrt(d))
+    s = np.where(vis[None], s, -np.inf)
+    p = np.where(vis[None], np.exp2(s - np.ceil(s.max(axis=-1, keepdims=True))), 0.0)
+    l = p.sum(axis=-1, keepdims=True)
+    pad = (-Lk) % 32
+    pb = np.concatenate([p, np.zeros((H, Lq, pad))], axis=-1).reshape(H, Lq, -1, 32).max(axis=-1)
+    pmax = np.repeat(pb, 32, axis=-1)[..., :Lk]
+    scale = np.ldexp(1.0, (np.floor(np.log2(np.where(pmax > 0, pmax, 1.0))) - 8).astype(int))
+    b = np.maximum(2.0 ** -4 * p, p - 448 * scale) + 2.0 ** -10 * scale
+    bound = (b @ np.abs(vd)) / l
+    err = np.abs(o - exact)
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-15)
+    assert err.max() > 0          # the probabilities really are rounded
