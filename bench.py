@@ -163,6 +163,8 @@ def main():
                     help="HBM-bound kernels: the flow update from the step's size to a >1 GB footprint (buffers "
                          "rotated through a 1.5 GiB pool, past the 256 MB Infinity Cache) beside a 1 GiB copy, and one "
                          "config-3 block over 1 and 8 chunks (for a kernel trace of its row kernels)")
+    ap.add_argument("--attention", action="store_true",
+                    help="bf16 and MXFP8 attention kernels at the step's self- and cross-attention shapes")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="turn the two rocprofv3 --pmc databases of a --counters run (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/hbm_traffic.json")
@@ -186,6 +188,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.elementwise:
         elementwise(args, dev)
+        return
+    if args.attention:
+        attention_kernels(args, dev)
         return
     if args.workload != WORKLOAD_ID and not args.counters:
         extra_workload(args, dev)
@@ -459,6 +464,62 @@ def elementwise(args, dev):
                       "config": {"workload": "flow update 2 branches, 24 B per element; config-3 block over 1 and 8 chunks"},
                       "hbm_peak_GBps": PEAK_HBM_GBS, "copy_1GiB_GBps": round(copy_gbps, 1),
                       "copy_frac": round(copy_gbps / PEAK_HBM_GBS, 3), "flow": flow, "block_ms": blocks}))
+
+
+def attention_kernels(args, dev):
+    """bf16 (`attn3_kernel`) and MXFP8 (`attn_mx_kernel`) attention at the config-3 shapes: self-attention
+    of 2 branches x 40 heads, 464 queries over 928 cached + 464 current keys (chunk-causal), and
+    cross-attention over the 769 condition tokens. Operands are random (N(0, 1), quantised on the
+    device for the MXFP8 op); HIP events around 20 back-to-back launches. Work: 4 br H Lq Lk_visible d."""
+    import torch
+
+    import world_action_video_amd as wam
+
+    br, H, Lq, d = 2, 40, 464, 128
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out = {}
+    for name, kv_total, kv_base, chunk_q in (("self", 1392, 928, 464), ("cross", 769, 0, 0)):
+        v_stride = (kv_total + 63) // 64 * 64
+        q = torch.randn((br, H, Lq, d), device=dev).to(torch.bfloat16)
+        k = torch.randn((br, H, kv_total, d), device=dev).to(torch.bfloat16)
+        vt = torch.zeros((br, H, d, v_stride), device=dev, dtype=torch.bfloat16)
+        vt[..., :kv_total] = torch.randn((br, H, d, kv_total), device=dev).to(torch.bfloat16)
+        o = torch.empty((br * Lq, H * d), dtype=torch.bfloat16, device=dev)
+        qc = torch.empty((br, H, Lq, d), dtype=torch.uint8, device=dev)
+        qs = torch.empty((br, H, Lq, d // 32), dtype=torch.uint8, device=dev)
+        kc = torch.empty((br, H, kv_total, d), dtype=torch.uint8, device=dev)
+        ks = torch.empty((br, H, kv_total, d // 32), dtype=torch.uint8, device=dev)
+        vc = torch.empty((br, H, d, v_stride), dtype=torch.uint8, device=dev)
+        vs = torch.empty((br, H, d, v_stride // 32), dtype=torch.uint8, device=dev)
+        wam.wam_mx_quantize(wam.WAM_BF16, q, d, br * H * Lq, d, qc, d, qs)
+        wam.wam_mx_quantize(wam.WAM_BF16, k, d, br * H * kv_total, d, kc, d, ks)
+        wam.wam_mx_quantize(wam.WAM_BF16, vt, v_stride, br * H * d, v_stride, vc, v_stride, vs)
+        vs_bm = vs.transpose(2, 3).contiguous()      # block-major scales of V^T
+        ops = {
+            "bf16": lambda: wam.wam_op_attention(wam.WAM_BF16, q, k, vt, o, br, H, d, Lq, kv_total, v_stride,
+                                                 kv_base, chunk_q, kv_total),
+            "mxfp8": lambda: wam.wam_op_attention_mx(qc, qs, kc, ks, vc, vs_bm, o, br, H, Lq, kv_total, v_stride,
+                                                     kv_base, chunk_q, kv_total),
+        }
+        lim = [min(kv_total, kv_base + (i // chunk_q + 1) * chunk_q) if chunk_q else kv_total for i in range(Lq)]
+        flops = 4.0 * br * H * sum(lim) * d
+        for kind, op in ops.items():
+            for _ in range(3):
+                op()
+            a, b = ev(), ev()
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(20):
+                op()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / 20 * 1e3
+            out["%s_%s_us" % (name, kind)] = round(us, 2)
+            out["%s_%s_tflops" % (name, kind)] = round(flops / (us * 1e-6) / 1e12, 1)
+    print(json.dumps({"metric": "attention kernel time at the config-3 shapes", "unit": "us", "n_gpus": 1,
+                      "dtype": "bf16 and mxfp8", "data": "synthetic N(0,1)",
+                      "config": {"workload": "2 x 40 heads, 464 queries; self 1392 keys chunk-causal, cross 769 keys"},
+                      **out}))
 
 
 def extra_workload(args, dev):

@@ -351,6 +351,25 @@ wam_status wam_op_attention(wam_dtype dtype, const void *Q, const void *K, const
                             int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,
                             void *ws, size_t ws_bytes, void *stream);
 
+/* MXFP8 attention ([N569] real-time optimisations, mixed precision: the fp8 QKV projection and an
+ * fp8 e4m3 softmax), head_dim 128, same visibility rule as wam_op_attention. Operands are OCP MXFP8:
+ * e4m3 codes with one e8m0 scale byte (value 2^(byte - 127)) per 32 consecutive values.
+ *   Q  [br][H][Lq][128] codes, Q_scales [br][H][Lq][4]        (blocks along the head dimension)
+ *   K  [br][H][k_rows][128] codes, K_scales [br][H][k_rows][4]
+ *   Vt [br][H][128][v_stride] codes (key-contiguous), Vt_scales [br][H][v_stride / 32][128]: the
+ *      scale of key block kb of value row r is byte kb * 128 + r (blocks along keys)
+ *   O  [br * Lq][H * 128] bfloat16.
+ * Scores in fp32 from the scaled matrix instruction; softmax with an integer reference (log2 units);
+ * each query's probabilities are quantised to MXFP8 in blocks of 32 keys (block rule of
+ * wam_mx_quantize) before the product with the values; the normaliser is the sum of the unquantised
+ * probabilities. Keys at or past kv_total never reach the output, whatever their codes hold; the scale
+ * of the 32-key block that holds key kv_total - 1 must be the one of its valid keys (quantise zero-padded
+ * rows). v_stride: a multiple of 64, >= kv_total rounded up to 64. Alignment: codes, Vt_scales and O
+ * 16 bytes, Q/K scales 4 bytes. Errors: WAM_E_ARG / WAM_E_SHAPE, nothing launched. */
+wam_status wam_op_attention_mx(const void *Q, const void *Q_scales, const void *K, const void *K_scales, const void *Vt,
+                               const void *Vt_scales, void *O, int br, int heads, int Lq, int k_rows, int v_stride,
+                               int kv_base, int chunk_q, int kv_total, void *stream);
+
 /* Sliding attention window ([WS1] continuous requests: the attention window releases old KV and
  * the frame position restarts; [HYPER] 方法: cached clean chunks are the only past a chunk sees).
  * Drops the oldest `drop_rows` committed rows of every layer and branch (whole chunks: a multiple

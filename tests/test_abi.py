@@ -120,6 +120,22 @@ def test_op_validation():
                              None) == wam.WAM_E_ARG
 
 
+def test_attention_mx_validation():
+    """The MXFP8 attention op rejects bad sizes and alignment on the host (fake pointers, nothing
+    launched)."""
+    lib = _lib()
+    ok = (0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert lib.wam_op_attention_mx(*ok, 2, 4, 100, 300, 300, 0, 0, 300, None) == wam.WAM_E_SHAPE   # v_stride % 64
+    assert lib.wam_op_attention_mx(*ok, 2, 4, 100, 300, 256, 0, 0, 300, None) == wam.WAM_E_SHAPE   # v_stride < 320
+    assert lib.wam_op_attention_mx(*ok, 2, 4, 100, 200, 320, 0, 0, 300, None) == wam.WAM_E_SHAPE   # k_rows < kv_total
+    assert lib.wam_op_attention_mx(*ok, 2, 4, 0, 300, 320, 0, 0, 300, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_attention_mx(*ok, 2, 4, 100, 300, 320, 0, -1, 300, None) == wam.WAM_E_SHAPE
+    bad = (0x1008,) + ok[1:]
+    assert lib.wam_op_attention_mx(*bad, 2, 4, 100, 300, 320, 0, 0, 300, None) == wam.WAM_E_ARG
+    assert lib.wam_op_attention_mx(None, *ok[1:], 2, 4, 100, 300, 320, 0, 0, 300, None) == wam.WAM_E_ARG
+    assert "aligned" in wam.wam_last_error() or "NULL" in wam.wam_last_error()
+
+
 def test_qkv_timer_host_side():
     """The measurement hook's host-side paths: disabling, bad sample counts and reads with nothing
     recorded make no HIP call (enabling creates events, which needs a GPU)."""

@@ -1,0 +1,134 @@
+"""MXFP8 attention through the C ABI (wam_op_attention_mx) against oracle/mx.py's mx_attention.
+
+Inputs are seeded N(0, 1) queries, keys and values, quantised on the host by the oracle's MX rule
+(the op's operands are codes and scale bytes, so both sides read the same operands). The oracle
+works in float64 on the exact dequantised values; the kernel differs by:
+* the scores: the scaled matrix instruction cuts each product toward zero 13 bits below the largest
+  of its group of 8 (2^-9 of the group's largest |q k| per group, 16 groups per score here);
+* the exp2 of the hardware and fp32 sums;
+* the probabilities' e4m3 rounding, taken on those slightly different values: where a probability
+  sits within the score error of a rounding boundary its code can differ by one unit (2^-3 of it);
+* the value product's own accumulation and the bf16 output (2^-9).
+Together these stay well below a relative L2 error of 2e-2 per output tensor, the bar used here. A
+wrong scale byte, key order or block assignment moves whole probabilities or values by factors of 2
+and fails it many times over. Keys past kv_total hold NaN codes and NaN scale bytes on purpose:
+they must not reach the output (bit-identical to a run with clean padding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import world_action_video_amd as wam
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def limits_of(Lq, kv_total, kv_base, chunk_q):
+    q = np.arange(Lq)
+    if chunk_q <= 0:
+        return np.full(Lq, kv_total)
+    return np.minimum(kv_total, kv_base + (q // chunk_q + 1) * chunk_q)
+
+
+class Case:
+    """Seeded operands of one call, their MX codes (host) and the device copies."""
+
+    def __init__(self, br, H, Lq, kv_total, k_rows, v_stride, seed, gpu):
+        k0 = synth.tensor_key(101, seed, "mx-attn")
+        self.q = synth.fill((br, H, Lq, D), k0, "normal", 1.0).astype(np.float64)
+        k = synth.fill((br, H, k_rows, D), k0 + 1, "normal", 1.0).astype(np.float64)
+        v = synth.fill((br, H, kv_total, D), k0 + 2, "normal", 1.0).astype(np.float64)
+        k[:, :, kv_total:] = 0.0
+        self.k, self.v = k, v
+        vt = np.zeros((br, H, D, v_stride))
+        vt[..., :kv_total] = np.swapaxes(v, 2, 3)
+        self.qc, self.qs = O.mx_quantize(self.q)
+        self.kc, self.ks = O.mx_quantize(k)
+        self.vtc, self.vts = O.mx_quantize(vt)               # scales [br][H][D][v_stride / 32]
+        self.dims = (br, H, Lq, kv_total, k_rows, v_stride)
+        self.gpu = gpu
+
+    def run(self, kv_base, chunk_q, poison=False):
+        br, H, Lq, kv_total, k_rows, v_stride = self.dims
+        kc, ks, vtc = self.kc.copy(), self.ks.copy(), self.vtc.copy()
+        vts = np.ascontiguousarray(np.swapaxes(self.vts, 2, 3))   # block-major [br][H][v_stride/32][D]
+        if poison:   # NaN codes (0x7f) and NaN scale bytes (0xff) at every key past kv_total
+            kc[:, :, kv_total:] = 0x7F
+            ks[:, :, kv_total:] = 0xFF
+            vtc[..., kv_total:] = 0x7F
+            vts[:, :, (kv_total + 31) // 32:] = 0xFF
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(self.gpu)  # noqa: E731
+        out = torch.empty((br * Lq, H * D), dtype=torch.bfloat16, device=self.gpu)
+        wam.wam_op_attention_mx(dev(self.qc), dev(self.qs), dev(kc), dev(ks), dev(vtc), dev(vts), out, br, H, Lq,
+                                k_rows, v_stride, kv_base, chunk_q, kv_total)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy().reshape(br, Lq, H, D).transpose(0, 2, 1, 3)   # [br][H][Lq][D]
+
+    def oracle(self, b, heads, kv_base, chunk_q):
+        _, _, Lq, kv_total, _, _ = self.dims
+        lim = limits_of(Lq, kv_total, kv_base, chunk_q)
+        return O.mx_attention(self.qc[b, heads], self.qs[b, heads], self.kc[b, heads, :, :], self.ks[b, heads],
+                              self.vtc[b, heads], self.vts[b, heads], lim)
+
+    def exact(self, b, heads, kv_base, chunk_q):
+        """Unquantised attention on the original float operands (quality, not parity)."""
+        _, _, Lq, kv_total, _, _ = self.dims
+        lim = limits_of(Lq, kv_total, kv_base, chunk_q)
+        vis = np.arange(kv_total)[None, :] < lim[:, None]
+        return O.attention(self.q[b, heads], self.k[b, heads, :kv_total], self.v[b, heads], vis)
+
+
+CASES = [
+    # br, H, Lq, kv_total, k_rows, v_stride, kv_base, chunk_q
+    (2, 3, 200, 300, 320, 320, 100, 100),     # chunk-causal, ragged queries and keys
+    (1, 2, 33, 40, 40, 64, 0, 0),             # one partial key tile
+    (2, 2, 130, 769, 769, 832, 0, 0),         # the condition-token count, no mask
+    (1, 1, 128, 64, 64, 64, 0, 0),            # exactly one full tile
+]
+
+
+@pytest.mark.parametrize("br,H,Lq,kv_total,k_rows,v_stride,kv_base,chunk_q", CASES)
+def test_attention_mx_matches_oracle(gpu, br, H, Lq, kv_total, k_rows, v_stride, kv_base, chunk_q):
+    c = Case(br, H, Lq, kv_total, k_rows, v_stride, Lq + kv_total, gpu)
+    got = c.run(kv_base, chunk_q)
+    heads = list(range(H))
+    for b in range(br):
+        ref = c.oracle(b, heads, kv_base, chunk_q)
+        e = rel_l2(got[b], ref)
+        q = rel_l2(got[b], c.exact(b, heads, kv_base, chunk_q))
+        print("b %d: rel-L2 vs oracle %.3e, vs unquantised attention %.3e" % (b, e, q), flush=True)
+        assert e <= 2e-2 and np.isfinite(got[b]).all()
+        assert q <= 0.1
+
+
+def test_attention_mx_ignores_keys_past_kv_total(gpu):
+    """NaN codes and NaN scale bytes at every key past kv_total (keys, values, whole value blocks)
+    leave the output bit-identical."""
+    c = Case(2, 2, 96, 300, 384, 384, 7, gpu)
+    clean = c.run(100, 100)
+    dirty = c.run(100, 100, poison=True)
+    assert np.isfinite(clean).all() and np.array_equal(clean, dirty)
+
+
+def test_attention_mx_full_size_sampled(gpu):
+    """The step's self-attention shape (2 branches x 40 heads, 464 queries over 928 cached + 464
+    current keys, chunk-causal), oracle on three heads of each branch."""
+    c = Case(2, 40, 464, 1392, 1392, 1408, 11, gpu)
+    got = c.run(928, 464)
+    for b in range(2):
+        heads = [0, 17, 39]
+        e = rel_l2(got[b, heads], c.oracle(b, heads, 928, 464))
+        q = rel_l2(got[b, heads], c.exact(b, heads, 928, 464))
+        print("b %d heads %s: rel-L2 vs oracle %.3e, vs unquantised %.3e" % (b, heads, e, q), flush=True)
+        assert e <= 2e-2 and q <= 0.1
+    assert np.isfinite(got).all()

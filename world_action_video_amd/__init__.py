@@ -22,7 +22,7 @@ EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_tim
            "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear",
            "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error",
-           "wam_qkv_timer_config", "wam_qkv_timer_read")
+           "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx")
 
 
 class WamError(RuntimeError):
@@ -114,6 +114,7 @@ def load(path: str = LIB_PATH):
         "wam_last_error": (ctypes.c_char_p, []),
         "wam_qkv_timer_config": (I, [I, I]),
         "wam_qkv_timer_read": (I, [ctypes.POINTER(ctypes.c_float), I, ctypes.POINTER(ctypes.c_int)]),
+        "wam_op_attention_mx": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -290,6 +291,12 @@ def wam_kv_reset(cache: wam_kv_cache):
 
 def wam_last_error() -> str:
     return load().wam_last_error().decode()
+
+
+def wam_op_attention_mx(Q, Qs, K, Ks, Vt, Vs, O, br, heads, Lq, k_rows, v_stride, kv_base, chunk_q, kv_total,
+                        stream=None):
+    _check(load().wam_op_attention_mx(_ptr(Q), _ptr(Qs), _ptr(K), _ptr(Ks), _ptr(Vt), _ptr(Vs), _ptr(O), br, heads,
+                                      Lq, k_rows, v_stride, kv_base, chunk_q, kv_total, _stream(stream)))
 
 
 def wam_qkv_timer_config(layer: int, max_samples: int = 1):

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -1124,6 +1125,32 @@ wam_status wam_op_attention(wam_dtype dtype, const void* Q, const void* K, const
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   a.part = reinterpret_cast<float*>(ws); a.part_elems = ws ? (long)(ws_bytes / 4) : 0;
   HIP_TRY(launch_attention(a, dtype == WAM_BF16 ? DT_BF16 : DT_F32, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
+wam_status wam_op_attention_mx(const void* Q, const void* Q_scales, const void* K, const void* K_scales, const void* Vt,
+                               const void* Vt_scales, void* O, int br, int heads, int Lq, int k_rows, int v_stride,
+                               int kv_base, int chunk_q, int kv_total, void* stream) {
+  if (!Q || !Q_scales || !K || !K_scales || !Vt || !Vt_scales || !O) return fail(WAM_E_ARG, "NULL operand");
+  if (unaligned16(Q) || unaligned16(K) || unaligned16(Vt) || unaligned16(Vt_scales) || unaligned16(O) ||
+      reinterpret_cast<uintptr_t>(Q_scales) % 4 || reinterpret_cast<uintptr_t>(K_scales) % 4)
+    return fail(WAM_E_ARG, "codes, V^T scales and O must be 16-byte aligned, Q/K scales 4-byte aligned");
+  if (br <= 0 || heads <= 0 || Lq <= 0 || kv_total <= 0 || kv_base < 0 || chunk_q < 0)
+    return fail(WAM_E_SHAPE, "bad sizes");
+  if (k_rows < kv_total || v_stride % 64 || v_stride < (kv_total + 63) / 64 * 64)
+    return fail(WAM_E_SHAPE, "k_rows must be >= kv_total and v_stride a multiple of 64 covering kv_total");
+  if ((long)k_rows * 128 > INT32_MAX || (long)v_stride * 128 > INT32_MAX)
+    return fail(WAM_E_SHAPE, "one head's keys exceed 2 GiB");
+  AttnMxArgs a{};
+  a.Q = static_cast<const uint8_t*>(Q); a.Qs = static_cast<const uint8_t*>(Q_scales);
+  a.K = static_cast<const uint8_t*>(K); a.Ks = static_cast<const uint8_t*>(K_scales);
+  a.Vt = static_cast<const uint8_t*>(Vt); a.Vs = static_cast<const uint8_t*>(Vt_scales); a.O = O;
+  a.q_bh = (long)Lq * 128; a.qs_bh = (long)Lq * 4; a.k_bh = (long)k_rows * 128; a.ks_bh = (long)k_rows * 4;
+  a.v_bh = 128L * v_stride; a.vs_bh = (long)(v_stride / 32) * 128;
+  a.v_stride = v_stride; a.Lq = Lq; a.H = heads; a.br = br; a.kv_base = kv_base; a.chunk_q = chunk_q;
+  a.kv_total = kv_total;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt(128.0));
+  HIP_TRY(launch_attention_mx(a, reinterpret_cast<hipStream_t>(stream)));
   return WAM_OK;
 }
 

@@ -76,6 +76,22 @@ struct AttnArgs {
   int frame_tokens;   // > 0 (with chunk_q > 0): frame-causal inside a chunk, frames of this many tokens
   int video_tokens;   // video tokens at the start of each chunk (frame-causal only)
 };
+// MXFP8 attention (head dim 128): e4m3 codes with e8m0 scales per 32 values; byte strides between
+// consecutive (branch, head) blocks.
+struct AttnMxArgs {
+  const uint8_t* Q;    // [br][H][Lq][128] codes
+  const uint8_t* Qs;   // [br][H][Lq][4] scales (blocks of 32 head-dim values)
+  const uint8_t* K;    // [br][H][k_rows][128]
+  const uint8_t* Ks;   // [br][H][k_rows][4]
+  const uint8_t* Vt;   // [br][H][128][v_stride] (key-contiguous)
+  const uint8_t* Vs;   // [br][H][v_stride / 32][128] (block-major: the 128 rows' scales of key block kb)
+  void* O;             // bf16 [br * Lq][H * 128]
+  long q_bh, qs_bh, k_bh, ks_bh, v_bh, vs_bh;
+  int v_stride, Lq, H, br, kv_base, chunk_q, kv_total;
+  float scale_log2;    // log2(e) / sqrt(128)
+};
+hipError_t launch_attention_mx(const AttnMxArgs& a, hipStream_t s);
+
 // Keys visible to query q: a prefix [0, limit) of the key rows. Cached keys (below kv_base) are
 // always visible; inside the pass, keys up to the end of the query's chunk (chunk_q > 0), or with
 // frame_tokens > 0 up to the end of the query's frame for video queries.
