@@ -94,6 +94,7 @@ CASES = [
     (1, 2, 33, 40, 40, 64, 0, 0),             # one partial key tile
     (2, 2, 130, 769, 769, 832, 0, 0),         # the condition-token count, no mask
     (1, 1, 128, 64, 64, 64, 0, 0),            # exactly one full tile
+    (1, 2, 5, 1, 1, 64, 0, 0),                # a single key: the output is its value row (times q(p)/p)
 ]
 
 

@@ -556,6 +556,30 @@ def test_flow_step_matches_oracle(gpu, nv, na):
     assert np.array_equal(Gv2.cpu().numpy(), vv[0])
 
 
+@pytest.mark.parametrize("nv,na", [(0, 192), (28160, 0), (5, 3)])
+def test_flow_step_one_group_or_tiny(gpu, nv, na):
+    """Degenerate sizes: no video part, no action part, and fewer elements than one vector (the scalar
+    path): the Euler update of what is there, nothing else touched."""
+    rng = synth.tensor_key(101, 1, "flow-edge")
+    v = synth.fill((2, nv + na), rng, "normal", 1.0)
+    xv = synth.fill((max(nv, 1),), rng + 1, "normal", 1.0)
+    xa = synth.fill((max(na, 1),), rng + 2, "normal", 1.0)
+    vv, va = np.ascontiguousarray(v[:, :nv]), np.ascontiguousarray(v[:, nv:])
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(gpu)  # noqa: E731
+    Xv, Xa = d(xv), d(xa)
+    ws = torch.empty(4096, dtype=torch.uint8, device=gpu)
+    wam.wam_flow_step(Xv, Xa, d(vv) if nv else None, d(va) if na else None, 2, 5.0, nv, na, 0.25, 0.5, None, None, None,
+                      None, ws)
+    torch.cuda.synchronize()
+    gv, ga = O.cfg_combine(vv, 5.0), O.cfg_combine(va, 5.0)
+    exp_v = O.euler_update(xv[:nv], gv, 0.0, 0.25) if nv else xv
+    exp_a = O.euler_update(xa[:na], ga, 0.0, 0.5) if na else xa
+    np.testing.assert_allclose(Xv.cpu().numpy()[:max(nv, 1)], np.concatenate([exp_v, xv[nv:]])[:max(nv, 1)],
+                               rtol=2e-6, atol=2e-6)
+    np.testing.assert_allclose(Xa.cpu().numpy()[:max(na, 1)], np.concatenate([exp_a, xa[na:]])[:max(na, 1)],
+                               rtol=2e-6, atol=2e-6)
+
+
 def cache_host(dc, length):
     """Device cache -> the oracle's layout: per layer [br, length, H*d] keys and values (float32)."""
     k = dc.k[..., :length, :].float().cpu().numpy()    # [L, br, H, len, d]
