@@ -558,7 +558,7 @@ wam_status stack_pass(const wam_config* cfg, const wam_weights* w, wam_kv_cache*
   hd.wa = w->ao_w; hd.ba = reinterpret_cast<const float*>(w->ao_b); hd.A = g.A;
   hd.vv = vv; hd.va = va; hd.rm = rowmap(p);
   hd.part = at<float>(ws, L.part);
-  hd.splits = g.D % 512 == 0 && g.D >= 2048 ? 8 : 1;   // 8 x M x 64 partials fit the split-K region
+  hd.part_elems = L.part_elems;
   HIP_TRY(launch_head(hd, g.dt, s));
   return WAM_OK;
 }

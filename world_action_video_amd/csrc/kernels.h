@@ -260,7 +260,8 @@ struct HeadArgs {
   const void* wa; const float* ba; int A;
   float* vv; float* va;
   RowMap rm;
-  float* part; int splits;
+  float* part; long part_elems;   // scratch for the K slices' partial outputs (fp32 capacity)
+  int splits;                      // set by launch_head
 };
 hipError_t launch_head(const HeadArgs& a, DType dt, hipStream_t s);
 // workgroups (and [3] partial-sum slots) of the flow step for these sizes: 1 .. 512

@@ -978,41 +978,68 @@ hipError_t launch_unipc_step(const UnipcArgs& a, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Output heads. One wave per (row, K split); lane n accumulates output n (fp32, k in order) from
-// 8-element vectors of the row and of weight row n. The second kernel sums the splits in order, adds
-// the bias and writes the row to its token-group output.
+// Output heads. A workgroup takes 16 rows and one K slice (at most 320 columns): the slice of both
+// head matrices goes to LDS once with coalesced 16-byte loads (video head rows 0 .. P-1, action head
+// rows 64 .. 64+A-1, rows padded by 8 elements so a wave's 64 row reads hit distinct banks), then
+// each wave computes 4 rows, lane n accumulating output n of each from LDS weight row n (fp32, k in
+// order). The second kernel sums the slices in order, adds the bias and writes the row to its
+// token-group output.
 // ------------------------------------------------------------------------------------------------
+constexpr int HEAD_ROWS = 16, HEAD_KMAX = 320;
+
 template <typename T>
 __global__ void __launch_bounds__(256) head_partial_kernel(HeadArgs a) {
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), n = threadIdx.x & 63, sp = blockIdx.y;
-  if (m >= a.M) return;
-  const int loc = (m % a.rm.rows_per_branch) % a.rm.Lq;
-  const bool video = loc < a.rm.Lv;
-  const int nout = video ? a.P : a.A;
-  if (n >= nout) return;
-  const T* w = reinterpret_cast<const T*>(video ? a.wv : a.wa) + (long)n * a.D;
-  const T* y = reinterpret_cast<const T*>(a.Y) + (long)m * a.D;
-  const int kspan = a.D / a.splits, k0 = sp * kspan;
+  extern __shared__ __attribute__((aligned(16))) unsigned char head_lds[];
+  T* wl = reinterpret_cast<T*>(head_lds);
   constexpr int EPU = 16 / sizeof(T);
-  float acc = 0.f;
-  for (int k = k0; k < k0 + kspan; k += 8) {
-    float yv[8], wv[8];
+  const int m0 = blockIdx.x * HEAD_ROWS, sp = blockIdx.y;
+  const int kspan = a.D / a.splits, k0 = sp * kspan, pitch = kspan + 8;
+  const int groups = kspan / 8;                              // 8-element groups per weight row
+  for (int x = threadIdx.x; x < (a.P + a.A) * groups; x += 256) {
+    const int r = x / groups, gidx = x % groups;
+    const bool vrow = r < a.P;
+    const T* src = reinterpret_cast<const T*>(vrow ? a.wv : a.wa) + (long)(vrow ? r : r - a.P) * a.D + k0 + gidx * 8;
+    T* dst = wl + (vrow ? r : 64 + r - a.P) * pitch + gidx * 8;
 #pragma unroll
-    for (int u = 0; u < 8 / EPU; ++u) {
-      const uint4 yy = *reinterpret_cast<const uint4*>(y + k + u * EPU);
-      const uint4 ww = *reinterpret_cast<const uint4*>(w + k + u * EPU);
-      const T* ye = reinterpret_cast<const T*>(&yy);
-      const T* we = reinterpret_cast<const T*>(&ww);
-#pragma unroll
-      for (int e = 0; e < EPU; ++e) {
-        yv[u * EPU + e] = Elem<T>::to_f(ye[e]);
-        wv[u * EPU + e] = Elem<T>::to_f(we[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(yv[e], wv[e], acc);
+    for (int u = 0; u < 8 / EPU; ++u) reinterpret_cast<uint4*>(dst)[u] = reinterpret_cast<const uint4*>(src)[u];
   }
-  a.part[((long)sp * a.M + m) * 64 + n] = acc;
+  __syncthreads();
+  const int n = threadIdx.x & 63, mb = m0 + (threadIdx.x >> 6) * 4;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const T* wrow[4];
+  const T* yrow[4];
+  bool act[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = min(mb + r, a.M - 1);
+    const bool video = (m % a.rm.rows_per_branch) % a.rm.Lq < a.rm.Lv;
+    act[r] = mb + r < a.M && n < (video ? a.P : a.A);
+    wrow[r] = wl + (video ? n : 64 + min(n, a.A - 1)) * pitch;
+    yrow[r] = reinterpret_cast<const T*>(a.Y) + (long)m * a.D + k0;
+  }
+  for (int k = 0; k < kspan; k += 8) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float yv[8], wv[8];
+#pragma unroll
+      for (int u = 0; u < 8 / EPU; ++u) {
+        const uint4 yy = *reinterpret_cast<const uint4*>(yrow[r] + k + u * EPU);
+        const uint4 ww = *reinterpret_cast<const uint4*>(wrow[r] + k + u * EPU);
+        const T* ye = reinterpret_cast<const T*>(&yy);
+        const T* we = reinterpret_cast<const T*>(&ww);
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) {
+          yv[u * EPU + e] = Elem<T>::to_f(ye[e]);
+          wv[u * EPU + e] = Elem<T>::to_f(we[e]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r] = fmaf(yv[e], wv[e], acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (act[r]) a.part[((long)sp * a.M + mb + r) * 64 + n] = acc[r];
 }
 
 __global__ void __launch_bounds__(256) head_reduce_kernel(HeadArgs a) {
@@ -1031,12 +1058,22 @@ __global__ void __launch_bounds__(256) head_reduce_kernel(HeadArgs a) {
   else a.va[((long)(b * nch + ch) * La + (loc - a.rm.Lv)) * a.A + n] = v;
 }
 
-hipError_t launch_head(const HeadArgs& a, DType dt, hipStream_t s) {
-  if (a.M <= 0) return hipSuccess;
-  if (a.P > 64 || a.A > 64 || a.splits < 1 || a.D % (8 * a.splits)) return hipErrorInvalidValue;
-  const dim3 grid((a.M + 3) / 4, a.splits), block(256);
-  if (dt == DT_BF16) hipLaunchKernelGGL(head_partial_kernel<bf16_t>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(head_partial_kernel<float>, grid, block, 0, s, a);
+hipError_t launch_head(const HeadArgs& a0, DType dt, hipStream_t s) {
+  if (a0.M <= 0) return hipSuccess;
+  if (a0.P > 64 || a0.A > 64 || a0.P < 1 || a0.A < 1 || a0.D % 8) return hipErrorInvalidValue;
+  // the fewest K slices of at most HEAD_KMAX columns, each a whole number of 8-column groups
+  // (and whose weight slices fit the 64 KB of dynamic LDS)
+  HeadArgs a = a0;
+  const size_t esz = dt == DT_BF16 ? 2 : 4;
+  auto lds_of = [&](int sp) { return (size_t)(64 + a.A) * (a.D / sp + 8) * esz; };
+  a.splits = 1;
+  while (a.splits <= a.D / 8 && (a.D / a.splits > HEAD_KMAX || a.D % (8 * a.splits) || lds_of(a.splits) > 65536))
+    ++a.splits;
+  if (a.splits > a.D / 8 || (long)a.splits * a.M * 64 > a.part_elems) return hipErrorInvalidValue;
+  const size_t lds = lds_of(a.splits);
+  const dim3 grid((a.M + HEAD_ROWS - 1) / HEAD_ROWS, a.splits), block(256);
+  if (dt == DT_BF16) hipLaunchKernelGGL(head_partial_kernel<bf16_t>, grid, block, lds, s, a);
+  else hipLaunchKernelGGL(head_partial_kernel<float>, grid, block, lds, s, a);
   hipLaunchKernelGGL(head_reduce_kernel, dim3((a.M + 3) / 4), block, 0, s, a);
   return hipGetLastError();
 }
