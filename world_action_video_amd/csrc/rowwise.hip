@@ -979,10 +979,10 @@ hipError_t launch_unipc_step(const UnipcArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------------------------------------------------
 // Output heads. A workgroup takes 16 rows and one K slice (at most 320 columns): the slice of both
-// head matrices goes to LDS once with coalesced 16-byte loads (video head rows 0 .. P-1, action head
-// rows 64 .. 64+A-1, rows padded by 8 elements so a wave's 64 row reads hit distinct banks), then
-// each wave computes 4 rows, lane n accumulating output n of each from LDS weight row n (fp32, k in
-// order). The second kernel sums the slices in order, adds the bias and writes the row to its
+// head matrices and of the 16 rows goes to LDS once with coalesced 16-byte loads (video head rows
+// 0 .. P-1, action head rows 64 .. 64+A-1, the activation rows after them; rows padded by 8
+// elements so a wave's 64 weight-row reads hit distinct banks), then each wave computes 4 rows, lane
+// n accumulating output n of each from LDS weight row n (fp32, k in order). The second kernel sums the slices in order, adds the bias and writes the row to its
 // token-group output.
 // ------------------------------------------------------------------------------------------------
 constexpr int HEAD_ROWS = 16, HEAD_KMAX = 320;
@@ -995,11 +995,20 @@ __global__ void __launch_bounds__(256) head_partial_kernel(HeadArgs a) {
   const int m0 = blockIdx.x * HEAD_ROWS, sp = blockIdx.y;
   const int kspan = a.D / a.splits, k0 = sp * kspan, pitch = kspan + 8;
   const int groups = kspan / 8;                              // 8-element groups per weight row
-  for (int x = threadIdx.x; x < (a.P + a.A) * groups; x += 256) {
+  T* yl = wl + (64 + a.A) * pitch;                          // the workgroup's activation rows
+  for (int x = threadIdx.x; x < (a.P + a.A + HEAD_ROWS) * groups; x += 256) {
     const int r = x / groups, gidx = x % groups;
-    const bool vrow = r < a.P;
-    const T* src = reinterpret_cast<const T*>(vrow ? a.wv : a.wa) + (long)(vrow ? r : r - a.P) * a.D + k0 + gidx * 8;
-    T* dst = wl + (vrow ? r : 64 + r - a.P) * pitch + gidx * 8;
+    const T* src;
+    T* dst;
+    if (r < a.P + a.A) {
+      const bool vrow = r < a.P;
+      src = reinterpret_cast<const T*>(vrow ? a.wv : a.wa) + (long)(vrow ? r : r - a.P) * a.D + k0 + gidx * 8;
+      dst = wl + (vrow ? r : 64 + r - a.P) * pitch + gidx * 8;
+    } else {
+      const int yr = r - a.P - a.A;
+      src = reinterpret_cast<const T*>(a.Y) + (long)min(m0 + yr, a.M - 1) * a.D + k0 + gidx * 8;
+      dst = yl + yr * pitch + gidx * 8;
+    }
 #pragma unroll
     for (int u = 0; u < 8 / EPU; ++u) reinterpret_cast<uint4*>(dst)[u] = reinterpret_cast<const uint4*>(src)[u];
   }
@@ -1015,7 +1024,7 @@ __global__ void __launch_bounds__(256) head_partial_kernel(HeadArgs a) {
     const bool video = (m % a.rm.rows_per_branch) % a.rm.Lq < a.rm.Lv;
     act[r] = mb + r < a.M && n < (video ? a.P : a.A);
     wrow[r] = wl + (video ? n : 64 + min(n, a.A - 1)) * pitch;
-    yrow[r] = reinterpret_cast<const T*>(a.Y) + (long)m * a.D + k0;
+    yrow[r] = yl + (mb + r - m0 < HEAD_ROWS ? mb + r - m0 : 0) * pitch;
   }
   for (int k = 0; k < kspan; k += 8) {
 #pragma unroll
@@ -1065,7 +1074,7 @@ hipError_t launch_head(const HeadArgs& a0, DType dt, hipStream_t s) {
   // (and whose weight slices fit the 64 KB of dynamic LDS)
   HeadArgs a = a0;
   const size_t esz = dt == DT_BF16 ? 2 : 4;
-  auto lds_of = [&](int sp) { return (size_t)(64 + a.A) * (a.D / sp + 8) * esz; };
+  auto lds_of = [&](int sp) { return (size_t)(64 + a.A + HEAD_ROWS) * (a.D / sp + 8) * esz; };
   a.splits = 1;
   while (a.splits <= a.D / 8 && (a.D / a.splits > HEAD_KMAX || a.D % (8 * a.splits) || lds_of(a.splits) > 65536))
     ++a.splits;
