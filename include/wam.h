@@ -222,11 +222,19 @@ wam_status wam_kv_append(const wam_config *cfg, const wam_weights *w, wam_kv_cac
  * norm -> cross-attention -> residual -> norm -> FFN -> residual) on the residual stream
  *   h:  [branches][n_chunks * Lq][D] float, updated in place
  *   e6: [n_chunks][2][6][D] float (device): shared time modulation per chunk and token group
- *       (0 = video, 1 = action), e.g. from wam_time_embed with t = {t_v0, t_a0, t_v1, ...}
- * `layer` selects the layer's slices of the caches; keys/values go to rows [length, length+n*Lq). */
+ *       (0 = video, 1 = action), e.g. from wam_time_embed with t = {t_v0, t_a0, t_v1, ...}; the
+ *       block adds its own mod offset
+ * `layer` selects the layer's slices of the caches; this block's keys/values (after RMSNorm and
+ * RoPE) go to rows [length, length + n_chunks * Lq) of that layer, and the queries attend to the
+ * committed rows and to these rows under the chunk-causal rule of wam_dit_stack_fwd.
+ * commit != 0 ([WS1] architecture: the DiT runner maintains the attention KV): once everything is
+ * enqueued, cache->length += n_chunks * Lq. The length is shared by all layers, so a caller that runs
+ * the stack block by block passes commit only with its last block, after every layer has written
+ * its rows at the same length (as wam_kv_append does in one call). Errors as wam_dit_stack_fwd
+ * (nothing enqueued, length unchanged). */
 wam_status wam_dit_block_fwd(const wam_config *cfg, const wam_block_weights *bw, int layer, wam_kv_cache *cache,
                              const wam_ctx_kv *ctx, float *h, const float *e6, int n_chunks, int start_frame,
-                             void *ws, size_t ws_bytes, void *stream);
+                             int commit, void *ws, size_t ws_bytes, void *stream);
 
 /* Guidance + Euler + similarity ([N569]: conditional/unconditional passes combined; DiT caching
  * by the cosine similarity of successive velocities).

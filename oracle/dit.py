@@ -522,6 +522,57 @@ def stack_forward(model: Model, cache: KVCache, ctx_kv: List[Tuple[Array, Array]
     return head_forward(w, g, h, e, n_chunks)
 
 
+@dataclass
+class PassSpec:
+    """One stack pass for ``stack_passes``: its chunks' latents and timesteps as for stack_forward,
+    whether it commits its keys/values, and whether its head outputs are wanted."""
+    x_video: Array
+    x_action: Array
+    t_video: Sequence[float]
+    t_action: Sequence[float]
+    n_chunks: int
+    start_frame: int
+    commit: bool = False
+    heads: bool = True
+
+
+def stack_passes(model: Model, ctx: Array, passes: Sequence[PassSpec], dt=np.float32,
+                 cache: Optional[KVCache] = None, progress=None) -> List[Optional[Tuple[Array, Array]]]:
+    """Several stack passes in the given order, each seeing the KV cache as the earlier passes left
+    it: the result equals calling stack_forward for each pass in turn (commit appends a pass's
+    keys/values, kv_append is a committing pass at t = 1 without heads). A pass's block l depends on
+    the earlier passes only through their layer-l keys/values, so the passes advance together layer
+    by layer: each layer's weights (``model.layers[l]``, which may be drawn on demand) and its
+    condition keys/values (from ``ctx`` [br, Lc, D], as context_kv) are formed once and dropped after
+    use. ``cache`` (default: empty) is extended in place. Returns per pass (v_video, v_action), or
+    None where heads=False. ``progress(l)`` is called after each layer."""
+    w, g = model.w, model.g
+    br = w.branches
+    L = len(model.layers)
+    if cache is None:
+        cache = KVCache.empty(L, br, w.dim, dt)
+    states = []
+    for p in passes:
+        e6, e = per_token_time(w, g, p.t_video, p.t_action, p.n_chunks, dt)
+        h0 = embed_tokens(g, p.x_video.astype(dt), p.x_action.astype(dt), w, p.n_chunks)
+        h = np.broadcast_to(h0[None], (br,) + h0.shape).astype(dt).copy()
+        states.append([h, e6, e, video_positions(w, p.n_chunks, p.start_frame)])
+    for l in range(L):
+        lp = model.layers[l]
+        ck, cv = context_kv(w, lp, ctx)
+        kc, vc = cache.k[l].astype(dt), cache.v[l].astype(dt)
+        for st, p in zip(states, passes):
+            st[0], kn, vn = block_forward(w, lp, st[0], st[1], ck, cv, kc, vc, p.n_chunks, st[3])
+            if p.commit:
+                kc = np.concatenate([kc, kn], axis=1)
+                vc = np.concatenate([vc, vn], axis=1)
+        cache.k[l], cache.v[l] = kc, vc
+        del lp, ck, cv
+        if progress is not None:
+            progress(l)
+    return [head_forward(w, g, st[0], st[2], p.n_chunks) if p.heads else None for st, p in zip(states, passes)]
+
+
 def kv_append(model: Model, cache: KVCache, ctx_kv, x_video: Array, x_action: Array,
               start_frame: int, dt=np.float32) -> None:
     """Commit one clean chunk: a stack pass at t_video = t_action = 1 whose keys/values are
@@ -623,6 +674,33 @@ def denoise_chunk(dit, x_video: Array, x_action: Array, grid: Sequence[float], t
 # ----------------------------------------------------------------------------------------------
 # Loading the synthetic weights as float arrays
 # ----------------------------------------------------------------------------------------------
+
+class LazyLayers:
+    """The per-layer weights of a workload, drawn from ``synth`` each time a layer is asked for and
+    not kept: a 40-layer model in float32 is 57 GB, one layer 1.4 GB."""
+
+    def __init__(self, w, dt=np.float32):
+        self.w, self.dt = w, dt
+
+    def __len__(self) -> int:
+        return self.w.layers
+
+    def __getitem__(self, l: int) -> Dict[str, Array]:
+        from synth.workloads import draw, layer_tensors
+        if not 0 <= l < self.w.layers:
+            raise IndexError(l)
+        return {s[0]: draw(self.w, l, s, "f32").astype(self.dt) for s in layer_tensors(self.w)}
+
+    def __iter__(self):
+        return (self[l] for l in range(len(self)))
+
+
+def load_model_lazy(w, dt=np.float32) -> Model:
+    """As load_model, with the layers drawn on demand (LazyLayers)."""
+    from synth.workloads import draw, global_tensors
+    g = {s[0]: draw(w, -1, s, "f32").astype(dt) for s in global_tensors(w)}
+    return Model(w, g, LazyLayers(w, dt))
+
 
 def load_model(w, dt=np.float32, layers: Optional[Sequence[int]] = None) -> Model:
     """Draw the workload's weights (bf16-representable values) from ``synth`` as ``dt`` arrays."""

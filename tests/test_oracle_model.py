@@ -392,3 +392,33 @@ def test_state_rows_in_the_condition_sequence(tiny):
     ctx_t = np.concatenate([ctx[:, :-1], ctx[:, -1:]], axis=1)
     vt, at = step(ctx_t, wt)
     assert np.array_equal(v0, vt) and np.array_equal(a0, at)
+
+
+def test_layer_major_passes_equal_sequential_calls(tiny):
+    # stack_passes runs appends and steps together layer by layer (each layer's weights drawn once);
+    # it must give exactly what kv_append / stack_forward give called one after another, and the lazily
+    # drawn layers must be the eagerly drawn ones.
+    w, m, txt, ckv, x1v, x1a, epv, epa = tiny
+    Fc = w.frames_per_chunk
+    cache = O.KVCache.empty(len(m.layers), w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    O.kv_append(m, cache, ckv, x1v[1], x1a[1], Fc)
+    ref = O.stack_forward(m, cache, ckv, epv[2], epa[2], [0.35], [0.6], 1, 2 * Fc)
+    ref2 = O.stack_forward(m, cache, ckv, np.concatenate([epv[0], epv[1]]), np.concatenate([epa[0], epa[1]]),
+                           [0.2, 0.7], [0.4, 0.9], 2, 2 * Fc)
+    lazy = O.load_model_lazy(w)
+    for model in (m, lazy):
+        ctx = O.build_context(w, model.g, txt, None)
+        passes = [O.PassSpec(x1v[0], x1a[0], [1.0], [1.0], 1, 0, commit=True, heads=False),
+                  O.PassSpec(x1v[1], x1a[1], [1.0], [1.0], 1, Fc, commit=True, heads=False),
+                  O.PassSpec(epv[2], epa[2], [0.35], [0.6], 1, 2 * Fc),
+                  O.PassSpec(np.concatenate([epv[0], epv[1]]), np.concatenate([epa[0], epa[1]]), [0.2, 0.7],
+                             [0.4, 0.9], 2, 2 * Fc)]
+        c2 = O.KVCache.empty(len(model.layers), w.branches, w.dim)
+        seen = []
+        outs = O.stack_passes(model, ctx, passes, cache=c2, progress=seen.append)
+        assert seen == list(range(w.layers)) and outs[0] is None and outs[1] is None
+        for got, want in ((outs[2], ref), (outs[3], ref2)):
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+        for l in range(w.layers):
+            assert np.array_equal(c2.k[l], cache.k[l]) and np.array_equal(c2.v[l], cache.v[l])

@@ -96,7 +96,7 @@ def load(path: str = LIB_PATH):
         "wam_time_embed": (I, [CFG, W, P, I, P, P, P, S, P]),
         "wam_dit_stack_fwd": (I, [CFG, W, KV, CX, I, P, P, P, P, I, P, P, P, S, P]),
         "wam_kv_append": (I, [CFG, W, KV, CX, P, P, I, P, S, P]),
-        "wam_dit_block_fwd": (I, [CFG, ctypes.POINTER(wam_block_weights), I, KV, CX, P, P, I, I, P, S, P]),
+        "wam_dit_block_fwd": (I, [CFG, ctypes.POINTER(wam_block_weights), I, KV, CX, P, P, I, I, I, P, S, P]),
         "wam_flow_step": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P, S, P]),
         "wam_denoise_chunk": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, P, P, P, P, P, P, S, P, P, P]),
         "wam_denoise_chunk_unipc": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, I, I, P, P, P, P, P, P, P, S, P, P,
@@ -186,10 +186,11 @@ def wam_kv_append(cfg, w, cache: wam_kv_cache, ctx: wam_ctx_kv, x_video, x_actio
                                 _ptr(x_video), _ptr(x_action), start_frame, _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def wam_dit_block_fwd(cfg, bw: wam_block_weights, layer, cache, ctx, h, e6, n_chunks, start_frame, ws, stream=None):
+def wam_dit_block_fwd(cfg, bw: wam_block_weights, layer, cache, ctx, h, e6, n_chunks, start_frame, ws, stream=None,
+                      commit=False):
     _check(load().wam_dit_block_fwd(ctypes.byref(cfg), ctypes.byref(bw), layer, ctypes.byref(cache),
-                                    ctypes.byref(ctx), _ptr(h), _ptr(e6), n_chunks, start_frame, _ptr(ws),
-                                    _nbytes(ws), _stream(stream)))
+                                    ctypes.byref(ctx), _ptr(h), _ptr(e6), n_chunks, start_frame, 1 if commit else 0,
+                                    _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def wam_flow_step(x_video, x_action, v_video, v_action, branches, guidance, n_video, n_action, dt_video, dt_action,

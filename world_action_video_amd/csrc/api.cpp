@@ -735,8 +735,8 @@ wam_status wam_kv_append(const wam_config* cfg, const wam_weights* w, wam_kv_cac
 }
 
 wam_status wam_dit_block_fwd(const wam_config* cfg, const wam_block_weights* bw, int layer, wam_kv_cache* cache,
-                             const wam_ctx_kv* ctx, float* h, const float* e6, int n_chunks, int start_frame, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             const wam_ctx_kv* ctx, float* h, const float* e6, int n_chunks, int start_frame, int commit,
+                             void* ws, size_t ws_bytes, void* stream) {
   CHECK(check_cfg(cfg));
   const Geo g = geo_of(*cfg);
   if (layer < 0 || layer >= g.L) return fail(WAM_E_ARG, "layer %d out of range", layer);
@@ -753,7 +753,9 @@ wam_status wam_dit_block_fwd(const wam_config* cfg, const wam_block_weights* bw,
   p.cx = ctx; p.h = h; p.e6 = e6; p.rope = at<float2>(ws, L.rope); p.s = reinterpret_cast<hipStream_t>(stream);
   HIP_TRY(launch_rope_table(p.rope, n_chunks, g.Lq, g.Lv, cfg->frames_per_chunk, cfg->grid_h, cfg->grid_w, start_frame,
                             g.d, cfg->rope_theta, p.s));
-  return run_block(p, *bw, layer, false, false, nullptr);
+  CHECK(run_block(p, *bw, layer, false, false, nullptr));
+  if (commit) cache->length += n_chunks * g.Lq;
+  return WAM_OK;
 }
 
 wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, const float* v_action, int branches,
