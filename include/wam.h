@@ -252,6 +252,20 @@ wam_status wam_flow_step(float *x_video, float *x_action, const float *v_video, 
                          float *g_video, float *g_action, const float *prev_video, float *cos_parts, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): wam_flow_step without a workspace. The cosine partials go to a
+ * device scratch array owned by the library, 6144 bytes (512 workgroups x 3 floats) on each GPU it
+ * runs on, held until the process ends; the call never allocates or frees memory. Every size
+ * wam_flow_step accepts fits that scratch (its grid is capped at 512 workgroups); a larger need is
+ * rejected with WAM_E_ARG. All calls on one GPU share the scratch, which keeps the last call's
+ * partials: calls that overlap on one GPU (different streams, or threads without ordering) race.
+ * Nothing in it needs clearing: each call writes every partial it reads. Arguments, results and
+ * errors otherwise as wam_flow_step (bit-identical results for the same inputs). */
+wam_status wam_flow_step_noalloc(float *x_video, float *x_action, const float *v_video, const float *v_action,
+                                 int branches, float guidance, int n_video, int n_action, float dt_video,
+                                 float dt_action, float *g_video, float *g_action, const float *prev_video,
+                                 float *cos_parts, void *stream);
+
 /* One chunk's denoising loop ([N569] dynamic DiT caching; [WS1] dynamic16 scheduler): n_steps Euler
  * steps over the host times grid[0..n_steps] (both token groups at grid[k]), CFG with `guidance`,
  * with velocity reuse: steps 0 and 1 always run the DiT; at step k >= 2, if the cosine similarity of

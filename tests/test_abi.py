@@ -118,6 +118,13 @@ def test_op_validation():
                              None) == wam.WAM_E_SHAPE
     assert lib.wam_flow_step(0x1000, 0x1000, 0x1000, 0x1000, 2, 5.0, 4, 4, 0.1, 0.1, None, None, 0x1000, None, None, 0,
                              None) == wam.WAM_E_ARG
+    # the allocation-free variant validates the same way before touching its scratch
+    assert lib.wam_flow_step_noalloc(0x1000, 0x1000, 0x1000, 0x1000, 3, 5.0, 4, 4, 0.1, 0.1, None, None, None, None,
+                                     None) == wam.WAM_E_SHAPE
+    assert lib.wam_flow_step_noalloc(0x1000, 0x1000, 0x1000, 0x1000, 2, 5.0, 4, 4, 0.1, 0.1, None, None, 0x1000, None,
+                                     None) == wam.WAM_E_ARG
+    assert lib.wam_flow_step_noalloc(None, 0x1000, 0x1000, 0x1000, 2, 5.0, 4, 4, 0.1, 0.1, None, None, None, None,
+                                     None) == wam.WAM_E_ARG
 
 
 def test_attention_mx_validation():

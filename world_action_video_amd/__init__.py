@@ -22,7 +22,7 @@ EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_tim
            "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear",
            "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error",
-           "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx")
+           "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx", "wam_flow_step_noalloc")
 
 
 class WamError(RuntimeError):
@@ -98,6 +98,7 @@ def load(path: str = LIB_PATH):
         "wam_kv_append": (I, [CFG, W, KV, CX, P, P, I, P, S, P]),
         "wam_dit_block_fwd": (I, [CFG, ctypes.POINTER(wam_block_weights), I, KV, CX, P, P, I, I, I, P, S, P]),
         "wam_flow_step": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P, S, P]),
+        "wam_flow_step_noalloc": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P]),
         "wam_denoise_chunk": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, P, P, P, P, P, P, S, P, P, P]),
         "wam_denoise_chunk_unipc": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, I, I, P, P, P, P, P, P, P, S, P, P,
                                         P]),
@@ -199,6 +200,14 @@ def wam_flow_step(x_video, x_action, v_video, v_action, branches, guidance, n_vi
                                 float(guidance), n_video, n_action, float(dt_video), float(dt_action), _ptr(g_video),
                                 _ptr(g_action), _ptr(prev_video), _ptr(cos_parts), _ptr(ws), _nbytes(ws),
                                 _stream(stream)))
+
+
+def wam_flow_step_noalloc(x_video, x_action, v_video, v_action, branches, guidance, n_video, n_action, dt_video,
+                          dt_action, g_video=None, g_action=None, prev_video=None, cos_parts=None, stream=None):
+    _check(load().wam_flow_step_noalloc(_ptr(x_video), _ptr(x_action), _ptr(v_video), _ptr(v_action), branches,
+                                        float(guidance), n_video, n_action, float(dt_video), float(dt_action),
+                                        _ptr(g_video), _ptr(g_action), _ptr(prev_video), _ptr(cos_parts),
+                                        _stream(stream)))
 
 
 def wam_denoise_chunk(cfg, weights, cache, ctx, x_video, x_action, grid, guidance, tau, v_video, v_action, g_video,

@@ -758,10 +758,16 @@ wam_status wam_dit_block_fwd(const wam_config* cfg, const wam_block_weights* bw,
   return WAM_OK;
 }
 
-wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, const float* v_action, int branches,
-                         float guidance, int n_video, int n_action, float dt_video, float dt_action, float* g_video,
-                         float* g_action, const float* prev_video, float* cos_parts, void* ws, size_t ws_bytes,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by wam_flow_step and wam_flow_step_noalloc: the cosine partials go to
+// the caller's workspace (ws, ws_bytes), or with library_scratch to the library's device scratch.
+wam_status flow_step(float* x_video, float* x_action, const float* v_video, const float* v_action, int branches,
+                     float guidance, int n_video, int n_action, float dt_video, float dt_action, float* g_video,
+                     float* g_action, const float* prev_video, float* cos_parts, void* ws, size_t ws_bytes,
+                     bool library_scratch, void* stream) {
   if (branches != 1 && branches != 2) return fail(WAM_E_SHAPE, "branches must be 1 or 2");
   if (n_video < 0 || n_action < 0) return fail(WAM_E_SHAPE, "negative sizes");
   if ((n_video && (!x_video || !v_video)) || (n_action && (!x_action || !v_action)))
@@ -771,14 +777,43 @@ wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, 
     return fail(WAM_E_ARG, "non-finite scalar");
   const int nblocks = flow_partial_blocks(n_video, n_action);
   const size_t need = (size_t)nblocks * 3 * 4;
-  if (prev_video && (!ws || ws_bytes < need)) return fail(WAM_E_ARG, "workspace too small for the cosine partials");
+  float* partials = nullptr;
+  if (prev_video && library_scratch) {
+    size_t have = 0;
+    HIP_TRY(flow_scratch(&partials, &have));
+    if (need > have)
+      return fail(WAM_E_ARG, "cosine partials need %zu bytes, above the %zu-byte library scratch", need, have);
+  } else if (prev_video) {
+    if (!ws || ws_bytes < need) return fail(WAM_E_ARG, "workspace too small for the cosine partials");
+    partials = reinterpret_cast<float*>(ws);
+  }
   FlowArgs fa{};
   fa.xv = x_video; fa.xa = x_action; fa.vv = v_video; fa.va = v_action; fa.br = branches; fa.w = guidance;
   fa.nv = n_video; fa.na = n_action; fa.dtv = dt_video; fa.dta = dt_action; fa.gv = g_video; fa.ga = g_action;
-  fa.prev = prev_video; fa.partials = prev_video ? reinterpret_cast<float*>(ws) : nullptr; fa.cos_parts = cos_parts;
+  fa.prev = prev_video; fa.partials = partials; fa.cos_parts = cos_parts;
   fa.nblocks = nblocks;
   HIP_TRY(launch_flow_step(fa, reinterpret_cast<hipStream_t>(stream)));
   return WAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+wam_status wam_flow_step(float* x_video, float* x_action, const float* v_video, const float* v_action, int branches,
+                         float guidance, int n_video, int n_action, float dt_video, float dt_action, float* g_video,
+                         float* g_action, const float* prev_video, float* cos_parts, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return flow_step(x_video, x_action, v_video, v_action, branches, guidance, n_video, n_action, dt_video, dt_action,
+                   g_video, g_action, prev_video, cos_parts, ws, ws_bytes, false, stream);
+}
+
+wam_status wam_flow_step_noalloc(float* x_video, float* x_action, const float* v_video, const float* v_action,
+                                 int branches, float guidance, int n_video, int n_action, float dt_video,
+                                 float dt_action, float* g_video, float* g_action, const float* prev_video,
+                                 float* cos_parts, void* stream) {
+  return flow_step(x_video, x_action, v_video, v_action, branches, guidance, n_video, n_action, dt_video, dt_action,
+                   g_video, g_action, prev_video, cos_parts, nullptr, 0, true, stream);
 }
 
 // ---- solvers of the denoising loop ------------------------------------------------------------------

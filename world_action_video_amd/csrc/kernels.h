@@ -266,5 +266,7 @@ struct HeadArgs {
 hipError_t launch_head(const HeadArgs& a, DType dt, hipStream_t s);
 // workgroups (and [3] partial-sum slots) of the flow step for these sizes: 1 .. 512
 int flow_partial_blocks(int nv, int na);
+// Device address (for the current device) and size of the library-owned flow-step scratch.
+hipError_t flow_scratch(float** ptr, size_t* bytes);
 
 }  // namespace wam

@@ -2,6 +2,8 @@
 // rotary embedding with the head-major / KV-cache scatter, the value transpose into the cache,
 // the rotary table, token embedding, the time-embedding MLP and the fused CFG + Euler + cosine
 // update. All statistics are accumulated in fp32 with a fixed reduction order (deterministic).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -912,6 +914,34 @@ hipError_t launch_flow_step(const FlowArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL(flow_kernel<1>, dim3(nb), dim3(256), 0, s, a);
   if (a.prev && a.cos_parts) hipLaunchKernelGGL(flow_reduce_kernel, dim3(1), dim3(64), 0, s, a.partials, nb, a.cos_parts);
   return hipGetLastError();
+}
+
+// Library-owned scratch of the allocation-free flow step (wam_flow_step_noalloc): the per-workgroup
+// cosine partials of one call, FLOW_MAX_BLOCKS x 3 floats (6 KB). Each GPU holds its own copy; host
+// code reaches it only through the address that hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept (the array's name is not a device address on the host).
+constexpr size_t kFlowScratchFloats = (size_t)FLOW_MAX_BLOCKS * 3;
+static __device__ __align__(256) float scratch[kFlowScratchFloats];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static float* g_scratch_ptr[kMaxDevices];   // per device, nullptr until looked up
+
+hipError_t flow_scratch(float** ptr, size_t* bytes) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kFlowScratchFloats * sizeof(float);
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------------------------------------------
