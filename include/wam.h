@@ -287,6 +287,22 @@ wam_status wam_denoise_chunk(const wam_config *cfg, const wam_weights *w, wam_kv
                              float *g_video, float *g_action, float *cos_parts, void *ws, size_t ws_bytes,
                              void *stream, int *dit_calls, unsigned char *reused);
 
+/* The Euler loop of wam_denoise_chunk with the reuse decisions given instead of taken: step k reuses
+ * the latest computed guided velocities iff replay[k] != 0 (host, n_steps bytes; replay[0] and
+ * replay[1] must be 0: the first two steps always run the DiT). For decisions another implementation
+ * took, e.g. when a similarity lies so close to the threshold that rounding may flip it ([N569] DiT
+ * caching: the rule compares a similarity with a predefined threshold).
+ *   cosines (host, n_steps floats, may be NULL): the similarity the rule would compare at step k (of
+ *   the two most recent DiT-computed guided video velocities), NaN where it compares none (k < 2).
+ *   With cosines the call synchronises `stream` once per DiT pass (12 bytes read back); without, never.
+ * Other arguments, results and errors as wam_denoise_chunk; WAM_E_ARG for a NULL mask or a set
+ * replay[0] / replay[1], nothing enqueued then. */
+wam_status wam_denoise_chunk_replay(const wam_config *cfg, const wam_weights *w, wam_kv_cache *cache,
+                                    const wam_ctx_kv *ctx, float *x_video, float *x_action, const float *grid,
+                                    int n_steps, float guidance, const unsigned char *replay, int start_frame,
+                                    float *v_video, float *v_action, float *g_video, float *g_action, float *cos_parts,
+                                    void *ws, size_t ws_bytes, void *stream, int *dit_calls, float *cosines);
+
 /* The same loop with the UniPC solver in place of Euler ([WS1] names UniPC as the scheduler's
  * solver; no formula on the pages: the published predictor UniP-p / corrector UniC-p in
  * data-prediction form with B(h) = e^h - 1, for alpha_t = t, sigma_t = 1 - t, lambda_t =

@@ -637,13 +637,14 @@ def cosine_fp64(a: Array, b: Array) -> float:
 
 
 def denoise_chunk(dit, x_video: Array, x_action: Array, grid: Sequence[float], tau: float,
-                  max_consecutive_reuse: Optional[int] = None):
+                  max_consecutive_reuse: Optional[int] = None, trace: Optional[list] = None):
     """Euler loop with velocity reuse ([N569] DiT caching; [WS1] dynamic16).
 
     dit(x_video, x_action, t) -> guided (v_video, v_action). Steps 0 and 1 always run the DiT;
     at step k >= 2, if the cosine similarity of the two most recent DiT-computed guided video
     velocities exceeds tau, the DiT is skipped and the latest computed velocity is reused
-    (reading R15). Returns (x_video, x_action, number of DiT calls, per-step flags).
+    (reading R15). Returns (x_video, x_action, number of DiT calls, per-step flags). ``trace``, if
+    given, receives (k, cosine) for every step whose decision evaluated a cosine.
     """
     computed: List[Tuple[Array, Array]] = []
     calls = 0
@@ -655,6 +656,8 @@ def denoise_chunk(dit, x_video: Array, x_action: Array, grid: Sequence[float], t
         reuse = False
         if k >= 2 and len(computed) >= 2:
             c = cosine_fp64(computed[-1][0], computed[-2][0])
+            if trace is not None:
+                trace.append((k, c))
             if c > tau and (max_consecutive_reuse is None or consecutive < max_consecutive_reuse):
                 reuse = True
         if reuse:

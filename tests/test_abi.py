@@ -315,3 +315,21 @@ def test_denoise_chunk_unipc_validation():
     assert call(outside, 2) == wam.WAM_E_ARG
     # valid loop arguments: the first DiT pass rejects the missing weights
     assert call(grid, 2) == wam.WAM_E_ARG and "weights" in wam.wam_last_error()
+
+
+def test_denoise_chunk_replay_validation():
+    """The replay loop rejects a NULL mask and a mask that skips step 0 or 1, before any launch."""
+    import ctypes
+    lib = _lib()
+    c = _cfg(1)
+    wts = wam.wam_weights()
+    kv = wam.wam_kv_cache(0x1000, 0x1000, 2, 256, 0)
+    cx = wam.wam_ctx_kv(0x1000, 0x1000, 2, 32, 64)
+    grid = (ctypes.c_float * 3)(0.0, 0.5, 1.0)
+    for mask in (None, (ctypes.c_ubyte * 2)(1, 0), (ctypes.c_ubyte * 2)(0, 1)):
+        st = lib.wam_denoise_chunk_replay(ctypes.byref(c), ctypes.byref(wts), ctypes.byref(kv), ctypes.byref(cx),
+                                          0x1000, 0x1000, ctypes.cast(grid, ctypes.c_void_p), 2, 5.0,
+                                          None if mask is None else ctypes.cast(mask, ctypes.c_void_p), 0, 0x1000,
+                                          0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 30, None, None, None)
+        assert st == wam.WAM_E_ARG, st
+

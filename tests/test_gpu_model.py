@@ -629,3 +629,90 @@ def test_kv_evict_matches_oracle(gpu, tiny_oracle, dtype):
     ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
     print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
     assert ev <= TOL[dtype] and ea <= TOL[dtype]
+
+
+# Reuse decisions taken on real cosines of the tiny model (seeded inputs; the oracle's cosines of
+# successive guided velocities lie in 0.994 .. 0.9988 on these grids). Each "decide" case's threshold
+# sits where the oracle's run decides by the cosine (some later steps reuse, some do not), 1.5e-4 to
+# 3e-4 from every cosine it compares. A decision is unique when both implementations' cosines lie on
+# the same side of tau: the GPU first replays the oracle's mask and reports the cosines it compares
+# along it; then, if every one is on the oracle's side, its own loop must take exactly the oracle's
+# decisions. The cosines agree within 1e-4 in fp32; in bf16 the first-order bound is
+# |d cos| <= (e_a + e_b) sin(theta) with e = 2e-2, the bf16 bar on the velocities.
+_G8 = [k / 8 for k in range(9)]
+_G6 = [0.0, 0.1, 0.25, 0.45, 0.7, 0.85, 1.0]
+_REUSE_CASES = [("g8", _G8, 0.998012, -1, "decide"), ("g8", _G8, 0.997458, 1, "decide"),
+                ("g6", _G6, 0.994261, 1, "decide"), ("g8", _G8, None, -1, "replay")]
+_REUSE_REF = {}
+
+
+def _oracle_reuse(tiny_oracle, name, grid, tau, max_reuse):
+    w, m, ckv = tiny_oracle
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+
+    def dit(xv, xa, t):
+        vb, ab = O.stack_forward(m, cache, ckv, xv, xa, [t], [t], 1, w.frames_per_chunk)
+        return O.cfg_combine(vb, w.guidance), O.cfg_combine(ab, w.guidance)
+    if tau is None:   # a threshold on top of an observed cosine: only the replay applies
+        trace = []
+        O.denoise_chunk(dit, epv[1], epa[1], grid, 1.5, trace=trace)
+        tau = trace[0][1]
+    trace = []
+    xv, xa, calls, flags = O.denoise_chunk(dit, epv[1], epa[1], grid, tau, None if max_reuse < 0 else max_reuse,
+                                           trace=trace)
+    return tau, xv, xa, calls, flags, trace
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", range(len(_REUSE_CASES)))
+def test_reuse_decisions_on_real_cosines(gpu, tiny_oracle, dtype, case):
+    name, grid, tau0, max_reuse, path = _REUSE_CASES[case]
+    if case not in _REUSE_REF:
+        _REUSE_REF[case] = _oracle_reuse(tiny_oracle, name, grid, tau0, max_reuse)
+    tau, ref_v, ref_a, n_ref, flags_ref, trace = _REUSE_REF[case]
+    w = tiny_oracle[0]
+    margin = min(abs(c - tau) for _, c in trace)
+    sin_max = max(np.sqrt(max(0.0, 1.0 - c * c)) for _, c in trace)
+    band = 1e-4 if dtype == "f32" else 2 * TOL["bf16"] * sin_max
+    print("reuse", dtype, name, "tau %.6f" % tau, "max_reuse", max_reuse, "margin %.2e" % margin,
+          "flags", "".join("R" if f else "." for f in flags_ref), flush=True)
+    if path == "decide":   # the cosine really decides: some steps reuse and some do not after step 1
+        assert margin > 1e-4 and any(flags_ref[2:]) and not all(flags_ref[2:])
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    rig = Rig(w, dtype, gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    br = rig.m.cfg.branches
+    bufs = lambda: (torch.empty((br, w.video_tokens, w.patch_dim), device=gpu),  # noqa: E731
+                    torch.empty((br, w.action_tokens, w.action_dim), device=gpu),
+                    torch.empty(w.video_tokens * w.patch_dim, device=gpu),
+                    torch.empty(w.action_tokens * w.action_dim, device=gpu), torch.empty(3, device=gpu))
+    # the oracle's decisions replayed, with the cosines the GPU compares along them
+    xv, xa = rig.f32(epv[1]), rig.f32(epa[1])
+    calls, cos = wam.wam_denoise_chunk_replay(rig.m.cfg, rig.m.weights, dc.c, rig.ctx.c, xv, xa, grid, w.guidance,
+                                              flags_ref, *bufs(), rig.ws, start_frame=w.frames_per_chunk)
+    torch.cuda.synchronize()
+    assert calls == n_ref
+    ev, ea = rel_l2(xv.cpu().numpy(), ref_v), rel_l2(xa.cpu().numpy(), ref_a)
+    dcos = max(abs(cos[k] - c) for k, c in trace)
+    evaluated = dict(trace)
+    assert all(np.isnan(cos[k]) for k in range(len(grid) - 1) if k not in evaluated)
+    same_side = all((cos[k] > tau) == (c > tau) for k, c in trace)
+    print("replayed: rel-L2 video %.2e action %.2e; max |cos_gpu - cos_oracle| %.2e (band %.1e); decisions %s"
+          % (ev, ea, dcos, band, "unique" if same_side else "ambiguous"), flush=True)
+    assert ev <= TOL[dtype] and ea <= TOL[dtype]
+    assert dcos <= band
+    if path == "decide" and dtype == "f32":
+        assert same_side   # the margin exceeds the fp32 band
+    if path == "decide" and same_side:   # the library's own decisions must be the oracle's
+        xv2, xa2 = rig.f32(epv[1]), rig.f32(epa[1])
+        calls2, flags = wam.wam_denoise_chunk(rig.m.cfg, rig.m.weights, dc.c, rig.ctx.c, xv2, xa2, grid, w.guidance,
+                                              tau, *bufs(), rig.ws, start_frame=w.frames_per_chunk,
+                                              max_consecutive_reuse=max_reuse)
+        torch.cuda.synchronize()
+        assert flags == list(flags_ref) and calls2 == n_ref
+        # same decisions, same kernels in the same order: the same latents bit for bit
+        assert np.array_equal(xv2.cpu().numpy(), xv.cpu().numpy())
+        assert np.array_equal(xa2.cpu().numpy(), xa.cpu().numpy())

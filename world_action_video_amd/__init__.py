@@ -22,7 +22,8 @@ EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_tim
            "wam_dit_block_fwd", "wam_flow_step", "wam_denoise_chunk", "wam_denoise_chunk_unipc", "wam_op_linear",
            "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error",
-           "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx", "wam_flow_step_noalloc")
+           "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx", "wam_flow_step_noalloc",
+           "wam_denoise_chunk_replay")
 
 
 class WamError(RuntimeError):
@@ -100,6 +101,7 @@ def load(path: str = LIB_PATH):
         "wam_flow_step": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P, S, P]),
         "wam_flow_step_noalloc": (I, [P, P, P, P, I, F, I, I, F, F, P, P, P, P, P]),
         "wam_denoise_chunk": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, P, P, P, P, P, P, S, P, P, P]),
+        "wam_denoise_chunk_replay": (I, [CFG, W, KV, CX, P, P, P, I, F, P, I, P, P, P, P, P, P, S, P, P, P]),
         "wam_denoise_chunk_unipc": (I, [CFG, W, KV, CX, P, P, P, I, F, F, I, I, I, I, P, P, P, P, P, P, P, S, P, P,
                                         P]),
         "wam_op_linear": (I, [I, P, I, P, I, P, P, I, I, I, I, I, P, S, P]),
@@ -225,6 +227,24 @@ def wam_denoise_chunk(cfg, weights, cache, ctx, x_video, x_action, grid, guidanc
                                     _nbytes(ws), _stream(stream), ctypes.cast(ctypes.byref(calls), ctypes.c_void_p),
                                     ctypes.cast(flags, ctypes.c_void_p)))
     return calls.value, [bool(flags[i]) for i in range(n)]
+
+
+def wam_denoise_chunk_replay(cfg, weights, cache, ctx, x_video, x_action, grid, guidance, replay, v_video, v_action,
+                             g_video, g_action, cos_parts, ws, start_frame=0, want_cosines=True, stream=None):
+    """Euler loop following the host reuse mask ``replay`` (n_steps flags). Returns (number of DiT passes,
+    per-step cosines the decision rule would compare, NaN where none; None without want_cosines)."""
+    n = len(grid) - 1
+    g = (ctypes.c_float * (n + 1))(*[float(t) for t in grid])
+    mask = (ctypes.c_ubyte * max(n, 1))(*[1 if f else 0 for f in replay])
+    calls = ctypes.c_int(0)
+    cos = (ctypes.c_float * max(n, 1))()
+    _check(load().wam_denoise_chunk_replay(
+        ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(ctx), _ptr(x_video),
+        _ptr(x_action), ctypes.cast(g, ctypes.c_void_p), n, float(guidance), ctypes.cast(mask, ctypes.c_void_p),
+        int(start_frame), _ptr(v_video), _ptr(v_action), _ptr(g_video), _ptr(g_action), _ptr(cos_parts), _ptr(ws),
+        _nbytes(ws), _stream(stream), ctypes.cast(ctypes.byref(calls), ctypes.c_void_p),
+        ctypes.cast(cos, ctypes.c_void_p) if want_cosines else None))
+    return calls.value, ([float(cos[i]) for i in range(n)] if want_cosines else None)
 
 
 def wam_denoise_chunk_unipc(cfg, weights, cache, ctx, x_video, x_action, grid, guidance, tau, v_video, v_action,

@@ -899,13 +899,17 @@ static wam_status denoise_loop(const wam_config* cfg, const wam_weights* w, wam_
                                float tau, int max_consecutive_reuse, int start_frame, int order, bool corrector,
                                float* v_video, float* v_action, float* g_video, float* g_action, float* cos_parts,
                                float* state, void* ws, size_t ws_bytes, void* stream, int* dit_calls,
-                               unsigned char* reused) {
+                               unsigned char* reused, const unsigned char* replay = nullptr,
+                               float* cos_host = nullptr) {
   CHECK(check_cfg(cfg));
   if (!grid || n_steps < 1) return fail(WAM_E_ARG, "grid must hold n_steps + 1 >= 2 times");
   for (int k = 0; k <= n_steps; ++k)
     if (!std::isfinite(grid[k])) return fail(WAM_E_ARG, "non-finite time in the grid");
   if (!g_video || !g_action || !cos_parts) return fail(WAM_E_ARG, "guided-velocity or cosine buffers are NULL");
   if (!std::isfinite(tau) && !std::isinf(tau)) return fail(WAM_E_ARG, "tau is NaN");
+  if (replay)
+    for (int k = 0; k < std::min(n_steps, 2); ++k)
+      if (replay[k]) return fail(WAM_E_ARG, "steps 0 and 1 always run the DiT: replay[%d] must be 0", k);
   if (order > 0) {
     if (order > 3) return fail(WAM_E_ARG, "UniPC order must be 1, 2 or 3");
     if (!state) return fail(WAM_E_ARG, "UniPC state buffer is NULL");
@@ -918,15 +922,20 @@ static wam_status denoise_loop(const wam_config* cfg, const wam_weights* w, wam_
   const Geo g = geo_of(*cfg);
   const int nv = g.Lv * g.P, na = g.La * g.A;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // reuse needs cos > tau with cos <= 1: a tau above 1 can never trigger it (no host read-back then)
-  const bool may_reuse = tau <= 1.f;
+  // reuse needs cos > tau with cos <= 1: a tau above 1 can never trigger it (no host read-back then);
+  // a replayed mask decides by itself and reads the cosine back only to report it
+  const bool may_reuse = !replay && tau <= 1.f;
+  const bool read_cos = may_reuse || cos_host;
   int computed = 0, consecutive = 0, calls = 0, prev_order = 0;
   double cos_last = -2.0;   // cosine of the two most recent DiT-computed guided video velocities
   for (int k = 0; k < n_steps; ++k) {
     const float t = grid[k], dt = grid[k + 1] - grid[k];
     bool reuse = false;
-    if (may_reuse && k >= 2 && computed >= 2 &&
-        (max_consecutive_reuse < 0 || consecutive < max_consecutive_reuse))
+    if (cos_host) cos_host[k] = k >= 2 && computed >= 2 ? (float)cos_last : NAN;
+    if (replay)
+      reuse = replay[k] != 0;
+    else if (may_reuse && k >= 2 && computed >= 2 &&
+             (max_consecutive_reuse < 0 || consecutive < max_consecutive_reuse))
       reuse = cos_last > (double)tau;
     if (!reuse)
       CHECK(wam_dit_stack_fwd(cfg, w, cache, ctx, 1, x_video, x_action, &t, &t, start_frame, v_video, v_action, ws,
@@ -979,7 +988,7 @@ static wam_status denoise_loop(const wam_config* cfg, const wam_weights* w, wam_
       ++computed;
       ++calls;
       consecutive = 0;
-      if (may_reuse && computed >= 2 && k + 1 < n_steps) {
+      if (read_cos && computed >= 2 && k + 1 < n_steps) {
         float parts[3];
         HIP_TRY(hipMemcpyAsync(parts, cos_parts, sizeof(parts), hipMemcpyDeviceToHost, s));
         HIP_TRY(hipStreamSynchronize(s));
@@ -1001,6 +1010,17 @@ wam_status wam_denoise_chunk(const wam_config* cfg, const wam_weights* w, wam_kv
   return denoise_loop(cfg, w, cache, ctx, x_video, x_action, grid, n_steps, guidance, tau, max_consecutive_reuse,
                       start_frame, 0, false, v_video, v_action, g_video, g_action, cos_parts, nullptr, ws, ws_bytes,
                       stream, dit_calls, reused);
+}
+
+wam_status wam_denoise_chunk_replay(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache,
+                                    const wam_ctx_kv* ctx, float* x_video, float* x_action, const float* grid,
+                                    int n_steps, float guidance, const unsigned char* replay, int start_frame,
+                                    float* v_video, float* v_action, float* g_video, float* g_action, float* cos_parts,
+                                    void* ws, size_t ws_bytes, void* stream, int* dit_calls, float* cosines) {
+  if (!replay) return fail(WAM_E_ARG, "replay mask is NULL");
+  return denoise_loop(cfg, w, cache, ctx, x_video, x_action, grid, n_steps, guidance, 2.f, -1, start_frame, 0, false,
+                      v_video, v_action, g_video, g_action, cos_parts, nullptr, ws, ws_bytes, stream, dit_calls,
+                      nullptr, replay, cosines);
 }
 
 wam_status wam_denoise_chunk_unipc(const wam_config* cfg, const wam_weights* w, wam_kv_cache* cache,
