@@ -104,6 +104,26 @@ def summarize_counters(fetch_db: str, write_db: str):
     print(json.dumps({TRAFFIC_KEY: {"bytes_per_launch": rec["bytes_per_launch"]}}))
 
 
+def summarize_pmc(dbs, name_filter: str):
+    """Mean of every counter per dispatch, per kernel whose name contains ``name_filter``, over the
+    rocprofv3 --pmc databases ``dbs`` (one pass each): a markdown table on stdout."""
+    import sqlite3
+    rows = {}
+    for db in dbs:
+        if not os.path.isfile(db):
+            raise SystemExit("no such database: %s" % db)
+        cur = sqlite3.connect("file:%s?mode=ro" % db, uri=True).cursor()
+        cols = [r[1] for r in cur.execute("pragma table_info(counters_collection)")]
+        name_col = "kernel_name" if "kernel_name" in cols else "name"
+        for n, c, v in cur.execute("select %s, counter_name, value from counters_collection" % name_col):
+            if name_filter in n:
+                rows.setdefault(n, {}).setdefault(c, []).append(float(v))
+    for n, cs in sorted(rows.items()):
+        print("\n`%s`\n\n| counter | dispatches | mean per dispatch |\n|---|---:|---:|" % n)
+        for c, vs in sorted(cs.items()):
+            print("| %s | %d | %.4g |" % (c, len(vs), sum(vs) / len(vs)))
+
+
 def cpu_baseline(w, timed_layers: int = 1) -> dict:
     """The oracle as it stands, timed on this host on a bounded sample: ``timed_layers`` full-width
     blocks of the workload's step (both CFG branches, its cached, current and condition tokens),
@@ -165,10 +185,17 @@ def main():
                          "config-3 block over 1 and 8 chunks (for a kernel trace of its row kernels)")
     ap.add_argument("--attention", action="store_true",
                     help="bf16 and MXFP8 attention kernels at the step's self- and cross-attention shapes")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
+                    help="per-kernel mean of every counter in rocprofv3 --pmc databases (kernels whose name contains "
+                         "--kernel-filter)")
+    ap.add_argument("--kernel-filter", default="", help="substring of the kernel names --summarize-pmc reports")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="turn the two rocprofv3 --pmc databases of a --counters run (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.kernel_filter)
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return

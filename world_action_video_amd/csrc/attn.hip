@@ -263,6 +263,9 @@ attn_kernel(AttnArgs a) {
 // accumulated against the old reference. The final normalisation divides by the sum accumulated
 // against the same reference, so the result is the exact softmax (rescaling is exact up to
 // rounding). The score scale is folded into the exponent: p = exp2(s c - m), c = log2(e)/sqrt(d).
+// The row sum is taken over the bf16-rounded probabilities (dot products of the packed pairs with
+// ones), i.e. over exactly the weights the value product uses, and the tile maximum is a tree of
+// three-input maxima (no NaN-quieting steps: scores are finite or -inf by construction).
 //
 // Keys at or past kv_total read as zero (the copy's buffer range ends there) and are masked; values
 // past kv_total are zeroed in LDS once their tile has landed, so stale rows never meet a zero
@@ -460,6 +463,29 @@ __device__ __forceinline__ void store_output(uint4* smem, const floatx16 (&o)[D 
   }
 }
 
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Row maximum of the 16 scores a lane holds (-inf start), then with the partner lane's 16, in log2 units.
+__device__ __forceinline__ float tile_max(const floatx16& s, float c) {
+  const float a0 = vmax3(s[0], s[1], s[2]), a1 = vmax3(s[3], s[4], s[5]), a2 = vmax3(s[6], s[7], s[8]);
+  const float a3 = vmax3(s[9], s[10], s[11]), a4 = vmax3(s[12], s[13], s[14]);
+  const float m = vmax3(vmax3(a0, a1, a2), vmax3(a3, a4, s[15]), -INFINITY);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return vmax3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), -INFINITY) * c;
+}
+
+// Scores of keys at or past the lane's limit become -inf (select). Register e holds key
+// key0 + 8 half + 16 (e / 8) + e % 8, so each test compares a constant with lim - key0 - 8 half.
+__device__ __forceinline__ void mask_tile(floatx16& s, int key0, int half, int lim) {
+  const int rel = lim - key0 - 8 * half;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s[e] = 16 * (e >> 3) + (e & 7) < rel ? s[e] : -INFINITY;
+}
+
 // Lazy softmax reference update for one tile (tmax already in log2 units): raise the reference and
 // rescale only when some query of the wave exceeds it by more than 2^8.
 template <int DB>
@@ -560,36 +586,28 @@ attn3_kernel(AttnArgs a) {
     load_kf((i + 1) % NS);
     // (6) softmax; register e of s holds key kt*32 + 16 (e / 8) + 8 half + (e % 8)
     const int key0 = kt * AT3_BKV;
-    float tmax = -INFINITY;
-    if (key0 + AT3_BKV <= it.wave_lim) {
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(s[e], s[e + 1]));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + 16 * (e >> 3) + 8 * half + (e & 7);
-        s[e] = key < it.my_lim ? s[e] : -INFINITY;
-        tmax = fmaxf(tmax, s[e]);
-      }
-    }
-    {   // max with the partner lane (l xor 32) holding the query's other 16 keys
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-    }
-    raise_reference(tmax, m_ref, l_run, o);
+    if (key0 + AT3_BKV > it.wave_lim) mask_tile(s, key0, half, it.my_lim);
+    raise_reference(tile_max(s, c), m_ref, l_run, o);
     // a query with no visible key yet keeps m_ref = -inf and must produce p = 0, not NaN
     const float moff = m_ref == -INFINITY ? 0.f : m_ref;
-    float p[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -moff));
-      l_run += p[e];
-    }
     uint4 pf[2];
+    {
+      uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      pf[j] = make_uint4(pack2_bf16(p[8 * j], p[8 * j + 1]), pack2_bf16(p[8 * j + 2], p[8 * j + 3]),
-                         pack2_bf16(p[8 * j + 4], p[8 * j + 5]), pack2_bf16(p[8 * j + 6], p[8 * j + 7]));
+      for (int e = 0; e < 16; e += 2)
+        w[e >> 1] = pack2_bf16(__builtin_amdgcn_exp2f(fmaf(s[e], c, -moff)), __builtin_amdgcn_exp2f(fmaf(s[e + 1], c, -moff)));
+      // row sum of exactly the bf16 weights the value product uses: dot products with ones
+      const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+      float la = 0.f, lb = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k]), one, la, false);
+        lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k + 1]), one, lb, false);
+      }
+      l_run += la + lb;
+      pf[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      pf[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
     // (7) O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -704,9 +722,9 @@ hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s) {
     b.kv_splits = attn_kv_splits(a.Lq_total, a.H, a.br, a.kv_total);
     if (b.kv_splits > 1 && (!a.part || a.part_elems < attn_split_floats(a.Lq_total, a.H, a.br, a.kv_total)))
       b.kv_splits = 1;   // no scratch for the partials: one range per block
+    const long heads = (long)a.H * a.br;
     // five waves (160 queries) per block when four-wave blocks would overflow the 256 CUs and
     // five-wave blocks fit them in one round (e.g. 2 x 40 heads x 464 queries: 320 -> 240 blocks)
-    const long heads = (long)a.H * a.br;
     const bool five = b.kv_splits == 1 && (a.Lq_total + 127) / 128 * heads > 256 && (a.Lq_total + 159) / 160 * heads <= 256;
     if (copy_ok && a.d == 128 && five) return launch_attn3<128, 4, 5>(b, s);
     if (copy_ok && a.d == 128) return launch_attn3<128>(b, s);
