@@ -104,6 +104,52 @@ def summarize_counters(fetch_db: str, write_db: str):
     print(json.dumps({TRAFFIC_KEY: {"bytes_per_launch": rec["bytes_per_launch"]}}))
 
 
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def measured_mfma_peak(wam, torch, dev):
+    """bf16 TFLOP/s of back-to-back independent 32x32x16 MFMAs on every SIMD (the library's probe
+    kernel, 256 workgroups of one wave per SIMD), median of 5 timed launches of about 1 ms."""
+    wg, iters = 256, 4096
+    out = torch.empty(wg * 256, device=dev)
+    wam.wam_mfma_peak_probe(out, wg, iters)
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        wam.wam_mfma_peak_probe(out, wg, iters)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    flops = wg * 4.0 * iters * 8 * 32768
+    return round(flops / (median(times) * 1e-3) / 1e12, 1)
+
+
+def host_description() -> dict:
+    """CPU model and the BLAS NumPy runs on (vendor, version, threads)."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas.append({"vendor": i.get("internal_api"), "version": i.get("version"),
+                             "threads": i.get("num_threads")})
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
 def summarize_pmc(dbs, name_filter: str):
     """Mean of every counter per dispatch, per kernel whose name contains ``name_filter``, over the
     rocprofv3 --pmc databases ``dbs`` (one pass each): a markdown table on stdout."""
@@ -153,7 +199,7 @@ def cpu_baseline(w, timed_layers: int = 1) -> dict:
         h, _, _ = O.block_forward(w, lp, h, e6, ctx_k, ctx_v, ck, cv, 1, pos)
     dt = time.perf_counter() - t0
     per_layer = dt / timed_layers
-    return {"value": round(per_layer * w.layers * 1e3, 1),
+    return {**host_description(), "value": round(per_layer * w.layers * 1e3, 1),
             "unit": "ms per %d-layer CFG step (extrapolated)" % w.layers if w.layers > 1 else "ms per block",
             "cores": int(threads), "kind": "oracle",
             "sample": "%d full-width block(s) of the step (CFG batch %d, %d cached + %d current tokens, %d "
@@ -165,7 +211,7 @@ def cpu_baseline(w, timed_layers: int = 1) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
@@ -295,13 +341,14 @@ def main():
     # product of the middle layer, recorded by the library on its own stream
     timer_layer = w.layers // 2
     wam.wam_qkv_timer_config(timer_layer, args.steps)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]   # one boundary per step
+    evs[0].record()
     for i in range(args.steps):
         step(float(ts[args.warmup + i]))
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_samples = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     qkv_samples = wam.wam_qkv_timer_read(args.steps)
     wam.wam_qkv_timer_config(-1)
     finite = bool(torch.isfinite(vv).all().item() and torch.isfinite(va).all().item())
@@ -335,7 +382,9 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     b2b_ms = e0.elapsed_time(e1) / reps
-    gemm_ms = sum(qkv_samples) / len(qkv_samples) if qkv_samples else b2b_ms
+    gemm_mean_ms = sum(qkv_samples) / len(qkv_samples) if qkv_samples else b2b_ms
+    gemm_ms = median(qkv_samples) if qkv_samples else b2b_ms
+    peak_meas = measured_mfma_peak(wam, torch, dev)
     gemm_flops = 2.0 * M * 3 * D * D
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     traffic = None if mx else load_traffic(TRAFFIC_KEY, source_hash(os.path.join(ROOT, "world_action_video_amd", "csrc",
@@ -365,6 +414,9 @@ def main():
         "step_tflop": round(fl["total"] / 1e12, 3),
         "step_tflops": round(step_tflops, 1),
         "step_mfma_frac": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+        "median_ms": round(median(step_samples), 3),
+        "min_ms": round(step_samples[0], 3),
+        "max_ms": round(step_samples[-1], 3),
         "first_step_ms": round(first_ms, 1),
         "setup_s": round(setup_s, 1),
         "outputs_finite": finite,
@@ -374,8 +426,10 @@ def main():
                      "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / peak, 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2),
-                     "timing": "HIP events around layer %d's QKV launch in each of the %d timed steps (%d samples)"
-                               % (timer_layer, args.steps, len(qkv_samples)),
+                     "mean_launch_us": round(gemm_mean_ms * 1e3, 2),
+                     "timing": "median of HIP event pairs around layer %d's QKV launch in each of the %d timed steps "
+                               "(%d samples; mean beside it)" % (timer_layer, args.steps, len(qkv_samples)),
+                     "measured_peak_tflops": peak_meas,
                      "back_to_back_us": round(b2b_ms * 1e3, 2)},
     }
     log("step %.3f ms; QKV GEMM %.1f us (%.1f TFLOP/s)" % (ms, gemm_ms * 1e3, gemm_tflops))

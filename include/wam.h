@@ -442,6 +442,13 @@ wam_status wam_qkv_timer_config(int layer, int max_samples);
  * call of this library that blocks the host. ms is a HOST array (may be NULL when cap = 0). */
 wam_status wam_qkv_timer_read(float *ms, int cap, int *n);
 
+/* Measurement hook: the matrix-core rate the hardware sustains. Launches `workgroups` x 256 threads
+ * (one wave per SIMD), each wave issuing iters x 8 independent bf16 32x32x16 MFMAs (32768 flops
+ * each: workgroups x 4 x iters x 8 x 32768 flops in all);
+ * out: device floats, workgroups x 256 (written so the products are not optimised away). Time it
+ * with events on `stream`. Errors: WAM_E_ARG (NULL out, workgroups outside [1, 65536], iters < 1). */
+wam_status wam_mfma_peak_probe(float *out, int workgroups, int iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

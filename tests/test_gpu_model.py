@@ -393,6 +393,32 @@ def test_run_to_run_bitwise_determinism(gpu, tiny_oracle):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kv_reset_then_reappend_equals_fresh_cache(gpu, tiny_oracle, dtype):
+    """Continuous requests (single-GPU docs: at a window boundary the old KV is released and the frame
+    position restarts): after two committed chunks and wam_kv_reset, appending a chunk at frame 0 and
+    stepping gives bit for bit what a fresh cache gives; the stale rows left past the new length never
+    reach the output."""
+    w, _, _ = tiny_oracle
+    Fc = w.frames_per_chunk
+    print("kv-reset", dtype, flush=True)
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    rig = Rig(w, dtype, gpu)
+    fresh = rig.cache()
+    rig.append(fresh, x1v[2], x1a[2], 0)
+    ref = rig.step(fresh, 1, epv[1], epa[1], [0.3], [0.3], Fc)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    rig.append(dc, x1v[1], x1a[1], Fc)
+    rig.step(dc, 1, epv[2], epa[2], [0.6], [0.6], 2 * Fc)   # also writes scratch rows past the length
+    wam.wam_kv_reset(dc.c)
+    assert dc.length == 0
+    rig.append(dc, x1v[2], x1a[2], 0)
+    assert dc.length == w.chunk_tokens
+    got = rig.step(dc, 1, epv[1], epa[1], [0.3], [0.3], Fc)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_cfg_batch_equals_two_single_branch_calls(gpu, tiny_oracle, dtype):
     """CFG as batch 2 computes each branch exactly as a one-branch call would. Every row of the
     step is independent of the other branch, so the fp32 path (one kernel configuration for any row

@@ -23,7 +23,7 @@ EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_tim
            "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error",
            "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx", "wam_flow_step_noalloc",
-           "wam_denoise_chunk_replay")
+           "wam_denoise_chunk_replay", "wam_mfma_peak_probe")
 
 
 class WamError(RuntimeError):
@@ -118,6 +118,7 @@ def load(path: str = LIB_PATH):
         "wam_qkv_timer_config": (I, [I, I]),
         "wam_qkv_timer_read": (I, [ctypes.POINTER(ctypes.c_float), I, ctypes.POINTER(ctypes.c_int)]),
         "wam_op_attention_mx": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]),
+        "wam_mfma_peak_probe": (I, [P, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -332,6 +333,11 @@ def wam_op_attention_mx(Q, Qs, K, Ks, Vt, Vs, O, br, heads, Lq, k_rows, v_stride
 def wam_qkv_timer_config(layer: int, max_samples: int = 1):
     """Record HIP events around block ``layer``'s QKV product in later passes (layer < 0: off)."""
     _check(load().wam_qkv_timer_config(layer, max_samples))
+
+
+def wam_mfma_peak_probe(out, workgroups: int, iters: int, stream=None):
+    """Back-to-back bf16 MFMAs on every SIMD (see include/wam.h); ``out`` holds workgroups x 256 floats."""
+    _check(load().wam_mfma_peak_probe(_ptr(out), workgroups, iters, _stream(stream)))
 
 
 def wam_qkv_timer_read(cap: int = 4096):

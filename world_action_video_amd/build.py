@@ -9,7 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libwam.so")
-SOURCES = ["gemm.hip", "attn.hip", "attn_mx.hip", "rowwise.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "attn.hip", "attn_mx.hip", "rowwise.hip", "probe.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 instructions stay off: the compiler may form them from ordinary float code, and they

@@ -1261,6 +1261,13 @@ wam_status wam_qkv_timer_config(int layer, int max_samples) {
   return WAM_OK;
 }
 
+wam_status wam_mfma_peak_probe(float* out, int workgroups, int iters, void* stream) {
+  if (!out) return fail(WAM_E_ARG, "out is NULL");
+  if (workgroups < 1 || workgroups > 65536 || iters < 1) return fail(WAM_E_ARG, "workgroups in [1, 65536], iters >= 1");
+  HIP_TRY(launch_mfma_peak(out, workgroups, iters, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
 wam_status wam_qkv_timer_read(float* ms, int cap, int* n) {
   if (!n || (cap > 0 && !ms) || cap < 0) return fail(WAM_E_ARG, "n is NULL, or ms is NULL with cap > 0");
   QkvTimer& tm = g_qkv_timer;

@@ -266,6 +266,9 @@ struct HeadArgs {
 hipError_t launch_head(const HeadArgs& a, DType dt, hipStream_t s);
 // workgroups (and [3] partial-sum slots) of the flow step for these sizes: 1 .. 512
 int flow_partial_blocks(int nv, int na);
+// Matrix-core peak probe: `workgroups` x 256 threads, each wave `iters` x 8 independent bf16
+// 32x32x16 MFMAs (32768 flops each); one float per thread to `out`.
+hipError_t launch_mfma_peak(float* out, int workgroups, int iters, hipStream_t s);
 // Device address (for the current device) and size of the library-owned flow-step scratch.
 hipError_t flow_scratch(float** ptr, size_t* bytes);
 
