@@ -150,6 +150,49 @@ def host_description() -> dict:
     return {"cpu_model": model, "blas": blas}
 
 
+def short_kernel_name(n: str) -> str:
+    """`wam::gemm4_kernel<0>` from the demangled signature of a kernel dispatch."""
+    n = n.replace("void ", "").replace("(anonymous namespace)::", "")
+    cut = n.find("(")
+    return n[:cut] if cut > 0 else n
+
+
+def summarize_trace(db: str):
+    """Kernel trace of a bench.py run (rocprofv3 --kernel-trace): per-kernel totals, the wall time of
+    each stack pass (between consecutive time-MLP launches), and one layer of the last timed step
+    (the dispatches from the middle layer's QKV product to the next one). Markdown on stdout."""
+    import sqlite3
+    if not os.path.isfile(db):
+        raise SystemExit("no such database: %s" % db)
+    cur = sqlite3.connect("file:%s?mode=ro" % db, uri=True).cursor()
+    rows = cur.execute("select name, start, end from kernels order by start").fetchall()
+    ks = [(short_kernel_name(n), s0, e0) for n, s0, e0 in rows]
+    tot = {}
+    for n, s0, e0 in ks:
+        c, t = tot.get(n, (0, 0.0))
+        tot[n] = (c + 1, t + (e0 - s0) / 1e3)
+    all_us = sum(t for _, t in tot.values())
+    print("| kernel | calls | total (us) | average (us) | share |\n|---|---:|---:|---:|---:|")
+    for n, (c, t) in sorted(tot.items(), key=lambda x: -x[1][1])[:20]:
+        print("| `%s` | %d | %.1f | %.2f | %.1f%% |" % (n, c, t, t / c, 100 * t / all_us))
+    starts = [s0 for n, s0, _ in ks if "sinusoid" in n]
+    if len(starts) > 1:
+        print("\nstack passes, wall time between consecutive time-embedding launches (ms): " +
+              ", ".join("%.3f" % ((b - a) / 1e6) for a, b in zip(starts, starts[1:])))
+    last = [i for i, (n, _, _) in enumerate(ks) if "sinusoid" in n]
+    if len(last) >= 2:
+        lo, hi = last[-2], last[-1]
+        qkv = [i for i in range(lo, hi) if ks[i][0].endswith("gemm4_kernel<0>")]
+        if len(qkv) > 21:
+            a, b = qkv[20], qkv[21]
+            print("\none layer of the last full stack pass (dispatch order, from the middle layer's QKV product):\n")
+            print("| kernel | us |\n|---|---:|")
+            for n, s0, e0 in ks[a:b]:
+                print("| `%s` | %.1f |" % (n, (e0 - s0) / 1e3))
+            print("| **layer (sum of kernel times)** | **%.1f** |" % (sum((e0 - s0) for _, s0, e0 in ks[a:b]) / 1e3))
+            print("| layer wall time (QKV start to next QKV start) | %.1f |" % ((ks[b][1] - ks[a][1]) / 1e3))
+
+
 def summarize_pmc(dbs, name_filter: str):
     """Mean of every counter per dispatch, per kernel whose name contains ``name_filter``, over the
     rocprofv3 --pmc databases ``dbs`` (one pass each): a markdown table on stdout."""
@@ -231,14 +274,22 @@ def main():
                          "config-3 block over 1 and 8 chunks (for a kernel trace of its row kernels)")
     ap.add_argument("--attention", action="store_true",
                     help="bf16 and MXFP8 attention kernels at the step's self- and cross-attention shapes")
+    ap.add_argument("--attention-shape", choices=("self", "cross", "both"), default="both",
+                    help="with --attention: only the self- or only the cross-attention shape (one shape per counter run)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
                     help="per-kernel mean of every counter in rocprofv3 --pmc databases (kernels whose name contains "
                          "--kernel-filter)")
     ap.add_argument("--kernel-filter", default="", help="substring of the kernel names --summarize-pmc reports")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="per-kernel totals, stack-pass wall times and one layer's dispatches of a rocprofv3 "
+                         "--kernel-trace database of a bench.py run")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="turn the two rocprofv3 --pmc databases of a --counters run (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.kernel_filter)
         return
@@ -560,6 +611,8 @@ def attention_kernels(args, dev):
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     out = {}
     for name, kv_total, kv_base, chunk_q in (("self", 1392, 928, 464), ("cross", 769, 0, 0)):
+        if args.attention_shape not in ("both", name):
+            continue
         v_stride = (kv_total + 63) // 64 * 64
         q = torch.randn((br, H, Lq, d), device=dev).to(torch.bfloat16)
         k = torch.randn((br, H, kv_total, d), device=dev).to(torch.bfloat16)
