@@ -471,9 +471,9 @@ def main():
         "first_step_ms": round(first_ms, 1),
         "setup_s": round(setup_s, 1),
         "outputs_finite": finite,
-        "roofline": {"kernel": ("gemm4mx_kernel<EPI_STORE, W4> (MXFP4 x MXFP8 scaled MFMA" if w4 else
-                                "gemm4mx_kernel<EPI_STORE> (MXFP8 scaled MFMA" if mx else
-                                "gemm4_kernel<EPI_STORE> (bf16") + " 256x256 tile, 4 waves; QKV projection, 928x15360x5120)",
+        "roofline": {"kernel": ("gemm4mx_kernel<EPI_STORE, W4> (MXFP4 x MXFP8 scaled MFMA, 256x256" if w4 else
+                                "gemm4mx_kernel<EPI_STORE> (MXFP8 scaled MFMA, 256x256" if mx else
+                                "gemm4_kernel<EPI_STORE, 3, 5> (bf16, 192x320") + " tile, 4 waves; QKV projection, 928x15360x5120)",
                      "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / peak, 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2),

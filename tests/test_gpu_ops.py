@@ -37,7 +37,8 @@ def host(t):
 
 LINEAR_CASES = [(1, 64, 64), (67, 200, 128), (300, 384, 512), (928, 1024, 256), (130, 96, 1024), (300, 520, 1024),
                 (257, 260, 2048), (260, 258, 192),
-                (520, 16380, 320)]   # 192 tiles of 256 x 256 -> 222 of 256 x 224 (ragged M and N)
+                (520, 16380, 320),    # 192 tiles of 256 x 256 -> 222 of 256 x 224 (ragged M and N)
+                (1024, 16384, 128)]   # 256 tiles of 256 x 256 (one round) against 312 of 192 x 320
 
 
 def split_ws(gpu, M, N):
@@ -50,7 +51,9 @@ def split_ws(gpu, M, N):
 @pytest.mark.parametrize("act", [0, 1, 2])
 @pytest.mark.parametrize("split", [False, True])
 def test_op_linear_small(gpu, dtype, M, N, K, act, split):
-    """With a workspace, bf16 products of fewer than 128 256x256 tiles split over K (M, N >= 256)."""
+    """bf16 products with M, N >= 256 take the four-wave tiles (192 x 320 for most of these shapes,
+    256 x 256 for the last, 256 x 224 for the wide one); with a workspace, those of fewer than 128
+    tiles split over K."""
     if split and dtype == "f32":
         pytest.skip("split-K serves the bf16 path only")
     print("linear", dtype, M, N, K, act, split, flush=True)

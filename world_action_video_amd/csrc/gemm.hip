@@ -248,8 +248,7 @@ gemm_kernel(GemmArgs g) {
 // ------------------------------------------------------------------------------------------------
 static constexpr int EPI_PARTIAL = 16;   // internal: fp32 partial products of one split
 
-// Epilogue of the 256x256 four-wave tiles (bf16 and MXFP8 operands alike).
-// Epilogue of a wave's TM x TN blocks of 32 x 32 whose first row / column are wrow / wcol.
+// Epilogue of the four-wave tiles (bf16 and MX operands alike): a wave's TM x TN blocks of 32 x 32 whose first row / column are wrow / wcol.
 template <int EPI, int TM, int TN>
 __device__ __forceinline__ void g4_epilogue_t(const GemmArgs& g, const floatx16 (&acc)[TM][TN], int wrow, int wcol,
                                               int sp, int l32, int half) {
@@ -365,20 +364,17 @@ __device__ __forceinline__ void g4_epilogue_t(const GemmArgs& g, const floatx16 
   }
 }
 
-// the 2 x 2 waves of 128 x 128 of the 256 x 256 tiles
-template <int EPI>
-__device__ __forceinline__ void g4_epilogue(const GemmArgs& g, const floatx16 (&acc)[4][4], int m0, int n0, int sp,
-                                            int wm, int wn, int l32, int half) {
-  g4_epilogue_t<EPI, 4, 4>(g, acc, m0 + wm * 128, n0 + wn * 128, sp, l32, half);
-}
-
-template <int EPI>
+template <int EPI, int TM, int TN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm4_kernel(GemmArgs g, int splits) {
   using T = bf16_t;
-  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 4, TN = 4;
+  // 2 x 2 waves of (32 TM) x (32 TN); BM + BN = 512 rows staged per k-tile in both shapes used
+  // (256 x 256 and 192 x 320), i.e. 16 units of 16 bytes per thread, in four quarters of 4 units
+  constexpr int BM = 64 * TM, BN = 64 * TN, WM = 32 * TM, WN = 32 * TN;
   constexpr int NT = 256, UNITS = 8, EPU = 8, BK = 64, CHUNKS = 4;
-  constexpr int PER_T = BM * UNITS / NT;   // 8 units of A and 8 of W per thread per tile
+  constexpr int PA = BM * UNITS / NT, PW = BN * UNITS / NT, PER_T = PA + PW;   // units of A / W per thread
+  constexpr int NMF = TM * TN;   // MFMAs per wave per k16 chunk
+  static_assert(PER_T == 16 && NMF >= 12, "staging and schedule assume 512 tile rows and at least 12 blocks");
   // Rows are padded to 9 units (144 bytes): row r's unit u sits in bank group (r + u) mod 8, so eight
   // consecutive rows or eight units of one row never collide, and every fragment address of a chunk
   // is one per-lane base plus a compile-time offset (no per-chunk swizzle registers).
@@ -407,31 +403,29 @@ gemm4_kernel(GemmArgs g, int splits) {
   const __amdgpu_buffer_rsrc_t rw_ = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.W), (short)0,
                                                                        (int)((long)g.N * g.ldw * 2), 0x00020000);
   const int lrow = tid >> 3, lunit = tid & 7;
-  int offa[PER_T], offw[PER_T];
+  // unit i < PA: A rows m0 + lrow + 32 i; else W rows n0 + lrow + 32 (i - PA)
+  int off[PER_T];
 #pragma unroll
-  for (int i = 0; i < PER_T; ++i) {
-    offa[i] = (int)(((long)(m0 + lrow + i * 32) * g.lda + lunit * EPU) * 2);
-    offw[i] = (int)(((long)(n0 + lrow + i * 32) * g.ldw + lunit * EPU) * 2);
-  }
+  for (int i = 0; i < PER_T; ++i)
+    off[i] = i < PA ? (int)(((long)(m0 + lrow + i * 32) * g.lda + lunit * EPU) * 2)
+                    : (int)(((long)(n0 + lrow + (i - PA) * 32) * g.ldw + lunit * EPU) * 2);
   const int sbase = lrow * PITCH + lunit;
 
-  uint4 rg[2][2 * PER_T];                  // [register set][A units 0..7, W units 8..15]
-  // quarter q of a tile: units 2q, 2q+1 of A and of W (rows 64q .. 64q+63)
+  uint4 rg[2][PER_T];                      // [register set][unit]
+  // quarter q of a tile: units 4q .. 4q+3 of the list
   auto gload_q = [&](int kt, int set, int q) {
     const int koff = (kb + min(kt, KT - 1)) * BK * 2;   // prefetches past the split re-read its last tile
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = 2 * q + u;
-      rg[set][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_, offa[i], koff, 0));
-      rg[set][PER_T + i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw_, offw[i], koff, 0));
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * q + u;
+      rg[set][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(i < PA ? ra_ : rw_, off[i], koff, 0));
     }
   };
   auto sstore_q = [&](int st, int set, int q) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = 2 * q + u;
-      smem[st][sbase + i * 32 * PITCH] = rg[set][i];
-      smem[st][BM * PITCH + sbase + i * 32 * PITCH] = rg[set][PER_T + i];
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * q + u;
+      smem[st][(i < PA ? i * 32 * PITCH : BM * PITCH + (i - PA) * 32 * PITCH) + sbase] = rg[set][i];
     }
   };
   auto fload = [&](int st, int c, uint4* fa, uint4* fb) {
@@ -472,13 +466,14 @@ gemm4_kernel(GemmArgs g, int splits) {
   auto mma = [&](int fc, int lo, int hi) {
 #pragma unroll
     for (int q = lo; q < hi; ++q)
-      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fb[fc][q & 3]),
-                                                                   __builtin_bit_cast(bf16x8_t, fa[fc][q >> 2]),
-                                                                   acc[q >> 2][q & 3], 0, 0, 0);
+      acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fb[fc][q % TN]),
+                                                                    __builtin_bit_cast(bf16x8_t, fa[fc][q / TN]),
+                                                                    acc[q / TN][q % TN], 0, 0, 0);
   };
   // Scheduling groups: one MFMA, then one memory instruction of the given class, so the LDS and
   // global traffic issues while the matrix core works instead of in a burst between MFMA groups.
   constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
+  constexpr int NRD = TM + TN;   // fragment reads per chunk
   auto tile = [&](int kt, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value, nset = cur ^ 1;
 #pragma unroll
@@ -488,9 +483,9 @@ gemm4_kernel(GemmArgs g, int splits) {
         fload(cur, c + 1, fa[fc ^ 1], fb[fc ^ 1]);
         sstore_q(nset, nset, c);
         gload_q(kt + 3, nset, c);
-        mma(fc, 0, 16);
+        mma(fc, 0, NMF);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < NRD; ++k) {
           __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
           __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
         }
@@ -500,14 +495,14 @@ gemm4_kernel(GemmArgs g, int splits) {
           __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < NMF - NRD - 4; ++k) {
           __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
           __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
-        // last chunk: half of its MFMAs cover the tile's final LDS writes, the barrier sits in the
-        // middle, and the other half cover the first fragment loads of the next tile
+        // last chunk: eight of its MFMAs cover the tile's final LDS writes and global loads, the
+        // barrier sits after them, and the rest cover the first fragment loads of the next tile
         sstore_q(nset, nset, c);
         gload_q(kt + 3, nset, c);
         mma(fc, 0, 8);
@@ -524,9 +519,9 @@ gemm4_kernel(GemmArgs g, int splits) {
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         fload(nset, 0, fa[fc ^ 1], fb[fc ^ 1]);
-        mma(fc, 8, 16);
+        mma(fc, 8, NMF);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < NMF - 8; ++k) {
           __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
           __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
         }
@@ -541,7 +536,7 @@ gemm4_kernel(GemmArgs g, int splits) {
   }
   if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
 
-  g4_epilogue<EPI>(g, acc, m0, n0, sp, wm, wn, l32, half);
+  g4_epilogue_t<EPI, TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, sp, l32, half);
 }
 
 
@@ -931,7 +926,7 @@ gemm4mx_kernel(GemmArgs g, int splits) {
     tile(kt + 1, std::integral_constant<int, 1>{});
   }
   if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
-  g4_epilogue<EPI>(g, acc, m0, n0, sp, wm, wn, l32, half);
+  g4_epilogue_t<EPI, TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, sp, l32, half);
 }
 
 // Sum of the split partials in split order, plus bias, then the epilogue. One thread per 4 columns.
@@ -1007,43 +1002,69 @@ static hipError_t launch_cfg(const GemmArgs& a, Epi epi, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Four-wave bf16 tiles: 256 x 256 (waves of 128 x 128) or 192 x 320 (waves of 96 x 160). Both stage
+// 512 rows per k-tile; the planner takes the one whose busiest CU has less work (rounds of 256
+// workgroups times the work of one), so M = 928 runs on 5 x 192 rows (3.4% padding) instead of 4 x 256
+// (9.4%) at the same workgroup count.
+struct G4Plan {
+  int splits = 0;     // 0: shape not suited, 1: direct epilogue, else split-K partials
+  bool t192 = false;  // 192 x 320 tiles
+};
+
 template <int EPI>
-static void launch_g4(const GemmArgs& a, int splits, hipStream_t s) {
-  const int items = ((a.M + 255) / 256) * ((a.N + 255) / 256) * splits;
-  hipLaunchKernelGGL((gemm4_kernel<EPI>), dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, a, splits);
+static void launch_g4(const GemmArgs& a, const G4Plan& p, hipStream_t s) {
+  const int bm = p.t192 ? 192 : 256, bn = p.t192 ? 320 : 256;
+  const int items = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn) * p.splits;
+  const dim3 grid(8 * ((items + 7) / 8)), block(256);
+  if (p.t192)
+    hipLaunchKernelGGL((gemm4_kernel<EPI, 3, 5>), grid, block, 0, s, a, p.splits);
+  else
+    hipLaunchKernelGGL((gemm4_kernel<EPI, 4, 4>), grid, block, 0, s, a, p.splits);
 }
 
-// bf16 256x256 four-wave path: direct epilogue when there are enough tiles to occupy the CUs, else
-// split-K (about 240 workgroups) with a finishing row kernel. Returns 0 when the shape does not suit
-// the kernel (the caller falls back to the 8-wave tiles), 1 for a direct launch, else the split count.
+// bf16 four-wave path: direct epilogue when there are enough tiles to occupy the CUs, else split-K
+// (about 240 workgroups) with a finishing row kernel. splits == 0 when the shape does not suit the
+// kernel (the caller falls back to the 8-wave tiles).
 static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
-static int g4_plan(const GemmArgs& a, Epi epi) {
-  if (epi == EPI_ROWSEL_F32 || a.M < 256 || a.N < 256) return 0;
+static G4Plan g4_plan(const GemmArgs& a, Epi epi) {
+  G4Plan best;
+  if (epi == EPI_ROWSEL_F32 || a.M < 256 || a.N < 256) return best;
   // vector epilogues: runs of four columns, 16-byte aligned fp32 rows, 8-byte aligned bf16 rows
   const bool vec_ok = a.N % 4 == 0 && (!a.bias || aligned16(a.bias)) &&
                       (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_SWIGLU
                            ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
                                                            : (aligned16(a.H) && a.ldh % 4 == 0)) &&
                       (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
-  if (!vec_ok) return 0;
-  const long tiles = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if (!vec_ok) return best;
   const int KT = a.K / 64;
-  int splits = 1;
-  if (tiles < 128 && a.part) {
-    splits = (int)((240 + tiles - 1) / tiles);
-    if (splits > 4) splits = 4;
-    while (splits > 1 && (KT < 4 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
+  long best_cost = 0;
+  for (const bool t192 : {false, true}) {
+    const int bm = t192 ? 192 : 256, bn = t192 ? 320 : 256;
+    const long tiles = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    int splits = 1;
+    if (tiles < 128 && a.part) {
+      splits = (int)((240 + tiles - 1) / tiles);
+      if (splits > 4) splits = 4;
+      while (splits > 1 && (KT < 4 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
+    }
+    const long rounds = (tiles * splits + 255) / 256;
+    const long cost = rounds * bm * bn * ((KT + splits - 1) / splits);
+    if (best.splits == 0 || cost < best_cost) {
+      best.splits = splits;
+      best.t192 = t192;
+      best_cost = cost;
+    }
   }
-  return splits;
+  return best;
 }
 
-static void launch_g4_direct(const GemmArgs& a, Epi epi, hipStream_t s) {
+static void launch_g4_direct(const GemmArgs& a, Epi epi, const G4Plan& p, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: launch_g4<EPI_STORE>(a, 1, s); break;
-    case EPI_GELU: launch_g4<EPI_GELU>(a, 1, s); break;
-    case EPI_SWIGLU: launch_g4<EPI_SWIGLU>(a, 1, s); break;
-    case EPI_RESID: launch_g4<EPI_RESID>(a, 1, s); break;
-    case EPI_RESID_GATED: launch_g4<EPI_RESID_GATED>(a, 1, s); break;
+    case EPI_STORE: launch_g4<EPI_STORE>(a, p, s); break;
+    case EPI_GELU: launch_g4<EPI_GELU>(a, p, s); break;
+    case EPI_SWIGLU: launch_g4<EPI_SWIGLU>(a, p, s); break;
+    case EPI_RESID: launch_g4<EPI_RESID>(a, p, s); break;
+    case EPI_RESID_GATED: launch_g4<EPI_RESID_GATED>(a, p, s); break;
     default: break;
   }
 }
@@ -1074,20 +1095,20 @@ static bool use_wide_rows(const GemmArgs& a, Epi epi) {
 }
 
 static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err) {
-  const int plan = g4_plan(a, epi);
-  if (plan == 0) return false;
-  if (plan == 1 && use_wide_rows(a, epi)) {
+  const G4Plan plan = g4_plan(a, epi);
+  if (plan.splits == 0) return false;
+  if (plan.splits == 1 && use_wide_rows(a, epi)) {
     const long items = (long)((a.M + 255) / 256) * ((a.N + 223) / 224);
     const dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(256);
     if (epi == EPI_GELU)
       hipLaunchKernelGGL((gemm4w_kernel<EPI_GELU>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((gemm4w_kernel<EPI_STORE>), grid, block, 0, s, a);
-  } else if (plan == 1) {
-    launch_g4_direct(a, epi, s);
+  } else if (plan.splits == 1) {
+    launch_g4_direct(a, epi, plan, s);
   } else {
     launch_g4<EPI_PARTIAL>(a, plan, s);
-    launch_reduce(a, epi, plan, s);
+    launch_reduce(a, epi, plan.splits, s);
   }
   *err = hipGetLastError();
   return true;
@@ -1101,7 +1122,8 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s) {
   const long esz = dt == DT_BF16 ? 2 : 4;
   if ((long)a.M * a.lda * esz >= (1L << 31) || (long)a.N * a.ldw * esz >= (1L << 31)) return hipErrorInvalidValue;
   // Tile choice (measured on MI355X over the step's shapes): bf16 products with M, N >= 256 take the
-  // four-wave 256x256 kernel (split over K when it has fewer than 128 tiles); the rest take 256x128 /
+  // four-wave kernel with 256x256 or 192x320 tiles (split over K when it has fewer than 128 tiles), or
+  // 256x224 tiles when those fill one round; the rest take 256x128 /
   // 128x256 tiles with 8 waves of 64x64, and smaller tiles for tiny shapes.
   if (dt == DT_BF16) {
     hipError_t e4;
@@ -1283,12 +1305,14 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
   else
     fused = fused && epi == EPI_STORE && post.qa.rope == nullptr && post.qa.D == a.N && post.qa.M == a.M &&
             post.qa.d % 4 == 0 && aligned16(post.qa.gain) && reinterpret_cast<uintptr_t>(post.qa.dst) % 8 == 0;
-  const int plan = !fused ? 0 : a.As ? (mx_operands_ok(a) ? mx_splits(a) : 0) : g4_plan(a, epi);
+  G4Plan p4;
+  if (fused && !a.As) p4 = g4_plan(a, epi);
+  const int plan = !fused ? 0 : a.As ? (mx_operands_ok(a) ? mx_splits(a) : 0) : p4.splits;
   if (plan > 1) {
     if (a.As)
       launch_g4mx_partial(a, plan, s);
     else
-      launch_g4<EPI_PARTIAL>(a, plan, s);
+      launch_g4<EPI_PARTIAL>(a, p4, s);
     const dim3 grid(a.M), block(256);
     const int groups = (a.N / 4 + 255) / 256;   // float4 groups per thread
 #define WAM_FINISH_G(E, P, S)                                                                              \
