@@ -16,6 +16,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -182,7 +183,7 @@ def summarize_trace(db: str):
     last = [i for i, (n, _, _) in enumerate(ks) if "sinusoid" in n]
     if len(last) >= 2:
         lo, hi = last[-2], last[-1]
-        qkv = [i for i in range(lo, hi) if ks[i][0].endswith("gemm4_kernel<0>")]
+        qkv = [i for i in range(lo, hi) if re.search(r"gemm4_kernel<0(>|, )", ks[i][0])]
         if len(qkv) > 21:
             a, b = qkv[20], qkv[21]
             print("\none layer of the last full stack pass (dispatch order, from the middle layer's QKV product):\n")
@@ -493,7 +494,9 @@ def main():
 
 
 def elementwise(args, dev):
-    """HBM-bound kernels at the step's size and past the Infinity Cache (one JSON line).
+    """HBM-bound kernels at the step's size and past the Infinity Cache (one JSON line): the flow
+    update, the split-K finish and the standalone adaLN, each resident and rotated up to >= 1 GB per
+    call, the 1 GiB device copy, and one block over 1 and 8 chunks.
 
     Flow update (guidance + Euler + cosine partials, 2 branches): 24 bytes per latent element (reads x,
     v_cond, v_uncond, prev; writes x, g). Guidance 1 and dt 0 keep every value bounded while the kernel
@@ -566,6 +569,45 @@ def elementwise(args, dev):
     del src, dst
     torch.cuda.empty_cache()
 
+    # Row kernels on their own, resident and rotated through a 4 GiB pool: the split-K finish (three
+    # fp32 partials and the residual read, the residual and the bf16 norm output written: 22 B per
+    # element) and the standalone adaLN (fp32 row in, bf16 out: 6 B per element). Per-column vectors
+    # (bias, modulation) are not counted.
+    D = 5120
+    pool_floats = 1 << 30
+    pool = torch.empty(pool_floats, device=dev)
+    pool.normal_()
+    vec = lambda: (torch.randn((6, D), device=dev) * 0.1)  # noqa: E731
+    e6v, mgv, mnv, biasv = vec(), vec(), vec(), torch.randn(D, device=dev) * 0.1
+    rowk = {"finish": [], "norm": []}
+    for kind, Ms in (("finish", (928, 2784, 9280)), ("norm", (928, 7424, 37120))):
+        for M in Ms:
+            n = M * D
+            span = ((4 * n + n // 2 if kind == "finish" else n + n // 2) + 63) // 64 * 64   # floats per set
+            sets = max(1, pool_floats // span)
+            nbytes = (22 if kind == "finish" else 6) * n
+            base = pool.data_ptr()
+
+            def call(i, rot, kind=kind, M=M, n=n, span=span, sets=sets, base=base):
+                o = base + 4 * ((i % sets) * span if rot else 0)
+                if kind == "finish":   # part [3][M][D], h [M][D], y bf16 [M][D]
+                    wam.wam_op_split_finish(o, 3, M, D, biasv, o + 12 * n, e6v, mgv, 5, mnv, 0, 1, o + 16 * n)
+                else:                  # x [M][D], y bf16 [M][D]
+                    wam.wam_op_modulated_norm(o, M, D, e6v, mnv, 0, 1, o + 4 * n)
+
+            for rot in (False, True):
+                call(0, rot)
+            res = timed(lambda i: call(i, False), 50 if n < (1 << 24) else 10)
+            rot = timed(lambda i: call(i, True), max(10, min(400, 4 * sets)))
+            rowk[kind].append({"rows": M, "bytes": nbytes, "sets": sets, "resident_us": round(res * 1e3, 2),
+                               "resident_GBps": round(nbytes / (res * 1e-3) / 1e9, 1),
+                               "rotated_us": round(rot * 1e3, 2), "rotated_GBps": round(nbytes / (rot * 1e-3) / 1e9, 1),
+                               "rotated_hbm_frac": round(nbytes / (rot * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+            log("%s rows=%d: resident %.2f us, rotated %.2f us (%.0f GB/s)" % (kind, M, res * 1e3, rot * 1e3,
+                                                                             nbytes / (rot * 1e-3) / 1e9))
+    del pool
+    torch.cuda.empty_cache()
+
     w = WORKLOADS[WORKLOAD_ID].with_(layers=1)
     Lq = w.chunk_tokens
     model = DeviceModel(w, "bf16", dev)
@@ -595,7 +637,8 @@ def elementwise(args, dev):
                       "unit": "GB/s", "n_gpus": 1, "dtype": "f32", "data": "synthetic",
                       "config": {"workload": "flow update 2 branches, 24 B per element; config-3 block over 1 and 8 chunks"},
                       "hbm_peak_GBps": PEAK_HBM_GBS, "copy_1GiB_GBps": round(copy_gbps, 1),
-                      "copy_frac": round(copy_gbps / PEAK_HBM_GBS, 3), "flow": flow, "block_ms": blocks}))
+                      "copy_frac": round(copy_gbps / PEAK_HBM_GBS, 3), "flow": flow, "split_finish": rowk["finish"],
+                      "modulated_norm": rowk["norm"], "block_ms": blocks}))
 
 
 def attention_kernels(args, dev):

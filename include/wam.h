@@ -337,6 +337,31 @@ wam_status wam_denoise_chunk_unipc(const wam_config *cfg, const wam_weights *w, 
 wam_status wam_op_linear(wam_dtype dtype, const void *A, int lda, const void *W, int ldw, const float *bias, void *C,
                          int ldc, int M, int N, int K, int act, void *ws, size_t ws_bytes, void *stream);
 
+/* Finishing row kernel of a split product, on its own ([ARCH] §2.3 single block: the gated residual
+ * that closes the self-attention and FFN sub-blocks, then the adaLN of the sub-block that follows;
+ * the block runs this kernel after every product it splits over K):
+ *   v[m][n] = (sum over s < splits, in order, of part[s][m][n]) + bias[n]
+ *   h[m][n] += gate[n] v[m][n], gate = e6[gate_idx] + mod_gate[gate_idx] (gate_idx in 0..5), or
+ *              gate = 1 (gate_idx < 0; mod_gate unused)
+ *   y[m][n] = bf16(norm(h[m])[n] (1 + e6[scale_idx][n] + mod_norm[scale_idx][n])
+ *                  + e6[shift_idx][n] + mod_norm[shift_idx][n])
+ * norm: LayerNorm without affine over the row (RMSNorm when rms != 0) with eps, in fp32.
+ * part fp32 [splits][M][N]; h fp32 [M][N], updated in place; e6, mod_gate, mod_norm fp32 [6][N]
+ * (e6 the time modulation of the rows, mod_* the layer offsets); bias fp32 [N] or NULL; y bf16
+ * [M][N]. All device pointers, owned by the caller, 16-byte aligned. 2 <= splits <= 4; N a multiple
+ * of 4 up to 8192; else WAM_E_SHAPE / WAM_E_ARG. M = 0 launches nothing. Deterministic. */
+wam_status wam_op_split_finish(const float *part, int splits, int M, int N, const float *bias, float *h,
+                               const float *e6, const float *mod_gate, int gate_idx, const float *mod_norm,
+                               int shift_idx, int scale_idx, int rms, float eps, void *y, void *stream);
+
+/* Modulated norm of fp32 rows, on its own ([ARCH] §2.3: the adaLN before self-attention and FFN;
+ * the block's first norm of a pass, and every norm of a product that is not split):
+ *   y[m][n] = bf16(norm(x[m])[n] (1 + e6[scale_idx][n] + mod[scale_idx][n]) + e6[shift_idx][n] + mod[shift_idx][n])
+ * x fp32 [M][D]; e6, mod fp32 [6][D]; y bf16 [M][D]; norm as in wam_op_split_finish. Device pointers,
+ * 16-byte aligned; D a multiple of 4 up to 8192; indices in 0..5; else WAM_E_SHAPE / WAM_E_ARG. */
+wam_status wam_op_modulated_norm(const float *x, int M, int D, const float *e6, const float *mod, int shift_idx,
+                                 int scale_idx, int rms, float eps, void *y, void *stream);
+
 /* Low-precision projections ([N569] real-time optimisations: quantised projections) in the OCP
  * microscaling format that gfx950's scaled matrix instructions read (MXFP8): fp8 e4m3 codes (bias
  * 7, subnormals, largest finite 448) sharing one e8m0 power-of-two scale per 32 consecutive elements

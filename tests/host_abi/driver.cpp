@@ -220,6 +220,28 @@ int main() {
     float ms[2];
     expect(wam_qkv_timer_read(ms, 2, &n), WAM_OK, "qkv timer read");
     expect(wam_qkv_timer_config(-1, 1), WAM_OK, "qkv timer off");
+    const int M = 40, N = 1024;
+    float* part = static_cast<float*>(dev((size_t)3 * M * N * 4, "finish partials"));
+    float* hh = static_cast<float*>(dev((size_t)M * N * 4, "finish h"));
+    float* e6v = static_cast<float*>(dev((size_t)6 * N * 4, "finish e6"));
+    float* mg = static_cast<float*>(dev((size_t)6 * N * 4, "finish gate offsets"));
+    float* mn = static_cast<float*>(dev((size_t)6 * N * 4, "finish norm offsets"));
+    void* yy = dev((size_t)M * N * 2, "finish y");
+    expect(wam_op_split_finish(part, 3, M, N, e6v, hh, e6v, mg, 5, mn, 0, 1, 0, 1e-6f, yy, nullptr), WAM_OK,
+           "op_split_finish gated");
+    expect(wam_op_split_finish(part, 3, M, N, nullptr, hh, e6v, nullptr, -1, mn, 3, 4, 1, 1e-6f, yy, nullptr), WAM_OK,
+           "op_split_finish plain");
+    expect(wam_op_modulated_norm(hh, M, N, e6v, mn, 0, 1, 0, 1e-6f, yy, nullptr), WAM_OK, "op_modulated_norm");
+    const long before_bad = host_abi::g_launches;
+    expect(wam_op_split_finish(part, 5, M, N, nullptr, hh, e6v, mg, 5, mn, 0, 1, 0, 1e-6f, yy, nullptr), WAM_E_SHAPE,
+           "op_split_finish 5 splits");
+    expect(wam_op_split_finish(part, 3, M, N, nullptr, hh, e6v, nullptr, 2, mn, 0, 1, 0, 1e-6f, yy, nullptr), WAM_E_ARG,
+           "op_split_finish gate without offsets");
+    expect(wam_op_modulated_norm(hh, M, N + 2, e6v, mn, 0, 1, 0, 1e-6f, yy, nullptr), WAM_E_SHAPE,
+           "op_modulated_norm D not a multiple of 4");
+    expect(wam_op_modulated_norm(hh, M, N, e6v, mn, 0, 6, 0, 1e-6f, yy, nullptr), WAM_E_ARG,
+           "op_modulated_norm slot 6");
+    expect((int)(host_abi::g_launches - before_bad), 0, "no launch by a rejected op");
     host_abi::clear_regions();
   }
   scenario("tiny bf16", config(false, WAM_BF16));

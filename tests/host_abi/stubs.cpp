@@ -73,6 +73,18 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
   if (p.mode == POST_NORM) check_norm(p.na, dt);
   return hipSuccess;
 }
+hipError_t launch_split_finish(const GemmArgs& a, Epi epi, const PostArgs& p, int splits, hipStream_t) {
+  ++host_abi::g_launches;
+  check(a.part, (size_t)splits * a.M * a.N * 4, "finish partials");
+  if (a.bias) check(a.bias, (size_t)a.N * 4, "finish bias");
+  if (epi == EPI_RESID || epi == EPI_RESID_GATED) check(a.H, ((size_t)(a.M - 1) * a.ldh + a.N) * 4, "finish H");
+  if (epi == EPI_RESID_GATED) check(a.mod, (size_t)6 * a.D * 4, "finish gate offsets");
+  if (p.mode == POST_NORM) {
+    check_norm(p.na, DT_BF16);
+    check(p.na.mod, (size_t)6 * p.na.D * 4, "finish norm offsets");
+  }
+  return hipSuccess;
+}
 hipError_t launch_mx_quantize(const void* src, long ld, DType dt, int rows, int cols, uint8_t* codes, long ldq,
                               uint8_t* scales, hipStream_t) {
   ++host_abi::g_launches;

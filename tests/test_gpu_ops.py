@@ -1,4 +1,5 @@
-"""Kernel-level parity through the C ABI (wam_op_linear, wam_op_attention) against the oracle.
+"""Kernel-level parity through the C ABI (wam_op_linear, wam_op_attention, wam_op_split_finish,
+wam_op_modulated_norm) against the oracle.
 
 Inputs are seeded synth draws (bf16-representable), identical on both sides. Tolerances:
 * linear, bf16: fp32 accumulation of exact bf16 products, then one rounding of the output to bf16,
@@ -275,3 +276,61 @@ def test_op_attention_full_shape_bf16(gpu):
     print("attention-full", flush=True)
     out, ref = _attn_case(gpu, "bf16", 2, 40, 128, 464, 928, 0, 1392, "full")
     assert rel_l2(out, ref) <= 1e-2
+
+
+def _f32(x, gpu):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(gpu)
+
+
+@pytest.mark.parametrize("M,N", [(1, 1024), (37, 5120), (928, 5120), (5, 8192), (3, 1028)])
+@pytest.mark.parametrize("splits", [2, 3, 4])
+@pytest.mark.parametrize("gate_idx,rms", [(5, False), (-1, False), (2, True)])
+def test_op_split_finish(gpu, M, N, splits, gate_idx, rms):
+    """The finishing row kernel of a split product against the oracle's residual update and
+    modulated norm: h to fp32 rounding of its terms, y within a bf16 half-ulp; bit-identical rerun."""
+    print("split-finish", M, N, splits, gate_idx, rms, flush=True)
+    tag = "%d_%d_%d" % (M, N, splits)
+    part = draw((splits, M, N), "part" + tag)
+    h0 = draw((M, N), "h" + tag)
+    bias = draw((N,), "fb" + tag, 0.1)
+    e6 = draw((6, N), "e6" + tag, 0.1)
+    mg = draw((6, N), "mg" + tag, 0.1)
+    mn = draw((6, N), "mn" + tag, 0.1)
+    shift_idx, scale_idx = (3, 4) if gate_idx == 2 else (0, 1)
+    eps = 1e-6
+    v = part.astype(np.float64).sum(axis=0) + bias
+    gate = (e6[gate_idx].astype(np.float64) + mg[gate_idx]) if gate_idx >= 0 else np.ones(N)
+    h_ref = h0 + gate * v
+    y_ref = O.modulated_norm(h_ref, e6[shift_idx].astype(np.float64) + mn[shift_idx],
+                             e6[scale_idx].astype(np.float64) + mn[scale_idx], eps, rms=rms)
+    P, B, E, MG, MN = (_f32(x, gpu) for x in (part, bias, e6, mg, mn))
+    outs = []
+    for _ in range(2):
+        H = _f32(h0, gpu)
+        Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=gpu)
+        wam.wam_op_split_finish(P, splits, M, N, B, H, E, MG if gate_idx >= 0 else None, gate_idx, MN, shift_idx,
+                                scale_idx, Y, rms=rms, eps=eps)
+        torch.cuda.synchronize()
+        outs.append((H.cpu().numpy(), host(Y)))
+    (h, y), (h2, y2) = outs
+    assert np.array_equal(h, h2) and np.array_equal(y, y2)
+    mag = np.abs(h0) + np.abs(gate) * (np.abs(part).sum(axis=0) + np.abs(bias))
+    assert np.all(np.abs(h - h_ref) <= 4 * 2.0 ** -24 * mag)
+    assert np.all(np.abs(y - y_ref) <= np.abs(y_ref) * 2.0 ** -8 + 1e-3)
+
+
+@pytest.mark.parametrize("M,D", [(1, 64), (5, 100), (928, 5120), (33, 8192)])
+@pytest.mark.parametrize("rms", [False, True])
+def test_op_modulated_norm(gpu, M, D, rms):
+    """The block's standalone adaLN kernel against the oracle's modulated norm (bf16 output)."""
+    print("modulated-norm", M, D, rms, flush=True)
+    tag = "%d_%d" % (M, D)
+    x = draw((M, D), "nx" + tag, 2.0) + 0.5
+    e6 = draw((6, D), "ne6" + tag, 0.1)
+    mod = draw((6, D), "nmod" + tag, 0.1)
+    y_ref = O.modulated_norm(x.astype(np.float64), e6[3].astype(np.float64) + mod[3],
+                             e6[4].astype(np.float64) + mod[4], 1e-6, rms=rms)
+    Y = torch.full((M, D), float("nan"), dtype=torch.bfloat16, device=gpu)
+    wam.wam_op_modulated_norm(_f32(x, gpu), M, D, _f32(e6, gpu), _f32(mod, gpu), 3, 4, Y, rms=rms, eps=1e-6)
+    torch.cuda.synchronize()
+    assert np.all(np.abs(host(Y) - y_ref) <= np.abs(y_ref) * 2.0 ** -8 + 1e-3)

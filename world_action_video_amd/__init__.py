@@ -23,7 +23,7 @@ EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_tim
            "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error",
            "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx", "wam_flow_step_noalloc",
-           "wam_denoise_chunk_replay", "wam_mfma_peak_probe")
+           "wam_denoise_chunk_replay", "wam_mfma_peak_probe", "wam_op_split_finish", "wam_op_modulated_norm")
 
 
 class WamError(RuntimeError):
@@ -119,6 +119,8 @@ def load(path: str = LIB_PATH):
         "wam_qkv_timer_read": (I, [ctypes.POINTER(ctypes.c_float), I, ctypes.POINTER(ctypes.c_int)]),
         "wam_op_attention_mx": (I, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]),
         "wam_mfma_peak_probe": (I, [P, I, I, P]),
+        "wam_op_split_finish": (I, [P, I, I, I, P, P, P, P, I, P, I, I, I, F, P, P]),
+        "wam_op_modulated_norm": (I, [P, I, I, P, P, I, I, I, F, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -270,6 +272,18 @@ def wam_op_linear(dtype, A, lda, W, ldw, bias, C, ldc, M, N, K, act=0, ws=None, 
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().wam_op_linear(dtype, _ptr(A), lda, _ptr(W), ldw, _ptr(bias), _ptr(C), ldc, M, N, K, act,
                                 _ptr(ws), nbytes, _stream(stream)))
+
+
+def wam_op_split_finish(part, splits, M, N, bias, h, e6, mod_gate, gate_idx, mod_norm, shift_idx, scale_idx, y,
+                        rms=False, eps=1e-6, stream=None):
+    _check(load().wam_op_split_finish(_ptr(part), splits, M, N, _ptr(bias), _ptr(h), _ptr(e6), _ptr(mod_gate),
+                                      gate_idx, _ptr(mod_norm), shift_idx, scale_idx, 1 if rms else 0, float(eps),
+                                      _ptr(y), _stream(stream)))
+
+
+def wam_op_modulated_norm(x, M, D, e6, mod, shift_idx, scale_idx, y, rms=False, eps=1e-6, stream=None):
+    _check(load().wam_op_modulated_norm(_ptr(x), M, D, _ptr(e6), _ptr(mod), shift_idx, scale_idx, 1 if rms else 0,
+                                        float(eps), _ptr(y), _stream(stream)))
 
 
 def wam_mx_quantize(dtype, src, ld, rows, cols, codes, ldq, scales, stream=None):

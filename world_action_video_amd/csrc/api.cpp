@@ -1058,6 +1058,51 @@ wam_status wam_op_linear(wam_dtype dtype, const void* A, int lda, const void* W,
   return WAM_OK;
 }
 
+wam_status wam_op_split_finish(const float* part, int splits, int M, int N, const float* bias, float* h,
+                               const float* e6, const float* mod_gate, int gate_idx, const float* mod_norm,
+                               int shift_idx, int scale_idx, int rms, float eps, void* y, void* stream) {
+  if (!part || !h || !e6 || !mod_norm || !y || (gate_idx >= 0 && !mod_gate)) return fail(WAM_E_ARG, "NULL buffer");
+  if (splits < 2 || splits > 4) return fail(WAM_E_SHAPE, "splits must be 2, 3 or 4");
+  if (M < 0 || N <= 0 || N % 4 || N > 8192) return fail(WAM_E_SHAPE, "N must be a positive multiple of 4 up to 8192");
+  if (gate_idx > 5 || shift_idx < 0 || shift_idx > 5 || scale_idx < 0 || scale_idx > 5)
+    return fail(WAM_E_ARG, "modulation slots must be in 0..5");
+  if (!(eps > 0.f)) return fail(WAM_E_ARG, "eps must be positive");
+  if (unaligned16(part) || unaligned16(h) || unaligned16(e6) || unaligned16(mod_norm) || unaligned16(y) ||
+      (bias && unaligned16(bias)) || (gate_idx >= 0 && unaligned16(mod_gate)))
+    return fail(WAM_E_ARG, "buffers must be 16-byte aligned");
+  if (M == 0) return WAM_OK;
+  const RowMap rm{M, M, M};   // one row type: every row takes slot block 0 of e6
+  GemmArgs ga{};
+  ga.bias = bias; ga.H = h; ga.ldh = N; ga.M = M; ga.N = N; ga.K = 0; ga.rm = rm;
+  ga.e6 = e6; ga.mod = mod_gate; ga.gate_idx = gate_idx < 0 ? 0 : gate_idx; ga.D = N;
+  ga.part = const_cast<float*>(part); ga.part_elems = (long)splits * M * N;
+  PostArgs post{};
+  post.mode = POST_NORM;
+  NormArgs& na = post.na;
+  na.X = h; na.Y = y; na.M = M; na.D = N; na.eps = eps; na.mode = NORM_ADALN; na.rm = rm;
+  na.e6 = e6; na.mod = mod_norm; na.shift_idx = shift_idx; na.scale_idx = scale_idx; na.rms = rms != 0;
+  HIP_TRY(launch_split_finish(ga, gate_idx >= 0 ? EPI_RESID_GATED : EPI_RESID, post, splits,
+                              reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
+wam_status wam_op_modulated_norm(const float* x, int M, int D, const float* e6, const float* mod, int shift_idx,
+                                 int scale_idx, int rms, float eps, void* y, void* stream) {
+  if (!x || !e6 || !mod || !y) return fail(WAM_E_ARG, "NULL buffer");
+  if (M < 0 || D <= 0 || D % 4 || D > 8192) return fail(WAM_E_SHAPE, "D must be a positive multiple of 4 up to 8192");
+  if (shift_idx < 0 || shift_idx > 5 || scale_idx < 0 || scale_idx > 5)
+    return fail(WAM_E_ARG, "modulation slots must be in 0..5");
+  if (!(eps > 0.f)) return fail(WAM_E_ARG, "eps must be positive");
+  if (unaligned16(x) || unaligned16(e6) || unaligned16(mod) || unaligned16(y))
+    return fail(WAM_E_ARG, "buffers must be 16-byte aligned");
+  if (M == 0) return WAM_OK;
+  NormArgs na{};
+  na.X = x; na.Y = y; na.M = M; na.D = D; na.eps = eps; na.mode = NORM_ADALN; na.rm = RowMap{M, M, M};
+  na.e6 = e6; na.mod = mod; na.shift_idx = shift_idx; na.scale_idx = scale_idx; na.rms = rms != 0;
+  HIP_TRY(launch_norm(na, DT_BF16, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
 wam_status wam_mx_quantize(wam_dtype dtype, const void* src, int ld, int rows, int cols, void* codes, int ldq,
                            void* scales, void* stream) {
   if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");

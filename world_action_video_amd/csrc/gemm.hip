@@ -1291,6 +1291,37 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
   }
 }
 
+hipError_t launch_split_finish(const GemmArgs& a, Epi epi, const PostArgs& post, int splits, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  if (splits < 2 || splits > 4 || a.N % 4 || a.N > 256 * 4 * FIN_G) return hipErrorInvalidValue;
+  const bool norm_ok = post.mode == POST_NORM && (epi == EPI_RESID || epi == EPI_RESID_GATED);
+  if (!norm_ok && !(post.mode == POST_QK && epi == EPI_STORE)) return hipErrorInvalidValue;
+  const dim3 grid(a.M), block(256);
+  const int groups = (a.N / 4 + 255) / 256;   // float4 groups per thread
+#define WAM_FINISH_G(E, P, S)                                                                              \
+  if (groups <= 1) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 1>), grid, block, 0, s, a, post);      \
+  else if (groups <= 5) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 5>), grid, block, 0, s, a, post); \
+  else hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, FIN_G>), grid, block, 0, s, a, post);
+#define WAM_FINISH(E, P)                  \
+  switch (splits) {                       \
+    case 2: WAM_FINISH_G(E, P, 2) break;  \
+    case 3: WAM_FINISH_G(E, P, 3) break;  \
+    default: WAM_FINISH_G(E, P, 4) break; \
+  }
+  if (post.mode == POST_NORM) {
+    if (epi == EPI_RESID) {
+      WAM_FINISH(EPI_RESID, POST_NORM)
+    } else {
+      WAM_FINISH(EPI_RESID_GATED, POST_NORM)
+    }
+  } else {
+    WAM_FINISH(EPI_STORE, POST_QK)
+  }
+#undef WAM_FINISH
+#undef WAM_FINISH_G
+  return hipGetLastError();
+}
+
 static int mx_splits(const GemmArgs& a);
 static bool mx_operands_ok(const GemmArgs& a);
 static void launch_g4mx_partial(const GemmArgs& a, int splits, hipStream_t s);
@@ -1313,30 +1344,7 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
       launch_g4mx_partial(a, plan, s);
     else
       launch_g4<EPI_PARTIAL>(a, p4, s);
-    const dim3 grid(a.M), block(256);
-    const int groups = (a.N / 4 + 255) / 256;   // float4 groups per thread
-#define WAM_FINISH_G(E, P, S)                                                                              \
-  if (groups <= 1) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 1>), grid, block, 0, s, a, post);      \
-  else if (groups <= 5) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 5>), grid, block, 0, s, a, post); \
-  else hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, FIN_G>), grid, block, 0, s, a, post);
-#define WAM_FINISH(E, P)                  \
-  switch (plan) {                         \
-    case 2: WAM_FINISH_G(E, P, 2) break;  \
-    case 3: WAM_FINISH_G(E, P, 3) break;  \
-    default: WAM_FINISH_G(E, P, 4) break; \
-  }
-    if (post.mode == POST_NORM) {
-      if (epi == EPI_RESID) {
-        WAM_FINISH(EPI_RESID, POST_NORM)
-      } else {
-        WAM_FINISH(EPI_RESID_GATED, POST_NORM)
-      }
-    } else {
-      WAM_FINISH(EPI_STORE, POST_QK)
-    }
-#undef WAM_FINISH
-#undef WAM_FINISH_G
-    return hipGetLastError();
+    return launch_split_finish(a, epi, post, plan, s);
   }
   hipError_t e = launch_gemm(a, dt, epi, s);
   if (e != hipSuccess) return e;

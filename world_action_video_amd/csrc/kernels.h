@@ -168,6 +168,10 @@ struct PostArgs {
   QkNormArgs qa;
 };
 hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs& post, hipStream_t s);
+// The finishing row kernel of a split product on its own: sums a.part[0 .. splits-1] in split order,
+// adds a.bias, applies the epilogue (EPI_RESID / EPI_RESID_GATED into a.H, or EPI_STORE feeding
+// POST_QK) and runs the row stage `post` (bf16 only, 2 <= splits <= 4, N % 4 == 0, N <= 8192).
+hipError_t launch_split_finish(const GemmArgs& a, Epi epi, const PostArgs& post, int splits, hipStream_t s);
 
 struct VCacheArgs {
   const void* src; long src_ld; int src_col;   // v = src[row][src_col + h*d + j]
