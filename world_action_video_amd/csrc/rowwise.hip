@@ -10,94 +10,95 @@
 namespace wam {
 
 // ------------------------------------------------------------------------------------------------
-// LayerNorm (+ modulation): one wave per row (4 rows per 256-thread workgroup). The row stays in
-// registers (VPL float4 per lane); mean and variance are two wave reductions, no LDS, no barrier.
+// LayerNorm (+ modulation): a 256-thread workgroup per row, over R consecutive rows per workgroup
+// (more rows per workgroup only for tall inputs, where workgroup dispatch would otherwise pace the
+// kernel); thread t holds columns 4 (t + 256 k), k < G. The row's fp32 input and its per-column
+// vectors, combined into one multiplier and one addend (1 + scale, shift for the adaLN and head modes;
+// w, b for the affine mode), are all loaded before the reductions; the vectors are kept while the
+// next row has the same token group. Mean and variance are two workgroup reductions in a fixed order.
 // With a.rms the mean is taken as zero: RMSNorm.
 // ------------------------------------------------------------------------------------------------
-template <typename T, int VPL>
-__global__ void __launch_bounds__(256) norm_kernel(NormArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.M) return;
-  const float4* x4 = reinterpret_cast<const float4*>(a.X + (long)row * a.D);
+template <typename T, int G>
+__global__ void __launch_bounds__(256) norm_kernel(NormArgs a, int R) {
+  __shared__ float red[4];
+  const int t = threadIdx.x;
   const int nv = a.D / 4;
-  float4 xv[VPL];
-  float s = 0.f;
+  const int r0 = blockIdx.x * R, r1 = min(a.M, r0 + R);
+  float4 mv[G], av[G];
+  int have = -2;   // token group whose vectors mv / av hold (-1: the affine weights)
+  for (int row = r0; row < r1; ++row) {
+    const float4* x4 = reinterpret_cast<const float4*>(a.X + (long)row * a.D);
+    float4 xv[G];
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) {
-    const int i = lane + 64 * k;
-    xv[k] = i < nv ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    s += (xv[k].x + xv[k].y) + (xv[k].z + xv[k].w);
-  }
-  const float mean = a.rms ? 0.f : wave_sum(s) / (float)a.D;
-  float ss = 0.f;
+    for (int k = 0; k < G; ++k) {
+      const int q = t + 256 * k;
+      xv[k] = q < nv ? x4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    int grp_id = -1;
+    if (a.mode != NORM_AFFINE) {
+      const int rb = row % a.rm.rows_per_branch;
+      grp_id = (rb / a.rm.Lq) * 2 + ((rb % a.rm.Lq) < a.rm.Lv ? 0 : 1);
+    }
+    if (grp_id != have) {   // uniform across the workgroup
+      have = grp_id;
+      const float4 *sh = nullptr, *sc = nullptr, *sh2 = nullptr, *sc2 = nullptr;
+      if (a.mode == NORM_ADALN) {
+        const float* e6 = a.e6 + (long)grp_id * 6 * a.D;
+        sh = reinterpret_cast<const float4*>(e6 + (long)a.shift_idx * a.D);
+        sc = reinterpret_cast<const float4*>(e6 + (long)a.scale_idx * a.D);
+        sh2 = reinterpret_cast<const float4*>(a.mod + (long)a.shift_idx * a.D);
+        sc2 = reinterpret_cast<const float4*>(a.mod + (long)a.scale_idx * a.D);
+      } else if (a.mode == NORM_HEAD) {   // e [n][2][D] + head_mod [2][D]
+        const float* e = a.e6 + (long)grp_id * a.D;
+        sh = sc = reinterpret_cast<const float4*>(e);
+        sh2 = reinterpret_cast<const float4*>(a.mod);
+        sc2 = reinterpret_cast<const float4*>(a.mod + a.D);
+      }
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) {
-    const int i = lane + 64 * k;
-    if (i < nv) {
+      for (int k = 0; k < G; ++k) {
+        const int q = t + 256 * k;
+        mv[k] = av[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q >= nv) continue;
+        if (a.mode == NORM_AFFINE) {
+          mv[k] = reinterpret_cast<const float4*>(a.w)[q];
+          av[k] = reinterpret_cast<const float4*>(a.b)[q];
+        } else {
+          const float4 p = sh[q], p2 = sh2[q], r = sc[q], r2 = sc2[q];
+          mv[k] = make_float4(1.f + (r.x + r2.x), 1.f + (r.y + r2.y), 1.f + (r.z + r2.z), 1.f + (r.w + r2.w));
+          av[k] = make_float4(p.x + p2.x, p.y + p2.y, p.z + p2.z, p.w + p2.w);
+        }
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) s += (xv[k].x + xv[k].y) + (xv[k].z + xv[k].w);
+    const float mean = a.rms ? 0.f : block_sum<256>(s, red) / (float)a.D;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      if (t + 256 * k >= nv) continue;
       const float d0 = xv[k].x - mean, d1 = xv[k].y - mean, d2 = xv[k].z - mean, d3 = xv[k].w - mean;
       ss += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
     }
-  }
-  const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)a.D + a.eps);
+    const float rstd = 1.f / sqrtf(block_sum<256>(ss, red) / (float)a.D + a.eps);
 
-  const float4 *sh4 = nullptr, *sc4 = nullptr, *sh24 = nullptr, *sc24 = nullptr;
-  if (a.mode != NORM_AFFINE) {
-    const int rb = row % a.rm.rows_per_branch;
-    const int ch = rb / a.rm.Lq, grp = (rb % a.rm.Lq) < a.rm.Lv ? 0 : 1;
-    if (a.mode == NORM_ADALN) {
-      const float* e6 = a.e6 + (long)(ch * 2 + grp) * 6 * a.D;
-      sh4 = reinterpret_cast<const float4*>(e6 + (long)a.shift_idx * a.D);
-      sc4 = reinterpret_cast<const float4*>(e6 + (long)a.scale_idx * a.D);
-      sh24 = reinterpret_cast<const float4*>(a.mod + (long)a.shift_idx * a.D);
-      sc24 = reinterpret_cast<const float4*>(a.mod + (long)a.scale_idx * a.D);
-    } else {  // NORM_HEAD: e [n][2][D] + head_mod [2][D]
-      const float* e = a.e6 + (long)(ch * 2 + grp) * a.D;
-      sh4 = sc4 = reinterpret_cast<const float4*>(e);
-      sh24 = reinterpret_cast<const float4*>(a.mod);
-      sc24 = reinterpret_cast<const float4*>(a.mod + a.D);
-    }
-  }
-  T* y = reinterpret_cast<T*>(a.Y) + (long)row * a.D;
+    T* y = reinterpret_cast<T*>(a.Y) + (long)row * a.D;
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) {
-    const int i = lane + 64 * k;
-    if constexpr (sizeof(T) == 2) {
-      if (a.mxq && 64 * k < nv) {   // MXFP8 copy of the stored (bf16-rounded) row; the whole wave calls it
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < nv) {
-          v = make_float4((xv[k].x - mean) * rstd, (xv[k].y - mean) * rstd, (xv[k].z - mean) * rstd,
-                          (xv[k].w - mean) * rstd);
-          if (a.mode == NORM_AFFINE) {
-            const float4 w = reinterpret_cast<const float4*>(a.w)[i], b = reinterpret_cast<const float4*>(a.b)[i];
-            v = make_float4(v.x * w.x + b.x, v.y * w.y + b.y, v.z * w.z + b.z, v.w * w.w + b.w);
-          } else {
-            const float4 p = sh4[i], q = sh24[i], r = sc4[i], t = sc24[i];
-            v = make_float4(v.x * (1.f + (r.x + t.x)) + (p.x + q.x), v.y * (1.f + (r.y + t.y)) + (p.y + q.y),
-                            v.z * (1.f + (r.z + t.z)) + (p.z + q.z), v.w * (1.f + (r.w + t.w)) + (p.w + q.w));
-          }
-          reinterpret_cast<uint2*>(y)[i] = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+    for (int k = 0; k < G; ++k) {
+      const int q = t + 256 * k;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (q < nv)
+        v = make_float4((xv[k].x - mean) * rstd * mv[k].x + av[k].x, (xv[k].y - mean) * rstd * mv[k].y + av[k].y,
+                        (xv[k].z - mean) * rstd * mv[k].z + av[k].z, (xv[k].w - mean) * rstd * mv[k].w + av[k].w);
+      if constexpr (sizeof(T) == 2) {
+        if (q < nv) reinterpret_cast<uint2*>(y)[q] = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+        if (a.mxq && 256 * k < nv) {   // MXFP8 copy of the stored (bf16-rounded) row; whole waves call it
           v = make_float4(bf16_round(v.x), bf16_round(v.y), bf16_round(v.z), bf16_round(v.w));
+          mx_store_quad(v, q < nv, a.mxq + (long)row * a.D, a.mxs + (long)row * (a.D / 32), q);
         }
-        mx_store_quad(v, i < nv, a.mxq + (long)row * a.D, a.mxs + (long)row * (a.D / 32), i);
-        continue;
+      } else {
+        if (q < nv) reinterpret_cast<float4*>(y)[q] = v;
       }
-    }
-    if (i >= nv) continue;
-    float4 v = make_float4((xv[k].x - mean) * rstd, (xv[k].y - mean) * rstd, (xv[k].z - mean) * rstd,
-                           (xv[k].w - mean) * rstd);
-    if (a.mode == NORM_AFFINE) {
-      const float4 w = reinterpret_cast<const float4*>(a.w)[i], b = reinterpret_cast<const float4*>(a.b)[i];
-      v = make_float4(v.x * w.x + b.x, v.y * w.y + b.y, v.z * w.z + b.z, v.w * w.w + b.w);
-    } else {
-      const float4 p = sh4[i], q = sh24[i], r = sc4[i], t = sc24[i];
-      v = make_float4(v.x * (1.f + (r.x + t.x)) + (p.x + q.x), v.y * (1.f + (r.y + t.y)) + (p.y + q.y),
-                      v.z * (1.f + (r.z + t.z)) + (p.z + q.z), v.w * (1.f + (r.w + t.w)) + (p.w + q.w));
-    }
-    if constexpr (sizeof(T) == 2) {
-      reinterpret_cast<uint2*>(y)[i] = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
-    } else {
-      reinterpret_cast<float4*>(y)[i] = v;
     }
   }
 }
@@ -142,12 +143,14 @@ hipError_t launch_add(void* dst, const void* src, long n, DType dt, hipStream_t 
 
 template <typename T>
 static hipError_t launch_norm_t(const NormArgs& a, hipStream_t s) {
-  const dim3 grid((a.M + 3) / 4), block(256);
-  const int vpl = (a.D / 4 + 63) / 64;
-  if (vpl <= 4) hipLaunchKernelGGL((norm_kernel<T, 4>), grid, block, 0, s, a);
-  else if (vpl <= 8) hipLaunchKernelGGL((norm_kernel<T, 8>), grid, block, 0, s, a);
-  else if (vpl <= 20) hipLaunchKernelGGL((norm_kernel<T, 20>), grid, block, 0, s, a);
-  else if (vpl <= 32) hipLaunchKernelGGL((norm_kernel<T, 32>), grid, block, 0, s, a);
+  // rows per workgroup: one up to 8192 rows, then enough for about 8192 workgroups, at most 8
+  const int R = a.M <= 8192 ? 1 : min(8, (a.M + 8191) / 8192);
+  const dim3 grid((a.M + R - 1) / R), block(256);
+  const int g = (a.D / 4 + 255) / 256;   // float4 groups per thread
+  if (g <= 1) hipLaunchKernelGGL((norm_kernel<T, 1>), grid, block, 0, s, a, R);
+  else if (g <= 2) hipLaunchKernelGGL((norm_kernel<T, 2>), grid, block, 0, s, a, R);
+  else if (g <= 5) hipLaunchKernelGGL((norm_kernel<T, 5>), grid, block, 0, s, a, R);
+  else if (g <= 8) hipLaunchKernelGGL((norm_kernel<T, 8>), grid, block, 0, s, a, R);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
