@@ -495,8 +495,8 @@ def main():
 
 def elementwise(args, dev):
     """HBM-bound kernels at the step's size and past the Infinity Cache (one JSON line): the flow
-    update, the split-K finish and the standalone adaLN, each resident and rotated up to >= 1 GB per
-    call, the 1 GiB device copy, and one block over 1 and 8 chunks.
+    update, the split-K finish, the standalone adaLN and the q/k/v post-processing, each resident and
+    rotated up to >= 1 GB per call, the 1 GiB device copy, and one block over 1 and 8 chunks.
 
     Flow update (guidance + Euler + cosine partials, 2 branches): 24 bytes per latent element (reads x,
     v_cond, v_uncond, prev; writes x, g). Guidance 1 and dt 0 keep every value bounded while the kernel
@@ -605,6 +605,35 @@ def elementwise(args, dev):
                                "rotated_hbm_frac": round(nbytes / (rot * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
             log("%s rows=%d: resident %.2f us, rotated %.2f us (%.0f GB/s)" % (kind, M, res * 1e3, rot * 1e3,
                                                                              nbytes / (rot * 1e-3) / 1e9))
+    # q/k norm + rotary + cache scatter (2 branches, 40 heads of 128): q, k, v bf16 read, q, k, v bf16
+    # written, 12 B per element of a row's D columns
+    H, dh, br = 40, 128, 2
+    ang = torch.rand((8352, dh // 2), device=dev) * 6.2832
+    rope = torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).contiguous()
+    gq, gk = torch.ones(D, device=dev), torch.ones(D, device=dev)
+    rowk["qkv"] = []
+    for rows in (464, 3712, 8352):
+        n = br * rows * D
+        span = (3 * n + 63) // 64 * 64       # floats per set: qkv (6 B), q, k, v (2 B each) per element
+        sets = max(1, pool_floats // span)
+        nbytes = 12 * n
+        base = pool.data_ptr()
+
+        def call(i, rot, rows=rows, n=n, span=span, sets=sets, base=base):
+            o = base + 4 * ((i % sets) * span if rot else 0)
+            wam.wam_op_qkv_cache(o, br, rows, 464, 440, H, dh, gq, gk, 1e-6, rope, o + 6 * n, o + 8 * n, o + 10 * n,
+                                 rows, 0)
+
+        for rot in (False, True):
+            call(0, rot)
+        res = timed(lambda i: call(i, False), 50 if n < (1 << 24) else 10)
+        rot = timed(lambda i: call(i, True), max(10, min(400, 4 * sets)))
+        rowk["qkv"].append({"rows": br * rows, "bytes": nbytes, "sets": sets, "resident_us": round(res * 1e3, 2),
+                            "resident_GBps": round(nbytes / (res * 1e-3) / 1e9, 1),
+                            "rotated_us": round(rot * 1e3, 2), "rotated_GBps": round(nbytes / (rot * 1e-3) / 1e9, 1),
+                            "rotated_hbm_frac": round(nbytes / (rot * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+        log("qkv rows=%d: resident %.2f us, rotated %.2f us (%.0f GB/s)" % (br * rows, res * 1e3, rot * 1e3,
+                                                                          nbytes / (rot * 1e-3) / 1e9))
     del pool
     torch.cuda.empty_cache()
 
@@ -635,10 +664,12 @@ def elementwise(args, dev):
         log("block over %d chunk(s): %.3f ms" % (n_chunks, blocks["chunks_%d" % n_chunks]))
     print(json.dumps({"metric": "HBM-bound kernels (flow update sweep, 1 GiB copy, block passes)",
                       "unit": "GB/s", "n_gpus": 1, "dtype": "f32", "data": "synthetic",
-                      "config": {"workload": "flow update 2 branches, 24 B per element; config-3 block over 1 and 8 chunks"},
+                      "config": {"workload": "flow update 2 branches, 24 B per element; split-K finish, 22 B per "
+                                             "element; adaLN, 6 B; q/k/v post-processing, 12 B; width 5120; "
+                                             "config-3 block over 1 and 8 chunks"},
                       "hbm_peak_GBps": PEAK_HBM_GBS, "copy_1GiB_GBps": round(copy_gbps, 1),
                       "copy_frac": round(copy_gbps / PEAK_HBM_GBS, 3), "flow": flow, "split_finish": rowk["finish"],
-                      "modulated_norm": rowk["norm"], "block_ms": blocks}))
+                      "modulated_norm": rowk["norm"], "qkv_cache": rowk["qkv"], "block_ms": blocks}))
 
 
 def attention_kernels(args, dev):

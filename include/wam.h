@@ -362,6 +362,23 @@ wam_status wam_op_split_finish(const float *part, int splits, int M, int N, cons
 wam_status wam_op_modulated_norm(const float *x, int M, int D, const float *e6, const float *mod, int shift_idx,
                                  int scale_idx, int rms, float eps, void *y, void *stream);
 
+/* Post-processing of the QKV projection output, on its own ([ARCH] §2.3 single block: q and k are
+ * RMS-normalised with learned gains and rotated by the 3-D rotary embedding before attention; the
+ * pass's keys and values enter the attention cache). For branch b < br and row r < rows:
+ *   q_out[b][h][r][:]          = rot_r(rmsnorm(q[b rows + r]) g_q)[h d .. h d + d)
+ *   k_cache[b][h][row0 + r][:] = rot_r(rmsnorm(k[b rows + r]) g_k)[h d .. h d + d)
+ *   v_cache[b][h][j][row0 + r] = v[b rows + r][h d + j]
+ * where q | k | v are columns [0, D), [D, 2D), [2D, 3D) of qkv (bf16 [br rows][3D], D = H d), rmsnorm
+ * is over all D columns with eps in fp32, and rot_r rotates the pairs (2i, 2i+1) of every head by
+ * (cos, sin) = rope[r][i] for the video rows of a chunk (r mod Lq < Lv) and leaves the action rows
+ * unrotated. g_q, g_k fp32 [D]; rope fp32 [rows][d/2][2]; q_out bf16 [br][H][rows][d]; k_cache bf16
+ * [br][H][cap][d]; v_cache bf16 [br][H][d][cap] (keys contiguous). Device pointers owned by the caller,
+ * 16-byte aligned. d is 64 or 128; rows, cap, row0 multiples of 8; row0 + rows <= cap; D <= 8192; else
+ * WAM_E_SHAPE / WAM_E_ARG. */
+wam_status wam_op_qkv_cache(const void *qkv, int br, int rows, int Lq, int Lv, int H, int d, const float *g_q,
+                            const float *g_k, float eps, const float *rope, void *q_out, void *k_cache, void *v_cache,
+                            int cap, int row0, void *stream);
+
 /* Low-precision projections ([N569] real-time optimisations: quantised projections) in the OCP
  * microscaling format that gfx950's scaled matrix instructions read (MXFP8): fp8 e4m3 codes (bias
  * 7, subnormals, largest finite 448) sharing one e8m0 power-of-two scale per 32 consecutive elements

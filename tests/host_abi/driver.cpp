@@ -242,6 +242,24 @@ int main() {
     expect(wam_op_modulated_norm(hh, M, N, e6v, mn, 0, 6, 0, 1e-6f, yy, nullptr), WAM_E_ARG,
            "op_modulated_norm slot 6");
     expect((int)(host_abi::g_launches - before_bad), 0, "no launch by a rejected op");
+    {
+      const int br = 2, rows = 48, H = 4, d = 64, D = H * d, cap = 64;
+      void* qkv = dev((size_t)br * rows * 3 * D * 2, "qkv rows");
+      float* gq = static_cast<float*>(dev((size_t)D * 4, "g_q"));
+      float* gk = static_cast<float*>(dev((size_t)D * 4, "g_k"));
+      float* rope = static_cast<float*>(dev((size_t)rows * d * 4, "rope table"));
+      void* qo = dev((size_t)br * H * rows * d * 2, "q out");
+      void* kc = dev((size_t)br * H * cap * d * 2, "k cache");
+      void* vc = dev((size_t)br * H * d * cap * 2, "v cache");
+      expect(wam_op_qkv_cache(qkv, br, rows, 24, 20, H, d, gq, gk, 1e-6f, rope, qo, kc, vc, cap, 16, nullptr), WAM_OK,
+             "op_qkv_cache");
+      const long before_q = host_abi::g_launches;
+      expect(wam_op_qkv_cache(qkv, br, rows, 24, 20, H, d, gq, gk, 1e-6f, rope, qo, kc, vc, cap, 24, nullptr),
+             WAM_E_SHAPE, "op_qkv_cache past the cache");
+      expect(wam_op_qkv_cache(qkv, br, rows, 24, 20, H, 96, gq, gk, 1e-6f, rope, qo, kc, vc, cap, 0, nullptr),
+             WAM_E_SHAPE, "op_qkv_cache head dim 96");
+      expect((int)(host_abi::g_launches - before_q), 0, "no launch by a rejected q/k/v op");
+    }
     host_abi::clear_regions();
   }
   scenario("tiny bf16", config(false, WAM_BF16));

@@ -1,5 +1,5 @@
 """Kernel-level parity through the C ABI (wam_op_linear, wam_op_attention, wam_op_split_finish,
-wam_op_modulated_norm) against the oracle.
+wam_op_modulated_norm, wam_op_qkv_cache) against the oracle.
 
 Inputs are seeded synth draws (bf16-representable), identical on both sides. Tolerances:
 * linear, bf16: fp32 accumulation of exact bf16 products, then one rounding of the output to bf16,
@@ -334,3 +334,49 @@ def test_op_modulated_norm(gpu, M, D, rms):
     wam.wam_op_modulated_norm(_f32(x, gpu), M, D, _f32(e6, gpu), _f32(mod, gpu), 3, 4, Y, rms=rms, eps=1e-6)
     torch.cuda.synchronize()
     assert np.all(np.abs(host(Y) - y_ref) <= np.abs(y_ref) * 2.0 ** -8 + 1e-3)
+
+
+@pytest.mark.parametrize("br,rows,Lq,Lv,H,d,row0", [(2, 48, 24, 20, 4, 64, 16), (1, 8, 8, 8, 2, 128, 0),
+                                                    (2, 464, 464, 440, 40, 128, 928)])
+def test_op_qkv_cache(gpu, br, rows, Lq, Lv, H, d, row0):
+    """q/k RMSNorm with gains, the rotary embedding of video rows and the scatter into head-major q and
+    the caches, against the oracle's rms_norm and apply_rope; values copied bit for bit; cache rows
+    outside [row0, row0 + rows) untouched; action rows ignore their (NaN) table entries."""
+    print("qkv-cache", br, rows, Lq, Lv, H, d, row0, flush=True)
+    D, eps, theta = H * d, 1e-6, 1e4
+    cap = row0 + rows + 8
+    tag = "%d_%d_%d_%d" % (br, rows, H, d)
+    qkv = draw((br * rows, 3 * D), "qkv" + tag)
+    gq = draw((D,), "gq" + tag, 0.1) + 1.0
+    gk = draw((D,), "gk" + tag, 0.1) + 1.0
+    rng = np.random.default_rng(rows + H)
+    pos = np.stack([rng.integers(0, 24, rows), rng.integers(0, 11, rows), rng.integers(0, 20, rows)], axis=1)
+    video = (np.arange(rows) % Lq) < Lv
+    axis, freq = O.rope_frequencies(d, theta)
+    ang = pos[:, axis].astype(np.float64) * freq[None, :]
+    table = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)   # [rows][d/2][2]
+    table[~video] = np.nan
+    QKV = to_device(qkv, "bf16", gpu)
+    Qo = torch.full((br, H, rows, d), float("nan"), dtype=torch.bfloat16, device=gpu)
+    Kc = torch.full((br, H, cap, d), float("nan"), dtype=torch.bfloat16, device=gpu)
+    Vc = torch.full((br, H, d, cap), float("nan"), dtype=torch.bfloat16, device=gpu)
+    wam.wam_op_qkv_cache(QKV, br, rows, Lq, Lv, H, d, _f32(gq, gpu), _f32(gk, gpu), eps, _f32(table, gpu), Qo, Kc, Vc,
+                         cap, row0)
+    torch.cuda.synchronize()
+    x = qkv.astype(np.float64).reshape(br, rows, 3, H, d)
+
+    def expect(t, gain):
+        out = np.empty((br, H, rows, d))
+        for b in range(br):
+            xn = O.rms_norm(x[b, :, t].reshape(rows, D), eps, gain.astype(np.float64)).reshape(rows, H, d)
+            xn[video] = O.apply_rope(xn[video], pos[video], d, theta)
+            out[b] = xn.transpose(1, 0, 2)
+        return out
+
+    q_ref, k_ref = expect(0, gq), expect(1, gk)
+    q, k, v = host(Qo), host(Kc), host(Vc)
+    assert np.all(np.abs(q - q_ref) <= np.abs(q_ref) * 2.0 ** -8 + 2e-3)
+    assert np.all(np.abs(k[:, :, row0:row0 + rows] - k_ref) <= np.abs(k_ref) * 2.0 ** -8 + 2e-3)
+    assert np.array_equal(v[:, :, :, row0:row0 + rows], x[:, :, 2].transpose(0, 2, 3, 1).astype(np.float32))
+    assert np.isnan(k[:, :, :row0]).all() and np.isnan(k[:, :, row0 + rows:]).all()
+    assert np.isnan(v[..., :row0]).all() and np.isnan(v[..., row0 + rows:]).all()

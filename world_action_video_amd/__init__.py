@@ -23,7 +23,8 @@ EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_tim
            "wam_mx_quantize", "wam_mx4_quantize", "wam_op_linear_mx", "wam_mx_block_bytes", "wam_mx_pack_block",
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error",
            "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx", "wam_flow_step_noalloc",
-           "wam_denoise_chunk_replay", "wam_mfma_peak_probe", "wam_op_split_finish", "wam_op_modulated_norm")
+           "wam_denoise_chunk_replay", "wam_mfma_peak_probe", "wam_op_split_finish", "wam_op_modulated_norm",
+           "wam_op_qkv_cache")
 
 
 class WamError(RuntimeError):
@@ -121,6 +122,7 @@ def load(path: str = LIB_PATH):
         "wam_mfma_peak_probe": (I, [P, I, I, P]),
         "wam_op_split_finish": (I, [P, I, I, I, P, P, P, P, I, P, I, I, I, F, P, P]),
         "wam_op_modulated_norm": (I, [P, I, I, P, P, I, I, I, F, P, P]),
+        "wam_op_qkv_cache": (I, [P, I, I, I, I, I, I, P, P, F, P, P, P, P, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -284,6 +286,12 @@ def wam_op_split_finish(part, splits, M, N, bias, h, e6, mod_gate, gate_idx, mod
 def wam_op_modulated_norm(x, M, D, e6, mod, shift_idx, scale_idx, y, rms=False, eps=1e-6, stream=None):
     _check(load().wam_op_modulated_norm(_ptr(x), M, D, _ptr(e6), _ptr(mod), shift_idx, scale_idx, 1 if rms else 0,
                                         float(eps), _ptr(y), _stream(stream)))
+
+
+def wam_op_qkv_cache(qkv, br, rows, Lq, Lv, H, d, g_q, g_k, eps, rope, q_out, k_cache, v_cache, cap, row0=0,
+                     stream=None):
+    _check(load().wam_op_qkv_cache(_ptr(qkv), br, rows, Lq, Lv, H, d, _ptr(g_q), _ptr(g_k), float(eps), _ptr(rope),
+                                   _ptr(q_out), _ptr(k_cache), _ptr(v_cache), cap, row0, _stream(stream)))
 
 
 def wam_mx_quantize(dtype, src, ld, rows, cols, codes, ldq, scales, stream=None):

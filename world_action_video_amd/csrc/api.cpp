@@ -1103,6 +1103,35 @@ wam_status wam_op_modulated_norm(const float* x, int M, int D, const float* e6, 
   return WAM_OK;
 }
 
+wam_status wam_op_qkv_cache(const void* qkv, int br, int rows, int Lq, int Lv, int H, int d, const float* g_q,
+                            const float* g_k, float eps, const float* rope, void* q_out, void* k_cache, void* v_cache,
+                            int cap, int row0, void* stream) {
+  if (!qkv || !g_q || !g_k || !rope || !q_out || !k_cache || !v_cache) return fail(WAM_E_ARG, "NULL buffer");
+  if (d != 64 && d != 128) return fail(WAM_E_SHAPE, "head dim must be 64 or 128");
+  if (br < 1 || H < 1 || (long)H * d > 8192) return fail(WAM_E_SHAPE, "need br >= 1 and 1 <= H d <= 8192");
+  if (rows < 0 || rows % 8 || row0 < 0 || row0 % 8 || cap % 8 || row0 + rows > cap)
+    return fail(WAM_E_SHAPE, "rows, row0 and cap must be multiples of 8 with row0 + rows <= cap");
+  if (Lq < 1 || Lv < 0 || Lv > Lq) return fail(WAM_E_SHAPE, "need 0 <= Lv <= Lq");
+  if (!(eps > 0.f)) return fail(WAM_E_ARG, "eps must be positive");
+  if (unaligned16(qkv) || unaligned16(g_q) || unaligned16(g_k) || unaligned16(rope) || unaligned16(q_out) ||
+      unaligned16(k_cache) || unaligned16(v_cache))
+    return fail(WAM_E_ARG, "buffers must be 16-byte aligned");
+  if (rows == 0) return WAM_OK;
+  const int D = H * d;
+  QkNormArgs qa{};
+  qa.src = qkv; qa.src_ld = 3L * D; qa.src_col = 0; qa.gain = g_q;
+  qa.dst = q_out; qa.dst_bh_stride = (long)rows * d; qa.dst_row0 = 0;
+  qa.M = br * rows; qa.D = D; qa.H = H; qa.d = d; qa.rows_per_branch = rows; qa.eps = eps;
+  qa.rope = reinterpret_cast<const float2*>(rope); qa.rm = RowMap{rows, Lq, Lv};
+  QkNormArgs ka = qa;
+  ka.src_col = D; ka.gain = g_k; ka.dst = k_cache; ka.dst_bh_stride = (long)cap * d; ka.dst_row0 = row0;
+  VCacheArgs va{};
+  va.src = qkv; va.src_ld = 3L * D; va.src_col = 2 * D; va.dst = v_cache; va.dst_bh_stride = (long)d * cap;
+  va.dst_stride = cap; va.dst_col0 = row0; va.rows_per_branch = rows; va.br = br; va.H = H; va.d = d;
+  HIP_TRY(launch_qkv_cache(&qa, ka, va, DT_BF16, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
 wam_status wam_mx_quantize(wam_dtype dtype, const void* src, int ld, int rows, int cols, void* codes, int ldq,
                            void* scales, void* stream) {
   if (dtype != WAM_BF16 && dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype");
