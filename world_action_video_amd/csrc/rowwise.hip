@@ -178,6 +178,15 @@ __device__ __forceinline__ void qk_row(const QkNormArgs& a, int row, int lane) {
   const int b = row / a.rows_per_branch, rb = row % a.rows_per_branch;
   const bool rotate = a.rope && (rb % a.rm.Lq) < a.rm.Lv;   // video rows only
   const int half_d = a.d / 2;
+  // A lane's groups are 512 channels apart: when d divides 512 they sit at the same offset inside
+  // their heads and share one set of rotary entries, loaded once.
+  const bool one_cs = rotate && 512 % a.d == 0;
+  float2 cs_lane[4];
+  if (one_cs) {
+    const float2* cs = a.rope + (long)rb * half_d + ((8 * lane) % a.d) / 2;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) cs_lane[pp] = cs[pp];
+  }
   float y[GPL][8];
   float ss = 0.f;
 #pragma unroll
@@ -201,7 +210,7 @@ __device__ __forceinline__ void qk_row(const QkNormArgs& a, int row, int lane) {
       const float2* cs = a.rope + (long)rb * half_d + (ch0 % a.d) / 2;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        const float2 t = cs[pp];
+        const float2 t = one_cs ? cs_lane[pp] : cs[pp];
         const float r0 = y[k][2 * pp] * t.x - y[k][2 * pp + 1] * t.y;
         const float r1 = y[k][2 * pp] * t.y + y[k][2 * pp + 1] * t.x;
         y[k][2 * pp] = r0;
