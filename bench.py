@@ -194,6 +194,24 @@ def summarize_trace(db: str):
             print("| layer wall time (QKV start to next QKV start) | %.1f |" % ((ks[b][1] - ks[a][1]) / 1e3))
 
 
+def summarize_grid(db: str, name_filter: str):
+    """Kernel durations of a rocprofv3 --kernel-trace database grouped by kernel and grid size (one
+    line per launch shape: calls, median and minimum microseconds), for kernels whose name contains
+    ``name_filter``. Markdown on stdout."""
+    import sqlite3
+    if not os.path.isfile(db):
+        raise SystemExit("no such database: %s" % db)
+    cur = sqlite3.connect("file:%s?mode=ro" % db, uri=True).cursor()
+    groups = {}
+    for n, gx, wx, s0, e0 in cur.execute("select name, grid_x, workgroup_x, start, end from kernels"):
+        k = short_kernel_name(n)
+        if name_filter in k:
+            groups.setdefault((k, gx // max(wx, 1), wx), []).append((e0 - s0) / 1e3)
+    print("| kernel | workgroups | threads | calls | median (us) | min (us) |\n|---|---:|---:|---:|---:|---:|")
+    for (k, wgs, wx), ds in sorted(groups.items()):
+        print("| `%s` | %d | %d | %d | %.2f | %.2f |" % (k, wgs, wx, len(ds), median(ds), min(ds)))
+
+
 def summarize_pmc(dbs, name_filter: str):
     """Mean of every counter per dispatch, per kernel whose name contains ``name_filter``, over the
     rocprofv3 --pmc databases ``dbs`` (one pass each): a markdown table on stdout."""
@@ -281,6 +299,9 @@ def main():
                     help="per-kernel mean of every counter in rocprofv3 --pmc databases (kernels whose name contains "
                          "--kernel-filter)")
     ap.add_argument("--kernel-filter", default="", help="substring of the kernel names --summarize-pmc reports")
+    ap.add_argument("--summarize-grid", metavar="DB",
+                    help="kernel durations of a rocprofv3 --kernel-trace database per kernel and grid size "
+                         "(with --kernel-filter)")
     ap.add_argument("--summarize-trace", metavar="DB",
                     help="per-kernel totals, stack-pass wall times and one layer's dispatches of a rocprofv3 "
                          "--kernel-trace database of a bench.py run")
@@ -288,6 +309,9 @@ def main():
                     help="turn the two rocprofv3 --pmc databases of a --counters run (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.summarize_grid:
+        summarize_grid(args.summarize_grid, args.kernel_filter)
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return
