@@ -333,3 +333,36 @@ def test_denoise_chunk_replay_validation():
                                           0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 1 << 30, None, None, None)
         assert st == wam.WAM_E_ARG, st
 
+
+
+def test_row_op_validation():
+    """The kernel-level row ops reject bad arguments before any launch, and an empty call succeeds
+    (fake pointers: nothing is dereferenced, no GPU needed)."""
+    lib = _lib()
+    P = 0x1000
+    # split finish: part, splits, M, N, bias, h, e6, mod_gate, gate_idx, mod_norm, shift, scale, rms, eps, y
+    ok = (P, 3, 0, 5120, None, P, P, P, 5, P, 0, 1, 0, 1e-6, P, None)
+    assert lib.wam_op_split_finish(*ok) == wam.WAM_OK
+    assert lib.wam_op_split_finish(P, 1, 8, 5120, None, P, P, P, 5, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_split_finish(P, 5, 8, 5120, None, P, P, P, 5, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_split_finish(P, 3, 8, 5122, None, P, P, P, 5, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_split_finish(P, 3, 8, 8196, None, P, P, P, 5, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_split_finish(P, 3, 8, 5120, None, P, P, None, 5, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_ARG
+    assert lib.wam_op_split_finish(P, 3, 8, 5120, None, P, P, P, 6, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_ARG
+    assert lib.wam_op_split_finish(P, 3, 8, 5120, None, P, P, P, 5, P, 0, 1, 0, 0.0, P, None) == wam.WAM_E_ARG
+    assert lib.wam_op_split_finish(P + 4, 3, 8, 5120, None, P, P, P, 5, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_ARG
+    # without a gate the gate offsets may be NULL
+    assert lib.wam_op_split_finish(P, 3, 0, 5120, None, P, P, None, -1, P, 3, 4, 0, 1e-6, P, None) == wam.WAM_OK
+    # modulated norm: x, M, D, e6, mod, shift, scale, rms, eps, y
+    assert lib.wam_op_modulated_norm(P, 0, 5120, P, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_OK
+    assert lib.wam_op_modulated_norm(P, 8, 5118, P, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_modulated_norm(P, 8, 5120, P, P, -1, 1, 0, 1e-6, P, None) == wam.WAM_E_ARG
+    assert lib.wam_op_modulated_norm(P, 8, 5120, None, P, 0, 1, 0, 1e-6, P, None) == wam.WAM_E_ARG
+    # q/k/v: qkv, br, rows, Lq, Lv, H, d, g_q, g_k, eps, rope, q_out, k_cache, v_cache, cap, row0
+    assert lib.wam_op_qkv_cache(P, 2, 0, 464, 440, 40, 128, P, P, 1e-6, P, P, P, P, 928, 0, None) == wam.WAM_OK
+    assert lib.wam_op_qkv_cache(P, 2, 464, 464, 440, 40, 96, P, P, 1e-6, P, P, P, P, 928, 0, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_qkv_cache(P, 2, 464, 464, 440, 40, 128, P, P, 1e-6, P, P, P, P, 928, 472, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_qkv_cache(P, 2, 460, 464, 440, 40, 128, P, P, 1e-6, P, P, P, P, 928, 0, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_qkv_cache(P, 2, 464, 464, 470, 40, 128, P, P, 1e-6, P, P, P, P, 928, 0, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_qkv_cache(P, 2, 464, 464, 440, 80, 128, P, P, 1e-6, P, P, P, P, 928, 0, None) == wam.WAM_E_SHAPE
+    assert lib.wam_op_qkv_cache(P, 2, 464, 464, 440, 40, 128, P, None, 1e-6, P, P, P, P, 928, 0, None) == wam.WAM_E_ARG
