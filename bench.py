@@ -290,7 +290,7 @@ def main():
     ap.add_argument("--elementwise", action="store_true",
                     help="HBM-bound kernels: the flow update from the step's size to a >1 GB footprint (buffers "
                          "rotated through a 1.5 GiB pool, past the 256 MB Infinity Cache) beside a 1 GiB copy, and one "
-                         "config-3 block over 1 and 8 chunks (for a kernel trace of its row kernels)")
+                         "one full-width block of the 40-layer step over 1 and 8 chunks (for a kernel trace of its row kernels)")
     ap.add_argument("--attention", action="store_true",
                     help="bf16 and MXFP8 attention kernels at the step's self- and cross-attention shapes")
     ap.add_argument("--attention-shape", choices=("self", "cross", "both"), default="both",
@@ -527,7 +527,7 @@ def elementwise(args, dev):
     still moves all of them. "resident" reuses one buffer set per call; "rotated" walks the calls through a
     1.5 GiB pool so that consecutive calls touch new memory. The copy is torch's device copy of 1 GiB
     between two rotated pairs (2 GiB moved per call), the practical HBM ceiling next to the 8 TB/s
-    nominal figure. The block pass runs one config-3 block (layer 0) over 1 and 8 chunks: its split-K
+    nominal figure. The block pass runs layer 0 of the 40-layer CFG-2 step (928 cached tokens) over 1 and 8 chunks: its split-K
     finishes and q/k/v kernel then see 105 MB and 840 MB footprints, timed per kernel by a trace."""
     import torch
 
@@ -690,14 +690,14 @@ def elementwise(args, dev):
                       "unit": "GB/s", "n_gpus": 1, "dtype": "f32", "data": "synthetic",
                       "config": {"workload": "flow update 2 branches, 24 B per element; split-K finish, 22 B per "
                                              "element; adaLN, 6 B; q/k/v post-processing, 12 B; width 5120; "
-                                             "config-3 block over 1 and 8 chunks"},
+                                             "one block of the 40-layer step over 1 and 8 chunks"},
                       "hbm_peak_GBps": PEAK_HBM_GBS, "copy_1GiB_GBps": round(copy_gbps, 1),
                       "copy_frac": round(copy_gbps / PEAK_HBM_GBS, 3), "flow": flow, "split_finish": rowk["finish"],
                       "modulated_norm": rowk["norm"], "qkv_cache": rowk["qkv"], "block_ms": blocks}))
 
 
 def attention_kernels(args, dev):
-    """bf16 (`attn3_kernel`) and MXFP8 (`attn_mx_kernel`) attention at the config-3 shapes: self-attention
+    """bf16 (`attn3_kernel`) and MXFP8 (`attn_mx_kernel`) attention at the 40-layer step's shapes: self-attention
     of 2 branches x 40 heads, 464 queries over 928 cached + 464 current keys (chunk-causal), and
     cross-attention over the 769 condition tokens. Operands are random (N(0, 1), quantised on the
     device for the MXFP8 op); HIP events around 20 back-to-back launches. Work: 4 br H Lq Lk_visible d."""
@@ -748,14 +748,15 @@ def attention_kernels(args, dev):
             us = a.elapsed_time(b) / 20 * 1e3
             out["%s_%s_us" % (name, kind)] = round(us, 2)
             out["%s_%s_tflops" % (name, kind)] = round(flops / (us * 1e-6) / 1e12, 1)
-    print(json.dumps({"metric": "attention kernel time at the config-3 shapes", "unit": "us", "n_gpus": 1,
+    print(json.dumps({"metric": "attention kernel time at the 40-layer step's shapes", "unit": "us", "n_gpus": 1,
                       "dtype": "bf16 and mxfp8", "data": "synthetic N(0,1)",
                       "config": {"workload": "2 x 40 heads, 464 queries; self 1392 keys chunk-causal, cross 769 keys"},
                       **out}))
 
 
 def extra_workload(args, dev):
-    """The other measured configurations (one JSON line each; the step metric is workload 3)."""
+    """The other measured configurations (one JSON line each): one full-width block, four chunks of 16
+    Euler steps, and the three-view long-context step; the default run measures the 40-layer CFG-2 step."""
     import numpy as np
     import torch
 
@@ -871,7 +872,7 @@ def extra_workload(args, dev):
         print(json.dumps(out))
         return
 
-    # workload 5: one step with decoupled timesteps, then a 16-step loop with velocity reuse
+    # three-view long context: one step with decoupled timesteps, then a 16-step loop with velocity reuse
     start = w.cache_chunks * w.frames_per_chunk
     xv = f32(draw_named(w, -1, "eps_video_%d" % w.cache_chunks, n_chunks=8))
     xa = f32(draw_named(w, -1, "eps_action_%d" % w.cache_chunks, n_chunks=8))

@@ -23,8 +23,8 @@ Sources (titles of the pages; sections named, never quoted):
           real-time optimisations (CFG in parallel, DiT caching by cosine
           similarity of successive velocities, DreamZero-Flash Beta schedule).
 
-Readings where the pages are silent, ambiguous or garbled are listed in
-the design doc and are repeated at the function that takes them.
+Readings where the pages are silent, ambiguous or garbled are stated at the
+function that takes them.
 
 Conventions: time t in [0, 1], t = 0 pure noise, t = 1 clean;
 x_t = t*x1 + (1-t)*eps; velocity target x1 - eps; Euler x += (t_next - t)*v.
@@ -604,7 +604,7 @@ def kv_evict(w, cache: KVCache, drop_rows: int, frame_shift: int) -> None:
 
 
 # ----------------------------------------------------------------------------------------------
-# Guidance, Euler update, velocity reuse ([N569] real-time optimisations; BASELINE Euler reading)
+# Guidance, Euler update, velocity reuse ([N569] real-time optimisations; Euler on the step grid)
 # ----------------------------------------------------------------------------------------------
 
 def cfg_combine(v_branches: Array, guidance: float) -> Array:

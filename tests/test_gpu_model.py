@@ -548,8 +548,8 @@ def test_denoise_chunk_unipc_matches_oracle(gpu, tiny_oracle, dtype, order, corr
 
 @pytest.mark.parametrize("nv,na", [(28160, 192), (28161, 193), (9_000_000, 4096)])
 def test_flow_step_matches_oracle(gpu, nv, na):
-    """The config-3 sizes (float4 path), odd sizes (scalar path) and a large latent whose grid reaches
-    the 512-workgroup limit."""
+    """The step's latent sizes (440 x 64 video and 24 x 8 action elements per branch; float4 path), odd
+    sizes (scalar path) and a large latent whose grid reaches the 512-workgroup limit."""
     rng = synth.tensor_key(101, 0, "flow")
     v = synth.fill((2, nv + na), rng, "normal", 1.0)
     xv = synth.fill((nv,), rng + 1, "normal", 1.0)
