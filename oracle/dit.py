@@ -47,7 +47,7 @@ Array = np.ndarray
 # ----------------------------------------------------------------------------------------------
 
 def silu(x: Array) -> Array:
-    """SiLU(x) = x * sigmoid(x) ([ARCH] §2.3: time embedding MLP; Wan-style, reading R2)."""
+    """SiLU(x) = x * sigmoid(x) ([ARCH] §2.3: time embedding MLP; Wan-style, a reading of the pages)."""
     return x / (x.dtype.type(1) + np.exp(-x))
 
 
@@ -61,7 +61,7 @@ def gelu_tanh(x: Array) -> Array:
 def layer_norm(x: Array, eps: float, weight: Optional[Array] = None, bias: Optional[Array] = None) -> Array:
     """LayerNorm over the last axis, biased variance: (x - mean) / sqrt(var + eps) [* w + b].
 
-    Reading R5: the block norms are LayerNorm (the running implementation's kernel policy on
+    Reading: the block norms are LayerNorm (the running implementation's kernel policy on
     [WS1] names LayerNorm), not the RMSNorm drawn on [ARCH] §2.3.
     """
     mu = x.mean(axis=-1, keepdims=True)
@@ -111,7 +111,7 @@ def project(w, x: Array, W: Array, b: Optional[Array] = None) -> Array:
 
 def modulated_norm(x: Array, shift: Array, scale: Array, eps: float, rms: bool = False) -> Array:
     """adaLN: LN(x) (1 + scale) + shift ([ARCH] §2.3 single block: the normed input is modulated
-    by shift and scale from the time embedding; reading R3: scale enters as 1 + scale). With
+    by shift and scale from the time embedding; reading: scale enters as 1 + scale). With
     ``rms`` (the RMSNorm variant drawn on [ARCH] §2.3) the normalisation is RMSNorm."""
     n = rms_norm(x, eps) if rms else layer_norm(x, eps)
     return n * (x.dtype.type(1) + scale) + shift
@@ -135,7 +135,7 @@ def attention(q: Array, k: Array, v: Array, visible: Optional[Array] = None) -> 
     q [H, Lq, d], k [H, Lk, d], v [H, Lk, d]; ``visible`` [Lq, Lk] bool or None.
     S = q k^T / sqrt(d); invisible entries are *selected* to -inf (so whatever the
     hidden keys hold cannot reach the output); P = softmax(S); o = P v  -> [H, Lq, d].
-    Reading R10: scale 1/sqrt(d), softmax in the working precision.
+    Reading: scale 1/sqrt(d), softmax in the working precision.
     """
     d = q.shape[-1]
     s = (q @ np.swapaxes(k, -1, -2)) * q.dtype.type(1.0 / math.sqrt(d))
@@ -152,7 +152,7 @@ def attention(q: Array, k: Array, v: Array, visible: Optional[Array] = None) -> 
 def timestep_sinusoid(t: float, freq_dim: int, dt=np.float32) -> Array:
     """Sinusoidal embedding of the noise level s = 1000 (1 - t).
 
-    Reading R1/R2: t follows x_t = t x1 + (1-t) eps, and the pages' training pipeline samples a
+    Reading: t follows x_t = t x1 + (1-t) eps, and the pages' training pipeline samples a
     noise step in [0, 1000] with noise at the top, so the embedded scalar is s = 1000 (1 - t).
     emb = [cos(s w_i)]_i ++ [sin(s w_i)]_i with w_i = 10000^(-i/half), i < half = freq_dim/2.
     The angles and their cos/sin are evaluated in float64 and rounded once to the working type.
@@ -167,7 +167,7 @@ def timestep_sinusoid(t: float, freq_dim: int, dt=np.float32) -> Array:
 def time_modulation(t: float, g: Dict[str, Array], freq_dim: int, dt=np.float32) -> Tuple[Array, Array]:
     """e = W2 SiLU(W1 emb + b1) + b2;  e6 = (Wp SiLU(e) + bp) as [6, D].
 
-    Reading R3/R4: one shared time projection to six vectors (shift1, scale1, gate1, shift2,
+    Reading: one shared time projection to six vectors (shift1, scale1, gate1, shift2,
     scale2, gate2); each layer adds its own learned [6, D] offset.
     """
     emb = timestep_sinusoid(t, freq_dim, dt)
@@ -178,7 +178,7 @@ def time_modulation(t: float, g: Dict[str, Array], freq_dim: int, dt=np.float32)
 
 # ----------------------------------------------------------------------------------------------
 # 3-D rotary embedding of video tokens ([ARCH] §2.3: video latents go through RoPE; action tokens
-# do not). Reading R9: per-head channel pairs (2j, 2j+1); the first d_t/2 pairs rotate with the
+# do not). Reading: per-head channel pairs (2j, 2j+1); the first d_t/2 pairs rotate with the
 # frame index, the next d_h/2 with the patch row, the last d_w/2 with the patch column;
 # d_h = d_w = 2 floor(d/6), d_t = d - 2 d_h; frequency theta^(-2j'/d_axis) for local pair j'.
 # ----------------------------------------------------------------------------------------------
@@ -202,7 +202,7 @@ def rope_frequencies(head_dim: int, theta: float) -> Tuple[Array, Array]:
 def video_positions(w, n_chunks: int, start_frame: int) -> Array:
     """(frame, row, col) of every video token of ``n_chunks`` consecutive chunks, [n*Lv, 3].
 
-    Tokens of a chunk are in raster order (frame, row, col) (reading R8); frame indices are
+    Tokens of a chunk are in raster order (frame, row, col) (a reading of the pages); frame indices are
     absolute within the attention window: start_frame + chunk * frames_per_chunk + local frame
     ([WS1] continuous requests: the pipeline carries a frame position across requests).
     """
@@ -247,7 +247,7 @@ def build_context(w, g: Dict[str, Array], txt: Array, img: Optional[Array], stat
     -> [br, Lc, D].
 
     [ARCH] §2.1: image and text features (1536-d) are concatenated into one condition sequence;
-    reading R12: one Linear per modality to the model width. Branch 1 carries the negative
+    reading: one Linear per modality to the model width. Branch 1 carries the negative
     (null) prompt ([WS1] request format); the image features are shared by both branches.
     State rows: [HYPER] 方法 has proprioception pass a state encoder beside the text encoder
     before the modalities are fused into the causal DiT, and [N569] (architecture) counts that
@@ -271,7 +271,7 @@ def build_context(w, g: Dict[str, Array], txt: Array, img: Optional[Array], stat
 def context_kv(w, lp: Dict[str, Array], ctx: Array) -> Tuple[Array, Array]:
     """Per-layer cross-attention keys/values of the condition sequence (computed once per request:
     [ARCH] §4 encodes the conditions once and caches them). Kc = RMS(ctx Wck^T + b) g; Vc = ctx Wcv^T + b.
-    Reading R11: RMSNorm on cross keys and queries, over the full width.
+    Reading: RMSNorm on cross keys and queries, over the full width.
     """
     kc = rms_norm(linear(ctx, lp["w_ck"], lp["b_ck"]), w.eps, lp["g_ck"])
     vc = linear(ctx, lp["w_cv"], lp["b_cv"])
@@ -321,7 +321,7 @@ def token_layout(w, n_chunks: int) -> Tuple[Array, Array, Array]:
 
 
 def feed_forward(w, lp: Dict[str, Array], y: Array) -> Array:
-    """GELU_tanh(y W1^T + b1) W2^T + b2 (reading R6); with the SwiGLU variant drawn on [ARCH] §2.3,
+    """GELU_tanh(y W1^T + b1) W2^T + b2 (a reading of the pages); with the SwiGLU variant drawn on [ARCH] §2.3,
     (SiLU(y Wg^T + bg) * (y Wu^T + bu)) W2^T + b2 where rows 2j / 2j+1 of W1 (and entries of b1)
     are the gate / up rows of hidden unit j."""
     u = project(w, y, lp["w_ff1"], lp["b_ff1"])
@@ -333,7 +333,7 @@ def feed_forward(w, lp: Dict[str, Array], y: Array) -> Array:
 
 
 def visibility(w, chunk: Array, group: Array, cached: int) -> Array:
-    """[T, cached + T] mask of the self-attention (reading R7): a query sees every cached clean key
+    """[T, cached + T] mask of the self-attention (a reading of the pages): a query sees every cached clean key
     and the keys of earlier chunks of the pass; inside its own chunk it sees every token
     (bidirectional), or, with the frame-causal variant of [ARCH] §2.3 causal mask, a video token sees
     the video tokens of its own and earlier frames of the chunk and an action token the whole chunk."""
@@ -382,9 +382,9 @@ def block_forward(w, lp: Dict[str, Array], h: Array, mods: Array, ctx_k: Array, 
     Returns (h_out, k_new, v_new) where k_new/v_new [br, T, D] are this call's keys/values.
 
     Order ([ARCH] §2.3 single block): norm -> modulation -> causal self-attention -> residual ->
-    norm -> cross-attention -> residual -> norm -> FFN -> residual. Readings: R3 (gates on the
-    self-attention and FFN residuals only; (1 + scale)), R5 (LayerNorm), R6 (GELU-tanh FFN),
-    R7 (chunk-level mask, bidirectional inside a chunk), R9 (RoPE), R11 (cross q/k RMSNorm).
+    norm -> cross-attention -> residual -> norm -> FFN -> residual. Readings: gates on the
+    self-attention and FFN residuals only, scale entering as (1 + scale); LayerNorm; GELU-tanh FFN;
+    chunk-level mask, bidirectional inside a chunk; RoPE as in apply_rope; cross q/k RMSNorm.
     """
     br, T, D = h.shape
     H, d = w.heads, w.head_dim
@@ -576,7 +576,7 @@ def stack_passes(model: Model, ctx: Array, passes: Sequence[PassSpec], dt=np.flo
 def kv_append(model: Model, cache: KVCache, ctx_kv, x_video: Array, x_action: Array,
               start_frame: int, dt=np.float32) -> None:
     """Commit one clean chunk: a stack pass at t_video = t_action = 1 whose keys/values are
-    appended (reading R17: cached chunks are clean, t = 1). [HYPER] 方法: predicted frames in the
+    appended (reading: cached chunks are clean, t = 1). [HYPER] 方法: predicted frames in the
     KV cache are replaced by real observations after the chunk executes."""
     stack_forward(model, cache, ctx_kv, x_video, x_action, [1.0], [1.0], 1, start_frame, dt, commit=True)
 
@@ -610,7 +610,7 @@ def kv_evict(w, cache: KVCache, drop_rows: int, frame_shift: int) -> None:
 def cfg_combine(v_branches: Array, guidance: float) -> Array:
     """Classifier-free guidance: v = v_uncond + w (v_cond - v_uncond); branch 0 is conditional,
     branch 1 the negative/null prompt ([N569]: the conditional and unconditional passes; [WS1]
-    request format: negative prompt). Reading R13: w applies to video and action alike; the sum
+    request format: negative prompt). Reading: w applies to video and action alike; the sum
     is evaluated as w v_cond + (1 - w) v_uncond, which is the same quantity and returns either
     branch exactly at w = 1 or w = 0."""
     v0, v1 = v_branches[0], v_branches[1]
@@ -620,12 +620,12 @@ def cfg_combine(v_branches: Array, guidance: float) -> Array:
 
 
 def euler_update(x: Array, v: Array, t: float, t_next: float) -> Array:
-    """x <- x + (t_next - t) v (reading R14: Euler on the flow-matching ODE)."""
+    """x <- x + (t_next - t) v (reading: Euler on the flow-matching ODE)."""
     return x + x.dtype.type(t_next - t) * v
 
 
 def interpolate(x1: Array, eps: Array, t: float) -> Array:
-    """x_t = t x1 + (1 - t) eps (reading R1 of the pages' linear interpolation)."""
+    """x_t = t x1 + (1 - t) eps (reading of the pages' linear interpolation)."""
     return x1.dtype.type(t) * x1 + x1.dtype.type(1.0 - t) * eps
 
 
@@ -643,7 +643,7 @@ def denoise_chunk(dit, x_video: Array, x_action: Array, grid: Sequence[float], t
     dit(x_video, x_action, t) -> guided (v_video, v_action). Steps 0 and 1 always run the DiT;
     at step k >= 2, if the cosine similarity of the two most recent DiT-computed guided video
     velocities exceeds tau, the DiT is skipped and the latest computed velocity is reused
-    (reading R15). Returns (x_video, x_action, number of DiT calls, per-step flags). ``trace``, if
+    (a reading of the pages). Returns (x_video, x_action, number of DiT calls, per-step flags). ``trace``, if
     given, receives (k, cosine) for every step whose decision evaluated a cosine.
     """
     computed: List[Tuple[Array, Array]] = []

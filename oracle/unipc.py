@@ -99,7 +99,7 @@ def denoise_chunk_unipc(dit, x_video: Array, x_action: Array, grid: Sequence[flo
     """UniPC loop with CFG-guided velocities and velocity reuse ([WS1] dynamic16; [N569] DiT caching).
 
     dit(x_video, x_action, t) -> guided (v_video, v_action). The reuse rule is the Euler loop's
-    (reading R15). Without ``corrector`` only the predictor runs (order 1 is then the Euler loop).
+    (a reading of the pages). Without ``corrector`` only the predictor runs (order 1 is then the Euler loop).
     Returns (x_video, x_action, number of DiT calls, per-step reuse flags).
     """
     assert all(b > a for a, b in zip(grid[:-1], grid[1:])) and grid[0] >= 0.0 and grid[-1] <= 1.0

@@ -7,13 +7,13 @@ positions, each against values fixed outside the function under test:
 * the [6, D] modulation split, through the block: with a zero modulation projection the six slots
   are the bias's six consecutive D-blocks, and a block whose first (or second) norm scale is -1
   collapses to a closed form that names which slot is shift, scale and gate (same page, §2.3 single
-  causal block: shift/scale modulation of each norm's output, gated residuals; reading R3);
+  causal block: shift/scale modulation of each norm's output, gated residuals; a reading of the pages);
 * output head: LN(h)(1 + scale_h) + shift_h with both shift and scale offset by e, pinned by row
   statistics (same page, §2.3 output split);
 * per-token timesteps: video rows of chunk c take t_video[c], action rows t_action[c] (paper
   walk-through, DreamZero-Flash: decoupled video / action noise levels);
 * video positions: raster order (frame, row, column) written out for grids with rows != columns,
-  and the rotary bands each axis turns (reading R9).
+  and the rotary bands each axis turns (a reading of the pages).
 """
 import math
 
