@@ -84,7 +84,7 @@ def summarize_counters(fetch_db: str, write_db: str):
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         rows = per_dispatch(db, counter)
         copy = max((v for n, v in rows if "elementwise" in n), default=None)
-        gemm = [v for n, v in rows if "gemm4_kernel<0" in n]
+        gemm = [v for n, v in rows if "gemm4p_kernel<0" in n]
         if copy is None or not gemm:
             raise SystemExit("counters not found in %s" % db)
         known = float(1 << 30)   # the copy moves 2^28 floats each way
@@ -183,7 +183,7 @@ def summarize_trace(db: str):
     last = [i for i, (n, _, _) in enumerate(ks) if "sinusoid" in n]
     if len(last) >= 2:
         lo, hi = last[-2], last[-1]
-        qkv = [i for i in range(lo, hi) if re.search(r"gemm4_kernel<0(>|, )", ks[i][0])]
+        qkv = [i for i in range(lo, hi) if re.search(r"gemm4p?_kernel<0(>|, )", ks[i][0])]
         if len(qkv) > 21:
             a, b = qkv[20], qkv[21]
             print("\none layer of the last full stack pass (dispatch order, from the middle layer's QKV product):\n")
@@ -279,6 +279,9 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
                     help="3: the step metric (default); 2: one full-width block (br = 2 and B = 1); 4: four chunks "
                          "of 16 Euler steps plus KV appends; 5: three-view long context, 16-step loop with reuse")
+    ap.add_argument("--unpacked", action="store_true",
+                    help="bf16 projections from the unpacked [out][in] matrices instead of the fragment-packed copies "
+                         "(the default); for comparisons on one box, reported under its own workload name")
     ap.add_argument("--precision", choices=("bf16", "mxfp8", "mxfp4w"), default="bf16",
                     help="bf16 (the metric); mxfp8: the six block projections quantised to MXFP8; mxfp4w: their "
                          "weights MXFP4, activations MXFP8 -- reported separately (own dtype and workload name)")
@@ -361,9 +364,11 @@ def main():
         torch.mul(x, 1.0, out=y)
         a = torch.randn((M, D), device=dev).to(torch.bfloat16)
         wq = (torch.randn((3 * D, D), device=dev) * 0.02).to(torch.bfloat16)
+        wqp = torch.empty_like(wq)
+        wam.wam_pack_weight(wq, D, 3 * D, D, wqp)
         c = torch.empty((M, 3 * D), dtype=torch.bfloat16, device=dev)
         for _ in range(5):
-            wam.wam_op_linear(wam.WAM_BF16, a, D, wq, D, None, c, 3 * D, M, 3 * D, D, 0)
+            wam.wam_op_linear_packed(a, D, wqp, None, c, 3 * D, M, 3 * D, D, 0)
         torch.cuda.synchronize()
         print(json.dumps({"counters_run": True, "copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4}))
         return
@@ -372,8 +377,9 @@ def main():
         print("[bench] %s" % msg, file=sys.stderr, flush=True)
 
     t_setup = time.perf_counter()
-    log("uploading %s weights" % w.name)
-    model = DeviceModel(w, "bf16", dev)
+    packed = not mx and not args.unpacked
+    log("uploading %s weights%s" % (w.name, " (fragment-packed projections)" if packed else ""))
+    model = DeviceModel(w, "bf16", dev, packed=packed)
     log("weights resident (%.1f s); building condition KV and %d cached chunks" % (time.perf_counter() - t_setup,
                                                                                   w.cache_chunks))
     ws = workspace(model.cfg, 1, dev)
@@ -429,14 +435,16 @@ def main():
     wam.wam_qkv_timer_config(-1)
     finite = bool(torch.isfinite(vv).all().item() and torch.isfinite(va).all().item())
 
-    # dominant kernel: the QKV projection GEMM (M = 928, N = 15360, K = 5120; bf16 MFMA, or the scaled fp8
-    # MFMA on the packed weights). The roofline uses the in-step samples above; 20 back-to-back launches of
-    # the same kernel and launch configuration (layer 0's weights, HIP events on the library's stream) are
-    # reported beside them: they run at the lower clock of sustained matrix work
+    # dominant kernel: the QKV projection GEMM (M = 928, N = 15360, K = 5120; bf16 MFMA on the fragment-packed
+    # weights, or the scaled fp8 MFMA on the MX-packed ones). The roofline uses the in-step samples above; 20
+    # back-to-back launches of the same kernel and launch configuration (layer 0's weights, HIP events on the
+    # library's stream) are reported beside them: they run at the lower clock of sustained matrix work
     y = torch.randn((M, D), device=dev).to(torch.bfloat16)
     cq = torch.empty((M, 3 * D), dtype=torch.bfloat16, device=dev)
-    wq, bq = model.layers[0]["w_qkv"], model.layers[0]["b_qkv"]
-    if mx:
+    bq = model.layers[0]["b_qkv"]
+    if packed:   # w_qkv's packed copy opens layer 0's arena
+        qkv_op = lambda: wam.wam_op_linear_packed(y, D, model.blocks[0].pk, bq, cq, 3 * D, M, 3 * D, D, 0)  # noqa: E731
+    elif mx:
         yq = torch.empty((M, D), dtype=torch.uint8, device=dev)
         ys = torch.empty((M, D // 32), dtype=torch.uint8, device=dev)
         wam.wam_mx_quantize(wam.WAM_BF16, y, D, M, D, yq, D, ys)
@@ -446,6 +454,7 @@ def main():
         qkv_op = lambda: wam.wam_op_linear_mx(yq, ys, D, arena, wq_s, wrow, bq, cq, 3 * D, M, 3 * D, D, 0,  # noqa: E731
                                               w_format=wam.WAM_MX_E2M1 if w4 else wam.WAM_MX_E4M3)
     else:
+        wq = model.layers[0]["w_qkv"]
         qkv_op = lambda: wam.wam_op_linear(wam.WAM_BF16, y, D, wq, D, bq, cq, 3 * D, M, 3 * D, D, 0)  # noqa: E731
     for _ in range(3):
         qkv_op()
@@ -463,8 +472,8 @@ def main():
     peak_meas = measured_mfma_peak(wam, torch, dev)
     gemm_flops = 2.0 * M * 3 * D * D
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
-    traffic = None if mx else load_traffic(TRAFFIC_KEY, source_hash(os.path.join(ROOT, "world_action_video_amd", "csrc",
-                                                                                  "gemm.hip")))
+    traffic = None if not packed else load_traffic(TRAFFIC_KEY, source_hash(os.path.join(ROOT, "world_action_video_amd",
+                                                                                          "csrc", "gemm.hip")))
     peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
 
     fl = step_flops(w)
@@ -484,6 +493,7 @@ def main():
                   "mxfp8 projections, bf16 elsewhere") if mx else "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latents/features)",
         "config": {"workload": w.name + (("+mxfp4w-projections" if w4 else "+mxfp8-projections") if mx else "") +
+                               ("+unpacked-weights" if args.unpacked and not mx else "") +
                                ("+variant%d" % args.variant if args.variant else ""), "layers": w.layers, "dim": w.dim, "heads": w.heads, "head_dim": w.head_dim,
                    "ffn_dim": w.ffn_dim, "branches": w.branches, "chunk_tokens": Lq, "cached_tokens": cache.length,
                    "ctx_tokens": w.ctx_len},
@@ -496,9 +506,12 @@ def main():
         "first_step_ms": round(first_ms, 1),
         "setup_s": round(setup_s, 1),
         "outputs_finite": finite,
-        "roofline": {"kernel": ("gemm4mx_kernel<EPI_STORE, W4> (MXFP4 x MXFP8 scaled MFMA, 256x256" if w4 else
-                                "gemm4mx_kernel<EPI_STORE> (MXFP8 scaled MFMA, 256x256" if mx else
-                                "gemm4_kernel<EPI_STORE, 3, 5> (bf16, 192x320") + " tile, 4 waves; QKV projection, 928x15360x5120)",
+        "roofline": {"kernel": ("gemm4mx_kernel<EPI_STORE, W4> (MXFP4 x MXFP8 scaled MFMA, 256x256 tile" if w4 else
+                                "gemm4mx_kernel<EPI_STORE> (MXFP8 scaled MFMA, 256x256 tile" if mx else
+                                "gemm4p_kernel<EPI_STORE, 5, 3> (bf16, fragment-packed weights, 160x384 tile, waves "
+                                "side by side along N" if packed else
+                                "gemm4_kernel<EPI_STORE, 3, 5> (bf16, 192x320 tile") + ", 4 waves; QKV projection, "
+                                "928x15360x5120)",
                      "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / peak, 4), "traffic": traffic,
                      "avg_launch_us": round(gemm_ms * 1e3, 2),
@@ -663,7 +676,7 @@ def elementwise(args, dev):
 
     w = WORKLOADS[WORKLOAD_ID].with_(layers=1)
     Lq = w.chunk_tokens
-    model = DeviceModel(w, "bf16", dev)
+    model = DeviceModel(w, "bf16", dev, packed=True)
     ctx = DeviceCtx(w, "bf16", dev)
     blocks = {}
     n_max = 8
@@ -773,7 +786,7 @@ def extra_workload(args, dev):
 
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)  # noqa: E731
     log("uploading %s weights" % w.name)
-    model = DeviceModel(w, "bf16", dev)
+    model = DeviceModel(w, "bf16", dev, packed=not args.unpacked)
     ctx = DeviceCtx(w, "bf16", dev)
     ws = workspace(model.cfg, 1, dev)
     img = draw_named(w, -1, "img") if w.ctx_img_len else None
@@ -781,8 +794,8 @@ def extra_workload(args, dev):
                       to_device(img, "bf16", dev) if img is not None else None, ctx.c, ws)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     base = {"n_gpus": 1, "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, N(0,1) latents/features)",
-            "config": {"workload": w.name, "layers": w.layers, "dim": w.dim, "branches": w.branches,
-                       "chunk_tokens": Lq}}
+            "config": {"workload": w.name + ("+unpacked-weights" if args.unpacked else ""), "layers": w.layers,
+                       "dim": w.dim, "branches": w.branches, "chunk_tokens": Lq}}
 
     if args.workload == 2:
         # one block on the residual stream, CFG batch 2 and the B = 1 per-GPU share of a branch split

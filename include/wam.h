@@ -112,6 +112,11 @@ typedef struct {
                                   wam_mx_block_bytes(cfg) bytes written by wam_mx_pack_block, 256-aligned */
   const void *w_cki, *b_cki, *g_cki;   /* IMG_XATTN only (else ignored): image keys [D][D], [D], RMSNorm gain [D] */
   const void *w_cvi, *b_cvi;           /* IMG_XATTN only: image values [D][D], [D] */
+  const void *pk;              /* bf16 NATIVE precision only (else ignored), optional: this layer's six
+                                  projections in the fragment-packed layout, wam_pack_block_bytes(cfg) bytes
+                                  written by wam_pack_block, 256-byte aligned. When set, the block's products
+                                  read it and w_qkv, w_o, w_cq, w_co, w_ff1 and w_ff2 are not read (they may
+                                  be NULL); the results equal the unpacked ones. NULL: unpacked matrices. */
 } wam_block_weights;
 
 /* Action encoder and decoder of one embodiment ([ARCH] §2.4: each robot body has its own linear from
@@ -426,6 +431,33 @@ wam_status wam_op_linear_mx(const void *A, const void *A_scales, int lda, const 
 size_t wam_mx_block_bytes(const wam_config *cfg);
 wam_status wam_mx_pack_block(const wam_config *cfg, const wam_block_weights *bw, void *dst, size_t dst_bytes,
                              void *stream);
+
+/* Fragment-packed weights (bf16): the same projections ([ARCH] §2.3 single causal block: q/k/v,
+ * attention output, cross-attention query and output, the two FFN matrices), stored once in the order
+ * the matrix instructions read them, so the products stream each weight fragment from memory in whole
+ * 1 KB lines instead of staging it through the compute unit's shared memory. Layout of a packed W
+ * [N][K] (N % 32 == 0, K % 64 == 0): N * K bf16 in blocks of 32 rows x 16 k, block (b, c) at element
+ * offset (b * K / 16 + c) * 512, 64 lanes x 8 bf16 in it, lane l holding W[32 b + l % 32][16 c + 8 (l / 32)
+ * .. + 7]; a band of 32 rows therefore occupies the bytes it would unpacked.
+ *   wam_pack_weight: packs W [N][ldw] (device, 16-byte aligned, ldw >= K a multiple of 8) into dst
+ *   (device, N * K * 2 bytes, 16-byte aligned); N * K * 2 < 2^31.
+ *   wam_op_linear_packed: C = act(A Wp^T + bias) as wam_op_linear (bf16 only; A [M][lda], lda >= K a
+ *   multiple of 8; C [M][ldc], ldc a multiple of 4; act 0 / 1 / 2; ws as wam_op_linear) with W given
+ *   packed. Where both products take the same split of K (none, or the same number of ranges, as at
+ *   the block's projection shapes), the result equals the unpacked product bit for bit: the same
+ *   matrix instructions consume the same operands in the same k order.
+ *   wam_pack_block_bytes: the packed size of one layer's six projections (w_qkv, w_o, w_cq, w_co,
+ *   w_ff1, w_ff2 back to back, in this order), 0 for a configuration that cannot be packed (dtype not
+ *   bf16, or a matrix of 2 GiB or more). wam_pack_block packs bw's six matrices into dst (device,
+ *   256-byte aligned, dst_bytes >= that size); run once per layer after the weights are loaded, then
+ *   set the block's pk to dst.
+ * Errors: WAM_E_ARG / WAM_E_SHAPE / WAM_E_UNSUPPORTED, nothing launched. */
+wam_status wam_pack_weight(const void *W, int ldw, int N, int K, void *dst, void *stream);
+wam_status wam_op_linear_packed(const void *A, int lda, const void *Wp, const float *bias, void *C, int ldc, int M,
+                                int N, int K, int act, void *ws, size_t ws_bytes, void *stream);
+size_t wam_pack_block_bytes(const wam_config *cfg);
+wam_status wam_pack_block(const wam_config *cfg, const wam_block_weights *bw, void *dst, size_t dst_bytes,
+                          void *stream);
 
 wam_status wam_op_attention(wam_dtype dtype, const void *Q, const void *K, const void *Vt, void *O, int br, int heads,
                             int head_dim, int Lq, int k_rows, int v_stride, int kv_base, int chunk_q, int kv_total,

@@ -53,7 +53,9 @@ wam_config config(bool full, wam_dtype dt) {
   return c;
 }
 
-Model build(const wam_config& c, int cache_chunks) {
+// packed: each block gets its fragment-packed projections (wam_pack_block) and loses the six unpacked
+// matrices, so a read of those would fall outside every registered region
+Model build(const wam_config& c, int cache_chunks, bool packed = false) {
   Model m;
   m.c = c;
   const size_t e = c.dtype == WAM_BF16 ? 2 : 4, D = c.dim, F = c.ffn_dim;
@@ -80,6 +82,15 @@ Model build(const wam_config& c, int cache_chunks) {
       b.w_cvi = dev(D * D * e, "w_cvi"); b.b_cvi = dev(D * 4, "b_cvi");
     }
     if (c.precision != WAM_PRECISION_NATIVE) b.mx = dev(wam_mx_block_bytes(&c), "mx arena");
+    if (packed) {
+      const size_t pk_bytes = wam_pack_block_bytes(&c);
+      if (!pk_bytes) { std::fprintf(stderr, "host_abi: packed size 0\n"); ++g_fail; }
+      void* pk = dev(pk_bytes, "packed projections");
+      expect(wam_pack_block(&c, &b, pk, pk_bytes, nullptr), WAM_OK, "pack_block");
+      expect(wam_pack_block(&c, &b, pk, pk_bytes - 256, nullptr), WAM_E_ARG, "pack_block into a short arena");
+      b.pk = pk;
+      b.w_qkv = b.w_o = b.w_cq = b.w_co = b.w_ff1 = b.w_ff2 = nullptr;
+    }
   }
   wam_weights& w = m.w;
   w.blocks = m.blocks.data();
@@ -107,9 +118,9 @@ Model build(const wam_config& c, int cache_chunks) {
   return m;
 }
 
-void scenario(const char* name, const wam_config& c) {
+void scenario(const char* name, const wam_config& c, bool packed = false) {
   std::fprintf(stderr, "host_abi: scenario %s\n", name);
-  Model m = build(c, 5);
+  Model m = build(c, 5, packed);
   const size_t e = c.dtype == WAM_BF16 ? 2 : 4;
   const int Lv = m.Lv, La = c.action_tokens, P = c.patch_dim, A = c.action_dim, br = c.branches;
   void* txt = dev((size_t)br * c.ctx_text_len * c.ctx_in_dim * e, "txt");
@@ -190,6 +201,13 @@ void scenario(const char* name, const wam_config& c) {
          WAM_E_CAPACITY, "block_fwd commit over capacity");
   expect(m.kv.length, len, "length unchanged by a failed call");
   expect(wam_kv_evict(&m.c, &m.kv, m.Lq + 8, 0, nullptr), WAM_E_SHAPE, "evict partial chunk");
+  if (packed) {   // a misaligned packed arena is rejected before anything runs
+    const void* pk = m.blocks[0].pk;
+    m.blocks[0].pk = static_cast<const char*>(pk) + 16;
+    expect(wam_dit_stack_fwd(&m.c, &m.w, &m.kv, &m.cx, 1, xv, xa, t1, t2, 4, vv, va, m.ws, m.ws_bytes, nullptr),
+           WAM_E_ARG, "stack_fwd with a misaligned packed arena");
+    m.blocks[0].pk = pk;
+  }
   unsigned char bad[16] = {0, 1};   // step 1 always runs the DiT
   expect(wam_denoise_chunk_replay(&m.c, &m.w, &m.kv, &m.cx, xv, xa, grid, 16, 5.f, bad, 4, vv, va, gv, ga, cp, m.ws,
                                   m.ws_bytes, nullptr, &calls, cos), WAM_E_ARG, "replay skipping step 1");
@@ -212,6 +230,28 @@ int main() {
            "op_linear K not a multiple of 64");
     expect(wam_op_attention(WAM_BF16, a, wt, cc, a, 1, 2, 64, 32, 64, 64, 0, 0, 64, nullptr, 0, nullptr), WAM_OK,
            "op_attention");
+    void* wp = dev(64 * 64 * 2, "packed W");
+    expect(wam_pack_weight(wt, 64, 64, 64, wp, nullptr), WAM_OK, "pack_weight");
+    expect(wam_op_linear_packed(a, 64, wp, nullptr, cc, 64, 64, 64, 64, 0, nullptr, 0, nullptr), WAM_OK,
+           "op_linear_packed");
+    expect(wam_op_linear_packed(a, 64, wp, nullptr, cc, 64, 40, 64, 64, 2, nullptr, 0, nullptr), WAM_OK,
+           "op_linear_packed swiglu");
+    {
+      const long before_pk = host_abi::g_launches;
+      expect(wam_pack_weight(wt, 64, 48, 64, wp, nullptr), WAM_E_SHAPE, "pack_weight N not a multiple of 32");
+      expect(wam_pack_weight(wt, 60, 64, 64, wp, nullptr), WAM_E_SHAPE, "pack_weight ldw below K");
+      expect(wam_op_linear_packed(a, 64, wp, nullptr, cc, 64, 64, 48, 64, 0, nullptr, 0, nullptr), WAM_E_SHAPE,
+             "op_linear_packed N not a multiple of 32");
+      expect(wam_op_linear_packed(a, 64, wp, nullptr, cc, 64, 64, 64, 64, 3, nullptr, 0, nullptr), WAM_E_ARG,
+             "op_linear_packed act 3");
+      expect(wam_op_linear_packed(a, 64, static_cast<char*>(wp) + 8, nullptr, cc, 64, 64, 64, 64, 0, nullptr, 0,
+                                  nullptr), WAM_E_ARG, "op_linear_packed misaligned W");
+      wam_config cf = config(false, WAM_F32);
+      expect((int)wam_pack_block_bytes(&cf), 0, "pack_block_bytes f32");
+      wam_block_weights nb{};
+      expect(wam_pack_block(&cf, &nb, wp, 1 << 20, nullptr), WAM_E_UNSUPPORTED, "pack_block f32");
+      expect((int)(host_abi::g_launches - before_pk), 0, "no launch by a rejected packing call");
+    }
     float* o = static_cast<float*>(dev(256 * 256 * 4, "probe"));
     expect(wam_mfma_peak_probe(o, 256, 8, nullptr), WAM_OK, "mfma peak probe");
     expect(wam_mfma_peak_probe(o, 0, 8, nullptr), WAM_E_ARG, "mfma peak probe, no workgroups");
@@ -282,7 +322,14 @@ int main() {
     c.precision = WAM_PRECISION_MXFP4W;
     scenario("tiny mxfp4 weights", c);
   }
+  scenario("tiny bf16, packed projections", config(false, WAM_BF16), true);
+  {
+    wam_config c = config(false, WAM_BF16);
+    c.variant = WAM_VARIANT_SWIGLU;
+    scenario("tiny swiglu, packed projections", c, true);
+  }
   scenario("full width bf16, 40 layers", config(true, WAM_BF16));
+  scenario("full width bf16, 40 layers, packed projections", config(true, WAM_BF16), true);
   if (g_fail || host_abi::g_errors) {
     std::fprintf(stderr, "host_abi: %d failed expectations, %d launch-bound errors\n", g_fail, host_abi::g_errors);
     return 1;

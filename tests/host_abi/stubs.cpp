@@ -44,7 +44,8 @@ static size_t esz(DType dt) { return dt == DT_BF16 ? 2 : 4; }
 static void check_gemm(const GemmArgs& a, size_t ea, size_t ew, size_t ec, Epi epi) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) { std::fprintf(stderr, "host_abi: gemm sizes\n"); ++host_abi::g_errors; return; }
   check(a.A, ((size_t)(a.M - 1) * a.lda + a.K) * ea, "gemm A");
-  check(a.W, ((size_t)(a.N - 1) * a.ldw + a.K) * ew, "gemm W");
+  if (a.w_packed) check(a.W, (size_t)a.N * a.K * 2, "gemm packed W");
+  else check(a.W, ((size_t)(a.N - 1) * a.ldw + a.K) * ew, "gemm W");
   if (a.bias) check(a.bias, (size_t)a.N * 4, "gemm bias");
   if (epi == EPI_RESID || epi == EPI_RESID_GATED) check(a.H, ((size_t)(a.M - 1) * a.ldh + a.N) * 4, "gemm H");
   else if (epi == EPI_SWIGLU) check(a.C, ((size_t)(a.M - 1) * a.ldc + a.N / 2) * ec, "gemm C");
@@ -54,6 +55,12 @@ static void check_gemm(const GemmArgs& a, size_t ea, size_t ew, size_t ec, Epi e
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t) {
   ++host_abi::g_launches;
   check_gemm(a, esz(dt), esz(dt), esz(dt), epi);
+  return hipSuccess;
+}
+hipError_t launch_pack_weight(const void* W, long ldw, int N, int K, void* Wp, hipStream_t) {
+  ++host_abi::g_launches;
+  check(W, ((size_t)(N - 1) * ldw + K) * 2, "pack source");
+  check(Wp, (size_t)N * K * 2, "pack destination");
   return hipSuccess;
 }
 hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t) {

@@ -61,9 +61,9 @@ def chunk_inputs(w, chunks):
 class GpuRun:
     """Model, condition keys/values and KV cache of one workload on the GPU."""
 
-    def __init__(self, w, dtype, dev, capacity_chunks, txt, img):
+    def __init__(self, w, dtype, dev, capacity_chunks, txt, img, packed=False):
         self.w, self.dtype, self.dev = w, dtype, dev
-        self.m = DeviceModel(w, dtype, dev)
+        self.m = DeviceModel(w, dtype, dev, packed=packed)
         self.ws = workspace(self.m.cfg, 2, dev)
         self.ctx = DeviceCtx(w, dtype, dev)
         wam.wam_ctx_build(self.m.cfg, self.m.weights, to_device(txt, dtype, dev),
@@ -110,7 +110,8 @@ def _check_outputs(say, gv, ga, ref_v, ref_a, tol):
 @pytest.mark.timeout(1500)
 def test_step_40_layers_cfg2_bf16_matches_oracle(gpu, capsys):
     """The benchmarked step: 40 layers, CFG batch 2, cache of 2 clean chunks (928 tokens), the noisy
-    latents and timestep of bench.py's first step."""
+    latents and timestep of bench.py's first step, with the fragment-packed projections bench.py uses
+    (the unpacked copies deleted)."""
     w = WORKLOADS[3]
     say = Say(capsys, "40-layer step")
     Fc = w.frames_per_chunk
@@ -119,7 +120,7 @@ def test_step_40_layers_cfg2_bf16_matches_oracle(gpu, capsys):
     xv, xa = draw_named(w, -1, "eps_video_2"), draw_named(w, -1, "eps_action_2")
     txt, img = draw_named(w, -1, "txt"), draw_named(w, -1, "img")
     say("gpu: uploading %d layers, condition build, 2 appends, step at t = %.4f" % (w.layers, t))
-    run = GpuRun(w, "bf16", gpu, 3, txt, img)
+    run = GpuRun(w, "bf16", gpu, 3, txt, img, packed=True)
     for c in range(2):
         run.append(x1v[c], x1a[c], c * Fc)
     assert run.cache.length == 2 * w.chunk_tokens
@@ -139,7 +140,7 @@ def test_step_40_layers_cfg2_bf16_matches_oracle(gpu, capsys):
 @pytest.mark.timeout(1500)
 def test_long_context_two_layers_decoupled_bf16_matches_oracle(gpu, capsys):
     """Three stitched views (1344 tokens per chunk), six committed chunks (8064 cached tokens), the
-    decoupled timesteps of bench.py's first long-context step, full width, 2 layers."""
+    decoupled timesteps of bench.py's first long-context step, full width, 2 layers, packed projections."""
     w = WORKLOADS[5].with_(layers=2)
     say = Say(capsys, "long context")
     Fc, C = w.frames_per_chunk, w.cache_chunks
@@ -149,7 +150,7 @@ def test_long_context_two_layers_decoupled_bf16_matches_oracle(gpu, capsys):
     xv, xa = draw_named(w, -1, "eps_video_%d" % C), draw_named(w, -1, "eps_action_%d" % C)
     txt, img = draw_named(w, -1, "txt"), draw_named(w, -1, "img")
     say("gpu: %d appends of %d tokens, step at t_v = %.4f, t_a = %.4f" % (C, w.chunk_tokens, tv, ta))
-    run = GpuRun(w, "bf16", gpu, C + 1, txt, img)
+    run = GpuRun(w, "bf16", gpu, C + 1, txt, img, packed=True)
     for c in range(C):
         run.append(x1v[c], x1a[c], c * Fc)
     assert run.cache.length == C * w.chunk_tokens == 8064
@@ -190,22 +191,23 @@ def block2():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_full_width_block(gpu, capsys, block2, dtype):
+@pytest.mark.parametrize("dtype,packed", [("bf16", False), ("f32", False), ("bf16", True)])
+def test_full_width_block(gpu, capsys, block2, dtype, packed):
     """One Wan-14B-sized block through the stack call (769 condition tokens, one cached chunk of 464
-    tokens, CFG batch 2) against the float32 oracle: 2e-2 in bf16, 1e-4 in the fp32 debug mode."""
+    tokens, CFG batch 2) against the float32 oracle: 2e-2 in bf16 (unpacked or packed projections),
+    1e-4 in the fp32 debug mode."""
     b = block2
     w, Fc = b["w"], b["w"].frames_per_chunk
-    say = Say(capsys, "full-width block " + dtype)
-    run = GpuRun(w, dtype, gpu, 2, b["txt"], b["img"])
+    say = Say(capsys, "full-width block %s%s" % (dtype, " packed" if packed else ""))
+    run = GpuRun(w, dtype, gpu, 2, b["txt"], b["img"], packed=packed)
     run.append(b["x1v"][0], b["x1a"][0], 0)
     gv, ga = run.step(b["xv1"], b["xa1"], [b["t"]], [b["t"]], Fc)
     _check_outputs(say, gv, ga, b["ref"][0], b["ref"][1], TOL[dtype])
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("branches", [2, 1])
-def test_block_fwd_full_width_bf16(gpu, capsys, block2, branches):
+@pytest.mark.parametrize("branches,packed", [(2, False), (1, False), (2, True)])
+def test_block_fwd_full_width_bf16(gpu, capsys, block2, branches, packed):
     """wam_dit_block_fwd at the full-width one-block shape (the entry point behind the one-block timing),
     with the embedded current chunk as residual stream and the modulation from wam_time_embed,
     committing its keys/values. One branch is the conditional branch of the CFG pair (the branches
@@ -213,8 +215,8 @@ def test_block_fwd_full_width_bf16(gpu, capsys, block2, branches):
     b = block2
     w = b["w"].with_(branches=branches)
     Fc, Lq, D = w.frames_per_chunk, w.chunk_tokens, w.dim
-    say = Say(capsys, "block_fwd full width br=%d" % branches)
-    run = GpuRun(w, "bf16", gpu, 2, b["txt"][:branches], b["img"])
+    say = Say(capsys, "block_fwd full width br=%d%s" % (branches, " packed" if packed else ""))
+    run = GpuRun(w, "bf16", gpu, 2, b["txt"][:branches], b["img"], packed=packed)
     run.append(b["x1v"][0], b["x1a"][0], 0)
     e6 = run.e6([b["t"]], [b["t"]])
     h = b["h"][:branches]

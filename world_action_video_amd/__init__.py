@@ -24,7 +24,7 @@ EXPORTS = ("wam_workspace_bytes", "wam_ctx_build", "wam_ctx_set_state", "wam_tim
            "wam_weights_for_embodiment", "wam_op_attention", "wam_kv_evict", "wam_kv_reset", "wam_last_error",
            "wam_qkv_timer_config", "wam_qkv_timer_read", "wam_op_attention_mx", "wam_flow_step_noalloc",
            "wam_denoise_chunk_replay", "wam_mfma_peak_probe", "wam_op_split_finish", "wam_op_modulated_norm",
-           "wam_op_qkv_cache")
+           "wam_op_qkv_cache", "wam_pack_weight", "wam_op_linear_packed", "wam_pack_block_bytes", "wam_pack_block")
 
 
 class WamError(RuntimeError):
@@ -52,7 +52,7 @@ GLOBAL_FIELDS = ("t_w1", "t_b1", "t_w2", "t_b2", "t_wp", "t_bp", "pe_w", "pe_b",
 
 class wam_block_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_FIELDS] + [("mx", ctypes.c_void_p)] + \
-               [(n, ctypes.c_void_p) for n in IMG_XATTN_FIELDS]
+               [(n, ctypes.c_void_p) for n in IMG_XATTN_FIELDS] + [("pk", ctypes.c_void_p)]
 
 
 class wam_action_io(ctypes.Structure):
@@ -123,6 +123,10 @@ def load(path: str = LIB_PATH):
         "wam_op_split_finish": (I, [P, I, I, I, P, P, P, P, I, P, I, I, I, F, P, P]),
         "wam_op_modulated_norm": (I, [P, I, I, P, P, I, I, I, F, P, P]),
         "wam_op_qkv_cache": (I, [P, I, I, I, I, I, I, P, P, F, P, P, P, P, I, I, P]),
+        "wam_pack_weight": (I, [P, I, I, I, P, P]),
+        "wam_op_linear_packed": (I, [P, I, P, P, P, I, I, I, I, I, P, S, P]),
+        "wam_pack_block_bytes": (S, [CFG]),
+        "wam_pack_block": (I, [CFG, ctypes.POINTER(wam_block_weights), P, S, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -315,6 +319,27 @@ def wam_mx_pack_block(cfg: wam_config, bw: wam_block_weights, dst, stream=None):
 
 def wam_mx4_quantize(dtype, src, ld, rows, cols, codes, ldq, scales, stream=None):
     _check(load().wam_mx4_quantize(dtype, _ptr(src), ld, rows, cols, _ptr(codes), ldq, _ptr(scales), _stream(stream)))
+
+
+def wam_pack_weight(W, ldw, N, K, dst, stream=None):
+    """Fragment-packed copy of the bf16 matrix W [N][ldw] into dst (N * K bf16)."""
+    _check(load().wam_pack_weight(_ptr(W), ldw, N, K, _ptr(dst), _stream(stream)))
+
+
+def wam_op_linear_packed(A, lda, Wp, bias, C, ldc, M, N, K, act=0, ws=None, stream=None):
+    """bf16 product with a fragment-packed weight (from wam_pack_weight)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().wam_op_linear_packed(_ptr(A), lda, _ptr(Wp), _ptr(bias), _ptr(C), ldc, M, N, K, act, _ptr(ws), nbytes,
+                                       _stream(stream)))
+
+
+def wam_pack_block_bytes(cfg: wam_config) -> int:
+    return int(load().wam_pack_block_bytes(ctypes.byref(cfg)))
+
+
+def wam_pack_block(cfg: wam_config, bw: wam_block_weights, dst, stream=None):
+    nbytes = dst.numel() * dst.element_size()
+    _check(load().wam_pack_block(ctypes.byref(cfg), ctypes.byref(bw), _ptr(dst), nbytes, _stream(stream)))
 
 
 def wam_op_linear_mx(A, A_scales, lda, W, W_scales, ldw, bias, C, ldc, M, N, K, act=0, ws=None, stream=None,

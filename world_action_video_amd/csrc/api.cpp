@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -102,6 +103,34 @@ MxBlock mx_block_of(const Geo& g) {
   return b;
 }
 
+// Fragment-packed projections of one layer (launch_pack_weight's layout): the six matrices back to
+// back in the order above, each N * K bf16 (a multiple of 4 KB, since N % 32 == 0 and K % 64 == 0).
+// A band of 32 rows occupies the bytes its rows would unpacked, so row offsets that are multiples of
+// 32 (the key / value rows of w_qkv) translate unchanged.
+struct PkBlock { size_t off[MX_MATS]; int N[MX_MATS], K[MX_MATS]; size_t total; };
+
+PkBlock pk_block_of(const Geo& g) {
+  PkBlock b{};
+  const int NK[MX_MATS][2] = {{3 * g.D, g.D}, {g.D, g.D}, {g.D, g.D}, {g.D, g.D}, {g.F1, g.D}, {g.D, g.F}};
+  size_t off = 0;
+  for (int i = 0; i < MX_MATS; ++i) {
+    b.N[i] = NK[i][0];
+    b.K[i] = NK[i][1];
+    b.off[i] = off;
+    off += (size_t)b.N[i] * b.K[i] * 2;
+  }
+  b.total = off;
+  return b;
+}
+
+// every packed matrix must stay below 2 GiB (32-bit buffer offsets)
+bool pk_fits(const Geo& g) {
+  const PkBlock b = pk_block_of(g);
+  for (int i = 0; i < MX_MATS; ++i)
+    if ((long)b.N[i] * b.K[i] * 2 >= (1L << 31)) return false;
+  return true;
+}
+
 wam_status check_cfg(const wam_config* c) {
   if (!c) return fail(WAM_E_ARG, "config is NULL");
   if (c->dtype != WAM_BF16 && c->dtype != WAM_F32) return fail(WAM_E_ARG, "unknown dtype %d", (int)c->dtype);
@@ -191,8 +220,15 @@ const char* const kBlockNames[] = {"mod", "w_qkv", "b_qkv", "g_q", "g_k", "w_o",
 
 bool unaligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; }
 
-wam_status check_block(const wam_block_weights* b, int l, bool mx, bool img_x) {
+// pk_used: the configuration reads fragment-packed projections when a block supplies them (bf16,
+// native precision); such a block's six unpacked projection matrices are then not read.
+// pk_fit: the configuration's projections can be packed (each below 2 GiB).
+wam_status check_block(const wam_block_weights* b, int l, bool mx, bool img_x, bool pk_used, bool pk_fit) {
   if (!b) return fail(WAM_E_ARG, "block weights of layer %d are NULL", l);
+  const bool packed = pk_used && b->pk;
+  if (packed && reinterpret_cast<uintptr_t>(b->pk) % 256)
+    return fail(WAM_E_ARG, "layer %d: the packed projections (pk) must be 256-byte aligned", l);
+  if (packed && !pk_fit) return fail(WAM_E_SHAPE, "layer %d: a projection is too large to pack (2 GiB)", l);
   if (img_x) {
     const void* q[5] = {b->w_cki, b->b_cki, b->g_cki, b->w_cvi, b->b_cvi};
     for (const void* x : q)
@@ -202,7 +238,13 @@ wam_status check_block(const wam_block_weights* b, int l, bool mx, bool img_x) {
   if (mx && (!b->mx || reinterpret_cast<uintptr_t>(b->mx) % 256))
     return fail(WAM_E_ARG, "layer %d: MXFP8 precision needs the packed projections (mx, 256-byte aligned)", l);
   const void* const* p = reinterpret_cast<const void* const*>(b);
+  auto replaced = [](const char* name) {   // a projection the packed copy stands in for
+    for (const char* m : {"w_qkv", "w_o", "w_cq", "w_co", "w_ff1", "w_ff2"})
+      if (!strcmp(name, m)) return true;
+    return false;
+  };
   for (int i = 0; i < (int)(sizeof(kBlockNames) / sizeof(kBlockNames[0])); ++i) {
+    if (packed && replaced(kBlockNames[i])) continue;
     if (!p[i]) return fail(WAM_E_ARG, "layer %d: %s is NULL", l, kBlockNames[i]);
     if (unaligned16(p[i])) return fail(WAM_E_ARG, "layer %d: %s is not 16-byte aligned", l, kBlockNames[i]);
   }
@@ -224,7 +266,8 @@ wam_status check_weights(const wam_config* c, const wam_weights* w, bool need_bl
     if (!w->blocks) return fail(WAM_E_ARG, "blocks array is NULL");
     for (int l = 0; l < c->layers; ++l) {
       wam_status st = check_block(&w->blocks[l], l, c->precision != WAM_PRECISION_NATIVE,
-                                  (c->variant & WAM_VARIANT_IMG_XATTN) != 0);
+                                  (c->variant & WAM_VARIANT_IMG_XATTN) != 0,
+                                  c->dtype == WAM_BF16 && c->precision == WAM_PRECISION_NATIVE, pk_fits(geo_of(*c)));
       if (st != WAM_OK) return st;
     }
   }
@@ -350,6 +393,14 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
   const float* mod = reinterpret_cast<const float*>(bw.mod);
   float* part = at<float>(p.ws, p.L.part);
   const long part_n = p.L.part_elems;
+  // fragment-packed projections (bf16, native precision): point the product at the packed copy
+  const bool packed = dt == DT_BF16 && !g.mx && bw.pk != nullptr;
+  const PkBlock pb = pk_block_of(g);
+  auto use_packed = [&](GemmArgs& ga, int mat, int row0) {
+    if (!packed) return;
+    ga.W = reinterpret_cast<const char*>(bw.pk) + pb.off[mat] + (size_t)row0 * pb.K[mat] * 2;
+    ga.w_packed = 1;
+  };
 
   // (1) y = LN(h) (1 + scale1) + shift1
   if (!pre_normed) HIP_TRY(launch_norm(adaln_args(p, mod, 0, 1), dt, p.s));
@@ -360,6 +411,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
                             reinterpret_cast<const float*>(bw.b_qkv) + col0, p.M, 3 * g.D - col0, g.D, part, part_n);
     ga.C = reinterpret_cast<char*>(qkv) + (size_t)col0 * g.esz;
     ga.ldc = 3 * g.D;
+    use_packed(ga, MX_QKV, col0);
     if (g.mx) HIP_TRY(mx_operands(p, bw, ga, y, MX_QKV, col0));
     QkvTimer& tm = g_qkv_timer;
     const bool timed = tm.layer == l && !kv_only && 2 * tm.n < (int)tm.ev.size();
@@ -405,6 +457,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     post.na = adaln_args(p, mod, 0, 1);
     post.na.mode = NORM_AFFINE; post.na.w = reinterpret_cast<const float*>(bw.ln3_w);
     post.na.b = reinterpret_cast<const float*>(bw.ln3_b);
+    use_packed(ga, MX_O, 0);
     if (g.mx) HIP_TRY(mx_operands(p, bw, ga, attn, MX_O, 0));
     HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID_GATED, post, p.s));
   }
@@ -417,6 +470,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     post.qa = qa;
     post.qa.src_ld = g.D; post.qa.src_col = 0; post.qa.gain = reinterpret_cast<const float*>(bw.g_cq); post.qa.rope = nullptr;
     post.qa.dst = qh; post.qa.dst_bh_stride = (long)p.R * g.d; post.qa.dst_row0 = 0;
+    use_packed(ga, MX_CQ, 0);
     if (g.mx) HIP_TRY(mx_operands(p, bw, ga, y, MX_CQ, 0));
     HIP_TRY(launch_gemm_post(ga, dt, EPI_STORE, post, p.s));
   }
@@ -451,6 +505,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     PostArgs post{};
     post.mode = POST_NORM;
     post.na = adaln_args(p, mod, 3, 4);
+    use_packed(ga, MX_CO, 0);
     if (g.mx) HIP_TRY(mx_operands(p, bw, ga, attn, MX_CO, 0));
     HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID, post, p.s));
   }
@@ -460,6 +515,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     const bool swiglu = (p.cfg->variant & WAM_VARIANT_SWIGLU) != 0;
     GemmArgs ga = gemm_args(y, g.D, bw.w_ff1, g.D, bw.b_ff1, p.M, swiglu ? 2 * g.F : g.F, g.D, part, part_n);
     ga.C = ffn; ga.ldc = g.F;
+    use_packed(ga, MX_FF1, 0);
     if (g.mx) HIP_TRY(mx_operands(p, bw, ga, y, MX_FF1, 0));
     HIP_TRY(launch_gemm(ga, dt, swiglu ? EPI_SWIGLU : EPI_GELU, p.s));
   }
@@ -468,6 +524,7 @@ wam_status run_block(const Pass& p, const wam_block_weights& bw, int l, bool kv_
     ga.H = p.h; ga.ldh = g.D; ga.rm = rm; ga.e6 = p.e6; ga.mod = mod; ga.gate_idx = 5; ga.D = g.D;
     PostArgs none{};
     none.mode = POST_NONE;
+    use_packed(ga, MX_FF2, 0);
     if (g.mx) HIP_TRY(mx_operands(p, bw, ga, ffn, MX_FF2, 0));
     HIP_TRY(launch_gemm_post(ga, dt, EPI_RESID_GATED, after ? *after : none, p.s));
   }
@@ -741,7 +798,7 @@ wam_status wam_dit_block_fwd(const wam_config* cfg, const wam_block_weights* bw,
   const Geo g = geo_of(*cfg);
   if (layer < 0 || layer >= g.L) return fail(WAM_E_ARG, "layer %d out of range", layer);
   if (n_chunks < 1 || n_chunks > kMaxChunks) return fail(WAM_E_SHAPE, "n_chunks must be in [1, %d]", kMaxChunks);
-  CHECK(check_block(bw, layer, g.mx, g.img_x));
+  CHECK(check_block(bw, layer, g.mx, g.img_x, g.dt == DT_BF16 && !g.mx, pk_fits(g)));
   CHECK(check_cache(g, cache, n_chunks * g.Lq));
   CHECK(check_ctx(g, ctx));
   if (!h || !e6) return fail(WAM_E_ARG, "h or e6 is NULL");
@@ -1236,6 +1293,66 @@ wam_status wam_mx_pack_block(const wam_config* cfg, const wam_block_weights* bw,
     else
       HIP_TRY(launch_mx_quantize(W[i], m.K, DT_BF16, m.N, m.K, codes, m.K, scales, s));
   }
+  return WAM_OK;
+}
+
+size_t wam_pack_block_bytes(const wam_config* cfg) {
+  if (check_cfg(cfg) != WAM_OK) return 0;
+  const Geo g = geo_of(*cfg);
+  if (g.dt != DT_BF16 || !pk_fits(g)) return 0;
+  return pk_block_of(g).total;
+}
+
+wam_status wam_pack_block(const wam_config* cfg, const wam_block_weights* bw, void* dst, size_t dst_bytes,
+                          void* stream) {
+  CHECK(check_cfg(cfg));
+  const Geo g = geo_of(*cfg);
+  if (g.dt != DT_BF16) return fail(WAM_E_UNSUPPORTED, "packed projections need dtype bf16");
+  if (!pk_fits(g)) return fail(WAM_E_SHAPE, "a projection is too large to pack (2 GiB)");
+  if (!bw) return fail(WAM_E_ARG, "block weights are NULL");
+  const PkBlock b = pk_block_of(g);
+  if (!dst || reinterpret_cast<uintptr_t>(dst) % 256) return fail(WAM_E_ARG, "dst must be a 256-byte aligned buffer");
+  if (dst_bytes < b.total) return fail(WAM_E_ARG, "dst holds %zu bytes, the packed layer needs %zu", dst_bytes, b.total);
+  const void* W[MX_MATS] = {bw->w_qkv, bw->w_o, bw->w_cq, bw->w_co, bw->w_ff1, bw->w_ff2};
+  const char* names[MX_MATS] = {"w_qkv", "w_o", "w_cq", "w_co", "w_ff1", "w_ff2"};
+  for (int i = 0; i < MX_MATS; ++i)
+    if (!W[i] || unaligned16(W[i])) return fail(WAM_E_ARG, "%s is NULL or not 16-byte aligned", names[i]);
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (int i = 0; i < MX_MATS; ++i)
+    HIP_TRY(launch_pack_weight(W[i], b.K[i], b.N[i], b.K[i], reinterpret_cast<char*>(dst) + b.off[i], s));
+  return WAM_OK;
+}
+
+wam_status wam_pack_weight(const void* W, int ldw, int N, int K, void* dst, void* stream) {
+  if (!W || !dst) return fail(WAM_E_ARG, "NULL operand");
+  if (unaligned16(W) || unaligned16(dst)) return fail(WAM_E_ARG, "W and dst must be 16-byte aligned");
+  if (N <= 0 || K <= 0 || N % 32 || K % 64) return fail(WAM_E_SHAPE, "N must be a multiple of 32 and K of 64");
+  if (ldw < K || ldw % 8) return fail(WAM_E_SHAPE, "ldw must be >= K and a multiple of 8");
+  if ((long)N * K * 2 >= (1L << 31)) return fail(WAM_E_SHAPE, "the packed matrix must stay below 2 GiB");
+  HIP_TRY(launch_pack_weight(W, ldw, N, K, dst, reinterpret_cast<hipStream_t>(stream)));
+  return WAM_OK;
+}
+
+wam_status wam_op_linear_packed(const void* A, int lda, const void* Wp, const float* bias, void* C, int ldc, int M,
+                                int N, int K, int act, void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !Wp || !C) return fail(WAM_E_ARG, "NULL operand");
+  if (M < 0 || N <= 0 || N % 32 || K <= 0 || K % 64) return fail(WAM_E_SHAPE, "N must be a multiple of 32 and K of 64");
+  if (lda < K || lda % 8 || ldc < (act == 2 ? N / 2 : N) || ldc % 4)
+    return fail(WAM_E_SHAPE, "lda must be >= K and a multiple of 8, ldc wide enough and a multiple of 4");
+  if (act < 0 || act > 2) return fail(WAM_E_ARG, "act must be 0, 1 or 2");
+  if (unaligned16(A) || unaligned16(Wp) || reinterpret_cast<uintptr_t>(C) % 8 || (bias && unaligned16(bias)))
+    return fail(WAM_E_ARG, "A, Wp and bias must be 16-byte aligned, C 8-byte aligned");
+  if ((long)M * lda * 2 >= (1L << 31) || (long)N * K * 2 >= (1L << 31))
+    return fail(WAM_E_SHAPE, "A and W must each stay below 2 GiB (32-bit buffer offsets): split the product");
+  if (ws && reinterpret_cast<uintptr_t>(ws) % 256) return fail(WAM_E_ARG, "workspace must be 256-byte aligned");
+  if (M == 0) return WAM_OK;
+  GemmArgs ga = gemm_args(A, lda, Wp, K, bias, M, N, K, ws ? reinterpret_cast<float*>(ws) : nullptr,
+                          ws ? (long)(ws_bytes / 4) : 0);
+  ga.C = C;
+  ga.ldc = ldc;
+  ga.w_packed = 1;
+  HIP_TRY(launch_gemm(ga, DT_BF16, act == 2 ? EPI_SWIGLU : act ? EPI_GELU : EPI_STORE,
+                      reinterpret_cast<hipStream_t>(stream)));
   return WAM_OK;
 }
 

@@ -458,6 +458,7 @@ gemm4_kernel(GemmArgs g, int splits) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) gload_q(2, 0, q);
   fload(0, 0, fa[0], fb[0]);
+  __builtin_amdgcn_sched_barrier(0);   // keep the prologue's loads ahead of the first tile's
 
   // One k-tile from LDS buffer CUR; register set CUR^1 holds tile kt+1 and is refilled with kt+3.
   // CUR is a compile-time constant so both register sets keep fixed registers.
@@ -529,12 +530,16 @@ gemm4_kernel(GemmArgs g, int splits) {
       }
     }
   };
-  int kt = 0;
+  // The first tile is peeled: the loop is then entered after an even tile both from before it and
+  // from its own end, so the wait counts the compiler derives for the loads in flight at its entry
+  // match the steady state (entered from the prologue, they would wait for tile 2's loads at once).
+  tile(0, std::integral_constant<int, 0>{});
+  int kt = 1;
   for (; kt + 1 < KT; kt += 2) {
-    tile(kt, std::integral_constant<int, 0>{});
-    tile(kt + 1, std::integral_constant<int, 1>{});
+    tile(kt, std::integral_constant<int, 1>{});
+    tile(kt + 1, std::integral_constant<int, 0>{});
   }
-  if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
+  if (kt < KT) tile(kt, std::integral_constant<int, 1>{});
 
   g4_epilogue_t<EPI, TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, sp, l32, half);
 }
@@ -625,6 +630,7 @@ gemm4w_kernel(GemmArgs g) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) gload_q(2, 0, q);
   fload(0, 0, fa[0], fb[0]);
+  __builtin_amdgcn_sched_barrier(0);   // keep the prologue's loads ahead of the first tile's
 
   auto mma = [&](int fc, int lo, int hi) {
 #pragma unroll
@@ -695,14 +701,222 @@ gemm4w_kernel(GemmArgs g) {
       }
     }
   };
-  int kt = 0;
+  // The first tile is peeled: the loop is then entered after an even tile both from before it and
+  // from its own end, so the wait counts the compiler derives for the loads in flight at its entry
+  // match the steady state (entered from the prologue, they would wait for tile 2's loads at once).
+  tile(0, std::integral_constant<int, 0>{});
+  int kt = 1;
   for (; kt + 1 < KT; kt += 2) {
-    tile(kt, std::integral_constant<int, 0>{});
-    tile(kt + 1, std::integral_constant<int, 1>{});
+    tile(kt, std::integral_constant<int, 1>{});
+    tile(kt + 1, std::integral_constant<int, 0>{});
   }
-  if (kt < KT) tile(kt, std::integral_constant<int, 0>{});
+  if (kt < KT) tile(kt, std::integral_constant<int, 1>{});
 
   g4_epilogue_t<EPI, TM, TN>(g, acc, m0 + wave * WM, n0, 0, l32, half);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Products with fragment-packed weights. W [N][K] is stored once, ahead of the products, in the
+// order the matrix instruction reads it: block (b, c) -- W rows 32 b .. 32 b + 31, k 16 c .. 16 c + 15
+// -- is 64 lanes x 16 bytes, lane l holding row 32 b + l % 32 at k 16 c + 8 (l / 32) .. + 7, and the
+// blocks of one 32-row band follow each other along k (so a band occupies the same 32 K * 2 bytes as
+// its rows do unpacked). One wave's load of a weight fragment is then one contiguous 1 KB read.
+//
+// gemm4p_kernel: a tile of 32 TM rows x 128 TN columns on 4 waves side by side along N; each wave
+// owns all 32 TM rows and 32 TN columns (TM x TN blocks of 32x32, v_mfma_f32_32x32x16_bf16, W block
+// first as in gemm4_kernel, so the epilogues are shared). Every weight fragment is used by exactly
+// one wave, which streams its own fragments from global memory straight into an 8-chunk register
+// ring (two k-tiles ahead); only the activation tile is staged through LDS (global -> two register
+// sets -> two LDS buffers, 144-byte padded rows, one barrier per k-tile). Per k16 chunk a CU then
+// reads 4 x TM activation fragments from LDS and writes TM / 4 units per thread, against 8 reads and
+// 4 writes per wave in gemm4_kernel: the LDS traffic that bounded that kernel drops by more than half,
+// while the weight stream goes through the vector memory path in whole 1 KB lines.
+// ------------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) pack_weight_kernel(const uint4* __restrict__ W, long ldw_units,
+                                                          uint4* __restrict__ Wp, int N, int K) {
+  const long total = (long)(N / 32) * (K / 16) * 64;
+  const int KC = K / 16;
+  for (long idx = (long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    const long blk = idx >> 6;
+    const int c = (int)(blk % KC), b = (int)(blk / KC);
+    Wp[idx] = W[(long)(b * 32 + (lane & 31)) * ldw_units + 2 * c + (lane >> 5)];
+  }
+}
+
+template <int EPI, int TM, int TN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm4p_kernel(GemmArgs g, int splits) {
+  constexpr int BM = 32 * TM, WN = 32 * TN, BN = 4 * WN;
+  constexpr int UNITS = 8, PITCH = UNITS + 1, BK = 64, CHUNKS = 4, RING = 8;
+  constexpr int PA = BM * UNITS / 256;   // activation units (16 bytes) per thread per k-tile
+  constexpr int NMF = TM * TN;           // MFMAs per wave per chunk
+  static_assert(PA == TM && RING == 2 * CHUNKS, "tile staging and ring layout");
+  __shared__ uint4 smem[2][BM * PITCH];
+
+  const int Mt = (g.M + BM - 1) / BM, Nt = (g.N + BN - 1) / BN;
+  const int items = Mt * Nt * splits;
+  const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+  const int per = items >> 3, rem = items & 7;
+  if (kx >= per + (xcd < rem ? 1 : 0)) return;
+  const int item = xcd * per + (xcd < rem ? xcd : rem) + kx;
+  const int mt = item % Mt, rest = item / Mt;
+  const int sp = rest % splits, nt = rest / splits;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KT_all = g.K / BK, KC = g.K / 16;
+  const int kb = (int)((long)sp * KT_all / splits), ke = (int)((long)(sp + 1) * KT_all / splits);
+  const int KT = ke - kb;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.A), (short)0,
+                                                                      (int)((long)g.M * g.lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g.W), (short)0,
+                                                                      (int)((long)g.N * g.K * 2), 0x00020000);
+  // activation unit i: row m0 + lrow + 32 i, 16-byte unit lunit of the k-tile; rows past M and weight
+  // bands past N lie outside the buffer ranges and read as zero
+  const int lrow = tid >> 3, lunit = tid & 7;
+  int aoff[PA];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) aoff[i] = (int)(((long)(m0 + lrow + 32 * i) * g.lda + lunit * 8) * 2);
+  const int sbase = lrow * PITCH + lunit;
+  const int band0 = (n0 + wave * WN) / 32;
+  int woff[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) woff[j] = ((band0 + j) * KC * 64 + lane) * 16;
+
+  uint4 rg[2][PA];       // activation register sets
+  uint4 fw[RING][TN];    // weight fragments of chunks c .. c + 7
+  uint4 fa[2][TM];       // activation fragments, double-buffered per chunk
+  auto gload_a = [&](int kt, int set, int c) {
+    const int koff = (kb + min(kt, KT - 1)) * BK * 2;   // prefetches past the split re-read its last tile
+#pragma unroll
+    for (int i = 0; i < PA; ++i)
+      if (i % CHUNKS == c)
+        rg[set][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i], koff, 0));
+  };
+  auto sstore_a = [&](int st, int set, int c) {
+#pragma unroll
+    for (int i = 0; i < PA; ++i)
+      if (i % CHUNKS == c) smem[st][i * 32 * PITCH + sbase] = rg[set][i];
+  };
+  auto wload = [&](int slot, int kc, int j) {   // kc: chunk of this split (clamped to its last)
+    const int koff = (4 * kb + min(kc, 4 * KT - 1)) * 1024;
+    fw[slot][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff[j], koff, 0));
+  };
+  auto fload = [&](int st, int c, uint4* f) {
+    const uint4* sa = smem[st] + l32 * PITCH + half;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f[i] = sa[i * 32 * PITCH + 2 * c];
+  };
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+
+  // Prologue, in the order the loop keeps loads in flight (activation tiles 0 and 1, ring chunks
+  // 0..3, activation tile 2, ring chunks 4..7), so that the waits the compiler derives at the loop's
+  // entry match those of its steady state.
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) gload_a(0, 0, c);
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) gload_a(1, 1, c);
+#pragma unroll
+  for (int s = 0; s < RING / 2; ++s)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) wload(s, s, j);
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) sstore_a(0, 0, c);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) gload_a(2, 0, c);
+#pragma unroll
+  for (int s = RING / 2; s < RING; ++s)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) wload(s, s, j);
+  fload(0, 0, fa[0]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto mma_col = [&](int fc, int slot, int j) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fw[slot][j]),
+                                                          __builtin_bit_cast(bf16x8_t, fa[fc][i]), acc[i][j], 0, 0, 0);
+  };
+  constexpr int SG_MFMA = 0x008, SG_VMEM_RD = 0x020, SG_DS_RD = 0x100, SG_DS_WR = 0x200;
+  constexpr int JB = (TN + 1) / 2;   // weight columns of the last chunk issued before the barrier
+  // One k-tile: LDS buffer CUR holds tile kt; register set CUR^1 holds tile kt+1 (written to LDS
+  // during this tile) and is refilled with kt+3; ring slots 4 CUR + c hold chunk 4 kt + c and are
+  // refilled with the chunk eight ahead once its column's MFMAs have read them. After each MFMA one
+  // memory instruction issues (the next chunk's fragment reads, the tile writes, then the loads).
+  auto tile = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value, nset = cur ^ 1;
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int fc = c & 1, slot = cur * CHUNKS + c, kc = kt * CHUNKS + c;
+      const int na = (PA - c + CHUNKS - 1) / CHUNKS;   // activation units of this chunk
+      if (c + 1 < CHUNKS) {
+        fload(cur, c + 1, fa[fc ^ 1]);
+        sstore_a(nset, nset, c);
+        gload_a(kt + 3, nset, c);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          mma_col(fc, slot, j);
+          wload(slot, kc + RING, j);
+        }
+#pragma unroll
+        for (int k = 0; k < NMF; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          if (k < TM) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+          else if (k < TM + na) __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+          else if (k < TM + 2 * na + TN) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        sstore_a(nset, nset, c);
+        gload_a(kt + 3, nset, c);
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+          mma_col(fc, slot, j);
+          wload(slot, kc + RING, j);
+        }
+#pragma unroll
+        for (int k = 0; k < TM * JB; ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          if (k < na) __builtin_amdgcn_sched_group_barrier(SG_DS_WR, 1, 0);
+          else if (k < 2 * na + JB) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fload(nset, 0, fa[fc ^ 1]);
+#pragma unroll
+        for (int j = JB; j < TN; ++j) {
+          mma_col(fc, slot, j);
+          wload(slot, kc + RING, j);
+        }
+#pragma unroll
+        for (int k = 0; k < TM * (TN - JB); ++k) {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          if (k < TM) __builtin_amdgcn_sched_group_barrier(SG_DS_RD, 1, 0);
+          else if (k < TM + TN - JB) __builtin_amdgcn_sched_group_barrier(SG_VMEM_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  // first tile peeled (the loop is entered after an even tile from both sides, as in gemm4_kernel)
+  tile(0, std::integral_constant<int, 0>{});
+  int kt = 1;
+  for (; kt + 1 < KT; kt += 2) {
+    tile(kt, std::integral_constant<int, 1>{});
+    tile(kt + 1, std::integral_constant<int, 0>{});
+  }
+  if (kt < KT) tile(kt, std::integral_constant<int, 1>{});
+
+  g4_epilogue_t<EPI, TM, TN>(g, acc, m0, n0 + wave * WN, sp, l32, half);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1026,16 +1240,18 @@ static void launch_g4(const GemmArgs& a, const G4Plan& p, hipStream_t s) {
 // (about 240 workgroups) with a finishing row kernel. splits == 0 when the shape does not suit the
 // kernel (the caller falls back to the 8-wave tiles).
 static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+// vector epilogues: runs of four columns, 16-byte aligned fp32 rows, 8-byte aligned bf16 rows
+static bool g4_vec_ok(const GemmArgs& a, Epi epi) {
+  return a.N % 4 == 0 && (!a.bias || aligned16(a.bias)) &&
+         (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_SWIGLU
+              ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
+              : (aligned16(a.H) && a.ldh % 4 == 0)) &&
+         (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
+}
 static G4Plan g4_plan(const GemmArgs& a, Epi epi) {
   G4Plan best;
   if (epi == EPI_ROWSEL_F32 || a.M < 256 || a.N < 256) return best;
-  // vector epilogues: runs of four columns, 16-byte aligned fp32 rows, 8-byte aligned bf16 rows
-  const bool vec_ok = a.N % 4 == 0 && (!a.bias || aligned16(a.bias)) &&
-                      (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_SWIGLU
-                           ? (reinterpret_cast<uintptr_t>(a.C) % 8 == 0 && a.ldc % 4 == 0)
-                                                           : (aligned16(a.H) && a.ldh % 4 == 0)) &&
-                      (epi != EPI_RESID_GATED || (aligned16(a.e6) && aligned16(a.mod) && a.D % 4 == 0));
-  if (!vec_ok) return best;
+  if (!g4_vec_ok(a, epi)) return best;
   const int KT = a.K / 64;
   long best_cost = 0;
   for (const bool t192 : {false, true}) {
@@ -1056,6 +1272,84 @@ static G4Plan g4_plan(const GemmArgs& a, Epi epi) {
     }
   }
   return best;
+}
+
+// Fragment-packed weights: 160 x 384 tiles (waves of 160 x 96) or 128 x 512 (waves of 128 x 128), the
+// one whose busiest CU has less work, split over K as in g4_plan when there are fewer than 128 tiles.
+// Every shape and every epilogue but the row gather runs here (a packed matrix has no unpacked copy
+// to fall back on): rows past M and columns past N are masked.
+struct G4pPlan {
+  int splits = 0;     // 0: not runnable (layout or alignment), 1: direct epilogue, else split-K
+  bool t160 = false;  // 160 x 384 tiles
+};
+static G4pPlan g4p_plan(const GemmArgs& a, Epi epi) {
+  G4pPlan best;
+  if (epi == EPI_ROWSEL_F32 || a.M <= 0 || a.N % 32 || a.K % 64 || a.K <= 0 || !aligned16(a.W) ||
+      (long)a.N * a.K * 2 >= (1L << 31) || (long)a.M * a.lda * 2 >= (1L << 31) || a.lda % 8 || !aligned16(a.A) ||
+      !g4_vec_ok(a, epi))
+    return best;
+  const int KT = a.K / 64;
+  long best_cost = 0;
+  for (const bool t160 : {false, true}) {
+    const int bm = t160 ? 160 : 128, bn = t160 ? 384 : 512;
+    const long tiles = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    int splits = 1;
+    if (tiles < 128 && a.part) {
+      splits = (int)((240 + tiles - 1) / tiles);
+      if (splits > 4) splits = 4;
+      while (splits > 1 && (KT < 4 * splits || (long)splits * a.M * a.N > a.part_elems)) --splits;
+    }
+    const long rounds = (tiles * splits + 255) / 256;
+    const long cost = rounds * bm * bn * ((KT + splits - 1) / splits);
+    if (best.splits == 0 || cost < best_cost) {
+      best.splits = splits;
+      best.t160 = t160;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <int EPI>
+static void launch_g4p(const GemmArgs& a, const G4pPlan& p, hipStream_t s) {
+  const int bm = p.t160 ? 160 : 128, bn = p.t160 ? 384 : 512;
+  const long items = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn) * p.splits;
+  const dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(256);
+  if (p.t160)
+    hipLaunchKernelGGL((gemm4p_kernel<EPI, 5, 3>), grid, block, 0, s, a, p.splits);
+  else
+    hipLaunchKernelGGL((gemm4p_kernel<EPI, 4, 4>), grid, block, 0, s, a, p.splits);
+}
+
+static void launch_reduce(const GemmArgs& a, Epi epi, int splits, hipStream_t s);
+
+static hipError_t launch_gemm_packed(const GemmArgs& a, Epi epi, hipStream_t s) {
+  const G4pPlan p = g4p_plan(a, epi);
+  if (p.splits == 0) return hipErrorInvalidValue;
+  if (p.splits > 1) {
+    launch_g4p<EPI_PARTIAL>(a, p, s);
+    launch_reduce(a, epi, p.splits, s);
+  } else {
+    switch (epi) {
+      case EPI_STORE: launch_g4p<EPI_STORE>(a, p, s); break;
+      case EPI_GELU: launch_g4p<EPI_GELU>(a, p, s); break;
+      case EPI_SWIGLU: launch_g4p<EPI_SWIGLU>(a, p, s); break;
+      case EPI_RESID: launch_g4p<EPI_RESID>(a, p, s); break;
+      case EPI_RESID_GATED: launch_g4p<EPI_RESID_GATED>(a, p, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weight(const void* W, long ldw, int N, int K, void* Wp, hipStream_t s) {
+  if (N <= 0 || K <= 0 || N % 32 || K % 64 || ldw < K || ldw % 8 || !aligned16(W) || !aligned16(Wp))
+    return hipErrorInvalidValue;
+  const long total = (long)(N / 32) * (K / 16) * 64;
+  const long blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(W), ldw / 8, reinterpret_cast<uint4*>(Wp), N, K);
+  return hipGetLastError();
 }
 
 static void launch_g4_direct(const GemmArgs& a, Epi epi, const G4Plan& p, hipStream_t s) {
@@ -1116,6 +1410,7 @@ static bool try_gemm4(const GemmArgs& a, Epi epi, hipStream_t s, hipError_t* err
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.w_packed) return dt == DT_BF16 && !a.As ? launch_gemm_packed(a, epi, s) : hipErrorInvalidValue;
   if (a.As) return dt == DT_BF16 ? launch_gemm_mx(a, epi, s) : hipErrorInvalidValue;   // MXFP8 operands
   if (epi == EPI_SWIGLU && a.N % 2) return hipErrorInvalidValue;   // (gate, up) column pairs
   // buffer descriptors address each operand with 32-bit byte offsets
@@ -1337,11 +1632,19 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
     fused = fused && epi == EPI_STORE && post.qa.rope == nullptr && post.qa.D == a.N && post.qa.M == a.M &&
             post.qa.d % 4 == 0 && aligned16(post.qa.gain) && reinterpret_cast<uintptr_t>(post.qa.dst) % 8 == 0;
   G4Plan p4;
-  if (fused && !a.As) p4 = g4_plan(a, epi);
-  const int plan = !fused ? 0 : a.As ? (mx_operands_ok(a) ? mx_splits(a) : 0) : p4.splits;
+  G4pPlan pp;
+  if (fused && !a.As) {
+    if (a.w_packed)
+      pp = g4p_plan(a, epi);
+    else
+      p4 = g4_plan(a, epi);
+  }
+  const int plan = !fused ? 0 : a.As ? (mx_operands_ok(a) ? mx_splits(a) : 0) : a.w_packed ? pp.splits : p4.splits;
   if (plan > 1) {
     if (a.As)
       launch_g4mx_partial(a, plan, s);
+    else if (a.w_packed)
+      launch_g4p<EPI_PARTIAL>(a, pp, s);
     else
       launch_g4<EPI_PARTIAL>(a, p4, s);
     return launch_split_finish(a, epi, post, plan, s);

@@ -41,9 +41,16 @@ struct GemmArgs {
   const uint8_t* As;         // MXFP8 operands only: e8m0 scales of A [M][K/32] and of W [N][K/32]
   const uint8_t* Ws;         //   (A and W then hold fp8 e4m3 codes, lda / ldw in bytes)
   int w_fp4;                 // MXFP8 operands only: W holds e2m1 nibbles (two k per byte, low first)
+  int w_packed;              // bf16 only: W holds the fragment-packed layout of launch_pack_weight (ldw
+                             //   unused; N % 32 == 0, K % 64 == 0, N * K * 2 < 2^31)
 };
 
 hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s);
+// Fragment-packed copy of a bf16 matrix W [N][K] (row stride ldw elements) for the products with
+// w_packed set: Wp holds N * K bf16 in blocks of 32 rows x 16 k, 64 lanes x 16 bytes each, lane l
+// holding row 32 b + l % 32 at k 16 c + 8 (l / 32) .. + 7, blocks of a row band consecutive along k.
+// N % 32 == 0, K % 64 == 0, ldw % 8 == 0, 16-byte aligned pointers.
+hipError_t launch_pack_weight(const void* W, long ldw, int N, int K, void* Wp, hipStream_t s);
 // MXFP8 product ([N569] real-time optimisations: quantised projections; the OCP microscaling format
 // that gfx950's scaled MFMA reads): A, W fp8 e4m3 with one power-of-two scale per 32 consecutive k,
 // fp32 accumulation, the same epilogues as the bf16 product (bf16 outputs). K % 128 == 0, N % 4 == 0.

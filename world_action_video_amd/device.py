@@ -15,8 +15,8 @@ import synth
 from synth.workloads import Workload, draw, global_tensors, is_matrix, layer_tensors
 
 from . import (GLOBAL_FIELDS, WAM_BF16, WAM_F32, wam_action_io, wam_block_weights, wam_config,
-               wam_ctx_kv, wam_kv_cache, wam_mx_block_bytes, wam_mx_pack_block, wam_weights, wam_weights_for_embodiment,
-               wam_workspace_bytes)
+               wam_ctx_kv, wam_kv_cache, wam_mx_block_bytes, wam_mx_pack_block, wam_pack_block, wam_pack_block_bytes,
+               wam_weights, wam_weights_for_embodiment, wam_workspace_bytes)
 
 
 def make_config(w: Workload, dtype: str = "bf16", branches: int | None = None) -> wam_config:
@@ -58,9 +58,16 @@ def _upload(w: Workload, layer: int, spec, dtype: str, device) -> torch.Tensor:
 class DeviceModel:
     """All weights of a workload on the GPU plus the ``wam_weights`` struct pointing at them."""
 
-    def __init__(self, w: Workload, dtype: str = "bf16", device="cuda:0", overrides=None):
+    PACKED_MATS = ("w_qkv", "w_o", "w_cq", "w_co", "w_ff1", "w_ff2")
+
+    def __init__(self, w: Workload, dtype: str = "bf16", device="cuda:0", overrides=None, packed=False):
+        """packed: give every block its fragment-packed projections (bf16, native precision) and drop the
+        unpacked copies of those six matrices, so only the packed ones can be read."""
         self.w, self.dtype, self.device = w, dtype, torch.device(device)
         self.cfg = make_config(w, dtype)
+        self.packed = bool(packed)
+        if self.packed and (dtype != "bf16" or self.cfg.precision != 0):
+            raise ValueError("packed projections need dtype bf16 and native precision")
         overrides = overrides or {}
         self.g = {}
         for spec in global_tensors(w):
@@ -102,6 +109,23 @@ class DeviceModel:
                 wam_mx_pack_block(self.cfg, self.blocks[l], arena)
                 self.blocks[l].mx = arena.data_ptr()
                 self.mx.append(buf)
+        self.pk = []
+        if self.packed:   # the library packs each layer's six projections once; the unpacked ones go
+            nbytes = wam_pack_block_bytes(self.cfg)
+            if nbytes == 0:
+                raise ValueError("configuration cannot take packed projections")
+            for l in range(self.w.layers):
+                buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+                off = (-buf.data_ptr()) % 256
+                arena = buf[off:off + nbytes]
+                wam_pack_block(self.cfg, self.blocks[l], arena)
+                self.blocks[l].pk = arena.data_ptr()
+                self.pk.append(buf)
+            torch.cuda.synchronize(self.device)
+            for l, lp in enumerate(self.layers):
+                for name in self.PACKED_MATS:
+                    del lp[name]
+                    setattr(self.blocks[l], name, None)
         self.weights = wam_weights()
         self.weights.blocks = ctypes.cast(self.blocks, ctypes.POINTER(wam_block_weights))
         for name in GLOBAL_FIELDS:
