@@ -246,7 +246,7 @@ gemm_kernel(GemmArgs g) {
 // partial products to g.part[split][M][N]; splitk_reduce_kernel sums them in split order (fixed,
 // deterministic) and applies the epilogue.
 // ------------------------------------------------------------------------------------------------
-static constexpr int EPI_PARTIAL = 16;   // internal: fp32 partial products of one split
+static constexpr int EPI_PARTIAL = 16;   // internal: partial products of one split (fp32, or bf16 with part_bf16)
 
 // Epilogue of the four-wave tiles (bf16 and MX operands alike): a wave's TM x TN blocks of 32 x 32 whose first row / column are wrow / wcol.
 template <int EPI, int TM, int TN>
@@ -260,7 +260,9 @@ __device__ __forceinline__ void g4_epilogue_t(const GemmArgs& g, const floatx16 
     return make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
   };
   if constexpr (EPI == EPI_PARTIAL) {
-    float* part = g.part + (long)sp * g.M * g.N;
+    const long base = (long)sp * g.M * g.N;
+    float* part = g.part + base;
+    bf16_t* part16 = reinterpret_cast<bf16_t*>(g.part) + base;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = mb + 32 * i;
@@ -270,7 +272,12 @@ __device__ __forceinline__ void g4_epilogue_t(const GemmArgs& g, const floatx16 
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int n = nb + 32 * j + 8 * gq;
-          if (n < g.N) *reinterpret_cast<float4*>(part + (long)m * g.N + n) = run(i, j, gq);
+          if (n >= g.N) continue;
+          const float4 v = run(i, j, gq);
+          if (g.part_bf16)
+            *reinterpret_cast<uint2*>(part16 + (long)m * g.N + n) = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+          else
+            *reinterpret_cast<float4*>(part + (long)m * g.N + n) = v;
         }
     }
     return;
@@ -1459,12 +1466,28 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
     const int q = t + 256 * k;
     v[k] = hv[k] = gv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (q >= nv) continue;
-    const float* pp = g.part + (long)m * g.N + 4 * q;
-    float4 a = *reinterpret_cast<const float4*>(pp);
+    float4 a;
+    if (g.part_bf16) {   // four bf16 partials per split: one 8-byte load each, widened exactly
+      const bf16_t* pp = reinterpret_cast<const bf16_t*>(g.part) + (long)m * g.N + 4 * q;
+      auto ld4 = [](const bf16_t* p) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+      };
+      a = ld4(pp);
 #pragma unroll
-    for (int sp = 1; sp < SPLITS; ++sp) {
-      const float4 b = *reinterpret_cast<const float4*>(pp + sp * pstride);
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      for (int sp = 1; sp < SPLITS; ++sp) {
+        const float4 b = ld4(pp + sp * pstride);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+    } else {
+      const float* pp = g.part + (long)m * g.N + 4 * q;
+      a = *reinterpret_cast<const float4*>(pp);
+#pragma unroll
+      for (int sp = 1; sp < SPLITS; ++sp) {
+        const float4 b = *reinterpret_cast<const float4*>(pp + sp * pstride);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
     }
     if (g.bias) {
       const float4 b = *reinterpret_cast<const float4*>(g.bias + 4 * q);
@@ -1641,13 +1664,18 @@ hipError_t launch_gemm_post(const GemmArgs& a, DType dt, Epi epi, const PostArgs
   }
   const int plan = !fused ? 0 : a.As ? (mx_operands_ok(a) ? mx_splits(a) : 0) : a.w_packed ? pp.splits : p4.splits;
   if (plan > 1) {
-    if (a.As)
-      launch_g4mx_partial(a, plan, s);
-    else if (a.w_packed)
-      launch_g4p<EPI_PARTIAL>(a, pp, s);
+    // The partials of this fused path are stored in bf16, each rounded once (about the single
+    // rounding a bf16 projection output gets), and summed in fp32 by the finish: half the bytes
+    // written at the product's end and read back by the finish.
+    GemmArgs b = a;
+    b.part_bf16 = 1;
+    if (b.As)
+      launch_g4mx_partial(b, plan, s);
+    else if (b.w_packed)
+      launch_g4p<EPI_PARTIAL>(b, pp, s);
     else
-      launch_g4<EPI_PARTIAL>(a, p4, s);
-    return launch_split_finish(a, epi, post, plan, s);
+      launch_g4<EPI_PARTIAL>(b, p4, s);
+    return launch_split_finish(b, epi, post, plan, s);
   }
   hipError_t e = launch_gemm(a, dt, epi, s);
   if (e != hipSuccess) return e;

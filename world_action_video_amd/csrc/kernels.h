@@ -36,11 +36,13 @@ struct GemmArgs {
   const float* mod;          // EPI_RESID_GATED: [6][D]
   int gate_idx, D;
   int sel_group;             // EPI_ROWSEL_F32: 0 = video rows, 1 = action rows
-  float* part;               // split-K scratch: [splits][M][N] fp32 partial products (nullptr: no split)
+  float* part;               // split-K scratch: [splits][M][N] partial products (nullptr: no split), fp32,
+                             //   or bf16 when part_bf16 is set (the block's fused split path)
   long part_elems;           // capacity of `part` in floats
   const uint8_t* As;         // MXFP8 operands only: e8m0 scales of A [M][K/32] and of W [N][K/32]
   const uint8_t* Ws;         //   (A and W then hold fp8 e4m3 codes, lda / ldw in bytes)
   int w_fp4;                 // MXFP8 operands only: W holds e2m1 nibbles (two k per byte, low first)
+  int part_bf16;             // split-K partials stored as bf16 (each rounded once), read back by the finish
   int w_packed;              // bf16 only: W holds the fragment-packed layout of launch_pack_weight (ldw
                              //   unused; N % 32 == 0, K % 64 == 0, N * K * 2 < 2^31)
 };
