@@ -1524,7 +1524,43 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
     v[k] = a;
   }
   if constexpr (POST == POST_NORM) {
+    // y = (v - mean) rstd mv + av with mv = 1 + scale (+ layer offset) and av = shift (+ offset), or
+    // mv = w, av = b (affine): both are loaded before the reductions, so their latency hides there
     const NormArgs& na = p.na;
+    float4 mv[G], av[G];
+    {
+      const float4 *sh = nullptr, *sc = nullptr, *sh2 = nullptr, *sc2 = nullptr;
+      if (na.mode != NORM_AFFINE) {
+        const int rb = m % na.rm.rows_per_branch;
+        const int ch = rb / na.rm.Lq, grp = (rb % na.rm.Lq) < na.rm.Lv ? 0 : 1;
+        if (na.mode == NORM_ADALN) {
+          const float* e6 = na.e6 + (long)(ch * 2 + grp) * 6 * na.D;
+          sh = reinterpret_cast<const float4*>(e6 + (long)na.shift_idx * na.D);
+          sc = reinterpret_cast<const float4*>(e6 + (long)na.scale_idx * na.D);
+          sh2 = reinterpret_cast<const float4*>(na.mod + (long)na.shift_idx * na.D);
+          sc2 = reinterpret_cast<const float4*>(na.mod + (long)na.scale_idx * na.D);
+        } else {
+          const float* e = na.e6 + (long)(ch * 2 + grp) * na.D;
+          sh = sc = reinterpret_cast<const float4*>(e);
+          sh2 = reinterpret_cast<const float4*>(na.mod);
+          sc2 = reinterpret_cast<const float4*>(na.mod + na.D);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int q = t + 256 * k;
+        mv[k] = av[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q >= nv) continue;
+        if (na.mode == NORM_AFFINE) {
+          mv[k] = reinterpret_cast<const float4*>(na.w)[q];
+          av[k] = reinterpret_cast<const float4*>(na.b)[q];
+        } else {
+          const float4 pa = sh[q], pb = sh2[q], ra = sc[q], rb2 = sc2[q];
+          mv[k] = make_float4(1.f + (ra.x + rb2.x), 1.f + (ra.y + rb2.y), 1.f + (ra.z + rb2.z), 1.f + (ra.w + rb2.w));
+          av[k] = make_float4(pa.x + pb.x, pa.y + pb.y, pa.z + pb.z, pa.w + pb.w);
+        }
+      }
+    }
     float s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < G; ++k) s1 += (v[k].x + v[k].y) + (v[k].z + v[k].w);
@@ -1537,39 +1573,20 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
       s2 += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
     }
     const float rstd = 1.f / sqrtf(block_sum<256>(s2, red) / (float)g.N + na.eps);
-    const float4 *sh = nullptr, *sc = nullptr, *sh2 = nullptr, *sc2 = nullptr;
-    if (na.mode != NORM_AFFINE) {
-      const int rb = m % na.rm.rows_per_branch;
-      const int ch = rb / na.rm.Lq, grp = (rb % na.rm.Lq) < na.rm.Lv ? 0 : 1;
-      if (na.mode == NORM_ADALN) {
-        const float* e6 = na.e6 + (long)(ch * 2 + grp) * 6 * na.D;
-        sh = reinterpret_cast<const float4*>(e6 + (long)na.shift_idx * na.D);
-        sc = reinterpret_cast<const float4*>(e6 + (long)na.scale_idx * na.D);
-        sh2 = reinterpret_cast<const float4*>(na.mod + (long)na.shift_idx * na.D);
-        sc2 = reinterpret_cast<const float4*>(na.mod + (long)na.scale_idx * na.D);
-      } else {
-        const float* e = na.e6 + (long)(ch * 2 + grp) * na.D;
-        sh = sc = reinterpret_cast<const float4*>(e);
-        sh2 = reinterpret_cast<const float4*>(na.mod);
-        sc2 = reinterpret_cast<const float4*>(na.mod + na.D);
-      }
-    }
     bf16_t* y = reinterpret_cast<bf16_t*>(na.Y) + (long)m * na.D;
+    auto modulate = [&](int k) {
+      const float4 o = make_float4((v[k].x - mean) * rstd, (v[k].y - mean) * rstd, (v[k].z - mean) * rstd,
+                                   (v[k].w - mean) * rstd);
+      return make_float4(o.x * mv[k].x + av[k].x, o.y * mv[k].y + av[k].y, o.z * mv[k].z + av[k].z,
+                         o.w * mv[k].w + av[k].w);
+    };
 #pragma unroll
     for (int k = 0; k < G; ++k) {
       const int q = t + 256 * k;
       if (na.mxq && 256 * k < nv) {   // MXFP8 copy of the stored (bf16-rounded) row; whole waves call it
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         if (q < nv) {
-          o = make_float4((v[k].x - mean) * rstd, (v[k].y - mean) * rstd, (v[k].z - mean) * rstd, (v[k].w - mean) * rstd);
-          if (na.mode == NORM_AFFINE) {
-            const float4 w = reinterpret_cast<const float4*>(na.w)[q], b = reinterpret_cast<const float4*>(na.b)[q];
-            o = make_float4(o.x * w.x + b.x, o.y * w.y + b.y, o.z * w.z + b.z, o.w * w.w + b.w);
-          } else {
-            const float4 pa = sh[q], pb = sh2[q], ra = sc[q], rb2 = sc2[q];
-            o = make_float4(o.x * (1.f + (ra.x + rb2.x)) + (pa.x + pb.x), o.y * (1.f + (ra.y + rb2.y)) + (pa.y + pb.y),
-                            o.z * (1.f + (ra.z + rb2.z)) + (pa.z + pb.z), o.w * (1.f + (ra.w + rb2.w)) + (pa.w + pb.w));
-          }
+          o = modulate(k);
           reinterpret_cast<uint2*>(y)[q] = make_uint2(pack2_bf16(o.x, o.y), pack2_bf16(o.z, o.w));
           o = make_float4(bf16_round(o.x), bf16_round(o.y), bf16_round(o.z), bf16_round(o.w));
         }
@@ -1577,19 +1594,17 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
         continue;
       }
       if (q >= nv) continue;
-      float4 o = make_float4((v[k].x - mean) * rstd, (v[k].y - mean) * rstd, (v[k].z - mean) * rstd, (v[k].w - mean) * rstd);
-      if (na.mode == NORM_AFFINE) {
-        const float4 w = reinterpret_cast<const float4*>(na.w)[q], b = reinterpret_cast<const float4*>(na.b)[q];
-        o = make_float4(o.x * w.x + b.x, o.y * w.y + b.y, o.z * w.z + b.z, o.w * w.w + b.w);
-      } else {
-        const float4 pa = sh[q], pb = sh2[q], ra = sc[q], rb2 = sc2[q];
-        o = make_float4(o.x * (1.f + (ra.x + rb2.x)) + (pa.x + pb.x), o.y * (1.f + (ra.y + rb2.y)) + (pa.y + pb.y),
-                        o.z * (1.f + (ra.z + rb2.z)) + (pa.z + pb.z), o.w * (1.f + (ra.w + rb2.w)) + (pa.w + pb.w));
-      }
+      const float4 o = modulate(k);
       reinterpret_cast<uint2*>(y)[q] = make_uint2(pack2_bf16(o.x, o.y), pack2_bf16(o.z, o.w));
     }
   } else {   // POST_QK
     const QkNormArgs& qa = p.qa;
+    float4 gn[G];   // the gain, loaded before the reduction
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int q = t + 256 * k;
+      gn[k] = q < nv ? *reinterpret_cast<const float4*>(qa.gain + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float s2 = 0.f;
 #pragma unroll
     for (int k = 0; k < G; ++k) s2 += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);
@@ -1601,10 +1616,9 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
       const int q = t + 256 * k;
       if (q >= nv) continue;
       const int c0 = 4 * q, hh = c0 / qa.d, j = c0 % qa.d;
-      const float4 gn = *reinterpret_cast<const float4*>(qa.gain + c0);
       bf16_t* o = dst + (long)(b * qa.H + hh) * qa.dst_bh_stride + (long)(qa.dst_row0 + rb) * qa.d + j;
-      *reinterpret_cast<uint2*>(o) = make_uint2(pack2_bf16(v[k].x * rstd * gn.x, v[k].y * rstd * gn.y),
-                                                pack2_bf16(v[k].z * rstd * gn.z, v[k].w * rstd * gn.w));
+      *reinterpret_cast<uint2*>(o) = make_uint2(pack2_bf16(v[k].x * rstd * gn[k].x, v[k].y * rstd * gn[k].y),
+                                                pack2_bf16(v[k].z * rstd * gn[k].z, v[k].w * rstd * gn[k].w));
     }
   }
 }
