@@ -751,6 +751,76 @@ __global__ void __launch_bounds__(256) pack_weight_kernel(const uint4* __restric
   }
 }
 
+// bf16 outputs of gemm4p_kernel (store, GELU, bf16 split-K partials) leave through LDS: each wave
+// writes one 32-row block row of its 32 TM x 32 TN tile into its own LDS rows (row-major, pitch
+// 32 TN + 8 bf16), then stores it with 16 bytes per lane, consecutive lanes along a row, so a store
+// instruction writes whole row segments instead of 16 bytes in each of 32 rows. When every workgroup
+// finishes at once (the split products), this halves the time the output takes to drain.
+// Whether a product takes this path depends on its arguments only, so all waves agree.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ bool g4p_staged_ok(const GemmArgs& g) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_GELU)
+    return g.ldc % 8 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0;
+  else if constexpr (EPI == EPI_PARTIAL)
+    return g.part_bf16 && g.N % 8 == 0;
+  else
+    return false;
+}
+
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void g4p_epilogue_staged(const GemmArgs& g, const floatx16 (&acc)[TM][TN], int m0, int wcol,
+                                                    int sp, int wave, int lane, bf16_t* lds) {
+  constexpr int WN = 32 * TN, SP = WN + 8, UPR = WN / 8;
+  const int l32 = lane & 31, half = lane >> 5;
+  bf16_t* stage = lds + wave * 32 * SP;
+  float4 bias[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int n = wcol + 32 * j + 8 * gq + 4 * half;
+      bias[j][gq] = (EPI != EPI_PARTIAL && g.bias && n < g.N) ? *reinterpret_cast<const float4*>(g.bias + n)
+                                                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  bf16_t* out;
+  long ld;
+  if constexpr (EPI == EPI_PARTIAL) {
+    out = reinterpret_cast<bf16_t*>(g.part) + (long)sp * g.M * g.N;
+    ld = g.N;
+  } else {
+    out = reinterpret_cast<bf16_t*>(g.C);
+    ld = g.ldc;
+  }
+  __syncthreads();   // every wave is done with the activation buffers the stage reuses
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float4 v = make_float4(acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+        const float4 b = bias[j][gq];
+        v.x += b.x; v.y += b.y; v.z += b.z; v.w += b.w;
+        if constexpr (EPI == EPI_GELU) {
+          v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
+        }
+        *reinterpret_cast<uint2*>(stage + l32 * SP + 32 * j + 8 * gq + 4 * half) =
+            make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+      }
+    // the wave reads back what its own lanes wrote: LDS operations of one wave complete in order
+#pragma unroll
+    for (int s = 0; s < (32 * UPR + 63) / 64; ++s) {
+      const int u = lane + 64 * s;
+      if (u < 32 * UPR) {
+        const int r = u / UPR, cu = u % UPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + r * SP + 8 * cu);
+        const int m = m0 + 32 * i + r, n = wcol + 8 * cu;
+        if (m < g.M && n < g.N) *reinterpret_cast<uint4*>(out + (long)m * ld + n) = v;
+      }
+    }
+  }
+}
+
 template <int EPI, int TM, int TN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm4p_kernel(GemmArgs g, int splits) {
@@ -923,7 +993,11 @@ gemm4p_kernel(GemmArgs g, int splits) {
   }
   if (kt < KT) tile(kt, std::integral_constant<int, 1>{});
 
-  g4_epilogue_t<EPI, TM, TN>(g, acc, m0, n0 + wave * WN, sp, l32, half);
+  static_assert(4 * 32 * (32 * TN + 8) * 2 <= (int)sizeof(smem), "the staged epilogue reuses the activation buffers");
+  if (g4p_staged_ok<EPI, TM, TN>(g))
+    g4p_epilogue_staged<EPI, TM, TN>(g, acc, m0, n0 + wave * WN, sp, wave, lane, reinterpret_cast<bf16_t*>(&smem[0][0]));
+  else
+    g4_epilogue_t<EPI, TM, TN>(g, acc, m0, n0 + wave * WN, sp, l32, half);
 }
 
 // ------------------------------------------------------------------------------------------------
