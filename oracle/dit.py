@@ -96,14 +96,16 @@ def project(w, x: Array, W: Array, b: Optional[Array] = None) -> Array:
     """A block projection y = x W^T + b. With MXFP8 precision (1; the low-precision projections of
     [N569] real-time optimisations; formats and block rule in ``oracle.mx``) the rows of x and of W
     are first quantised along the input features and the product is taken of the quantised values,
-    exactly (then cast back to the dtype of x); precision 2 quantises W to MXFP4 instead."""
+    exactly (then cast back to the dtype of x); precision 2 quantises W to MXFP4 instead.
+    Reading: the low-precision projections belong to the bf16 data type, whose activations are stored
+    as bf16 rows; the rows the quantiser reads are those bf16 values, so x is rounded to bf16 first."""
     prec = getattr(w, "precision", 0)
     if prec not in (1, 2):
         return linear(x, W, b)
-    from .mx import mx_linear, mx_quantize
+    from .mx import mx_linear, mx_quantize, round_bf16
     w_fmt = "e2m1" if prec == 2 else "e4m3"   # precision 2: MXFP4 weights, MXFP8 activations
     lead = x.shape[:-1]
-    xc, xs = mx_quantize(x.reshape(-1, x.shape[-1]).astype(np.float64))
+    xc, xs = mx_quantize(round_bf16(x.reshape(-1, x.shape[-1])).astype(np.float64))
     wc, ws = mx_quantize(W.astype(np.float64), fmt=w_fmt)
     y = mx_linear(xc, xs, wc, ws, None if b is None else b.astype(np.float64), w_fmt=w_fmt)
     return y.reshape(lead + (W.shape[0],)).astype(x.dtype)

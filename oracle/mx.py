@@ -26,6 +26,16 @@ Array = np.ndarray
 E4M3_MAX = 448.0
 
 
+def round_bf16(x: Array) -> Array:
+    """Nearest bfloat16 value of each finite element, in the dtype of x: bfloat16 keeps float32's sign
+    and 8 exponent bits and the top 7 of its 23 mantissa bits, so the float32 pattern is rounded on its
+    16 low bits, half to even (add 0x7fff plus the lowest kept bit, then clear the 16 low bits)."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(f.shape).astype(np.asarray(x).dtype)
+
+
 def e4m3_value(code: Array) -> Array:
     """Real value of e4m3 codes (no NaN codes expected)."""
     c = np.asarray(code, dtype=np.int64)

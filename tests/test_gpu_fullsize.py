@@ -205,6 +205,48 @@ def test_full_width_block(gpu, capsys, block2, dtype, packed):
     _check_outputs(say, gv, ga, b["ref"][0], b["ref"][1], TOL[dtype])
 
 
+# Full-width low-precision bound. At this width the MXFP8 block is ill-conditioned against changes
+# of its projection inputs at bf16's precision: one such change flips about 1.5% of the fp8 codes by
+# one step, and on the oracle alone rounding the six projection inputs to bf16 (at most 2^-9 relative)
+# moves this block's MXFP8 output by 4.7e-2 (video) / 5.8e-2 (action), against 6.4e-2 / 7.4e-2 for
+# the whole quantisation. The library's bf16 path perturbs every stored activation by as much, so the
+# bound is twice that sensitivity; and the output must lie closer to the quantised oracle than the
+# quantisation moves it (at most 0.85 of that distance), which a path that skipped or misplaced the
+# quantisation (ratio about 1 or more) fails.
+MX_FULL_TOL = 1e-1
+MX_FULL_RATIO = 0.85
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("precision", [synth.workloads.PRECISION_MXFP8, synth.workloads.PRECISION_MXFP4W])
+def test_full_width_block_low_precision(gpu, capsys, block2, precision):
+    """The one-block full-width workload with the six projections in MXFP8 (or MXFP4 weights): at
+    this width the K = 5120 / 13824 products split over K and their partials take the fused finish
+    (which also writes the quantised copy of the next projection's input), a path only full-width
+    shapes reach. Against the oracle with the same quantised projections."""
+    b = block2
+    w = b["w"].with_(precision=precision)
+    Fc = w.frames_per_chunk
+    say = Say(capsys, "full-width block precision %d" % precision)
+    run = GpuRun(w, "bf16", gpu, 2, b["txt"], b["img"])
+    run.append(b["x1v"][0], b["x1a"][0], 0)
+    gv, ga = run.step(b["xv1"], b["xa1"], [b["t"]], [b["t"]], Fc)
+    del run
+    torch.cuda.empty_cache()
+    m = O.load_model(w)
+    ctx = O.build_context(w, m.g, b["txt"], b["img"])
+    ckv = [O.context_kv(w, lp, ctx) for lp in m.layers]
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, b["x1v"][0], b["x1a"][0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, b["xv1"], b["xa1"], [b["t"]], [b["t"]], 1, Fc)
+    nat_v, nat_a = b["ref"]
+    qv, qa = rel_l2(ref_v, nat_v), rel_l2(ref_a, nat_a)
+    say("to the unquantised oracle: video %.3e action %.3e; oracle quantised to unquantised: video %.3e "
+        "action %.3e" % (rel_l2(gv, nat_v), rel_l2(ga, nat_a), qv, qa))
+    _check_outputs(say, gv, ga, ref_v, ref_a, MX_FULL_TOL)
+    assert rel_l2(gv, ref_v) <= MX_FULL_RATIO * qv and rel_l2(ga, ref_a) <= MX_FULL_RATIO * qa
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("branches,packed", [(2, False), (1, False), (2, True)])
 def test_block_fwd_full_width_bf16(gpu, capsys, block2, branches, packed):

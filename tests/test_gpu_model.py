@@ -183,10 +183,10 @@ def test_variant_stack_matches_oracle(gpu, tiny_oracle, dtype, variant):
 
 
 # MXFP8 projections against the oracle taking the same quantised projections. Both sides quantise
-# the same activations except that the library stores them in bf16 first: about 1% of the codes then
-# round to the neighbouring fp8 value (the bf16 half-ulp, 2^-9, against an fp8 spacing of 2^-4 to
-# 2^-3), a relative change near 1e-2 of each projection input; on top of the bf16 path's 2e-2.
-MX_TOL = 5e-2
+# the bf16 rows of the projection inputs (the oracle rounds its fp32 activations to bf16 first, as
+# the library stores them), so what remains is the bf16 path's own difference, whose bar is 2e-2; at
+# this width it flips few fp8 codes (measured 2.3e-3 / 6.2e-3 at most, video / action).
+MX_TOL = 2e-2
 
 
 @pytest.mark.parametrize("precision", [synth.workloads.PRECISION_MXFP8, synth.workloads.PRECISION_MXFP4W])

@@ -205,10 +205,42 @@ def test_projection_mxfp4_weights():
     rng = np.random.default_rng(6)
     x = rng.standard_normal((5, 64))
     W = rng.standard_normal((7, 64))
-    xc, xs = O.mx_quantize(x)
+    xc, xs = O.mx_quantize(O.round_bf16(x))   # the activations enter as their bf16 rows
     wc, ws = O.mx_quantize(W, fmt="e2m1")
     want = O.mx_dequantize(xc, xs) @ O.mx_dequantize(wc, ws, fmt="e2m1").T
     assert np.array_equal(O.project(W2, x, W, None), want)
+
+
+def test_projection_mx_reads_bf16_rows():
+    """The low-precision projection quantises the bf16 value of each activation: inputs that differ
+    only below bf16's precision give the same product, and the product equals the one of the rounded
+    input."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((6, 128)).astype(np.float32)
+    W = rng.standard_normal((9, 128)) * 0.05
+    xr = O.round_bf16(x)
+    nudge = (xr * np.float32(2.0 ** -12)).astype(np.float32)   # well inside half a bf16 step of xr
+    assert np.array_equal(O.round_bf16(xr + nudge), xr)
+    assert np.array_equal(O.project(_W, x, W, None), O.project(_W, xr, W, None))
+    assert np.array_equal(O.project(_W, xr + nudge, W, None), O.project(_W, xr, W, None))
+
+
+def test_round_bf16_is_round_to_nearest_even():
+    """Against the library conversion (torch, float32 -> bfloat16 -> float32, round to nearest even) on
+    random values over many binades, exact halfway patterns (ties go to the even neighbour) and signed
+    zeros and subnormals."""
+    import torch
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(4096) * np.exp2(rng.integers(-60, 60, 4096))).astype(np.float32)
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x40490000 | 0x8000, 0x00018000, 0x7F7F8000 - 0x10000],
+                    dtype=np.uint32).view(np.float32)
+    special = np.array([0.0, -0.0, 1e-40, -1e-40, 1.0, -3.5], dtype=np.float32)
+    for v in (x, ties, special):
+        want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+        assert np.array_equal(O.round_bf16(v).view(np.uint32), want.view(np.uint32))
+    # the halfway cases land on the even neighbour: 1 + 2^-8 -> 1, (1 + 2^-7) + 2^-8 -> 1 + 2^-6
+    assert O.round_bf16(np.float32(1 + 2.0 ** -8)) == np.float32(1.0)
+    assert O.round_bf16(np.float32(1 + 2.0 ** -7 + 2.0 ** -8)) == np.float32(1 + 2.0 ** -6)
 
 
 # ---- MXFP8 attention (probabilities quantised in blocks of 32 keys) ----------------------------------
