@@ -1520,6 +1520,13 @@ hipError_t launch_gemm(const GemmArgs& a, DType dt, Epi epi, hipStream_t s) {
 // (POST_QK). Row statistics are block reductions in a fixed order (deterministic).
 // ------------------------------------------------------------------------------------------------
 constexpr int FIN_G = 8;   // float4 groups per thread (template G <= FIN_G): rows of up to 8192 columns
+// Stands in for a missing bias, so that the finish adds a bias unconditionally (no branch between
+// its loads).
+__device__ float fin_zero_row[FIN_G * 1024];
+
+__device__ __forceinline__ float4 keep_if(bool c, float4 a) {   // component selects, never a memory select
+  return make_float4(c ? a.x : 0.f, c ? a.y : 0.f, c ? a.z : 0.f, c ? a.w : 0.f);
+}
 
 template <int EPI, int POST, int SPLITS, int G>
 __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs p) {
@@ -1527,54 +1534,68 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
   const int m = blockIdx.x, t = threadIdx.x;
   const int nv = g.N / 4;
   const long pstride = (long)g.M * g.N;
-  // all loads of the row first (partials, residual, gate), then the arithmetic and the stores
+  // Every load of the row (partials, bias, residual, gate) is issued before any arithmetic, with no
+  // control flow between them, so their latencies overlap: lanes past the row's end read its last quad
+  // (the values are dropped), and a missing bias is read from a valid address and selected away.
   float4 v[G], hv[G], gv[G];
+  int qc[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) qc[k] = min(t + 256 * k, nv - 1);
+  const float* bsrc = g.bias ? g.bias : fin_zero_row;
   const float* grow = nullptr;
   if constexpr (EPI == EPI_RESID_GATED) {
     const int rb = m % g.rm.rows_per_branch;
     const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
     grow = g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D;
   }
+  auto load_all = [&](auto bf16_parts) {
+    constexpr bool PB = decltype(bf16_parts)::value;
+    using Raw = std::conditional_t<PB, uint2, float4>;
+    const Raw* pp = reinterpret_cast<const Raw*>(g.part) + (long)m * nv;   // one quad per element
+    const long qstride = pstride / 4;                                        // quads per split
+    Raw raw[G][SPLITS];
+    float4 bv[G], ge[G], gm[G];
 #pragma unroll
-  for (int k = 0; k < G; ++k) {
-    const int q = t + 256 * k;
-    v[k] = hv[k] = gv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (q >= nv) continue;
-    float4 a;
-    if (g.part_bf16) {   // four bf16 partials per split: one 8-byte load each, widened exactly
-      const bf16_t* pp = reinterpret_cast<const bf16_t*>(g.part) + (long)m * g.N + 4 * q;
-      auto ld4 = [](const bf16_t* p) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p);
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-      };
-      a = ld4(pp);
+    for (int k = 0; k < G; ++k) {
 #pragma unroll
-      for (int sp = 1; sp < SPLITS; ++sp) {
-        const float4 b = ld4(pp + sp * pstride);
-        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-      }
-    } else {
-      const float* pp = g.part + (long)m * g.N + 4 * q;
-      a = *reinterpret_cast<const float4*>(pp);
-#pragma unroll
-      for (int sp = 1; sp < SPLITS; ++sp) {
-        const float4 b = *reinterpret_cast<const float4*>(pp + sp * pstride);
-        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      for (int sp = 0; sp < SPLITS; ++sp) raw[k][sp] = pp[sp * qstride + qc[k]];
+      bv[k] = reinterpret_cast<const float4*>(bsrc)[qc[k]];
+      if constexpr (EPI != EPI_STORE) hv[k] = reinterpret_cast<const float4*>(g.H + (long)m * g.ldh)[qc[k]];
+      if constexpr (EPI == EPI_RESID_GATED) {
+        ge[k] = reinterpret_cast<const float4*>(grow)[qc[k]];
+        gm[k] = reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D)[qc[k]];
       }
     }
-    if (g.bias) {
-      const float4 b = *reinterpret_cast<const float4*>(g.bias + 4 * q);
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    auto widen = [](const Raw& r) {
+      if constexpr (PB)   // four bf16 values, widened exactly
+        return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                           __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+      else
+        return r;
+    };
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      float4 a = widen(raw[k][0]);   // partials summed in split order
+#pragma unroll
+      for (int sp = 1; sp < SPLITS; ++sp) {
+        const float4 b = widen(raw[k][sp]);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      a.x += bv[k].x; a.y += bv[k].y; a.z += bv[k].z; a.w += bv[k].w;
+      const bool in = t + 256 * k < nv;
+      v[k] = keep_if(in, a);
+      if constexpr (EPI != EPI_STORE) hv[k] = keep_if(in, hv[k]);
+      else hv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (EPI == EPI_RESID_GATED)
+        gv[k] = keep_if(in, make_float4(ge[k].x + gm[k].x, ge[k].y + gm[k].y, ge[k].z + gm[k].z, ge[k].w + gm[k].w));
+      else
+        gv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    v[k] = a;
-    if constexpr (EPI != EPI_STORE) hv[k] = *reinterpret_cast<const float4*>(g.H + (long)m * g.ldh + 4 * q);
-    if constexpr (EPI == EPI_RESID_GATED) {
-      const float4 ge = *reinterpret_cast<const float4*>(grow + 4 * q);
-      const float4 gm = *reinterpret_cast<const float4*>(g.mod + (long)g.gate_idx * g.D + 4 * q);
-      gv[k] = make_float4(ge.x + gm.x, ge.y + gm.y, ge.z + gm.z, ge.w + gm.w);
-    }
-  }
+  };
+  if (g.part_bf16)
+    load_all(std::true_type{});
+  else
+    load_all(std::false_type{});
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     const int q = t + 256 * k;
@@ -1620,18 +1641,23 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
           sc2 = reinterpret_cast<const float4*>(na.mod + na.D);
         }
       }
+      if (na.mode == NORM_AFFINE) {
 #pragma unroll
-      for (int k = 0; k < G; ++k) {
-        const int q = t + 256 * k;
-        mv[k] = av[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (q >= nv) continue;
-        if (na.mode == NORM_AFFINE) {
-          mv[k] = reinterpret_cast<const float4*>(na.w)[q];
-          av[k] = reinterpret_cast<const float4*>(na.b)[q];
-        } else {
-          const float4 pa = sh[q], pb = sh2[q], ra = sc[q], rb2 = sc2[q];
-          mv[k] = make_float4(1.f + (ra.x + rb2.x), 1.f + (ra.y + rb2.y), 1.f + (ra.z + rb2.z), 1.f + (ra.w + rb2.w));
-          av[k] = make_float4(pa.x + pb.x, pa.y + pb.y, pa.z + pb.z, pa.w + pb.w);
+        for (int k = 0; k < G; ++k) {
+          mv[k] = reinterpret_cast<const float4*>(na.w)[qc[k]];
+          av[k] = reinterpret_cast<const float4*>(na.b)[qc[k]];
+        }
+      } else {
+        float4 pa[G], pb[G], ra[G], rb2[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          pa[k] = sh[qc[k]]; pb[k] = sh2[qc[k]]; ra[k] = sc[qc[k]]; rb2[k] = sc2[qc[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          mv[k] = make_float4(1.f + (ra[k].x + rb2[k].x), 1.f + (ra[k].y + rb2[k].y), 1.f + (ra[k].z + rb2[k].z),
+                              1.f + (ra[k].w + rb2[k].w));
+          av[k] = make_float4(pa[k].x + pb[k].x, pa[k].y + pb[k].y, pa[k].z + pb[k].z, pa[k].w + pb[k].w);
         }
       }
     }
@@ -1675,10 +1701,7 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
     const QkNormArgs& qa = p.qa;
     float4 gn[G];   // the gain, loaded before the reduction
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const int q = t + 256 * k;
-      gn[k] = q < nv ? *reinterpret_cast<const float4*>(qa.gain + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int k = 0; k < G; ++k) gn[k] = reinterpret_cast<const float4*>(qa.gain)[qc[k]];   // lanes past the end store nothing
     float s2 = 0.f;
 #pragma unroll
     for (int k = 0; k < G; ++k) s2 += (v[k].x * v[k].x + v[k].y * v[k].y) + (v[k].z * v[k].z + v[k].w * v[k].w);

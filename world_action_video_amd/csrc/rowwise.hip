@@ -164,20 +164,43 @@ hipError_t launch_norm(const NormArgs& a, DType dt, hipStream_t s) {
 // ------------------------------------------------------------------------------------------------
 // q/k RMSNorm over the full width + rotary embedding of video rows + scatter to head-major rows.
 // One wave per row; each lane owns groups of 8 consecutive channels (16-byte loads and stores; a
-// group never straddles a head since the head dim is a multiple of 8). The gain and the rotation are
-// linear, so they are applied to the raw row while the sum of squares is still being reduced:
-// y = rstd * R(x * g). Every load of the row (values, gain, rotation table) is then issued in one
-// round trip, and only the final scaling waits for the reduction.
+// group never straddles a head since the head dim is a multiple of 8). The row's values are loaded in
+// one batch with no control flow between the loads (lanes past the row's end read its last group and
+// drop it); the workgroup meanwhile copies the gain into LDS (`stage`), so one memory round trip
+// precedes the sum of squares. The output is rstd * R(x * g): gain, rotation, then the row scale.
 // ------------------------------------------------------------------------------------------------
+template <int GPL>
+struct GainLds {   // the gain of a width of up to 512 GPL channels, copied once per workgroup
+  float4 v[GPL * 128];
+  static_assert(GPL * 128 % 256 == 0, "whole rounds of the 256 threads");
+  static constexpr int GS = GPL * 128 / 256;   // quads per thread
+};
+
+// `valid` false: the wave only takes part in the workgroup's staging (its loads read the last row).
 template <typename T, int GPL>
-__device__ __forceinline__ void qk_row(const QkNormArgs& a, int row, int lane) {
+__device__ __forceinline__ void qk_row(const QkNormArgs& a, int row, bool valid, int lane, GainLds<GPL>& gl) {
   constexpr int EPU = 16 / sizeof(T);            // elements per 16-byte unit
   constexpr int UPG = 8 / EPU;                   // units per group of 8 channels
+  if (!valid) row = a.M - 1;
+  // The gain's loads go out first (clamped to its end: the copies past the width are never read, and
+  // no branch separates the loads), the row's right behind them.
+  constexpr int GS = GainLds<GPL>::GS;
+  float4 gt[GS];
+#pragma unroll
+  for (int j = 0; j < GS; ++j)
+    gt[j] = reinterpret_cast<const float4*>(a.gain)[min((int)threadIdx.x + 256 * j, a.D / 4 - 1)];
   const T* src = reinterpret_cast<const T*>(a.src) + (long)row * a.src_ld + a.src_col;
   const int ng = a.D / 8;
   const int b = row / a.rows_per_branch, rb = row % a.rows_per_branch;
   const bool rotate = a.rope && (rb % a.rm.Lq) < a.rm.Lv;   // video rows only
   const int half_d = a.d / 2;
+  uint4 u[GPL][UPG];
+#pragma unroll
+  for (int k = 0; k < GPL; ++k) {
+    const int ch0 = min(lane + 64 * k, ng - 1) * 8;
+#pragma unroll
+    for (int q = 0; q < UPG; ++q) u[k][q] = reinterpret_cast<const uint4*>(src + ch0)[q];
+  }
   // A lane's groups are 512 channels apart: when d divides 512 they sit at the same offset inside
   // their heads and share one set of rotary entries, loaded once.
   const bool one_cs = rotate && 512 % a.d == 0;
@@ -187,62 +210,71 @@ __device__ __forceinline__ void qk_row(const QkNormArgs& a, int row, int lane) {
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) cs_lane[pp] = cs[pp];
   }
-  float y[GPL][8];
+#pragma unroll
+  for (int j = 0; j < GS; ++j) gl.v[threadIdx.x + 256 * j] = gt[j];
+  __syncthreads();
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < GPL; ++k) {
-    const int gi = lane + 64 * k;
-    if (gi >= ng) continue;
-    const int ch0 = gi * 8;
-    uint4 u[UPG];
-#pragma unroll
-    for (int q = 0; q < UPG; ++q) u[q] = reinterpret_cast<const uint4*>(src + ch0)[q];
-    const float4 g0 = reinterpret_cast<const float4*>(a.gain + ch0)[0], g1 = reinterpret_cast<const float4*>(a.gain + ch0)[1];
-    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const T* e = reinterpret_cast<const T*>(u);
+    const bool in = lane + 64 * k < ng;
+    const T* e = reinterpret_cast<const T*>(u[k]);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float x = Elem<T>::to_f(e[c]);
-      ss += x * x;
-      y[k][c] = x * g[c];
-    }
-    if (rotate) {
-      const float2* cs = a.rope + (long)rb * half_d + (ch0 % a.d) / 2;
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const float2 t = one_cs ? cs_lane[pp] : cs[pp];
-        const float r0 = y[k][2 * pp] * t.x - y[k][2 * pp + 1] * t.y;
-        const float r1 = y[k][2 * pp] * t.y + y[k][2 * pp + 1] * t.x;
-        y[k][2 * pp] = r0;
-        y[k][2 * pp + 1] = r1;
-      }
+      ss += in ? x * x : 0.f;
     }
   }
   const float rstd = 1.f / sqrtf(wave_sum(ss) / (float)a.D + a.eps);
+  if (!valid) return;
   T* dst = reinterpret_cast<T*>(a.dst);
+  // cs(k, ch0, pp): rotary entry pp of group k (the lane's shared set, or loaded per group), so the
+  // two cases run as separate loops and the shared case waits on no load.
+  auto emit = [&](auto cs) {
 #pragma unroll
-  for (int k = 0; k < GPL; ++k) {
-    const int gi = lane + 64 * k;
-    if (gi >= ng) continue;
-    const int ch0 = gi * 8, hh = ch0 / a.d;
-    T* o = dst + ((long)b * a.H + hh) * a.dst_bh_stride + (long)(a.dst_row0 + rb) * a.d + ch0 % a.d;
-    float v[8];
+    for (int k = 0; k < GPL; ++k) {
+      const int gi = lane + 64 * k;
+      if (gi >= ng) continue;
+      const int ch0 = gi * 8, hh = ch0 / a.d;
+      const float4 g0 = gl.v[ch0 / 4], g1 = gl.v[ch0 / 4 + 1];
+      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const T* e = reinterpret_cast<const T*>(u[k]);
+      float y[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = y[k][c] * rstd;
-    if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<uint4*>(o) = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]),
-                                                pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
-    } else {
-      reinterpret_cast<float4*>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
-      reinterpret_cast<float4*>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+      for (int c = 0; c < 8; ++c) y[c] = Elem<T>::to_f(e[c]) * g[c];
+      if (rotate) {
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const float2 t = cs(ch0, pp);
+          const float r0 = y[2 * pp] * t.x - y[2 * pp + 1] * t.y;
+          const float r1 = y[2 * pp] * t.y + y[2 * pp + 1] * t.x;
+          y[2 * pp] = r0;
+          y[2 * pp + 1] = r1;
+        }
+      }
+      T* o = dst + ((long)b * a.H + hh) * a.dst_bh_stride + (long)(a.dst_row0 + rb) * a.d + ch0 % a.d;
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = y[c] * rstd;
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint4*>(o) = make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]),
+                                                  pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
+      } else {
+        reinterpret_cast<float4*>(o)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4*>(o)[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
     }
-  }
+  };
+  if (one_cs || !rotate)
+    emit([&](int, int pp) { return cs_lane[pp]; });
+  else
+    emit([&](int ch0, int pp) { return a.rope[(long)rb * half_d + (ch0 % a.d) / 2 + pp]; });
 }
 
 template <typename T, int GPL>
 __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkNormArgs a) {
+  __shared__ GainLds<GPL> gl;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row < a.M) qk_row<T, GPL>(a, row, threadIdx.x & 63);
+  qk_row<T, GPL>(a, row, row < a.M, threadIdx.x & 63, gl);
 }
 
 template <typename T>
@@ -326,17 +358,18 @@ __device__ __forceinline__ void v_block_bf16(const VCacheArgs& a, int blk) {
 
 template <int GPL, int D>
 __global__ void __launch_bounds__(256) qkv_cache_kernel(QkNormArgs q, QkNormArgs k, VCacheArgs v, int nq_blk, int nk_blk) {
+  __shared__ GainLds<GPL> gl;
   int blk = blockIdx.x;
   const int row4 = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (blk < nk_blk) {
     const int row = blk * 4 + row4;
-    if (row < k.M) qk_row<bf16_t, GPL>(k, row, lane);
+    qk_row<bf16_t, GPL>(k, row, row < k.M, lane, gl);
     return;
   }
   blk -= nk_blk;
   if (blk < nq_blk) {
     const int row = blk * 4 + row4;
-    if (row < q.M) qk_row<bf16_t, GPL>(q, row, lane);
+    qk_row<bf16_t, GPL>(q, row, row < q.M, lane, gl);
     return;
   }
   v_block_bf16<D>(v, blk - nq_blk);
