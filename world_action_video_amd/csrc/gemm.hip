@@ -248,6 +248,33 @@ gemm_kernel(GemmArgs g) {
 // ------------------------------------------------------------------------------------------------
 static constexpr int EPI_PARTIAL = 16;   // internal: partial products of one split (fp32, or bf16 with part_bf16)
 
+// Accumulators of a 32 TM x 32 TN wave tile in the transposed layout the epilogue reads (lane
+// (l32, half) holds columns wcol + 4 half + 32 j + 8 g + 0..3 of block (i, j) in acc[i][j][4 g ..]).
+// They start at zero, except for split 0 of a product whose partials are stored in bf16: those start
+// at the bias, so the stored partial carries it and the finish adds none.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void g4_acc_init(floatx16 (&acc)[TM][TN], const GemmArgs& g, int sp, int wcol, int half) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+  if constexpr (EPI == EPI_PARTIAL) {
+    if (g.part_bf16 && sp == 0 && g.bias) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = wcol + 4 * half + 32 * j + 8 * gq;
+          const float4 b = n < g.N ? *reinterpret_cast<const float4*>(g.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            acc[i][j][4 * gq] = b.x; acc[i][j][4 * gq + 1] = b.y; acc[i][j][4 * gq + 2] = b.z; acc[i][j][4 * gq + 3] = b.w;
+          }
+        }
+    }
+  }
+}
+
 // Epilogue of the four-wave tiles (bf16 and MX operands alike): a wave's TM x TN blocks of 32 x 32 whose first row / column are wrow / wcol.
 template <int EPI, int TM, int TN>
 __device__ __forceinline__ void g4_epilogue_t(const GemmArgs& g, const floatx16 (&acc)[TM][TN], int wrow, int wcol,
@@ -445,10 +472,7 @@ gemm4_kernel(GemmArgs g, int splits) {
   };
 
   floatx16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+  g4_acc_init<EPI, TM, TN>(acc, g, sp, n0 + wn * WN, half);
 
   // The loop body has no data-dependent branches: loads past the split's last k-tile read other
   // valid rows or fall outside the buffer range (returning zero), and stores/fragment loads into the
@@ -889,10 +913,7 @@ gemm4p_kernel(GemmArgs g, int splits) {
   };
 
   floatx16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+  g4_acc_init<EPI, TM, TN>(acc, g, sp, n0 + wave * WN, half);
 
   // Prologue, in the order the loop keeps loads in flight (activation tiles 0 and 1, ring chunks
   // 0..3, activation tile 2, ring chunks 4..7), so that the waits the compiler derives at the loop's
@@ -1128,10 +1149,7 @@ gemm4mx_kernel(GemmArgs g, int splits) {
   };
 
   floatx16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+  g4_acc_init<EPI, TM, TN>(acc, g, sp, n0 + wn * WN, half);
 
 #pragma unroll
   for (int q = 0; q < 4; ++q) gload_q(0, q);
@@ -1528,7 +1546,7 @@ __device__ __forceinline__ float4 keep_if(bool c, float4 a) {   // component sel
   return make_float4(c ? a.x : 0.f, c ? a.y : 0.f, c ? a.z : 0.f, c ? a.w : 0.f);
 }
 
-template <int EPI, int POST, int SPLITS, int G>
+template <int EPI, int POST, int SPLITS, int G, bool PB>   // PB: bf16 partials (else fp32)
 __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs p) {
   __shared__ float red[4];
   const int m = blockIdx.x, t = threadIdx.x;
@@ -1536,11 +1554,12 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
   const long pstride = (long)g.M * g.N;
   // Every load of the row (partials, bias, residual, gate) is issued before any arithmetic, with no
   // control flow between them, so their latencies overlap: lanes past the row's end read its last quad
-  // (the values are dropped), and a missing bias is read from a valid address and selected away.
+  // (the values are dropped), and a missing bias is read from a zero row.
   float4 v[G], hv[G], gv[G];
   int qc[G];
 #pragma unroll
   for (int k = 0; k < G; ++k) qc[k] = min(t + 256 * k, nv - 1);
+  // fp32 partials: the bias is added here; bf16 partials (the block's fused path): split 0's carries it
   const float* bsrc = g.bias ? g.bias : fin_zero_row;
   const float* grow = nullptr;
   if constexpr (EPI == EPI_RESID_GATED) {
@@ -1548,8 +1567,7 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
     const int ch = rb / g.rm.Lq, grp = (rb % g.rm.Lq) < g.rm.Lv ? 0 : 1;
     grow = g.e6 + ((long)(ch * 2 + grp) * 6 + g.gate_idx) * g.D;
   }
-  auto load_all = [&](auto bf16_parts) {
-    constexpr bool PB = decltype(bf16_parts)::value;
+  {
     using Raw = std::conditional_t<PB, uint2, float4>;
     const Raw* pp = reinterpret_cast<const Raw*>(g.part) + (long)m * nv;   // one quad per element
     const long qstride = pstride / 4;                                        // quads per split
@@ -1559,7 +1577,7 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
     for (int k = 0; k < G; ++k) {
 #pragma unroll
       for (int sp = 0; sp < SPLITS; ++sp) raw[k][sp] = pp[sp * qstride + qc[k]];
-      bv[k] = reinterpret_cast<const float4*>(bsrc)[qc[k]];
+      if constexpr (!PB) bv[k] = reinterpret_cast<const float4*>(bsrc)[qc[k]];
       if constexpr (EPI != EPI_STORE) hv[k] = reinterpret_cast<const float4*>(g.H + (long)m * g.ldh)[qc[k]];
       if constexpr (EPI == EPI_RESID_GATED) {
         ge[k] = reinterpret_cast<const float4*>(grow)[qc[k]];
@@ -1581,7 +1599,7 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
         const float4 b = widen(raw[k][sp]);
         a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
       }
-      a.x += bv[k].x; a.y += bv[k].y; a.z += bv[k].z; a.w += bv[k].w;
+      if constexpr (!PB) { a.x += bv[k].x; a.y += bv[k].y; a.z += bv[k].z; a.w += bv[k].w; }
       const bool in = t + 256 * k < nv;
       v[k] = keep_if(in, a);
       if constexpr (EPI != EPI_STORE) hv[k] = keep_if(in, hv[k]);
@@ -1591,11 +1609,7 @@ __global__ void __launch_bounds__(256) splitk_finish_kernel(GemmArgs g, PostArgs
       else
         gv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  };
-  if (g.part_bf16)
-    load_all(std::true_type{});
-  else
-    load_all(std::false_type{});
+  }
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     const int q = t + 256 * k;
@@ -1727,10 +1741,16 @@ hipError_t launch_split_finish(const GemmArgs& a, Epi epi, const PostArgs& post,
   if (!norm_ok && !(post.mode == POST_QK && epi == EPI_STORE)) return hipErrorInvalidValue;
   const dim3 grid(a.M), block(256);
   const int groups = (a.N / 4 + 255) / 256;   // float4 groups per thread
-#define WAM_FINISH_G(E, P, S)                                                                              \
-  if (groups <= 1) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 1>), grid, block, 0, s, a, post);      \
-  else if (groups <= 5) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 5>), grid, block, 0, s, a, post); \
-  else hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, FIN_G>), grid, block, 0, s, a, post);
+#define WAM_FINISH_GP(E, P, S, B)                                                                                \
+  if (groups <= 1) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 1, B>), grid, block, 0, s, a, post);      \
+  else if (groups <= 5) hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, 5, B>), grid, block, 0, s, a, post); \
+  else hipLaunchKernelGGL((splitk_finish_kernel<E, P, S, FIN_G, B>), grid, block, 0, s, a, post);
+#define WAM_FINISH_G(E, P, S)        \
+  if (a.part_bf16) {                 \
+    WAM_FINISH_GP(E, P, S, true)     \
+  } else {                           \
+    WAM_FINISH_GP(E, P, S, false)    \
+  }
 #define WAM_FINISH(E, P)                  \
   switch (splits) {                       \
     case 2: WAM_FINISH_G(E, P, 2) break;  \
@@ -1748,6 +1768,7 @@ hipError_t launch_split_finish(const GemmArgs& a, Epi epi, const PostArgs& post,
   }
 #undef WAM_FINISH
 #undef WAM_FINISH_G
+#undef WAM_FINISH_GP
   return hipGetLastError();
 }
 
