@@ -1373,14 +1373,18 @@ static G4Plan g4_plan(const GemmArgs& a, Epi epi) {
   return best;
 }
 
-// Fragment-packed weights: 160 x 384 tiles (waves of 160 x 96) or 128 x 512 (waves of 128 x 128), the
-// one whose busiest CU has less work, split over K as in g4_plan when there are fewer than 128 tiles.
+// Fragment-packed weights: 160 x 384 tiles (waves of 160 x 96), 160 x 256 (waves of 160 x 64) or
+// 128 x 512 (waves of 128 x 128), the one whose busiest CU has less work (the first on a tie), split
+// over K as in g4_plan when there are fewer than 128 tiles. At 928 x 5120 x 5120 the 160 x 256 tiles
+// have no partly filled column of tiles and split K in two instead of three, so the finish that sums
+// the partials reads a third less.
 // Every shape and every epilogue but the row gather runs here (a packed matrix has no unpacked copy
 // to fall back on): rows past M and columns past N are masked.
 struct G4pPlan {
-  int splits = 0;     // 0: not runnable (layout or alignment), 1: direct epilogue, else split-K
-  bool t160 = false;  // 160 x 384 tiles
+  int splits = 0;     // 0: the packed kernel does not take this product
+  int tile = 0;       // 0: 128 x 512, 1: 160 x 384, 2: 160 x 256
 };
+static constexpr int G4P_BM[3] = {128, 160, 160}, G4P_BN[3] = {512, 384, 256};
 static G4pPlan g4p_plan(const GemmArgs& a, Epi epi) {
   G4pPlan best;
   if (epi == EPI_ROWSEL_F32 || a.M <= 0 || a.N % 32 || a.K % 64 || a.K <= 0 || !aligned16(a.W) ||
@@ -1389,8 +1393,8 @@ static G4pPlan g4p_plan(const GemmArgs& a, Epi epi) {
     return best;
   const int KT = a.K / 64;
   long best_cost = 0;
-  for (const bool t160 : {false, true}) {
-    const int bm = t160 ? 160 : 128, bn = t160 ? 384 : 512;
+  for (int tile = 0; tile < 3; ++tile) {
+    const int bm = G4P_BM[tile], bn = G4P_BN[tile];
     const long tiles = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
     int splits = 1;
     if (tiles < 128 && a.part) {
@@ -1402,7 +1406,7 @@ static G4pPlan g4p_plan(const GemmArgs& a, Epi epi) {
     const long cost = rounds * bm * bn * ((KT + splits - 1) / splits);
     if (best.splits == 0 || cost < best_cost) {
       best.splits = splits;
-      best.t160 = t160;
+      best.tile = tile;
       best_cost = cost;
     }
   }
@@ -1411,11 +1415,13 @@ static G4pPlan g4p_plan(const GemmArgs& a, Epi epi) {
 
 template <int EPI>
 static void launch_g4p(const GemmArgs& a, const G4pPlan& p, hipStream_t s) {
-  const int bm = p.t160 ? 160 : 128, bn = p.t160 ? 384 : 512;
+  const int bm = G4P_BM[p.tile], bn = G4P_BN[p.tile];
   const long items = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn) * p.splits;
   const dim3 grid((unsigned)(8 * ((items + 7) / 8))), block(256);
-  if (p.t160)
+  if (p.tile == 1)
     hipLaunchKernelGGL((gemm4p_kernel<EPI, 5, 3>), grid, block, 0, s, a, p.splits);
+  else if (p.tile == 2)
+    hipLaunchKernelGGL((gemm4p_kernel<EPI, 5, 2>), grid, block, 0, s, a, p.splits);
   else
     hipLaunchKernelGGL((gemm4p_kernel<EPI, 4, 4>), grid, block, 0, s, a, p.splits);
 }
