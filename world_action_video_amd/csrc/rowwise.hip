@@ -938,6 +938,91 @@ __global__ void __launch_bounds__(256) flow_kernel(FlowArgs a) {
   }
 }
 
+// float4 form: the video and the action part each run their own grid-stride loop, four of a
+// thread's float4s per pass with every load of the pass issued before any arithmetic (positions past
+// the end re-read the last float4; their results are dropped), and the branch count, the cosine
+// and the velocity store are compile-time cases, so no control flow sits between the loads. A
+// thread visits the video float4s in the same order as the single-loop form, so the cosine partials
+// are summed in that order.
+template <bool TWO, bool PREV, bool GOUT>
+__device__ __forceinline__ void flow_range4(const float4* v, long nn, float4* x,
+                                            const float4* prev, float4* gout, float wc,
+                                            float wu, float dt, float& dot, float& gg, float& pp) {
+  constexpr int U = 4;
+  const long S = (long)gridDim.x * 256;
+  for (long i0 = (long)blockIdx.x * 256 + threadIdx.x; i0 < nn; i0 += U * S) {
+    float4 cv[U], uv[U], xv[U], pv[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const long i = min(i0 + j * S, nn - 1);
+      cv[j] = nt_load(v + i);
+      if constexpr (TWO) uv[j] = nt_load(v + nn + i);
+      xv[j] = x[i];
+      if constexpr (PREV) pv[j] = prev[i];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const long i = i0 + j * S;
+      if (i < nn) {
+        float4 g = cv[j];
+        if constexpr (TWO) {
+          const float4 u = uv[j];
+          g.x = wc * g.x + wu * u.x; g.y = wc * g.y + wu * u.y; g.z = wc * g.z + wu * u.z; g.w = wc * g.w + wu * u.w;
+        }
+        float4 xn = xv[j];
+        xn.x += dt * g.x; xn.y += dt * g.y; xn.z += dt * g.z; xn.w += dt * g.w;
+        nt_store(x + i, xn);
+        if constexpr (PREV) {
+          const float4 q = pv[j];
+          dot += g.x * q.x; dot += g.y * q.y; dot += g.z * q.z; dot += g.w * q.w;
+          gg += g.x * g.x; gg += g.y * g.y; gg += g.z * g.z; gg += g.w * g.w;
+          pp += q.x * q.x; pp += q.y * q.y; pp += q.z * q.z; pp += q.w * q.w;
+        }
+        if constexpr (GOUT) nt_store(gout + i, g);
+      }
+    }
+  }
+}
+
+template <bool TWO>
+__device__ __forceinline__ void flow_parts4(const FlowArgs& a, float& dot, float& gg, float& pp) {
+  const float wc = TWO ? a.w : 1.f, wu = TWO ? 1.f - a.w : 0.f;
+  const float4* vv = reinterpret_cast<const float4*>(a.vv);
+  const float4* va = reinterpret_cast<const float4*>(a.va);
+  float4* xv = reinterpret_cast<float4*>(a.xv);
+  float4* xa = reinterpret_cast<float4*>(a.xa);
+  const float4* pr = reinterpret_cast<const float4*>(a.prev);
+  float4* gv = reinterpret_cast<float4*>(a.gv);
+  float4* ga = reinterpret_cast<float4*>(a.ga);
+  const long nv = a.nv / 4, na = a.na / 4;
+  if (a.prev) {
+    if (a.gv) flow_range4<TWO, true, true>(vv, nv, xv, pr, gv, wc, wu, a.dtv, dot, gg, pp);
+    else flow_range4<TWO, true, false>(vv, nv, xv, pr, gv, wc, wu, a.dtv, dot, gg, pp);
+  } else {
+    if (a.gv) flow_range4<TWO, false, true>(vv, nv, xv, pr, gv, wc, wu, a.dtv, dot, gg, pp);
+    else flow_range4<TWO, false, false>(vv, nv, xv, pr, gv, wc, wu, a.dtv, dot, gg, pp);
+  }
+  if (a.ga) flow_range4<TWO, false, true>(va, na, xa, nullptr, ga, wc, wu, a.dta, dot, gg, pp);
+  else flow_range4<TWO, false, false>(va, na, xa, nullptr, ga, wc, wu, a.dta, dot, gg, pp);
+}
+
+__global__ void __launch_bounds__(256) flow4_kernel(FlowArgs a) {
+  __shared__ float red[4];
+  float dot = 0.f, gg = 0.f, pp = 0.f;
+  if (a.br == 2) flow_parts4<true>(a, dot, gg, pp);
+  else flow_parts4<false>(a, dot, gg, pp);
+  if (a.prev) {
+    dot = block_sum<256>(dot, red);
+    gg = block_sum<256>(gg, red);
+    pp = block_sum<256>(pp, red);
+    if (threadIdx.x == 0) {
+      a.partials[blockIdx.x * 3 + 0] = dot;
+      a.partials[blockIdx.x * 3 + 1] = gg;
+      a.partials[blockIdx.x * 3 + 2] = pp;
+    }
+  }
+}
+
 // One wave: lane l sums blocks l, l + 64, ... in order, then a fixed butterfly across the lanes.
 __global__ void __launch_bounds__(64) flow_reduce_kernel(const float* partials, int nblocks, float* out) {
   float s[3] = {0.f, 0.f, 0.f};
@@ -955,7 +1040,7 @@ hipError_t launch_flow_step(const FlowArgs& a, hipStream_t s) {
   const bool v4 = flow_vec4(a);
   const int nb = a.nblocks;
   if (nb < 1 || nb > FLOW_MAX_BLOCKS) return hipErrorInvalidValue;
-  if (v4) hipLaunchKernelGGL(flow_kernel<4>, dim3(nb), dim3(256), 0, s, a);
+  if (v4) hipLaunchKernelGGL(flow4_kernel, dim3(nb), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(flow_kernel<1>, dim3(nb), dim3(256), 0, s, a);
   if (a.prev && a.cos_parts) hipLaunchKernelGGL(flow_reduce_kernel, dim3(1), dim3(64), 0, s, a.partials, nb, a.cos_parts);
   return hipGetLastError();
