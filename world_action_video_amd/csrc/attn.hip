@@ -262,7 +262,9 @@ attn_kernel(AttnArgs a) {
 // exceeds it by more than 2^8 for some query of the wave; otherwise probabilities up to 2^8 are
 // accumulated against the old reference. The final normalisation divides by the sum accumulated
 // against the same reference, so the result is the exact softmax (rescaling is exact up to
-// rounding). The score scale is folded into the exponent: p = exp2(s c - m), c = log2(e)/sqrt(d).
+// rounding). p = exp2(s c - m), c = log2(e)/sqrt(d), comes out of the score product itself: the
+// query fragments are pre-scaled by c (rounded to bf16 once more) and the first MFMA of a tile
+// accumulates onto a block holding -m, so the exponent needs no vector arithmetic.
 // The row sum is taken over the bf16-rounded probabilities (dot products of the packed pairs with
 // ones), i.e. over exactly the weights the value product uses, and the tile maximum is a tree of
 // three-input maxima (no NaN-quieting steps: scores are finite or -inf by construction).
@@ -469,13 +471,19 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return r;
 }
 
-// Row maximum of the 16 scores a lane holds (-inf start), then with the partner lane's 16, in log2 units.
-__device__ __forceinline__ float tile_max(const floatx16& s, float c) {
+// Row maximum of the 16 relative scores a lane holds (-inf start), then with the partner lane's 16.
+__device__ __forceinline__ float tile_max_rel(const floatx16& s) {
   const float a0 = vmax3(s[0], s[1], s[2]), a1 = vmax3(s[3], s[4], s[5]), a2 = vmax3(s[6], s[7], s[8]);
   const float a3 = vmax3(s[9], s[10], s[11]), a4 = vmax3(s[12], s[13], s[14]);
   const float m = vmax3(vmax3(a0, a1, a2), vmax3(a3, a4, s[15]), -INFINITY);
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  return vmax3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), -INFINITY) * c;
+  return vmax3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), -INFINITY);
+}
+
+// Eight bf16 values times c, rounded back to bf16 (to nearest even).
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float c) {
+  auto sc = [c](uint32_t w) { return pack2_bf16(__uint_as_float(w << 16) * c, __uint_as_float(w & 0xffff0000u) * c); };
+  return make_uint4(sc(v.x), sc(v.y), sc(v.z), sc(v.w));
 }
 
 // Scores of keys at or past the lane's limit become -inf (select). Register e holds key
@@ -484,22 +492,6 @@ __device__ __forceinline__ void mask_tile(floatx16& s, int key0, int half, int l
   const int rel = lim - key0 - 8 * half;
 #pragma unroll
   for (int e = 0; e < 16; ++e) s[e] = 16 * (e >> 3) + (e & 7) < rel ? s[e] : -INFINITY;
-}
-
-// Lazy softmax reference update for one tile (tmax already in log2 units): raise the reference and
-// rescale only when some query of the wave exceeds it by more than 2^8.
-template <int DB>
-__device__ __forceinline__ void raise_reference(float tmax, float& m_ref, float& l_run, floatx16 (&o)[DB]) {
-  if (__any(tmax > m_ref + 8.f)) {
-    const float m_new = fmaxf(m_ref, tmax);
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-    m_ref = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-  }
 }
 
 // Per tile kt: scores from K fragments already in registers, value fragments requested, stage
@@ -532,8 +524,15 @@ attn3_kernel(AttnArgs a) {
   floatx16 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = floatx16{};
-  float m_ref = -INFINITY, l_run = 0.f;   // m_ref in scaled (log2) units
-  const float c = a.scale_log2;
+  // The query fragments are multiplied by log2(e)/sqrt(d) once (one more bf16 rounding of each
+  // query element), so scores leave the product in log2 units; the product starts from -m_ref
+  // (negm, the lane's reference broadcast over its 16 scores), so they also leave it relative to the
+  // reference and go straight into exp2. m_ref = -inf: no visible key yet (negm holds 0). thr is
+  // the relative score that raises the reference: any visible score while there is none, else 2^8.
+#pragma unroll
+  for (int cc = 0; cc < DC; ++cc) qf[cc] = scale_bf16x8(qf[cc], a.scale_log2);
+  float m_ref = -INFINITY, l_run = 0.f, thr = -INFINITY;
+  floatx16 negm = floatx16{};
 
   const int srow = swap_bits_2_3(l32);
   uint4 kf[DC];
@@ -560,9 +559,10 @@ attn3_kernel(AttnArgs a) {
     const int kt = t0 + i;
     const char* sb = lds + (i % NS) * SB;
     // (1) S^T = K Q^T for 32 keys (rows permuted) x this wave's 32 queries
-    floatx16 s = floatx16{};
+    floatx16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[0]),
+                                                         __builtin_bit_cast(bf16x8_t, qf[0]), negm, 0, 0, 0);
 #pragma unroll
-    for (int cc = 0; cc < DC; ++cc)
+    for (int cc = 1; cc < DC; ++cc)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[cc]), __builtin_bit_cast(bf16x8_t, qf[cc]), s,
                                                   0, 0, 0);
     // (2) value fragments of this tile
@@ -587,24 +587,39 @@ attn3_kernel(AttnArgs a) {
     // (6) softmax; register e of s holds key kt*32 + 16 (e / 8) + 8 half + (e % 8)
     const int key0 = kt * AT3_BKV;
     if (key0 + AT3_BKV > it.wave_lim) mask_tile(s, key0, half, it.my_lim);
-    raise_reference(tile_max(s, c), m_ref, l_run, o);
-    // a query with no visible key yet keeps m_ref = -inf and must produce p = 0, not NaN
-    const float moff = m_ref == -INFINITY ? 0.f : m_ref;
+    {
+      // lazy reference: raised only when some query of the wave needs it (rare after the first tile)
+      const float tm = tile_max_rel(s);
+      if (__any(tm > thr)) {
+        const float off = m_ref == -INFINITY ? 0.f : m_ref;                 // what negm subtracted
+        const float m_new = m_ref == -INFINITY ? tm : fmaxf(m_ref, off + tm);
+        const float up = m_new == -INFINITY ? 0.f : m_new - off;
+        if (m_ref != -INFINITY && m_new > m_ref) {
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] -= up;
+        m_ref = m_new;
+        thr = m_new == -INFINITY ? -INFINITY : 8.f;
+        const float nm = m_new == -INFINITY ? 0.f : -m_new;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) negm[e] = nm;
+      }
+    }
     uint4 pf[2];
     {
       uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 16; e += 2)
-        w[e >> 1] = pack2_bf16(__builtin_amdgcn_exp2f(fmaf(s[e], c, -moff)), __builtin_amdgcn_exp2f(fmaf(s[e + 1], c, -moff)));
+      for (int e = 0; e < 16; e += 2) w[e >> 1] = pack2_bf16(__builtin_amdgcn_exp2f(s[e]), __builtin_amdgcn_exp2f(s[e + 1]));
       // row sum of exactly the bf16 weights the value product uses: dot products with ones
       const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-      float la = 0.f, lb = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; k += 2) {
-        la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k]), one, la, false);
-        lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k + 1]), one, lb, false);
-      }
-      l_run += la + lb;
+      for (int k = 0; k < 8; ++k) l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k]), one, l_run, false);
       pf[0] = make_uint4(w[0], w[1], w[2], w[3]);
       pf[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
