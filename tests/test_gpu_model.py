@@ -582,6 +582,35 @@ def test_flow_step_matches_oracle(gpu, nv, na):
     assert np.array_equal(Gv2.cpu().numpy(), vv[0])
 
 
+@pytest.mark.parametrize("nv,na", [(28160, 192), (1_000_000, 4096)])
+def test_flow_step_single_branch_and_cosine_only(gpu, nv, na):
+    """The float4 path's other cases: one branch (the velocity is the guided velocity, no guidance
+    arithmetic) with the cosine but no stored video velocity, and two branches with the cosine and
+    neither velocity stored; both against the oracle's Euler update and fp64 cosine."""
+    rng = synth.tensor_key(101, 2, "flow-cases")
+    v = synth.fill((2, nv + na), rng, "normal", 1.0)
+    xv = synth.fill((nv,), rng + 1, "normal", 1.0)
+    xa = synth.fill((na,), rng + 2, "normal", 1.0)
+    prev = synth.fill((nv,), rng + 3, "normal", 1.0)
+    vv, va = np.ascontiguousarray(v[:, :nv]), np.ascontiguousarray(v[:, nv:])
+    d = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(gpu)  # noqa: E731
+    ws = torch.empty(32768, dtype=torch.uint8, device=gpu)
+    for br in (1, 2):
+        print("flow-cases", nv, na, br, flush=True)
+        Xv, Xa, cos = d(xv), d(xa), torch.empty(3, device=gpu)
+        Ga = torch.empty(na, device=gpu) if br == 1 else None
+        wam.wam_flow_step(Xv, Xa, d(vv[:br]), d(va[:br]), br, 5.0, nv, na, 1 / 16, 0.25, None, Ga, d(prev), cos, ws)
+        torch.cuda.synchronize()
+        gv = vv[0] if br == 1 else O.cfg_combine(vv, 5.0)
+        ga = va[0] if br == 1 else O.cfg_combine(va, 5.0)
+        if br == 1:
+            assert np.array_equal(Ga.cpu().numpy(), va[0])
+        np.testing.assert_allclose(Xv.cpu().numpy(), O.euler_update(xv, gv, 0.0, 1 / 16), rtol=2e-6, atol=2e-6)
+        np.testing.assert_allclose(Xa.cpu().numpy(), O.euler_update(xa, ga, 0.0, 0.25), rtol=2e-6, atol=2e-6)
+        c = cos.cpu().numpy().astype(np.float64)
+        assert abs(c[0] / np.sqrt(c[1] * c[2]) - O.cosine_fp64(gv, prev)) < 1e-5
+
+
 @pytest.mark.parametrize("nv,na", [(0, 192), (28160, 0), (5, 3)])
 def test_flow_step_one_group_or_tiny(gpu, nv, na):
     """Degenerate sizes: no video part, no action part, and fewer elements than one vector (the scalar

@@ -226,10 +226,13 @@ def test_op_attention_key_split(gpu, d, Lq, kv_base, chunk_q, kv_total):
     (40, 464, 0, 0, 769),       # cross-attention geometry
     (33, 480, 0, 160, 480),     # full-sequence pass of three chunks
     (36, 385, 0, 0, 1000),      # last block of 65 queries: waves 2-4 hold (almost) none
+    (40, 400, 0, 0, 20),        # one key tile per block: the single-range five-wave kernel
 ])
 def test_op_attention_five_wave_blocks(gpu, H, Lq, kv_base, chunk_q, kv_total):
     """Shapes whose 128-query blocks overflow the 256 CUs while 160-query blocks fit in one round take
-    five-wave workgroups (the fifth wave only computes): against the oracle."""
+    five-wave query blocks: the ten-wave kernel that splits each block's key tiles into two halves
+    (odd tile counts, ragged last tiles, chunk limits inside either half), or the five-wave kernel
+    when a block holds a single key tile: against the oracle."""
     print("attention-five-wave", H, Lq, kv_base, chunk_q, kv_total, flush=True)
     assert -(-Lq // 128) * 2 * H > 256 and -(-Lq // 160) * 2 * H <= 256
     out, ref = _attn_case(gpu, "bf16", 2, H, 128, Lq, kv_base, chunk_q, kv_total, "w5_%d_%d_%d" % (H, Lq, kv_total))

@@ -647,6 +647,199 @@ attn3_kernel(AttnArgs a) {
   }
 }
 
+// Two key ranges inside one workgroup: NW query waves x 2 (waves NW .. 2 NW - 1 take the upper
+// half of the block's key tiles, one tile more when the count is odd). With NW = 5 the ten waves sit
+// three, three, two and two on the SIMDs, so the busiest SIMD issues three half-length chains (66
+// tile steps at 44 tiles) instead of two full ones (88). Three waves per SIMD leave 168 registers per
+// lane, so the block's query fragments (pre-scaled as in attn3_kernel) live in LDS, fragment-major,
+// and each tile reads them with its key fragments in two bounded halves. Each key half streams its
+// tiles through its own three-stage ring with attn3_kernel's copy / hand-over protocol; the rings
+// share the workgroup's barriers, so every wave runs the same number of loop steps (a half that has
+// run out of tiles skips the compute). At the end the upper half publishes its accumulators,
+// reference and row-sum shares in LDS and the lower half merges them in a fixed order (lower, then
+// upper: deterministic), normalises and stores. Every block must hold at least two key tiles (the
+// launcher checks the first query block, whose limit is the least).
+template <int D, int NS, int NW>
+__global__ void __launch_bounds__(2 * NW * 64) attn3h_kernel(AttnArgs a) {
+  using Ring = KvRing<D, NS, NW>;
+  constexpr int SB = Ring::SB, DC = D / 16, DB = D / 32;
+  constexpr int SROW = D + 8;
+  constexpr int RINGS = 2 * NS * SB;
+  constexpr int QBYTES = NW * DC * 64 * 16;                  // query fragments of the block
+  constexpr int PART_ACC = DB * 4 * 64;                      // float4 accumulators of one wave's share
+  constexpr int PART_BYTES = NW * (PART_ACC * 16 + 2 * 64 * 4);
+  static_assert(D == 128, "ring, partials and output staging are sized for 128-wide heads");
+  static_assert(NS >= 3, "the hand-over waits for the copies issued one tile earlier");
+  static_assert(PART_BYTES + NW * 32 * SROW * 2 <= RINGS + QBYTES, "partials and output staging fit");
+  __shared__ __attribute__((aligned(1024))) uint4 smem[(RINGS + QBYTES) / 16];
+  char* lds = reinterpret_cast<char*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave >= NW ? 1 : 0;   // key half (wave-uniform)
+  const int qw = wave - kh * NW;       // query wave inside the block
+  const int half = lane >> 5, l32 = lane & 31;
+  const AttnItem<NW> it(a, qw, l32, 1);
+  if (!it.valid) return;   // workgroup-uniform
+  const int nh = it.n_tiles / 2;
+  const int t0 = kh ? nh : 0, t1 = kh ? it.n_tiles : nh;
+  const int nt = t1 - t0, n_iter = it.n_tiles - nh;   // the upper half holds the odd tile
+  char* rl = lds + kh * NS * SB;
+  const Ring ring(a, it.bh, rl, qw, lane, t1);
+  const int tail_tile = (a.kv_total % AT3_BKV) ? a.kv_total / AT3_BKV : -1;
+  const int tail0 = tail_tile >= 0 && tail_tile < nh ? tail_tile : -1;
+  const int tail1 = tail_tile >= nh && tail_tile < it.n_tiles ? tail_tile - nh : -1;
+  const int my_tail = kh ? tail1 : tail0;
+  const uint4* qlds = reinterpret_cast<const uint4*>(lds + RINGS) + qw * DC * 64 + lane;
+
+  if (!kh) {   // the lower half stages the block's pre-scaled query fragments
+    uint4 qf[DC];
+    load_q_frags<D, NW>(a, it, half, qf);
+    uint4* qd = reinterpret_cast<uint4*>(lds + RINGS) + qw * DC * 64 + lane;
+#pragma unroll
+    for (int cc = 0; cc < DC; ++cc) qd[cc * 64] = scale_bf16x8(qf[cc], a.scale_log2);
+  }
+  floatx16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = floatx16{};
+  float m_ref = -INFINITY, l_run = 0.f, thr = -INFINITY;
+  floatx16 negm = floatx16{};
+
+  const int srow = swap_bits_2_3(l32);
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) ring.copy(t0 + t, t);
+  vmcnt_wait<Ring::PER_WAVE * (NS - 2)>();
+  lds_barrier();   // the copies of each half's first tile and the query fragments are visible
+  if (my_tail == 0) Ring::zero_tail(rl, 0, tail_tile, a.kv_total, qw * 64 + lane);
+  if (tail0 == 0 || tail1 == 0) lds_barrier();
+  for (int i = 0; i < n_iter; ++i) {
+    const int kt = t0 + i;
+    const bool act = i < nt;   // wave-uniform: only the lower half can run out, one step early
+    const char* sb = rl + (i % NS) * SB;
+    const char* sk = sb + srow * (D * 2);
+    floatx16 s = negm;
+    if (act) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        uint4 kf[DC / 2], qf[DC / 2];
+#pragma unroll
+        for (int c2 = 0; c2 < DC / 2; ++c2) {
+          const int cc = hb * (DC / 2) + c2;
+          kf[c2] = *reinterpret_cast<const uint4*>(sk + (((2 * cc + half) ^ Ring::kswz(srow)) * 16));
+          qf[c2] = qlds[cc * 64];
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < DC / 2; ++c2)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[c2]), __builtin_bit_cast(bf16x8_t, qf[c2]),
+                                                      s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    vmcnt_wait<Ring::PER_WAVE * (NS - 3)>();
+    lds_hand_over();
+    if (i + 1 == my_tail) Ring::zero_tail(rl, (i + 1) % NS, tail_tile, a.kv_total, qw * 64 + lane);
+    if (i + 1 == tail0 || i + 1 == tail1) lds_barrier();
+    ring.copy(kt + NS - 1, (i + NS - 1) % NS);
+    if (act) {
+      uint4 vf[DB][2];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = db * 32 + l32;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          vf[db][j] = *reinterpret_cast<const uint4*>(sb + Ring::KB + row * 64 + (((2 * j + half) ^ Ring::vswz(row)) * 16));
+      }
+      const int key0 = kt * AT3_BKV;
+      if (key0 + AT3_BKV > it.wave_lim) mask_tile(s, key0, half, it.my_lim);
+      {
+        const float tm = tile_max_rel(s);
+        if (__any(tm > thr)) {
+          const float off = m_ref == -INFINITY ? 0.f : m_ref;
+          const float m_new = m_ref == -INFINITY ? tm : fmaxf(m_ref, off + tm);
+          const float up = m_new == -INFINITY ? 0.f : m_new - off;
+          if (m_ref != -INFINITY && m_new > m_ref) {
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] -= up;
+          m_ref = m_new;
+          thr = m_new == -INFINITY ? -INFINITY : 8.f;
+          const float nm = m_new == -INFINITY ? 0.f : -m_new;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) negm[e] = nm;
+        }
+      }
+      uint4 pf[2];
+      {
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) w[e >> 1] = pack2_bf16(__builtin_amdgcn_exp2f(s[e]), __builtin_amdgcn_exp2f(s[e + 1]));
+        const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[k]), one, l_run, false);
+        pf[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        pf[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[db][j]),
+                                                           __builtin_bit_cast(bf16x8_t, pf[j]), o[db], 0, 0, 0);
+    }
+  }
+  vmcnt_wait<0>();
+  lds_barrier();
+  // the upper half publishes (accumulator float4 q of lane l at q * 64 + l), the lower half merges
+  float4* pacc = reinterpret_cast<float4*>(lds) + qw * PART_ACC;
+  float* pml = reinterpret_cast<float*>(lds + NW * PART_ACC * 16) + qw * 128;
+  if (kh) {
+#pragma unroll
+    for (int q = 0; q < DB * 4; ++q)
+      pacc[q * 64 + lane] = make_float4(o[q >> 2][4 * (q & 3)], o[q >> 2][4 * (q & 3) + 1], o[q >> 2][4 * (q & 3) + 2],
+                                        o[q >> 2][4 * (q & 3) + 3]);
+    pml[lane] = m_ref;
+    pml[64 + lane] = l_run;
+  }
+  lds_barrier();
+  bf16_t* stage = reinterpret_cast<bf16_t*>(lds + PART_BYTES) + qw * 32 * SROW;
+  if (!kh) {
+    const float m1 = pml[lane], l1 = pml[64 + lane];
+    const float mx = fmaxf(m_ref, m1);
+    const float f0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mx);
+    const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+    const float l = f0 * l_run + f1 * l1;
+    const float l_tot = l + __shfl_xor(l, 32, 64);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int q = 0; q < DB * 4; ++q) {
+      const float4 u = pacc[q * 64 + lane];
+      const int db = q >> 2, e = 4 * (q & 3);
+      stage[l32 * SROW + db * 32 + acc_row(e, lane)] = f32_to_bf16((f0 * o[db][e] + f1 * u.x) * inv);
+      stage[l32 * SROW + db * 32 + acc_row(e + 1, lane)] = f32_to_bf16((f0 * o[db][e + 1] + f1 * u.y) * inv);
+      stage[l32 * SROW + db * 32 + acc_row(e + 2, lane)] = f32_to_bf16((f0 * o[db][e + 2] + f1 * u.z) * inv);
+      stage[l32 * SROW + db * 32 + acc_row(e + 3, lane)] = f32_to_bf16((f0 * o[db][e + 3] + f1 * u.w) * inv);
+    }
+  }
+  lds_barrier();
+  if (!kh) {
+    constexpr int ROW_UNITS = D / 8;
+    bf16_t* O = reinterpret_cast<bf16_t*>(a.O);
+    for (int u = lane; u < 32 * ROW_UNITS; u += 64) {
+      const int r = u / ROW_UNITS, cu = u % ROW_UNITS;
+      const int qq = it.qblk + qw * 32 + r;
+      if (qq < a.Lq_total)
+        *reinterpret_cast<uint4*>(O + ((long)it.b * a.Lq_total + qq) * ((long)a.H * D) + (long)it.h * D + cu * 8) =
+            reinterpret_cast<const uint4*>(stage + r * SROW)[cu];
+    }
+  }
+}
+
 // Merge of the key-split partials of one query block (one workgroup): every lane combines the
 // values it held in each range, p-weighted by 2^(m_s - M) with M the largest reference, in range
 // order (deterministic), then normalises and stores like the unsplit kernel. A range with no
@@ -698,6 +891,13 @@ static hipError_t launch_attn3(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Five query waves x two key halves (ten waves per workgroup), three-stage rings.
+static hipError_t launch_attn3h(const AttnArgs& a, hipStream_t s) {
+  const int blocks = ((a.Lq_total + 159) / 160) * a.H * a.br;
+  hipLaunchKernelGGL((attn3h_kernel<128, 3, 5>), dim3(8 * ((blocks + 7) / 8)), dim3(640), 0, s, a);
+  return hipGetLastError();
+}
+
 // Key split (flash-decoding style): only when the query blocks fill fewer than half of the 256 CUs
 // and every range keeps at least four tiles; ranges up to the CU count, at most eight.
 int attn_kv_splits(int Lq_total, int H, int br, int kv_total) {
@@ -741,6 +941,9 @@ hipError_t launch_attention(const AttnArgs& a, DType dt, hipStream_t s) {
     // five waves (160 queries) per block when four-wave blocks would overflow the 256 CUs and
     // five-wave blocks fit them in one round (e.g. 2 x 40 heads x 464 queries: 320 -> 240 blocks)
     const bool five = b.kv_splits == 1 && (a.Lq_total + 127) / 128 * heads > 256 && (a.Lq_total + 159) / 160 * heads <= 256;
+    // the two-half kernel needs two key tiles in every block; the first block's limit is the least
+    const bool halves = ((long)attn_limit(a, std::min(160, a.Lq_total) - 1) + AT3_BKV - 1) / AT3_BKV >= 2;
+    if (copy_ok && a.d == 128 && five && halves) return launch_attn3h(b, s);
     if (copy_ok && a.d == 128 && five) return launch_attn3<128, 4, 5>(b, s);
     if (copy_ok && a.d == 128) return launch_attn3<128>(b, s);
     if (copy_ok && a.d == 64) return launch_attn3<64>(b, s);
