@@ -717,14 +717,6 @@ __global__ void __launch_bounds__(2 * NW * 64) attn3h_kernel(AttnArgs a) {
     const bool act = i < nt;   // wave-uniform: only the lower half can run out, one step early
     const char* sb = rl + (i % NS) * SB;
     const char* sk = sb + srow * (D * 2);
-    // hand-over first (tile kt+1 visible, the stage of tile kt-1 free, the copy of tile kt+2 issued),
-    // then the whole of tile kt inside one barrier interval: every wave's chain runs between two
-    // barriers instead of straddling one
-    vmcnt_wait<Ring::PER_WAVE * (NS - 3)>();
-    lds_hand_over();
-    if (i + 1 == my_tail) Ring::zero_tail(rl, (i + 1) % NS, tail_tile, a.kv_total, qw * 64 + lane);
-    if (i + 1 == tail0 || i + 1 == tail1) lds_barrier();
-    ring.copy(kt + NS - 1, (i + NS - 1) % NS);
     floatx16 s = negm;
     if (act) {
 #pragma unroll
@@ -743,6 +735,11 @@ __global__ void __launch_bounds__(2 * NW * 64) attn3h_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    vmcnt_wait<Ring::PER_WAVE * (NS - 3)>();
+    lds_hand_over();
+    if (i + 1 == my_tail) Ring::zero_tail(rl, (i + 1) % NS, tail_tile, a.kv_total, qw * 64 + lane);
+    if (i + 1 == tail0 || i + 1 == tail1) lds_barrier();
+    ring.copy(kt + NS - 1, (i + NS - 1) % NS);
     if (act) {
       uint4 vf[DB][2];
 #pragma unroll
