@@ -166,9 +166,11 @@ def _attn_case(gpu, dtype, br, H, d, Lq, kv_base, chunk_q, kv_total, tag, v_stri
 ])
 def test_op_attention(gpu, dtype, d, Lq, kv_base, chunk_q, kv_total):
     print("attention", dtype, d, Lq, kv_base, chunk_q, kv_total, flush=True)
-    out, ref = _attn_case(gpu, dtype, 2, 3, d, Lq, kv_base, chunk_q, kv_total, "%d_%d_%d_%d_%d" % (d, Lq, kv_base, chunk_q, kv_total))
+    (out, out2), ref = _attn_case(gpu, dtype, 2, 3, d, Lq, kv_base, chunk_q, kv_total,
+                                  "%d_%d_%d_%d_%d" % (d, Lq, kv_base, chunk_q, kv_total), runs=2)
     assert np.all(np.isfinite(out))
     assert rel_l2(out, ref) <= (1e-2 if dtype == "bf16" else 1e-5)
+    assert np.array_equal(out, out2)   # a second run is bit-identical
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -196,9 +198,11 @@ def test_op_attention_long_ranges(gpu, d, Lq, kv_base, chunk_q, kv_total):
     """Query and key ranges of the long-context workload's order (1024+ queries over 3072+ keys, many
     tiles per workgroup); one branch and two heads keep the oracle fast."""
     print("attention-long", d, Lq, kv_base, chunk_q, kv_total, flush=True)
-    out, ref = _attn_case(gpu, "bf16", 1, 2, d, Lq, kv_base, chunk_q, kv_total, "l%d_%d_%d" % (d, Lq, kv_total))
+    (out, out2), ref = _attn_case(gpu, "bf16", 1, 2, d, Lq, kv_base, chunk_q, kv_total, "l%d_%d_%d" % (d, Lq, kv_total),
+                                  runs=2)
     assert np.all(np.isfinite(out))
     assert rel_l2(out, ref) <= 1e-2
+    assert np.array_equal(out, out2)   # a second run is bit-identical
 
 
 @pytest.mark.parametrize("d", [64, 128])
