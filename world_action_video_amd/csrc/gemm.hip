@@ -1404,7 +1404,8 @@ static G4pPlan g4p_plan(const GemmArgs& a, Epi epi) {
     }
     const long rounds = (tiles * splits + 255) / 256;
     const long cost = rounds * bm * bn * ((KT + splits - 1) / splits);
-    if (best.splits == 0 || cost < best_cost) {
+    // on a tie the plan with fewer K ranges wins: its finish reads fewer partials
+    if (best.splits == 0 || cost < best_cost || (cost == best_cost && splits < best.splits)) {
       best.splits = splits;
       best.tile = tile;
       best_cost = cost;
