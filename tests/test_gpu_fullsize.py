@@ -9,6 +9,7 @@
   committed chunks (8064 cached tokens), decoupled timesteps t_v = 1 - Beta(2, 1) and t_a ~ U(0, 1),
   full width with 2 layers.
 * One full-width block through the stack call in bf16 (2e-2) and in the fp32 debug mode (1e-4).
+* The step's kernels at full width (2 layers) twice on the same inputs: bit-identical outputs.
 * wam_dit_block_fwd: incremental, two-chunk and committing chains at the tiny width (f32 and bf16),
   and at the full-width one-block shape with 2 branches and with 1 (the per-GPU share of a branch
   split), against oracle.block_forward on the same residual stream and modulation.
@@ -135,6 +136,30 @@ def test_step_40_layers_cfg2_bf16_matches_oracle(gpu, capsys):
               O.PassSpec(xv, xa, [t], [t], 1, 2 * Fc)]
     outs = O.stack_passes(m, ctx, passes, progress=lambda l: say("oracle layer %d/%d" % (l + 1, w.layers)))
     _check_outputs(say, gv, ga, outs[2][0], outs[2][1], TOL["bf16"])
+
+
+@pytest.mark.timeout(600)
+def test_full_width_step_run_to_run_bitwise(gpu, capsys):
+    """The benchmarked step's kernels at full width (2 layers, CFG batch 2, 928 cached tokens, packed
+    projections: the ten-wave attention, the split products and their finishes) give bit-identical
+    outputs when the same step runs twice: every reduction has a fixed order."""
+    w = WORKLOADS[3].with_(layers=2)
+    say = Say(capsys, "full-width determinism")
+    Fc = w.frames_per_chunk
+    t = float(synth.workloads.timesteps(w, 1)[0])
+    x1v, x1a, _, _ = chunk_inputs(w, range(2))
+    xv, xa = draw_named(w, -1, "eps_video_2"), draw_named(w, -1, "eps_action_2")
+    txt, img = draw_named(w, -1, "txt"), draw_named(w, -1, "img")
+    say("gpu: 2 appends, the step twice at t = %.4f" % t)
+    run = GpuRun(w, "bf16", gpu, 3, txt, img, packed=True)
+    for c in range(2):
+        run.append(x1v[c], x1a[c], c * Fc)
+    gv1, ga1 = run.step(xv, xa, [t], [t], 2 * Fc)
+    gv2, ga2 = run.step(xv, xa, [t], [t], 2 * Fc)
+    del run
+    torch.cuda.empty_cache()
+    assert np.isfinite(gv1).all() and np.isfinite(ga1).all()
+    assert np.array_equal(gv1, gv2) and np.array_equal(ga1, ga2)
 
 
 @pytest.mark.timeout(1500)
