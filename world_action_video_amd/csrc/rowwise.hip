@@ -1138,7 +1138,7 @@ hipError_t launch_unipc_step(const UnipcArgs& a, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Output heads. A workgroup takes 16 rows and one K slice (at most 320 columns): the slice of both
+// Output heads (fp32, or bf16 with unaligned operands). A workgroup takes 16 rows and one K slice (at most 320 columns): the slice of both
 // head matrices and of the 16 rows goes to LDS once with coalesced 16-byte loads (video head rows
 // 0 .. P-1, action head rows 64 .. 64+A-1, the activation rows after them; rows padded by 8
 // elements so a wave's 64 weight-row reads hit distinct banks), then each wave computes 4 rows, lane
@@ -1211,6 +1211,84 @@ __global__ void __launch_bounds__(256) head_partial_kernel(HeadArgs a) {
     if (act[r]) a.part[((long)sp * a.M + mb + r) * 64 + n] = acc[r];
 }
 
+// bf16 heads on the matrix cores: a wave takes 32 rows and one K slice and forms, with 32x32x16
+// MFMAs (weight block first, so a lane holds one row's outputs in four runs of four), VB 32-column
+// blocks of the video head and AB of the action head for those rows; each row keeps the outputs of
+// the head its token belongs to. Operands come straight from memory (16 bytes per lane and step; the
+// two head matrices, under 1 MB, stay in L2). Weight rows past P (A) and activation rows past M
+// re-read the last one; their results are dropped. The slice's partial sums go to
+// part[slice][row][64] like the LDS kernel's, and head_reduce_kernel sums them in slice order.
+template <int VB, int AB>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) head_mfma_kernel(HeadArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sp = blockIdx.y * 4 + wave;   // K slice (wave-uniform)
+  if (sp >= a.splits) return;
+  const int kspan = a.D / a.splits, k0 = sp * kspan;
+  const int l32 = lane & 31, hk = (lane >> 5) * 8;
+  const int row = blockIdx.x * 32 + l32;
+  const bf16_t* y = reinterpret_cast<const bf16_t*>(a.Y) + (long)min(row, a.M - 1) * a.D + k0 + hk;
+  const bf16_t* wv[VB];
+  const bf16_t* wa[AB];
+#pragma unroll
+  for (int b = 0; b < VB; ++b)
+    wv[b] = reinterpret_cast<const bf16_t*>(a.wv) + (long)min(b * 32 + l32, a.P - 1) * a.D + k0 + hk;
+#pragma unroll
+  for (int b = 0; b < AB; ++b)
+    wa[b] = reinterpret_cast<const bf16_t*>(a.wa) + (long)min(b * 32 + l32, a.A - 1) * a.D + k0 + hk;
+  floatx16 accv[VB], acca[AB];
+#pragma unroll
+  for (int b = 0; b < VB; ++b) accv[b] = floatx16{};
+#pragma unroll
+  for (int b = 0; b < AB; ++b) acca[b] = floatx16{};
+  // five 16-column steps per pass, every load of the pass issued before its products, with no branch
+  // between them: a step past the slice re-reads the last one and its activation fragment becomes
+  // zero (a select), so its products add exact zeros
+  constexpr int C = 5;
+  for (int k = 0; k < kspan; k += 16 * C) {
+    uint4 yf[C];
+    bf16x8_t vf[C][VB], af[C][AB];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int kk = min(k + 16 * c, kspan - 16);
+      yf[c] = *reinterpret_cast<const uint4*>(y + kk);
+#pragma unroll
+      for (int b = 0; b < VB; ++b) vf[c][b] = *reinterpret_cast<const bf16x8_t*>(wv[b] + kk);
+#pragma unroll
+      for (int b = 0; b < AB; ++b) af[c][b] = *reinterpret_cast<const bf16x8_t*>(wa[b] + kk);
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const bool in = k + 16 * c < kspan;
+      const uint4 yv = make_uint4(in ? yf[c].x : 0u, in ? yf[c].y : 0u, in ? yf[c].z : 0u, in ? yf[c].w : 0u);
+      const bf16x8_t yb = __builtin_bit_cast(bf16x8_t, yv);
+#pragma unroll
+      for (int b = 0; b < VB; ++b) accv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c][b], yb, accv[b], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < AB; ++b) acca[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][b], yb, acca[b], 0, 0, 0);
+    }
+  }
+  if (row >= a.M) return;
+  const bool video = (row % a.rm.rows_per_branch) % a.rm.Lq < a.rm.Lv;
+  float* dst = a.part + ((long)sp * a.M + row) * 64;
+  // register e of block b holds output b * 32 + 8 (e / 4) + 4 (lane / 32) + e % 4 of this row
+  auto put = [&](const floatx16& acc, int b, int nout) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n0 = b * 32 + 8 * q + 4 * (lane >> 5);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n0 + e < nout) dst[n0 + e] = acc[4 * q + e];
+    }
+  };
+  if (video) {
+#pragma unroll
+    for (int b = 0; b < VB; ++b) put(accv[b], b, a.P);
+  } else {
+#pragma unroll
+    for (int b = 0; b < AB; ++b) put(acca[b], b, a.A);
+  }
+}
+
 __global__ void __launch_bounds__(256) head_reduce_kernel(HeadArgs a) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), n = threadIdx.x & 63;
   if (m >= a.M) return;
@@ -1220,8 +1298,19 @@ __global__ void __launch_bounds__(256) head_reduce_kernel(HeadArgs a) {
   const bool video = loc < a.rm.Lv;
   const int nout = video ? a.P : a.A;
   if (n >= nout) return;
+  // the slices in order; their loads issued eight at a time
+  const float* pp = a.part + (long)m * 64 + n;
+  const long st = (long)a.M * 64;
   float v = 0.f;
-  for (int sp = 0; sp < a.splits; ++sp) v += a.part[((long)sp * a.M + m) * 64 + n];
+  int sp = 0;
+  for (; sp + 8 <= a.splits; sp += 8) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = pp[(sp + j) * st];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += x[j];
+  }
+  for (; sp < a.splits; ++sp) v += pp[sp * st];
   v += video ? a.bv[n] : a.ba[n];
   if (video) a.vv[((long)(b * nch + ch) * a.rm.Lv + loc) * a.P + n] = v;
   else a.va[((long)(b * nch + ch) * La + (loc - a.rm.Lv)) * a.A + n] = v;
@@ -1230,9 +1319,28 @@ __global__ void __launch_bounds__(256) head_reduce_kernel(HeadArgs a) {
 hipError_t launch_head(const HeadArgs& a0, DType dt, hipStream_t s) {
   if (a0.M <= 0) return hipSuccess;
   if (a0.P > 64 || a0.A > 64 || a0.P < 1 || a0.A < 1 || a0.D % 8) return hipErrorInvalidValue;
+  HeadArgs a = a0;
+  // bf16 with 16-byte aligned operands: the matrix-core kernel, with K slices of a whole number of
+  // 16-column steps (up to 32 slices of at least 160 columns), four slices per workgroup
+  const bool al16 = reinterpret_cast<uintptr_t>(a.Y) % 16 == 0 && reinterpret_cast<uintptr_t>(a.wv) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(a.wa) % 16 == 0;
+  if (dt == DT_BF16 && al16 && a.D % 16 == 0) {
+    int sp = std::min(32, std::max(1, a.D / 160));
+    while (sp > 1 && (a.D % (16 * sp) || (long)sp * a.M * 64 > a.part_elems)) --sp;
+    if ((long)sp * a.M * 64 <= a.part_elems) {
+      a.splits = sp;
+      const dim3 grid((a.M + 31) / 32, (sp + 3) / 4), block(256);
+      const int vb = (a.P + 31) / 32, ab = (a.A + 31) / 32;
+      if (vb == 1 && ab == 1) hipLaunchKernelGGL((head_mfma_kernel<1, 1>), grid, block, 0, s, a);
+      else if (vb == 1) hipLaunchKernelGGL((head_mfma_kernel<1, 2>), grid, block, 0, s, a);
+      else if (ab == 1) hipLaunchKernelGGL((head_mfma_kernel<2, 1>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((head_mfma_kernel<2, 2>), grid, block, 0, s, a);
+      hipLaunchKernelGGL(head_reduce_kernel, dim3((a.M + 3) / 4), block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   // the fewest K slices of at most HEAD_KMAX columns, each a whole number of 8-column groups
   // (and whose weight slices fit the 64 KB of dynamic LDS)
-  HeadArgs a = a0;
   const size_t esz = dt == DT_BF16 ? 2 : 4;
   auto lds_of = [&](int sp) { return (size_t)(64 + a.A + HEAD_ROWS) * (a.D / sp + 8) * esz; };
   a.splits = 1;
