@@ -76,6 +76,32 @@ def tiny_oracle():
     return w, m, ckv
 
 
+@pytest.mark.parametrize("P,A", [(32, 8), (16, 40), (48, 64)])
+def test_stack_tiny_head_widths_bf16(gpu, P, A):
+    """Patch and action widths that give the output heads one or two 32-column blocks each (the
+    benchmarked shapes have 64 and 8): the bf16 step of a one-layer tiny model against the oracle."""
+    w = WORKLOADS[1].with_(layers=1, patch_dim=P, action_dim=A)
+    print("stack-tiny-heads", P, A, flush=True)
+    m = O.load_model(w)
+    txt = draw_named(w, -1, "txt")
+    ckv = [O.context_kv(w, lp, O.build_context(w, m.g, txt, None)) for lp in m.layers]
+    x1v, x1a, epv, epa = tiny_inputs(w)
+    xv1 = O.interpolate(x1v[1], epv[1], 0.5)
+    xa1 = O.interpolate(x1a[1], epa[1], 0.5)
+    cache = O.KVCache.empty(w.layers, w.branches, w.dim)
+    O.kv_append(m, cache, ckv, x1v[0], x1a[0], 0)
+    ref_v, ref_a = O.stack_forward(m, cache, ckv, xv1, xa1, [0.5], [0.5], 1, w.frames_per_chunk)
+    rig = Rig(w, "bf16", gpu)
+    dc = rig.cache()
+    rig.append(dc, x1v[0], x1a[0], 0)
+    gv, ga = rig.step(dc, 1, xv1, xa1, [0.5], [0.5], w.frames_per_chunk)
+    ev, ea = rel_l2(gv, ref_v), rel_l2(ga, ref_a)
+    print("rel-L2 video %.3e action %.3e" % (ev, ea), flush=True)
+    assert gv.shape[-1] == P and ga.shape[-1] == A
+    assert np.all(np.isfinite(gv)) and np.all(np.isfinite(ga))
+    assert ev <= TOL["bf16"] and ea <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_stack_tiny_matches_oracle(gpu, tiny_oracle, dtype):
     w, m, ckv = tiny_oracle
